@@ -1,0 +1,214 @@
+"""Seeded synthetic workloads for the LayerNorm / RMSNorm backward pass.
+
+This module only draws inputs. It holds none of the backward arithmetic: the
+GPU path and the fp64 oracle each implement that on their own, and both read
+their inputs from here.
+
+What a workload carries (the norm backward consumes the forward's saved
+per-row statistics, see "Norm backward in Triton — the dγ/dβ reduction",
+section "The dx kernel — recompute the stat, don't store x̂"):
+
+* ``x``, ``dy``, ``gamma`` in the I/O dtype (round-to-nearest-even casts of
+  fp32 draws), and for LayerNorm workloads that list one, ``beta`` (it enters
+  only the forward output, never the backward).
+* ``rstd`` (and ``mean`` for LayerNorm) in fp32: the statistics a forward pass
+  would have saved, evaluated in fp64 on the *cast* ``x`` and then rounded to
+  fp32. LayerNorm uses the biased variance (divide by N), as the forward in
+  "05: Layer norm" (the Phobos tutorial's ``ln_fwd``) does; RMSNorm uses the
+  mean of squares, as in "Norm backward in Triton", section "The gradients".
+
+Everything is drawn on the CPU from a ``torch.Generator`` with a fixed seed,
+in the fixed order x, dy, gamma, beta, outlier columns, so every consumer sees
+the same bits.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional, Sequence
+
+import torch
+
+LAYERNORM = "layernorm"
+RMSNORM = "rmsnorm"
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One synthetic backward problem: shapes, dtypes, distributions, seed."""
+
+    name: str
+    kind: str                     # LAYERNORM or RMSNORM
+    M: int                        # rows (tokens)
+    N: int                        # features
+    io_dtype: torch.dtype         # x, dy, gamma, dx
+    wgrad_dtype: torch.dtype      # dgamma, dbeta
+    eps: float
+    seed: int
+    x_dist: str = "normal"        # "normal" | "row_shift_scale"
+    dy_std: float = 1.0
+    gamma_lo: float = 0.5
+    gamma_hi: float = 1.5
+    with_beta: bool = False       # draw beta ~ U(0,1) (forward-only input)
+    outlier_frac: float = 0.0     # fraction of feature columns scaled
+    outlier_scale: float = 1.0
+    outlier_mode: str = "columns" # "columns" | "entries"
+
+    @property
+    def io_bytes(self) -> int:
+        return torch.tensor([], dtype=self.io_dtype).element_size()
+
+    def algorithmic_bytes(self, with_dbeta: Optional[bool] = None) -> int:
+        """Bytes the method must move: read x, dy, gamma and the saved stats,
+        write dx and the weight gradients. Workspace traffic is excluded."""
+        if with_dbeta is None:
+            with_dbeta = self.kind == LAYERNORM
+        s = self.io_bytes
+        w = torch.tensor([], dtype=self.wgrad_dtype).element_size()
+        stats = (8 if self.kind == LAYERNORM else 4) * self.M
+        nw = 2 if with_dbeta else 1
+        return 3 * self.M * self.N * s + self.N * s + stats + nw * self.N * w
+
+
+# The five problems the benchmark and the parity tests use. Shapes follow the
+# pages' worked example (16384 x 4096 bf16 RMSNorm, "Norm & activation
+# backward", "Worked number") and the Phobos tutorial's check (1151 x 8192
+# fp16 LayerNorm, "05: Layer norm").
+WORKLOADS: Dict[str, Workload] = {}
+
+
+def _register(w: Workload) -> Workload:
+    WORKLOADS[w.name] = w
+    return w
+
+
+LN_F32_128x512 = _register(Workload(
+    "layernorm_f32_128x512", LAYERNORM, 128, 512, torch.float32, torch.float32,
+    1e-5, 1001, dy_std=1.0, gamma_lo=0.5, gamma_hi=1.5))
+RMS_F32_128x512 = _register(dataclasses.replace(
+    LN_F32_128x512, name="rmsnorm_f32_128x512", kind=RMSNORM))
+LN_F16_1151x8192 = _register(Workload(
+    "layernorm_f16_1151x8192", LAYERNORM, 1151, 8192, torch.float16, torch.float16,
+    1e-5, 1002, dy_std=0.1, gamma_lo=0.0, gamma_hi=1.0, with_beta=True))
+RMS_BF16_16384x4096 = _register(Workload(
+    "rmsnorm_bf16_16384x4096", RMSNORM, 16384, 4096, torch.bfloat16, torch.float32,
+    1e-6, 1003, dy_std=1e-2, gamma_lo=0.8, gamma_hi=1.2))
+LN_BF16_65536x8192 = _register(Workload(
+    "layernorm_bf16_65536x8192", LAYERNORM, 65536, 8192, torch.bfloat16, torch.float32,
+    1e-5, 1004, x_dist="row_shift_scale", dy_std=1e-2, gamma_lo=0.5, gamma_hi=1.5))
+RMS_BF16_262144x768 = _register(Workload(
+    "rmsnorm_bf16_262144x768", RMSNORM, 262144, 768, torch.bfloat16, torch.float32,
+    1e-6, 1005, dy_std=1e-2, gamma_lo=0.5, gamma_hi=1.5,
+    outlier_frac=0.01, outlier_scale=50.0, outlier_mode="columns"))
+
+# The benchmark's headline problem.
+HEADLINE = RMS_BF16_16384x4096
+
+
+def scaled(w: Workload, M: Optional[int] = None, N: Optional[int] = None,
+           **kw) -> Workload:
+    """Same distributions at another size (for small parity cases)."""
+    M = w.M if M is None else M
+    N = w.N if N is None else N
+    name = kw.pop("name", f"{w.kind}_{_dt(w.io_dtype)}_{M}x{N}")
+    return dataclasses.replace(w, name=name, M=M, N=N, **kw)
+
+
+def _dt(d: torch.dtype) -> str:
+    return {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[d]
+
+
+def outlier_columns(w: Workload, gen: torch.Generator) -> torch.Tensor:
+    k = int(round(w.outlier_frac * w.N))
+    return torch.randperm(w.N, generator=gen)[:k]
+
+
+def make_inputs(w: Workload) -> Dict[str, torch.Tensor]:
+    """Draw the workload's inputs on the CPU (contiguous tensors).
+
+    Returns x, dy, gamma (io dtype), rstd (fp32 [M]), mean (fp32 [M], LayerNorm
+    only), beta (io dtype, only when the workload lists one), and the index
+    tensor ``outliers`` when outlier features are drawn.
+    """
+    g = torch.Generator().manual_seed(w.seed)
+    M, N = w.M, w.N
+    x = torch.randn(M, N, generator=g, dtype=torch.float32)
+    if w.x_dist == "row_shift_scale":
+        mu = torch.rand(M, 1, generator=g, dtype=torch.float32) * 4.0 - 2.0
+        sc = torch.rand(M, 1, generator=g, dtype=torch.float32) * 3.5 + 0.5
+        x.mul_(sc).add_(mu)
+    elif w.x_dist != "normal":
+        raise ValueError(w.x_dist)
+    dy = torch.randn(M, N, generator=g, dtype=torch.float32).mul_(w.dy_std)
+    gamma = torch.rand(N, generator=g, dtype=torch.float32)
+    gamma.mul_(w.gamma_hi - w.gamma_lo).add_(w.gamma_lo)
+    out: Dict[str, torch.Tensor] = {}
+    if w.with_beta:
+        out["beta"] = torch.rand(N, generator=g, dtype=torch.float32).to(w.io_dtype)
+    if w.outlier_frac > 0:
+        if w.outlier_mode == "columns":
+            cols = outlier_columns(w, g)
+            if M and cols.numel():
+                x[:, cols] *= w.outlier_scale
+            out["outliers"] = cols
+        elif w.outlier_mode == "entries":
+            mask = torch.rand(M, N, generator=g) < w.outlier_frac
+            x[mask] *= w.outlier_scale
+            out["outliers"] = mask.nonzero()
+        else:
+            raise ValueError(w.outlier_mode)
+    out["x"] = x.to(w.io_dtype)
+    del x
+    out["dy"] = dy.to(w.io_dtype)
+    del dy
+    out["gamma"] = gamma.to(w.io_dtype)
+    mean, rstd = saved_stats(out["x"], w.kind, w.eps)
+    out["rstd"] = rstd
+    if w.kind == LAYERNORM:
+        out["mean"] = mean
+    return out
+
+
+def saved_stats(x: torch.Tensor, kind: str, eps: float, chunk_rows: int = 4096):
+    """fp32 mean/rstd a forward pass would save, evaluated in fp64.
+
+    LayerNorm: mean = Σx/N, var = Σ(x−mean)²/N, rstd = 1/sqrt(var+eps).
+    RMSNorm:   rstd = 1/sqrt(Σx²/N + eps); mean is None.
+    """
+    M = x.shape[0]
+    rstd = torch.empty(M, dtype=torch.float32)
+    mean = torch.empty(M, dtype=torch.float32) if kind == LAYERNORM else None
+    for r0 in range(0, M, chunk_rows):
+        xd = x[r0:r0 + chunk_rows].double()
+        if kind == LAYERNORM:
+            mu = xd.mean(dim=1)
+            var = (xd - mu[:, None]).square_().mean(dim=1)
+            mean[r0:r0 + chunk_rows] = mu.float()
+            rstd[r0:r0 + chunk_rows] = (1.0 / torch.sqrt(var + eps)).float()
+        elif kind == RMSNORM:
+            ms = xd.square_().mean(dim=1)
+            rstd[r0:r0 + chunk_rows] = (1.0 / torch.sqrt(ms + eps)).float()
+        else:
+            raise ValueError(kind)
+    return mean, rstd
+
+
+def sample_rows(M: int, k: int, seed: int = 7, extra: Sequence[int] = ()) -> torch.Tensor:
+    """Row indices for sampled checks: first, last, a seeded random set, and
+    any extra rows (e.g. row-group boundaries), de-duplicated and sorted."""
+    if M == 0:
+        return torch.empty(0, dtype=torch.long)
+    g = torch.Generator().manual_seed(seed)
+    picks = set([0, M - 1]) | set(int(r) for r in extra if 0 <= r < M)
+    picks |= set(torch.randint(0, M, (k,), generator=g).tolist())
+    return torch.tensor(sorted(picks), dtype=torch.long)
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+__all__ = [
+    "Workload", "WORKLOADS", "HEADLINE", "LAYERNORM", "RMSNORM", "make_inputs",
+    "saved_stats", "scaled", "sample_rows", "ceil_div",
+]
