@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark the LayerNorm / RMSNorm backward pass on one MI355X.
+
+One step = one full backward pass (kernel A: dx + per-group partial
+dgamma/dbeta; kernel B: fixed-order reduction of the partials) over one batch
+of synthetic, seeded inputs already resident in HBM. The headline workload is
+the 16384 x 4096 bf16 RMSNorm backward (fp32 rstd and dgamma).
+
+Timing: HIP events recorded on the stream the library launches on (torch's
+current stream), around exactly --steps calls after --warmup untimed calls.
+Input/output buffer sets are rotated so that consecutive steps touch
+different memory (the set count makes the rotation exceed the 256 MB
+Infinity Cache several times over): every step streams from HBM.
+
+Prints ONE JSON line. `value` is algorithmic GB/s of the whole step:
+  bytes = read x, dy, gamma, saved stats; write dx, dgamma(, dbeta)
+(workspace traffic excluded). `roofline` is kernel A alone against the
+8 TB/s HBM peak; `cpu_baseline` is the fp64 CPU oracle timed on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "norm-backward achieved HBM GB/s and % of peak (16384×4096 bf16 RMSNorm)"
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E, published
+MALL_BYTES = 256 << 20        # Infinity Cache
+KERNEL_SOURCE = os.path.join(ROOT, "rmsnorm_backward_amd", "csrc", "nb_device.hpp")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0 = auto)")
+    ap.add_argument("--groups", type=int, default=0, help="explicit row-group count (0 = auto)")
+    return ap.parse_args(argv)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per kernel-A launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"pmc_dx_partials_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not m or not t or m.group(1) != kernel_source_hash():
+        return None
+    return int(t.group(1))
+
+
+def kernel_a_bytes(w) -> int:
+    """Algorithmic bytes of one kernel-A launch: x, dy read and dx written
+    (3*N*s per row), the saved statistics (4 or 8 B per row), gamma once."""
+    s = w.io_bytes
+    stats = 8 if w.kind == "layernorm" else 4
+    return w.M * (3 * w.N * s + stats) + w.N * s
+
+
+def time_loop(torch, fn, steps, stream):
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        fn(i)
+    end.record(stream)
+    end.synchronize()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per call
+
+
+def cpu_baseline(w, inp):
+    """The fp64 oracle (plain C, one thread) on the same workload, timed on
+    this host. Inputs are widened to fp64 before the clock starts."""
+    import numpy as np
+
+    import oracle
+    o = oracle.default()
+    max_rows = max(1, (1 << 27) // max(w.N, 1))      # bound the sample (~1-20 s)
+    rows = min(w.M, max_rows)
+    x = inp["x"][:rows].double().numpy()
+    dy = inp["dy"][:rows].double().numpy()
+    gamma = inp["gamma"].double().numpy()
+    rstd = inp["rstd"][:rows].double().numpy()
+    mean = inp["mean"][:rows].double().numpy() if w.kind == "layernorm" else None
+    t0 = time.perf_counter()
+    o.bwd(w.kind, x, dy, gamma, mean, rstd, want_dbeta=w.kind == "layernorm")
+    dt = time.perf_counter() - t0
+    import dataclasses
+    ws = dataclasses.replace(w, M=rows)
+    sample = (f"full {w.M}x{w.N} workload" if rows == w.M else
+              f"first {rows} of {w.M} rows x {w.N}") + ", one fp64 pass (dx, dgamma" + \
+             (", dbeta)" if w.kind == "layernorm" else ")")
+    return {"value": round(ws.algorithmic_bytes() / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "sample": sample, "seconds": round(dt, 3)}
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one GPU; "
+              "the multi-GPU sharding is a design note only. Use --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import rmsnorm_backward_amd as nb
+    from rmsnorm_backward_amd import workloads as W
+
+    if not os.path.exists(nb.LIB_PATH):
+        from rmsnorm_backward_amd import _build
+        _build.build()
+    lib = nb.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    w = W.WORKLOADS[args.workload] if args.workload else W.HEADLINE
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    inp = W.make_inputs(w)
+    with_db = w.kind == "layernorm"
+    io = nb._DTYPE_CODE[w.io_dtype]
+    wg = nb._DTYPE_CODE[w.wgrad_dtype]
+    plan = nb.norm_bwd_make_plan(w.kind, w.M, w.N, w.io_dtype, with_db, args.groups)
+    set_bytes = 3 * w.M * w.N * w.io_bytes
+    nsets = args.sets or max(2, math.ceil(4 * MALL_BYTES / max(set_bytes, 1)))
+    nsets = min(nsets, 64)
+    base = {k: inp[k].to(dev) for k in ("x", "dy", "gamma", "rstd", "mean") if k in inp}
+    sets = []
+    for i in range(nsets):
+        s = {k: (v if i == 0 else v.clone()) for k, v in base.items()}
+        s["dx"] = torch.empty_like(base["x"])
+        sets.append(s)
+    dgamma = torch.empty(w.N, dtype=w.wgrad_dtype, device=dev)
+    dbeta = torch.empty(w.N, dtype=w.wgrad_dtype, device=dev) if with_db else None
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+    P = ctypes.c_void_p
+    ptr = lambda t: None if t is None else P(t.data_ptr())  # noqa: E731
+
+    full_args, part_args = [], []
+    for s in sets:
+        if w.kind == "layernorm":
+            full_args.append((ptr(s["x"]), ptr(s["dy"]), ptr(s["gamma"]), ptr(s["mean"]),
+                              ptr(s["rstd"]), w.M, w.N, io, wg, w.eps, ptr(s["dx"]), ptr(dgamma),
+                              ptr(dbeta), ptr(ws), ws.numel(), sh))
+        else:
+            full_args.append((ptr(s["x"]), ptr(s["dy"]), ptr(s["gamma"]), ptr(s["rstd"]), w.M,
+                              w.N, io, wg, w.eps, ptr(s["dx"]), ptr(dgamma), ptr(dbeta), ptr(ws),
+                              ws.numel(), sh))
+        part_args.append((ctypes.byref(plan), ptr(s["x"]), ptr(s["dy"]), ptr(s["gamma"]),
+                          ptr(s.get("mean")), ptr(s["rstd"]), ptr(s["dx"]), ptr(ws), ws.numel(),
+                          sh))
+    fn = lib.norm_bwd_layernorm if w.kind == "layernorm" else lib.norm_bwd_rmsnorm
+    if args.groups:
+        fn = None
+
+    def step(i):
+        if fn is None:
+            a = part_args[i % nsets]
+            st = lib.norm_bwd_execute(a[0], a[1], a[2], a[3], a[4], a[5], wg, a[6], ptr(dgamma),
+                                      ptr(dbeta), a[7], a[8], a[9])
+        else:
+            st = fn(*full_args[i % nsets])
+        if st:
+            raise RuntimeError(nb.norm_bwd_last_error())
+
+    def step_a(i):
+        st = lib.norm_bwd_execute_partials(*part_args[i % nsets])
+        if st:
+            raise RuntimeError(nb.norm_bwd_last_error())
+
+    def step_b(i):
+        st = lib.norm_bwd_reduce_partials(plan.groups, w.N, wg, ptr(ws), ws.numel(), ptr(dgamma),
+                                          ptr(dbeta), sh)
+        if st:
+            raise RuntimeError(nb.norm_bwd_last_error())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms = time_loop(torch, step, args.steps, stream)
+    ms_a = time_loop(torch, step_a, args.steps, stream)
+    ms_b = time_loop(torch, step_b, max(args.steps, 50), stream)
+
+    # copy probe: the achievable streaming ceiling next to the kernels
+    cp_bytes = min(512 << 20, max(set_bytes // 3 * 2, 64 << 20)) // 16 * 16
+    src = torch.empty(cp_bytes // 4, dtype=torch.int32, device=dev).fill_(1)
+    dsts = [torch.empty_like(src) for _ in range(2)]
+    srcs = [src, src.clone()]
+    for i in range(3):
+        nb.norm_bwd_probe_copy(srcs[i % 2], dsts[i % 2])
+    ms_cp = time_loop(torch, lambda i: nb.norm_bwd_probe_copy(srcs[i % 2], dsts[i % 2]),
+                      20, stream)
+    copy_gbps = 2 * cp_bytes / (ms_cp * 1e-3) / 1e9
+    del src, dsts, srcs
+
+    alg = w.algorithmic_bytes()
+    value = alg / (ms * 1e-3) / 1e9
+    a_bytes = kernel_a_bytes(w)
+    achieved = a_bytes / (ms_a * 1e-3) / 1e9
+    traffic = committed_traffic(w.name)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "kind": w.kind, "M": w.M, "N": w.N,
+            "io_dtype": W._dt(w.io_dtype), "wgrad_dtype": W._dt(w.wgrad_dtype),
+            "stats_dtype": "f32", "eps": w.eps, "seed": w.seed,
+            "algorithmic_bytes": alg, "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+            "rows_per_s": round(w.M / (ms * 1e-3), 1),
+            "kernel_a_us": round(ms_a * 1e3, 3), "kernel_b_us": round(ms_b * 1e3, 3),
+            "copy_probe_GBps": round(copy_gbps, 1),
+            "pct_of_copy_probe": round(100 * value / copy_gbps, 2),
+            "buffer_sets": nsets,
+            "workspace_bytes": plan.workspace_bytes,
+            "counted_GBps_incl_workspace": round(
+                (alg + 2 * plan.workspace_bytes) / (ms * 1e-3) / 1e9, 2),
+            "plan": {k: v for k, v in plan.as_dict().items()
+                     if k in ("groups", "rows_per_group", "vec", "chunks", "waves_per_row",
+                              "rows_in_flight", "threads", "grid")},
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+            "kernel": "dx_partials_kernel", "bytes_per_launch": a_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

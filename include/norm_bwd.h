@@ -1,0 +1,217 @@
+/*
+ * norm_bwd.h -- C ABI of the LayerNorm / RMSNorm backward library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What is computed. "Norm backward in Triton -- the dγ/dβ reduction",
+ * section "The gradients (the half-page you reverse)": for every row r of
+ * x[M, N] with the forward's saved per-row statistics mean[r] and
+ * rstd[r] = 1/sigma_r,
+ *
+ *     xhat  = (x - mean) * rstd          (RMSNorm: xhat = x * rstd)
+ *     dyhat = dy * gamma
+ *     dx    = rstd * (dyhat - mean_j(dyhat) - xhat * mean_j(dyhat * xhat))
+ *             (RMSNorm has no mean_j(dyhat) term)
+ *     dgamma[j] = sum over all rows of dy * xhat
+ *     dbeta[j]  = sum over all rows of dy
+ *
+ * How. The per-feature sums run over the token axis, the same axis dx is
+ * parallel over ("Norm & activation backward", section "Half two: dγ and dβ
+ * reduce across the whole batch", its strategy table). This library takes the
+ * deterministic two-pass route from that table: kernel A computes dx and, for
+ * each disjoint contiguous block ("group") of rows, the block's partial
+ * dgamma/dbeta in registers, stored once into a caller-provided fp32
+ * workspace[groups, N]; kernel B sums the groups in one fixed order. There are
+ * no atomics, so dx, dgamma and dbeta are bitwise identical across calls with
+ * equal arguments (same kind, M, N, dtypes, groups, and pointer alignment
+ * class) on the same device type. The group count never depends on the GPU's
+ * compute-unit count.
+ *
+ * Memory. Every pointer is a device pointer owned by the caller. The library
+ * allocates nothing. Tensors are dense row-major: x, dy, dx are [M, N] with
+ * row stride N elements; gamma, dgamma, dbeta are [N]; mean, rstd are fp32 [M].
+ * Outputs must not overlap any input, each other, or the workspace.
+ *
+ * Streams and errors. All calls that launch work are asynchronous on
+ * `stream` (a hipStream_t passed as void*, NULL = the default stream); results
+ * are valid once the caller synchronises that stream. Arguments are checked
+ * on the host before anything is launched: on a non-zero status nothing was
+ * enqueued, except NORM_BWD_ERR_HIP, which reports a failed launch.
+ * norm_bwd_last_error() gives a message for the calling thread's last failure.
+ * Nothing prints or aborts.
+ */
+#ifndef NORM_BWD_H
+#define NORM_BWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define NORM_BWD_OK 0
+#define NORM_BWD_ERR_INVALID_ARG 1   /* NULL pointer, negative size, bad eps, overlap, misaligned plan */
+#define NORM_BWD_ERR_UNSUPPORTED 2   /* dtype code, dtype pair, or N beyond the fused path's limit */
+#define NORM_BWD_ERR_WORKSPACE 3     /* workspace NULL or smaller than required */
+#define NORM_BWD_ERR_HIP 4           /* a HIP launch failed (hipGetLastError) */
+
+/* Element types (x, dy, gamma, dx use io_dtype; dgamma, dbeta use wgrad_dtype). */
+#define NORM_BWD_F32 0
+#define NORM_BWD_F16 1   /* IEEE binary16 */
+#define NORM_BWD_BF16 2  /* bfloat16 */
+
+/* Normalisation kinds. */
+#define NORM_BWD_LAYERNORM 0
+#define NORM_BWD_RMSNORM 1
+
+/*
+ * Largest N the fused path takes. "Aligned" means N is a multiple of
+ * 16 / element size and x, dy, gamma, dx start on 16-byte boundaries; other
+ * rows use one element per lane. Larger N returns NORM_BWD_ERR_UNSUPPORTED.
+ */
+#define NORM_BWD_MAX_N_16BIT 32768          /* fp16/bf16, aligned, dbeta NULL */
+#define NORM_BWD_MAX_N_16BIT_DBETA 16384    /* fp16/bf16, aligned, dbeta requested */
+#define NORM_BWD_MAX_N_F32 16384            /* fp32, aligned */
+#define NORM_BWD_MAX_N_UNALIGNED 8192
+
+/*
+ * LayerNorm backward ("Norm backward in Triton -- the dγ/dβ reduction",
+ * "The gradients"; the same dx and dgamma/dbeta are the Phobos tutorial
+ * "05: Layer norm" kernels ln_bwd_dx and ln_bwd_dwdb).
+ *
+ *   x, dy, gamma   [M,N], [M,N], [N] in io_dtype (read)
+ *   mean, rstd     fp32 [M], the forward's saved statistics (read)
+ *   M, N           rows and features, >= 0. M = 0 writes zeros to dgamma and
+ *                  dbeta (the empty sum); N = 0 does nothing.
+ *   io_dtype       NORM_BWD_F32 / F16 / BF16
+ *   wgrad_dtype    NORM_BWD_F32 or io_dtype: dgamma/dbeta are accumulated in
+ *                  fp32 and rounded (to nearest even) once at the end
+ *   eps            the forward's epsilon; checked (finite, >= 0) but unused,
+ *                  because rstd already contains it
+ *   dx             [M,N] io_dtype (written, rounded to nearest even)
+ *   dgamma         [N] wgrad_dtype (written)
+ *   dbeta          [N] wgrad_dtype (written), or NULL to skip it
+ *   workspace      at least norm_bwd_workspace_bytes(NORM_BWD_LAYERNORM, M, N,
+ *                  io_dtype, dbeta != NULL) bytes of device memory, 16-byte
+ *                  aligned; its prior contents are never read
+ *   stream         hipStream_t or NULL
+ * Returns a status code.
+ */
+int norm_bwd_layernorm(const void *x, const void *dy, const void *gamma,
+                       const float *mean, const float *rstd, int64_t M,
+                       int64_t N, int io_dtype, int wgrad_dtype, float eps,
+                       void *dx, void *dgamma, void *dbeta, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/*
+ * RMSNorm backward ("Norm backward in Triton", "The gradients": no mean, so
+ * xhat = x * rstd and dx loses the mean_j(dyhat) term). Same arguments as
+ * norm_bwd_layernorm without `mean`. dbeta may be NULL (RMSNorm has no bias);
+ * when given it receives the column sum of dy, which does not depend on the
+ * normalisation.
+ */
+int norm_bwd_rmsnorm(const void *x, const void *dy, const void *gamma,
+                     const float *rstd, int64_t M, int64_t N, int io_dtype,
+                     int wgrad_dtype, float eps, void *dx, void *dgamma,
+                     void *dbeta, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/*
+ * Workspace size in bytes for the automatic plan of (kind, M, N, io_dtype):
+ * groups * N * 4 bytes per gradient vector (two when with_dbeta != 0).
+ * Returns 0 for M = 0 or N = 0, and (size_t)-1 for invalid arguments.
+ * Host-only; launches nothing.
+ */
+size_t norm_bwd_workspace_bytes(int kind, int64_t M, int64_t N, int io_dtype,
+                                int with_dbeta);
+
+/*
+ * An execution plan: the row grouping and the launch geometry of kernel A.
+ * Produced by norm_bwd_make_plan; a caller may change `groups` (then call
+ * norm_bwd_make_plan again with it) or the geometry fields for tuning, and
+ * norm_bwd_execute re-validates every field. Results depend on groups,
+ * rows_per_group, rows_in_flight (dgamma/dbeta order) and vec, chunks,
+ * waves_per_row (order of the in-row sums), never on the device.
+ */
+typedef struct norm_bwd_plan {
+    int32_t kind;            /* NORM_BWD_LAYERNORM / RMSNORM */
+    int32_t io_dtype;        /* element type of x, dy, gamma, dx */
+    int32_t with_dbeta;      /* 1: kernel A also sums dy for dbeta */
+    int32_t vec;             /* elements per lane per load (16 bytes, or 1) */
+    int64_t M, N;            /* problem size */
+    int64_t groups;          /* G: disjoint contiguous row blocks = workspace rows */
+    int64_t rows_per_group;  /* R: group g owns rows [g*R, min((g+1)*R, M)) */
+    int32_t chunks;          /* C: loads of `vec` elements per lane per row slice */
+    int32_t waves_per_row;   /* S: 64-lane waves sharing one row */
+    int32_t rows_in_flight;  /* P: rows a workgroup processes at once */
+    int32_t threads;         /* 64 * S * P, kernel A's workgroup size */
+    int32_t grid;            /* kernel A workgroups (groups are strided over them) */
+    int32_t lds_bytes;       /* kernel A dynamic LDS */
+    size_t workspace_bytes;  /* with_dbeta ? 2 : 1, times groups * N * 4 */
+} norm_bwd_plan_t;
+
+/*
+ * Fill *plan for (kind, M, N, io_dtype, with_dbeta). groups = 0 chooses the
+ * automatic group count (a function of kind, M, N, io_dtype only); groups > 0
+ * asks for that many row blocks (clamped to M; rows_per_group = ceil(M/groups)
+ * and groups = ceil(M/rows_per_group) so that no block is empty). The plan
+ * assumes 16-byte aligned base pointers; norm_bwd_execute rejects a plan
+ * whose vec the pointers do not allow. Host-only. Returns a status code.
+ */
+int norm_bwd_make_plan(int kind, int64_t M, int64_t N, int io_dtype,
+                       int with_dbeta, int64_t groups, norm_bwd_plan_t *plan);
+
+/*
+ * Run kernel A then kernel B of `plan` on `stream` (the whole backward pass).
+ * mean is ignored for RMSNorm. dbeta must be non-NULL exactly when
+ * plan->with_dbeta. Other arguments as for norm_bwd_layernorm.
+ */
+int norm_bwd_execute(const norm_bwd_plan_t *plan, const void *x,
+                     const void *dy, const void *gamma, const float *mean,
+                     const float *rstd, int wgrad_dtype, void *dx,
+                     void *dgamma, void *dbeta, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/*
+ * Kernel A alone: writes dx and the per-group partial sums into
+ * workspace[groups, N] (dgamma partials), followed by workspace[groups, N]
+ * (dbeta partials) when plan->with_dbeta. For callers that overlap the
+ * group reduction with other work, and for timing each kernel.
+ */
+int norm_bwd_execute_partials(const norm_bwd_plan_t *plan, const void *x,
+                              const void *dy, const void *gamma,
+                              const float *mean, const float *rstd, void *dx,
+                              void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/*
+ * Kernel B alone: dgamma[j] = sum over g of workspace[g, j] (and dbeta from
+ * the second plane when dbeta != NULL), summed in one fixed order that
+ * depends only on `groups`, rounded to wgrad_dtype. groups = 0 writes zeros.
+ * The workspace holds fp32 [with_dbeta ? 2 : 1][groups][N] as kernel A
+ * writes it.
+ */
+int norm_bwd_reduce_partials(int64_t groups, int64_t N, int wgrad_dtype,
+                             const void *workspace, size_t workspace_bytes,
+                             void *dgamma, void *dbeta, void *stream);
+
+/* Static text for a status code. */
+const char *norm_bwd_status_string(int status);
+
+/* Message describing the calling thread's most recent failure ("" if none). */
+const char *norm_bwd_last_error(void);
+
+/*
+ * Measurement aid, not part of the backward pass: copy `bytes` (a multiple
+ * of 16, 16-byte aligned pointers) from src to dst with a plain streaming
+ * kernel on `stream`. Used to calibrate hardware byte counters and to measure
+ * the achievable HBM copy bandwidth next to the norm kernels.
+ */
+int norm_bwd_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NORM_BWD_H */

@@ -1,0 +1,316 @@
+"""LayerNorm / RMSNorm backward for AMD MI355X (gfx950): Python binding.
+
+Thin ctypes marshalling over the C ABI in ``include/norm_bwd.h`` (library
+``rmsnorm_backward_amd/_lib/libnorm_bwd.so``). Every step of the backward pass
+runs in the library's HIP kernels on the tensors' GPU; this module only checks
+tensor metadata, allocates outputs and the workspace with ``torch.empty``
+(PyTorch supplies device memory and the current stream), and forwards raw
+pointers. There is no CPU fallback: without the built library, or with tensors
+that are not on a GPU, the calls raise.
+
+The functions carry the C names:
+
+* ``norm_bwd_layernorm(x, dy, gamma, mean, rstd, eps)`` -> (dx, dgamma, dbeta)
+* ``norm_bwd_rmsnorm(x, dy, gamma, rstd, eps)`` -> (dx, dgamma, dbeta or None)
+* ``norm_bwd_workspace_bytes``, ``norm_bwd_make_plan``, ``norm_bwd_execute``,
+  ``norm_bwd_execute_partials``, ``norm_bwd_reduce_partials``,
+  ``norm_bwd_probe_copy``, ``norm_bwd_status_string``, ``norm_bwd_last_error``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libnorm_bwd.so")
+
+# Codes from include/norm_bwd.h
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+F32, F16, BF16 = 0, 1, 2
+LAYERNORM, RMSNORM = 0, 1
+_DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+_KIND_CODE = {"layernorm": LAYERNORM, "rmsnorm": RMSNORM, LAYERNORM: LAYERNORM, RMSNORM: RMSNORM}
+
+
+class NormBwdError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class NormBwdPlan(ctypes.Structure):
+    """Mirror of norm_bwd_plan_t."""
+    _fields_ = [
+        ("kind", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+        ("with_dbeta", ctypes.c_int32), ("vec", ctypes.c_int32),
+        ("M", ctypes.c_int64), ("N", ctypes.c_int64),
+        ("groups", ctypes.c_int64), ("rows_per_group", ctypes.c_int64),
+        ("chunks", ctypes.c_int32), ("waves_per_row", ctypes.c_int32),
+        ("rows_in_flight", ctypes.c_int32), ("threads", ctypes.c_int32),
+        ("grid", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+    def copy(self) -> "NormBwdPlan":
+        c = NormBwdPlan()
+        ctypes.memmove(ctypes.byref(c), ctypes.byref(self), ctypes.sizeof(self))
+        return c
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it first (python -m rmsnorm_backward_amd._build "
+                "or __graft_entry__.build()). There is no CPU fallback.")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz, fp = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                ctypes.c_size_t, ctypes.c_float)
+        P = ctypes.POINTER(NormBwdPlan)
+        sigs = {
+            "norm_bwd_layernorm": [vp, vp, vp, vp, vp, i64, i64, i32, i32, fp, vp, vp, vp, vp, sz, vp],
+            "norm_bwd_rmsnorm": [vp, vp, vp, vp, i64, i64, i32, i32, fp, vp, vp, vp, vp, sz, vp],
+            "norm_bwd_workspace_bytes": [i32, i64, i64, i32, i32],
+            "norm_bwd_make_plan": [i32, i64, i64, i32, i32, i64, P],
+            "norm_bwd_execute": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp],
+            "norm_bwd_execute_partials": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "norm_bwd_reduce_partials": [i64, i64, i32, vp, sz, vp, vp, vp],
+            "norm_bwd_status_string": [i32],
+            "norm_bwd_last_error": [],
+            "norm_bwd_probe_copy": [vp, vp, sz, vp],
+        }
+        for name, args in sigs.items():
+            f = getattr(lib, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        lib.norm_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.norm_bwd_status_string.restype = ctypes.c_char_p
+        lib.norm_bwd_last_error.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def norm_bwd_status_string(status: int) -> str:
+    return load_library().norm_bwd_status_string(status).decode()
+
+
+def norm_bwd_last_error() -> str:
+    return load_library().norm_bwd_last_error().decode()
+
+
+def _check(status: int):
+    if status != OK:
+        raise NormBwdError(status, norm_bwd_last_error() or norm_bwd_status_string(status))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _gpu(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device}); there is no CPU path")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _rows(x: torch.Tensor):
+    if x.dim() < 1:
+        raise ValueError("x must have at least one dimension (features last)")
+    N = x.shape[-1]
+    M = 1
+    for d in x.shape[:-1]:
+        M *= d
+    return M, N
+
+
+def _code(dtype: torch.dtype, what: str) -> int:
+    try:
+        return _DTYPE_CODE[dtype]
+    except KeyError:
+        raise ValueError(f"{what} dtype {dtype} not supported (float32, float16, bfloat16)")
+
+
+def norm_bwd_workspace_bytes(kind, M: int, N: int, io_dtype, with_dbeta: bool) -> int:
+    code = io_dtype if isinstance(io_dtype, int) else _code(io_dtype, "io")
+    n = load_library().norm_bwd_workspace_bytes(_KIND_CODE[kind], M, N, code, int(bool(with_dbeta)))
+    if n == ctypes.c_size_t(-1).value:
+        raise NormBwdError(ERR_INVALID_ARG, "invalid arguments for norm_bwd_workspace_bytes")
+    return n
+
+
+def norm_bwd_make_plan(kind, M: int, N: int, io_dtype, with_dbeta: bool,
+                       groups: int = 0) -> NormBwdPlan:
+    code = io_dtype if isinstance(io_dtype, int) else _code(io_dtype, "io")
+    plan = NormBwdPlan()
+    _check(load_library().norm_bwd_make_plan(_KIND_CODE[kind], M, N, code,
+                                              int(bool(with_dbeta)), groups, ctypes.byref(plan)))
+    return plan
+
+
+def _backward(kind, x, dy, gamma, mean, rstd, eps, wgrad_dtype, dx, dgamma, dbeta,
+              with_dbeta, workspace, stream, plan: Optional[NormBwdPlan]):
+    lib = load_library()
+    for t, n in ((x, "x"), (dy, "dy"), (gamma, "gamma"), (rstd, "rstd")):
+        _gpu(t, n)
+    if kind == LAYERNORM:
+        _gpu(mean, "mean")
+    M, N = _rows(x)
+    io = _code(x.dtype, "x")
+    if dy.dtype != x.dtype or gamma.dtype != x.dtype:
+        raise ValueError("x, dy and gamma must share one dtype")
+    if dy.shape != x.shape or gamma.numel() != N or rstd.numel() != M:
+        raise ValueError("shape mismatch: dy like x, gamma [N], rstd [M]")
+    if rstd.dtype != torch.float32 or (kind == LAYERNORM and
+                                       (mean.dtype != torch.float32 or mean.numel() != M)):
+        raise ValueError("mean and rstd must be float32 [M]")
+    wgrad_dtype = wgrad_dtype or torch.float32
+    wcode = _code(wgrad_dtype, "wgrad")
+    dev = x.device
+    if dx is None:
+        dx = torch.empty_like(x)
+    if dgamma is None:
+        dgamma = torch.empty(N, dtype=wgrad_dtype, device=dev)
+    if with_dbeta and dbeta is None:
+        dbeta = torch.empty(N, dtype=wgrad_dtype, device=dev)
+    for t, n in ((dx, "dx"), (dgamma, "dgamma")) + (((dbeta, "dbeta"),) if dbeta is not None else ()):
+        _gpu(t, n)
+    s = _stream(stream, dev)
+    with torch.cuda.device(dev):
+        if plan is None:
+            need = norm_bwd_workspace_bytes(kind, M, N, io, dbeta is not None)
+            if workspace is None:
+                workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+            wsb = workspace.numel() * workspace.element_size()
+            if kind == LAYERNORM:
+                st = lib.norm_bwd_layernorm(_ptr(x), _ptr(dy), _ptr(gamma), _ptr(mean), _ptr(rstd),
+                                            M, N, io, wcode, float(eps), _ptr(dx), _ptr(dgamma),
+                                            _ptr(dbeta), _ptr(workspace), wsb, s)
+            else:
+                st = lib.norm_bwd_rmsnorm(_ptr(x), _ptr(dy), _ptr(gamma), _ptr(rstd), M, N, io,
+                                          wcode, float(eps), _ptr(dx), _ptr(dgamma), _ptr(dbeta),
+                                          _ptr(workspace), wsb, s)
+        else:
+            if workspace is None:
+                workspace = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+            wsb = workspace.numel() * workspace.element_size()
+            st = lib.norm_bwd_execute(ctypes.byref(plan), _ptr(x), _ptr(dy), _ptr(gamma),
+                                      _ptr(mean) if kind == LAYERNORM else None, _ptr(rstd),
+                                      wcode, _ptr(dx), _ptr(dgamma), _ptr(dbeta),
+                                      _ptr(workspace), wsb, s)
+    _check(st)
+    return dx, dgamma, dbeta
+
+
+def norm_bwd_layernorm(x: torch.Tensor, dy: torch.Tensor, gamma: torch.Tensor,
+                       mean: torch.Tensor, rstd: torch.Tensor, eps: float = 1e-5, *,
+                       wgrad_dtype: Optional[torch.dtype] = None, dx=None, dgamma=None,
+                       dbeta=None, with_dbeta: bool = True, workspace=None, stream=None
+                       ) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    """LayerNorm backward on the GPU: returns (dx, dgamma, dbeta)."""
+    return _backward(LAYERNORM, x, dy, gamma, mean, rstd, eps, wgrad_dtype, dx, dgamma, dbeta,
+                     with_dbeta or dbeta is not None, workspace, stream, None)
+
+
+def norm_bwd_rmsnorm(x: torch.Tensor, dy: torch.Tensor, gamma: torch.Tensor,
+                     rstd: torch.Tensor, eps: float = 1e-6, *,
+                     wgrad_dtype: Optional[torch.dtype] = None, dx=None, dgamma=None,
+                     dbeta=None, with_dbeta: bool = False, workspace=None, stream=None
+                     ) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    """RMSNorm backward on the GPU: returns (dx, dgamma, dbeta or None)."""
+    return _backward(RMSNORM, x, dy, gamma, None, rstd, eps, wgrad_dtype, dx, dgamma, dbeta,
+                     with_dbeta or dbeta is not None, workspace, stream, None)
+
+
+def norm_bwd_execute(plan: NormBwdPlan, x, dy, gamma, mean, rstd, *, wgrad_dtype=None,
+                     dx=None, dgamma=None, dbeta=None, workspace=None, stream=None):
+    """Run an explicit plan (kernel A then kernel B)."""
+    kind = plan.kind
+    return _backward(kind, x, dy, gamma, mean, rstd, 0.0, wgrad_dtype, dx, dgamma, dbeta,
+                     bool(plan.with_dbeta), workspace, stream, plan)
+
+
+def norm_bwd_execute_partials(plan: NormBwdPlan, x, dy, gamma, mean, rstd, dx, workspace,
+                              stream=None):
+    """Kernel A alone (dx and the per-group partials in `workspace`)."""
+    lib = load_library()
+    for t, n in ((x, "x"), (dy, "dy"), (gamma, "gamma"), (rstd, "rstd"), (dx, "dx"),
+                 (workspace, "workspace")):
+        _gpu(t, n)
+    if plan.kind == LAYERNORM:
+        _gpu(mean, "mean")
+    s = _stream(stream, x.device)
+    with torch.cuda.device(x.device):
+        st = lib.norm_bwd_execute_partials(
+            ctypes.byref(plan), _ptr(x), _ptr(dy), _ptr(gamma),
+            _ptr(mean) if plan.kind == LAYERNORM else None, _ptr(rstd), _ptr(dx),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), s)
+    _check(st)
+
+
+def norm_bwd_reduce_partials(groups: int, N: int, workspace: torch.Tensor,
+                             dgamma: torch.Tensor, dbeta: Optional[torch.Tensor] = None,
+                             stream=None):
+    """Kernel B alone: fixed-order sum of the per-group partials."""
+    lib = load_library()
+    _gpu(workspace, "workspace")
+    _gpu(dgamma, "dgamma")
+    if dbeta is not None:
+        _gpu(dbeta, "dbeta")
+        if dbeta.dtype != dgamma.dtype:
+            raise ValueError("dgamma and dbeta must share a dtype")
+    s = _stream(stream, dgamma.device)
+    with torch.cuda.device(dgamma.device):
+        st = lib.norm_bwd_reduce_partials(groups, N, _code(dgamma.dtype, "dgamma"), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(),
+                                          _ptr(dgamma), _ptr(dbeta), s)
+    _check(st)
+
+
+def norm_bwd_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
+    """Plain streaming copy kernel (bandwidth and counter calibration)."""
+    lib = load_library()
+    _gpu(src, "src")
+    _gpu(dst, "dst")
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst smaller than src")
+    s = _stream(stream, src.device)
+    with torch.cuda.device(src.device):
+        _check(lib.norm_bwd_probe_copy(_ptr(src), _ptr(dst), n, s))
+
+
+__all__ = [
+    "norm_bwd_layernorm", "norm_bwd_rmsnorm", "norm_bwd_workspace_bytes", "norm_bwd_make_plan",
+    "norm_bwd_execute", "norm_bwd_execute_partials", "norm_bwd_reduce_partials",
+    "norm_bwd_probe_copy", "norm_bwd_status_string", "norm_bwd_last_error", "NormBwdPlan",
+    "NormBwdError", "load_library", "library_path",
+]

@@ -1,0 +1,281 @@
+// api.cpp -- the C ABI (include/norm_bwd.h): argument checks, planning, and
+// the two launches on the caller's stream. Nothing here allocates memory.
+#include <hip/hip_runtime_api.h>
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "nb_launch.hpp"
+#include "norm_bwd.h"
+#include "plan.hpp"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int set_error(int status, const char* what) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s", norm_bwd_status_string(status),
+           what ? what : "");
+  return status;
+}
+
+int hip_error(hipError_t e, const char* where) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s: %s",
+           norm_bwd_status_string(NORM_BWD_ERR_HIP), where, hipGetErrorString(e));
+  return NORM_BWD_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Buffers {
+  const void* x;
+  const void* dy;
+  const void* gamma;
+  const float* mean;
+  const float* rstd;
+  void* dx;
+  void* dgamma;
+  void* dbeta;
+  void* ws;
+  size_t ws_bytes;
+};
+
+// Checks shared by every entry point that runs kernel A and/or kernel B.
+int check_buffers(int kind, int64_t M, int64_t N, int io_dtype, int wgrad_dtype, bool run_a,
+                  bool run_b, size_t ws_needed, const Buffers& b) {
+  const int eb = nb::dtype_bytes(io_dtype);
+  const int wb = nb::dtype_bytes(wgrad_dtype);
+  if (run_b) {
+    if (wb == 0) return set_error(NORM_BWD_ERR_UNSUPPORTED, "unknown wgrad_dtype");
+    if (wgrad_dtype != NORM_BWD_F32 && wgrad_dtype != io_dtype)
+      return set_error(NORM_BWD_ERR_UNSUPPORTED, "wgrad_dtype must be NORM_BWD_F32 or io_dtype");
+  }
+  if (M < 0 || N < 0) return set_error(NORM_BWD_ERR_INVALID_ARG, "M and N must be >= 0");
+  if (N > 0 && M > (int64_t)(((uint64_t)1 << 62) / (uint64_t)N / 4u))
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "M * N too large");
+  if (N == 0) return NORM_BWD_OK;
+  const bool rows = run_a && M > 0;
+  if (rows) {
+    if (!b.x || !b.dy || !b.gamma || !b.rstd || !b.dx)
+      return set_error(NORM_BWD_ERR_INVALID_ARG, "x, dy, gamma, rstd and dx must be non-NULL");
+    if (kind == NORM_BWD_LAYERNORM && !b.mean)
+      return set_error(NORM_BWD_ERR_INVALID_ARG, "LayerNorm needs mean");
+  }
+  if (run_b && !b.dgamma) return set_error(NORM_BWD_ERR_INVALID_ARG, "dgamma must be non-NULL");
+  if (ws_needed > 0) {
+    if (!b.ws) return set_error(NORM_BWD_ERR_WORKSPACE, "workspace is NULL");
+    if (b.ws_bytes < ws_needed) return set_error(NORM_BWD_ERR_WORKSPACE, "workspace too small");
+    if (!aligned16(b.ws)) return set_error(NORM_BWD_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  // No output may overlap an input, another output or the workspace.
+  const size_t mat = (size_t)M * (size_t)N * (size_t)eb;
+  const size_t vec_in = (size_t)N * (size_t)eb;
+  const size_t vec_out = (size_t)N * (size_t)(wb ? wb : 4);
+  const size_t stat = (size_t)M * 4u;
+  struct R { const void* p; size_t n; };
+  const R inputs[] = {{rows ? b.x : nullptr, mat},
+                      {rows ? b.dy : nullptr, mat},
+                      {rows ? b.gamma : nullptr, vec_in},
+                      {rows && kind == NORM_BWD_LAYERNORM ? b.mean : nullptr, stat},
+                      {rows ? b.rstd : nullptr, stat}};
+  const R outputs[] = {{rows ? b.dx : nullptr, mat},
+                       {run_b ? b.dgamma : nullptr, vec_out},
+                       {run_b ? b.dbeta : nullptr, vec_out},
+                       {b.ws, ws_needed}};
+  const int nout = sizeof(outputs) / sizeof(outputs[0]);
+  for (int i = 0; i < nout; ++i) {
+    for (const R& in : inputs)
+      if (nb::ranges_overlap(outputs[i].p, outputs[i].n, in.p, in.n))
+        return set_error(NORM_BWD_ERR_INVALID_ARG, "an output overlaps an input");
+    for (int j = i + 1; j < nout; ++j)
+      if (nb::ranges_overlap(outputs[i].p, outputs[i].n, outputs[j].p, outputs[j].n))
+        return set_error(NORM_BWD_ERR_INVALID_ARG, "outputs/workspace overlap each other");
+  }
+  return NORM_BWD_OK;
+}
+
+int launch_partials(const norm_bwd_plan_t& p, const Buffers& b, hipStream_t stream) {
+  if (p.M == 0 || p.N == 0) return NORM_BWD_OK;
+  nb::LaunchA a;
+  a.kind = p.kind;
+  a.nacc = p.with_dbeta ? 2 : 1;
+  a.vec_full = p.vec > 1 ? 1 : 0;
+  a.chunks = p.chunks;
+  a.x = b.x;
+  a.dy = b.dy;
+  a.gamma = b.gamma;
+  a.mean = b.mean;
+  a.rstd = b.rstd;
+  a.dx = b.dx;
+  a.ws = static_cast<float*>(b.ws);
+  a.M = p.M;
+  a.N = (int)p.N;
+  a.G = p.groups;
+  a.R = p.rows_per_group;
+  a.S = p.waves_per_row;
+  a.P = p.rows_in_flight;
+  a.threads = p.threads;
+  a.grid = p.grid;
+  a.lds = p.lds_bytes;
+  a.stream = stream;
+  (void)hipGetLastError();  // clear a stale error so a launch failure is ours
+  hipError_t e;
+  switch (p.io_dtype) {
+    case NORM_BWD_F32: e = nb::launch_a_f32(a); break;
+    case NORM_BWD_F16: e = nb::launch_a_f16(a); break;
+    default: e = nb::launch_a_bf16(a); break;
+  }
+  if (e != hipSuccess) return hip_error(e, "kernel A launch");
+  return NORM_BWD_OK;
+}
+
+int launch_reduce(int64_t groups, int64_t N, int wgrad_dtype, const void* ws, void* dgamma,
+                  void* dbeta, hipStream_t stream) {
+  if (N == 0) return NORM_BWD_OK;
+  (void)hipGetLastError();
+  hipError_t e = nb::launch_reduce(wgrad_dtype, static_cast<const float*>(ws), groups, (int)N,
+                                   dgamma, dbeta, stream);
+  if (e != hipSuccess) return hip_error(e, "kernel B launch");
+  return NORM_BWD_OK;
+}
+
+// Pointer alignment the plan's vector width needs (x, dy, gamma, dx).
+int check_vec_alignment(const norm_bwd_plan_t& p, const Buffers& b) {
+  if (p.vec > 1 && p.M > 0 && p.N > 0) {
+    if (!aligned16(b.x) || !aligned16(b.dy) || !aligned16(b.gamma) || !aligned16(b.dx))
+      return set_error(NORM_BWD_ERR_INVALID_ARG,
+                       "plan.vec > 1 needs 16-byte aligned x, dy, gamma and dx");
+  }
+  return NORM_BWD_OK;
+}
+
+int run_auto(int kind, const void* x, const void* dy, const void* gamma, const float* mean,
+             const float* rstd, int64_t M, int64_t N, int io_dtype, int wgrad_dtype, float eps,
+             void* dx, void* dgamma, void* dbeta, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  if (!(eps >= 0.0f) || isinf(eps))
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const bool vec_ok = aligned16(x) && aligned16(dy) && aligned16(gamma) && aligned16(dx);
+  norm_bwd_plan_t p;
+  const char* why = nullptr;
+  int st = nb::make_plan(kind, M, N, io_dtype, dbeta ? 1 : 0, 0, vec_ok, &p, &why);
+  if (st != NORM_BWD_OK) return set_error(st, why);
+  Buffers b{x, dy, gamma, mean, rstd, dx, dgamma, dbeta, workspace, workspace_bytes};
+  st = check_buffers(kind, M, N, io_dtype, wgrad_dtype, true, true, p.workspace_bytes, b);
+  if (st != NORM_BWD_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launch_partials(p, b, s);
+  if (st != NORM_BWD_OK) return st;
+  return launch_reduce(p.groups, N, wgrad_dtype, workspace, dgamma, dbeta, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int norm_bwd_layernorm(const void* x, const void* dy, const void* gamma, const float* mean,
+                       const float* rstd, int64_t M, int64_t N, int io_dtype, int wgrad_dtype,
+                       float eps, void* dx, void* dgamma, void* dbeta, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return run_auto(NORM_BWD_LAYERNORM, x, dy, gamma, mean, rstd, M, N, io_dtype, wgrad_dtype, eps,
+                  dx, dgamma, dbeta, workspace, workspace_bytes, stream);
+}
+
+int norm_bwd_rmsnorm(const void* x, const void* dy, const void* gamma, const float* rstd,
+                     int64_t M, int64_t N, int io_dtype, int wgrad_dtype, float eps, void* dx,
+                     void* dgamma, void* dbeta, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return run_auto(NORM_BWD_RMSNORM, x, dy, gamma, nullptr, rstd, M, N, io_dtype, wgrad_dtype,
+                  eps, dx, dgamma, dbeta, workspace, workspace_bytes, stream);
+}
+
+size_t norm_bwd_workspace_bytes(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta) {
+  norm_bwd_plan_t p;
+  if (nb::make_plan(kind, M, N, io_dtype, with_dbeta ? 1 : 0, 0, true, &p, nullptr) != NORM_BWD_OK)
+    return (size_t)-1;
+  return p.workspace_bytes;
+}
+
+int norm_bwd_make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,
+                       int64_t groups, norm_bwd_plan_t* plan) {
+  const char* why = nullptr;
+  int st = nb::make_plan(kind, M, N, io_dtype, with_dbeta, groups, true, plan, &why);
+  if (st != NORM_BWD_OK) return set_error(st, why);
+  return NORM_BWD_OK;
+}
+
+int norm_bwd_execute(const norm_bwd_plan_t* plan, const void* x, const void* dy,
+                     const void* gamma, const float* mean, const float* rstd, int wgrad_dtype,
+                     void* dx, void* dgamma, void* dbeta, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  const char* why = nullptr;
+  int st = nb::validate_plan(plan, &why);
+  if (st != NORM_BWD_OK) return set_error(st, why);
+  if ((dbeta != nullptr) != (plan->with_dbeta != 0))
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "dbeta must be non-NULL exactly when plan.with_dbeta");
+  Buffers b{x, dy, gamma, mean, rstd, dx, dgamma, dbeta, workspace, workspace_bytes};
+  st = check_buffers(plan->kind, plan->M, plan->N, plan->io_dtype, wgrad_dtype, true, true,
+                     plan->workspace_bytes, b);
+  if (st != NORM_BWD_OK) return st;
+  st = check_vec_alignment(*plan, b);
+  if (st != NORM_BWD_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launch_partials(*plan, b, s);
+  if (st != NORM_BWD_OK) return st;
+  return launch_reduce(plan->groups, plan->N, wgrad_dtype, workspace, dgamma, dbeta, s);
+}
+
+int norm_bwd_execute_partials(const norm_bwd_plan_t* plan, const void* x, const void* dy,
+                              const void* gamma, const float* mean, const float* rstd, void* dx,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  const char* why = nullptr;
+  int st = nb::validate_plan(plan, &why);
+  if (st != NORM_BWD_OK) return set_error(st, why);
+  Buffers b{x, dy, gamma, mean, rstd, dx, nullptr, nullptr, workspace, workspace_bytes};
+  st = check_buffers(plan->kind, plan->M, plan->N, plan->io_dtype, NORM_BWD_F32, true, false,
+                     plan->workspace_bytes, b);
+  if (st != NORM_BWD_OK) return st;
+  st = check_vec_alignment(*plan, b);
+  if (st != NORM_BWD_OK) return st;
+  return launch_partials(*plan, b, static_cast<hipStream_t>(stream));
+}
+
+int norm_bwd_reduce_partials(int64_t groups, int64_t N, int wgrad_dtype, const void* workspace,
+                             size_t workspace_bytes, void* dgamma, void* dbeta, void* stream) {
+  if (groups < 0 || N < 0) return set_error(NORM_BWD_ERR_INVALID_ARG, "groups and N must be >= 0");
+  if (N > INT32_MAX) return set_error(NORM_BWD_ERR_UNSUPPORTED, "N too large");
+  const size_t need = (size_t)(dbeta ? 2 : 1) * (size_t)groups * (size_t)N * 4u;
+  Buffers b{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dgamma, dbeta,
+            const_cast<void*>(workspace), workspace_bytes};
+  int st = check_buffers(NORM_BWD_RMSNORM, 0, N, NORM_BWD_F32, wgrad_dtype, false, true, need, b);
+  if (st != NORM_BWD_OK) return st;
+  return launch_reduce(groups, N, wgrad_dtype, workspace, dgamma, dbeta,
+                       static_cast<hipStream_t>(stream));
+}
+
+const char* norm_bwd_status_string(int status) {
+  switch (status) {
+    case NORM_BWD_OK: return "NORM_BWD_OK";
+    case NORM_BWD_ERR_INVALID_ARG: return "NORM_BWD_ERR_INVALID_ARG";
+    case NORM_BWD_ERR_UNSUPPORTED: return "NORM_BWD_ERR_UNSUPPORTED";
+    case NORM_BWD_ERR_WORKSPACE: return "NORM_BWD_ERR_WORKSPACE";
+    case NORM_BWD_ERR_HIP: return "NORM_BWD_ERR_HIP";
+    default: return "NORM_BWD_ERR_UNKNOWN";
+  }
+}
+
+const char* norm_bwd_last_error(void) { return g_last_error; }
+
+int norm_bwd_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (bytes == 0) return NORM_BWD_OK;
+  if (!src || !dst || bytes % 16 != 0 || !aligned16(src) || !aligned16(dst))
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "copy probe needs 16-byte aligned, 16-byte multiple");
+  if (nb::ranges_overlap(src, bytes, dst, bytes))
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "copy probe buffers overlap");
+  (void)hipGetLastError();  // clear a stale error so a launch failure is ours
+  hipError_t e = nb::launch_copy(src, dst, bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_error(e, "copy probe launch");
+  return NORM_BWD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// nb_launch.hpp -- internal launch interface between the C ABI and the
+// per-dtype kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nb {
+
+struct LaunchA {
+  int kind;      // NORM_BWD_LAYERNORM / RMSNORM
+  int nacc;      // 1: dgamma partials, 2: dgamma and dbeta partials
+  int vec_full;  // 1: 16-byte vectors, 0: one element per lane
+  int chunks;
+  const void* x;
+  const void* dy;
+  const void* gamma;
+  const float* mean;
+  const float* rstd;
+  void* dx;
+  float* ws;
+  int64_t M;
+  int N;
+  int64_t G, R;
+  int S, P, threads, grid, lds;
+  hipStream_t stream;
+};
+
+hipError_t launch_a_f32(const LaunchA& a);
+hipError_t launch_a_f16(const LaunchA& a);
+hipError_t launch_a_bf16(const LaunchA& a);
+hipError_t launch_reduce(int wgrad_dtype, const float* ws, int64_t G, int N, void* dgamma,
+                         void* dbeta, hipStream_t stream);
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
+}  // namespace nb

@@ -1,0 +1,186 @@
+// plan.cpp -- host-side planning and validation (no HIP calls).
+//
+// The group count G is what fixes the summation order of dgamma/dbeta, so it
+// is a function of (kind, M, N, io_dtype) alone and never of the device's
+// compute-unit count: results are the same on any partitioning of the GPU.
+#include "plan.hpp"
+
+#include <string.h>
+
+namespace nb {
+
+namespace {
+constexpr int64_t kAutoGroupTarget = 512;  // row blocks per call (see auto_groups)
+constexpr int64_t kMaxGrid = 1 << 20;
+constexpr int kMaxLdsBytes = 65536 - 1024;  // dynamic LDS; the kernel adds 256 B static
+constexpr int kTargetThreads = 256;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+}  // namespace
+
+int dtype_bytes(int dtype) {
+  switch (dtype) {
+    case NORM_BWD_F32: return 4;
+    case NORM_BWD_F16: return 2;
+    case NORM_BWD_BF16: return 2;
+    default: return 0;
+  }
+}
+
+int max_lane_elems(int io_dtype, int vec_full, int with_dbeta) {
+  if (!vec_full) return 8;
+  if (dtype_bytes(io_dtype) == 4) return 16;
+  return with_dbeta ? 32 : 64;
+}
+
+bool kernel_a_exists(int io_dtype, int vec_full, int with_dbeta, int chunks) {
+  if (dtype_bytes(io_dtype) == 0) return false;
+  if (chunks != 1 && chunks != 2 && chunks != 4 && chunks != 8) return false;
+  const int vec = vec_full ? 16 / dtype_bytes(io_dtype) : 1;
+  return vec * chunks <= max_lane_elems(io_dtype, vec_full, with_dbeta);
+}
+
+int kernel_a_max_threads(int lane_elems) { return lane_elems > 16 ? 512 : 1024; }
+
+int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype) {
+  (void)kind; (void)N; (void)io_dtype;
+  if (M <= 0) return 0;
+  const int64_t target = M < kAutoGroupTarget ? M : kAutoGroupTarget;
+  const int64_t R = ceil_div(M, target);
+  return ceil_div(M, R);
+}
+
+static int fail(const char** why, const char* msg, int status) {
+  if (why) *why = msg;
+  return status;
+}
+
+int make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,
+              int64_t groups, bool vec_ok16, norm_bwd_plan_t* plan, const char** why) {
+  if (!plan) return fail(why, "plan is NULL", NORM_BWD_ERR_INVALID_ARG);
+  if (kind != NORM_BWD_LAYERNORM && kind != NORM_BWD_RMSNORM)
+    return fail(why, "kind must be NORM_BWD_LAYERNORM or NORM_BWD_RMSNORM", NORM_BWD_ERR_INVALID_ARG);
+  const int eb = dtype_bytes(io_dtype);
+  if (eb == 0) return fail(why, "unknown io_dtype", NORM_BWD_ERR_UNSUPPORTED);
+  if (M < 0 || N < 0) return fail(why, "M and N must be >= 0", NORM_BWD_ERR_INVALID_ARG);
+  if (groups < 0) return fail(why, "groups must be >= 0", NORM_BWD_ERR_INVALID_ARG);
+  if (with_dbeta != 0 && with_dbeta != 1)
+    return fail(why, "with_dbeta must be 0 or 1", NORM_BWD_ERR_INVALID_ARG);
+
+  norm_bwd_plan_t p;
+  memset(&p, 0, sizeof(p));
+  p.kind = kind;
+  p.io_dtype = io_dtype;
+  p.with_dbeta = with_dbeta;
+  p.M = M;
+  p.N = N;
+  const int nacc = with_dbeta ? 2 : 1;
+
+  const int vw = 16 / eb;
+  const int full = (vec_ok16 && N % vw == 0) ? 1 : 0;
+  p.vec = full ? vw : 1;
+
+  if (N == 0) {  // nothing to compute; keep a minimal valid geometry
+    p.chunks = 1;
+    p.waves_per_row = 1;
+    p.rows_in_flight = 1;
+    p.threads = 64;
+    *plan = p;
+    return NORM_BWD_OK;
+  }
+  const int64_t max_n = !full ? NORM_BWD_MAX_N_UNALIGNED
+                       : eb == 4 ? NORM_BWD_MAX_N_F32
+                       : with_dbeta ? NORM_BWD_MAX_N_16BIT_DBETA : NORM_BWD_MAX_N_16BIT;
+  if (N > max_n) return fail(why, "N exceeds the fused path's limit", NORM_BWD_ERR_UNSUPPORTED);
+
+  // Smallest S (waves sharing a row: fewer barriers), then smallest C.
+  int S = 0, C = 0;
+  for (int s = 1; s <= 16 && !S; s *= 2) {
+    for (int c = 1; c <= 8; c *= 2) {
+      if (!kernel_a_exists(io_dtype, full, with_dbeta, c)) continue;
+      if (s * 64 > kernel_a_max_threads(p.vec * c)) continue;
+      if ((int64_t)s * 64 * p.vec * c >= N) { S = s; C = c; break; }
+    }
+  }
+  if (!S) return fail(why, "no kernel geometry covers N", NORM_BWD_ERR_UNSUPPORTED);
+  int P = kTargetThreads / (64 * S);
+  if (P < 1) P = 1;
+  while (P > 1 && S * P * 64 > kernel_a_max_threads(p.vec * C)) P /= 2;
+  int lds = nacc * S * C * 64 * p.vec * 4;
+  if (P == 1 || lds > kMaxLdsBytes) { P = 1; lds = 0; }
+  p.chunks = C;
+  p.waves_per_row = S;
+  p.rows_in_flight = P;
+  p.threads = 64 * S * P;
+  p.lds_bytes = lds;
+
+  if (M > 0) {
+    int64_t target = groups ? groups : auto_groups(kind, M, N, io_dtype);
+    if (target > M) target = M;
+    p.rows_per_group = ceil_div(M, target);
+    p.groups = ceil_div(M, p.rows_per_group);
+    p.grid = (int32_t)(p.groups < kMaxGrid ? p.groups : kMaxGrid);
+  } else {
+    p.rows_per_group = 1;
+    p.groups = 0;
+    p.grid = 0;
+  }
+  p.workspace_bytes = (size_t)nacc * (size_t)p.groups * (size_t)N * 4u;
+  *plan = p;
+  return NORM_BWD_OK;
+}
+
+int validate_plan(const norm_bwd_plan_t* p, const char** why) {
+  if (!p) return fail(why, "plan is NULL", NORM_BWD_ERR_INVALID_ARG);
+  if (p->kind != NORM_BWD_LAYERNORM && p->kind != NORM_BWD_RMSNORM)
+    return fail(why, "plan.kind invalid", NORM_BWD_ERR_INVALID_ARG);
+  const int eb = dtype_bytes(p->io_dtype);
+  if (eb == 0) return fail(why, "plan.io_dtype unknown", NORM_BWD_ERR_UNSUPPORTED);
+  if (p->with_dbeta != 0 && p->with_dbeta != 1)
+    return fail(why, "plan.with_dbeta must be 0 or 1", NORM_BWD_ERR_INVALID_ARG);
+  if (p->M < 0 || p->N < 0) return fail(why, "plan.M/N negative", NORM_BWD_ERR_INVALID_ARG);
+  const int nacc = p->with_dbeta ? 2 : 1;
+  if (p->workspace_bytes != (size_t)nacc * (size_t)p->groups * (size_t)p->N * 4u)
+    return fail(why, "plan.workspace_bytes inconsistent with groups and N", NORM_BWD_ERR_INVALID_ARG);
+  if (p->N == 0) return NORM_BWD_OK;
+  const int vw = 16 / eb;
+  int full;
+  if (p->vec == vw && p->N % vw == 0) full = 1;
+  else if (p->vec == 1) full = 0;
+  else return fail(why, "plan.vec must be 16/elem_size (with N a multiple of it) or 1",
+                   NORM_BWD_ERR_INVALID_ARG);
+  if (!kernel_a_exists(p->io_dtype, full, p->with_dbeta, p->chunks))
+    return fail(why, "plan.chunks: no kernel for this vec*chunks", NORM_BWD_ERR_UNSUPPORTED);
+  const int S = p->waves_per_row, P = p->rows_in_flight;
+  if (S < 1 || P < 1 || S * P > 16)
+    return fail(why, "plan.waves_per_row * rows_in_flight must be in [1, 16]", NORM_BWD_ERR_INVALID_ARG);
+  if (p->threads != 64 * S * P)
+    return fail(why, "plan.threads must be 64 * waves_per_row * rows_in_flight", NORM_BWD_ERR_INVALID_ARG);
+  if (p->threads > kernel_a_max_threads(p->vec * p->chunks))
+    return fail(why, "plan.threads above the kernel's launch bound", NORM_BWD_ERR_INVALID_ARG);
+  if ((int64_t)S * 64 * p->vec * p->chunks < p->N)
+    return fail(why, "plan geometry does not cover N", NORM_BWD_ERR_INVALID_ARG);
+  const int want_lds = P > 1 ? nacc * S * p->chunks * 64 * p->vec * 4 : 0;
+  if (p->lds_bytes != want_lds || want_lds > kMaxLdsBytes)
+    return fail(why, "plan.lds_bytes inconsistent (or above 63 KiB)", NORM_BWD_ERR_INVALID_ARG);
+  if (p->M == 0) {
+    if (p->groups != 0) return fail(why, "plan.groups must be 0 when M = 0", NORM_BWD_ERR_INVALID_ARG);
+    return NORM_BWD_OK;
+  }
+  if (p->groups < 1 || p->rows_per_group < 1)
+    return fail(why, "plan.groups and rows_per_group must be >= 1", NORM_BWD_ERR_INVALID_ARG);
+  if (p->groups * p->rows_per_group < p->M || (p->groups - 1) * p->rows_per_group >= p->M)
+    return fail(why, "plan.groups * rows_per_group must cover M with no empty group",
+                NORM_BWD_ERR_INVALID_ARG);
+  if (p->grid < 1 || p->grid > p->groups || p->grid > kMaxGrid)
+    return fail(why, "plan.grid must be in [1, groups]", NORM_BWD_ERR_INVALID_ARG);
+  return NORM_BWD_OK;
+}
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+}  // namespace nb

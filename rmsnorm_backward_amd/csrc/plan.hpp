@@ -1,0 +1,38 @@
+// plan.hpp -- host-side planning and validation for the norm-backward
+// library. Pure C++ (no HIP headers), so it runs and is tested without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "norm_bwd.h"
+
+namespace nb {
+
+// Element size in bytes of a NORM_BWD_* dtype code, or 0 if unknown.
+int dtype_bytes(int dtype);
+
+// Largest elements-per-lane (vec * chunks) kernel A is instantiated for.
+int max_lane_elems(int io_dtype, int vec_full, int with_dbeta);
+
+// Whether kernel A is instantiated for these template parameters.
+bool kernel_a_exists(int io_dtype, int vec_full, int with_dbeta, int chunks);
+
+// Largest workgroup kernel A accepts for vec * chunks elements per lane.
+int kernel_a_max_threads(int lane_elems);
+
+// Automatic group count for (kind, M, N, io_dtype): independent of the device.
+int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype);
+
+// Fill *plan (see norm_bwd_make_plan). `vec_ok16` says whether the caller's
+// pointers are 16-byte aligned. Writes a message into *why on failure.
+int make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,
+              int64_t groups, bool vec_ok16, norm_bwd_plan_t* plan, const char** why);
+
+// Check every field of a (possibly caller-edited) plan. Returns a status.
+int validate_plan(const norm_bwd_plan_t* plan, const char** why);
+
+// Byte ranges [p, p+n) overlap?
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb);
+
+}  // namespace nb

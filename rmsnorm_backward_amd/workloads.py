@@ -17,14 +17,20 @@ section "The dx kernel — recompute the stat, don't store x̂"):
   "05: Layer norm" (the Phobos tutorial's ``ln_fwd``) does; RMSNorm uses the
   mean of squares, as in "Norm backward in Triton", section "The gradients".
 
-Everything is drawn on the CPU from a ``torch.Generator`` with a fixed seed,
-in the fixed order x, dy, gamma, beta, outlier columns, so every consumer sees
-the same bits.
+Everything is drawn on the CPU from seeded ``torch.Generator`` objects, so
+every consumer sees the same bits. The [M, N] draws (x, dy, an outlier mask)
+come in blocks of 4096 rows; block b of draw t uses its own generator seeded
+with ``block_seed(seed, t, b)``, so blocks can be filled in parallel and the
+result does not depend on the thread count. The small draws (per-row shift and
+scale, gamma, beta, outlier columns) come, in that order, from one generator
+seeded with the workload's seed.
 """
 
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Dict, Optional, Sequence
 
 import torch
@@ -123,23 +129,55 @@ def outlier_columns(w: Workload, gen: torch.Generator) -> torch.Tensor:
     return torch.randperm(w.N, generator=gen)[:k]
 
 
+BLOCK_ROWS = 4096
+_X, _DY, _MASK = 1, 2, 3   # draw tags
+
+
+def block_seed(seed: int, tag: int, block: int) -> int:
+    """Seed of one 4096-row block of one [M, N] draw."""
+    return (seed * 1_000_003 + tag * 65_537 + block * 8_191 + 12_345) % (1 << 62)
+
+
+def _blocked(seed: int, tag: int, M: int, N: int, kind: str) -> torch.Tensor:
+    """[M, N] fp32 draw (standard normal, or uniform [0,1)), block by block."""
+    out = torch.empty(M, N, dtype=torch.float32)
+    nblk = -(-M // BLOCK_ROWS)
+
+    def fill(b):
+        g = torch.Generator().manual_seed(block_seed(seed, tag, b))
+        r0, r1 = b * BLOCK_ROWS, min(M, (b + 1) * BLOCK_ROWS)
+        if kind == "normal":
+            torch.randn(r1 - r0, N, generator=g, out=out[r0:r1])
+        else:
+            torch.rand(r1 - r0, N, generator=g, out=out[r0:r1])
+
+    if nblk <= 1:
+        for b in range(nblk):
+            fill(b)
+    else:
+        with ThreadPoolExecutor(max_workers=min(nblk, os.cpu_count() or 4, 16)) as ex:
+            list(ex.map(fill, range(nblk)))
+    return out
+
+
 def make_inputs(w: Workload) -> Dict[str, torch.Tensor]:
     """Draw the workload's inputs on the CPU (contiguous tensors).
 
     Returns x, dy, gamma (io dtype), rstd (fp32 [M]), mean (fp32 [M], LayerNorm
-    only), beta (io dtype, only when the workload lists one), and the index
-    tensor ``outliers`` when outlier features are drawn.
+    only), beta (io dtype, only when the workload lists one), and
+    ``outliers`` (column indices, or [k, 2] entry indices) when outliers are
+    drawn.
     """
     g = torch.Generator().manual_seed(w.seed)
     M, N = w.M, w.N
-    x = torch.randn(M, N, generator=g, dtype=torch.float32)
+    x = _blocked(w.seed, _X, M, N, "normal")
     if w.x_dist == "row_shift_scale":
         mu = torch.rand(M, 1, generator=g, dtype=torch.float32) * 4.0 - 2.0
         sc = torch.rand(M, 1, generator=g, dtype=torch.float32) * 3.5 + 0.5
         x.mul_(sc).add_(mu)
     elif w.x_dist != "normal":
         raise ValueError(w.x_dist)
-    dy = torch.randn(M, N, generator=g, dtype=torch.float32).mul_(w.dy_std)
+    dy = _blocked(w.seed, _DY, M, N, "normal").mul_(w.dy_std)
     gamma = torch.rand(N, generator=g, dtype=torch.float32)
     gamma.mul_(w.gamma_hi - w.gamma_lo).add_(w.gamma_lo)
     out: Dict[str, torch.Tensor] = {}
@@ -152,7 +190,7 @@ def make_inputs(w: Workload) -> Dict[str, torch.Tensor]:
                 x[:, cols] *= w.outlier_scale
             out["outliers"] = cols
         elif w.outlier_mode == "entries":
-            mask = torch.rand(M, N, generator=g) < w.outlier_frac
+            mask = _blocked(w.seed, _MASK, M, N, "uniform") < w.outlier_frac
             x[mask] *= w.outlier_scale
             out["outliers"] = mask.nonzero()
         else:

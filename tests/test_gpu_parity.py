@@ -1,0 +1,391 @@
+"""GPU path against the fp64 oracle, through the C ABI (needs a gfx950 GPU).
+
+Inputs come from the seeded generator; both sides read the same bits. Small
+and mid sizes are compared element by element; the full-size workloads are
+run in the benchmark's launch configuration (the automatic plan) and compared
+on sampled rows of dx and sampled columns of dgamma/dbeta, which the oracle
+computes exactly one by one (dx is row-local; a weight-gradient column needs
+only that column of x and dy).
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+from rmsnorm_backward_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module")
+def nb():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import rmsnorm_backward_amd as nbmod
+    nbmod.load_library()
+    return nbmod
+
+
+def to_gpu(inp):
+    return {k: (v.cuda() if isinstance(v, torch.Tensor) and k != "outliers" else v)
+            for k, v in inp.items()}
+
+
+def run(nb, w, g, *, dbeta=None, groups=0, wgrad=None, stream=None, plan=None):
+    """Run the library on GPU tensors g; returns CPU (dx, dgamma, dbeta)."""
+    with_db = (w.kind == "layernorm") if dbeta is None else dbeta
+    wg = wgrad or w.wgrad_dtype
+    if plan is None and groups:
+        plan = nb.norm_bwd_make_plan(w.kind, w.M, w.N, w.io_dtype, with_db, groups)
+    if plan is not None:
+        out = nb.norm_bwd_execute(plan, g["x"], g["dy"], g["gamma"], g.get("mean"), g["rstd"],
+                                  wgrad_dtype=wg, stream=stream)
+    elif w.kind == "layernorm":
+        out = nb.norm_bwd_layernorm(g["x"], g["dy"], g["gamma"], g["mean"], g["rstd"], w.eps,
+                                    wgrad_dtype=wg, with_dbeta=with_db, stream=stream)
+    else:
+        out = nb.norm_bwd_rmsnorm(g["x"], g["dy"], g["gamma"], g["rstd"], w.eps,
+                                  wgrad_dtype=wg, with_dbeta=with_db, stream=stream)
+    torch.cuda.synchronize()
+    return tuple(None if t is None else t.cpu() for t in out)
+
+
+def compare_full(w, inp, out, with_db):
+    dx, dg, db = out
+    rdx, rdg, rdb = oracle.bwd(w.kind, inp["x"], inp["dy"], inp["gamma"], inp.get("mean"),
+                               inp["rstd"], want_dbeta=True)
+    stats = {"dx": parity.check_dx(w.io_dtype, dx, rdx),
+             "dgamma": parity.check_wgrad(w.io_dtype, dg, rdg)}
+    if with_db:
+        stats["dbeta"] = parity.check_wgrad(w.io_dtype, db, rdb, "dbeta")
+    return stats
+
+
+# ----------------------------------------------------------------------------
+# The five workloads at sizes the oracle finishes in seconds, spanning many
+# row groups and a ragged last group (and the first two at their full size).
+SMALL = [
+    W.LN_F32_128x512,
+    W.RMS_F32_128x512,
+    W.LN_F16_1151x8192,
+    W.scaled(W.RMS_BF16_16384x4096, M=2003),
+    W.scaled(W.LN_BF16_65536x8192, M=777),
+    W.scaled(W.RMS_BF16_262144x768, M=5001),
+    W.scaled(W.RMS_BF16_262144x768, M=3001, name="rmsnorm_bf16_3001x768_entry_outliers",
+             outlier_mode="entries"),
+    W.scaled(W.LN_F16_1151x8192, M=257, N=8192, name="layernorm_f16_phobos_like",
+             x_dist="normal"),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_workload_parity(nb, w):
+    inp = W.make_inputs(w)
+    with_db = w.kind == "layernorm"
+    out = run(nb, w, to_gpu(inp))
+    s = compare_full(w, inp, out, with_db)
+    print(w.name, s)
+
+
+def test_phobos_check_distribution(nb):
+    """The Phobos tutorial's own inputs: x = -2.3 + 0.5*N(0,1), dy = 0.1*N(0,1),
+    gamma, beta ~ U(0,1), fp16, 1151 x 8192 ("05: Layer norm", its check)."""
+    g = torch.Generator().manual_seed(0)
+    M, N, eps = 1151, 8192, 1e-5
+    gamma = torch.rand(N, generator=g).half()
+    x = (-2.3 + 0.5 * torch.randn(M, N, generator=g)).half()
+    dy = (0.1 * torch.randn(M, N, generator=g)).half()
+    mean, rstd = W.saved_stats(x, "layernorm", eps)
+    inp = {"x": x, "dy": dy, "gamma": gamma, "mean": mean, "rstd": rstd}
+    w = W.scaled(W.LN_F16_1151x8192, name="phobos_check")
+    out = run(nb, w, to_gpu(inp))
+    compare_full(w, inp, out, True)
+
+
+# ----------------------------------------------------------------------------
+# Full sizes, automatic plan (what the benchmark times), sampled outputs.
+FULL = [W.RMS_BF16_16384x4096, W.LN_BF16_65536x8192, W.RMS_BF16_262144x768]
+
+
+@pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
+def test_full_size_sampled(nb, w):
+    print(f"[gen] {w.name}", flush=True)
+    inp = W.make_inputs(w)
+    g = to_gpu(inp)
+    with_db = w.kind == "layernorm"
+    plan = nb.norm_bwd_make_plan(w.kind, w.M, w.N, w.io_dtype, with_db)
+    print(f"[run] {w.name} plan={plan.as_dict()}", flush=True)
+    dx_g, dg_g, db_g = run(nb, w, g)
+    del g
+    R = plan.rows_per_group
+    extra = [k * R + d for k in (1, plan.groups // 2, plan.groups - 1) for d in (-1, 0)]
+    rows = W.sample_rows(w.M, 48, seed=w.seed, extra=extra)
+    mean = inp.get("mean")
+    rdx = oracle.bwd_dx(w.kind, inp["x"][rows], inp["dy"][rows], inp["gamma"],
+                        None if mean is None else mean[rows], inp["rstd"][rows])
+    parity.check_dx(w.io_dtype, dx_g[rows], rdx)
+    cols = W.sample_rows(w.N, 40, seed=w.seed + 1)
+    if "outliers" in inp and inp["outliers"].dim() == 1:
+        cols = torch.unique(torch.cat([cols, inp["outliers"]]))
+    rdg, rdb = oracle.bwd_wgrad(w.kind, inp["x"][:, cols], inp["dy"][:, cols], mean,
+                                inp["rstd"], want_dbeta=True)
+    # the normwise floor uses the largest |dgamma| over all columns; the
+    # sample's max stands in for it (it can only tighten the bound)
+    parity.check_wgrad(w.io_dtype, dg_g[cols], rdg)
+    if with_db:
+        parity.check_wgrad(w.io_dtype, db_g[cols], rdb, "dbeta")
+    # dbeta over all columns is the plain column sum of dy (a closed form)
+    if with_db:
+        ref = inp["dy"].double().sum(0)
+        parity.check_wgrad(w.io_dtype, db_g, ref, "dbeta(all)")
+
+
+# ----------------------------------------------------------------------------
+# Edge shapes: ragged N (vector and scalar paths), tiny and maximal rows.
+EDGE_N = {
+    torch.float32: [1, 3, 4, 8, 63, 64, 65, 255, 256, 257, 1000, 1024, 4100, 8191, 16384],
+    torch.float16: [1, 2, 8, 63, 64, 65, 512, 513, 768, 1000, 4096, 4100, 8191, 8192, 32768],
+    torch.bfloat16: [1, 7, 8, 16, 63, 64, 65, 520, 768, 2048, 4096, 6144, 8192, 16384, 32768],
+}
+EDGE_M = [1, 2, 3, 511, 513]
+
+
+def _edge_cases():
+    out = []
+    for dt, ns in EDGE_N.items():
+        for i, n in enumerate(ns):
+            for kind in ("layernorm", "rmsnorm"):
+                m = EDGE_M[(i + (kind == "rmsnorm")) % len(EDGE_M)]
+                if n >= 16384:
+                    m = min(m, 64)
+                out.append((kind, dt, m, n))
+    return out
+
+
+@pytest.mark.parametrize("kind,dt,M,N", _edge_cases(),
+                         ids=lambda v: str(v).replace("torch.", ""))
+def test_edge_shapes(nb, kind, dt, M, N):
+    base = W.LN_F32_128x512 if kind == "layernorm" else W.RMS_F32_128x512
+    w = W.scaled(base, M=M, N=N, io_dtype=dt, wgrad_dtype=torch.float32, seed=99 + M + N)
+    inp = W.make_inputs(w)
+    for with_db in (True, False):
+        if dt != torch.float32 and with_db and N > 16384:
+            with pytest.raises(nb.NormBwdError) as e:      # documented limit
+                run(nb, w, to_gpu(inp), dbeta=with_db)
+            assert e.value.status == nb.ERR_UNSUPPORTED
+            continue
+        out = run(nb, w, to_gpu(inp), dbeta=with_db)
+        compare_full(w, inp, out, with_db)
+        if not with_db:
+            assert out[2] is None
+
+
+@pytest.mark.parametrize("groups", [1, 2, 7, 100, 999, 1000])
+def test_explicit_groups(nb, groups):
+    w = W.scaled(W.LN_BF16_65536x8192, M=1000, N=1536)
+    inp = W.make_inputs(w)
+    out = run(nb, w, to_gpu(inp), groups=groups)
+    compare_full(w, inp, out, True)
+
+
+@pytest.mark.parametrize("kind", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16])
+def test_wgrad_in_io_dtype(nb, kind, dt):
+    base = W.LN_F16_1151x8192 if kind == "layernorm" else W.RMS_BF16_16384x4096
+    w = W.scaled(base, M=300, N=2048, io_dtype=dt, wgrad_dtype=dt)
+    inp = W.make_inputs(w)
+    out = run(nb, w, to_gpu(inp), dbeta=True)
+    assert out[1].dtype == dt and out[2].dtype == dt
+    compare_full(w, inp, out, True)
+
+
+def test_geometry_variants_agree(nb):
+    """Edited plans (waves per row, rows in flight, chunks) stay in tolerance,
+    and dgamma bits do not depend on the lane layout when the row grouping is
+    unchanged (only the in-row sums, i.e. dx, may differ in the last bit)."""
+    w = W.scaled(W.RMS_BF16_16384x4096, M=1500, N=4096)
+    inp = W.make_inputs(w)
+    g = to_gpu(inp)
+    base = nb.norm_bwd_make_plan("rmsnorm", w.M, w.N, torch.bfloat16, False)
+    ref = None
+    for S, C, P in ((1, 8, 4), (1, 8, 2), (2, 4, 2), (2, 4, 4), (4, 2, 1), (4, 2, 2), (8, 1, 1),
+                    (2, 4, 8), (4, 2, 4)):
+        p = base.copy()
+        p.waves_per_row, p.chunks, p.rows_in_flight = S, C, P
+        p.threads = 64 * S * P
+        p.lds_bytes = S * C * 64 * p.vec * 4 if P > 1 else 0
+        if p.threads > (512 if p.vec * C > 16 else 1024):
+            continue
+        out = run(nb, w, g, plan=p)
+        compare_full(w, inp, out, False)
+        if P == base.rows_in_flight:
+            if ref is None:
+                ref = out[1]
+            assert torch.equal(out[1], ref), (S, C, P)
+
+
+def test_determinism_repeats_and_perturbation(nb):
+    w = W.scaled(W.LN_BF16_65536x8192, M=4099, N=4096)
+    g = to_gpu(W.make_inputs(w))
+    first = run(nb, w, g)
+    side = torch.cuda.Stream()
+    junk = torch.randn(4096, 4096, device="cuda")
+    for i in range(20):
+        if i % 2:
+            with torch.cuda.stream(side):     # concurrent work perturbs scheduling
+                junk = junk @ junk
+                junk = junk / junk.abs().max()
+        out = run(nb, w, g)
+        for a, b, name in zip(out, first, ("dx", "dgamma", "dbeta")):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), \
+                f"{name} changed on repeat {i}"
+    torch.cuda.synchronize()
+
+
+def test_nan_poisoned_outputs_and_workspace(nb):
+    """Prior contents of dx, dgamma, dbeta and the workspace are never read."""
+    w = W.scaled(W.LN_BF16_65536x8192, M=999, N=768)
+    inp = W.make_inputs(w)
+    g = to_gpu(inp)
+    clean = run(nb, w, g)
+    need = nb.norm_bwd_workspace_bytes("layernorm", w.M, w.N, w.io_dtype, True)
+    ws = torch.full((need // 4,), float("nan"), device="cuda")
+    dx = torch.full((w.M, w.N), float("nan"), dtype=w.io_dtype, device="cuda")
+    dg = torch.full((w.N,), float("nan"), device="cuda")
+    db = torch.full((w.N,), float("nan"), device="cuda")
+    nb.norm_bwd_layernorm(g["x"], g["dy"], g["gamma"], g["mean"], g["rstd"], w.eps,
+                          dx=dx, dgamma=dg, dbeta=db, workspace=ws)
+    torch.cuda.synchronize()
+    for a, b in zip((dx.cpu(), dg.cpu(), db.cpu()), clean):
+        assert torch.equal(a, b)
+
+
+def test_guard_bands_untouched(nb):
+    """Outputs and workspace carved out of larger buffers: the bytes around
+    them keep their canary values (no out-of-bounds writes)."""
+    w = W.scaled(W.RMS_BF16_262144x768, M=1031, N=1000)   # ragged N, vector path
+    inp = W.make_inputs(w)
+    g = to_gpu(inp)
+    pad = 4096
+    canary = -1536.0   # exact in bf16, fp16 and fp32
+    n_dx = w.M * w.N
+    dx_buf = torch.full((n_dx + 2 * pad,), canary, dtype=w.io_dtype, device="cuda")
+    dg_buf = torch.full((w.N + 2 * pad,), canary, device="cuda")
+    db_buf = torch.full((w.N + 2 * pad,), canary, device="cuda")
+    need = nb.norm_bwd_workspace_bytes("rmsnorm", w.M, w.N, w.io_dtype, True)
+    ws_buf = torch.full((need // 4 + 2 * pad,), canary, device="cuda")
+    dx = dx_buf[pad:pad + n_dx].view(w.M, w.N)
+    dg, db = dg_buf[pad:pad + w.N], db_buf[pad:pad + w.N]
+    ws = ws_buf[pad:pad + need // 4]
+    nb.norm_bwd_rmsnorm(g["x"], g["dy"], g["gamma"], g["rstd"], w.eps, dx=dx, dgamma=dg,
+                        dbeta=db, workspace=ws)
+    torch.cuda.synchronize()
+    for buf, n in ((dx_buf, n_dx), (dg_buf, w.N), (db_buf, w.N), (ws_buf, need // 4)):
+        c = buf.float().cpu()
+        assert torch.all(c[:pad] == canary) and torch.all(c[pad + n:] == canary)
+    compare_full(w, inp, (dx.cpu(), dg.cpu(), db.cpu()), True)
+
+
+def test_misaligned_rows_take_the_scalar_path(nb):
+    """Tensors offset by one element (not 16-byte aligned) still give the
+    right answer (the automatic plan falls back to one element per lane)."""
+    w = W.scaled(W.RMS_BF16_16384x4096, M=130, N=1024)
+    inp = W.make_inputs(w)
+    def off(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
+        v = buf[1:].view(t.shape)
+        v.copy_(t.cuda())
+        return v
+    g = {"x": off(inp["x"]), "dy": off(inp["dy"]), "gamma": off(inp["gamma"]),
+         "rstd": inp["rstd"].cuda()}
+    out = run(nb, w, g)
+    compare_full(w, inp, out, False)
+
+
+def test_stream_semantics(nb):
+    w = W.scaled(W.RMS_BF16_16384x4096, M=512, N=4096)
+    inp = W.make_inputs(w)
+    g = to_gpu(inp)
+    ref = run(nb, w, g)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out = nb.norm_bwd_rmsnorm(g["x"], g["dy"], g["gamma"], g["rstd"], w.eps)
+        ev = torch.cuda.Event()
+        ev.record(s)
+    ev.synchronize()
+    for a, b in zip(out, ref):
+        if b is not None:
+            assert torch.equal(a.cpu(), b)
+
+
+def test_two_phase_api_matches_full_call(nb):
+    w = W.scaled(W.LN_BF16_65536x8192, M=2048, N=2048)
+    g = to_gpu(W.make_inputs(w))
+    full = run(nb, w, g)
+    plan = nb.norm_bwd_make_plan("layernorm", w.M, w.N, w.io_dtype, True)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    dx = torch.empty_like(g["x"])
+    nb.norm_bwd_execute_partials(plan, g["x"], g["dy"], g["gamma"], g["mean"], g["rstd"], dx, ws)
+    dg = torch.empty(w.N, device="cuda")
+    db = torch.empty(w.N, device="cuda")
+    nb.norm_bwd_reduce_partials(plan.groups, w.N, ws, dg, db)
+    torch.cuda.synchronize()
+    assert torch.equal(dx.cpu(), full[0])
+    assert torch.equal(dg.cpu(), full[1]) and torch.equal(db.cpu(), full[2])
+
+
+def test_empty_problems(nb):
+    for kind in ("layernorm", "rmsnorm"):
+        x = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+        st = torch.empty(0, device="cuda")
+        dg = torch.full((64,), float("nan"), device="cuda")
+        db = torch.full((64,), float("nan"), device="cuda")
+        gam = torch.ones(64, dtype=torch.bfloat16, device="cuda")
+        if kind == "layernorm":
+            nb.norm_bwd_layernorm(x, x, gam, st, st, dgamma=dg, dbeta=db)
+        else:
+            nb.norm_bwd_rmsnorm(x, x, gam, st, dgamma=dg, dbeta=db)
+        torch.cuda.synchronize()
+        assert torch.all(dg == 0) and torch.all(db == 0)      # the empty sum
+        x0 = torch.empty(5, 0, dtype=torch.bfloat16, device="cuda")
+        st5 = torch.ones(5, device="cuda")
+        g0 = torch.empty(0, dtype=torch.bfloat16, device="cuda")
+        if kind == "layernorm":
+            out = nb.norm_bwd_layernorm(x0, x0, g0, st5, st5)
+        else:
+            out = nb.norm_bwd_rmsnorm(x0, x0, g0, st5)
+        torch.cuda.synchronize()
+        assert out[0].shape == (5, 0) and out[1].shape == (0,)
+
+
+def test_rejects_bad_tensors_before_launch(nb):
+    w = W.scaled(W.RMS_BF16_16384x4096, M=64, N=256)
+    g = to_gpu(W.make_inputs(w))
+    small_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(nb.NormBwdError) as e:
+        nb.norm_bwd_rmsnorm(g["x"], g["dy"], g["gamma"], g["rstd"], workspace=small_ws)
+    assert e.value.status == nb.ERR_WORKSPACE
+    with pytest.raises(nb.NormBwdError) as e:
+        nb.norm_bwd_rmsnorm(g["x"], g["dy"], g["gamma"], g["rstd"], dx=g["x"])
+    assert e.value.status == nb.ERR_INVALID_ARG
+    with pytest.raises(nb.NormBwdError) as e:
+        nb.norm_bwd_rmsnorm(g["x"], g["dy"], g["gamma"], g["rstd"], eps=-1.0)
+    assert e.value.status == nb.ERR_INVALID_ARG
+    with pytest.raises(ValueError):
+        nb.norm_bwd_rmsnorm(g["x"], g["dy"].float(), g["gamma"], g["rstd"])
+
+
+def test_copy_probe(nb):
+    src = torch.randint(0, 1 << 30, (1 << 20,), dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    nb.norm_bwd_probe_copy(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)

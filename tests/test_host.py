@@ -1,0 +1,273 @@
+"""Host-side tests of the C ABI (no GPU needed, no kernel launched).
+
+The library loads and exports every function include/norm_bwd.h declares; the
+planner's rules hold; every invalid argument is rejected with the documented
+status before anything touches the HIP runtime (fake device pointers are
+never dereferenced on these paths).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "norm_bwd.h")
+
+
+@pytest.fixture(scope="module")
+def nb():
+    import rmsnorm_backward_amd as nbmod
+    if not os.path.exists(nbmod.LIB_PATH):
+        from rmsnorm_backward_amd import _build
+        _build.build()
+    nbmod.load_library()
+    return nbmod
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(norm_bwd_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_documented_entry_points():
+    names = declared_functions()
+    for want in ("norm_bwd_layernorm", "norm_bwd_rmsnorm", "norm_bwd_workspace_bytes",
+                 "norm_bwd_make_plan", "norm_bwd_execute", "norm_bwd_execute_partials",
+                 "norm_bwd_reduce_partials", "norm_bwd_status_string", "norm_bwd_last_error",
+                 "norm_bwd_probe_copy"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(nb):
+    lib = ctypes.CDLL(nb.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_plan_struct_layout_matches_header(nb):
+    # norm_bwd_plan_t: 4 int32, 4 int64, 6 int32, size_t -> 80 bytes
+    assert ctypes.sizeof(nb.NormBwdPlan) == 80
+    assert nb.NormBwdPlan.workspace_bytes.offset == 72
+    assert nb.NormBwdPlan.chunks.offset == 48
+
+
+def test_status_strings(nb):
+    assert nb.norm_bwd_status_string(0) == "NORM_BWD_OK"
+    assert nb.norm_bwd_status_string(1) == "NORM_BWD_ERR_INVALID_ARG"
+    assert nb.norm_bwd_status_string(2) == "NORM_BWD_ERR_UNSUPPORTED"
+    assert nb.norm_bwd_status_string(3) == "NORM_BWD_ERR_WORKSPACE"
+    assert nb.norm_bwd_status_string(4) == "NORM_BWD_ERR_HIP"
+    assert nb.norm_bwd_status_string(99) == "NORM_BWD_ERR_UNKNOWN"
+
+
+def _auto_groups(M):
+    if M == 0:
+        return 0
+    t = min(M, 512)
+    R = -(-M // t)
+    return -(-M // R)
+
+
+@pytest.mark.parametrize("kind,M,N,dt,db", [
+    ("layernorm", 128, 512, torch.float32, True),
+    ("rmsnorm", 128, 512, torch.float32, False),
+    ("layernorm", 1151, 8192, torch.float16, True),
+    ("rmsnorm", 16384, 4096, torch.bfloat16, False),
+    ("layernorm", 65536, 8192, torch.bfloat16, True),
+    ("rmsnorm", 262144, 768, torch.bfloat16, False),
+    ("rmsnorm", 0, 768, torch.bfloat16, True),
+    ("layernorm", 5, 0, torch.float16, True),
+])
+def test_workspace_bytes_rule(nb, kind, M, N, dt, db):
+    got = nb.norm_bwd_workspace_bytes(kind, M, N, dt, db)
+    assert got == (2 if db else 1) * _auto_groups(M) * N * 4
+    plan = nb.norm_bwd_make_plan(kind, M, N, dt, db)
+    assert plan.workspace_bytes == got
+
+
+def test_workspace_bytes_rejects_bad_arguments(nb):
+    lib = nb.load_library()
+    bad = ctypes.c_size_t(-1).value
+    assert lib.norm_bwd_workspace_bytes(7, 10, 10, 0, 0) == bad
+    assert lib.norm_bwd_workspace_bytes(0, 10, 10, 9, 0) == bad
+    assert lib.norm_bwd_workspace_bytes(0, -1, 10, 0, 0) == bad
+    assert lib.norm_bwd_workspace_bytes(0, 10, 40000, 2, 0) == bad
+
+
+GEOMS = [(kind, dt, M, N, db, g)
+         for kind in ("layernorm", "rmsnorm")
+         for dt in (torch.float32, torch.float16, torch.bfloat16)
+         for (M, N) in ((1, 1), (3, 7), (17, 63), (64, 64), (65, 65), (1151, 8192),
+                        (2, 768), (100, 4096), (7, 16384), (9, 1000))
+         for db in (False, True)
+         for g in (0, 1, 5)]
+
+
+@pytest.mark.parametrize("kind,dt,M,N,db,groups", GEOMS)
+def test_plan_invariants(nb, kind, dt, M, N, db, groups):
+    eb = torch.tensor([], dtype=dt).element_size()
+    if N > (16384 if eb == 4 or db else 32768):
+        return
+    p = nb.norm_bwd_make_plan(kind, M, N, dt, db, groups)
+    S, P, C, vec = p.waves_per_row, p.rows_in_flight, p.chunks, p.vec
+    assert vec in (1, 16 // eb) and (vec == 1 or N % vec == 0)
+    assert S * 64 * vec * C >= N                       # the lanes cover the row
+    assert p.threads == 64 * S * P and 1 <= S * P <= 16
+    assert C in (1, 2, 4, 8)
+    assert p.groups * p.rows_per_group >= M            # every row in a group
+    assert (p.groups - 1) * p.rows_per_group < M       # no empty group
+    if groups:
+        assert p.groups <= groups
+    else:
+        assert p.groups == _auto_groups(M)
+    assert 1 <= p.grid <= p.groups
+    nacc = 2 if db else 1
+    assert p.workspace_bytes == nacc * p.groups * N * 4
+    assert p.lds_bytes == (nacc * S * C * 64 * vec * 4 if P > 1 else 0)
+    assert p.lds_bytes <= 65536
+
+
+def test_groups_do_not_depend_on_device(nb):
+    # the plan is a pure function of its arguments (no device query)
+    a = nb.norm_bwd_make_plan("rmsnorm", 16384, 4096, torch.bfloat16, False).as_dict()
+    b = nb.norm_bwd_make_plan("rmsnorm", 16384, 4096, torch.bfloat16, False).as_dict()
+    assert a == b
+
+
+def test_make_plan_rejects(nb):
+    lib = nb.load_library()
+    p = nb.NormBwdPlan()
+    assert lib.norm_bwd_make_plan(5, 1, 1, 0, 0, 0, ctypes.byref(p)) == nb.ERR_INVALID_ARG
+    assert lib.norm_bwd_make_plan(0, 1, 1, 3, 0, 0, ctypes.byref(p)) == nb.ERR_UNSUPPORTED
+    assert lib.norm_bwd_make_plan(0, -1, 1, 0, 0, 0, ctypes.byref(p)) == nb.ERR_INVALID_ARG
+    assert lib.norm_bwd_make_plan(0, 1, -1, 0, 0, 0, ctypes.byref(p)) == nb.ERR_INVALID_ARG
+    assert lib.norm_bwd_make_plan(0, 1, 1, 0, 0, -2, ctypes.byref(p)) == nb.ERR_INVALID_ARG
+    assert lib.norm_bwd_make_plan(0, 1, 16385, 0, 0, 0, ctypes.byref(p)) == nb.ERR_UNSUPPORTED
+    assert lib.norm_bwd_make_plan(0, 1, 32769, 2, 0, 0, ctypes.byref(p)) == nb.ERR_UNSUPPORTED
+    assert lib.norm_bwd_make_plan(1, 1, 32768, 2, 0, 0, ctypes.byref(p)) == nb.OK
+    assert lib.norm_bwd_make_plan(1, 1, 32768, 2, 1, 0, ctypes.byref(p)) == nb.ERR_UNSUPPORTED
+    assert lib.norm_bwd_make_plan(1, 1, 16384, 2, 1, 0, ctypes.byref(p)) == nb.OK
+    assert lib.norm_bwd_make_plan(0, 1, 1, 0, 2, 0, ctypes.byref(p)) == nb.ERR_INVALID_ARG
+    assert "N exceeds" in nb.norm_bwd_last_error() or nb.norm_bwd_last_error()
+
+
+# ---- argument rejection in the entry points (host checks only) -------------
+# These calls pass fake device addresses and must be rejected before any
+# launch. As a second guard they only run where no GPU is visible, so a test
+# mistake can never hand a fake address to a kernel.
+no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                            reason="fake-pointer rejection tests run only without a GPU")
+B = 1 << 40   # fake, 256-byte aligned device addresses; never dereferenced
+M_, N_ = 64, 256
+
+
+def _addr(i):
+    return ctypes.c_void_p(B + i * (1 << 30))
+
+
+def _rms(nb, **over):
+    a = dict(x=_addr(0), dy=_addr(1), gamma=_addr(2), rstd=_addr(3), M=M_, N=N_, io=2, wg=0,
+             eps=1e-6, dx=_addr(4), dgamma=_addr(5), dbeta=None, ws=_addr(6),
+             wsb=nb.norm_bwd_workspace_bytes("rmsnorm", M_, N_, 2, False), stream=None)
+    a.update(over)
+    lib = nb.load_library()
+    return lib.norm_bwd_rmsnorm(a["x"], a["dy"], a["gamma"], a["rstd"], a["M"], a["N"], a["io"],
+                                a["wg"], a["eps"], a["dx"], a["dgamma"], a["dbeta"], a["ws"],
+                                a["wsb"], a["stream"])
+
+
+def _ln(nb, **over):
+    a = dict(x=_addr(0), dy=_addr(1), gamma=_addr(2), mean=_addr(7), rstd=_addr(3), M=M_, N=N_,
+             io=1, wg=1, eps=1e-5, dx=_addr(4), dgamma=_addr(5), dbeta=_addr(8), ws=_addr(6),
+             wsb=nb.norm_bwd_workspace_bytes("layernorm", M_, N_, 1, True), stream=None)
+    a.update(over)
+    lib = nb.load_library()
+    return lib.norm_bwd_layernorm(a["x"], a["dy"], a["gamma"], a["mean"], a["rstd"], a["M"],
+                                  a["N"], a["io"], a["wg"], a["eps"], a["dx"], a["dgamma"],
+                                  a["dbeta"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(x=None), 1), (dict(dy=None), 1), (dict(gamma=None), 1), (dict(rstd=None), 1),
+    (dict(dx=None), 1), (dict(dgamma=None), 1),
+    (dict(M=-1), 1), (dict(N=-3), 1), (dict(eps=-1.0), 1), (dict(eps=float("nan")), 1),
+    (dict(eps=float("inf")), 1),
+    (dict(io=5), 2), (dict(wg=1), 2), (dict(wg=7), 2), (dict(N=40000), 2),
+    (dict(ws=None), 3), (dict(wsb=16), 3),
+    (dict(ws=ctypes.c_void_p(B + 6 * (1 << 30) + 8)), 1),
+    (dict(dx=_addr(0)), 1),                                  # dx aliases x
+    (dict(dgamma=ctypes.c_void_p(B + 4 * (1 << 30) + 64)), 1),  # dgamma inside dx
+    (dict(ws=_addr(5)), 1),                                  # workspace aliases dgamma
+    (dict(dbeta=_addr(5), wsb=1 << 20), 1),                  # dbeta aliases dgamma
+])
+@no_gpu
+def test_rmsnorm_rejects(nb, over, status):
+    assert _rms(nb, **over) == status
+    assert nb.norm_bwd_last_error().startswith(nb.norm_bwd_status_string(status))
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(mean=None), 1), (dict(wg=2), 2), (dict(dbeta=_addr(6)), 1),
+    (dict(wsb=100), 3),
+    (dict(mean=_addr(4)), 1),                                 # dx overlaps mean
+])
+@no_gpu
+def test_layernorm_rejects(nb, over, status):
+    assert _ln(nb, **over) == status
+
+
+@no_gpu
+def test_execute_rejects_edited_plans(nb):
+    lib = nb.load_library()
+    base = nb.norm_bwd_make_plan("rmsnorm", M_, N_, torch.bfloat16, False)
+
+    def run(p):
+        return lib.norm_bwd_execute(ctypes.byref(p), _addr(0), _addr(1), _addr(2), None,
+                                    _addr(3), 0, _addr(4), _addr(5), None, _addr(6),
+                                    p.workspace_bytes, None)
+
+    edits = [
+        ("threads", 100), ("chunks", 3), ("vec", 2), ("waves_per_row", 0),
+        ("rows_in_flight", 17), ("groups", base.groups + 5), ("rows_per_group", base.rows_per_group + 1),
+        ("grid", 0), ("grid", base.groups + 1), ("lds_bytes", 4), ("workspace_bytes", 8),
+        ("kind", 3), ("io_dtype", 9), ("with_dbeta", 1),
+    ]
+    for field, value in edits:
+        p = base.copy()
+        setattr(p, field, value)
+        assert run(p) in (1, 2), (field, value)
+    # geometry that does not cover N
+    p = nb.norm_bwd_make_plan("rmsnorm", M_, 4096, torch.bfloat16, False)
+    assert p.waves_per_row * 64 * p.vec * p.chunks >= 4096
+    p.chunks = 1
+    p.waves_per_row = 1
+    p.rows_in_flight = 1
+    p.threads = 64
+    p.lds_bytes = 0
+    assert run(p) == 1
+    # misaligned x for a vectorised plan
+    p = base.copy()
+    assert lib.norm_bwd_execute(ctypes.byref(p), ctypes.c_void_p(B + 2), _addr(1), _addr(2),
+                                None, _addr(3), 0, _addr(4), _addr(5), None, _addr(6),
+                                p.workspace_bytes, None) == 1
+
+
+@no_gpu
+def test_reduce_and_probe_reject(nb):
+    lib = nb.load_library()
+    assert lib.norm_bwd_reduce_partials(-1, 8, 0, _addr(0), 1 << 20, _addr(1), None, None) == 1
+    assert lib.norm_bwd_reduce_partials(4, 8, 0, _addr(0), 16, _addr(1), None, None) == 3
+    assert lib.norm_bwd_reduce_partials(4, 8, 0, _addr(0), 1 << 20, None, None, None) == 1
+    assert lib.norm_bwd_reduce_partials(4, 8, 5, _addr(0), 1 << 20, _addr(1), None, None) == 2
+    assert lib.norm_bwd_probe_copy(_addr(0), _addr(1), 17, None) == 1
+    assert lib.norm_bwd_probe_copy(_addr(0), ctypes.c_void_p(B + 8), 1024, None) == 1
+
+
+def test_binding_refuses_cpu_tensors(nb):
+    x = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        nb.norm_bwd_rmsnorm(x, x, torch.zeros(8, dtype=torch.bfloat16), torch.ones(4))
