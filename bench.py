@@ -106,16 +106,22 @@ def cpu_baseline(w, inp):
     gamma = inp["gamma"].double().numpy()
     rstd = inp["rstd"][:rows].double().numpy()
     mean = inp["mean"][:rows].double().numpy() if w.kind == "layernorm" else None
-    t0 = time.perf_counter()
-    o.bwd(w.kind, x, dy, gamma, mean, rstd, want_dbeta=w.kind == "layernorm")
-    dt = time.perf_counter() - t0
+    # repeat the pass until about 10 s of CPU time has accumulated (at most 200)
+    reps, total = 0, 0.0
+    while reps < 200 and (total < 10.0 or reps < 1):
+        t0 = time.perf_counter()
+        o.bwd(w.kind, x, dy, gamma, mean, rstd, want_dbeta=w.kind == "layernorm")
+        total += time.perf_counter() - t0
+        reps += 1
+    dt = total / reps
     import dataclasses
     ws = dataclasses.replace(w, M=rows)
     sample = (f"full {w.M}x{w.N} workload" if rows == w.M else
-              f"first {rows} of {w.M} rows x {w.N}") + ", one fp64 pass (dx, dgamma" + \
-             (", dbeta)" if w.kind == "layernorm" else ")")
+              f"first {rows} of {w.M} rows x {w.N}") + \
+        f", fp64 passes (dx, dgamma{', dbeta' if w.kind == 'layernorm' else ''}) repeated " \
+        f"{reps}x, {total:.1f} s total, mean per pass"
     return {"value": round(ws.algorithmic_bytes() / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "sample": sample, "seconds": round(dt, 3)}
+            "kind": "oracle", "sample": sample, "seconds_per_pass": round(dt, 4)}
 
 
 def main(argv=None) -> int:

@@ -206,7 +206,7 @@ def _backward(kind, x, dy, gamma, mean, rstd, eps, wgrad_dtype, dx, dgamma, dbet
     s = _stream(stream, dev)
     with torch.cuda.device(dev):
         if plan is None:
-            need = norm_bwd_workspace_bytes(kind, M, N, io, dbeta is not None)
+            need = norm_bwd_make_plan(kind, M, N, io, dbeta is not None).workspace_bytes
             if workspace is None:
                 workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
             wsb = workspace.numel() * workspace.element_size()

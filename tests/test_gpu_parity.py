@@ -60,7 +60,9 @@ def compare_full(w, inp, out, with_db):
     dx, dg, db = out
     rdx, rdg, rdb = oracle.bwd(w.kind, inp["x"], inp["dy"], inp["gamma"], inp.get("mean"),
                                inp["rstd"], want_dbeta=True)
-    stats = {"dx": parity.check_dx(w.io_dtype, dx, rdx),
+    scale = parity.dx_term_scale(w.kind, inp["x"], inp["dy"], inp["gamma"], inp.get("mean"),
+                                 inp["rstd"])
+    stats = {"dx": parity.check_dx(w.io_dtype, dx, rdx, scale=scale),
              "dgamma": parity.check_wgrad(w.io_dtype, dg, rdg)}
     if with_db:
         stats["dbeta"] = parity.check_wgrad(w.io_dtype, db, rdb, "dbeta")
@@ -129,7 +131,9 @@ def test_full_size_sampled(nb, w):
     mean = inp.get("mean")
     rdx = oracle.bwd_dx(w.kind, inp["x"][rows], inp["dy"][rows], inp["gamma"],
                         None if mean is None else mean[rows], inp["rstd"][rows])
-    parity.check_dx(w.io_dtype, dx_g[rows], rdx)
+    scale = parity.dx_term_scale(w.kind, inp["x"][rows], inp["dy"][rows], inp["gamma"],
+                                 None if mean is None else mean[rows], inp["rstd"][rows])
+    parity.check_dx(w.io_dtype, dx_g[rows], rdx, scale=scale)
     cols = W.sample_rows(w.N, 40, seed=w.seed + 1)
     if "outliers" in inp and inp["outliers"].dim() == 1:
         cols = torch.unique(torch.cat([cols, inp["outliers"]]))
