@@ -18,9 +18,10 @@
  * parallel over ("Norm & activation backward", section "Half two: dγ and dβ
  * reduce across the whole batch", its strategy table). This library takes the
  * deterministic two-pass route from that table: kernel A computes dx and, for
- * each disjoint contiguous block ("group") of rows, the block's partial
- * dgamma/dbeta in registers, stored once into a caller-provided fp32
- * workspace[groups, N]; kernel B sums the groups in one fixed order. There are
+ * each of G disjoint row groups (group g = the rows r with r mod G == g), the
+ * group's partial dgamma/dbeta in registers, stored once into a
+ * caller-provided fp32 workspace[G, N]; kernel B sums the groups in one fixed
+ * order. There are
  * no atomics, so dx, dgamma and dbeta are bitwise identical across calls with
  * equal arguments (same kind, M, N, dtypes, groups, and pointer alignment
  * class) on the same device type. The group count never depends on the GPU's
@@ -130,9 +131,9 @@ size_t norm_bwd_workspace_bytes(int kind, int64_t M, int64_t N, int io_dtype,
  * An execution plan: the row grouping and the launch geometry of kernel A.
  * Produced by norm_bwd_make_plan; a caller may change `groups` (then call
  * norm_bwd_make_plan again with it) or the geometry fields for tuning, and
- * norm_bwd_execute re-validates every field. Results depend on groups,
- * rows_per_group, rows_in_flight (dgamma/dbeta order) and vec, chunks,
- * waves_per_row (order of the in-row sums), never on the device.
+ * norm_bwd_execute re-validates every field. Results depend on groups and
+ * rows_in_flight (dgamma/dbeta order) and on vec, chunks, waves_per_row
+ * (order of the in-row sums), never on the device.
  */
 typedef struct norm_bwd_plan {
     int32_t kind;            /* NORM_BWD_LAYERNORM / RMSNORM */
@@ -140,8 +141,8 @@ typedef struct norm_bwd_plan {
     int32_t with_dbeta;      /* 1: kernel A also sums dy for dbeta */
     int32_t vec;             /* elements per lane per load (16 bytes, or 1) */
     int64_t M, N;            /* problem size */
-    int64_t groups;          /* G: disjoint contiguous row blocks = workspace rows */
-    int64_t rows_per_group;  /* R: group g owns rows [g*R, min((g+1)*R, M)) */
+    int64_t groups;          /* G: row groups = workspace rows; group g = rows r, r mod G == g */
+    int64_t rows_per_group;  /* ceil(M / G): the most rows any group holds */
     int32_t chunks;          /* C: loads of `vec` elements per lane per row slice */
     int32_t waves_per_row;   /* S: 64-lane waves sharing one row */
     int32_t rows_in_flight;  /* P: rows a workgroup processes at once */
@@ -153,9 +154,9 @@ typedef struct norm_bwd_plan {
 
 /*
  * Fill *plan for (kind, M, N, io_dtype, with_dbeta). groups = 0 chooses the
- * automatic group count (a function of kind, M, N, io_dtype only); groups > 0
- * asks for that many row blocks (clamped to M; rows_per_group = ceil(M/groups)
- * and groups = ceil(M/rows_per_group) so that no block is empty). The plan
+ * automatic group count (min(512, ceil(M / 8)): a function of the problem
+ * only, never of the device); groups > 0 asks for that many row groups,
+ * clamped to M so that no group is empty. The plan
  * assumes 16-byte aligned base pointers; norm_bwd_execute rejects a plan
  * whose vec the pointers do not allow. Host-only. Returns a status code.
  */

@@ -47,7 +47,8 @@ int check_buffers(int kind, int64_t M, int64_t N, int io_dtype, int wgrad_dtype,
   const int wb = nb::dtype_bytes(wgrad_dtype);
   if (run_b) {
     if (wb == 0) return set_error(NORM_BWD_ERR_UNSUPPORTED, "unknown wgrad_dtype");
-    if (wgrad_dtype != NORM_BWD_F32 && wgrad_dtype != io_dtype)
+    // with kernel A in the same call, dgamma/dbeta are fp32 or the I/O type
+    if (run_a && wgrad_dtype != NORM_BWD_F32 && wgrad_dtype != io_dtype)
       return set_error(NORM_BWD_ERR_UNSUPPORTED, "wgrad_dtype must be NORM_BWD_F32 or io_dtype");
   }
   if (M < 0 || N < 0) return set_error(NORM_BWD_ERR_INVALID_ARG, "M and N must be >= 0");

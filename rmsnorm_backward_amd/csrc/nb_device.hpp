@@ -3,12 +3,15 @@
 // Kernel A (dx_partials_kernel): one pass over x and dy. For each row it
 // recomputes xhat from the saved statistics, takes the in-row sums
 // sum_j(dy*gamma) (LayerNorm only) and sum_j(dy*gamma*xhat), writes dx, and
-// adds dy*xhat (and dy) into per-lane fp32 accumulators. Each workgroup owns
-// whole row groups (disjoint contiguous row blocks) and stores one partial
-// row per group into the workspace. This is the disjoint-block, register-
-// accumulated partial scheme of "Norm backward in Triton -- the dγ/dβ
-// reduction", section "2 · grouped partial buffers + a tiny reduce kernel",
-// without its atomics.
+// adds dy*xhat (and dy) into per-lane fp32 accumulators. Workgroup g owns row
+// group g -- the rows r with r mod G == g -- processes them in ascending
+// order and stores one partial row per group into the workspace. No two
+// workgroups ever write the same slot, so there are no atomics: this is the
+// register-accumulated disjoint-row partial scheme of "Norm backward in
+// Triton -- the dγ/dβ reduction", section "2 · grouped partial buffers + a
+// tiny reduce kernel", without its atomics. Interleaving the groups (rather
+// than giving each a contiguous block) makes all workgroups sweep one
+// address window together, which the HBM sustains measurably better.
 //
 // Kernel B (reduce_partials_kernel): column tiles of 64 features; 16 waves
 // each sum a fixed contiguous slice of the groups in ascending order, then
@@ -37,6 +40,8 @@ struct TBF16 { static constexpr int kBytes = 2; };
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <class Tg> __device__ __forceinline__ float lo16_to_f32(uint32_t w);
 template <class Tg> __device__ __forceinline__ float hi16_to_f32(uint32_t w);
@@ -84,12 +89,13 @@ struct Pack {
 #pragma unroll
     for (int i = 0; i < kWords; ++i) w[i] = 0u;
   }
+  // Plain loads/stores (cached): gamma and anything read again soon.
   __device__ __forceinline__ void load(const void* p) {
     if constexpr (kBytes == 16) {
-      uint4 t = *reinterpret_cast<const uint4*>(p);
+      const u32x4 t = *reinterpret_cast<const u32x4*>(p);
       w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
     } else if constexpr (kBytes == 8) {
-      uint2 t = *reinterpret_cast<const uint2*>(p);
+      const u32x2 t = *reinterpret_cast<const u32x2*>(p);
       w[0] = t.x; w[1] = t.y;
     } else if constexpr (kBytes == 4) {
       w[0] = *reinterpret_cast<const uint32_t*>(p);
@@ -97,15 +103,32 @@ struct Pack {
       w[0] = *reinterpret_cast<const uint16_t*>(p);
     }
   }
-  __device__ __forceinline__ void store(void* p) const {
+  // Streaming loads/stores for data touched exactly once (x, dy, dx): the
+  // non-temporal hint keeps them from displacing reused lines in the caches.
+  __device__ __forceinline__ void load_stream(const void* p) {
     if constexpr (kBytes == 16) {
-      *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+      const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+      w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
     } else if constexpr (kBytes == 8) {
-      *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+      const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+      w[0] = t.x; w[1] = t.y;
     } else if constexpr (kBytes == 4) {
-      *reinterpret_cast<uint32_t*>(p) = w[0];
+      w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
     } else {
-      *reinterpret_cast<uint16_t*>(p) = (uint16_t)w[0];
+      w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+    }
+  }
+  __device__ __forceinline__ void store_stream(void* p) const {
+    if constexpr (kBytes == 16) {
+      const u32x4 t = {w[0], w[1], w[2], w[3]};
+      __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p));
+    } else if constexpr (kBytes == 8) {
+      const u32x2 t = {w[0], w[1]};
+      __builtin_nontemporal_store(t, reinterpret_cast<u32x2*>(p));
+    } else if constexpr (kBytes == 4) {
+      __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t*>(p));
+    } else {
+      __builtin_nontemporal_store((uint16_t)w[0], reinterpret_cast<uint16_t*>(p));
     }
   }
   // element v as fp32 (exact widening)
@@ -144,6 +167,18 @@ __device__ __forceinline__ void keep_packed(Pack<Tg, VEC> (&p)[C]) {
     for (int i = 0; i < Pack<Tg, VEC>::kWords; ++i) asm volatile("" : "+v"(p[c].w[i]));
 }
 
+// Same for fp32 values: they must be materialised here (so work that feeds
+// them cannot be deferred past this point, keeping its inputs alive).
+template <int NA, int C, int VEC>
+__device__ __forceinline__ void pin(float (&a)[NA][C][VEC]) {
+#pragma unroll
+  for (int i = 0; i < NA; ++i)
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) asm volatile("" : "+v"(a[i][c][v]));
+}
+
 // ---------------------------------------------------------------- wave sums
 // Butterfly over 16 lanes with DPP (lane^1, lane^2, mirror in 8, mirror in
 // 16): afterwards every lane of a 16-lane row holds that row's sum, bitwise
@@ -176,7 +211,150 @@ constexpr int kMaxWaves = 16;
 template <int VEC, int C>
 constexpr int max_threads_for() { return VEC * C > 16 ? 512 : 1024; }
 
+// Rows of x/dy held in registers per wave (a ring: D - 1 rows in flight
+// while one is processed), sized by the bytes each lane holds per operand and
+// the register budget the launch bound leaves (128 VGPRs at 1024 threads,
+// 256 at 512): 32 B -> 3 rows; 64 B -> 2 rows within 256 VGPRs; otherwise 1
+// (no prefetch).
+template <class Tg, int VEC, int C>
+constexpr int prefetch_depth() {
+  constexpr int bytes = VEC * C * Tg::kBytes;
+  return max_threads_for<VEC, C>() == 1024 ? (bytes <= 32 ? 3 : 1) : (bytes <= 64 ? 2 : 1);
+}
+
 // ---------------------------------------------------------------- kernel A
+// A zero the compiler cannot see through (it lives in a vector register).
+// Adding it to the index of a per-row statistic keeps that load on the vector
+// memory path, in issue order with the row's x/dy loads. A scalar load there
+// would be worse: scalar loads return out of order, so every use of one waits
+// for all scalar loads in flight -- including those issued for the rows being
+// prefetched -- and every LDS wait before a barrier would wait for them too.
+__device__ __forceinline__ int opaque_lane_zero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+
+// One row's operands as they come from memory, plus its saved statistics.
+template <class Tg, int VEC, int C>
+struct RowBuf {
+  Pack<Tg, VEC> x[C], dy[C];
+  float mu, rs;
+};
+
+// Issue the loads of row r into b. Nothing is loaded for an inactive row or
+// for a lane's chunks past the row's end; process_row never reads those
+// registers (it skips exactly the same cases).
+template <int KIND, class Tg, int VEC, int C>
+__device__ __forceinline__ void fetch_row(RowBuf<Tg, VEC, C>& b, const char* __restrict__ x,
+                                          const char* __restrict__ dy,
+                                          const float* __restrict__ mean,
+                                          const float* __restrict__ rstd, int64_t r, bool active,
+                                          int N, int col0, int cstride) {
+  constexpr int EB = Tg::kBytes;
+  if (active) {
+    const int64_t rz = r + opaque_lane_zero();
+    b.rs = rstd[rz];
+    b.mu = (KIND == kLayerNorm) ? mean[rz] : 0.0f;
+    const int64_t rb = r * (int64_t)N;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int col = col0 + c * cstride;
+      if (col < N) {
+        b.x[c].load_stream(x + (rb + col) * EB);
+        b.dy[c].load_stream(dy + (rb + col) * EB);
+      }
+    }
+  }
+}
+
+// Everything kernel A does with one row once its operands are in registers.
+// With xc = x - mean (RMSNorm: xc = x), xhat = xc * rstd and dyhat = dy * gamma:
+//   pass 1: s1 = sum_j dyhat (LayerNorm only), s2 = sum_j dyhat * xc, and the
+//           row's weight-gradient terms dy * xhat = (dy * xc) * rstd and dy go
+//           into the lane's accumulators (an inactive row holds zeros and
+//           adds exact zeros);
+//   the sums are completed across the wave (butterfly) and across the S
+//   waves of the row (LDS), then
+//   pass 2: dx = rstd * (dyhat - mean(dyhat) - xhat * mean(dyhat * xhat))
+//              = dyhat * rstd + xc * c2 + c1,
+//           with the per-row constants mean(dyhat * xhat) = rstd * s2 / N,
+//           c2 = -rstd^2 * mean(dyhat * xhat) and c1 = -rstd * s1 / N.
+template <int KIND, class Tg, int VEC, int C, int NACC>
+__device__ __forceinline__ void process_row(RowBuf<Tg, VEC, C>& b, const float (&gam)[C][VEC],
+                                            float (&acc)[NACC][C][VEC], char* __restrict__ dx,
+                                            float (*red)[kMaxWaves][2], int& phase, int64_t r,
+                                            bool active, int N, float inv_n, int col0, int cstride,
+                                            int lane, int wave, int S, int p) {
+  constexpr int EB = Tg::kBytes;
+  float s1 = 0.0f, s2 = 0.0f;
+  if (active) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      if (col0 + c * cstride < N) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          const float xc = b.x[c].get(v) - b.mu;
+          const float dyv = b.dy[c].get(v);
+          const float dyh = dyv * gam[c][v];
+          if (KIND == kLayerNorm) s1 += dyh;
+          s2 = __builtin_fmaf(dyh, xc, s2);
+          acc[0][c][v] = __builtin_fmaf(dyv * xc, b.rs, acc[0][c][v]);
+          if (NACC == 2) acc[NACC - 1][c][v] += dyv;
+        }
+      }
+    }
+  }
+  pin(acc);
+  keep_packed(b.x);
+  keep_packed(b.dy);
+  s2 = wave_sum(s2);
+  if (KIND == kLayerNorm) s1 = wave_sum(s1);
+  if (S > 1) {
+    const int buf = phase & 1;
+    if (lane == 0) {
+      red[buf][wave][0] = s1;
+      red[buf][wave][1] = s2;
+    }
+    __syncthreads();
+    // lane q < S fetches slice q's pair in one LDS read; the S pairs are then
+    // added in slice order 0, 1, ..., S-1 from scalar copies
+    float2 mine = make_float2(0.0f, 0.0f);
+    if (lane < S) mine = *reinterpret_cast<const float2*>(&red[buf][p * S + lane][0]);
+    const int m1b = __builtin_bit_cast(int, mine.x), m2b = __builtin_bit_cast(int, mine.y);
+    float t1 = 0.0f, t2 = 0.0f;
+    for (int q = 0; q < S; ++q) {
+      t1 += __builtin_bit_cast(float, __builtin_amdgcn_readlane(m1b, q));
+      t2 += __builtin_bit_cast(float, __builtin_amdgcn_readlane(m2b, q));
+    }
+    s1 = t1;
+    s2 = t2;
+  }
+  ++phase;
+  if (active) {
+    const float m2 = s2 * inv_n * b.rs;  // mean_j(dyhat * xhat)
+    const float c2 = -(b.rs * b.rs) * m2;
+    const float c1 = (KIND == kLayerNorm) ? -b.rs * (s1 * inv_n) : 0.0f;
+    const int64_t rb = r * (int64_t)N;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int col = col0 + c * cstride;
+      if (col < N) {
+        float o[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          const float xc = b.x[c].get(v) - b.mu;
+          const float dyh = b.dy[c].get(v) * gam[c][v];
+          o[v] = __builtin_fmaf(dyh, b.rs, __builtin_fmaf(xc, c2, c1));
+        }
+        Pack<Tg, VEC> out;
+        out.set(o);
+        out.store_stream(dx + (rb + col) * EB);
+      }
+    }
+  }
+}
+
 template <int KIND, class Tg, int VEC, int C, int NACC>
 __global__ __launch_bounds__((max_threads_for<VEC, C>()))
 void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dyv,
@@ -185,13 +363,14 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
                         float* __restrict__ ws, int64_t M, int N, int64_t G, int64_t R,
                         int S, int P) {
   using PK = Pack<Tg, VEC>;
+  using RB = RowBuf<Tg, VEC, C>;
   constexpr int EB = Tg::kBytes;
   const char* __restrict__ x = static_cast<const char*>(xv);
   const char* __restrict__ dy = static_cast<const char*>(dyv);
   const char* __restrict__ gm = static_cast<const char*>(gv);
   char* __restrict__ dx = static_cast<char*>(dxv);
 
-  __shared__ float red[2][kMaxWaves][2];
+  __shared__ __align__(8) float red[2][kMaxWaves][2];
   extern __shared__ float comb[];
 
   const int lane = threadIdx.x & 63;
@@ -200,22 +379,28 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
   const int p = wave / S;         // which of the P rows in flight
   const int cstride = S * 64 * VEC;
   const int col0 = (s * 64 + lane) * VEC;
-  const float fN = (float)N;
+  const float inv_n = 1.0f / (float)N;
 
-  // gamma for this lane's columns, kept packed in registers for every row
-  PK gam[C];
+  // gamma for this lane's columns, widened to fp32 once and kept in registers
+  float gam[C][VEC];
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     const int col = col0 + c * cstride;
-    if (col < N) gam[c].load(gm + (int64_t)col * EB);
-    else gam[c].zero();
+    PK t;
+    if (col < N) t.load(gm + (int64_t)col * EB);
+    else t.zero();
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) gam[c][v] = t.get(v);
   }
 
   int phase = 0;  // parity of the row-sum exchange buffer (S > 1)
   for (int64_t g = blockIdx.x; g < G; g += gridDim.x) {
-    const int64_t r0 = g * R;
-    const int64_t r1 = (r0 + R < M) ? r0 + R : M;
-    const int iters = (int)((r1 - r0 + P - 1) / P);
+    // group g holds rows g, g + G, g + 2G, ...; row-lane p of the workgroup
+    // takes every P-th of them, so iteration k of row-lane p is row
+    // g + (k*P + p)*G. Every wave runs the same number of iterations.
+    const int64_t rows = (M - g + G - 1) / G;
+    const int iters = (int)((rows + P - 1) / P);
+    auto row_of = [&](int k) { return g + ((int64_t)k * P + p) * G; };
 
     float acc[NACC][C][VEC];
 #pragma unroll
@@ -225,86 +410,31 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
 #pragma unroll
         for (int v = 0; v < VEC; ++v) acc[a][c][v] = 0.0f;
 
-    for (int it = 0; it < iters; ++it, ++phase) {
-      const int64_t r = r0 + (int64_t)it * P + p;
-      const bool active = r < r1;  // uniform over the wave
-      keep_packed(gam);
-      PK xr[C], dr[C];
-      float mu = 0.0f, rs = 0.0f;
-      if (active) {
-        rs = rstd[r];
-        if (KIND == kLayerNorm) mu = mean[r];
-        const int64_t rb = r * (int64_t)N;
+    // Ring of D row buffers: the loads of row k + D - 1 are issued before
+    // row k is processed, so each wave keeps D - 1 rows of x and dy in flight
+    // while it computes.
+    constexpr int D = prefetch_depth<Tg, VEC, C>();
+    RB buf[D];
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-          const int col = col0 + c * cstride;
-          if (col < N) {
-            xr[c].load(x + (rb + col) * EB);
-            dr[c].load(dy + (rb + col) * EB);
-          } else {
-            xr[c].zero();
-            dr[c].zero();
-          }
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < C; ++c) { xr[c].zero(); dr[c].zero(); }
+    for (int k = 0; k < D - 1; ++k) {
+      if (k < iters) {
+        const int64_t rk = row_of(k);
+        fetch_row<KIND>(buf[k], x, dy, mean, rstd, rk, rk < M, N, col0, cstride);
       }
-
-      // in-row sums: s1 = sum(dyhat) (LayerNorm), s2 = sum(dyhat * xhat)
-      float s1 = 0.0f, s2 = 0.0f;
+    }
+    for (int it = 0; it < iters; it += D) {
 #pragma unroll
-      for (int c = 0; c < C; ++c)
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-          const float xh = (xr[c].get(v) - mu) * rs;
-          const float dyh = dr[c].get(v) * gam[c].get(v);
-          if (KIND == kLayerNorm) s1 += dyh;
-          s2 = __builtin_fmaf(dyh, xh, s2);
+      for (int d = 0; d < D; ++d) {
+        const int k = it + d;
+        if (k + D - 1 < iters) {
+          const int64_t rf = row_of(k + D - 1);
+          fetch_row<KIND>(buf[(d + D - 1) % D], x, dy, mean, rstd, rf, rf < M, N, col0,
+                          cstride);
         }
-      keep_packed(xr);
-      keep_packed(dr);
-      keep_packed(gam);
-      s2 = wave_sum(s2);
-      if (KIND == kLayerNorm) s1 = wave_sum(s1);
-      if (S > 1) {
-        const int buf = phase & 1;
-        if (lane == 0) {
-          red[buf][wave][0] = s1;
-          red[buf][wave][1] = s2;
-        }
-        __syncthreads();
-        float t1 = 0.0f, t2 = 0.0f;
-        for (int q = 0; q < S; ++q) {
-          t1 += red[buf][p * S + q][0];
-          t2 += red[buf][p * S + q][1];
-        }
-        s1 = t1;
-        s2 = t2;
-      }
-
-      if (active) {
-        const float m2 = s2 / fN;
-        const float m1 = (KIND == kLayerNorm) ? s1 / fN : 0.0f;
-        const int64_t rb = r * (int64_t)N;
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-          const int col = col0 + c * cstride;
-          if (col < N) {
-            float o[VEC];
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) {
-              const float dyv_ = dr[c].get(v);
-              const float xh = (xr[c].get(v) - mu) * rs;
-              const float dyh = dyv_ * gam[c].get(v);
-              o[v] = (dyh - m1 - xh * m2) * rs;
-              acc[0][c][v] = __builtin_fmaf(dyv_, xh, acc[0][c][v]);
-              if (NACC == 2) acc[NACC - 1][c][v] += dyv_;
-            }
-            PK out;
-            out.set(o);
-            out.store(dx + (rb + col) * EB);
-          }
+        if (k < iters) {
+          const int64_t rk = row_of(k);
+          process_row<KIND>(buf[d], gam, acc, dx, red, phase, rk, rk < M, N, inv_n, col0,
+                            cstride, lane, wave, S, p);
         }
       }
     }
@@ -361,6 +491,7 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
 // ---------------------------------------------------------------- kernel B
 constexpr int kReduceWaves = 16;
 constexpr int kReduceCols = 64;
+constexpr int kReduceUnroll = 8;
 
 template <class OutT> __device__ __forceinline__ void store_out(void* p, int j, float v);
 template <> __device__ __forceinline__ void store_out<TF32>(void* p, int j, float v) {
@@ -373,6 +504,10 @@ template <> __device__ __forceinline__ void store_out<TBF16>(void* p, int j, flo
   static_cast<uint16_t*>(p)[j] = pack1<TBF16>(v);
 }
 
+// Lane = feature (each wave load reads 256 contiguous bytes of one partial
+// row); wave q sums groups [q*G/16, (q+1)*G/16) in ascending order, issuing
+// kReduceUnroll loads before adding them in order; wave 0 then adds the 16
+// slice sums in slice order.
 template <class OutT>
 __global__ __launch_bounds__(kReduceWaves * 64)
 void reduce_partials_kernel(const float* __restrict__ ws, int64_t G, int N,
@@ -388,12 +523,12 @@ void reduce_partials_kernel(const float* __restrict__ ws, int64_t G, int N,
   float sum = 0.0f;
   if (col < N) {
     int64_t g = lo;
-    for (; g + 8 <= hi; g += 8) {
-      float t[8];
+    for (; g + kReduceUnroll <= hi; g += kReduceUnroll) {
+      float t[kReduceUnroll];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) t[k] = src[(g + k) * (int64_t)N + col];
+      for (int k = 0; k < kReduceUnroll; ++k) t[k] = src[(g + k) * (int64_t)N + col];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) sum += t[k];
+      for (int k = 0; k < kReduceUnroll; ++k) sum += t[k];
     }
     for (; g < hi; ++g) sum += src[g * (int64_t)N + col];
   }

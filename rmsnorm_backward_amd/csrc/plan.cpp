@@ -10,12 +10,19 @@
 namespace nb {
 
 namespace {
-constexpr int64_t kAutoGroupTarget = 512;  // row blocks per call (see auto_groups)
+constexpr int64_t kTargetWaves = 2048;  // waves in flight the group count aims at
+constexpr int64_t kMinRowsPerGroup = 8;
 constexpr int64_t kMaxGrid = 1 << 20;
 constexpr int kMaxLdsBytes = 65536 - 1024;  // dynamic LDS; the kernel adds 256 B static
-constexpr int kTargetThreads = 256;
+constexpr int kTargetThreads = 512;
+constexpr int kPreferredLaneElems = 16;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int fail(const char** why, const char* msg, int status) {
+  if (why) *why = msg;
+  return status;
+}
 }  // namespace
 
 int dtype_bytes(int dtype) {
@@ -42,17 +49,73 @@ bool kernel_a_exists(int io_dtype, int vec_full, int with_dbeta, int chunks) {
 
 int kernel_a_max_threads(int lane_elems) { return lane_elems > 16 ? 512 : 1024; }
 
-int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype) {
-  (void)kind; (void)N; (void)io_dtype;
-  if (M <= 0) return 0;
-  const int64_t target = M < kAutoGroupTarget ? M : kAutoGroupTarget;
-  const int64_t R = ceil_div(M, target);
-  return ceil_div(M, R);
+// Lane layout of kernel A for rows of N elements (fills vec, chunks,
+// waves_per_row, rows_in_flight, threads, lds_bytes of *p).
+int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok16,
+                  norm_bwd_plan_t* p, const char** why) {
+  (void)kind;
+  const int eb = dtype_bytes(io_dtype);
+  const int nacc = with_dbeta ? 2 : 1;
+  const int vw = 16 / eb;
+  const int full = (vec_ok16 && N % vw == 0) ? 1 : 0;
+  p->vec = full ? vw : 1;
+  if (N == 0) {  // a minimal valid geometry
+    p->chunks = 1;
+    p->waves_per_row = 1;
+    p->rows_in_flight = 1;
+    p->threads = 64;
+    p->lds_bytes = 0;
+    return NORM_BWD_OK;
+  }
+  const int64_t max_n = !full ? NORM_BWD_MAX_N_UNALIGNED
+                       : eb == 4 ? NORM_BWD_MAX_N_F32
+                       : with_dbeta ? NORM_BWD_MAX_N_16BIT_DBETA : NORM_BWD_MAX_N_16BIT;
+  if (N > max_n) return fail(why, "N exceeds the fused path's limit", NORM_BWD_ERR_UNSUPPORTED);
+
+  // Prefer at most kPreferredLaneElems elements per lane (the pipelined
+  // kernel holds three rows of them in registers), then the smallest S (fewer
+  // waves coupled by a barrier per row), then the smallest C. Wider lanes are
+  // used only when nothing narrower covers N.
+  int S = 0, C = 0;
+  for (int pass = 0; pass < 2 && !S; ++pass) {
+    for (int s = 1; s <= 16 && !S; s *= 2) {
+      for (int c = 1; c <= 8; c *= 2) {
+        if (!kernel_a_exists(io_dtype, full, with_dbeta, c)) continue;
+        if (pass == 0 && p->vec * c > kPreferredLaneElems) continue;
+        if (s * 64 > kernel_a_max_threads(p->vec * c)) continue;
+        if ((int64_t)s * 64 * p->vec * c >= N) { S = s; C = c; break; }
+      }
+    }
+  }
+  if (!S) return fail(why, "no kernel geometry covers N", NORM_BWD_ERR_UNSUPPORTED);
+  int P = kTargetThreads / (64 * S);
+  if (P < 1) P = 1;
+  while (P > 1 && S * P * 64 > kernel_a_max_threads(p->vec * C)) P /= 2;
+  int lds = nacc * S * C * 64 * p->vec * 4;
+  if (P == 1 || lds > kMaxLdsBytes) { P = 1; lds = 0; }
+  p->chunks = C;
+  p->waves_per_row = S;
+  p->rows_in_flight = P;
+  p->threads = 64 * S * P;
+  p->lds_bytes = lds;
+  return NORM_BWD_OK;
 }
 
-static int fail(const char** why, const char* msg, int status) {
-  if (why) *why = msg;
-  return status;
+int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype) {
+  if (M <= 0) return 0;
+  // Enough workgroups for about kTargetWaves waves in flight (8 per compute
+  // unit on a 256-CU part), never fewer than kMinRowsPerGroup rows per
+  // group. The geometry is itself a function of (kind, N, io_dtype), so the
+  // group count depends on the problem only, never on the device.
+  norm_bwd_plan_t g;
+  const char* why = nullptr;
+  int waves = 8;
+  if (N > 0 && make_geometry(kind, N, io_dtype, 0, true, &g, &why) == NORM_BWD_OK)
+    waves = g.threads / 64;
+  int64_t G = kTargetWaves / waves;
+  const int64_t cap = ceil_div(M, kMinRowsPerGroup);
+  if (G > cap) G = cap;
+  return G < 1 ? 1 : G;
 }
 
 int make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,
@@ -76,50 +139,20 @@ int make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,
   p.N = N;
   const int nacc = with_dbeta ? 2 : 1;
 
-  const int vw = 16 / eb;
-  const int full = (vec_ok16 && N % vw == 0) ? 1 : 0;
-  p.vec = full ? vw : 1;
-
-  if (N == 0) {  // nothing to compute; keep a minimal valid geometry
-    p.chunks = 1;
-    p.waves_per_row = 1;
-    p.rows_in_flight = 1;
-    p.threads = 64;
+  const char* gwhy = nullptr;
+  const int st = make_geometry(kind, N, io_dtype, with_dbeta, vec_ok16, &p, &gwhy);
+  if (st != NORM_BWD_OK) return fail(why, gwhy, st);
+  if (N == 0) {  // nothing to compute
     *plan = p;
     return NORM_BWD_OK;
   }
-  const int64_t max_n = !full ? NORM_BWD_MAX_N_UNALIGNED
-                       : eb == 4 ? NORM_BWD_MAX_N_F32
-                       : with_dbeta ? NORM_BWD_MAX_N_16BIT_DBETA : NORM_BWD_MAX_N_16BIT;
-  if (N > max_n) return fail(why, "N exceeds the fused path's limit", NORM_BWD_ERR_UNSUPPORTED);
-
-  // Smallest S (waves sharing a row: fewer barriers), then smallest C.
-  int S = 0, C = 0;
-  for (int s = 1; s <= 16 && !S; s *= 2) {
-    for (int c = 1; c <= 8; c *= 2) {
-      if (!kernel_a_exists(io_dtype, full, with_dbeta, c)) continue;
-      if (s * 64 > kernel_a_max_threads(p.vec * c)) continue;
-      if ((int64_t)s * 64 * p.vec * c >= N) { S = s; C = c; break; }
-    }
-  }
-  if (!S) return fail(why, "no kernel geometry covers N", NORM_BWD_ERR_UNSUPPORTED);
-  int P = kTargetThreads / (64 * S);
-  if (P < 1) P = 1;
-  while (P > 1 && S * P * 64 > kernel_a_max_threads(p.vec * C)) P /= 2;
-  int lds = nacc * S * C * 64 * p.vec * 4;
-  if (P == 1 || lds > kMaxLdsBytes) { P = 1; lds = 0; }
-  p.chunks = C;
-  p.waves_per_row = S;
-  p.rows_in_flight = P;
-  p.threads = 64 * S * P;
-  p.lds_bytes = lds;
 
   if (M > 0) {
-    int64_t target = groups ? groups : auto_groups(kind, M, N, io_dtype);
-    if (target > M) target = M;
-    p.rows_per_group = ceil_div(M, target);
-    p.groups = ceil_div(M, p.rows_per_group);
-    p.grid = (int32_t)(p.groups < kMaxGrid ? p.groups : kMaxGrid);
+    int64_t G = groups ? groups : auto_groups(kind, M, N, io_dtype);
+    if (G > M) G = M;  // every group holds at least one row
+    p.groups = G;
+    p.rows_per_group = ceil_div(M, G);
+    p.grid = (int32_t)(G < kMaxGrid ? G : kMaxGrid);
   } else {
     p.rows_per_group = 1;
     p.groups = 0;
@@ -167,11 +200,10 @@ int validate_plan(const norm_bwd_plan_t* p, const char** why) {
     if (p->groups != 0) return fail(why, "plan.groups must be 0 when M = 0", NORM_BWD_ERR_INVALID_ARG);
     return NORM_BWD_OK;
   }
-  if (p->groups < 1 || p->rows_per_group < 1)
-    return fail(why, "plan.groups and rows_per_group must be >= 1", NORM_BWD_ERR_INVALID_ARG);
-  if (p->groups * p->rows_per_group < p->M || (p->groups - 1) * p->rows_per_group >= p->M)
-    return fail(why, "plan.groups * rows_per_group must cover M with no empty group",
-                NORM_BWD_ERR_INVALID_ARG);
+  if (p->groups < 1 || p->groups > p->M)
+    return fail(why, "plan.groups must be in [1, M]", NORM_BWD_ERR_INVALID_ARG);
+  if (p->rows_per_group != ceil_div(p->M, p->groups))
+    return fail(why, "plan.rows_per_group must be ceil(M / groups)", NORM_BWD_ERR_INVALID_ARG);
   if (p->grid < 1 || p->grid > p->groups || p->grid > kMaxGrid)
     return fail(why, "plan.grid must be in [1, groups]", NORM_BWD_ERR_INVALID_ARG);
   return NORM_BWD_OK;

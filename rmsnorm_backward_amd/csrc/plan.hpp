@@ -21,6 +21,11 @@ bool kernel_a_exists(int io_dtype, int vec_full, int with_dbeta, int chunks);
 // Largest workgroup kernel A accepts for vec * chunks elements per lane.
 int kernel_a_max_threads(int lane_elems);
 
+// Kernel A lane layout for rows of N elements (vec, chunks, waves_per_row,
+// rows_in_flight, threads, lds_bytes of *plan). Returns a status.
+int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok16,
+                  norm_bwd_plan_t* plan, const char** why);
+
 // Automatic group count for (kind, M, N, io_dtype): independent of the device.
 int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype);
 

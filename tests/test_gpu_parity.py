@@ -125,8 +125,9 @@ def test_full_size_sampled(nb, w):
     print(f"[run] {w.name} plan={plan.as_dict()}", flush=True)
     dx_g, dg_g, db_g = run(nb, w, g)
     del g
-    R = plan.rows_per_group
-    extra = [k * R + d for k in (1, plan.groups // 2, plan.groups - 1) for d in (-1, 0)]
+    G = plan.groups   # group g = rows r with r % G == g: sample both ends of a sweep
+    extra = [k * G + d for k in (1, plan.rows_per_group // 2, plan.rows_per_group - 1)
+             for d in (-1, 0, 1)]
     rows = W.sample_rows(w.M, 48, seed=w.seed, extra=extra)
     mean = inp.get("mean")
     rdx = oracle.bwd_dx(w.kind, inp["x"][rows], inp["dy"][rows], inp["gamma"],
@@ -344,6 +345,25 @@ def test_two_phase_api_matches_full_call(nb):
     torch.cuda.synchronize()
     assert torch.equal(dx.cpu(), full[0])
     assert torch.equal(dg.cpu(), full[1]) and torch.equal(db.cpu(), full[2])
+
+
+@pytest.mark.parametrize("wdt", [torch.float16, torch.bfloat16, torch.float32])
+def test_two_phase_reduce_output_dtypes(nb, wdt):
+    """Kernel B alone rounds the same fp32 sums to any output type."""
+    w = W.scaled(W.LN_F16_1151x8192, M=333, N=1000)
+    g = to_gpu(W.make_inputs(w))
+    plan = nb.norm_bwd_make_plan("layernorm", w.M, w.N, w.io_dtype, True)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    dx = torch.empty_like(g["x"])
+    nb.norm_bwd_execute_partials(plan, g["x"], g["dy"], g["gamma"], g["mean"], g["rstd"], dx, ws)
+    ref_g = torch.empty(w.N, device="cuda")
+    ref_b = torch.empty(w.N, device="cuda")
+    nb.norm_bwd_reduce_partials(plan.groups, w.N, ws, ref_g, ref_b)
+    dg = torch.empty(w.N, dtype=wdt, device="cuda")
+    db = torch.empty(w.N, dtype=wdt, device="cuda")
+    nb.norm_bwd_reduce_partials(plan.groups, w.N, ws, dg, db)
+    torch.cuda.synchronize()
+    assert torch.equal(dg.cpu(), ref_g.cpu().to(wdt)) and torch.equal(db.cpu(), ref_b.cpu().to(wdt))
 
 
 def test_empty_problems(nb):

@@ -64,12 +64,13 @@ def test_status_strings(nb):
     assert nb.norm_bwd_status_string(99) == "NORM_BWD_ERR_UNKNOWN"
 
 
-def _auto_groups(M):
+def _auto_groups(nb, kind, M, N, dt):
+    """The documented rule: about 2048 waves in flight, >= 8 rows per group,
+    where the waves per workgroup come from the (dbeta-less) geometry."""
     if M == 0:
         return 0
-    t = min(M, 512)
-    R = -(-M // t)
-    return -(-M // R)
+    waves = nb.norm_bwd_make_plan(kind, 1, N, dt, False).threads // 64 if N else 8
+    return max(1, min(2048 // waves, -(-M // 8)))
 
 
 @pytest.mark.parametrize("kind,M,N,dt,db", [
@@ -84,7 +85,7 @@ def _auto_groups(M):
 ])
 def test_workspace_bytes_rule(nb, kind, M, N, dt, db):
     got = nb.norm_bwd_workspace_bytes(kind, M, N, dt, db)
-    assert got == (2 if db else 1) * _auto_groups(M) * N * 4
+    assert got == (2 if db else 1) * _auto_groups(nb, kind, M, N, dt) * N * 4
     plan = nb.norm_bwd_make_plan(kind, M, N, dt, db)
     assert plan.workspace_bytes == got
 
@@ -118,12 +119,12 @@ def test_plan_invariants(nb, kind, dt, M, N, db, groups):
     assert S * 64 * vec * C >= N                       # the lanes cover the row
     assert p.threads == 64 * S * P and 1 <= S * P <= 16
     assert C in (1, 2, 4, 8)
-    assert p.groups * p.rows_per_group >= M            # every row in a group
-    assert (p.groups - 1) * p.rows_per_group < M       # no empty group
+    assert 1 <= p.groups <= M                          # no empty group
+    assert p.rows_per_group == -(-M // p.groups)       # largest group
     if groups:
-        assert p.groups <= groups
+        assert p.groups == min(groups, M)
     else:
-        assert p.groups == _auto_groups(M)
+        assert p.groups == _auto_groups(nb, kind, M, N, dt)
     assert 1 <= p.grid <= p.groups
     nacc = 2 if db else 1
     assert p.workspace_bytes == nacc * p.groups * N * 4
@@ -263,6 +264,7 @@ def test_reduce_and_probe_reject(nb):
     assert lib.norm_bwd_reduce_partials(4, 8, 0, _addr(0), 16, _addr(1), None, None) == 3
     assert lib.norm_bwd_reduce_partials(4, 8, 0, _addr(0), 1 << 20, None, None, None) == 1
     assert lib.norm_bwd_reduce_partials(4, 8, 5, _addr(0), 1 << 20, _addr(1), None, None) == 2
+    assert lib.norm_bwd_reduce_partials(4, 8, 1, _addr(0), 16, _addr(1), None, None) == 3
     assert lib.norm_bwd_probe_copy(_addr(0), _addr(1), 17, None) == 1
     assert lib.norm_bwd_probe_copy(_addr(0), ctypes.c_void_p(B + 8), 1024, None) == 1
 
