@@ -252,6 +252,7 @@ def main(argv=None) -> int:
             "rows_per_s": round(w.M / (ms * 1e-3), 1),
             "kernel_a_us": round(ms_a * 1e3, 3), "kernel_b_us": round(ms_b * 1e3, 3),
             "copy_probe_GBps": round(copy_gbps, 1),
+            "copy_probe_bytes": cp_bytes,
             "pct_of_copy_probe": round(100 * value / copy_gbps, 2),
             "buffer_sets": nsets,
             "workspace_bytes": plan.workspace_bytes,

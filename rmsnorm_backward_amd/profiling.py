@@ -1,0 +1,162 @@
+"""Summaries of rocprofv3 output for the profiles/ directory.
+
+Two summaries, each a short Markdown text that records the exact commands
+that produced it:
+
+* ``stats``: per-kernel durations from ``rocprofv3 --kernel-trace --stats``
+  (kernel_stats.csv), next to the kernel-A time the benchmark measured with
+  HIP events in the same run (its JSON line), so the two can be compared.
+
+* ``pmc``: HBM traffic of kernel A from two counter runs, ``--pmc
+  FETCH_SIZE`` and ``--pmc WRITE_SIZE`` (counter_collection.csv, KiB per
+  dispatch). Each counter is calibrated on the benchmark's plain copy kernel
+  of known size in the same run: scale = bytes the copy moves / bytes the
+  counter reports for it. The summary carries the kernel source hash, so the
+  benchmark reports the traffic only while the kernel is unchanged.
+
+Usage:
+  python -m rmsnorm_backward_amd.profiling stats KERNEL_STATS_CSV BENCH_JSON --cmd "..."
+  python -m rmsnorm_backward_amd.profiling pmc FETCH_CSV WRITE_CSV BENCH_JSON --cmd "..." --cmd "..."
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+KERNEL_A = "dx_partials_kernel"
+KERNEL_B = "reduce_partials_kernel"
+COPY = "copy_probe_kernel"
+_HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCE = os.path.join(_HERE, "csrc", "nb_device.hpp")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _bench(path):
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("{"):
+                return json.loads(line)
+    raise ValueError(f"no JSON line in {path}")
+
+
+def stats_summary(stats_csv: str, bench_json: str, cmds) -> str:
+    rows = list(csv.DictReader(open(stats_csv)))
+    b = _bench(bench_json)
+    c = b["config"]
+    out = [f"# Kernel durations: {c['workload']}", "",
+           "Commands (run from the repository root on one MI355X):", "", "```"]
+    out += list(cmds) + ["```", "",
+                         "| kernel | calls | average (us) | min (us) | max (us) | share |",
+                         "|---|---|---|---|---|---|"]
+    avg_a = None
+    for r in rows:
+        name = r["Name"]
+        short = name.split("(")[0].replace("void ", "")
+        avg = float(r["AverageNs"]) / 1e3
+        if KERNEL_A in name:
+            avg_a = avg
+        out.append(f"| `{short}` | {r['Calls']} | {avg:.2f} | {float(r['MinNs'])/1e3:.2f} | "
+                   f"{float(r['MaxNs'])/1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    out += ["", "Benchmark line of the same run (HIP events on the launch stream):", "",
+            f"- step: {b['ms_per_step']*1e3:.2f} us, {b['value']} GB/s ({c['pct_of_peak']}% of 8 TB/s)",
+            f"- kernel A by events: {c['kernel_a_us']} us; kernel B by events: {c['kernel_b_us']} us",
+            f"- plan: {json.dumps(c['plan'])}"]
+    if avg_a is not None:
+        out.append(f"- kernel A by the trace: {avg_a:.2f} us "
+                   f"(events / trace = {c['kernel_a_us'] / avg_a:.3f})")
+    out += ["", f"kernel_source_sha256_16: {kernel_source_hash()}", ""]
+    return "\n".join(out)
+
+
+def _counter_rows(path, counter):
+    rows = list(csv.DictReader(open(path)))
+    per_dispatch = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter:
+            continue
+        key = (r["Dispatch_Id"], r["Kernel_Name"])
+        per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+    return per_dispatch
+
+
+def _mean_for(per_dispatch, needle):
+    vals = [v for (d, name), v in per_dispatch.items() if needle in name]
+    return (statistics.median(vals), len(vals)) if vals else (None, 0)
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, bench_json: str, cmds) -> str:
+    b = _bench(bench_json)
+    c = b["config"]
+    copy_bytes = c["copy_probe_bytes"]
+    f = _counter_rows(fetch_csv, "FETCH_SIZE")
+    w = _counter_rows(write_csv, "WRITE_SIZE")
+    fa, na = _mean_for(f, KERNEL_A)
+    wa, _ = _mean_for(w, KERNEL_A)
+    fc, nc = _mean_for(f, COPY)
+    wc, _ = _mean_for(w, COPY)
+    fb, _ = _mean_for(f, KERNEL_B)
+    wb, _ = _mean_for(w, KERNEL_B)
+    if fa is None or fc is None or wc is None or wa is None:
+        raise ValueError("counter rows for kernel A or the copy kernel are missing")
+    fscale = copy_bytes / (fc * 1024.0)
+    wscale = copy_bytes / (wc * 1024.0)
+    read_bytes = fa * 1024.0 * fscale
+    write_bytes = wa * 1024.0 * wscale
+    alg = b["roofline"]["bytes_per_launch"]
+    alg_read = alg - c["M"] * c["N"] * (2 if c["io_dtype"] != "f32" else 4)
+    alg_write = alg - alg_read
+    ws = c["workspace_bytes"]
+    traffic = int(round(read_bytes + write_bytes))
+    out = [f"# HBM traffic of kernel A: {c['workload']}", "",
+           "Commands (run from the repository root on one MI355X; counters in runs of their own):",
+           "", "```"] + list(cmds) + ["```", "",
+           f"Calibration on the copy kernel ({copy_bytes} bytes read and written per launch,",
+           f"{nc} launches): FETCH_SIZE reads {fc:.1f} KiB -> scale {fscale:.4f}; "
+           f"WRITE_SIZE reads {wc:.1f} KiB -> scale {wscale:.4f}.", "",
+           "| kernel A, per launch | counter (KiB) | scaled bytes | algorithmic bytes | ratio |",
+           "|---|---|---|---|---|",
+           f"| read (FETCH_SIZE) | {fa:.1f} | {read_bytes:.0f} | {alg_read} | {read_bytes/alg_read:.4f} |",
+           f"| write (WRITE_SIZE) | {wa:.1f} | {write_bytes:.0f} | {alg_write} (+{ws} workspace) | "
+           f"{write_bytes/(alg_write + ws):.4f} |",
+           f"| total | | {traffic} | {alg} (+{ws}) | {traffic/(alg + ws):.4f} |", ""]
+    if fb is not None and wb is not None:
+        out.append(f"Kernel B per launch: FETCH_SIZE {fb:.1f} KiB ({fb*1024*fscale:.0f} B), "
+                   f"WRITE_SIZE {wb:.1f} KiB ({wb*1024*wscale:.0f} B); workspace {ws} B.")
+    out += ["", f"kernel A launches counted: {na}",
+            f"traffic_bytes_per_launch: {traffic}",
+            f"kernel_source_sha256_16: {kernel_source_hash()}", ""]
+    return "\n".join(out)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("stats_csv")
+    s.add_argument("bench_json")
+    s.add_argument("--cmd", action="append", default=[])
+    p = sub.add_parser("pmc")
+    p.add_argument("fetch_csv")
+    p.add_argument("write_csv")
+    p.add_argument("bench_json")
+    p.add_argument("--cmd", action="append", default=[])
+    a = ap.parse_args(argv)
+    if a.what == "stats":
+        sys.stdout.write(stats_summary(a.stats_csv, a.bench_json, a.cmd))
+    else:
+        sys.stdout.write(pmc_summary(a.fetch_csv, a.write_csv, a.bench_json, a.cmd))
+
+
+if __name__ == "__main__":
+    main()
