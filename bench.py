@@ -43,8 +43,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0 = auto)")
