@@ -12,6 +12,9 @@ Input/output buffer sets are rotated so that consecutive steps touch
 different memory (the set count makes the rotation exceed the 256 MB
 Infinity Cache several times over): every step streams from HBM.
 
+The saved statistics the backward reads are produced by the library's GPU
+forward; the forward is also timed on its own (config.forward).
+
 Prints ONE JSON line. `value` is algorithmic GB/s of the whole step:
   bytes = read x, dy, gamma, saved stats; write dx, dgamma(, dbeta)
 (workspace traffic excluded). `roofline` is kernel A alone against the
@@ -79,6 +82,14 @@ def kernel_a_bytes(w) -> int:
     return w.M * (3 * w.N * s + stats) + w.N * s
 
 
+def forward_bytes(w, with_beta: bool) -> int:
+    """Algorithmic bytes of one forward launch: x read and y written (2*N*s
+    per row), the statistics written (4 or 8 B per row), gamma (and beta)."""
+    s = w.io_bytes
+    stats = 8 if w.kind == "layernorm" else 4
+    return w.M * (2 * w.N * s + stats) + w.N * s * (2 if with_beta else 1)
+
+
 def time_loop(torch, fn, steps, stream):
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -104,8 +115,10 @@ def cpu_baseline(w, inp):
     x = inp["x"][:rows].double().numpy()
     dy = inp["dy"][:rows].double().numpy()
     gamma = inp["gamma"].double().numpy()
-    rstd = inp["rstd"][:rows].double().numpy()
-    mean = inp["mean"][:rows].double().numpy() if w.kind == "layernorm" else None
+    # the saved statistics: the oracle's forward, rounded to fp32 (untimed)
+    m64, r64 = o.fwd_stats(w.kind, x, w.eps)
+    rstd = r64.astype(np.float32).astype(np.float64)
+    mean = m64.astype(np.float32).astype(np.float64) if w.kind == "layernorm" else None
     # repeat the pass until about 10 s of CPU time has accumulated (at most 200)
     reps, total = 0, 0.0
     while reps < 200 and (total < 10.0 or reps < 1):
@@ -157,11 +170,20 @@ def main(argv=None) -> int:
     set_bytes = 3 * w.M * w.N * w.io_bytes
     nsets = args.sets or max(2, math.ceil(4 * MALL_BYTES / max(set_bytes, 1)))
     nsets = min(nsets, 64)
-    base = {k: inp[k].to(dev) for k in ("x", "dy", "gamma", "rstd", "mean") if k in inp}
+    base = {k: inp[k].to(dev) for k in ("x", "dy", "gamma", "beta") if k in inp}
+    # the saved statistics the backward reads come from the GPU forward
+    if w.kind == "layernorm":
+        _, base["mean"], base["rstd"] = nb.norm_fwd_layernorm(base["x"], base["gamma"],
+                                                             base.get("beta"), w.eps)
+    else:
+        _, base["rstd"] = nb.norm_fwd_rmsnorm(base["x"], base["gamma"], w.eps)
+    torch.cuda.synchronize()
     sets = []
     for i in range(nsets):
         s = {k: (v if i == 0 else v.clone()) for k, v in base.items()}
         s["dx"] = torch.empty_like(base["x"])
+        s["f_mean"] = torch.empty_like(base["rstd"])
+        s["f_rstd"] = torch.empty_like(base["rstd"])
         sets.append(s)
     dgamma = torch.empty(w.N, dtype=w.wgrad_dtype, device=dev)
     dbeta = torch.empty(w.N, dtype=w.wgrad_dtype, device=dev) if with_db else None
@@ -207,12 +229,33 @@ def main(argv=None) -> int:
         if st:
             raise RuntimeError(nb.norm_bwd_last_error())
 
+    # the forward that produces the statistics, into per-set y and stats
+    # buffers (y lands in the dx buffer of the set, which the backward rewrites)
+    fwd_args = []
+    for s in sets:
+        if w.kind == "layernorm":
+            fwd_args.append((ptr(s["x"]), ptr(s["gamma"]), ptr(s.get("beta")), w.M, w.N, io,
+                             w.eps, ptr(s["dx"]), ptr(s["f_mean"]), ptr(s["f_rstd"]), sh))
+        else:
+            fwd_args.append((ptr(s["x"]), ptr(s["gamma"]), w.M, w.N, io, w.eps, ptr(s["dx"]),
+                             ptr(s["f_rstd"]), sh))
+    ffn = lib.norm_fwd_layernorm if w.kind == "layernorm" else lib.norm_fwd_rmsnorm
+
+    def step_f(i):
+        st = ffn(*fwd_args[i % nsets])
+        if st:
+            raise RuntimeError(nb.norm_bwd_last_error())
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     ms = time_loop(torch, step, args.steps, stream)
     ms_a = time_loop(torch, step_a, args.steps, stream)
     ms_b = time_loop(torch, step_b, max(args.steps, 50), stream)
+    for i in range(min(args.warmup, 50)):
+        step_f(i)
+    ms_f = time_loop(torch, step_f, args.steps, stream)
+    f_bytes = forward_bytes(w, "beta" in base)
 
     # copy probe: the achievable streaming ceiling next to the kernels
     cp_bytes = min(512 << 20, max(set_bytes // 3 * 2, 64 << 20)) // 16 * 16
@@ -258,6 +301,12 @@ def main(argv=None) -> int:
             "workspace_bytes": plan.workspace_bytes,
             "counted_GBps_incl_workspace": round(
                 (alg + 2 * plan.workspace_bytes) / (ms * 1e-3) / 1e9, 2),
+            "forward": {
+                "kernel": "norm_fwd_kernel", "us": round(ms_f * 1e3, 3),
+                "bytes_per_launch": f_bytes, "with_beta": "beta" in base,
+                "GBps": round(f_bytes / (ms_f * 1e-3) / 1e9, 2),
+                "pct_of_peak": round(100 * f_bytes / (ms_f * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+            },
             "plan": {k: v for k, v in plan.as_dict().items()
                      if k in ("groups", "rows_per_group", "vec", "chunks", "waves_per_row",
                               "rows_in_flight", "threads", "grid")},

@@ -197,6 +197,27 @@ int norm_bwd_reduce_partials(int64_t groups, int64_t N, int wgrad_dtype,
                              const void *workspace, size_t workspace_bytes,
                              void *dgamma, void *dbeta, void *stream);
 
+/*
+ * Forward pass that produces the saved statistics the backward consumes
+ * ("05: Layer norm", the Phobos tutorial's ln_fwd; RMSNorm per "Norm backward
+ * in Triton", "The gradients"). For each row of x[M, N]:
+ *   LayerNorm: mean = sum(x)/N, var = sum((x - mean)^2)/N (biased),
+ *              rstd = 1/sqrt(var + eps), y = gamma * (x - mean) * rstd + beta
+ *   RMSNorm:   rstd = 1/sqrt(sum(x^2)/N + eps), y = gamma * x * rstd
+ * computed in fp32 from the io_dtype inputs; y is rounded to nearest even.
+ *   x [M,N], gamma [N], beta [N] or NULL (read, io_dtype)
+ *   y [M,N] io_dtype (written); mean, rstd fp32 [M] (written; either may be
+ *   NULL to skip it)
+ * Same size limits as the backward without dbeta. Asynchronous on `stream`;
+ * checked on the host first (status codes as above). Allocates nothing.
+ */
+int norm_fwd_layernorm(const void *x, const void *gamma, const void *beta,
+                       int64_t M, int64_t N, int io_dtype, float eps, void *y,
+                       float *mean, float *rstd, void *stream);
+int norm_fwd_rmsnorm(const void *x, const void *gamma, int64_t M, int64_t N,
+                     int io_dtype, float eps, void *y, float *rstd,
+                     void *stream);
+
 /* Static text for a status code. */
 const char *norm_bwd_status_string(int status);
 

@@ -12,6 +12,9 @@ The functions carry the C names:
 
 * ``norm_bwd_layernorm(x, dy, gamma, mean, rstd, eps)`` -> (dx, dgamma, dbeta)
 * ``norm_bwd_rmsnorm(x, dy, gamma, rstd, eps)`` -> (dx, dgamma, dbeta or None)
+* ``norm_fwd_layernorm(x, gamma, beta, eps)`` -> (y, mean, rstd),
+  ``norm_fwd_rmsnorm(x, gamma, eps)`` -> (y, rstd): the forward pass that
+  produces the statistics the backward consumes
 * ``norm_bwd_workspace_bytes``, ``norm_bwd_make_plan``, ``norm_bwd_execute``,
   ``norm_bwd_execute_partials``, ``norm_bwd_reduce_partials``,
   ``norm_bwd_probe_copy``, ``norm_bwd_status_string``, ``norm_bwd_last_error``.
@@ -98,6 +101,8 @@ def load_library():
             "norm_bwd_status_string": [i32],
             "norm_bwd_last_error": [],
             "norm_bwd_probe_copy": [vp, vp, sz, vp],
+            "norm_fwd_layernorm": [vp, vp, vp, i64, i64, i32, fp, vp, vp, vp, vp],
+            "norm_fwd_rmsnorm": [vp, vp, i64, i64, i32, fp, vp, vp, vp],
         }
         for name, args in sigs.items():
             f = getattr(lib, name)
@@ -295,6 +300,54 @@ def norm_bwd_reduce_partials(groups: int, N: int, workspace: torch.Tensor,
     _check(st)
 
 
+def _forward(kind, x, gamma, beta, eps, y, mean, rstd, want_mean, want_rstd, stream):
+    lib = load_library()
+    _gpu(x, "x")
+    _gpu(gamma, "gamma")
+    if beta is not None:
+        _gpu(beta, "beta")
+    M, N = _rows(x)
+    io = _code(x.dtype, "x")
+    if gamma.dtype != x.dtype or (beta is not None and beta.dtype != x.dtype):
+        raise ValueError("x, gamma and beta must share one dtype")
+    if gamma.numel() != N or (beta is not None and beta.numel() != N):
+        raise ValueError("gamma and beta must have N elements")
+    dev = x.device
+    if y is None:
+        y = torch.empty_like(x)
+    if want_mean and mean is None:
+        mean = torch.empty(M, dtype=torch.float32, device=dev)
+    if want_rstd and rstd is None:
+        rstd = torch.empty(M, dtype=torch.float32, device=dev)
+    for t, n in ((y, "y"), (mean, "mean"), (rstd, "rstd")):
+        if t is not None:
+            _gpu(t, n)
+    s = _stream(stream, dev)
+    with torch.cuda.device(dev):
+        if kind == LAYERNORM:
+            st = lib.norm_fwd_layernorm(_ptr(x), _ptr(gamma), _ptr(beta), M, N, io, float(eps),
+                                        _ptr(y), _ptr(mean), _ptr(rstd), s)
+        else:
+            st = lib.norm_fwd_rmsnorm(_ptr(x), _ptr(gamma), M, N, io, float(eps), _ptr(y),
+                                      _ptr(rstd), s)
+    _check(st)
+    return y, mean, rstd
+
+
+def norm_fwd_layernorm(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.Tensor] = None,
+                       eps: float = 1e-5, *, y=None, mean=None, rstd=None, want_stats: bool = True,
+                       stream=None):
+    """LayerNorm forward on the GPU: returns (y, mean, rstd) with fp32 statistics."""
+    return _forward(LAYERNORM, x, gamma, beta, eps, y, mean, rstd, want_stats, want_stats, stream)
+
+
+def norm_fwd_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, *, y=None,
+                     rstd=None, want_stats: bool = True, stream=None):
+    """RMSNorm forward on the GPU: returns (y, rstd) with fp32 rstd."""
+    y, _, rstd = _forward(RMSNORM, x, gamma, None, eps, y, None, rstd, False, want_stats, stream)
+    return y, rstd
+
+
 def norm_bwd_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
     """Plain streaming copy kernel (bandwidth and counter calibration)."""
     lib = load_library()
@@ -312,5 +365,6 @@ __all__ = [
     "norm_bwd_layernorm", "norm_bwd_rmsnorm", "norm_bwd_workspace_bytes", "norm_bwd_make_plan",
     "norm_bwd_execute", "norm_bwd_execute_partials", "norm_bwd_reduce_partials",
     "norm_bwd_probe_copy", "norm_bwd_status_string", "norm_bwd_last_error", "NormBwdPlan",
+    "norm_fwd_layernorm", "norm_fwd_rmsnorm",
     "NormBwdError", "load_library", "library_path",
 ]

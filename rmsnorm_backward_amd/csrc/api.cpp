@@ -170,9 +170,83 @@ int run_auto(int kind, const void* x, const void* dy, const void* gamma, const f
   return launch_reduce(p.groups, N, wgrad_dtype, workspace, dgamma, dbeta, s);
 }
 
+int run_forward(int kind, const void* x, const void* gamma, const void* beta, int64_t M,
+                int64_t N, int io_dtype, float eps, void* y, float* mean, float* rstd,
+                void* stream) {
+  if (kind != NORM_BWD_LAYERNORM && kind != NORM_BWD_RMSNORM)
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "kind invalid");
+  const int eb = nb::dtype_bytes(io_dtype);
+  if (eb == 0) return set_error(NORM_BWD_ERR_UNSUPPORTED, "unknown io_dtype");
+  if (M < 0 || N < 0) return set_error(NORM_BWD_ERR_INVALID_ARG, "M and N must be >= 0");
+  if (N > 0 && M > (int64_t)(((uint64_t)1 << 62) / (uint64_t)N / 4u))
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "M * N too large");
+  if (!(eps >= 0.0f) || isinf(eps))
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (M == 0 || N == 0) return NORM_BWD_OK;
+  if (!x || !gamma || !y) return set_error(NORM_BWD_ERR_INVALID_ARG, "x, gamma and y must be non-NULL");
+  const bool vec_ok = aligned16(x) && aligned16(gamma) && aligned16(y) && (!beta || aligned16(beta));
+  norm_bwd_plan_t g;
+  const char* why = nullptr;
+  int st = nb::make_geometry(kind, N, io_dtype, 0, vec_ok, &g, &why);
+  if (st != NORM_BWD_OK) return set_error(st, why);
+  // y and the statistics must not overlap the inputs or each other
+  const size_t mat = (size_t)M * (size_t)N * (size_t)eb, vec = (size_t)N * (size_t)eb;
+  const size_t stat = (size_t)M * 4u;
+  struct R { const void* p; size_t n; };
+  const R inputs[] = {{x, mat}, {gamma, vec}, {beta, vec}};
+  const R outputs[] = {{y, mat}, {kind == NORM_BWD_LAYERNORM ? mean : nullptr, stat}, {rstd, stat}};
+  for (int i = 0; i < 3; ++i) {
+    for (const R& in : inputs)
+      if (nb::ranges_overlap(outputs[i].p, outputs[i].n, in.p, in.n))
+        return set_error(NORM_BWD_ERR_INVALID_ARG, "an output overlaps an input");
+    for (int j = i + 1; j < 3; ++j)
+      if (nb::ranges_overlap(outputs[i].p, outputs[i].n, outputs[j].p, outputs[j].n))
+        return set_error(NORM_BWD_ERR_INVALID_ARG, "outputs overlap each other");
+  }
+  nb::LaunchF f;
+  f.kind = kind;
+  f.vec_full = g.vec > 1 ? 1 : 0;
+  f.chunks = g.chunks;
+  f.x = x;
+  f.gamma = gamma;
+  f.beta = beta;
+  f.y = y;
+  f.mean = kind == NORM_BWD_LAYERNORM ? mean : nullptr;
+  f.rstd = rstd;
+  f.M = M;
+  f.N = (int)N;
+  f.eps = eps;
+  f.S = g.waves_per_row;
+  f.P = g.rows_in_flight;
+  f.threads = g.threads;
+  f.grid = (int)nb::forward_grid(M, g.waves_per_row, g.rows_in_flight);
+  f.stream = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // clear a stale error so a launch failure is ours
+  hipError_t e;
+  switch (io_dtype) {
+    case NORM_BWD_F32: e = nb::launch_f_f32(f); break;
+    case NORM_BWD_F16: e = nb::launch_f_f16(f); break;
+    default: e = nb::launch_f_bf16(f); break;
+  }
+  if (e != hipSuccess) return hip_error(e, "forward launch");
+  return NORM_BWD_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int norm_fwd_layernorm(const void* x, const void* gamma, const void* beta, int64_t M, int64_t N,
+                       int io_dtype, float eps, void* y, float* mean, float* rstd, void* stream) {
+  return run_forward(NORM_BWD_LAYERNORM, x, gamma, beta, M, N, io_dtype, eps, y, mean, rstd,
+                     stream);
+}
+
+int norm_fwd_rmsnorm(const void* x, const void* gamma, int64_t M, int64_t N, int io_dtype,
+                     float eps, void* y, float* rstd, void* stream) {
+  return run_forward(NORM_BWD_RMSNORM, x, gamma, nullptr, M, N, io_dtype, eps, y, nullptr, rstd,
+                     stream);
+}
 
 int norm_bwd_layernorm(const void* x, const void* dy, const void* gamma, const float* mean,
                        const float* rstd, int64_t M, int64_t N, int io_dtype, int wgrad_dtype,

@@ -1,6 +1,8 @@
-// kernels_f16.hip -- kernel A instantiations for one I/O element type.
+// kernels_f16.hip -- kernel A and forward-kernel instantiations for one I/O
+// element type.
 #include "nb_launch_a.hpp"
 
 namespace nb {
 hipError_t launch_a_f16(const LaunchA& a) { return launch_a_impl<TF16>(a); }
+hipError_t launch_f_f16(const LaunchF& f) { return launch_f_impl<TF16>(f); }
 }  // namespace nb

@@ -1,6 +1,8 @@
-// kernels_f32.hip -- kernel A instantiations for one I/O element type.
+// kernels_f32.hip -- kernel A and forward-kernel instantiations for one I/O
+// element type.
 #include "nb_launch_a.hpp"
 
 namespace nb {
 hipError_t launch_a_f32(const LaunchA& a) { return launch_a_impl<TF32>(a); }
+hipError_t launch_f_f32(const LaunchF& f) { return launch_f_impl<TF32>(f); }
 }  // namespace nb

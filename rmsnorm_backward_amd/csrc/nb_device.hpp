@@ -223,6 +223,39 @@ constexpr int prefetch_depth() {
 }
 
 // ---------------------------------------------------------------- kernel A
+// Turn per-lane partial sums into row sums: the wave butterfly, then, when
+// S > 1 waves share the row, an exchange through LDS in which the S wave sums
+// are added in slice order 0, 1, ..., S-1 (lane q < S fetches slice q's pair
+// in one LDS read; the pairs are added from scalar copies). `a` takes part
+// only when USE_A. Every wave of the workgroup must make the same sequence of
+// calls (the exchange holds a barrier); `phase` alternates the two LDS
+// buffers so that one barrier per call suffices.
+template <bool USE_A>
+__device__ __forceinline__ void row_sum2(float& a, float& b, float (*red)[kMaxWaves][2],
+                                         int& phase, int lane, int wave, int S, int p) {
+  b = wave_sum(b);
+  if (USE_A) a = wave_sum(a);
+  if (S > 1) {
+    const int buf = phase & 1;
+    if (lane == 0) {
+      red[buf][wave][0] = a;
+      red[buf][wave][1] = b;
+    }
+    __syncthreads();
+    float2 mine = make_float2(0.0f, 0.0f);
+    if (lane < S) mine = *reinterpret_cast<const float2*>(&red[buf][p * S + lane][0]);
+    const int ab = __builtin_bit_cast(int, mine.x), bb = __builtin_bit_cast(int, mine.y);
+    float ta = 0.0f, tb = 0.0f;
+    for (int q = 0; q < S; ++q) {
+      ta += __builtin_bit_cast(float, __builtin_amdgcn_readlane(ab, q));
+      tb += __builtin_bit_cast(float, __builtin_amdgcn_readlane(bb, q));
+    }
+    a = ta;
+    b = tb;
+  }
+  ++phase;
+}
+
 // A zero the compiler cannot see through (it lives in a vector register).
 // Adding it to the index of a per-row statistic keeps that load on the vector
 // memory path, in issue order with the row's x/dy loads. A scalar load there
@@ -308,29 +341,7 @@ __device__ __forceinline__ void process_row(RowBuf<Tg, VEC, C>& b, const float (
   pin(acc);
   keep_packed(b.x);
   keep_packed(b.dy);
-  s2 = wave_sum(s2);
-  if (KIND == kLayerNorm) s1 = wave_sum(s1);
-  if (S > 1) {
-    const int buf = phase & 1;
-    if (lane == 0) {
-      red[buf][wave][0] = s1;
-      red[buf][wave][1] = s2;
-    }
-    __syncthreads();
-    // lane q < S fetches slice q's pair in one LDS read; the S pairs are then
-    // added in slice order 0, 1, ..., S-1 from scalar copies
-    float2 mine = make_float2(0.0f, 0.0f);
-    if (lane < S) mine = *reinterpret_cast<const float2*>(&red[buf][p * S + lane][0]);
-    const int m1b = __builtin_bit_cast(int, mine.x), m2b = __builtin_bit_cast(int, mine.y);
-    float t1 = 0.0f, t2 = 0.0f;
-    for (int q = 0; q < S; ++q) {
-      t1 += __builtin_bit_cast(float, __builtin_amdgcn_readlane(m1b, q));
-      t2 += __builtin_bit_cast(float, __builtin_amdgcn_readlane(m2b, q));
-    }
-    s1 = t1;
-    s2 = t2;
-  }
-  ++phase;
+  row_sum2<KIND == kLayerNorm>(s1, s2, red, phase, lane, wave, S, p);
   if (active) {
     const float m2 = s2 * inv_n * b.rs;  // mean_j(dyhat * xhat)
     const float c2 = -(b.rs * b.rs) * m2;

@@ -1,0 +1,151 @@
+// nb_forward.hpp -- the forward pass that produces the statistics the
+// backward consumes (gfx950, wave64).
+//
+// Per row x of width N ("05: Layer norm", the Phobos tutorial's ln_fwd;
+// "Norm backward in Triton -- the dγ/dβ reduction", "The gradients" for
+// RMSNorm):
+//   LayerNorm: mean = sum(x)/N, var = sum((x - mean)^2)/N (biased, two passes
+//              over the registers), rstd = 1/sqrt(var + eps),
+//              y = gamma * (x - mean) * rstd + beta
+//   RMSNorm:   rstd = 1/sqrt(sum(x^2)/N + eps), y = gamma * x * rstd (+ beta)
+// and mean/rstd are stored as fp32 for the backward.
+//
+// The layout is kernel A's: S waves share a row, each lane holds C chunks of
+// VEC contiguous elements, P rows in flight per workgroup, and a ring of
+// register buffers keeps the next rows' loads in flight. Rows carry no
+// cross-row state, so workgroup b simply takes rows (k*gridDim.x + b)*P + p:
+// all workgroups sweep one address window together.
+#pragma once
+
+#include "nb_device.hpp"
+
+namespace nb {
+
+template <class Tg, int VEC, int C>
+struct XBuf {
+  Pack<Tg, VEC> x[C];
+};
+
+template <int KIND, class Tg, int VEC, int C, bool BETA>
+__global__ __launch_bounds__((max_threads_for<VEC, C>()))
+void norm_fwd_kernel(const void* __restrict__ xv, const void* __restrict__ gv,
+                     const void* __restrict__ bv, void* __restrict__ yv,
+                     float* __restrict__ mean_out, float* __restrict__ rstd_out, int64_t M,
+                     int N, float eps, int S, int P) {
+  using PK = Pack<Tg, VEC>;
+  constexpr int EB = Tg::kBytes;
+  const char* __restrict__ x = static_cast<const char*>(xv);
+  char* __restrict__ y = static_cast<char*>(yv);
+
+  __shared__ __align__(8) float red[2][kMaxWaves][2];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int s = wave % S;
+  const int p = wave / S;
+  const int cstride = S * 64 * VEC;
+  const int col0 = (s * 64 + lane) * VEC;
+  const float inv_n = 1.0f / (float)N;
+
+  float gam[C][VEC], bet[C][VEC];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int col = col0 + c * cstride;
+    PK tg, tb;
+    tg.zero();
+    tb.zero();
+    if (col < N) {
+      tg.load(static_cast<const char*>(gv) + (int64_t)col * EB);
+      if (BETA) tb.load(static_cast<const char*>(bv) + (int64_t)col * EB);
+    }
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      gam[c][v] = tg.get(v);
+      bet[c][v] = BETA ? tb.get(v) : 0.0f;
+    }
+  }
+
+  const int64_t rows_per_sweep = (int64_t)gridDim.x * P;
+  const int iters = (int)((M + rows_per_sweep - 1) / rows_per_sweep);
+  auto row_of = [&](int k) { return ((int64_t)k * gridDim.x + blockIdx.x) * P + p; };
+
+  auto fetch = [&](XBuf<Tg, VEC, C>& b, int64_t r) {
+    if (r < M) {
+      const int64_t rb = r * (int64_t)N;
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int col = col0 + c * cstride;
+        if (col < N) b.x[c].load_stream(x + (rb + col) * EB);
+      }
+    }
+  };
+
+  int phase = 0;
+  auto process = [&](XBuf<Tg, VEC, C>& b, int64_t r) {
+    const bool active = r < M;
+    float unused = 0.0f, s1 = 0.0f;
+    float mu = 0.0f;
+    if (KIND == kLayerNorm) {
+      if (active) {
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+          if (col0 + c * cstride < N)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) s1 += b.x[c].get(v);
+      }
+      row_sum2<false>(unused, s1, red, phase, lane, wave, S, p);
+      mu = s1 * inv_n;
+    }
+    float s2 = 0.0f;  // sum((x - mean)^2), RMSNorm: sum(x^2)
+    if (active) {
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+        if (col0 + c * cstride < N)
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) {
+            const float xc = b.x[c].get(v) - mu;
+            s2 = __builtin_fmaf(xc, xc, s2);
+          }
+    }
+    keep_packed(b.x);
+    row_sum2<false>(unused, s2, red, phase, lane, wave, S, p);
+    if (active) {
+      const float rs = 1.0f / __builtin_sqrtf(s2 * inv_n + eps);
+      const int64_t rb = r * (int64_t)N;
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int col = col0 + c * cstride;
+        if (col < N) {
+          float o[VEC];
+#pragma unroll
+          for (int v = 0; v < VEC; ++v)
+            o[v] = __builtin_fmaf((b.x[c].get(v) - mu) * rs, gam[c][v], bet[c][v]);
+          PK out;
+          out.set(o);
+          out.store_stream(y + (rb + col) * EB);
+        }
+      }
+      // one lane stores the row's statistics (a predicated vector store)
+      if (s == 0 && lane == 0) {
+        if (mean_out && KIND == kLayerNorm) mean_out[r] = mu;
+        if (rstd_out) rstd_out[r] = rs;
+      }
+    }
+  };
+
+  constexpr int D = prefetch_depth<Tg, VEC, C>();
+  XBuf<Tg, VEC, C> buf[D];
+#pragma unroll
+  for (int k = 0; k < D - 1; ++k)
+    if (k < iters) fetch(buf[k], row_of(k));
+  for (int it = 0; it < iters; it += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int k = it + d;
+      if (k + D - 1 < iters) fetch(buf[(d + D - 1) % D], row_of(k + D - 1));
+      if (k < iters) process(buf[d], row_of(k));
+    }
+  }
+}
+
+}  // namespace nb

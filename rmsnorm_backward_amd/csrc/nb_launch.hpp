@@ -26,9 +26,29 @@ struct LaunchA {
   hipStream_t stream;
 };
 
+struct LaunchF {
+  int kind;
+  int vec_full;
+  int chunks;
+  const void* x;
+  const void* gamma;
+  const void* beta;  // may be NULL
+  void* y;
+  float* mean;       // may be NULL
+  float* rstd;       // may be NULL
+  int64_t M;
+  int N;
+  float eps;
+  int S, P, threads, grid;
+  hipStream_t stream;
+};
+
 hipError_t launch_a_f32(const LaunchA& a);
 hipError_t launch_a_f16(const LaunchA& a);
 hipError_t launch_a_bf16(const LaunchA& a);
+hipError_t launch_f_f32(const LaunchF& f);
+hipError_t launch_f_f16(const LaunchF& f);
+hipError_t launch_f_bf16(const LaunchF& f);
 hipError_t launch_reduce(int wgrad_dtype, const float* ws, int64_t G, int N, void* dgamma,
                          void* dbeta, hipStream_t stream);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);

@@ -3,6 +3,7 @@
 #pragma once
 
 #include "nb_device.hpp"
+#include "nb_forward.hpp"
 #include "nb_launch.hpp"
 
 namespace nb {
@@ -52,6 +53,48 @@ hipError_t launch_a_impl(const LaunchA& a) {
     return a.nacc == 2 ? launch_by_vec<Tg, kLayerNorm, 2>(a) : launch_by_vec<Tg, kLayerNorm, 1>(a);
   }
   return a.nacc == 2 ? launch_by_vec<Tg, kRmsNorm, 2>(a) : launch_by_vec<Tg, kRmsNorm, 1>(a);
+}
+
+template <class Tg, int KIND, int VEC, int C, bool BETA>
+hipError_t launch_fwd_one(const LaunchF& f) {
+  hipLaunchKernelGGL((norm_fwd_kernel<KIND, Tg, VEC, C, BETA>), dim3(f.grid), dim3(f.threads), 0,
+                     f.stream, f.x, f.gamma, f.beta, f.y, f.mean, f.rstd, f.M, f.N, f.eps, f.S,
+                     f.P);
+  return hipGetLastError();
+}
+
+template <class Tg, int KIND, bool FULL, bool BETA>
+hipError_t launch_fwd_by_chunks(const LaunchF& f) {
+  constexpr int VEC = FULL ? 16 / Tg::kBytes : 1;
+  constexpr int LIM = lane_elem_limit<Tg, 1, FULL>();
+  switch (f.chunks) {
+    case 1: return launch_fwd_one<Tg, KIND, VEC, 1, BETA>(f);
+    case 2:
+      if constexpr (VEC * 2 <= LIM) return launch_fwd_one<Tg, KIND, VEC, 2, BETA>(f);
+      break;
+    case 4:
+      if constexpr (VEC * 4 <= LIM) return launch_fwd_one<Tg, KIND, VEC, 4, BETA>(f);
+      break;
+    case 8:
+      if constexpr (VEC * 8 <= LIM) return launch_fwd_one<Tg, KIND, VEC, 8, BETA>(f);
+      break;
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class Tg, int KIND, bool BETA>
+hipError_t launch_fwd_by_vec(const LaunchF& f) {
+  return f.vec_full ? launch_fwd_by_chunks<Tg, KIND, true, BETA>(f)
+                    : launch_fwd_by_chunks<Tg, KIND, false, BETA>(f);
+}
+
+template <class Tg>
+hipError_t launch_f_impl(const LaunchF& f) {
+  const bool beta = f.beta != nullptr;
+  if (f.kind == 0)
+    return beta ? launch_fwd_by_vec<Tg, kLayerNorm, true>(f) : launch_fwd_by_vec<Tg, kLayerNorm, false>(f);
+  return beta ? launch_fwd_by_vec<Tg, kRmsNorm, true>(f) : launch_fwd_by_vec<Tg, kRmsNorm, false>(f);
 }
 
 }  // namespace nb

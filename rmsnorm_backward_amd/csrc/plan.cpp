@@ -101,6 +101,15 @@ int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok
   return NORM_BWD_OK;
 }
 
+int64_t forward_grid(int64_t M, int S, int P) {
+  if (M <= 0) return 0;
+  int64_t g = kTargetWaves / (S * P);
+  const int64_t sweep = ceil_div(M, P);
+  if (g > sweep) g = sweep;
+  if (g > kMaxGrid) g = kMaxGrid;
+  return g < 1 ? 1 : g;
+}
+
 int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype) {
   if (M <= 0) return 0;
   // Enough workgroups for about kTargetWaves waves in flight (8 per compute

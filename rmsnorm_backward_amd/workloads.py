@@ -1,8 +1,8 @@
 """Seeded synthetic workloads for the LayerNorm / RMSNorm backward pass.
 
-This module only draws inputs. It holds none of the backward arithmetic: the
-GPU path and the fp64 oracle each implement that on their own, and both read
-their inputs from here.
+This module only draws inputs. It holds none of the forward or backward
+arithmetic: the GPU path and the fp64 oracle each implement that on their own,
+and both read their inputs from here.
 
 What a workload carries (the norm backward consumes the forward's saved
 per-row statistics, see "Norm backward in Triton — the dγ/dβ reduction",
@@ -11,11 +11,10 @@ section "The dx kernel — recompute the stat, don't store x̂"):
 * ``x``, ``dy``, ``gamma`` in the I/O dtype (round-to-nearest-even casts of
   fp32 draws), and for LayerNorm workloads that list one, ``beta`` (it enters
   only the forward output, never the backward).
-* ``rstd`` (and ``mean`` for LayerNorm) in fp32: the statistics a forward pass
-  would have saved, evaluated in fp64 on the *cast* ``x`` and then rounded to
-  fp32. LayerNorm uses the biased variance (divide by N), as the forward in
-  "05: Layer norm" (the Phobos tutorial's ``ln_fwd``) does; RMSNorm uses the
-  mean of squares, as in "Norm backward in Triton", section "The gradients".
+The saved statistics (fp32 ``rstd``, and ``mean`` for LayerNorm) are not drawn
+here: they are what a forward pass computes from the cast ``x``, so each
+consumer runs one (the tests and the CPU baseline the fp64 oracle's forward,
+rounded to fp32; the benchmark the GPU forward).
 
 Everything is drawn on the CPU from seeded ``torch.Generator`` objects, so
 every consumer sees the same bits. The [M, N] draws (x, dy, an outlier mask)
@@ -163,10 +162,11 @@ def _blocked(seed: int, tag: int, M: int, N: int, kind: str) -> torch.Tensor:
 def make_inputs(w: Workload) -> Dict[str, torch.Tensor]:
     """Draw the workload's inputs on the CPU (contiguous tensors).
 
-    Returns x, dy, gamma (io dtype), rstd (fp32 [M]), mean (fp32 [M], LayerNorm
-    only), beta (io dtype, only when the workload lists one), and
-    ``outliers`` (column indices, or [k, 2] entry indices) when outliers are
-    drawn.
+    Returns x, dy, gamma (io dtype), beta (io dtype, only when the workload
+    lists one), and ``outliers`` (column indices, or [k, 2] entry indices)
+    when outliers are drawn. The saved statistics the backward reads are not
+    drawn here: they are what a forward pass computes from x (the caller runs
+    one).
     """
     g = torch.Generator().manual_seed(w.seed)
     M, N = w.M, w.N
@@ -200,35 +200,7 @@ def make_inputs(w: Workload) -> Dict[str, torch.Tensor]:
     out["dy"] = dy.to(w.io_dtype)
     del dy
     out["gamma"] = gamma.to(w.io_dtype)
-    mean, rstd = saved_stats(out["x"], w.kind, w.eps)
-    out["rstd"] = rstd
-    if w.kind == LAYERNORM:
-        out["mean"] = mean
     return out
-
-
-def saved_stats(x: torch.Tensor, kind: str, eps: float, chunk_rows: int = 4096):
-    """fp32 mean/rstd a forward pass would save, evaluated in fp64.
-
-    LayerNorm: mean = Σx/N, var = Σ(x−mean)²/N, rstd = 1/sqrt(var+eps).
-    RMSNorm:   rstd = 1/sqrt(Σx²/N + eps); mean is None.
-    """
-    M = x.shape[0]
-    rstd = torch.empty(M, dtype=torch.float32)
-    mean = torch.empty(M, dtype=torch.float32) if kind == LAYERNORM else None
-    for r0 in range(0, M, chunk_rows):
-        xd = x[r0:r0 + chunk_rows].double()
-        if kind == LAYERNORM:
-            mu = xd.mean(dim=1)
-            var = (xd - mu[:, None]).square_().mean(dim=1)
-            mean[r0:r0 + chunk_rows] = mu.float()
-            rstd[r0:r0 + chunk_rows] = (1.0 / torch.sqrt(var + eps)).float()
-        elif kind == RMSNORM:
-            ms = xd.square_().mean(dim=1)
-            rstd[r0:r0 + chunk_rows] = (1.0 / torch.sqrt(ms + eps)).float()
-        else:
-            raise ValueError(kind)
-    return mean, rstd
 
 
 def sample_rows(M: int, k: int, seed: int = 7, extra: Sequence[int] = ()) -> torch.Tensor:
@@ -248,5 +220,5 @@ def ceil_div(a: int, b: int) -> int:
 
 __all__ = [
     "Workload", "WORKLOADS", "HEADLINE", "LAYERNORM", "RMSNORM", "make_inputs",
-    "saved_stats", "scaled", "sample_rows", "ceil_div",
+    "scaled", "sample_rows", "ceil_div",
 ]

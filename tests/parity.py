@@ -27,6 +27,16 @@ Tolerances (all comparisons in fp64, oracle unrounded):
   stored in fp16 or bf16, the rounding of the stored value (at most 2^-11 or
   2^-8 of it, to nearest even) is added to the bound.
 
+* forward y: per element |got - ref| <= out_round*|ref| + k*T_y with
+  T_y = |gamma|*(|xhat| + rstd*mean_k|x_k|) + |beta|, the size of the terms y
+  is built from including the error a fp32 mean brings into xhat; k = 2^-16
+  for fp16/bf16 outputs (out_round 2^-11 / 2^-8, plus half the subnormal
+  spacing, 2^-25 for fp16, where the rounding error is absolute) and fp32
+  outputs use
+  1e-5 + 1e-5*|ref| + 2^-18*T_y. Statistics: |mean - ref| <= 2^-16 *
+  mean_k|x_k| (+ 1e-7 * |ref| for its fp32 rounding), |rstd - ref| <= 2^-16 *
+  rstd: the fp32 row sums carry at most ~90 ulps of the summed magnitudes.
+
 Both sides read the same input bits (the oracle widens them exactly).
 """
 
@@ -116,3 +126,40 @@ def check_wgrad(io_dtype, got, ref, what="dgamma"):
         _fail(what, g, r, np.unravel_index(np.argmax(err - lim), err.shape))
     scale = max(float(np.max(np.abs(r))), 1e-300)
     return {"max_abs": float(err.max()), "max_rel_to_max": float(err.max() / scale)}
+
+
+# Below the smallest normal number the formats are evenly spaced (fp16: 2^-24,
+# bf16: 2^-133), so rounding to nearest errs there by up to half that spacing
+# rather than by a fraction of |ref|.
+SUBNORMAL_HALF_SPACING = {torch.float16: 2.0 ** -25, torch.bfloat16: 2.0 ** -134}
+
+
+def check_forward(io_dtype, kind, x, gamma, beta, got_y, got_mean, got_rstd, ref_y, ref_mean,
+                  ref_rstd):
+    xs, g = f64(x), f64(gamma)
+    b = f64(beta) if beta is not None else np.zeros_like(g)
+    rm = f64(ref_mean)[:, None] if kind == "layernorm" else 0.0
+    rr = f64(ref_rstd)[:, None]
+    mabs = np.abs(xs).mean(axis=1, keepdims=True)
+    ty = np.abs(g)[None, :] * (np.abs((xs - rm) * rr) + rr * mabs) + np.abs(b)[None, :]
+    gy, ry = f64(got_y), f64(ref_y)
+    err = np.abs(gy - ry)
+    if io_dtype == torch.float32:
+        lim = 1e-5 + 1e-5 * np.abs(ry) + 2.0 ** -18 * ty
+    else:
+        lim = OUT_ROUND[io_dtype] * np.abs(ry) + SUBNORMAL_HALF_SPACING[io_dtype] + \
+            2.0 ** -16 * ty
+    if not np.all(err <= lim):
+        _fail("y", gy, ry, np.unravel_index(np.argmax(err - lim), err.shape))
+    if got_rstd is not None:
+        gr, rr1 = f64(got_rstd), f64(ref_rstd)
+        e = np.abs(gr - rr1)
+        if not np.all(e <= 2.0 ** -16 * rr1):
+            _fail("rstd", gr, rr1, (int(np.argmax(e - 2.0 ** -16 * rr1)),))
+    if kind == "layernorm" and got_mean is not None:
+        gm, rm1 = f64(got_mean), f64(ref_mean)
+        e = np.abs(gm - rm1)
+        lim = 2.0 ** -16 * mabs[:, 0] + 1e-7 * np.abs(rm1)
+        if not np.all(e <= lim):
+            _fail("mean", gm, rm1, (int(np.argmax(e - lim)),))
+    return {"y_max_abs": float(err.max()) if err.size else 0.0}

@@ -18,6 +18,7 @@ import torch
 
 import oracle
 import parity
+from inputs import backward_inputs, oracle_stats
 from rmsnorm_backward_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -88,7 +89,7 @@ SMALL = [
 
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
 def test_workload_parity(nb, w):
-    inp = W.make_inputs(w)
+    inp = backward_inputs(w)
     with_db = w.kind == "layernorm"
     out = run(nb, w, to_gpu(inp))
     s = compare_full(w, inp, out, with_db)
@@ -103,7 +104,7 @@ def test_phobos_check_distribution(nb):
     gamma = torch.rand(N, generator=g).half()
     x = (-2.3 + 0.5 * torch.randn(M, N, generator=g)).half()
     dy = (0.1 * torch.randn(M, N, generator=g)).half()
-    mean, rstd = W.saved_stats(x, "layernorm", eps)
+    mean, rstd = oracle_stats(x, "layernorm", eps)
     inp = {"x": x, "dy": dy, "gamma": gamma, "mean": mean, "rstd": rstd}
     w = W.scaled(W.LN_F16_1151x8192, name="phobos_check")
     out = run(nb, w, to_gpu(inp))
@@ -118,7 +119,7 @@ FULL = [W.RMS_BF16_16384x4096, W.LN_BF16_65536x8192, W.RMS_BF16_262144x768]
 @pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
 def test_full_size_sampled(nb, w):
     print(f"[gen] {w.name}", flush=True)
-    inp = W.make_inputs(w)
+    inp = backward_inputs(w)
     g = to_gpu(inp)
     with_db = w.kind == "layernorm"
     plan = nb.norm_bwd_make_plan(w.kind, w.M, w.N, w.io_dtype, with_db)
@@ -178,7 +179,7 @@ def _edge_cases():
 def test_edge_shapes(nb, kind, dt, M, N):
     base = W.LN_F32_128x512 if kind == "layernorm" else W.RMS_F32_128x512
     w = W.scaled(base, M=M, N=N, io_dtype=dt, wgrad_dtype=torch.float32, seed=99 + M + N)
-    inp = W.make_inputs(w)
+    inp = backward_inputs(w)
     for with_db in (True, False):
         if dt != torch.float32 and with_db and N > 16384:
             with pytest.raises(nb.NormBwdError) as e:      # documented limit
@@ -194,7 +195,7 @@ def test_edge_shapes(nb, kind, dt, M, N):
 @pytest.mark.parametrize("groups", [1, 2, 7, 100, 999, 1000])
 def test_explicit_groups(nb, groups):
     w = W.scaled(W.LN_BF16_65536x8192, M=1000, N=1536)
-    inp = W.make_inputs(w)
+    inp = backward_inputs(w)
     out = run(nb, w, to_gpu(inp), groups=groups)
     compare_full(w, inp, out, True)
 
@@ -204,7 +205,7 @@ def test_explicit_groups(nb, groups):
 def test_wgrad_in_io_dtype(nb, kind, dt):
     base = W.LN_F16_1151x8192 if kind == "layernorm" else W.RMS_BF16_16384x4096
     w = W.scaled(base, M=300, N=2048, io_dtype=dt, wgrad_dtype=dt)
-    inp = W.make_inputs(w)
+    inp = backward_inputs(w)
     out = run(nb, w, to_gpu(inp), dbeta=True)
     assert out[1].dtype == dt and out[2].dtype == dt
     compare_full(w, inp, out, True)
@@ -215,7 +216,7 @@ def test_geometry_variants_agree(nb):
     and dgamma bits do not depend on the lane layout when the row grouping is
     unchanged (only the in-row sums, i.e. dx, may differ in the last bit)."""
     w = W.scaled(W.RMS_BF16_16384x4096, M=1500, N=4096)
-    inp = W.make_inputs(w)
+    inp = backward_inputs(w)
     g = to_gpu(inp)
     base = nb.norm_bwd_make_plan("rmsnorm", w.M, w.N, torch.bfloat16, False)
     ref = None
@@ -237,7 +238,7 @@ def test_geometry_variants_agree(nb):
 
 def test_determinism_repeats_and_perturbation(nb):
     w = W.scaled(W.LN_BF16_65536x8192, M=4099, N=4096)
-    g = to_gpu(W.make_inputs(w))
+    g = to_gpu(backward_inputs(w))
     first = run(nb, w, g)
     side = torch.cuda.Stream()
     junk = torch.randn(4096, 4096, device="cuda")
@@ -257,7 +258,7 @@ def test_determinism_repeats_and_perturbation(nb):
 def test_nan_poisoned_outputs_and_workspace(nb):
     """Prior contents of dx, dgamma, dbeta and the workspace are never read."""
     w = W.scaled(W.LN_BF16_65536x8192, M=999, N=768)
-    inp = W.make_inputs(w)
+    inp = backward_inputs(w)
     g = to_gpu(inp)
     clean = run(nb, w, g)
     need = nb.norm_bwd_workspace_bytes("layernorm", w.M, w.N, w.io_dtype, True)
@@ -276,7 +277,7 @@ def test_guard_bands_untouched(nb):
     """Outputs and workspace carved out of larger buffers: the bytes around
     them keep their canary values (no out-of-bounds writes)."""
     w = W.scaled(W.RMS_BF16_262144x768, M=1031, N=1000)   # ragged N, vector path
-    inp = W.make_inputs(w)
+    inp = backward_inputs(w)
     g = to_gpu(inp)
     pad = 4096
     canary = -1536.0   # exact in bf16, fp16 and fp32
@@ -302,7 +303,7 @@ def test_misaligned_rows_take_the_scalar_path(nb):
     """Tensors offset by one element (not 16-byte aligned) still give the
     right answer (the automatic plan falls back to one element per lane)."""
     w = W.scaled(W.RMS_BF16_16384x4096, M=130, N=1024)
-    inp = W.make_inputs(w)
+    inp = backward_inputs(w)
     def off(t):
         buf = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
         v = buf[1:].view(t.shape)
@@ -316,7 +317,7 @@ def test_misaligned_rows_take_the_scalar_path(nb):
 
 def test_stream_semantics(nb):
     w = W.scaled(W.RMS_BF16_16384x4096, M=512, N=4096)
-    inp = W.make_inputs(w)
+    inp = backward_inputs(w)
     g = to_gpu(inp)
     ref = run(nb, w, g)
     s = torch.cuda.Stream()
@@ -333,7 +334,7 @@ def test_stream_semantics(nb):
 
 def test_two_phase_api_matches_full_call(nb):
     w = W.scaled(W.LN_BF16_65536x8192, M=2048, N=2048)
-    g = to_gpu(W.make_inputs(w))
+    g = to_gpu(backward_inputs(w))
     full = run(nb, w, g)
     plan = nb.norm_bwd_make_plan("layernorm", w.M, w.N, w.io_dtype, True)
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
@@ -351,7 +352,7 @@ def test_two_phase_api_matches_full_call(nb):
 def test_two_phase_reduce_output_dtypes(nb, wdt):
     """Kernel B alone rounds the same fp32 sums to any output type."""
     w = W.scaled(W.LN_F16_1151x8192, M=333, N=1000)
-    g = to_gpu(W.make_inputs(w))
+    g = to_gpu(backward_inputs(w))
     plan = nb.norm_bwd_make_plan("layernorm", w.M, w.N, w.io_dtype, True)
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
     dx = torch.empty_like(g["x"])
@@ -392,7 +393,7 @@ def test_empty_problems(nb):
 
 def test_rejects_bad_tensors_before_launch(nb):
     w = W.scaled(W.RMS_BF16_16384x4096, M=64, N=256)
-    g = to_gpu(W.make_inputs(w))
+    g = to_gpu(backward_inputs(w))
     small_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(nb.NormBwdError) as e:
         nb.norm_bwd_rmsnorm(g["x"], g["dy"], g["gamma"], g["rstd"], workspace=small_ws)

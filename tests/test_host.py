@@ -30,7 +30,7 @@ def nb():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(norm_bwd_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(norm_(?:bwd|fwd)_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_documented_entry_points():
@@ -38,7 +38,7 @@ def test_header_declares_the_documented_entry_points():
     for want in ("norm_bwd_layernorm", "norm_bwd_rmsnorm", "norm_bwd_workspace_bytes",
                  "norm_bwd_make_plan", "norm_bwd_execute", "norm_bwd_execute_partials",
                  "norm_bwd_reduce_partials", "norm_bwd_status_string", "norm_bwd_last_error",
-                 "norm_bwd_probe_copy"):
+                 "norm_bwd_probe_copy", "norm_fwd_layernorm", "norm_fwd_rmsnorm"):
         assert want in names
 
 
@@ -267,6 +267,42 @@ def test_reduce_and_probe_reject(nb):
     assert lib.norm_bwd_reduce_partials(4, 8, 1, _addr(0), 16, _addr(1), None, None) == 3
     assert lib.norm_bwd_probe_copy(_addr(0), _addr(1), 17, None) == 1
     assert lib.norm_bwd_probe_copy(_addr(0), ctypes.c_void_p(B + 8), 1024, None) == 1
+
+
+def _fwd(nb, kind, **over):
+    a = dict(x=_addr(0), gamma=_addr(1), beta=_addr(2), M=M_, N=N_, io=2, eps=1e-5, y=_addr(3),
+             mean=_addr(4), rstd=_addr(5), stream=None)
+    a.update(over)
+    lib = nb.load_library()
+    if kind == "layernorm":
+        return lib.norm_fwd_layernorm(a["x"], a["gamma"], a["beta"], a["M"], a["N"], a["io"],
+                                      a["eps"], a["y"], a["mean"], a["rstd"], a["stream"])
+    return lib.norm_fwd_rmsnorm(a["x"], a["gamma"], a["M"], a["N"], a["io"], a["eps"], a["y"],
+                                a["rstd"], a["stream"])
+
+
+@pytest.mark.parametrize("kind", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("over,status", [
+    (dict(x=None), 1), (dict(gamma=None), 1), (dict(y=None), 1),
+    (dict(M=-1), 1), (dict(N=-1), 1), (dict(eps=-1.0), 1), (dict(eps=float("nan")), 1),
+    (dict(io=3), 2), (dict(N=40000), 2), (dict(io=0, N=20000), 2),
+    (dict(y=_addr(0)), 1),                                    # y aliases x
+    (dict(rstd=ctypes.c_void_p(B + 3 * (1 << 30) + 256)), 1),  # rstd inside y
+    (dict(rstd=_addr(1)), 1),                                 # rstd aliases gamma
+])
+@no_gpu
+def test_forward_rejects(nb, kind, over, status):
+    assert _fwd(nb, kind, **over) == status
+    assert nb.norm_bwd_last_error().startswith(nb.norm_bwd_status_string(status))
+
+
+@no_gpu
+def test_forward_layernorm_rejects_overlapping_statistics(nb):
+    assert _fwd(nb, "layernorm", mean=_addr(5)) == 1          # mean aliases rstd
+    assert _fwd(nb, "layernorm", mean=_addr(2)) == 1          # mean aliases beta
+    # empty problems return OK without touching any pointer
+    assert _fwd(nb, "layernorm", M=0, x=None, y=None) == 0
+    assert _fwd(nb, "rmsnorm", N=0, x=None, y=None) == 0
 
 
 def test_binding_refuses_cpu_tensors(nb):

@@ -82,30 +82,13 @@ def test_planted_mistake_is_caught(oracle_mod, tmp_path, name):
     assert caught, f"planted mistake {name} passed every pin"
 
 
-def test_generator_stats_match_oracle_forward(oracle_mod):
-    """The seeded generator's fp32 statistics equal the oracle's fp64 forward
-    statistics rounded to fp32 (two independent implementations)."""
-    from rmsnorm_backward_amd import workloads as W
-    for base in (W.LN_F32_128x512, W.RMS_F32_128x512, W.LN_F16_1151x8192,
-                 W.RMS_BF16_16384x4096, W.LN_BF16_65536x8192, W.RMS_BF16_262144x768):
-        w = W.scaled(base, M=min(base.M, 96), N=min(base.N, 1024))
-        inp = W.make_inputs(w)
-        mean, rstd = oracle_mod.default().fwd_stats(w.kind, inp["x"], w.eps)
-        r32 = torch.from_numpy(rstd).float()
-        assert torch.equal(r32, inp["rstd"]) or \
-            (r32 - inp["rstd"]).abs().max() <= 1e-7 * r32.abs().max()
-        if w.kind == "layernorm":
-            m32 = torch.from_numpy(mean).float()
-            assert (m32 - inp["mean"]).abs().max() <= 1e-7 * (1 + m32.abs().max())
-
-
 def test_generator_is_seeded_and_distributed():
     from rmsnorm_backward_amd import workloads as W
     w = W.scaled(W.RMS_BF16_262144x768, M=512)
     a, b = W.make_inputs(w), W.make_inputs(w)
-    for k in ("x", "dy", "gamma", "rstd"):
+    for k in ("x", "dy", "gamma", "outliers"):
         assert torch.equal(a[k], b[k])
-    assert a["x"].dtype == torch.bfloat16 and a["rstd"].dtype == torch.float32
+    assert a["x"].dtype == torch.bfloat16 and "rstd" not in a and "mean" not in a
     cols = a["outliers"]
     assert cols.numel() == 8                       # 1% of 768 features
     big = a["x"][:, cols].float().abs().mean()
