@@ -74,6 +74,21 @@ def committed_traffic(workload: str):
     return int(t.group(1))
 
 
+def committed_forward_traffic(workload: str):
+    """HBM bytes per forward launch from the same counter summary, if it was
+    taken on the current forward source; else None."""
+    from rmsnorm_backward_amd import profiling
+    path = os.path.join(PROFILES, f"pmc_dx_partials_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"forward_source_sha256_16:\s*([0-9a-f]{16})", text)
+    t = re.search(r"forward_traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not m or not t or m.group(1) != profiling.forward_source_hash():
+        return None
+    return int(t.group(1))
+
+
 def kernel_a_bytes(w) -> int:
     """Algorithmic bytes of one kernel-A launch: x, dy read and dx written
     (3*N*s per row), the saved statistics (4 or 8 B per row), gamma once."""
@@ -305,6 +320,7 @@ def main(argv=None) -> int:
                 "kernel": "norm_fwd_kernel", "us": round(ms_f * 1e3, 3),
                 "bytes_per_launch": f_bytes, "with_beta": "beta" in base,
                 "GBps": round(f_bytes / (ms_f * 1e-3) / 1e9, 2),
+                "traffic": committed_forward_traffic(w.name),
                 "pct_of_peak": round(100 * f_bytes / (ms_f * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
             },
             "plan": {k: v for k, v in plan.as_dict().items()

@@ -11,6 +11,9 @@ namespace nb {
 
 namespace {
 constexpr int64_t kTargetWaves = 2048;  // waves in flight the group count aims at
+// The forward streams one operand per row where kernel A streams two, so it
+// needs twice the waves (16 per compute unit) for as many bytes in flight.
+constexpr int64_t kForwardTargetWaves = 4096;
 constexpr int64_t kMinRowsPerGroup = 8;
 constexpr int64_t kMaxGrid = 1 << 20;
 constexpr int kMaxLdsBytes = 65536 - 1024;  // dynamic LDS; the kernel adds 256 B static
@@ -103,7 +106,7 @@ int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok
 
 int64_t forward_grid(int64_t M, int S, int P) {
   if (M <= 0) return 0;
-  int64_t g = kTargetWaves / (S * P);
+  int64_t g = kForwardTargetWaves / (S * P);
   const int64_t sweep = ceil_div(M, P);
   if (g > sweep) g = sweep;
   if (g > kMaxGrid) g = kMaxGrid;

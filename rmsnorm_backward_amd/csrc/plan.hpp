@@ -27,7 +27,8 @@ int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok
                   norm_bwd_plan_t* plan, const char** why);
 
 // Workgroups of the forward kernel for M rows with S waves per row and P rows
-// in flight: enough for about kTargetWaves waves, at most one sweep of rows.
+// in flight: enough for about 4096 waves (16 per compute unit), at most one
+// sweep of rows.
 int64_t forward_grid(int64_t M, int S, int P);
 
 // Automatic group count for (kind, M, N, io_dtype): independent of the device.

@@ -31,14 +31,29 @@ import sys
 
 KERNEL_A = "dx_partials_kernel"
 KERNEL_B = "reduce_partials_kernel"
+FORWARD = "norm_fwd_kernel"
 COPY = "copy_probe_kernel"
 _HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCE = os.path.join(_HERE, "csrc", "nb_device.hpp")
+FORWARD_SOURCES = (KERNEL_SOURCE, os.path.join(_HERE, "csrc", "nb_forward.hpp"))
+
+
+def _hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of kernel A's source (the counters are valid while it holds)."""
+    return _hash([KERNEL_SOURCE])
+
+
+def forward_source_hash() -> str:
+    """Hash of the forward kernel's sources."""
+    return _hash(FORWARD_SOURCES)
 
 
 def _bench(path):
@@ -59,13 +74,15 @@ def stats_summary(stats_csv: str, bench_json: str, cmds) -> str:
     out += list(cmds) + ["```", "",
                          "| kernel | calls | average (us) | min (us) | max (us) | share |",
                          "|---|---|---|---|---|---|"]
-    avg_a = None
+    avg_a = avg_f = None
     for r in rows:
         name = r["Name"]
         short = name.split("(")[0].replace("void ", "")
         avg = float(r["AverageNs"]) / 1e3
         if KERNEL_A in name:
             avg_a = avg
+        if FORWARD in name:
+            avg_f = avg
         out.append(f"| `{short}` | {r['Calls']} | {avg:.2f} | {float(r['MinNs'])/1e3:.2f} | "
                    f"{float(r['MaxNs'])/1e3:.2f} | {float(r['Percentage']):.1f}% |")
     out += ["", "Benchmark line of the same run (HIP events on the launch stream):", "",
@@ -75,7 +92,15 @@ def stats_summary(stats_csv: str, bench_json: str, cmds) -> str:
     if avg_a is not None:
         out.append(f"- kernel A by the trace: {avg_a:.2f} us "
                    f"(events / trace = {c['kernel_a_us'] / avg_a:.3f})")
-    out += ["", f"kernel_source_sha256_16: {kernel_source_hash()}", ""]
+    fw = c.get("forward")
+    if fw:
+        out.append(f"- forward by events: {fw['us']} us, {fw['GBps']} GB/s "
+                   f"({fw['pct_of_peak']}% of 8 TB/s)")
+        if avg_f is not None:
+            out.append(f"- forward by the trace: {avg_f:.2f} us "
+                       f"(events / trace = {fw['us'] / avg_f:.3f})")
+    out += ["", f"kernel_source_sha256_16: {kernel_source_hash()}",
+            f"forward_source_sha256_16: {forward_source_hash()}", ""]
     return "\n".join(out)
 
 
@@ -133,6 +158,21 @@ def pmc_summary(fetch_csv: str, write_csv: str, bench_json: str, cmds) -> str:
     if fb is not None and wb is not None:
         out.append(f"Kernel B per launch: FETCH_SIZE {fb:.1f} KiB ({fb*1024*fscale:.0f} B), "
                    f"WRITE_SIZE {wb:.1f} KiB ({wb*1024*wscale:.0f} B); workspace {ws} B.")
+    ff, nf = _mean_for(f, FORWARD)
+    wf, _ = _mean_for(w, FORWARD)
+    fw = c.get("forward")
+    ftraffic = None
+    if ff is not None and wf is not None and fw:
+        fr, fwb = ff * 1024.0 * fscale, wf * 1024.0 * wscale
+        ftraffic = int(round(fr + fwb))
+        falg = fw["bytes_per_launch"]
+        out += ["", "| forward, per launch | counter (KiB) | scaled bytes |", "|---|---|---|",
+                f"| read (FETCH_SIZE) | {ff:.1f} | {fr:.0f} |",
+                f"| write (WRITE_SIZE) | {wf:.1f} | {fwb:.0f} |",
+                f"| total | | {ftraffic} (algorithmic {falg}, ratio {ftraffic / falg:.4f}) |",
+                "", f"forward launches counted: {nf}",
+                f"forward_traffic_bytes_per_launch: {ftraffic}",
+                f"forward_source_sha256_16: {forward_source_hash()}"]
     out += ["", f"kernel A launches counted: {na}",
             f"traffic_bytes_per_launch: {traffic}",
             f"kernel_source_sha256_16: {kernel_source_hash()}", ""]
