@@ -272,6 +272,21 @@ def main(argv=None) -> int:
     ms_f = time_loop(torch, step_f, args.steps, stream)
     f_bytes = forward_bytes(w, "beta" in base)
 
+    # the backward in recompute mode: NULL statistics, recomputed from x
+    rc_args = [(a[0], a[1], a[2], None, None) + a[5:] if w.kind == "layernorm"
+                else (a[0], a[1], a[2], None) + a[4:] for a in full_args]
+    fn_rc = lib.norm_bwd_layernorm if w.kind == "layernorm" else lib.norm_bwd_rmsnorm
+
+    def step_rc(i):
+        st = fn_rc(*rc_args[i % nsets])
+        if st:
+            raise RuntimeError(nb.norm_bwd_last_error())
+
+    for i in range(min(args.warmup, 50)):
+        step_rc(i)
+    ms_rc = time_loop(torch, step_rc, args.steps, stream)
+    rc_bytes = w.algorithmic_bytes() - w.M * (8 if w.kind == "layernorm" else 4)
+
     # copy probe: the achievable streaming ceiling next to the kernels
     cp_bytes = min(512 << 20, max(set_bytes // 3 * 2, 64 << 20)) // 16 * 16
     src = torch.empty(cp_bytes // 4, dtype=torch.int32, device=dev).fill_(1)
@@ -322,6 +337,12 @@ def main(argv=None) -> int:
                 "GBps": round(f_bytes / (ms_f * 1e-3) / 1e9, 2),
                 "traffic": committed_forward_traffic(w.name),
                 "pct_of_peak": round(100 * f_bytes / (ms_f * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+            },
+            "recompute": {
+                "what": "whole backward step with mean/rstd recomputed from x (no stats read)",
+                "us": round(ms_rc * 1e3, 3), "bytes": rc_bytes,
+                "GBps": round(rc_bytes / (ms_rc * 1e-3) / 1e9, 2),
+                "pct_of_peak": round(100 * rc_bytes / (ms_rc * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
             },
             "plan": {k: v for k, v in plan.as_dict().items()
                      if k in ("groups", "rows_per_group", "vec", "chunks", "waves_per_row",

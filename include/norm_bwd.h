@@ -82,14 +82,23 @@ extern "C" {
  * "05: Layer norm" kernels ln_bwd_dx and ln_bwd_dwdb).
  *
  *   x, dy, gamma   [M,N], [M,N], [N] in io_dtype (read)
- *   mean, rstd     fp32 [M], the forward's saved statistics (read)
+ *   mean, rstd     fp32 [M], the forward's saved statistics (read); or both
+ *                  NULL: recompute mode, in which each row's statistics are
+ *                  computed from x in fp32 as the forward does (mean =
+ *                  sum(x)/N, then var = sum((x - mean)^2)/N, rstd =
+ *                  1/sqrt(var + eps)) before the gradient. This follows the
+ *                  option of recomputing sigma on chip rather than reading
+ *                  it ("Norm & activation backward", "Half one"). Exactly
+ *                  one of them NULL is NORM_BWD_ERR_INVALID_ARG.
  *   M, N           rows and features, >= 0. M = 0 writes zeros to dgamma and
  *                  dbeta (the empty sum); N = 0 does nothing.
  *   io_dtype       NORM_BWD_F32 / F16 / BF16
  *   wgrad_dtype    NORM_BWD_F32 or io_dtype: dgamma/dbeta are accumulated in
  *                  fp32 and rounded (to nearest even) once at the end
- *   eps            the forward's epsilon; checked (finite, >= 0) but unused,
- *                  because rstd already contains it
+ *   eps            the forward's epsilon; checked (finite, >= 0); used only
+ *                  in recompute mode (a saved rstd already contains it).
+ *                  With eps = 0 a constant row has rstd = inf, and its dx is
+ *                  not finite, as the formula gives.
  *   dx             [M,N] io_dtype (written, rounded to nearest even)
  *   dgamma         [N] wgrad_dtype (written)
  *   dbeta          [N] wgrad_dtype (written), or NULL to skip it
@@ -110,7 +119,8 @@ int norm_bwd_layernorm(const void *x, const void *dy, const void *gamma,
  * xhat = x * rstd and dx loses the mean_j(dyhat) term). Same arguments as
  * norm_bwd_layernorm without `mean`. dbeta may be NULL (RMSNorm has no bias);
  * when given it receives the column sum of dy, which does not depend on the
- * normalisation.
+ * normalisation. rstd = NULL selects recompute mode (rstd = 1/sqrt(sum(x^2)/N
+ * + eps) per row, from x).
  */
 int norm_bwd_rmsnorm(const void *x, const void *dy, const void *gamma,
                      const float *rstd, int64_t M, int64_t N, int io_dtype,
@@ -154,8 +164,9 @@ typedef struct norm_bwd_plan {
 
 /*
  * Fill *plan for (kind, M, N, io_dtype, with_dbeta). groups = 0 chooses the
- * automatic group count (min(512, ceil(M / 8)): a function of the problem
- * only, never of the device); groups > 0 asks for that many row groups,
+ * automatic group count (2048 / (waves per workgroup), at most ceil(M / 8):
+ * a function of the problem only, never of the device); groups > 0 asks for
+ * that many row groups,
  * clamped to M so that no group is empty. The plan
  * assumes 16-byte aligned base pointers; norm_bwd_execute rejects a plan
  * whose vec the pointers do not allow. Host-only. Returns a status code.
@@ -166,7 +177,9 @@ int norm_bwd_make_plan(int kind, int64_t M, int64_t N, int io_dtype,
 /*
  * Run kernel A then kernel B of `plan` on `stream` (the whole backward pass).
  * mean is ignored for RMSNorm. dbeta must be non-NULL exactly when
- * plan->with_dbeta. Other arguments as for norm_bwd_layernorm.
+ * plan->with_dbeta. Other arguments as for norm_bwd_layernorm, except that
+ * the saved statistics are required (there is no eps argument, so no
+ * recompute mode: use norm_bwd_layernorm / norm_bwd_rmsnorm for that).
  */
 int norm_bwd_execute(const norm_bwd_plan_t *plan, const void *x,
                      const void *dy, const void *gamma, const float *mean,

@@ -184,19 +184,25 @@ def norm_bwd_make_plan(kind, M: int, N: int, io_dtype, with_dbeta: bool,
 def _backward(kind, x, dy, gamma, mean, rstd, eps, wgrad_dtype, dx, dgamma, dbeta,
               with_dbeta, workspace, stream, plan: Optional[NormBwdPlan]):
     lib = load_library()
-    for t, n in ((x, "x"), (dy, "dy"), (gamma, "gamma"), (rstd, "rstd")):
+    for t, n in ((x, "x"), (dy, "dy"), (gamma, "gamma")):
         _gpu(t, n)
-    if kind == LAYERNORM:
-        _gpu(mean, "mean")
+    # rstd None (LayerNorm: mean and rstd None) selects the recompute mode
+    recompute = rstd is None
+    if kind == LAYERNORM and (mean is None) != recompute:
+        raise ValueError("LayerNorm takes both mean and rstd, or neither (recompute)")
+    if recompute and plan is not None:
+        raise ValueError("an explicit plan needs the saved statistics")
     M, N = _rows(x)
     io = _code(x.dtype, "x")
     if dy.dtype != x.dtype or gamma.dtype != x.dtype:
         raise ValueError("x, dy and gamma must share one dtype")
-    if dy.shape != x.shape or gamma.numel() != N or rstd.numel() != M:
-        raise ValueError("shape mismatch: dy like x, gamma [N], rstd [M]")
-    if rstd.dtype != torch.float32 or (kind == LAYERNORM and
-                                       (mean.dtype != torch.float32 or mean.numel() != M)):
-        raise ValueError("mean and rstd must be float32 [M]")
+    if dy.shape != x.shape or gamma.numel() != N:
+        raise ValueError("shape mismatch: dy like x, gamma [N]")
+    for t, n in ((rstd, "rstd"), (mean if kind == LAYERNORM else None, "mean")):
+        if t is not None:
+            _gpu(t, n)
+            if t.dtype != torch.float32 or t.numel() != M:
+                raise ValueError("mean and rstd must be float32 [M]")
     wgrad_dtype = wgrad_dtype or torch.float32
     wcode = _code(wgrad_dtype, "wgrad")
     dev = x.device
@@ -236,21 +242,24 @@ def _backward(kind, x, dy, gamma, mean, rstd, eps, wgrad_dtype, dx, dgamma, dbet
 
 
 def norm_bwd_layernorm(x: torch.Tensor, dy: torch.Tensor, gamma: torch.Tensor,
-                       mean: torch.Tensor, rstd: torch.Tensor, eps: float = 1e-5, *,
+                       mean: Optional[torch.Tensor], rstd: Optional[torch.Tensor],
+                       eps: float = 1e-5, *,
                        wgrad_dtype: Optional[torch.dtype] = None, dx=None, dgamma=None,
                        dbeta=None, with_dbeta: bool = True, workspace=None, stream=None
                        ) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
-    """LayerNorm backward on the GPU: returns (dx, dgamma, dbeta)."""
+    """LayerNorm backward on the GPU: returns (dx, dgamma, dbeta). mean = rstd =
+    None recomputes the statistics from x with eps."""
     return _backward(LAYERNORM, x, dy, gamma, mean, rstd, eps, wgrad_dtype, dx, dgamma, dbeta,
                      with_dbeta or dbeta is not None, workspace, stream, None)
 
 
 def norm_bwd_rmsnorm(x: torch.Tensor, dy: torch.Tensor, gamma: torch.Tensor,
-                     rstd: torch.Tensor, eps: float = 1e-6, *,
+                     rstd: Optional[torch.Tensor], eps: float = 1e-6, *,
                      wgrad_dtype: Optional[torch.dtype] = None, dx=None, dgamma=None,
                      dbeta=None, with_dbeta: bool = False, workspace=None, stream=None
                      ) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
-    """RMSNorm backward on the GPU: returns (dx, dgamma, dbeta or None)."""
+    """RMSNorm backward on the GPU: returns (dx, dgamma, dbeta or None). rstd =
+    None recomputes it from x with eps."""
     return _backward(RMSNORM, x, dy, gamma, None, rstd, eps, wgrad_dtype, dx, dgamma, dbeta,
                      with_dbeta or dbeta is not None, workspace, stream, None)
 

@@ -22,7 +22,8 @@ LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libnorm_bwd.so")
 
 SOURCES = ["api.cpp", "plan.cpp", "reduce.hip", "kernels_f32.hip", "kernels_f16.hip",
-           "kernels_bf16.hip"]
+           "kernels_bf16.hip", "kernels_f32_recompute.hip", "kernels_f16_recompute.hip",
+           "kernels_bf16_recompute.hip"]
 ARCH = "gfx950"
 
 
@@ -38,6 +39,9 @@ def common_flags():
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # no packed-fp32 instructions anywhere in the device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # no implicit multiply-add fusion: every fma is written in the source,
+        # so the rounding of each result follows from the source alone
+        "-ffp-contract=off",
         "-Wall", "-Wno-unused-command-line-argument",
         "-I", INCLUDE, "-I", CSRC,
     ]

@@ -41,8 +41,9 @@ struct Buffers {
 };
 
 // Checks shared by every entry point that runs kernel A and/or kernel B.
+// `recompute`: kernel A computes the statistics from x (mean/rstd are NULL).
 int check_buffers(int kind, int64_t M, int64_t N, int io_dtype, int wgrad_dtype, bool run_a,
-                  bool run_b, size_t ws_needed, const Buffers& b) {
+                  bool run_b, size_t ws_needed, const Buffers& b, bool recompute = false) {
   const int eb = nb::dtype_bytes(io_dtype);
   const int wb = nb::dtype_bytes(wgrad_dtype);
   if (run_b) {
@@ -57,9 +58,11 @@ int check_buffers(int kind, int64_t M, int64_t N, int io_dtype, int wgrad_dtype,
   if (N == 0) return NORM_BWD_OK;
   const bool rows = run_a && M > 0;
   if (rows) {
-    if (!b.x || !b.dy || !b.gamma || !b.rstd || !b.dx)
-      return set_error(NORM_BWD_ERR_INVALID_ARG, "x, dy, gamma, rstd and dx must be non-NULL");
-    if (kind == NORM_BWD_LAYERNORM && !b.mean)
+    if (!b.x || !b.dy || !b.gamma || !b.dx)
+      return set_error(NORM_BWD_ERR_INVALID_ARG, "x, dy, gamma and dx must be non-NULL");
+    if (!recompute && !b.rstd)
+      return set_error(NORM_BWD_ERR_INVALID_ARG, "rstd must be non-NULL");
+    if (!recompute && kind == NORM_BWD_LAYERNORM && !b.mean)
       return set_error(NORM_BWD_ERR_INVALID_ARG, "LayerNorm needs mean");
   }
   if (run_b && !b.dgamma) return set_error(NORM_BWD_ERR_INVALID_ARG, "dgamma must be non-NULL");
@@ -77,8 +80,8 @@ int check_buffers(int kind, int64_t M, int64_t N, int io_dtype, int wgrad_dtype,
   const R inputs[] = {{rows ? b.x : nullptr, mat},
                       {rows ? b.dy : nullptr, mat},
                       {rows ? b.gamma : nullptr, vec_in},
-                      {rows && kind == NORM_BWD_LAYERNORM ? b.mean : nullptr, stat},
-                      {rows ? b.rstd : nullptr, stat}};
+                      {rows && !recompute && kind == NORM_BWD_LAYERNORM ? b.mean : nullptr, stat},
+                      {rows && !recompute ? b.rstd : nullptr, stat}};
   const R outputs[] = {{rows ? b.dx : nullptr, mat},
                        {run_b ? b.dgamma : nullptr, vec_out},
                        {run_b ? b.dbeta : nullptr, vec_out},
@@ -95,7 +98,8 @@ int check_buffers(int kind, int64_t M, int64_t N, int io_dtype, int wgrad_dtype,
   return NORM_BWD_OK;
 }
 
-int launch_partials(const norm_bwd_plan_t& p, const Buffers& b, hipStream_t stream) {
+int launch_partials(const norm_bwd_plan_t& p, const Buffers& b, hipStream_t stream,
+                    bool recompute = false, float eps = 0.0f) {
   if (p.M == 0 || p.N == 0) return NORM_BWD_OK;
   nb::LaunchA a;
   a.kind = p.kind;
@@ -118,6 +122,8 @@ int launch_partials(const norm_bwd_plan_t& p, const Buffers& b, hipStream_t stre
   a.threads = p.threads;
   a.grid = p.grid;
   a.lds = p.lds_bytes;
+  a.recompute = recompute ? 1 : 0;
+  a.eps = eps;
   a.stream = stream;
   (void)hipGetLastError();  // clear a stale error so a launch failure is ours
   hipError_t e;
@@ -156,16 +162,22 @@ int run_auto(int kind, const void* x, const void* dy, const void* gamma, const f
              void* stream) {
   if (!(eps >= 0.0f) || isinf(eps))
     return set_error(NORM_BWD_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  // NULL statistics (LayerNorm: both) select the recompute mode
+  if (kind == NORM_BWD_LAYERNORM && (mean == nullptr) != (rstd == nullptr))
+    return set_error(NORM_BWD_ERR_INVALID_ARG,
+                     "LayerNorm takes both mean and rstd, or neither (recompute)");
+  const bool recompute = rstd == nullptr;
   const bool vec_ok = aligned16(x) && aligned16(dy) && aligned16(gamma) && aligned16(dx);
   norm_bwd_plan_t p;
   const char* why = nullptr;
   int st = nb::make_plan(kind, M, N, io_dtype, dbeta ? 1 : 0, 0, vec_ok, &p, &why);
   if (st != NORM_BWD_OK) return set_error(st, why);
   Buffers b{x, dy, gamma, mean, rstd, dx, dgamma, dbeta, workspace, workspace_bytes};
-  st = check_buffers(kind, M, N, io_dtype, wgrad_dtype, true, true, p.workspace_bytes, b);
+  st = check_buffers(kind, M, N, io_dtype, wgrad_dtype, true, true, p.workspace_bytes, b,
+                     recompute);
   if (st != NORM_BWD_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = launch_partials(p, b, s);
+  st = launch_partials(p, b, s, recompute, eps);
   if (st != NORM_BWD_OK) return st;
   return launch_reduce(p.groups, N, wgrad_dtype, workspace, dgamma, dbeta, s);
 }

@@ -3,6 +3,8 @@
 #include "nb_launch_a.hpp"
 
 namespace nb {
-hipError_t launch_a_bf16(const LaunchA& a) { return launch_a_impl<TBF16>(a); }
+hipError_t launch_a_bf16(const LaunchA& a) {
+  return a.recompute ? launch_a_recompute_bf16(a) : launch_a_impl<TBF16, false>(a);
+}
 hipError_t launch_f_bf16(const LaunchF& f) { return launch_f_impl<TBF16>(f); }
 }  // namespace nb

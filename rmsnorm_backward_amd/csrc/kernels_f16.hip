@@ -3,6 +3,8 @@
 #include "nb_launch_a.hpp"
 
 namespace nb {
-hipError_t launch_a_f16(const LaunchA& a) { return launch_a_impl<TF16>(a); }
+hipError_t launch_a_f16(const LaunchA& a) {
+  return a.recompute ? launch_a_recompute_f16(a) : launch_a_impl<TF16, false>(a);
+}
 hipError_t launch_f_f16(const LaunchF& f) { return launch_f_impl<TF16>(f); }
 }  // namespace nb

@@ -3,6 +3,8 @@
 #include "nb_launch_a.hpp"
 
 namespace nb {
-hipError_t launch_a_f32(const LaunchA& a) { return launch_a_impl<TF32>(a); }
+hipError_t launch_a_f32(const LaunchA& a) {
+  return a.recompute ? launch_a_recompute_f32(a) : launch_a_impl<TF32, false>(a);
+}
 hipError_t launch_f_f32(const LaunchF& f) { return launch_f_impl<TF32>(f); }
 }  // namespace nb

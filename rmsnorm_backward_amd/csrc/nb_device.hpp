@@ -277,8 +277,9 @@ struct RowBuf {
 
 // Issue the loads of row r into b. Nothing is loaded for an inactive row or
 // for a lane's chunks past the row's end; process_row never reads those
-// registers (it skips exactly the same cases).
-template <int KIND, class Tg, int VEC, int C>
+// registers (it skips exactly the same cases). With RECOMP the statistics are
+// not loaded: process_row computes them from x.
+template <int KIND, bool RECOMP, class Tg, int VEC, int C>
 __device__ __forceinline__ void fetch_row(RowBuf<Tg, VEC, C>& b, const char* __restrict__ x,
                                           const char* __restrict__ dy,
                                           const float* __restrict__ mean,
@@ -286,9 +287,11 @@ __device__ __forceinline__ void fetch_row(RowBuf<Tg, VEC, C>& b, const char* __r
                                           int N, int col0, int cstride) {
   constexpr int EB = Tg::kBytes;
   if (active) {
-    const int64_t rz = r + opaque_lane_zero();
-    b.rs = rstd[rz];
-    b.mu = (KIND == kLayerNorm) ? mean[rz] : 0.0f;
+    if constexpr (!RECOMP) {
+      const int64_t rz = r + opaque_lane_zero();
+      b.rs = rstd[rz];
+      b.mu = (KIND == kLayerNorm) ? mean[rz] : 0.0f;
+    }
     const int64_t rb = r * (int64_t)N;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -313,39 +316,105 @@ __device__ __forceinline__ void fetch_row(RowBuf<Tg, VEC, C>& b, const char* __r
 //              = dyhat * rstd + xc * c2 + c1,
 //           with the per-row constants mean(dyhat * xhat) = rstd * s2 / N,
 //           c2 = -rstd^2 * mean(dyhat * xhat) and c1 = -rstd * s1 / N.
-template <int KIND, class Tg, int VEC, int C, int NACC>
+// With RECOMP the statistics are recomputed from the row in registers, as
+// the forward computes them: LayerNorm first sums x (with s1 = sum dyhat in
+// the same exchange), then with mean = sum(x)/N sums xc^2 and dyhat * xc;
+// RMSNorm sums x^2 and dyhat * x in one exchange. rstd = 1/sqrt(sum(xc^2)/N
+// + eps). The dgamma terms, which need rstd, are then accumulated before
+// pass 2.
+template <int KIND, bool RECOMP, class Tg, int VEC, int C, int NACC>
 __device__ __forceinline__ void process_row(RowBuf<Tg, VEC, C>& b, const float (&gam)[C][VEC],
                                             float (&acc)[NACC][C][VEC], char* __restrict__ dx,
                                             float (*red)[kMaxWaves][2], int& phase, int64_t r,
-                                            bool active, int N, float inv_n, int col0, int cstride,
-                                            int lane, int wave, int S, int p) {
+                                            bool active, int N, float inv_n, float eps, int col0,
+                                            int cstride, int lane, int wave, int S, int p) {
   constexpr int EB = Tg::kBytes;
   float s1 = 0.0f, s2 = 0.0f;
-  if (active) {
+  float mu, rs;
+  if constexpr (!RECOMP) {
+    mu = b.mu;
+    rs = b.rs;
+    if (active) {
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      if (col0 + c * cstride < N) {
+      for (int c = 0; c < C; ++c) {
+        if (col0 + c * cstride < N) {
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-          const float xc = b.x[c].get(v) - b.mu;
-          const float dyv = b.dy[c].get(v);
-          const float dyh = dyv * gam[c][v];
-          if (KIND == kLayerNorm) s1 += dyh;
-          s2 = __builtin_fmaf(dyh, xc, s2);
-          acc[0][c][v] = __builtin_fmaf(dyv * xc, b.rs, acc[0][c][v]);
-          if (NACC == 2) acc[NACC - 1][c][v] += dyv;
+          for (int v = 0; v < VEC; ++v) {
+            const float xc = b.x[c].get(v) - mu;
+            const float dyv = b.dy[c].get(v);
+            const float dyh = dyv * gam[c][v];
+            if (KIND == kLayerNorm) s1 = __builtin_fmaf(dyv, gam[c][v], s1);
+            s2 = __builtin_fmaf(dyh, xc, s2);
+            acc[0][c][v] = __builtin_fmaf(dyv * xc, rs, acc[0][c][v]);
+            if (NACC == 2) acc[NACC - 1][c][v] += dyv;
+          }
         }
       }
     }
+    pin(acc);
+    keep_packed(b.x);
+    keep_packed(b.dy);
+    row_sum2<KIND == kLayerNorm>(s1, s2, red, phase, lane, wave, S, p);
+  } else {
+    mu = 0.0f;
+    if constexpr (KIND == kLayerNorm) {
+      float sx = 0.0f;
+      if (active) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          if (col0 + c * cstride < N) {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+              const float dyv = b.dy[c].get(v);
+              sx += b.x[c].get(v);
+              s1 = __builtin_fmaf(dyv, gam[c][v], s1);
+              if (NACC == 2) acc[NACC - 1][c][v] += dyv;
+            }
+          }
+        }
+      }
+      keep_packed(b.x);
+      keep_packed(b.dy);
+      row_sum2<true>(sx, s1, red, phase, lane, wave, S, p);
+      mu = sx * inv_n;
+    }
+    float sxx = 0.0f;
+    if (active) {
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        if (col0 + c * cstride < N) {
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) {
+            const float xc = b.x[c].get(v) - mu;
+            const float dyv = b.dy[c].get(v);
+            sxx = __builtin_fmaf(xc, xc, sxx);
+            s2 = __builtin_fmaf(dyv * gam[c][v], xc, s2);
+            if (KIND != kLayerNorm && NACC == 2) acc[NACC - 1][c][v] += dyv;
+          }
+        }
+      }
+    }
+    keep_packed(b.x);
+    keep_packed(b.dy);
+    row_sum2<true>(sxx, s2, red, phase, lane, wave, S, p);
+    rs = 1.0f / __builtin_sqrtf(__builtin_fmaf(sxx, inv_n, eps));
+    if (active) {
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        if (col0 + c * cstride < N) {
+#pragma unroll
+          for (int v = 0; v < VEC; ++v)
+            acc[0][c][v] = __builtin_fmaf(b.dy[c].get(v) * (b.x[c].get(v) - mu), rs,
+                                          acc[0][c][v]);
+        }
+      }
+    }
+    pin(acc);
   }
-  pin(acc);
-  keep_packed(b.x);
-  keep_packed(b.dy);
-  row_sum2<KIND == kLayerNorm>(s1, s2, red, phase, lane, wave, S, p);
   if (active) {
-    const float m2 = s2 * inv_n * b.rs;  // mean_j(dyhat * xhat)
-    const float c2 = -(b.rs * b.rs) * m2;
-    const float c1 = (KIND == kLayerNorm) ? -b.rs * (s1 * inv_n) : 0.0f;
+    const float m2 = s2 * inv_n * rs;  // mean_j(dyhat * xhat)
+    const float c2 = -(rs * rs) * m2;
+    const float c1 = (KIND == kLayerNorm) ? -rs * (s1 * inv_n) : 0.0f;
     const int64_t rb = r * (int64_t)N;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -354,9 +423,9 @@ __device__ __forceinline__ void process_row(RowBuf<Tg, VEC, C>& b, const float (
         float o[VEC];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
-          const float xc = b.x[c].get(v) - b.mu;
+          const float xc = b.x[c].get(v) - mu;
           const float dyh = b.dy[c].get(v) * gam[c][v];
-          o[v] = __builtin_fmaf(dyh, b.rs, __builtin_fmaf(xc, c2, c1));
+          o[v] = __builtin_fmaf(dyh, rs, __builtin_fmaf(xc, c2, c1));
         }
         Pack<Tg, VEC> out;
         out.set(o);
@@ -366,13 +435,13 @@ __device__ __forceinline__ void process_row(RowBuf<Tg, VEC, C>& b, const float (
   }
 }
 
-template <int KIND, class Tg, int VEC, int C, int NACC>
+template <int KIND, bool RECOMP, class Tg, int VEC, int C, int NACC>
 __global__ __launch_bounds__((max_threads_for<VEC, C>()))
 void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dyv,
                         const void* __restrict__ gv, const float* __restrict__ mean,
                         const float* __restrict__ rstd, void* __restrict__ dxv,
                         float* __restrict__ ws, int64_t M, int N, int64_t G, int64_t R,
-                        int S, int P) {
+                        int S, int P, float eps) {
   using PK = Pack<Tg, VEC>;
   using RB = RowBuf<Tg, VEC, C>;
   constexpr int EB = Tg::kBytes;
@@ -430,7 +499,7 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
     for (int k = 0; k < D - 1; ++k) {
       if (k < iters) {
         const int64_t rk = row_of(k);
-        fetch_row<KIND>(buf[k], x, dy, mean, rstd, rk, rk < M, N, col0, cstride);
+        fetch_row<KIND, RECOMP>(buf[k], x, dy, mean, rstd, rk, rk < M, N, col0, cstride);
       }
     }
     for (int it = 0; it < iters; it += D) {
@@ -439,13 +508,13 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
         const int k = it + d;
         if (k + D - 1 < iters) {
           const int64_t rf = row_of(k + D - 1);
-          fetch_row<KIND>(buf[(d + D - 1) % D], x, dy, mean, rstd, rf, rf < M, N, col0,
-                          cstride);
+          fetch_row<KIND, RECOMP>(buf[(d + D - 1) % D], x, dy, mean, rstd, rf, rf < M, N,
+                                  col0, cstride);
         }
         if (k < iters) {
           const int64_t rk = row_of(k);
-          process_row<KIND>(buf[d], gam, acc, dx, red, phase, rk, rk < M, N, inv_n, col0,
-                            cstride, lane, wave, S, p);
+          process_row<KIND, RECOMP>(buf[d], gam, acc, dx, red, phase, rk, rk < M, N, inv_n,
+                                    eps, col0, cstride, lane, wave, S, p);
         }
       }
     }

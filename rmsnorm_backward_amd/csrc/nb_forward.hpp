@@ -110,7 +110,7 @@ void norm_fwd_kernel(const void* __restrict__ xv, const void* __restrict__ gv,
     keep_packed(b.x);
     row_sum2<false>(unused, s2, red, phase, lane, wave, S, p);
     if (active) {
-      const float rs = 1.0f / __builtin_sqrtf(s2 * inv_n + eps);
+      const float rs = 1.0f / __builtin_sqrtf(__builtin_fmaf(s2, inv_n, eps));
       const int64_t rb = r * (int64_t)N;
 #pragma unroll
       for (int c = 0; c < C; ++c) {

@@ -23,6 +23,8 @@ struct LaunchA {
   int N;
   int64_t G, R;
   int S, P, threads, grid, lds;
+  int recompute;  // 1: mean/rstd are NULL and recomputed from x with eps
+  float eps;
   hipStream_t stream;
 };
 
@@ -46,6 +48,9 @@ struct LaunchF {
 hipError_t launch_a_f32(const LaunchA& a);
 hipError_t launch_a_f16(const LaunchA& a);
 hipError_t launch_a_bf16(const LaunchA& a);
+hipError_t launch_a_recompute_f32(const LaunchA& a);
+hipError_t launch_a_recompute_f16(const LaunchA& a);
+hipError_t launch_a_recompute_bf16(const LaunchA& a);
 hipError_t launch_f_f32(const LaunchF& f);
 hipError_t launch_f_f16(const LaunchF& f);
 hipError_t launch_f_bf16(const LaunchF& f);

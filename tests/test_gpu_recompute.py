@@ -1,0 +1,193 @@
+"""Recompute mode of the GPU backward (mean/rstd = NULL) against the oracle.
+
+In this mode kernel A computes each row's statistics from x with eps before
+the gradient (recomputing sigma on chip instead of reading it: "Norm &
+activation backward", "Half one"). The reference is the oracle's backward on
+the oracle's fp64 forward statistics of the same x and eps; the tolerance adds
+the first-order effect of fp32 statistics (parity.recompute_terms).
+"""
+
+from __future__ import annotations
+
+import pytest
+import torch
+
+import oracle
+import parity
+from rmsnorm_backward_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nb():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import rmsnorm_backward_amd as nbmod
+    nbmod.load_library()
+    return nbmod
+
+
+def run_recompute(nb, w, x, dy, gamma, with_db, eps=None):
+    eps = w.eps if eps is None else eps
+    x, dy, gamma = x.cuda(), dy.cuda(), gamma.cuda()
+    if w.kind == "layernorm":
+        out = nb.norm_bwd_layernorm(x, dy, gamma, None, None, eps, wgrad_dtype=w.wgrad_dtype,
+                                    with_dbeta=with_db)
+    else:
+        out = nb.norm_bwd_rmsnorm(x, dy, gamma, None, eps, wgrad_dtype=w.wgrad_dtype,
+                                  with_dbeta=with_db)
+    torch.cuda.synchronize()
+    return tuple(None if t is None else t.cpu() for t in out)
+
+
+def compare(w, x, dy, gamma, out, with_db, eps=None, rows=None, cols=None):
+    """Check dx on `rows` (all by default) and dgamma/dbeta on `cols`."""
+    eps = w.eps if eps is None else eps
+    dx, dg, db = out
+    mean, rstd = oracle.fwd_stats(w.kind, x, eps)          # fp64, not rounded
+    xs, dys = (x, dy) if rows is None else (x[rows], dy[rows])
+    ms = None if mean is None else (mean if rows is None else mean[rows.numpy()])
+    rs = rstd if rows is None else rstd[rows.numpy()]
+    rdx = oracle.bwd_dx(w.kind, xs, dys, gamma, ms, rs)
+    t_dx, _ = parity.recompute_terms(w.kind, xs, dys, gamma, ms, rs)
+    parity.check_dx(w.io_dtype, dx if rows is None else dx[rows], rdx, scale=t_dx,
+                    coef32=2.0 ** -16)
+    xc, dyc = (x, dy) if cols is None else (x[:, cols], dy[:, cols])
+    rdg, rdb = oracle.bwd_wgrad(w.kind, xc, dyc, mean, rstd, want_dbeta=True)
+    _, t_dg = parity.recompute_terms(w.kind, xc, dyc, gamma if cols is None else gamma[cols],
+                                     mean, rstd)
+    parity.check_wgrad(w.io_dtype, dg if cols is None else dg[cols], rdg,
+                       extra=2.0 ** -16 * t_dg)
+    if with_db:
+        parity.check_wgrad(w.io_dtype, db if cols is None else db[cols], rdb, "dbeta")
+
+
+SMALL = [
+    W.LN_F32_128x512,
+    W.RMS_F32_128x512,
+    W.LN_F16_1151x8192,
+    W.scaled(W.RMS_BF16_16384x4096, M=2003),
+    W.scaled(W.LN_BF16_65536x8192, M=777),
+    W.scaled(W.RMS_BF16_262144x768, M=5001),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_recompute_parity(nb, w):
+    inp = W.make_inputs(w)
+    for with_db in (w.kind == "layernorm", w.kind != "layernorm"):
+        out = run_recompute(nb, w, inp["x"], inp["dy"], inp["gamma"], with_db)
+        compare(w, inp["x"], inp["dy"], inp["gamma"], out, with_db)
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-3, 1.0, 100.0])
+@pytest.mark.parametrize("kind", ["layernorm", "rmsnorm"])
+def test_recompute_uses_eps(nb, kind, eps):
+    """eps enters rstd = 1/sqrt(var + eps); a large eps changes dx a lot, so
+    a kernel that dropped or misplaced it fails here."""
+    base = W.LN_F32_128x512 if kind == "layernorm" else W.RMS_F32_128x512
+    w = W.scaled(base, M=64, N=1024, io_dtype=torch.float32)
+    inp = W.make_inputs(w)
+    out = run_recompute(nb, w, inp["x"], inp["dy"], inp["gamma"], True, eps=eps)
+    compare(w, inp["x"], inp["dy"], inp["gamma"], out, True, eps=eps)
+
+
+REC_EDGES = [(kind, dt, m, n)
+             for kind in ("layernorm", "rmsnorm")
+             for dt, ns in ((torch.float32, [1, 3, 65, 1000, 16384]),
+                            (torch.float16, [2, 63, 513, 4100, 32768]),
+                            (torch.bfloat16, [7, 64, 768, 6144, 20000]))
+             for m, n in zip([1, 3, 511, 2, 64], ns)]
+
+
+@pytest.mark.parametrize("kind,dt,M,N", REC_EDGES, ids=lambda v: str(v).replace("torch.", ""))
+def test_recompute_edge_shapes(nb, kind, dt, M, N):
+    base = W.LN_F32_128x512 if kind == "layernorm" else W.RMS_F32_128x512
+    w = W.scaled(base, M=M, N=N, io_dtype=dt, wgrad_dtype=torch.float32, seed=500 + M + N)
+    inp = W.make_inputs(w)
+    with_db = not (dt != torch.float32 and N > 16384)
+    out = run_recompute(nb, w, inp["x"], inp["dy"], inp["gamma"], with_db)
+    compare(w, inp["x"], inp["dy"], inp["gamma"], out, with_db)
+
+
+def test_recompute_constant_rows(nb):
+    """A constant LayerNorm row has var = 0: rstd = 1/sqrt(eps), xhat = 0, so
+    dx = rstd * (dyhat - mean(dyhat)) and its dgamma terms vanish."""
+    w = W.scaled(W.LN_F32_128x512, M=6, N=512)
+    inp = W.make_inputs(w)
+    x = inp["x"].clone()
+    x[1] = 2.5
+    x[4] = -0.75
+    out = run_recompute(nb, w, x, inp["dy"], inp["gamma"], True)
+    compare(w, x, inp["dy"], inp["gamma"], out, True)
+
+
+@pytest.mark.parametrize("w", [W.RMS_BF16_16384x4096, W.LN_BF16_65536x8192,
+                               W.RMS_BF16_262144x768], ids=lambda w: w.name)
+def test_recompute_full_size_sampled(nb, w):
+    print(f"[gen] {w.name}", flush=True)
+    inp = W.make_inputs(w)
+    with_db = w.kind == "layernorm"
+    print(f"[run] {w.name}", flush=True)
+    out = run_recompute(nb, w, inp["x"], inp["dy"], inp["gamma"], with_db)
+    rows = W.sample_rows(w.M, 48, seed=w.seed + 9)
+    cols = W.sample_rows(w.N, 32, seed=w.seed + 10)
+    if "outliers" in inp and inp["outliers"].dim() == 1:
+        cols = torch.unique(torch.cat([cols, inp["outliers"]]))
+    compare(w, inp["x"], inp["dy"], inp["gamma"], out, with_db, rows=rows, cols=cols)
+
+
+@pytest.mark.parametrize("w", [W.scaled(W.RMS_BF16_16384x4096, M=1024),
+                               W.scaled(W.LN_BF16_65536x8192, M=600),
+                               W.scaled(W.LN_F32_128x512, M=300, N=1000)],
+                         ids=lambda w: w.name)
+def test_recompute_matches_forward_statistics_bitwise(nb, w):
+    """Where the backward's lane layout equals the forward's, the recomputed
+    statistics are summed in the forward's order, so recompute mode equals
+    the saved-statistics path fed by the GPU forward bit for bit."""
+    with_db = w.kind == "layernorm"
+    p_bwd = nb.norm_bwd_make_plan(w.kind, w.M, w.N, w.io_dtype, with_db)
+    p_fwd = nb.norm_bwd_make_plan(w.kind, w.M, w.N, w.io_dtype, False)
+    assert (p_bwd.vec, p_bwd.chunks, p_bwd.waves_per_row) == \
+        (p_fwd.vec, p_fwd.chunks, p_fwd.waves_per_row)
+    inp = W.make_inputs(w)
+    x, dy, g = inp["x"].cuda(), inp["dy"].cuda(), inp["gamma"].cuda()
+    if w.kind == "layernorm":
+        _, mean, rstd = nb.norm_fwd_layernorm(x, g, None, w.eps)
+        a = nb.norm_bwd_layernorm(x, dy, g, mean, rstd, w.eps, wgrad_dtype=w.wgrad_dtype)
+        b = nb.norm_bwd_layernorm(x, dy, g, None, None, w.eps, wgrad_dtype=w.wgrad_dtype)
+    else:
+        _, rstd = nb.norm_fwd_rmsnorm(x, g, w.eps)
+        a = nb.norm_bwd_rmsnorm(x, dy, g, rstd, w.eps, wgrad_dtype=w.wgrad_dtype)
+        b = nb.norm_bwd_rmsnorm(x, dy, g, None, w.eps, wgrad_dtype=w.wgrad_dtype)
+    torch.cuda.synchronize()
+    for ta, tb in zip(a, b):
+        if ta is not None:
+            assert torch.equal(ta, tb)
+
+
+def test_recompute_is_deterministic(nb):
+    w = W.scaled(W.LN_BF16_65536x8192, M=1000, N=2048)
+    inp = W.make_inputs(w)
+    outs = [run_recompute(nb, w, inp["x"], inp["dy"], inp["gamma"], True) for _ in range(5)]
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert torch.equal(a, b)
+
+
+def test_recompute_argument_rules(nb):
+    w = W.scaled(W.LN_F32_128x512, M=8, N=64)
+    inp = W.make_inputs(w)
+    x, dy, g = inp["x"].cuda(), inp["dy"].cuda(), inp["gamma"].cuda()
+    rstd = torch.ones(8, device="cuda")
+    with pytest.raises(ValueError):
+        nb.norm_bwd_layernorm(x, dy, g, None, rstd)
+    plan = nb.norm_bwd_make_plan("layernorm", 8, 64, torch.float32, True)
+    with pytest.raises(ValueError):
+        nb.norm_bwd_execute(plan, x, dy, g, None, None)
+    # an empty problem in recompute mode still writes the empty sums
+    x0 = torch.empty(0, 64, device="cuda")
+    dg = torch.full((64,), float("nan"), device="cuda")
+    nb.norm_bwd_rmsnorm(x0, x0, g, None, dgamma=dg)
+    torch.cuda.synchronize()
+    assert torch.all(dg == 0)

@@ -193,8 +193,9 @@ def _ln(nb, **over):
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(x=None), 1), (dict(dy=None), 1), (dict(gamma=None), 1), (dict(rstd=None), 1),
+    (dict(x=None), 1), (dict(dy=None), 1), (dict(gamma=None), 1),
     (dict(dx=None), 1), (dict(dgamma=None), 1),
+    (dict(rstd=None, x=None), 1), (dict(rstd=None, eps=-1.0), 1),   # recompute mode checks too
     (dict(M=-1), 1), (dict(N=-3), 1), (dict(eps=-1.0), 1), (dict(eps=float("nan")), 1),
     (dict(eps=float("inf")), 1),
     (dict(io=5), 2), (dict(wg=1), 2), (dict(wg=7), 2), (dict(N=40000), 2),
@@ -212,7 +213,10 @@ def test_rmsnorm_rejects(nb, over, status):
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(mean=None), 1), (dict(wg=2), 2), (dict(dbeta=_addr(6)), 1),
+    (dict(mean=None), 1), (dict(rstd=None), 1),               # exactly one statistic NULL
+    (dict(mean=None, rstd=None, dx=_addr(0)), 1),             # recompute: dx aliases x
+    (dict(mean=None, rstd=None, wsb=100), 3),
+    (dict(wg=2), 2), (dict(dbeta=_addr(6)), 1),
     (dict(wsb=100), 3),
     (dict(mean=_addr(4)), 1),                                 # dx overlaps mean
 ])
@@ -250,6 +254,12 @@ def test_execute_rejects_edited_plans(nb):
     p.threads = 64
     p.lds_bytes = 0
     assert run(p) == 1
+    # the plan entry points have no eps, so they always need the statistics
+    p = base.copy()
+    assert lib.norm_bwd_execute(ctypes.byref(p), _addr(0), _addr(1), _addr(2), None, None, 0,
+                                _addr(4), _addr(5), None, _addr(6), p.workspace_bytes, None) == 1
+    assert lib.norm_bwd_execute_partials(ctypes.byref(p), _addr(0), _addr(1), _addr(2), None,
+                                         None, _addr(4), _addr(6), p.workspace_bytes, None) == 1
     # misaligned x for a vectorised plan
     p = base.copy()
     assert lib.norm_bwd_execute(ctypes.byref(p), ctypes.c_void_p(B + 2), _addr(1), _addr(2),
