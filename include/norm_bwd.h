@@ -138,6 +138,64 @@ size_t norm_bwd_workspace_bytes(int kind, int64_t M, int64_t N, int io_dtype,
                                 int with_dbeta);
 
 /*
+ * Extended backward: everything norm_bwd_layernorm / norm_bwd_rmsnorm do, plus
+ * row strides, an explicit group count and accumulation into existing weight
+ * gradients. Accumulating is what a training step needs when several
+ * micro-batches (or a parameter shared between layers) add into one gradient
+ * buffer ("Matmul backward in Triton", "Accumulate into the grad buffer, never
+ * overwrite"); the row stride follows the row-stride argument of the
+ * kernels in "Norm backward in Triton" (stride_row).
+ *
+ *   kind, io_dtype, wgrad_dtype, M, N, eps, gamma, mean, rstd, dgamma, dbeta,
+ *   workspace, workspace_bytes, stream: as for norm_bwd_layernorm (mean is
+ *   ignored for RMSNorm; mean = rstd = NULL selects recompute mode).
+ *   flags     NORM_BWD_ACCUMULATE: dgamma[j] (and dbeta[j]) become
+ *             old + (this call's sum), added in fp32 after the fixed-order
+ *             group sum and rounded once to wgrad_dtype; M = 0 leaves them
+ *             unchanged. Without it they are overwritten. Other bits:
+ *             NORM_BWD_ERR_INVALID_ARG.
+ *   groups    0 = automatic, else as norm_bwd_make_plan; the workspace must
+ *             hold norm_bwd_make_plan(kind, M, N, io_dtype, dbeta != NULL,
+ *             groups).workspace_bytes
+ *   ldx, lddy, lddx  row strides of x, dy and dx in elements (0 = N, else
+ *             >= N). Row r of x starts at x + r * ldx. Elements between rows
+ *             are neither read nor written. 16-byte vector access is used only
+ *             when every row start is 16-byte aligned; otherwise one element
+ *             per lane (same results up to summation order).
+ *   Outputs may not overlap any input's or output's span (first row start to
+ *   last row end). Returns a status code; checks as for the other entry
+ *   points.
+ */
+#define NORM_BWD_ACCUMULATE 1u
+
+typedef struct norm_bwd_args {
+    int32_t kind;
+    int32_t io_dtype;
+    int32_t wgrad_dtype;
+    uint32_t flags;
+    int64_t M, N;
+    int64_t groups;
+    const void *x;
+    int64_t ldx;
+    const void *dy;
+    int64_t lddy;
+    const void *gamma;
+    const float *mean;
+    const float *rstd;
+    void *dx;
+    int64_t lddx;
+    void *dgamma;
+    void *dbeta;
+    void *workspace;
+    size_t workspace_bytes;
+    void *stream;
+    float eps;
+    int32_t reserved;  /* must be 0 */
+} norm_bwd_args_t;
+
+int norm_bwd_ex(const norm_bwd_args_t *args);
+
+/*
  * An execution plan: the row grouping and the launch geometry of kernel A.
  * Produced by norm_bwd_make_plan; a caller may change `groups` (then call
  * norm_bwd_make_plan again with it) or the geometry fields for tuning, and

@@ -68,6 +68,25 @@ class NormBwdPlan(ctypes.Structure):
         return c
 
 
+ACCUMULATE = 1
+
+
+class NormBwdArgs(ctypes.Structure):
+    """Mirror of norm_bwd_args_t (the argument block of norm_bwd_ex)."""
+    _fields_ = [
+        ("kind", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+        ("wgrad_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+        ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("groups", ctypes.c_int64),
+        ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64),
+        ("dy", ctypes.c_void_p), ("lddy", ctypes.c_int64),
+        ("gamma", ctypes.c_void_p), ("mean", ctypes.c_void_p), ("rstd", ctypes.c_void_p),
+        ("dx", ctypes.c_void_p), ("lddx", ctypes.c_int64),
+        ("dgamma", ctypes.c_void_p), ("dbeta", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p), ("eps", ctypes.c_float), ("reserved", ctypes.c_int32),
+    ]
+
+
 _lock = threading.Lock()
 _lib = None
 
@@ -103,6 +122,7 @@ def load_library():
             "norm_bwd_probe_copy": [vp, vp, sz, vp],
             "norm_fwd_layernorm": [vp, vp, vp, i64, i64, i32, fp, vp, vp, vp, vp],
             "norm_fwd_rmsnorm": [vp, vp, i64, i64, i32, fp, vp, vp, vp],
+            "norm_bwd_ex": [ctypes.POINTER(NormBwdArgs)],
         }
         for name, args in sigs.items():
             f = getattr(lib, name)
@@ -138,13 +158,21 @@ def _stream(stream, device) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def _gpu(t: torch.Tensor, name: str):
+def _gpu_any(t: torch.Tensor, name: str):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on a GPU (got {t.device}); there is no CPU path")
+
+
+def _gpu(t: torch.Tensor, name: str):
+    _gpu_any(t, name)
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _addr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
 
 
 def _rows(x: torch.Tensor):
@@ -264,6 +292,82 @@ def norm_bwd_rmsnorm(x: torch.Tensor, dy: torch.Tensor, gamma: torch.Tensor,
                      with_dbeta or dbeta is not None, workspace, stream, None)
 
 
+def _rows2d(t: torch.Tensor, name: str):
+    """(rows, cols, row stride) of a 2-D view with unit column stride."""
+    _gpu_any(t, name)
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be a 2-D view with unit column stride")
+    return t.shape[0], t.shape[1], (t.stride(0) if t.shape[0] > 1 else t.shape[1])
+
+
+def norm_bwd_ex(kind: str, x: torch.Tensor, dy: torch.Tensor, gamma: torch.Tensor,
+                mean: Optional[torch.Tensor] = None, rstd: Optional[torch.Tensor] = None,
+                eps: float = 1e-5, *, wgrad_dtype: Optional[torch.dtype] = None, dx=None,
+                dgamma=None, dbeta=None, with_dbeta: Optional[bool] = None,
+                accumulate: bool = False, groups: int = 0, workspace=None, stream=None):
+    """Extended backward (norm_bwd_ex): x, dy (and dx) may be row-strided 2-D
+    views; accumulate=True adds into the given dgamma/dbeta. Returns
+    (dx, dgamma, dbeta)."""
+    lib = load_library()
+    code = kind = _KIND_CODE[kind]
+    M, N, ldx = _rows2d(x, "x")
+    M2, N2, lddy = _rows2d(dy, "dy")
+    _gpu(gamma, "gamma")
+    if (M2, N2) != (M, N) or gamma.numel() != N:
+        raise ValueError("dy must match x; gamma must have N elements")
+    if dy.dtype != x.dtype or gamma.dtype != x.dtype:
+        raise ValueError("x, dy and gamma must share one dtype")
+    if kind == RMSNORM:
+        mean = None
+    for t, n in ((mean, "mean"), (rstd, "rstd")):
+        if t is not None:
+            _gpu(t, n)
+            if t.dtype != torch.float32 or t.numel() != M:
+                raise ValueError("mean and rstd must be float32 [M]")
+    if with_dbeta is None:
+        with_dbeta = dbeta is not None or (kind == LAYERNORM and not accumulate)
+    dev = x.device
+    if accumulate and (dgamma is None or (with_dbeta and dbeta is None)):
+        raise ValueError("accumulate=True needs the dgamma (and dbeta) to add into")
+    wgrad_dtype = wgrad_dtype or (dgamma.dtype if dgamma is not None else torch.float32)
+    if dx is None:
+        dx = torch.empty((M, N), dtype=x.dtype, device=dev)
+    M3, N3, lddx = _rows2d(dx, "dx")
+    if (M3, N3) != (M, N) or dx.dtype != x.dtype:
+        raise ValueError("dx must be [M, N] in x's dtype")
+    if dgamma is None:
+        dgamma = torch.empty(N, dtype=wgrad_dtype, device=dev)
+    if with_dbeta and dbeta is None:
+        dbeta = torch.empty(N, dtype=wgrad_dtype, device=dev)
+    for t, n in ((dgamma, "dgamma"), (dbeta, "dbeta")):
+        if t is not None:
+            _gpu(t, n)
+            if t.dtype != wgrad_dtype or t.numel() != N:
+                raise ValueError(f"{n} must be [N] in wgrad_dtype")
+    io = _code(x.dtype, "x")
+    need = norm_bwd_make_plan(kind, M, N, io, dbeta is not None, groups).workspace_bytes
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _gpu(workspace, "workspace")
+    a = NormBwdArgs()
+    a.kind, a.io_dtype, a.wgrad_dtype = code, io, _code(wgrad_dtype, "wgrad")
+    a.flags = ACCUMULATE if accumulate else 0
+    a.M, a.N, a.groups = M, N, groups
+    a.x, a.ldx = _addr(x), ldx
+    a.dy, a.lddy = _addr(dy), lddy
+    a.gamma, a.mean, a.rstd = _addr(gamma), _addr(mean), _addr(rstd)
+    a.dx, a.lddx = _addr(dx), lddx
+    a.dgamma, a.dbeta = _addr(dgamma), _addr(dbeta)
+    a.workspace = _addr(workspace)
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a.stream = _stream(stream, dev).value
+    a.eps = float(eps)
+    with torch.cuda.device(dev):
+        st = lib.norm_bwd_ex(ctypes.byref(a))
+    _check(st)
+    return dx, dgamma, dbeta
+
+
 def norm_bwd_execute(plan: NormBwdPlan, x, dy, gamma, mean, rstd, *, wgrad_dtype=None,
                      dx=None, dgamma=None, dbeta=None, workspace=None, stream=None):
     """Run an explicit plan (kernel A then kernel B)."""
@@ -374,6 +478,6 @@ __all__ = [
     "norm_bwd_layernorm", "norm_bwd_rmsnorm", "norm_bwd_workspace_bytes", "norm_bwd_make_plan",
     "norm_bwd_execute", "norm_bwd_execute_partials", "norm_bwd_reduce_partials",
     "norm_bwd_probe_copy", "norm_bwd_status_string", "norm_bwd_last_error", "NormBwdPlan",
-    "norm_fwd_layernorm", "norm_fwd_rmsnorm",
+    "norm_fwd_layernorm", "norm_fwd_rmsnorm", "norm_bwd_ex", "NormBwdArgs", "ACCUMULATE",
     "NormBwdError", "load_library", "library_path",
 ]

@@ -38,7 +38,25 @@ struct Buffers {
   void* dbeta;
   void* ws;
   size_t ws_bytes;
+  int64_t ldx = 0, ldy = 0, ldo = 0;  // row strides in elements; 0 = N
 };
+
+// Bytes spanned by M rows of N elements with row stride ld (elements).
+size_t extent(int64_t M, int64_t N, int64_t ld, int eb) {
+  if (M <= 0 || N <= 0) return 0;
+  return (size_t)((M - 1) * ld + N) * (size_t)eb;
+}
+
+// Row strides valid for (M, N)? Fills in 0 -> N. Returns a status.
+int check_strides(int64_t M, int64_t N, Buffers& b) {
+  for (int64_t* ld : {&b.ldx, &b.ldy, &b.ldo}) {
+    if (*ld == 0) *ld = N;
+    if (*ld < N) return set_error(NORM_BWD_ERR_INVALID_ARG, "row stride smaller than N");
+    if (M > 1 && *ld > (int64_t)(((uint64_t)1 << 62) / (uint64_t)M / 4u))
+      return set_error(NORM_BWD_ERR_INVALID_ARG, "M * row stride too large");
+  }
+  return NORM_BWD_OK;
+}
 
 // Checks shared by every entry point that runs kernel A and/or kernel B.
 // `recompute`: kernel A computes the statistics from x (mean/rstd are NULL).
@@ -71,18 +89,21 @@ int check_buffers(int kind, int64_t M, int64_t N, int io_dtype, int wgrad_dtype,
     if (b.ws_bytes < ws_needed) return set_error(NORM_BWD_ERR_WORKSPACE, "workspace too small");
     if (!aligned16(b.ws)) return set_error(NORM_BWD_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   }
-  // No output may overlap an input, another output or the workspace.
-  const size_t mat = (size_t)M * (size_t)N * (size_t)eb;
+  // No output may overlap an input, another output or the workspace (for a
+  // strided matrix: anything within its first row's start and its last
+  // row's end).
+  const int64_t N_ = N;
+  auto mat = [&](int64_t ld) { return extent(M, N_, ld ? ld : N_, eb); };
   const size_t vec_in = (size_t)N * (size_t)eb;
   const size_t vec_out = (size_t)N * (size_t)(wb ? wb : 4);
   const size_t stat = (size_t)M * 4u;
   struct R { const void* p; size_t n; };
-  const R inputs[] = {{rows ? b.x : nullptr, mat},
-                      {rows ? b.dy : nullptr, mat},
+  const R inputs[] = {{rows ? b.x : nullptr, mat(b.ldx)},
+                      {rows ? b.dy : nullptr, mat(b.ldy)},
                       {rows ? b.gamma : nullptr, vec_in},
                       {rows && !recompute && kind == NORM_BWD_LAYERNORM ? b.mean : nullptr, stat},
                       {rows && !recompute ? b.rstd : nullptr, stat}};
-  const R outputs[] = {{rows ? b.dx : nullptr, mat},
+  const R outputs[] = {{rows ? b.dx : nullptr, mat(b.ldo)},
                        {run_b ? b.dgamma : nullptr, vec_out},
                        {run_b ? b.dbeta : nullptr, vec_out},
                        {b.ws, ws_needed}};
@@ -115,6 +136,9 @@ int launch_partials(const norm_bwd_plan_t& p, const Buffers& b, hipStream_t stre
   a.ws = static_cast<float*>(b.ws);
   a.M = p.M;
   a.N = (int)p.N;
+  a.ldx = b.ldx ? b.ldx : p.N;
+  a.ldy = b.ldy ? b.ldy : p.N;
+  a.ldo = b.ldo ? b.ldo : p.N;
   a.G = p.groups;
   a.R = p.rows_per_group;
   a.S = p.waves_per_row;
@@ -137,11 +161,12 @@ int launch_partials(const norm_bwd_plan_t& p, const Buffers& b, hipStream_t stre
 }
 
 int launch_reduce(int64_t groups, int64_t N, int wgrad_dtype, const void* ws, void* dgamma,
-                  void* dbeta, hipStream_t stream) {
+                  void* dbeta, hipStream_t stream, bool accumulate = false) {
   if (N == 0) return NORM_BWD_OK;
+  if (accumulate && groups == 0) return NORM_BWD_OK;  // adds the empty sum: nothing
   (void)hipGetLastError();
   hipError_t e = nb::launch_reduce(wgrad_dtype, static_cast<const float*>(ws), groups, (int)N,
-                                   dgamma, dbeta, stream);
+                                   dgamma, dbeta, accumulate ? 1 : 0, stream);
   if (e != hipSuccess) return hip_error(e, "kernel B launch");
   return NORM_BWD_OK;
 }
@@ -156,30 +181,43 @@ int check_vec_alignment(const norm_bwd_plan_t& p, const Buffers& b) {
   return NORM_BWD_OK;
 }
 
-int run_auto(int kind, const void* x, const void* dy, const void* gamma, const float* mean,
-             const float* rstd, int64_t M, int64_t N, int io_dtype, int wgrad_dtype, float eps,
-             void* dx, void* dgamma, void* dbeta, void* workspace, size_t workspace_bytes,
-             void* stream) {
+// The whole backward with an automatic or explicit group count: the named
+// entry points and norm_bwd_ex. Row strides of b must be filled in (>= N).
+int run_backward(int kind, Buffers b, int64_t M, int64_t N, int io_dtype, int wgrad_dtype,
+                 float eps, int64_t groups, bool accumulate, void* stream) {
   if (!(eps >= 0.0f) || isinf(eps))
     return set_error(NORM_BWD_ERR_INVALID_ARG, "eps must be finite and >= 0");
   // NULL statistics (LayerNorm: both) select the recompute mode
-  if (kind == NORM_BWD_LAYERNORM && (mean == nullptr) != (rstd == nullptr))
+  if (kind == NORM_BWD_LAYERNORM && (b.mean == nullptr) != (b.rstd == nullptr))
     return set_error(NORM_BWD_ERR_INVALID_ARG,
                      "LayerNorm takes both mean and rstd, or neither (recompute)");
-  const bool recompute = rstd == nullptr;
-  const bool vec_ok = aligned16(x) && aligned16(dy) && aligned16(gamma) && aligned16(dx);
+  const bool recompute = b.rstd == nullptr;
+  const int eb = nb::dtype_bytes(io_dtype);
+  // 16-byte vectors need every row of x, dy and dx to start 16-byte aligned
+  const bool rows16 = eb > 0 && (b.ldx * eb) % 16 == 0 && (b.ldy * eb) % 16 == 0 &&
+                      (b.ldo * eb) % 16 == 0;
+  const bool vec_ok = rows16 && aligned16(b.x) && aligned16(b.dy) && aligned16(b.gamma) &&
+                      aligned16(b.dx);
   norm_bwd_plan_t p;
   const char* why = nullptr;
-  int st = nb::make_plan(kind, M, N, io_dtype, dbeta ? 1 : 0, 0, vec_ok, &p, &why);
+  int st = nb::make_plan(kind, M, N, io_dtype, b.dbeta ? 1 : 0, groups, vec_ok, &p, &why);
   if (st != NORM_BWD_OK) return set_error(st, why);
-  Buffers b{x, dy, gamma, mean, rstd, dx, dgamma, dbeta, workspace, workspace_bytes};
   st = check_buffers(kind, M, N, io_dtype, wgrad_dtype, true, true, p.workspace_bytes, b,
                      recompute);
   if (st != NORM_BWD_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = launch_partials(p, b, s, recompute, eps);
   if (st != NORM_BWD_OK) return st;
-  return launch_reduce(p.groups, N, wgrad_dtype, workspace, dgamma, dbeta, s);
+  return launch_reduce(p.groups, N, wgrad_dtype, b.ws, b.dgamma, b.dbeta, s, accumulate);
+}
+
+int run_auto(int kind, const void* x, const void* dy, const void* gamma, const float* mean,
+             const float* rstd, int64_t M, int64_t N, int io_dtype, int wgrad_dtype, float eps,
+             void* dx, void* dgamma, void* dbeta, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  Buffers b{x, dy, gamma, mean, rstd, dx, dgamma, dbeta, workspace, workspace_bytes};
+  b.ldx = b.ldy = b.ldo = N > 0 ? N : 0;
+  return run_backward(kind, b, M, N, io_dtype, wgrad_dtype, eps, 0, false, stream);
 }
 
 int run_forward(int kind, const void* x, const void* gamma, const void* beta, int64_t M,
@@ -289,6 +327,28 @@ int norm_bwd_make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_db
   int st = nb::make_plan(kind, M, N, io_dtype, with_dbeta, groups, true, plan, &why);
   if (st != NORM_BWD_OK) return set_error(st, why);
   return NORM_BWD_OK;
+}
+
+int norm_bwd_ex(const norm_bwd_args_t* a) {
+  if (!a) return set_error(NORM_BWD_ERR_INVALID_ARG, "args is NULL");
+  if (a->kind != NORM_BWD_LAYERNORM && a->kind != NORM_BWD_RMSNORM)
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "kind invalid");
+  if (a->flags & ~(uint32_t)NORM_BWD_ACCUMULATE)
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "unknown flag bits");
+  if (a->M < 0 || a->N < 0) return set_error(NORM_BWD_ERR_INVALID_ARG, "M and N must be >= 0");
+  if (a->groups < 0) return set_error(NORM_BWD_ERR_INVALID_ARG, "groups must be >= 0");
+  if (a->reserved != 0) return set_error(NORM_BWD_ERR_INVALID_ARG, "reserved must be 0");
+  Buffers b{a->x, a->dy, a->gamma, a->mean, a->rstd, a->dx, a->dgamma, a->dbeta,
+            a->workspace, a->workspace_bytes};
+  b.ldx = a->ldx;
+  b.ldy = a->lddy;
+  b.ldo = a->lddx;
+  if (a->ldx < 0 || a->lddy < 0 || a->lddx < 0)
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "row strides must be >= 0");
+  int st = check_strides(a->M, a->N, b);
+  if (st != NORM_BWD_OK) return st;
+  return run_backward(a->kind, b, a->M, a->N, a->io_dtype, a->wgrad_dtype, a->eps, a->groups,
+                      (a->flags & NORM_BWD_ACCUMULATE) != 0, a->stream);
 }
 
 int norm_bwd_execute(const norm_bwd_plan_t* plan, const void* x, const void* dy,

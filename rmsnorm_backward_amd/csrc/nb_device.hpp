@@ -284,7 +284,8 @@ __device__ __forceinline__ void fetch_row(RowBuf<Tg, VEC, C>& b, const char* __r
                                           const char* __restrict__ dy,
                                           const float* __restrict__ mean,
                                           const float* __restrict__ rstd, int64_t r, bool active,
-                                          int N, int col0, int cstride) {
+                                          int N, int64_t ldx, int64_t ldy, int col0,
+                                          int cstride) {
   constexpr int EB = Tg::kBytes;
   if (active) {
     if constexpr (!RECOMP) {
@@ -292,13 +293,13 @@ __device__ __forceinline__ void fetch_row(RowBuf<Tg, VEC, C>& b, const char* __r
       b.rs = rstd[rz];
       b.mu = (KIND == kLayerNorm) ? mean[rz] : 0.0f;
     }
-    const int64_t rb = r * (int64_t)N;
+    const int64_t xb = r * ldx, yb = r * ldy;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int col = col0 + c * cstride;
       if (col < N) {
-        b.x[c].load_stream(x + (rb + col) * EB);
-        b.dy[c].load_stream(dy + (rb + col) * EB);
+        b.x[c].load_stream(x + (xb + col) * EB);
+        b.dy[c].load_stream(dy + (yb + col) * EB);
       }
     }
   }
@@ -320,14 +321,14 @@ __device__ __forceinline__ void fetch_row(RowBuf<Tg, VEC, C>& b, const char* __r
 // the forward computes them: LayerNorm first sums x (with s1 = sum dyhat in
 // the same exchange), then with mean = sum(x)/N sums xc^2 and dyhat * xc;
 // RMSNorm sums x^2 and dyhat * x in one exchange. rstd = 1/sqrt(sum(xc^2)/N
-// + eps). The dgamma terms, which need rstd, are then accumulated before
-// pass 2.
+// + eps). The dgamma terms, which need rstd, are accumulated in pass 2.
 template <int KIND, bool RECOMP, class Tg, int VEC, int C, int NACC>
 __device__ __forceinline__ void process_row(RowBuf<Tg, VEC, C>& b, const float (&gam)[C][VEC],
                                             float (&acc)[NACC][C][VEC], char* __restrict__ dx,
                                             float (*red)[kMaxWaves][2], int& phase, int64_t r,
-                                            bool active, int N, float inv_n, float eps, int col0,
-                                            int cstride, int lane, int wave, int S, int p) {
+                                            bool active, int N, int64_t ldo, float inv_n, float eps,
+                                            int col0, int cstride, int lane, int wave, int S,
+                                            int p) {
   constexpr int EB = Tg::kBytes;
   float s1 = 0.0f, s2 = 0.0f;
   float mu, rs;
@@ -398,24 +399,12 @@ __device__ __forceinline__ void process_row(RowBuf<Tg, VEC, C>& b, const float (
     keep_packed(b.dy);
     row_sum2<true>(sxx, s2, red, phase, lane, wave, S, p);
     rs = 1.0f / __builtin_sqrtf(__builtin_fmaf(sxx, inv_n, eps));
-    if (active) {
-#pragma unroll
-      for (int c = 0; c < C; ++c) {
-        if (col0 + c * cstride < N) {
-#pragma unroll
-          for (int v = 0; v < VEC; ++v)
-            acc[0][c][v] = __builtin_fmaf(b.dy[c].get(v) * (b.x[c].get(v) - mu), rs,
-                                          acc[0][c][v]);
-        }
-      }
-    }
-    pin(acc);
   }
   if (active) {
     const float m2 = s2 * inv_n * rs;  // mean_j(dyhat * xhat)
     const float c2 = -(rs * rs) * m2;
     const float c1 = (KIND == kLayerNorm) ? -rs * (s1 * inv_n) : 0.0f;
-    const int64_t rb = r * (int64_t)N;
+    const int64_t rb = r * ldo;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int col = col0 + c * cstride;
@@ -426,6 +415,9 @@ __device__ __forceinline__ void process_row(RowBuf<Tg, VEC, C>& b, const float (
           const float xc = b.x[c].get(v) - mu;
           const float dyh = b.dy[c].get(v) * gam[c][v];
           o[v] = __builtin_fmaf(dyh, rs, __builtin_fmaf(xc, c2, c1));
+          // recompute mode: the dgamma term, now that rstd is known
+          if constexpr (RECOMP)
+            acc[0][c][v] = __builtin_fmaf(b.dy[c].get(v) * xc, rs, acc[0][c][v]);
         }
         Pack<Tg, VEC> out;
         out.set(o);
@@ -440,8 +432,8 @@ __global__ __launch_bounds__((max_threads_for<VEC, C>()))
 void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dyv,
                         const void* __restrict__ gv, const float* __restrict__ mean,
                         const float* __restrict__ rstd, void* __restrict__ dxv,
-                        float* __restrict__ ws, int64_t M, int N, int64_t G, int64_t R,
-                        int S, int P, float eps) {
+                        float* __restrict__ ws, int64_t M, int N, int64_t ldx, int64_t ldy,
+                        int64_t ldo, int64_t G, int64_t R, int S, int P, float eps) {
   using PK = Pack<Tg, VEC>;
   using RB = RowBuf<Tg, VEC, C>;
   constexpr int EB = Tg::kBytes;
@@ -499,7 +491,8 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
     for (int k = 0; k < D - 1; ++k) {
       if (k < iters) {
         const int64_t rk = row_of(k);
-        fetch_row<KIND, RECOMP>(buf[k], x, dy, mean, rstd, rk, rk < M, N, col0, cstride);
+        fetch_row<KIND, RECOMP>(buf[k], x, dy, mean, rstd, rk, rk < M, N, ldx, ldy, col0,
+                                cstride);
       }
     }
     for (int it = 0; it < iters; it += D) {
@@ -508,13 +501,13 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
         const int k = it + d;
         if (k + D - 1 < iters) {
           const int64_t rf = row_of(k + D - 1);
-          fetch_row<KIND, RECOMP>(buf[(d + D - 1) % D], x, dy, mean, rstd, rf, rf < M, N,
-                                  col0, cstride);
+          fetch_row<KIND, RECOMP>(buf[(d + D - 1) % D], x, dy, mean, rstd, rf, rf < M, N, ldx,
+                                  ldy, col0, cstride);
         }
         if (k < iters) {
           const int64_t rk = row_of(k);
-          process_row<KIND, RECOMP>(buf[d], gam, acc, dx, red, phase, rk, rk < M, N, inv_n,
-                                    eps, col0, cstride, lane, wave, S, p);
+          process_row<KIND, RECOMP>(buf[d], gam, acc, dx, red, phase, rk, rk < M, N, ldo,
+                                    inv_n, eps, col0, cstride, lane, wave, S, p);
         }
       }
     }
@@ -583,15 +576,26 @@ template <> __device__ __forceinline__ void store_out<TF16>(void* p, int j, floa
 template <> __device__ __forceinline__ void store_out<TBF16>(void* p, int j, float v) {
   static_cast<uint16_t*>(p)[j] = pack1<TBF16>(v);
 }
+template <class OutT> __device__ __forceinline__ float load_out(const void* p, int j) {
+  if constexpr (OutT::kBytes == 4) {
+    return static_cast<const float*>(p)[j];
+  } else {
+    Pack<OutT, 1> t;
+    t.load(static_cast<const char*>(p) + (int64_t)j * 2);
+    return t.get(0);
+  }
+}
 
 // Lane = feature (each wave load reads 256 contiguous bytes of one partial
 // row); wave q sums groups [q*G/16, (q+1)*G/16) in ascending order, issuing
 // kReduceUnroll loads before adding them in order; wave 0 then adds the 16
-// slice sums in slice order.
+// slice sums in slice order. With `accumulate` the output's previous value is
+// added to that sum (old + sum, one rounding to the output type).
 template <class OutT>
 __global__ __launch_bounds__(kReduceWaves * 64)
 void reduce_partials_kernel(const float* __restrict__ ws, int64_t G, int N,
-                            void* __restrict__ dgamma, void* __restrict__ dbeta) {
+                            void* __restrict__ dgamma, void* __restrict__ dbeta,
+                            int accumulate) {
   __shared__ float part[kReduceWaves][kReduceCols];
   const int lane = threadIdx.x & 63;
   const int q = threadIdx.x >> 6;
@@ -618,7 +622,9 @@ void reduce_partials_kernel(const float* __restrict__ ws, int64_t G, int N,
     float t = part[0][lane];
 #pragma unroll
     for (int k = 1; k < kReduceWaves; ++k) t += part[k][lane];
-    store_out<OutT>(plane == 0 ? dgamma : dbeta, col, t);
+    void* out = plane == 0 ? dgamma : dbeta;
+    if (accumulate) t = load_out<OutT>(out, col) + t;
+    store_out<OutT>(out, col, t);
   }
 }
 

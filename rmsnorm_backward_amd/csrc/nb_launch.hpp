@@ -21,6 +21,7 @@ struct LaunchA {
   float* ws;
   int64_t M;
   int N;
+  int64_t ldx, ldy, ldo;  // row strides (elements) of x, dy, dx
   int64_t G, R;
   int S, P, threads, grid, lds;
   int recompute;  // 1: mean/rstd are NULL and recomputed from x with eps
@@ -55,7 +56,7 @@ hipError_t launch_f_f32(const LaunchF& f);
 hipError_t launch_f_f16(const LaunchF& f);
 hipError_t launch_f_bf16(const LaunchF& f);
 hipError_t launch_reduce(int wgrad_dtype, const float* ws, int64_t G, int N, void* dgamma,
-                         void* dbeta, hipStream_t stream);
+                         void* dbeta, int accumulate, hipStream_t stream);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
 }  // namespace nb

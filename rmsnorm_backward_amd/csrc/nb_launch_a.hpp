@@ -17,7 +17,7 @@ template <class Tg, int KIND, bool RECOMP, int NACC, int VEC, int C>
 hipError_t launch_one(const LaunchA& a) {
   hipLaunchKernelGGL((dx_partials_kernel<KIND, RECOMP, Tg, VEC, C, NACC>), dim3(a.grid),
                      dim3(a.threads), a.lds, a.stream, a.x, a.dy, a.gamma, a.mean, a.rstd, a.dx,
-                     a.ws, a.M, a.N, a.G, a.R, a.S, a.P, a.eps);
+                     a.ws, a.M, a.N, a.ldx, a.ldy, a.ldo, a.G, a.R, a.S, a.P, a.eps);
   return hipGetLastError();
 }
 

@@ -1,0 +1,175 @@
+"""norm_bwd_ex on the GPU: row strides, accumulation into existing weight
+gradients, explicit groups and the recompute mode through one entry point.
+
+Accumulating follows "Matmul backward in Triton", "Accumulate into the grad
+buffer, never overwrite"; the row stride follows the stride_row argument of
+the kernels in "Norm backward in Triton". Values are checked against the fp64
+oracle on contiguous copies of the same inputs; the accumulated result is
+also checked bit for bit against old + (the plain call's fp32 result).
+"""
+
+from __future__ import annotations
+
+import pytest
+import torch
+
+import oracle
+import parity
+from inputs import backward_inputs
+from rmsnorm_backward_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+CANARY = -1536.0
+
+
+@pytest.fixture(scope="module")
+def nb():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import rmsnorm_backward_amd as nbmod
+    nbmod.load_library()
+    return nbmod
+
+
+def strided(t: torch.Tensor, ld: int, fill=CANARY) -> torch.Tensor:
+    """A [M, N] view with row stride ld of a canary-filled GPU buffer, holding t."""
+    M, N = t.shape
+    buf = torch.full((M * ld + 8,), fill, dtype=t.dtype, device="cuda")
+    v = buf[:M * ld].view(M, ld)[:, :N]
+    v.copy_(t.cuda())
+    return v
+
+
+def reference(w, inp, with_db):
+    rdx, rdg, rdb = oracle.bwd(w.kind, inp["x"], inp["dy"], inp["gamma"], inp.get("mean"),
+                               inp["rstd"], want_dbeta=True)
+    scale = parity.dx_term_scale(w.kind, inp["x"], inp["dy"], inp["gamma"], inp.get("mean"),
+                                 inp["rstd"])
+    return rdx, rdg, (rdb if with_db else None), scale
+
+
+@pytest.mark.parametrize("dt,pad", [(torch.bfloat16, 8), (torch.bfloat16, 3), (torch.float32, 4),
+                                    (torch.float16, 64), (torch.float32, 1)],
+                         ids=lambda v: str(v).replace("torch.", ""))
+@pytest.mark.parametrize("kind", ["layernorm", "rmsnorm"])
+def test_row_strides(nb, kind, dt, pad):
+    """x, dy and dx as row-strided views (padding 16-byte aligned or not);
+    the gaps between rows of dx keep their canary."""
+    base = W.LN_F32_128x512 if kind == "layernorm" else W.RMS_F32_128x512
+    w = W.scaled(base, M=333, N=1024, io_dtype=dt, seed=800 + pad)
+    inp = backward_inputs(w)
+    with_db = kind == "layernorm"
+    N = w.N
+    x = strided(inp["x"], N + pad)
+    dy = strided(inp["dy"], N + 2 * pad)
+    dxv = strided(torch.zeros(w.M, N, dtype=dt), N + 3 * pad)
+    g = inp["gamma"].cuda()
+    mean = inp["mean"].cuda() if kind == "layernorm" else None
+    dx, dg, db = nb.norm_bwd_ex(kind, x, dy, g, mean, inp["rstd"].cuda(), w.eps, dx=dxv,
+                                with_dbeta=with_db)
+    torch.cuda.synchronize()
+    assert dx.data_ptr() == dxv.data_ptr()
+    rdx, rdg, rdb, scale = reference(w, inp, with_db)
+    parity.check_dx(dt, dx.cpu(), rdx, scale=scale)
+    parity.check_wgrad(dt, dg.cpu(), rdg)
+    if with_db:
+        parity.check_wgrad(dt, db.cpu(), rdb, "dbeta")
+    # the padding between dx's rows is untouched
+    full = dxv.as_strided((w.M, N + 3 * pad), (N + 3 * pad, 1))
+    assert torch.all(full[:, N:].float().cpu() == CANARY)
+    # the same call on contiguous tensors gives the same bits when both use
+    # the same lane layout (aligned padding), else agrees within tolerance
+    dx2, dg2, db2 = nb.norm_bwd_ex(kind, inp["x"].cuda(), inp["dy"].cuda(), g, mean,
+                                   inp["rstd"].cuda(), w.eps, with_dbeta=with_db)
+    torch.cuda.synchronize()
+    if (pad * dt.itemsize) % 16 == 0:
+        assert torch.equal(dx2.cpu(), dx.cpu()) and torch.equal(dg2.cpu(), dg.cpu())
+
+
+@pytest.mark.parametrize("w", [W.scaled(W.RMS_BF16_16384x4096, M=700),
+                               W.scaled(W.LN_BF16_65536x8192, M=500, N=2048),
+                               W.LN_F32_128x512], ids=lambda w: w.name)
+def test_accumulate_is_old_plus_sum(nb, w):
+    """With fp32 weight gradients, accumulate gives exactly fl(old + s) where s
+    is the plain call's (fp32) result."""
+    inp = backward_inputs(w)
+    with_db = w.kind == "layernorm"
+    g = {k: v.cuda() for k, v in inp.items() if k != "outliers"}
+    _, s_g, s_b = nb.norm_bwd_ex(w.kind, g["x"], g["dy"], g["gamma"], g.get("mean"), g["rstd"],
+                                 w.eps, with_dbeta=with_db)
+    gen = torch.Generator().manual_seed(5)
+    old_g = torch.randn(w.N, generator=gen).cuda()
+    old_b = torch.randn(w.N, generator=gen).cuda() if with_db else None
+    acc_g, acc_b = old_g.clone(), (old_b.clone() if with_db else None)
+    nb.norm_bwd_ex(w.kind, g["x"], g["dy"], g["gamma"], g.get("mean"), g["rstd"], w.eps,
+                   dgamma=acc_g, dbeta=acc_b, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(acc_g, old_g + s_g)
+    if with_db:
+        assert torch.equal(acc_b, old_b + s_b)
+
+
+@pytest.mark.parametrize("wdt", [torch.float32, torch.bfloat16])
+def test_accumulate_two_micro_batches(nb, wdt):
+    """Two micro-batches accumulated into one buffer match the oracle's
+    gradient of the concatenated batch."""
+    w = W.scaled(W.LN_BF16_65536x8192, M=600, N=1536, wgrad_dtype=wdt)
+    inp = backward_inputs(w)
+    g = {k: v.cuda() for k, v in inp.items() if k != "outliers"}
+    dg = torch.zeros(w.N, dtype=wdt, device="cuda")
+    db = torch.zeros(w.N, dtype=wdt, device="cuda")
+    for lo, hi in ((0, 250), (250, 600)):
+        nb.norm_bwd_ex(w.kind, g["x"][lo:hi], g["dy"][lo:hi], g["gamma"], g["mean"][lo:hi],
+                       g["rstd"][lo:hi], w.eps, wgrad_dtype=wdt, dgamma=dg, dbeta=db,
+                       accumulate=True)
+    torch.cuda.synchronize()
+    _, rdg, rdb, _ = reference(w, inp, True)
+    extra = extra_b = None
+    if wdt != torch.float32:
+        # the bf16 buffer is also rounded after the first micro-batch: up to
+        # 2^-8 of that partial sum (taken twice over for the partial's own error)
+        p_g, p_b = oracle.bwd_wgrad(w.kind, inp["x"][:250], inp["dy"][:250], inp["mean"][:250],
+                                    inp["rstd"][:250], want_dbeta=True)
+        extra, extra_b = 2.0 ** -7 * abs(p_g), 2.0 ** -7 * abs(p_b)
+    parity.check_wgrad(w.io_dtype, dg.cpu(), rdg, extra=extra)
+    parity.check_wgrad(w.io_dtype, db.cpu(), rdb, "dbeta", extra=extra_b)
+
+
+def test_accumulate_empty_batch_leaves_gradients(nb):
+    g = torch.ones(64, dtype=torch.bfloat16, device="cuda")
+    x0 = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    st = torch.empty(0, device="cuda")
+    old = torch.tensor([-0.0, 1.5, -2.25] + [3.0] * 61, device="cuda")
+    dg = old.clone()
+    nb.norm_bwd_ex("rmsnorm", x0, x0, g, None, st, dgamma=dg, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dg.view(torch.int32), old.view(torch.int32))
+
+
+@pytest.mark.parametrize("groups", [1, 5, 64, 333])
+def test_explicit_groups_match_the_plan_path(nb, groups):
+    w = W.scaled(W.LN_BF16_65536x8192, M=333, N=768)
+    inp = backward_inputs(w)
+    g = {k: v.cuda() for k, v in inp.items() if k != "outliers"}
+    a = nb.norm_bwd_ex(w.kind, g["x"], g["dy"], g["gamma"], g["mean"], g["rstd"], w.eps,
+                       groups=groups)
+    plan = nb.norm_bwd_make_plan(w.kind, w.M, w.N, w.io_dtype, True, groups)
+    b = nb.norm_bwd_execute(plan, g["x"], g["dy"], g["gamma"], g["mean"], g["rstd"])
+    torch.cuda.synchronize()
+    for ta, tb in zip(a, b):
+        assert torch.equal(ta, tb)
+
+
+def test_recompute_with_strides(nb):
+    w = W.scaled(W.RMS_BF16_16384x4096, M=257, N=4096)
+    inp = W.make_inputs(w)
+    x = strided(inp["x"], w.N + 64)
+    dy = strided(inp["dy"], w.N + 128)
+    dx, dg, _ = nb.norm_bwd_ex("rmsnorm", x, dy, inp["gamma"].cuda(), None, None, w.eps)
+    ref = nb.norm_bwd_ex("rmsnorm", inp["x"].cuda(), inp["dy"].cuda(), inp["gamma"].cuda(),
+                         None, None, w.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(dx.cpu(), ref[0].cpu()) and torch.equal(dg.cpu(), ref[1].cpu())
+    mean, rstd = oracle.fwd_stats("rmsnorm", inp["x"], w.eps)
+    rdx = oracle.bwd_dx("rmsnorm", inp["x"], inp["dy"], inp["gamma"], None, rstd)
+    t_dx, _ = parity.recompute_terms("rmsnorm", inp["x"], inp["dy"], inp["gamma"], None, rstd)
+    parity.check_dx(w.io_dtype, dx.cpu(), rdx, scale=t_dx)

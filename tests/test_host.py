@@ -55,6 +55,32 @@ def test_plan_struct_layout_matches_header(nb):
     assert nb.NormBwdPlan.chunks.offset == 48
 
 
+def _c_layout(struct, fields, tmp_path):
+    """sizeof and field offsets of `struct` as the C compiler lays it out."""
+    import subprocess
+    src = tmp_path / "layout.c"
+    body = "".join(f'  printf("{f} %zu\\n", offsetof({struct}, {f}));\n' for f in fields)
+    src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"norm_bwd.h\"\n"
+                   "int main(void) {\n"
+                   f'  printf("sizeof %zu\\n", sizeof({struct}));\n{body}  return 0;\n}}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                    str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    return {k: int(v) for k, v in (line.split() for line in out.splitlines())}
+
+
+@pytest.mark.parametrize("struct,pyname", [("norm_bwd_plan_t", "NormBwdPlan"),
+                                           ("norm_bwd_args_t", "NormBwdArgs")])
+def test_struct_layouts_match_the_c_compiler(nb, struct, pyname, tmp_path):
+    cls = getattr(nb, pyname)
+    names = [f for f, _ in cls._fields_]
+    c = _c_layout(struct, names, tmp_path)
+    assert c["sizeof"] == ctypes.sizeof(cls)
+    for f in names:
+        assert c[f] == getattr(cls, f).offset, f
+
+
 def test_status_strings(nb):
     assert nb.norm_bwd_status_string(0) == "NORM_BWD_OK"
     assert nb.norm_bwd_status_string(1) == "NORM_BWD_ERR_INVALID_ARG"
@@ -315,7 +341,50 @@ def test_forward_layernorm_rejects_overlapping_statistics(nb):
     assert _fwd(nb, "rmsnorm", N=0, x=None, y=None) == 0
 
 
+def _ex(nb, **over):
+    a = nb.NormBwdArgs()
+    vals = dict(kind=1, io_dtype=2, wgrad_dtype=0, flags=0, M=M_, N=N_, groups=0,
+                x=B, ldx=0, dy=B + (1 << 30), lddy=0, gamma=B + 2 * (1 << 30), mean=None,
+                rstd=B + 3 * (1 << 30), dx=B + 4 * (1 << 30), lddx=0,
+                dgamma=B + 5 * (1 << 30), dbeta=None, workspace=B + 6 * (1 << 30),
+                workspace_bytes=1 << 20, stream=None, eps=1e-6, reserved=0)
+    vals.update(over)
+    for k, v in vals.items():
+        setattr(a, k, v)
+    return nb.load_library().norm_bwd_ex(ctypes.byref(a))
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(flags=2), 1), (dict(reserved=1), 1), (dict(kind=4), 1), (dict(groups=-1), 1),
+    (dict(ldx=N_ - 1), 1), (dict(lddy=-8), 1), (dict(lddx=1), 1),
+    (dict(M=-1), 1), (dict(eps=-1.0), 1), (dict(io_dtype=7), 2),
+    (dict(kind=0, mean=B + 7 * (1 << 30), rstd=None), 1),          # exactly one statistic
+    (dict(ldx=1 << 60), 1),                                          # M * stride overflows
+    (dict(lddx=2 * N_, dx=B + 1024), 1),                             # dx's span overlaps x
+    (dict(workspace_bytes=64), 3), (dict(groups=M_, workspace_bytes=4 * N_ * 8), 3),
+])
+@no_gpu
+def test_ex_rejects(nb, over, status):
+    assert _ex(nb, **over) == status
+    assert nb.norm_bwd_last_error().startswith(nb.norm_bwd_status_string(status))
+
+
+@no_gpu
+def test_ex_empty_accumulate_is_a_no_op(nb):
+    # M = 0 with NORM_BWD_ACCUMULATE adds nothing: no launch, status OK
+    assert _ex(nb, M=0, flags=1) == 0
+    assert _ex(nb, N=0) == 0
+
+
 def test_binding_refuses_cpu_tensors(nb):
     x = torch.zeros(4, 8, dtype=torch.bfloat16)
+    g = torch.zeros(8, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
-        nb.norm_bwd_rmsnorm(x, x, torch.zeros(8, dtype=torch.bfloat16), torch.ones(4))
+        nb.norm_bwd_rmsnorm(x, x, g, torch.ones(4))
+    for kind in ("layernorm", "rmsnorm", 0, 1):
+        with pytest.raises(ValueError, match="GPU"):
+            nb.norm_bwd_ex(kind, x, x, g, None, None)
+    with pytest.raises(ValueError, match="GPU"):
+        nb.norm_fwd_layernorm(x, g, None)
+    with pytest.raises(ValueError, match="GPU"):
+        nb.norm_fwd_rmsnorm(x, g)
