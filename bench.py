@@ -287,6 +287,46 @@ def main(argv=None) -> int:
     ms_rc = time_loop(torch, step_rc, args.steps, stream)
     rc_bytes = w.algorithmic_bytes() - w.M * (8 if w.kind == "layernorm" else 4)
 
+    # norm_bwd_ex: x, dy, dx as row-strided views (row stride N + 64 elements)
+    # and the weight gradients accumulated into (read, added, written)
+    ld = w.N + 64
+    ex_args, ex_keep = [], []
+    for s in sets:
+        views = {}
+        for k in ("x", "dy", "dx"):
+            buf = torch.empty(w.M * ld, dtype=w.io_dtype, device=dev)
+            v = buf.view(w.M, ld)[:, :w.N]
+            v.copy_(s[k])
+            views[k] = v
+        ex_keep.append(views)
+        a = nb.NormBwdArgs()
+        a.kind, a.io_dtype, a.wgrad_dtype = (0 if w.kind == "layernorm" else 1), io, wg
+        a.flags, a.M, a.N, a.groups = nb.ACCUMULATE, w.M, w.N, 0
+        a.x, a.ldx, a.dy, a.lddy = views["x"].data_ptr(), ld, views["dy"].data_ptr(), ld
+        a.gamma = s["gamma"].data_ptr()
+        a.mean = s["mean"].data_ptr() if w.kind == "layernorm" else None
+        a.rstd = s["rstd"].data_ptr()
+        a.dx, a.lddx = views["dx"].data_ptr(), ld
+        a.dgamma = dgamma.data_ptr()
+        a.dbeta = dbeta.data_ptr() if dbeta is not None else None
+        a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+        a.stream, a.eps = stream.cuda_stream, w.eps
+        ex_args.append(a)
+
+    def step_ex(i):
+        st = lib.norm_bwd_ex(ctypes.byref(ex_args[i % nsets]))
+        if st:
+            raise RuntimeError(nb.norm_bwd_last_error())
+
+    dgamma.zero_()
+    if dbeta is not None:
+        dbeta.zero_()
+    for i in range(min(args.warmup, 50)):
+        step_ex(i)
+    ms_ex = time_loop(torch, step_ex, args.steps, stream)
+    ex_bytes = w.algorithmic_bytes() + w.N * w.wgrad_bytes * (2 if with_db else 1)
+    del ex_keep, ex_args
+
     # copy probe: the achievable streaming ceiling next to the kernels
     cp_bytes = min(512 << 20, max(set_bytes // 3 * 2, 64 << 20)) // 16 * 16
     src = torch.empty(cp_bytes // 4, dtype=torch.int32, device=dev).fill_(1)
@@ -343,6 +383,12 @@ def main(argv=None) -> int:
                 "us": round(ms_rc * 1e3, 3), "bytes": rc_bytes,
                 "GBps": round(rc_bytes / (ms_rc * 1e-3) / 1e9, 2),
                 "pct_of_peak": round(100 * rc_bytes / (ms_rc * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+            },
+            "strided_accumulate": {
+                "what": "norm_bwd_ex: x, dy, dx row stride N+64, dgamma/dbeta accumulated",
+                "us": round(ms_ex * 1e3, 3), "bytes": ex_bytes,
+                "GBps": round(ex_bytes / (ms_ex * 1e-3) / 1e9, 2),
+                "pct_of_peak": round(100 * ex_bytes / (ms_ex * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
             },
             "plan": {k: v for k, v in plan.as_dict().items()
                      if k in ("groups", "rows_per_group", "vec", "chunks", "waves_per_row",

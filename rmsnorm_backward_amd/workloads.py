@@ -63,6 +63,10 @@ class Workload:
     def io_bytes(self) -> int:
         return torch.tensor([], dtype=self.io_dtype).element_size()
 
+    @property
+    def wgrad_bytes(self) -> int:
+        return torch.tensor([], dtype=self.wgrad_dtype).element_size()
+
     def algorithmic_bytes(self, with_dbeta: Optional[bool] = None) -> int:
         """Bytes the method must move: read x, dy, gamma and the saved stats,
         write dx and the weight gradients. Workspace traffic is excluded."""
