@@ -324,6 +324,21 @@ def main(argv=None) -> int:
     for i in range(min(args.warmup, 50)):
         step_ex(i)
     ms_ex = time_loop(torch, step_ex, args.steps, stream)
+
+    # weight gradients alone by the column walk (no dx, no workspace)
+    def step_cw(i):
+        s = sets[i % nsets]
+        st = lib.norm_bwd_wgrad(0 if w.kind == "layernorm" else 1, ptr(s["x"]), ptr(s["dy"]),
+                                ptr(s.get("mean")), ptr(s["rstd"]), w.M, w.N, io, wg,
+                                ptr(dgamma), ptr(dbeta), 0, sh)
+        if st:
+            raise RuntimeError(nb.norm_bwd_last_error())
+
+    for i in range(min(args.warmup, 50)):
+        step_cw(i)
+    ms_cw = time_loop(torch, step_cw, args.steps, stream)
+    cw_bytes = w.M * (2 * w.N * w.io_bytes + (8 if with_db else 4)) + \
+        w.N * w.wgrad_bytes * (2 if with_db else 1)
     ex_bytes = w.algorithmic_bytes() + w.N * w.wgrad_bytes * (2 if with_db else 1)
     del ex_keep, ex_args
 
@@ -389,6 +404,12 @@ def main(argv=None) -> int:
                 "us": round(ms_ex * 1e3, 3), "bytes": ex_bytes,
                 "GBps": round(ex_bytes / (ms_ex * 1e-3) / 1e9, 2),
                 "pct_of_peak": round(100 * ex_bytes / (ms_ex * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+            },
+            "colwalk_wgrad": {
+                "what": "dgamma/dbeta alone by the column walk (reads x, dy, stats; no dx)",
+                "kernel": "wgrad_colwalk_kernel", "us": round(ms_cw * 1e3, 3), "bytes": cw_bytes,
+                "GBps": round(cw_bytes / (ms_cw * 1e-3) / 1e9, 2),
+                "pct_of_peak": round(100 * cw_bytes / (ms_cw * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
             },
             "plan": {k: v for k, v in plan.as_dict().items()
                      if k in ("groups", "rows_per_group", "vec", "chunks", "waves_per_row",

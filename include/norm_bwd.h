@@ -196,6 +196,26 @@ typedef struct norm_bwd_args {
 int norm_bwd_ex(const norm_bwd_args_t *args);
 
 /*
+ * Weight gradients alone, by a column walk: dgamma[j] = sum over rows of
+ * dy * xhat (and dbeta[j] = sum of dy) without dx and without a workspace.
+ * Each workgroup owns a tile of adjacent columns and walks all M rows, as the
+ * Phobos tutorial's ln_bwd_dwdb does ("05: Layer norm"), so no two workgroups
+ * write the same column. For callers that need only the weight gradients; it
+ * reads x and dy once more where the fused path reads them once for dx too.
+ *
+ *   kind, x, dy, mean, rstd, M, N, io_dtype, wgrad_dtype, dgamma, dbeta as for
+ *   norm_bwd_layernorm (contiguous [M,N]; the saved statistics are required;
+ *   dbeta may be NULL). Any N up to INT32_MAX (no register-resident rows).
+ *   flags   NORM_BWD_ACCUMULATE: old + sum, as for norm_bwd_ex.
+ * The summation order depends on M, N and io_dtype only (reproducible), and
+ * differs from the fused path's. Returns a status code.
+ */
+int norm_bwd_wgrad(int kind, const void *x, const void *dy, const float *mean,
+                   const float *rstd, int64_t M, int64_t N, int io_dtype,
+                   int wgrad_dtype, void *dgamma, void *dbeta, unsigned flags,
+                   void *stream);
+
+/*
  * An execution plan: the row grouping and the launch geometry of kernel A.
  * Produced by norm_bwd_make_plan; a caller may change `groups` (then call
  * norm_bwd_make_plan again with it) or the geometry fields for tuning, and

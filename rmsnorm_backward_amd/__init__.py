@@ -123,6 +123,7 @@ def load_library():
             "norm_fwd_layernorm": [vp, vp, vp, i64, i64, i32, fp, vp, vp, vp, vp],
             "norm_fwd_rmsnorm": [vp, vp, i64, i64, i32, fp, vp, vp, vp],
             "norm_bwd_ex": [ctypes.POINTER(NormBwdArgs)],
+            "norm_bwd_wgrad": [i32, vp, vp, vp, vp, i64, i64, i32, i32, vp, vp, ctypes.c_uint, vp],
         }
         for name, args in sigs.items():
             f = getattr(lib, name)
@@ -368,6 +369,49 @@ def norm_bwd_ex(kind: str, x: torch.Tensor, dy: torch.Tensor, gamma: torch.Tenso
     return dx, dgamma, dbeta
 
 
+def norm_bwd_wgrad(kind, x: torch.Tensor, dy: torch.Tensor, mean: Optional[torch.Tensor],
+                   rstd: torch.Tensor, *, wgrad_dtype: Optional[torch.dtype] = None,
+                   dgamma=None, dbeta=None, with_dbeta: Optional[bool] = None,
+                   accumulate: bool = False, stream=None):
+    """dgamma (and dbeta) alone by the column walk (no dx, no workspace)."""
+    lib = load_library()
+    code = kind = _KIND_CODE[kind]
+    for t, n in ((x, "x"), (dy, "dy"), (rstd, "rstd")):
+        _gpu(t, n)
+    if kind == LAYERNORM:
+        _gpu(mean, "mean")
+    else:
+        mean = None
+    M, N = _rows(x)
+    if dy.shape != x.shape or dy.dtype != x.dtype:
+        raise ValueError("dy must match x")
+    for t in (mean, rstd):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != M):
+            raise ValueError("mean and rstd must be float32 [M]")
+    if with_dbeta is None:
+        with_dbeta = dbeta is not None or (kind == LAYERNORM and not accumulate)
+    if accumulate and (dgamma is None or (with_dbeta and dbeta is None)):
+        raise ValueError("accumulate=True needs the dgamma (and dbeta) to add into")
+    wgrad_dtype = wgrad_dtype or (dgamma.dtype if dgamma is not None else torch.float32)
+    dev = x.device
+    if dgamma is None:
+        dgamma = torch.empty(N, dtype=wgrad_dtype, device=dev)
+    if with_dbeta and dbeta is None:
+        dbeta = torch.empty(N, dtype=wgrad_dtype, device=dev)
+    for t, n in ((dgamma, "dgamma"), (dbeta, "dbeta")):
+        if t is not None:
+            _gpu(t, n)
+            if t.dtype != wgrad_dtype or t.numel() != N:
+                raise ValueError(f"{n} must be [N] in wgrad_dtype")
+    s = _stream(stream, dev)
+    with torch.cuda.device(dev):
+        st = lib.norm_bwd_wgrad(code, _ptr(x), _ptr(dy), _ptr(mean), _ptr(rstd), M, N,
+                                _code(x.dtype, "x"), _code(wgrad_dtype, "wgrad"), _ptr(dgamma),
+                                _ptr(dbeta), ACCUMULATE if accumulate else 0, s)
+    _check(st)
+    return dgamma, dbeta
+
+
 def norm_bwd_execute(plan: NormBwdPlan, x, dy, gamma, mean, rstd, *, wgrad_dtype=None,
                      dx=None, dgamma=None, dbeta=None, workspace=None, stream=None):
     """Run an explicit plan (kernel A then kernel B)."""
@@ -479,5 +523,6 @@ __all__ = [
     "norm_bwd_execute", "norm_bwd_execute_partials", "norm_bwd_reduce_partials",
     "norm_bwd_probe_copy", "norm_bwd_status_string", "norm_bwd_last_error", "NormBwdPlan",
     "norm_fwd_layernorm", "norm_fwd_rmsnorm", "norm_bwd_ex", "NormBwdArgs", "ACCUMULATE",
+    "norm_bwd_wgrad",
     "NormBwdError", "load_library", "library_path",
 ]

@@ -351,6 +351,75 @@ int norm_bwd_ex(const norm_bwd_args_t* a) {
                       (a->flags & NORM_BWD_ACCUMULATE) != 0, a->stream);
 }
 
+int norm_bwd_wgrad(int kind, const void* x, const void* dy, const float* mean, const float* rstd,
+                   int64_t M, int64_t N, int io_dtype, int wgrad_dtype, void* dgamma,
+                   void* dbeta, unsigned flags, void* stream) {
+  if (kind != NORM_BWD_LAYERNORM && kind != NORM_BWD_RMSNORM)
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "kind invalid");
+  if (flags & ~(unsigned)NORM_BWD_ACCUMULATE)
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "unknown flag bits");
+  const int eb = nb::dtype_bytes(io_dtype);
+  const int wb = nb::dtype_bytes(wgrad_dtype);
+  if (eb == 0) return set_error(NORM_BWD_ERR_UNSUPPORTED, "unknown io_dtype");
+  if (wb == 0 || (wgrad_dtype != NORM_BWD_F32 && wgrad_dtype != io_dtype))
+    return set_error(NORM_BWD_ERR_UNSUPPORTED, "wgrad_dtype must be NORM_BWD_F32 or io_dtype");
+  if (M < 0 || N < 0) return set_error(NORM_BWD_ERR_INVALID_ARG, "M and N must be >= 0");
+  if (N > INT32_MAX) return set_error(NORM_BWD_ERR_UNSUPPORTED, "N too large");
+  if (N > 0 && M > (int64_t)(((uint64_t)1 << 62) / (uint64_t)N / 4u))
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "M * N too large");
+  if (N == 0) return NORM_BWD_OK;
+  if (!dgamma) return set_error(NORM_BWD_ERR_INVALID_ARG, "dgamma must be non-NULL");
+  if (M > 0) {
+    if (!x || !dy || !rstd)
+      return set_error(NORM_BWD_ERR_INVALID_ARG, "x, dy and rstd must be non-NULL");
+    if (kind == NORM_BWD_LAYERNORM && !mean)
+      return set_error(NORM_BWD_ERR_INVALID_ARG, "LayerNorm needs mean");
+  }
+  const size_t mat = (size_t)M * (size_t)N * (size_t)eb, stat = (size_t)M * 4u;
+  const size_t vec_out = (size_t)N * (size_t)wb;
+  struct R { const void* p; size_t n; };
+  const R inputs[] = {{x, mat}, {dy, mat}, {kind == NORM_BWD_LAYERNORM ? mean : nullptr, stat},
+                      {rstd, stat}};
+  const R outputs[] = {{dgamma, vec_out}, {dbeta, vec_out}};
+  for (int i = 0; i < 2; ++i)
+    for (const R& in : inputs)
+      if (nb::ranges_overlap(outputs[i].p, outputs[i].n, in.p, in.n))
+        return set_error(NORM_BWD_ERR_INVALID_ARG, "an output overlaps an input");
+  if (nb::ranges_overlap(dgamma, vec_out, dbeta, vec_out))
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "dgamma and dbeta overlap");
+  const bool accumulate = (flags & NORM_BWD_ACCUMULATE) != 0;
+  if (accumulate && M == 0) return NORM_BWD_OK;  // adds the empty sum: nothing
+  const bool vec_ok = M == 0 || (aligned16(x) && aligned16(dy) && ((size_t)N * eb) % 16 == 0);
+  nb::LaunchW w;
+  w.kind = kind;
+  w.nacc = dbeta ? 2 : 1;
+  w.vec_full = vec_ok ? 1 : 0;
+  const int vec = vec_ok ? 16 / eb : 1;
+  w.lpr = nb::wgrad_lanes_per_row(N, vec);
+  w.x = x;
+  w.dy = dy;
+  w.mean = kind == NORM_BWD_LAYERNORM ? mean : nullptr;
+  w.rstd = rstd;
+  w.M = M;
+  w.N = N;
+  w.ldx = w.ldy = N;
+  w.dgamma = dgamma;
+  w.dbeta = dbeta;
+  w.out_dtype = wgrad_dtype;
+  w.accumulate = accumulate ? 1 : 0;
+  w.grid = (N + (int64_t)w.lpr * vec - 1) / ((int64_t)w.lpr * vec);
+  w.stream = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // clear a stale error so a launch failure is ours
+  hipError_t e;
+  switch (io_dtype) {
+    case NORM_BWD_F32: e = nb::launch_w_f32(w); break;
+    case NORM_BWD_F16: e = nb::launch_w_f16(w); break;
+    default: e = nb::launch_w_bf16(w); break;
+  }
+  if (e != hipSuccess) return hip_error(e, "column-walk launch");
+  return NORM_BWD_OK;
+}
+
 int norm_bwd_execute(const norm_bwd_plan_t* plan, const void* x, const void* dy,
                      const void* gamma, const float* mean, const float* rstd, int wgrad_dtype,
                      void* dx, void* dgamma, void* dbeta, void* workspace, size_t workspace_bytes,

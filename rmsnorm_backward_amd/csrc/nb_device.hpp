@@ -566,22 +566,22 @@ constexpr int kReduceWaves = 16;
 constexpr int kReduceCols = 64;
 constexpr int kReduceUnroll = 8;
 
-template <class OutT> __device__ __forceinline__ void store_out(void* p, int j, float v);
-template <> __device__ __forceinline__ void store_out<TF32>(void* p, int j, float v) {
+template <class OutT> __device__ __forceinline__ void store_out(void* p, int64_t j, float v);
+template <> __device__ __forceinline__ void store_out<TF32>(void* p, int64_t j, float v) {
   static_cast<float*>(p)[j] = v;
 }
-template <> __device__ __forceinline__ void store_out<TF16>(void* p, int j, float v) {
+template <> __device__ __forceinline__ void store_out<TF16>(void* p, int64_t j, float v) {
   static_cast<uint16_t*>(p)[j] = pack1<TF16>(v);
 }
-template <> __device__ __forceinline__ void store_out<TBF16>(void* p, int j, float v) {
+template <> __device__ __forceinline__ void store_out<TBF16>(void* p, int64_t j, float v) {
   static_cast<uint16_t*>(p)[j] = pack1<TBF16>(v);
 }
-template <class OutT> __device__ __forceinline__ float load_out(const void* p, int j) {
+template <class OutT> __device__ __forceinline__ float load_out(const void* p, int64_t j) {
   if constexpr (OutT::kBytes == 4) {
     return static_cast<const float*>(p)[j];
   } else {
     Pack<OutT, 1> t;
-    t.load(static_cast<const char*>(p) + (int64_t)j * 2);
+    t.load(static_cast<const char*>(p) + j * 2);
     return t.get(0);
   }
 }

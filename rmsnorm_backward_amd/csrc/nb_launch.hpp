@@ -46,6 +46,28 @@ struct LaunchF {
   hipStream_t stream;
 };
 
+struct LaunchW {
+  int kind;
+  int nacc;      // 2 when dbeta is written
+  int vec_full;  // 1: 16-byte vectors, 0: one element per lane
+  int lpr;       // lanes per row of the column tile (tile = lpr * vec columns)
+  const void* x;
+  const void* dy;
+  const float* mean;
+  const float* rstd;
+  int64_t M, N, ldx, ldy;
+  void* dgamma;
+  void* dbeta;
+  int out_dtype;
+  int accumulate;
+  int64_t grid;
+  hipStream_t stream;
+};
+
+hipError_t launch_w_f32(const LaunchW& w);
+hipError_t launch_w_f16(const LaunchW& w);
+hipError_t launch_w_bf16(const LaunchW& w);
+
 hipError_t launch_a_f32(const LaunchA& a);
 hipError_t launch_a_f16(const LaunchA& a);
 hipError_t launch_a_bf16(const LaunchA& a);

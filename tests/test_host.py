@@ -38,7 +38,8 @@ def test_header_declares_the_documented_entry_points():
     for want in ("norm_bwd_layernorm", "norm_bwd_rmsnorm", "norm_bwd_workspace_bytes",
                  "norm_bwd_make_plan", "norm_bwd_execute", "norm_bwd_execute_partials",
                  "norm_bwd_reduce_partials", "norm_bwd_status_string", "norm_bwd_last_error",
-                 "norm_bwd_probe_copy", "norm_fwd_layernorm", "norm_fwd_rmsnorm"):
+                 "norm_bwd_probe_copy", "norm_fwd_layernorm", "norm_fwd_rmsnorm", "norm_bwd_ex",
+                 "norm_bwd_wgrad"):
         assert want in names
 
 
@@ -376,6 +377,35 @@ def test_ex_empty_accumulate_is_a_no_op(nb):
     assert _ex(nb, N=0) == 0
 
 
+def _wg(nb, **over):
+    a = dict(kind=0, x=_addr(0), dy=_addr(1), mean=_addr(2), rstd=_addr(3), M=M_, N=N_, io=2,
+             wg=0, dgamma=_addr(4), dbeta=_addr(5), flags=0, stream=None)
+    a.update(over)
+    return nb.load_library().norm_bwd_wgrad(a["kind"], a["x"], a["dy"], a["mean"], a["rstd"],
+                                            a["M"], a["N"], a["io"], a["wg"], a["dgamma"],
+                                            a["dbeta"], a["flags"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(kind=2), 1), (dict(flags=4), 1), (dict(io=9), 2), (dict(wg=1), 2), (dict(wg=5), 2),
+    (dict(M=-1), 1), (dict(N=-1), 1), (dict(N=1 << 31), 2),
+    (dict(x=None), 1), (dict(dy=None), 1), (dict(rstd=None), 1), (dict(mean=None), 1),
+    (dict(dgamma=None), 1), (dict(dgamma=_addr(0)), 1), (dict(dbeta=_addr(3)), 1),
+    (dict(dbeta=ctypes.c_void_p(B + 4 * (1 << 30) + 64)), 1),
+])
+@no_gpu
+def test_wgrad_rejects(nb, over, status):
+    assert _wg(nb, **over) == status
+    assert nb.norm_bwd_last_error().startswith(nb.norm_bwd_status_string(status))
+
+
+@no_gpu
+def test_wgrad_trivial_cases_launch_nothing(nb):
+    assert _wg(nb, N=0) == 0
+    assert _wg(nb, M=0, flags=1, x=None, dy=None, mean=None, rstd=None) == 0
+    assert _wg(nb, kind=1, mean=None, M=0, flags=1) == 0
+
+
 def test_binding_refuses_cpu_tensors(nb):
     x = torch.zeros(4, 8, dtype=torch.bfloat16)
     g = torch.zeros(8, dtype=torch.bfloat16)
@@ -388,3 +418,5 @@ def test_binding_refuses_cpu_tensors(nb):
         nb.norm_fwd_layernorm(x, g, None)
     with pytest.raises(ValueError, match="GPU"):
         nb.norm_fwd_rmsnorm(x, g)
+    with pytest.raises(ValueError, match="GPU"):
+        nb.norm_bwd_wgrad("rmsnorm", x, x, None, torch.ones(4))
