@@ -242,7 +242,7 @@ typedef struct norm_bwd_plan {
 
 /*
  * Fill *plan for (kind, M, N, io_dtype, with_dbeta). groups = 0 chooses the
- * automatic group count (2048 / (waves per workgroup), at most ceil(M / 8):
+ * automatic group count (2048 / (waves per workgroup), at most ceil(M / 4):
  * a function of the problem only, never of the device); groups > 0 asks for
  * that many row groups,
  * clamped to M so that no group is empty. The plan

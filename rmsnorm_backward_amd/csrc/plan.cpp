@@ -14,7 +14,7 @@ constexpr int64_t kTargetWaves = 2048;  // waves in flight the group count aims 
 // The forward streams one operand per row where kernel A streams two, so it
 // needs twice the waves (16 per compute unit) for as many bytes in flight.
 constexpr int64_t kForwardTargetWaves = 4096;
-constexpr int64_t kMinRowsPerGroup = 8;
+constexpr int64_t kMinRowsPerGroup = 4;
 constexpr int64_t kMaxGrid = 1 << 20;
 constexpr int kMaxLdsBytes = 65536 - 1024;  // dynamic LDS; the kernel adds 256 B static
 constexpr int kTargetThreads = 512;

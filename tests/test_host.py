@@ -97,7 +97,7 @@ def _auto_groups(nb, kind, M, N, dt):
     if M == 0:
         return 0
     waves = nb.norm_bwd_make_plan(kind, 1, N, dt, False).threads // 64 if N else 8
-    return max(1, min(2048 // waves, -(-M // 8)))
+    return max(1, min(2048 // waves, -(-M // 4)))
 
 
 @pytest.mark.parametrize("kind,M,N,dt,db", [
