@@ -13,6 +13,13 @@
 // registers; then the RPW slots of a wave are added by an xor butterfly (the
 // same tree for every lane), and the 16 wave sums in wave order through LDS.
 // The order depends on (M, LPR, VEC) only, so results are reproducible.
+//
+// Tiles narrower than a 128-byte line share lines with their neighbours.
+// Workgroups are dispatched to the 8 XCDs round-robin (block b to XCD b mod 8)
+// and each XCD has its own L2, so neighbouring tiles on different XCDs would
+// each fetch the shared lines from HBM. Block b therefore takes tile
+// (b mod 8) * (T / 8) + b / 8 when the tile count T is a multiple of 8: each
+// XCD walks a contiguous run of tiles, and line neighbours share its L2.
 #pragma once
 
 #include "nb_device.hpp"
@@ -20,6 +27,7 @@
 namespace nb {
 
 constexpr int kWgradWaves = 16;
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
 constexpr int kWgradUnroll = 4;
 constexpr int kWgradMaxTile = 64;  // columns
 
@@ -48,7 +56,11 @@ void wgrad_colwalk_kernel(const void* __restrict__ xv, const void* __restrict__ 
   const int c = lane % LPR;
   const int slot = lane / LPR;
   const int TW = LPR * VEC;
-  const int64_t col = (int64_t)blockIdx.x * TW + (int64_t)c * VEC;
+  const int64_t T = gridDim.x;
+  const int64_t tile = (T % kXcds == 0)
+                           ? (int64_t)(blockIdx.x % kXcds) * (T / kXcds) + blockIdx.x / kXcds
+                           : (int64_t)blockIdx.x;
+  const int64_t col = tile * TW + (int64_t)c * VEC;
   const bool colok = col < N;  // N is a multiple of VEC on this path
   const int64_t rstep = (int64_t)kWgradWaves * RPW;
 
@@ -109,7 +121,7 @@ void wgrad_colwalk_kernel(const void* __restrict__ xv, const void* __restrict__ 
   const int t = threadIdx.x;
   if (t < NACC * TW) {
     const int plane = t / TW, j = t % TW;
-    const int64_t oc = (int64_t)blockIdx.x * TW + j;
+    const int64_t oc = tile * TW + j;
     if (oc < N) {
       float s = part[plane][0][j];
       for (int w = 1; w < kWgradWaves; ++w) s += part[plane][w][j];

@@ -32,7 +32,7 @@ int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok
 int64_t forward_grid(int64_t M, int S, int P);
 
 // Lanes per row of the column-walk tile (tile = lpr * vec columns) for N
-// columns: the widest tile (up to 64 columns) that still gives at least 128
+// columns: the widest tile (up to 64 columns) that still gives at least 256
 // tiles, and at least one lane.
 int wgrad_lanes_per_row(int64_t N, int vec);
 

@@ -32,6 +32,7 @@ import sys
 KERNEL_A = "dx_partials_kernel"
 KERNEL_B = "reduce_partials_kernel"
 FORWARD = "norm_fwd_kernel"
+COLWALK = "wgrad_colwalk_kernel"
 COPY = "copy_probe_kernel"
 _HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCE = os.path.join(_HERE, "csrc", "nb_device.hpp")
@@ -173,6 +174,17 @@ def pmc_summary(fetch_csv: str, write_csv: str, bench_json: str, cmds) -> str:
                 "", f"forward launches counted: {nf}",
                 f"forward_traffic_bytes_per_launch: {ftraffic}",
                 f"forward_source_sha256_16: {forward_source_hash()}"]
+    fc_, ncw = _mean_for(f, COLWALK)
+    wc_, _ = _mean_for(w, COLWALK)
+    cw = c.get("colwalk_wgrad")
+    if fc_ is not None and wc_ is not None and cw:
+        cr, cwb = fc_ * 1024.0 * fscale, wc_ * 1024.0 * wscale
+        ct = int(round(cr + cwb))
+        out += ["", "| column walk, per launch | counter (KiB) | scaled bytes |", "|---|---|---|",
+                f"| read (FETCH_SIZE) | {fc_:.1f} | {cr:.0f} |",
+                f"| write (WRITE_SIZE) | {wc_:.1f} | {cwb:.0f} |",
+                f"| total | | {ct} (algorithmic {cw['bytes']}, ratio {ct / cw['bytes']:.4f}) |",
+                "", f"column-walk launches counted: {ncw}"]
     out += ["", f"kernel A launches counted: {na}",
             f"traffic_bytes_per_launch: {traffic}",
             f"kernel_source_sha256_16: {kernel_source_hash()}", ""]
