@@ -67,8 +67,8 @@ def committed_traffic(workload: str):
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
-    t = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    m = re.search(r"^kernel_source_sha256_16:\s*([0-9a-f]{16})", text, re.M)
+    t = re.search(r"^traffic_bytes_per_launch:\s*([0-9]+)", text, re.M)
     if not m or not t or m.group(1) != kernel_source_hash():
         return None
     return int(t.group(1))
@@ -82,8 +82,8 @@ def committed_forward_traffic(workload: str):
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m = re.search(r"forward_source_sha256_16:\s*([0-9a-f]{16})", text)
-    t = re.search(r"forward_traffic_bytes_per_launch:\s*([0-9]+)", text)
+    m = re.search(r"^forward_source_sha256_16:\s*([0-9a-f]{16})", text, re.M)
+    t = re.search(r"^forward_traffic_bytes_per_launch:\s*([0-9]+)", text, re.M)
     if not m or not t or m.group(1) != profiling.forward_source_hash():
         return None
     return int(t.group(1))

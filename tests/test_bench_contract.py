@@ -1,0 +1,70 @@
+"""The benchmark's host-side contract (no GPU): byte accounting, the refusal
+of several GPUs, and reading the committed counter summaries."""
+
+from __future__ import annotations
+
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from rmsnorm_backward_amd import profiling  # noqa: E402
+from rmsnorm_backward_amd import workloads as W  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+@pytest.mark.parametrize("w", list(W.WORKLOADS.values()), ids=lambda w: w.name)
+def test_byte_accounting(w):
+    s = w.io_bytes
+    stats = 8 if w.kind == "layernorm" else 4
+    # kernel A: x, dy read, dx written, statistics, gamma once
+    assert bench.kernel_a_bytes(w) == w.M * (3 * w.N * s + stats) + w.N * s
+    # the whole step adds the weight gradients written
+    nw = 2 if w.kind == "layernorm" else 1
+    assert w.algorithmic_bytes() == bench.kernel_a_bytes(w) + nw * w.N * w.wgrad_bytes
+    # forward: x read, y written, statistics written, gamma (and beta)
+    assert bench.forward_bytes(w, False) == w.M * (2 * w.N * s + stats) + w.N * s
+    assert bench.forward_bytes(w, True) == bench.forward_bytes(w, False) + w.N * s
+
+
+def _summaries():
+    d = os.path.join(ROOT, "profiles")
+    return sorted(f for f in os.listdir(d) if f.startswith("pmc_dx_partials_"))
+
+
+@pytest.mark.parametrize("name", _summaries())
+def test_committed_traffic_is_read_from_the_right_lines(name):
+    """Each summary names kernel A's and the forward's traffic on lines of their
+    own; the reader must take kernel A's line, not the forward's (whose key
+    contains kernel A's key)."""
+    workload = name[len("pmc_dx_partials_"):-len(".md")]
+    w = W.WORKLOADS[workload]
+    text = open(os.path.join(ROOT, "profiles", name)).read()
+    a = int(re.search(r"^traffic_bytes_per_launch:\s*([0-9]+)", text, re.M).group(1))
+    f = int(re.search(r"^forward_traffic_bytes_per_launch:\s*([0-9]+)", text, re.M).group(1))
+    assert a >= bench.kernel_a_bytes(w) and f >= bench.forward_bytes(w, False)
+    got_a = bench.committed_traffic(workload)
+    got_f = bench.committed_forward_traffic(workload)
+    if re.search(r"^kernel_source_sha256_16:\s*(\S+)", text, re.M).group(1) == \
+            profiling.kernel_source_hash():
+        assert got_a == a
+    else:
+        assert got_a is None          # a stale summary is never reported
+    if re.search(r"^forward_source_sha256_16:\s*(\S+)", text, re.M).group(1) == \
+            profiling.forward_source_hash():
+        assert got_f == f
+    else:
+        assert got_f is None
