@@ -70,8 +70,9 @@ void oracle_norm_fwd_stats(int kind, const double *x, long M, long N,
 
 /*
  * Forward output y = gamma * xhat + beta (beta may be NULL: treated as 0),
- * also returning the statistics. Used only to take finite differences of
- * L = sum(dy * y) in the oracle's own self-tests.
+ * also returning the statistics ("05: Layer norm", the Phobos tutorial's
+ * forward). The reference for the GPU forward, and the function whose finite
+ * differences of L = sum(dy * y) pin the backward.
  */
 void oracle_norm_fwd(int kind, const double *x, const double *gamma,
                      const double *beta, long M, long N, double eps,

@@ -146,7 +146,8 @@ def check_jacobian(orc, seed=12):
 
 
 def check_torch_autograd(orc, seed=13):
-    """torch CPU float64 autograd of F.layer_norm / F.rms_norm."""
+    """torch CPU float64 autograd of F.layer_norm / F.rms_norm, and their
+    forward outputs."""
     import torch
     import torch.nn.functional as F
     rng = np.random.default_rng(seed)
@@ -166,6 +167,16 @@ def check_torch_autograd(orc, seed=13):
             _close(dx, tx.grad.numpy(), 1e-10, 1e-12, f"{kind} {M}x{N} torch dx")
             _close(dg, tg.grad.numpy(), 1e-10, 1e-12, f"{kind} {M}x{N} torch dgamma")
             _close(db, tb.grad.numpy(), 1e-12, 1e-12, f"{kind} {M}x{N} torch dbeta")
+            # the forward output matches torch's forward (with beta, and without)
+            oy, _, _ = orc.fwd(kind, x, gamma, beta, eps)
+            _close(oy, y.detach().numpy(), 1e-12, 1e-13, f"{kind} {M}x{N} torch y")
+            with torch.no_grad():
+                if kind == "layernorm":
+                    y0 = F.layer_norm(torch.tensor(x), (N,), torch.tensor(gamma), None, eps)
+                else:
+                    y0 = F.rms_norm(torch.tensor(x), (N,), torch.tensor(gamma), eps)
+            oy0, _, _ = orc.fwd(kind, x, gamma, None, eps)
+            _close(oy0, y0.numpy(), 1e-12, 1e-13, f"{kind} {M}x{N} torch y (no beta)")
             # the forward statistics the oracle saves match torch's
             xt = torch.tensor(x)
             if kind == "layernorm":

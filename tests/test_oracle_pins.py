@@ -57,6 +57,10 @@ MUTANTS = {
     "rms_eps_dropped": (
         "rstd[r] = 1.0 / sqrt(q / (double)N + eps);",
         "rstd[r] = 1.0 / sqrt(q / (double)N);"),
+    "y_drops_beta": (
+        "double b = beta ? beta[j] : 0.0;", "double b = 0.0;"),
+    "y_gamma_reversed": (
+        "y[r * N + j] = gamma[j] * xh + b;", "y[r * N + j] = gamma[N - 1 - j] * xh + b;"),
     "gamma_transposed_in_sum": (
         "            double dyh = dyr[j] * gamma[j];\n            sum_dyhat += dyh;",
         "            double dyh = dyr[j] * gamma[N - 1 - j];\n            sum_dyhat += dyh;"),
