@@ -1,9 +1,11 @@
 // nb_device.hpp -- device code of the norm-backward library (gfx950, wave64).
 //
 // Kernel A (dx_partials_kernel): one pass over x and dy. For each row it
-// recomputes xhat from the saved statistics, takes the in-row sums
-// sum_j(dy*gamma) (LayerNorm only) and sum_j(dy*gamma*xhat), writes dx, and
-// adds dy*xhat (and dy) into per-lane fp32 accumulators. Workgroup g owns row
+// recomputes xhat from the saved statistics (or, in recompute mode, first
+// recomputes the statistics themselves from the row held in registers),
+// takes the in-row sums sum_j(dy*gamma) (LayerNorm only) and
+// sum_j(dy*gamma*xhat), writes dx, and adds dy*xhat (and dy) into per-lane
+// fp32 accumulators. Rows of x, dy and dx may have their own strides. Workgroup g owns row
 // group g -- the rows r with r mod G == g -- processes them in ascending
 // order and stores one partial row per group into the workspace. No two
 // workgroups ever write the same slot, so there are no atomics: this is the
@@ -15,8 +17,9 @@
 //
 // Kernel B (reduce_partials_kernel): column tiles of 64 features; 16 waves
 // each sum a fixed contiguous slice of the groups in ascending order, then
-// one wave adds the 16 slice sums in slice order and rounds to the output
-// type. The order depends only on the group count.
+// one wave adds the 16 slice sums in slice order (and, when accumulating, the
+// output's previous value) and rounds to the output type. The order depends
+// only on the group count.
 //
 // Lane ownership inside a row (kernel A). A row of N elements is split into
 // C chunks; chunk c is covered by the S waves sharing the row, wave s taking
