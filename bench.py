@@ -202,7 +202,10 @@ def main(argv=None) -> int:
         sets.append(s)
     dgamma = torch.empty(w.N, dtype=w.wgrad_dtype, device=dev)
     dbeta = torch.empty(w.N, dtype=w.wgrad_dtype, device=dev) if with_db else None
-    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+    # enough for the explicit plan and for the automatic plan of either
+    # statistics mode (LayerNorm recompute plans more row groups)
+    ws_bytes = max(plan.workspace_bytes, nb.norm_bwd_workspace_bytes(w.kind, w.M, w.N, io, with_db))
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     P = ctypes.c_void_p
     ptr = lambda t: None if t is None else P(t.data_ptr())  # noqa: E731
 
@@ -395,6 +398,8 @@ def main(argv=None) -> int:
             },
             "recompute": {
                 "what": "whole backward step with mean/rstd recomputed from x (no stats read)",
+                "groups": nb.norm_bwd_workspace_bytes(w.kind, w.M, w.N, io, with_db) //
+                (w.N * 4 * (2 if with_db else 1)),
                 "us": round(ms_rc * 1e3, 3), "bytes": rc_bytes,
                 "GBps": round(rc_bytes / (ms_rc * 1e-3) / 1e9, 2),
                 "pct_of_peak": round(100 * rc_bytes / (ms_rc * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),

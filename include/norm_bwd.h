@@ -154,9 +154,11 @@ size_t norm_bwd_workspace_bytes(int kind, int64_t M, int64_t N, int io_dtype,
  *             group sum and rounded once to wgrad_dtype; M = 0 leaves them
  *             unchanged. Without it they are overwritten. Other bits:
  *             NORM_BWD_ERR_INVALID_ARG.
- *   groups    0 = automatic, else as norm_bwd_make_plan; the workspace must
- *             hold norm_bwd_make_plan(kind, M, N, io_dtype, dbeta != NULL,
- *             groups).workspace_bytes
+ *   groups    0 = automatic (the workspace must then hold
+ *             norm_bwd_workspace_bytes(kind, M, N, io_dtype, dbeta != NULL)),
+ *             else as norm_bwd_make_plan (the workspace must hold
+ *             norm_bwd_make_plan(kind, M, N, io_dtype, dbeta != NULL,
+ *             groups).workspace_bytes)
  *   ldx, lddy, lddx  row strides of x, dy and dx in elements (0 = N, else
  *             >= N). Row r of x starts at x + r * ldx. Elements between rows
  *             are neither read nor written. 16-byte vector access is used only
@@ -214,6 +216,13 @@ int norm_bwd_wgrad(int kind, const void *x, const void *dy, const float *mean,
                    const float *rstd, int64_t M, int64_t N, int io_dtype,
                    int wgrad_dtype, void *dgamma, void *dbeta, unsigned flags,
                    void *stream);
+
+/*
+ * (Declared above.) norm_bwd_workspace_bytes returns enough for the automatic
+ * plan of either statistics mode: LayerNorm in recompute mode plans twice the
+ * row groups (two workgroups per compute unit hide its second exchange per
+ * row), so for LayerNorm it is max(saved-statistics plan, recompute plan).
+ */
 
 /*
  * An execution plan: the row grouping and the launch geometry of kernel A.

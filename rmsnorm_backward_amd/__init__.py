@@ -246,7 +246,10 @@ def _backward(kind, x, dy, gamma, mean, rstd, eps, wgrad_dtype, dx, dgamma, dbet
     s = _stream(stream, dev)
     with torch.cuda.device(dev):
         if plan is None:
-            need = norm_bwd_make_plan(kind, M, N, io, dbeta is not None).workspace_bytes
+            # the plan call raises the precise status for unsupported shapes;
+            # the size call covers the automatic plan of either statistics mode
+            need = max(norm_bwd_make_plan(kind, M, N, io, dbeta is not None).workspace_bytes,
+                       norm_bwd_workspace_bytes(kind, M, N, io, dbeta is not None))
             if workspace is None:
                 workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
             wsb = workspace.numel() * workspace.element_size()
@@ -347,6 +350,8 @@ def norm_bwd_ex(kind: str, x: torch.Tensor, dy: torch.Tensor, gamma: torch.Tenso
                 raise ValueError(f"{n} must be [N] in wgrad_dtype")
     io = _code(x.dtype, "x")
     need = norm_bwd_make_plan(kind, M, N, io, dbeta is not None, groups).workspace_bytes
+    if not groups:
+        need = max(need, norm_bwd_workspace_bytes(kind, M, N, io, dbeta is not None))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     _gpu(workspace, "workspace")

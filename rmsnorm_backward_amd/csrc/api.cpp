@@ -200,7 +200,8 @@ int run_backward(int kind, Buffers b, int64_t M, int64_t N, int io_dtype, int wg
                       aligned16(b.dx);
   norm_bwd_plan_t p;
   const char* why = nullptr;
-  int st = nb::make_plan(kind, M, N, io_dtype, b.dbeta ? 1 : 0, groups, vec_ok, &p, &why);
+  int st = nb::make_plan(kind, M, N, io_dtype, b.dbeta ? 1 : 0, groups, vec_ok, &p, &why,
+                         recompute);
   if (st != NORM_BWD_OK) return set_error(st, why);
   st = check_buffers(kind, M, N, io_dtype, wgrad_dtype, true, true, p.workspace_bytes, b,
                      recompute);
@@ -315,10 +316,13 @@ int norm_bwd_rmsnorm(const void* x, const void* dy, const void* gamma, const flo
 }
 
 size_t norm_bwd_workspace_bytes(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta) {
-  norm_bwd_plan_t p;
-  if (nb::make_plan(kind, M, N, io_dtype, with_dbeta ? 1 : 0, 0, true, &p, nullptr) != NORM_BWD_OK)
+  // enough for the automatic plan of either statistics mode
+  norm_bwd_plan_t p, q;
+  if (nb::make_plan(kind, M, N, io_dtype, with_dbeta ? 1 : 0, 0, true, &p, nullptr) != NORM_BWD_OK ||
+      nb::make_plan(kind, M, N, io_dtype, with_dbeta ? 1 : 0, 0, true, &q, nullptr, true) !=
+          NORM_BWD_OK)
     return (size_t)-1;
-  return p.workspace_bytes;
+  return p.workspace_bytes > q.workspace_bytes ? p.workspace_bytes : q.workspace_bytes;
 }
 
 int norm_bwd_make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,

@@ -11,6 +11,10 @@ namespace nb {
 
 namespace {
 constexpr int64_t kTargetWaves = 2048;  // waves in flight the group count aims at
+// LayerNorm in recompute mode exchanges twice per row; a second workgroup per
+// compute unit hides that latency (65536 x 8192 bf16: 570 us at 512 groups
+// against 645 us at 256), so it aims at twice the waves.
+constexpr int64_t kRecomputeLnTargetWaves = 4096;
 // The forward streams one operand per row where kernel A streams two, so it
 // needs twice the waves (16 per compute unit) for as many bytes in flight.
 constexpr int64_t kForwardTargetWaves = 4096;
@@ -125,7 +129,7 @@ int wgrad_lanes_per_row(int64_t N, int vec) {
   return lpr;
 }
 
-int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype) {
+int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype, bool recompute) {
   if (M <= 0) return 0;
   // Enough workgroups for about kTargetWaves waves in flight (8 per compute
   // unit on a 256-CU part), never fewer than kMinRowsPerGroup rows per
@@ -136,14 +140,16 @@ int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype) {
   int waves = 8;
   if (N > 0 && make_geometry(kind, N, io_dtype, 0, true, &g, &why) == NORM_BWD_OK)
     waves = g.threads / 64;
-  int64_t G = kTargetWaves / waves;
+  int64_t G = ((recompute && kind == NORM_BWD_LAYERNORM) ? kRecomputeLnTargetWaves : kTargetWaves) /
+              waves;
   const int64_t cap = ceil_div(M, kMinRowsPerGroup);
   if (G > cap) G = cap;
   return G < 1 ? 1 : G;
 }
 
 int make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,
-              int64_t groups, bool vec_ok16, norm_bwd_plan_t* plan, const char** why) {
+              int64_t groups, bool vec_ok16, norm_bwd_plan_t* plan, const char** why,
+              bool recompute) {
   if (!plan) return fail(why, "plan is NULL", NORM_BWD_ERR_INVALID_ARG);
   if (kind != NORM_BWD_LAYERNORM && kind != NORM_BWD_RMSNORM)
     return fail(why, "kind must be NORM_BWD_LAYERNORM or NORM_BWD_RMSNORM", NORM_BWD_ERR_INVALID_ARG);
@@ -172,7 +178,7 @@ int make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,
   }
 
   if (M > 0) {
-    int64_t G = groups ? groups : auto_groups(kind, M, N, io_dtype);
+    int64_t G = groups ? groups : auto_groups(kind, M, N, io_dtype, recompute);
     if (G > M) G = M;  // every group holds at least one row
     p.groups = G;
     p.rows_per_group = ceil_div(M, G);

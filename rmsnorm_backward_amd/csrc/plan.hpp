@@ -36,13 +36,17 @@ int64_t forward_grid(int64_t M, int S, int P);
 // tiles, and at least one lane.
 int wgrad_lanes_per_row(int64_t N, int vec);
 
-// Automatic group count for (kind, M, N, io_dtype): independent of the device.
-int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype);
+// Automatic group count for (kind, M, N, io_dtype) and the statistics mode:
+// about 2048 waves in flight (4096 for LayerNorm in recompute mode), at least
+// 4 rows per group. Independent of the device.
+int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype, bool recompute = false);
 
 // Fill *plan (see norm_bwd_make_plan). `vec_ok16` says whether the caller's
 // pointers are 16-byte aligned. Writes a message into *why on failure.
+// `recompute`: the plan is for recompute mode (affects the automatic groups).
 int make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,
-              int64_t groups, bool vec_ok16, norm_bwd_plan_t* plan, const char** why);
+              int64_t groups, bool vec_ok16, norm_bwd_plan_t* plan, const char** why,
+              bool recompute = false);
 
 // Check every field of a (possibly caller-edited) plan. Returns a status.
 int validate_plan(const norm_bwd_plan_t* plan, const char** why);

@@ -175,6 +175,26 @@ def test_recompute_is_deterministic(nb):
             assert torch.equal(a, b)
 
 
+def test_recompute_workspace_rule(nb):
+    """LayerNorm in recompute mode plans twice the row groups (4096 waves);
+    norm_bwd_workspace_bytes covers it, the saved-statistics plan's size does
+    not, and a short workspace is refused before any launch."""
+    w = W.scaled(W.LN_BF16_65536x8192, M=4096, N=1024)
+    inp = W.make_inputs(w)
+    x, dy, g = inp["x"].cuda(), inp["dy"].cuda(), inp["gamma"].cuda()
+    saved = nb.norm_bwd_make_plan("layernorm", w.M, w.N, w.io_dtype, True).workspace_bytes
+    need = nb.norm_bwd_workspace_bytes("layernorm", w.M, w.N, w.io_dtype, True)
+    assert need == 2 * saved
+    short = torch.empty(saved, dtype=torch.uint8, device="cuda")
+    with pytest.raises(nb.NormBwdError) as e:
+        nb.norm_bwd_layernorm(x, dy, g, None, None, w.eps, workspace=short)
+    assert e.value.status == nb.ERR_WORKSPACE
+    full = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = nb.norm_bwd_layernorm(x, dy, g, None, None, w.eps, workspace=full)
+    torch.cuda.synchronize()
+    compare(w, inp["x"], inp["dy"], inp["gamma"], tuple(t.cpu() for t in out), True)
+
+
 def test_recompute_argument_rules(nb):
     w = W.scaled(W.LN_F32_128x512, M=8, N=64)
     inp = W.make_inputs(w)

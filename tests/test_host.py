@@ -91,13 +91,15 @@ def test_status_strings(nb):
     assert nb.norm_bwd_status_string(99) == "NORM_BWD_ERR_UNKNOWN"
 
 
-def _auto_groups(nb, kind, M, N, dt):
-    """The documented rule: about 2048 waves in flight, >= 8 rows per group,
-    where the waves per workgroup come from the (dbeta-less) geometry."""
+def _auto_groups(nb, kind, M, N, dt, recompute=False):
+    """The documented rule: about 2048 waves in flight (4096 for LayerNorm in
+    recompute mode), >= 4 rows per group, where the waves per workgroup come
+    from the (dbeta-less) geometry."""
     if M == 0:
         return 0
     waves = nb.norm_bwd_make_plan(kind, 1, N, dt, False).threads // 64 if N else 8
-    return max(1, min(2048 // waves, -(-M // 4)))
+    target = 4096 if (recompute and kind == "layernorm") else 2048
+    return max(1, min(target // waves, -(-M // 4)))
 
 
 @pytest.mark.parametrize("kind,M,N,dt,db", [
@@ -112,9 +114,11 @@ def _auto_groups(nb, kind, M, N, dt):
 ])
 def test_workspace_bytes_rule(nb, kind, M, N, dt, db):
     got = nb.norm_bwd_workspace_bytes(kind, M, N, dt, db)
-    assert got == (2 if db else 1) * _auto_groups(nb, kind, M, N, dt) * N * 4
-    plan = nb.norm_bwd_make_plan(kind, M, N, dt, db)
-    assert plan.workspace_bytes == got
+    groups = max(_auto_groups(nb, kind, M, N, dt), _auto_groups(nb, kind, M, N, dt, True))
+    assert got == (2 if db else 1) * groups * N * 4
+    plan = nb.norm_bwd_make_plan(kind, M, N, dt, db)   # the saved-statistics plan
+    assert plan.workspace_bytes <= got
+    assert plan.workspace_bytes == (2 if db else 1) * _auto_groups(nb, kind, M, N, dt) * N * 4
 
 
 def test_workspace_bytes_rejects_bad_arguments(nb):
