@@ -414,3 +414,36 @@ def test_copy_probe(nb):
     nb.norm_bwd_probe_copy(src, dst)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+
+
+def test_offsets_beyond_2gib(nb):
+    """x, dy and dx of 2^20 + 3 rows x 1024 bf16 (just over 2 GiB each): rows
+    near the end sit past byte offset 2^31, so every kernel's address
+    arithmetic must be 64-bit. Inputs are drawn on the GPU from a seeded
+    generator; sampled rows and columns go to the oracle."""
+    M, N, eps = (1 << 20) + 3, 1024, 1e-6
+    gen = torch.Generator(device="cuda").manual_seed(2024)
+    x = torch.randn(M, N, generator=gen, device="cuda").to(torch.bfloat16)
+    dy = (torch.randn(M, N, generator=gen, device="cuda") * 1e-2).to(torch.bfloat16)
+    gamma = (torch.rand(N, generator=gen, device="cuda") + 0.5).to(torch.bfloat16)
+    assert (M - 1) * N * 2 > (1 << 31)
+    y, rstd = nb.norm_fwd_rmsnorm(x, gamma, eps)
+    dx, dg, _ = nb.norm_bwd_rmsnorm(x, dy, gamma, rstd, eps)
+    cg, _ = nb.norm_bwd_wgrad("rmsnorm", x, dy, None, rstd)
+    torch.cuda.synchronize()
+    rows = torch.tensor([0, 1, M // 2, (1 << 20) - 1, 1 << 20, M - 2, M - 1])
+    xr, dyr, gc = x[rows].cpu(), dy[rows].cpu(), gamma.cpu()
+    ry, _, rr = oracle.fwd("rmsnorm", xr, gc, None, eps)
+    parity.check_forward(torch.bfloat16, "rmsnorm", xr, gc, None, y[rows].cpu(), None,
+                         rstd[rows].cpu(), ry, None, rr)
+    rs = rstd[rows].cpu()
+    rdx = oracle.bwd_dx("rmsnorm", xr, dyr, gc, None, rs)
+    parity.check_dx(torch.bfloat16, dx[rows].cpu(),
+                    rdx, scale=parity.dx_term_scale("rmsnorm", xr, dyr, gc, None, rs))
+    cols = torch.tensor([0, 5, 511, 1023])
+    rdg, _ = oracle.bwd_wgrad("rmsnorm", x[:, cols].cpu(), dy[:, cols].cpu(), None,
+                              rstd.cpu(), want_dbeta=False)
+    parity.check_wgrad(torch.bfloat16, dg[cols].cpu(), rdg)
+    parity.check_wgrad(torch.bfloat16, cg[cols].cpu(), rdg)
+    del x, dy, dx, y
+    torch.cuda.empty_cache()
