@@ -67,9 +67,16 @@ extern "C" {
 #define NORM_BWD_RMSNORM 1
 
 /*
- * Largest N the fused path takes. "Aligned" means N is a multiple of
- * 16 / element size and x, dy, gamma, dx start on 16-byte boundaries; other
- * rows use one element per lane. Larger N returns NORM_BWD_ERR_UNSUPPORTED.
+ * Largest N the fused path takes (rows held in registers). "Aligned" means N
+ * is a multiple of 16 / element size and x, dy, gamma, dx start on 16-byte
+ * boundaries; other rows use one element per lane. Wider rows (up to
+ * INT32_MAX) take the wide-row path in norm_bwd_layernorm, norm_bwd_rmsnorm,
+ * norm_bwd_ex (automatic groups) and the forward: a row-loop kernel streams
+ * each row in chunks (one workgroup per row) for dx or y, and the column walk
+ * (see norm_bwd_wgrad) forms dgamma/dbeta, with no workspace beyond the
+ * recomputed statistics (4 or 8 bytes per row) in recompute mode. The
+ * explicit-plan entry points (norm_bwd_make_plan, norm_bwd_execute*) cover
+ * the fused path only and return NORM_BWD_ERR_UNSUPPORTED beyond it.
  */
 #define NORM_BWD_MAX_N_16BIT 32768          /* fp16/bf16, aligned, dbeta NULL */
 #define NORM_BWD_MAX_N_16BIT_DBETA 16384    /* fp16/bf16, aligned, dbeta requested */
@@ -308,7 +315,8 @@ int norm_bwd_reduce_partials(int64_t groups, int64_t N, int wgrad_dtype,
  *   x [M,N], gamma [N], beta [N] or NULL (read, io_dtype)
  *   y [M,N] io_dtype (written); mean, rstd fp32 [M] (written; either may be
  *   NULL to skip it)
- * Same size limits as the backward without dbeta. Asynchronous on `stream`;
+ * Any N up to INT32_MAX (wider than the fused limits without dbeta: the
+ * row-loop forward, three passes over each row). Asynchronous on `stream`;
  * checked on the host first (status codes as above). Allocates nothing.
  */
 int norm_fwd_layernorm(const void *x, const void *gamma, const void *beta,

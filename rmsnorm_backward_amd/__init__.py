@@ -201,6 +201,16 @@ def norm_bwd_workspace_bytes(kind, M: int, N: int, io_dtype, with_dbeta: bool) -
     return n
 
 
+def _auto_workspace(kind, M, N, io, with_dbeta) -> int:
+    """Workspace for an automatic plan of either statistics mode (fused or
+    wide-row path). An invalid shape raises with the plan call's status."""
+    n = load_library().norm_bwd_workspace_bytes(_KIND_CODE[kind], M, N, io, int(bool(with_dbeta)))
+    if n == ctypes.c_size_t(-1).value:
+        norm_bwd_make_plan(kind, M, N, io, with_dbeta)      # raises the precise status
+        raise NormBwdError(ERR_INVALID_ARG, "invalid arguments for norm_bwd_workspace_bytes")
+    return n
+
+
 def norm_bwd_make_plan(kind, M: int, N: int, io_dtype, with_dbeta: bool,
                        groups: int = 0) -> NormBwdPlan:
     code = io_dtype if isinstance(io_dtype, int) else _code(io_dtype, "io")
@@ -246,10 +256,7 @@ def _backward(kind, x, dy, gamma, mean, rstd, eps, wgrad_dtype, dx, dgamma, dbet
     s = _stream(stream, dev)
     with torch.cuda.device(dev):
         if plan is None:
-            # the plan call raises the precise status for unsupported shapes;
-            # the size call covers the automatic plan of either statistics mode
-            need = max(norm_bwd_make_plan(kind, M, N, io, dbeta is not None).workspace_bytes,
-                       norm_bwd_workspace_bytes(kind, M, N, io, dbeta is not None))
+            need = _auto_workspace(kind, M, N, io, dbeta is not None)
             if workspace is None:
                 workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
             wsb = workspace.numel() * workspace.element_size()
@@ -349,9 +356,8 @@ def norm_bwd_ex(kind: str, x: torch.Tensor, dy: torch.Tensor, gamma: torch.Tenso
             if t.dtype != wgrad_dtype or t.numel() != N:
                 raise ValueError(f"{n} must be [N] in wgrad_dtype")
     io = _code(x.dtype, "x")
-    need = norm_bwd_make_plan(kind, M, N, io, dbeta is not None, groups).workspace_bytes
-    if not groups:
-        need = max(need, norm_bwd_workspace_bytes(kind, M, N, io, dbeta is not None))
+    need = (norm_bwd_make_plan(kind, M, N, io, dbeta is not None, groups).workspace_bytes
+            if groups else _auto_workspace(kind, M, N, io, dbeta is not None))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     _gpu(workspace, "workspace")

@@ -181,6 +181,105 @@ int check_vec_alignment(const norm_bwd_plan_t& p, const Buffers& b) {
   return NORM_BWD_OK;
 }
 
+// Launch the column walk (arguments already checked). M = 0 writes zeros, or
+// with `accumulate` launches nothing.
+int launch_colwalk(int kind, const void* x, const void* dy, const float* mean, const float* rstd,
+                   int64_t M, int64_t N, int64_t ldx, int64_t ldy, int io_dtype, int wgrad_dtype,
+                   void* dgamma, void* dbeta, bool accumulate, hipStream_t stream) {
+  if (N == 0 || (accumulate && M == 0)) return NORM_BWD_OK;
+  const int eb = nb::dtype_bytes(io_dtype);
+  const bool vec_ok = M == 0 || (aligned16(x) && aligned16(dy) && ((size_t)N * eb) % 16 == 0 &&
+                                 ((size_t)ldx * eb) % 16 == 0 && ((size_t)ldy * eb) % 16 == 0);
+  const int vec = vec_ok ? 16 / eb : 1;
+  nb::LaunchW w;
+  w.kind = kind;
+  w.nacc = dbeta ? 2 : 1;
+  w.vec_full = vec_ok ? 1 : 0;
+  w.lpr = nb::wgrad_lanes_per_row(N, vec);
+  w.x = x;
+  w.dy = dy;
+  w.mean = kind == NORM_BWD_LAYERNORM ? mean : nullptr;
+  w.rstd = rstd;
+  w.M = M;
+  w.N = N;
+  w.ldx = ldx;
+  w.ldy = ldy;
+  w.dgamma = dgamma;
+  w.dbeta = dbeta;
+  w.out_dtype = wgrad_dtype;
+  w.accumulate = accumulate ? 1 : 0;
+  w.grid = (N + (int64_t)w.lpr * vec - 1) / ((int64_t)w.lpr * vec);
+  w.stream = stream;
+  (void)hipGetLastError();  // clear a stale error so a launch failure is ours
+  hipError_t e;
+  switch (io_dtype) {
+    case NORM_BWD_F32: e = nb::launch_w_f32(w); break;
+    case NORM_BWD_F16: e = nb::launch_w_f16(w); break;
+    default: e = nb::launch_w_bf16(w); break;
+  }
+  if (e != hipSuccess) return hip_error(e, "column-walk launch");
+  return NORM_BWD_OK;
+}
+
+// Workspace of the wide-row path: the recomputed statistics (LayerNorm mean
+// and rstd, RMSNorm rstd) in recompute mode, nothing otherwise.
+size_t rowloop_workspace(int kind, int64_t M, bool recompute) {
+  return recompute ? (size_t)M * 4u * (kind == NORM_BWD_LAYERNORM ? 2u : 1u) : 0;
+}
+
+// Rows too wide for the fused kernels: dx by the row-loop kernel (which also
+// stores the statistics in recompute mode), then the weight gradients by the
+// column walk.
+int run_wide(int kind, const Buffers& b, int64_t M, int64_t N, int io_dtype, int wgrad_dtype,
+             float eps, bool recompute, bool accumulate, hipStream_t stream) {
+  if (N > INT32_MAX) return set_error(NORM_BWD_ERR_UNSUPPORTED, "N too large");
+  const size_t need = rowloop_workspace(kind, M, recompute);
+  int st = check_buffers(kind, M, N, io_dtype, wgrad_dtype, true, true, need, b, recompute);
+  if (st != NORM_BWD_OK) return st;
+  if (N == 0) return NORM_BWD_OK;
+  float* stats = static_cast<float*>(b.ws);
+  float* mean_out = recompute && kind == NORM_BWD_LAYERNORM ? stats : nullptr;
+  float* rstd_out = recompute ? (kind == NORM_BWD_LAYERNORM ? stats + M : stats) : nullptr;
+  if (M > 0) {
+    const int eb = nb::dtype_bytes(io_dtype);
+    nb::LaunchL l;
+    l.kind = kind;
+    l.recompute = recompute ? 1 : 0;
+    l.vec_full = (aligned16(b.x) && aligned16(b.dy) && aligned16(b.gamma) && aligned16(b.dx) &&
+                  (N * eb) % 16 == 0 && (b.ldx * eb) % 16 == 0 && (b.ldy * eb) % 16 == 0 &&
+                  (b.ldo * eb) % 16 == 0)
+                     ? 1
+                     : 0;
+    l.x = b.x;
+    l.dy = b.dy;
+    l.gamma = b.gamma;
+    l.mean = b.mean;
+    l.rstd = b.rstd;
+    l.dx = b.dx;
+    l.mean_out = mean_out;
+    l.rstd_out = rstd_out;
+    l.M = M;
+    l.N = N;
+    l.ldx = b.ldx;
+    l.ldy = b.ldy;
+    l.ldo = b.ldo;
+    l.eps = eps;
+    l.grid = nb::rowloop_grid(M);
+    l.stream = stream;
+    (void)hipGetLastError();  // clear a stale error so a launch failure is ours
+    hipError_t e;
+    switch (io_dtype) {
+      case NORM_BWD_F32: e = nb::launch_l_f32(l); break;
+      case NORM_BWD_F16: e = nb::launch_l_f16(l); break;
+      default: e = nb::launch_l_bf16(l); break;
+    }
+    if (e != hipSuccess) return hip_error(e, "row-loop launch");
+  }
+  return launch_colwalk(kind, b.x, b.dy, recompute ? mean_out : b.mean,
+                        recompute ? rstd_out : b.rstd, M, N, b.ldx, b.ldy, io_dtype, wgrad_dtype,
+                        b.dgamma, b.dbeta, accumulate, stream);
+}
+
 // The whole backward with an automatic or explicit group count: the named
 // entry points and norm_bwd_ex. Row strides of b must be filled in (>= N).
 int run_backward(int kind, Buffers b, int64_t M, int64_t N, int io_dtype, int wgrad_dtype,
@@ -198,6 +297,14 @@ int run_backward(int kind, Buffers b, int64_t M, int64_t N, int io_dtype, int wg
                       (b.ldo * eb) % 16 == 0;
   const bool vec_ok = rows16 && aligned16(b.x) && aligned16(b.dy) && aligned16(b.gamma) &&
                       aligned16(b.dx);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (eb > 0 && N > 0 && !nb::fused_fits(N, io_dtype, b.dbeta ? 1 : 0, vec_ok)) {
+    if (groups != 0)
+      return set_error(NORM_BWD_ERR_UNSUPPORTED, "explicit groups need rows the fused path holds");
+    if (wgrad_dtype != NORM_BWD_F32 && wgrad_dtype != io_dtype)
+      return set_error(NORM_BWD_ERR_UNSUPPORTED, "wgrad_dtype must be NORM_BWD_F32 or io_dtype");
+    return run_wide(kind, b, M, N, io_dtype, wgrad_dtype, eps, recompute, accumulate, s);
+  }
   norm_bwd_plan_t p;
   const char* why = nullptr;
   int st = nb::make_plan(kind, M, N, io_dtype, b.dbeta ? 1 : 0, groups, vec_ok, &p, &why,
@@ -206,7 +313,6 @@ int run_backward(int kind, Buffers b, int64_t M, int64_t N, int io_dtype, int wg
   st = check_buffers(kind, M, N, io_dtype, wgrad_dtype, true, true, p.workspace_bytes, b,
                      recompute);
   if (st != NORM_BWD_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   st = launch_partials(p, b, s, recompute, eps);
   if (st != NORM_BWD_OK) return st;
   return launch_reduce(p.groups, N, wgrad_dtype, b.ws, b.dgamma, b.dbeta, s, accumulate);
@@ -238,8 +344,9 @@ int run_forward(int kind, const void* x, const void* gamma, const void* beta, in
   const bool vec_ok = aligned16(x) && aligned16(gamma) && aligned16(y) && (!beta || aligned16(beta));
   norm_bwd_plan_t g;
   const char* why = nullptr;
-  int st = nb::make_geometry(kind, N, io_dtype, 0, vec_ok, &g, &why);
-  if (st != NORM_BWD_OK) return set_error(st, why);
+  // rows the fused forward cannot hold in registers take the row-loop kernel
+  const bool wide = nb::make_geometry(kind, N, io_dtype, 0, vec_ok, &g, &why) != NORM_BWD_OK;
+  if (wide && N > INT32_MAX) return set_error(NORM_BWD_ERR_UNSUPPORTED, "N too large");
   // y and the statistics must not overlap the inputs or each other
   const size_t mat = (size_t)M * (size_t)N * (size_t)eb, vec = (size_t)N * (size_t)eb;
   const size_t stat = (size_t)M * 4u;
@@ -256,8 +363,8 @@ int run_forward(int kind, const void* x, const void* gamma, const void* beta, in
   }
   nb::LaunchF f;
   f.kind = kind;
-  f.vec_full = g.vec > 1 ? 1 : 0;
-  f.chunks = g.chunks;
+  f.vec_full = wide ? ((vec_ok && ((size_t)N * eb) % 16 == 0) ? 1 : 0) : (g.vec > 1 ? 1 : 0);
+  f.chunks = wide ? 0 : g.chunks;
   f.x = x;
   f.gamma = gamma;
   f.beta = beta;
@@ -267,17 +374,18 @@ int run_forward(int kind, const void* x, const void* gamma, const void* beta, in
   f.M = M;
   f.N = (int)N;
   f.eps = eps;
-  f.S = g.waves_per_row;
-  f.P = g.rows_in_flight;
-  f.threads = g.threads;
-  f.grid = (int)nb::forward_grid(M, g.waves_per_row, g.rows_in_flight);
+  f.S = wide ? 0 : g.waves_per_row;
+  f.P = wide ? 0 : g.rows_in_flight;
+  f.threads = wide ? 0 : g.threads;
+  f.grid = wide ? (int)nb::rowloop_grid(M)
+                : (int)nb::forward_grid(M, g.waves_per_row, g.rows_in_flight);
   f.stream = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so a launch failure is ours
   hipError_t e;
   switch (io_dtype) {
-    case NORM_BWD_F32: e = nb::launch_f_f32(f); break;
-    case NORM_BWD_F16: e = nb::launch_f_f16(f); break;
-    default: e = nb::launch_f_bf16(f); break;
+    case NORM_BWD_F32: e = wide ? nb::launch_fl_f32(f) : nb::launch_f_f32(f); break;
+    case NORM_BWD_F16: e = wide ? nb::launch_fl_f16(f) : nb::launch_f_f16(f); break;
+    default: e = wide ? nb::launch_fl_bf16(f) : nb::launch_f_bf16(f); break;
   }
   if (e != hipSuccess) return hip_error(e, "forward launch");
   return NORM_BWD_OK;
@@ -316,13 +424,23 @@ int norm_bwd_rmsnorm(const void* x, const void* dy, const void* gamma, const flo
 }
 
 size_t norm_bwd_workspace_bytes(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta) {
-  // enough for the automatic plan of either statistics mode
-  norm_bwd_plan_t p, q;
-  if (nb::make_plan(kind, M, N, io_dtype, with_dbeta ? 1 : 0, 0, true, &p, nullptr) != NORM_BWD_OK ||
-      nb::make_plan(kind, M, N, io_dtype, with_dbeta ? 1 : 0, 0, true, &q, nullptr, true) !=
-          NORM_BWD_OK)
+  // enough for the automatic plan of either statistics mode, on the fused
+  // path or (rows too wide for it, or unaligned) the row-loop path
+  if ((kind != NORM_BWD_LAYERNORM && kind != NORM_BWD_RMSNORM) || nb::dtype_bytes(io_dtype) == 0 ||
+      M < 0 || N < 0 || N > INT32_MAX)
     return (size_t)-1;
-  return p.workspace_bytes > q.workspace_bytes ? p.workspace_bytes : q.workspace_bytes;
+  size_t need = rowloop_workspace(kind, M, true);
+  if (nb::fused_fits(N, io_dtype, with_dbeta ? 1 : 0, true)) {
+    norm_bwd_plan_t p, q;
+    if (nb::make_plan(kind, M, N, io_dtype, with_dbeta ? 1 : 0, 0, true, &p, nullptr) !=
+            NORM_BWD_OK ||
+        nb::make_plan(kind, M, N, io_dtype, with_dbeta ? 1 : 0, 0, true, &q, nullptr, true) !=
+            NORM_BWD_OK)
+      return (size_t)-1;
+    if (p.workspace_bytes > need) need = p.workspace_bytes;
+    if (q.workspace_bytes > need) need = q.workspace_bytes;
+  }
+  return need;
 }
 
 int norm_bwd_make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,
@@ -391,37 +509,8 @@ int norm_bwd_wgrad(int kind, const void* x, const void* dy, const float* mean, c
         return set_error(NORM_BWD_ERR_INVALID_ARG, "an output overlaps an input");
   if (nb::ranges_overlap(dgamma, vec_out, dbeta, vec_out))
     return set_error(NORM_BWD_ERR_INVALID_ARG, "dgamma and dbeta overlap");
-  const bool accumulate = (flags & NORM_BWD_ACCUMULATE) != 0;
-  if (accumulate && M == 0) return NORM_BWD_OK;  // adds the empty sum: nothing
-  const bool vec_ok = M == 0 || (aligned16(x) && aligned16(dy) && ((size_t)N * eb) % 16 == 0);
-  nb::LaunchW w;
-  w.kind = kind;
-  w.nacc = dbeta ? 2 : 1;
-  w.vec_full = vec_ok ? 1 : 0;
-  const int vec = vec_ok ? 16 / eb : 1;
-  w.lpr = nb::wgrad_lanes_per_row(N, vec);
-  w.x = x;
-  w.dy = dy;
-  w.mean = kind == NORM_BWD_LAYERNORM ? mean : nullptr;
-  w.rstd = rstd;
-  w.M = M;
-  w.N = N;
-  w.ldx = w.ldy = N;
-  w.dgamma = dgamma;
-  w.dbeta = dbeta;
-  w.out_dtype = wgrad_dtype;
-  w.accumulate = accumulate ? 1 : 0;
-  w.grid = (N + (int64_t)w.lpr * vec - 1) / ((int64_t)w.lpr * vec);
-  w.stream = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();  // clear a stale error so a launch failure is ours
-  hipError_t e;
-  switch (io_dtype) {
-    case NORM_BWD_F32: e = nb::launch_w_f32(w); break;
-    case NORM_BWD_F16: e = nb::launch_w_f16(w); break;
-    default: e = nb::launch_w_bf16(w); break;
-  }
-  if (e != hipSuccess) return hip_error(e, "column-walk launch");
-  return NORM_BWD_OK;
+  return launch_colwalk(kind, x, dy, mean, rstd, M, N, N, N, io_dtype, wgrad_dtype, dgamma, dbeta,
+                        (flags & NORM_BWD_ACCUMULATE) != 0, static_cast<hipStream_t>(stream));
 }
 
 int norm_bwd_execute(const norm_bwd_plan_t* plan, const void* x, const void* dy,

@@ -64,6 +64,31 @@ struct LaunchW {
   hipStream_t stream;
 };
 
+struct LaunchL {  // dx for wide rows (row loop)
+  int kind;
+  int recompute;
+  int vec_full;
+  const void* x;
+  const void* dy;
+  const void* gamma;
+  const float* mean;
+  const float* rstd;
+  void* dx;
+  float* mean_out;  // recompute mode: the statistics, for the weight-gradient pass
+  float* rstd_out;
+  int64_t M, N, ldx, ldy, ldo;
+  float eps;
+  int64_t grid;
+  hipStream_t stream;
+};
+
+hipError_t launch_fl_f32(const LaunchF& f);  // forward for wide rows (row loop)
+hipError_t launch_fl_f16(const LaunchF& f);
+hipError_t launch_fl_bf16(const LaunchF& f);
+hipError_t launch_l_f32(const LaunchL& l);
+hipError_t launch_l_f16(const LaunchL& l);
+hipError_t launch_l_bf16(const LaunchL& l);
+
 hipError_t launch_w_f32(const LaunchW& w);
 hipError_t launch_w_f16(const LaunchW& w);
 hipError_t launch_w_bf16(const LaunchW& w);

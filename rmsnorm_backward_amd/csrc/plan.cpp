@@ -114,6 +114,15 @@ int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok
   return NORM_BWD_OK;
 }
 
+bool fused_fits(int64_t N, int io_dtype, int with_dbeta, bool vec_ok16) {
+  norm_bwd_plan_t g;
+  const char* why = nullptr;
+  return make_geometry(NORM_BWD_RMSNORM, N, io_dtype, with_dbeta, vec_ok16, &g, &why) ==
+         NORM_BWD_OK;
+}
+
+int64_t rowloop_grid(int64_t M) { return M < 512 ? (M < 1 ? 1 : M) : 512; }
+
 int64_t forward_grid(int64_t M, int S, int P) {
   if (M <= 0) return 0;
   int64_t g = kForwardTargetWaves / (S * P);

@@ -26,6 +26,14 @@ int kernel_a_max_threads(int lane_elems);
 int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok16,
                   norm_bwd_plan_t* plan, const char** why);
 
+// Whether the fused kernels (rows held in registers) cover rows of N elements
+// of io_dtype; wider rows take the row-loop path.
+bool fused_fits(int64_t N, int io_dtype, int with_dbeta, bool vec_ok16);
+
+// Workgroups of the row-loop kernel for M rows: one 16-wave workgroup per row,
+// at most two per compute unit.
+int64_t rowloop_grid(int64_t M);
+
 // Workgroups of the forward kernel for M rows with S waves per row and P rows
 // in flight: enough for about 4096 waves (16 per compute unit), at most one
 // sweep of rows.

@@ -122,17 +122,26 @@ def test_forward_edge_shapes(nb, kind, dt, M, N):
     check(w, inp["x"], inp["gamma"], beta, got)
 
 
-def test_forward_limits(nb):
-    x = torch.zeros(2, 16385, device="cuda")
-    g = torch.ones(16385, device="cuda")
-    with pytest.raises(nb.NormBwdError) as e:
-        nb.norm_fwd_rmsnorm(x, g)
-    assert e.value.status == nb.ERR_UNSUPPORTED
-    xh = torch.zeros(2, 32769, dtype=torch.bfloat16, device="cuda")
-    gh = torch.ones(32769, dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(nb.NormBwdError) as e:
-        nb.norm_fwd_layernorm(xh, gh, None)
-    assert e.value.status == nb.ERR_UNSUPPORTED
+WIDE_FWD = [(kind, dt, M, N)
+            for kind in ("layernorm", "rmsnorm")
+            for dt, M, N in ((torch.float32, 3, 16385), (torch.float32, 7, 40000),
+                             (torch.bfloat16, 5, 32776), (torch.float16, 2, 100003),
+                             (torch.bfloat16, 300, 65536), (torch.float16, 11, 9001))]
+
+
+@pytest.mark.parametrize("kind,dt,M,N", WIDE_FWD, ids=lambda v: str(v).replace("torch.", ""))
+def test_forward_wide_rows(nb, kind, dt, M, N):
+    """Rows wider than the fused forward holds (or unaligned beyond 8192) take
+    the row-loop forward; same results to the same tolerance."""
+    base = W.LN_F32_128x512 if kind == "layernorm" else W.RMS_F32_128x512
+    w = W.scaled(base, M=M, N=N, io_dtype=dt, seed=40 + M + N)
+    inp = W.make_inputs(w)
+    beta = _beta(w, inp)
+    got = gpu_forward(nb, w, inp["x"], inp["gamma"], beta)
+    check(w, inp["x"], inp["gamma"], beta, got)
+    if kind == "layernorm":
+        got0 = gpu_forward(nb, w, inp["x"], inp["gamma"], None)
+        check(w, inp["x"], inp["gamma"], None, got0)
 
 
 def test_forward_constant_rows_and_zero_rows(nb):

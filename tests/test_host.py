@@ -115,7 +115,9 @@ def _auto_groups(nb, kind, M, N, dt, recompute=False):
 def test_workspace_bytes_rule(nb, kind, M, N, dt, db):
     got = nb.norm_bwd_workspace_bytes(kind, M, N, dt, db)
     groups = max(_auto_groups(nb, kind, M, N, dt), _auto_groups(nb, kind, M, N, dt, True))
-    assert got == (2 if db else 1) * groups * N * 4
+    # the wide-row path's recompute statistics (4 or 8 bytes per row) also fit
+    wide = M * 4 * (2 if kind == "layernorm" else 1)
+    assert got == max((2 if db else 1) * groups * N * 4, wide)
     plan = nb.norm_bwd_make_plan(kind, M, N, dt, db)   # the saved-statistics plan
     assert plan.workspace_bytes <= got
     assert plan.workspace_bytes == (2 if db else 1) * _auto_groups(nb, kind, M, N, dt) * N * 4
@@ -127,7 +129,10 @@ def test_workspace_bytes_rejects_bad_arguments(nb):
     assert lib.norm_bwd_workspace_bytes(7, 10, 10, 0, 0) == bad
     assert lib.norm_bwd_workspace_bytes(0, 10, 10, 9, 0) == bad
     assert lib.norm_bwd_workspace_bytes(0, -1, 10, 0, 0) == bad
-    assert lib.norm_bwd_workspace_bytes(0, 10, 40000, 2, 0) == bad
+    assert lib.norm_bwd_workspace_bytes(0, 10, 1 << 31, 2, 0) == bad
+    # rows wider than the fused path: the wide-row path's statistics only
+    assert lib.norm_bwd_workspace_bytes(0, 10, 40000, 2, 1) == 10 * 8
+    assert lib.norm_bwd_workspace_bytes(1, 10, 40000, 2, 0) == 10 * 4
 
 
 GEOMS = [(kind, dt, M, N, db, g)
@@ -229,7 +234,7 @@ def _ln(nb, **over):
     (dict(rstd=None, x=None), 1), (dict(rstd=None, eps=-1.0), 1),   # recompute mode checks too
     (dict(M=-1), 1), (dict(N=-3), 1), (dict(eps=-1.0), 1), (dict(eps=float("nan")), 1),
     (dict(eps=float("inf")), 1),
-    (dict(io=5), 2), (dict(wg=1), 2), (dict(wg=7), 2), (dict(N=40000), 2),
+    (dict(io=5), 2), (dict(wg=1), 2), (dict(wg=7), 2), (dict(N=1 << 31), 2),
     (dict(ws=None), 3), (dict(wsb=16), 3),
     (dict(ws=ctypes.c_void_p(B + 6 * (1 << 30) + 8)), 1),
     (dict(dx=_addr(0)), 1),                                  # dx aliases x
@@ -326,7 +331,7 @@ def _fwd(nb, kind, **over):
 @pytest.mark.parametrize("over,status", [
     (dict(x=None), 1), (dict(gamma=None), 1), (dict(y=None), 1),
     (dict(M=-1), 1), (dict(N=-1), 1), (dict(eps=-1.0), 1), (dict(eps=float("nan")), 1),
-    (dict(io=3), 2), (dict(N=40000), 2), (dict(io=0, N=20000), 2),
+    (dict(io=3), 2), (dict(N=1 << 31), 2),
     (dict(y=_addr(0)), 1),                                    # y aliases x
     (dict(rstd=ctypes.c_void_p(B + 3 * (1 << 30) + 256)), 1),  # rstd inside y
     (dict(rstd=_addr(1)), 1),                                 # rstd aliases gamma
