@@ -118,6 +118,57 @@ def time_loop(torch, fn, steps, stream):
     return start.elapsed_time(end) / steps  # ms per call
 
 
+def measure_wide(torch, nb, W, lib, dev, stream, args):
+    """The wide-row path (rows beyond the fused limits): 1024 x 65536 bf16
+    RMSNorm, backward step (row-loop dx + column walk) and forward. Bytes are
+    the same algorithmic count as the fused path's; the row loop reads each
+    row twice and the column walk once more, so traffic exceeds them."""
+    w = W.scaled(W.HEADLINE, M=1024, N=65536, name="rmsnorm_bf16_1024x65536")
+    inp = W.make_inputs(w)
+    sets = []
+    for i in range(3):
+        s = {k: inp[k].to(dev) for k in ("x", "dy", "gamma")}
+        s["y"] = torch.empty_like(s["x"])
+        s["rstd"] = torch.empty(w.M, device=dev)
+        s["dx"] = torch.empty_like(s["x"])
+        sets.append(s)
+    dg = torch.empty(w.N, device=dev)
+    io = nb._DTYPE_CODE[w.io_dtype]
+    P = ctypes.c_void_p
+    sh = P(stream.cuda_stream)
+    pt = lambda t: P(t.data_ptr())  # noqa: E731
+    for s in sets:
+        lib.norm_fwd_rmsnorm(pt(s["x"]), pt(s["gamma"]), w.M, w.N, io, w.eps, pt(s["y"]),
+                             pt(s["rstd"]), sh)
+
+    def fwd(i):
+        s = sets[i % 3]
+        if lib.norm_fwd_rmsnorm(pt(s["x"]), pt(s["gamma"]), w.M, w.N, io, w.eps, pt(s["y"]),
+                                pt(s["rstd"]), sh):
+            raise RuntimeError(nb.norm_bwd_last_error())
+
+    def bwd(i):
+        s = sets[i % 3]
+        if lib.norm_bwd_rmsnorm(pt(s["x"]), pt(s["dy"]), pt(s["gamma"]), pt(s["rstd"]), w.M,
+                                w.N, io, 0, w.eps, pt(s["dx"]), pt(dg), None, None, 0, sh):
+            raise RuntimeError(nb.norm_bwd_last_error())
+
+    steps = max(args.steps // 5, 20)
+    for i in range(20):
+        bwd(i)
+        fwd(i)
+    ms_b = time_loop(torch, bwd, steps, stream)
+    ms_f = time_loop(torch, fwd, steps, stream)
+    b_bytes = w.algorithmic_bytes()
+    f_bytes = forward_bytes(w, False)
+    return {"workload": w.name, "backward_us": round(ms_b * 1e3, 2),
+            "backward_GBps": round(b_bytes / (ms_b * 1e-3) / 1e9, 1),
+            "backward_pct_of_peak": round(100 * b_bytes / (ms_b * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+            "forward_us": round(ms_f * 1e3, 2),
+            "forward_GBps": round(f_bytes / (ms_f * 1e-3) / 1e9, 1),
+            "forward_pct_of_peak": round(100 * f_bytes / (ms_f * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2)}
+
+
 def cpu_baseline(w, inp):
     """The fp64 oracle (plain C, one thread) on the same workload, timed on
     this host. Inputs are widened to fp64 before the clock starts."""
@@ -357,6 +408,8 @@ def main(argv=None) -> int:
     copy_gbps = 2 * cp_bytes / (ms_cp * 1e-3) / 1e9
     del src, dsts, srcs
 
+    wide = measure_wide(torch, nb, W, lib, dev, stream, args)
+
     alg = w.algorithmic_bytes()
     value = alg / (ms * 1e-3) / 1e9
     a_bytes = kernel_a_bytes(w)
@@ -416,6 +469,7 @@ def main(argv=None) -> int:
                 "GBps": round(cw_bytes / (ms_cw * 1e-3) / 1e9, 2),
                 "pct_of_peak": round(100 * cw_bytes / (ms_cw * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
             },
+            "wide_rows": wide,
             "plan": {k: v for k, v in plan.as_dict().items()
                      if k in ("groups", "rows_per_group", "vec", "chunks", "waves_per_row",
                               "rows_in_flight", "threads", "grid")},
