@@ -1,5 +1,7 @@
 // api.cpp -- the C ABI (include/norm_bwd.h): argument checks, planning, and
-// the two launches on the caller's stream. Nothing here allocates memory.
+// the launches on the caller's stream (kernel A then kernel B; for rows too
+// wide for them the row-loop kernel then the column walk; the forward).
+// Every check happens before the first launch. Nothing here allocates memory.
 #include <hip/hip_runtime_api.h>
 #include <math.h>
 #include <stdio.h>

@@ -1,5 +1,7 @@
-// nb_launch_a.hpp -- maps a validated plan onto one kernel A instantiation.
-// Included by exactly one translation unit per I/O element type.
+// nb_launch_a.hpp -- maps a validated plan onto one kernel A instantiation,
+// and a forward launch onto one forward-kernel instantiation. Included by the
+// per-element-type translation units (kernel A with saved statistics and the
+// forward in kernels_<type>.hip, recompute mode in kernels_<type>_recompute.hip).
 #pragma once
 
 #include "nb_device.hpp"

@@ -1,8 +1,9 @@
 // plan.cpp -- host-side planning and validation (no HIP calls).
 //
 // The group count G is what fixes the summation order of dgamma/dbeta, so it
-// is a function of (kind, M, N, io_dtype) alone and never of the device's
-// compute-unit count: results are the same on any partitioning of the GPU.
+// is a function of (kind, M, N, io_dtype, statistics mode) alone and never of
+// the device's compute-unit count: results are the same on any partitioning
+// of the GPU.
 #include "plan.hpp"
 
 #include <string.h>
