@@ -5,8 +5,8 @@
 // "Norm backward in Triton -- the dγ/dβ reduction", "The gradients" for
 // RMSNorm):
 //   LayerNorm: mean = sum(x)/N, var = sum((x - mean)^2)/N (biased, two passes
-//              over the registers), rstd = 1/sqrt(var + eps),
-//              y = gamma * (x - mean) * rstd + beta
+//              over the registers, the two exchanges pipelined across rows),
+//              rstd = 1/sqrt(var + eps), y = gamma * (x - mean) * rstd + beta
 //   RMSNorm:   rstd = 1/sqrt(sum(x^2)/N + eps), y = gamma * x * rstd (+ beta)
 // and mean/rstd are stored as fp32 for the backward.
 //
@@ -81,22 +81,12 @@ void norm_fwd_kernel(const void* __restrict__ xv, const void* __restrict__ gv,
   };
 
   int phase = 0;
+  // RMSNorm: one exchange per row (sum of x^2), then y
   auto process = [&](XBuf<Tg, VEC, C>& b, int64_t r) {
     const bool active = r < M;
-    float unused = 0.0f, s1 = 0.0f;
-    float mu = 0.0f;
-    if (KIND == kLayerNorm) {
-      if (active) {
-#pragma unroll
-        for (int c = 0; c < C; ++c)
-          if (col0 + c * cstride < N)
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) s1 += b.x[c].get(v);
-      }
-      row_sum2<false>(unused, s1, red, phase, lane, wave, S, p);
-      mu = s1 * inv_n;
-    }
-    float s2 = 0.0f;  // sum((x - mean)^2), RMSNorm: sum(x^2)
+    float unused = 0.0f;
+    const float mu = 0.0f;
+    float s2 = 0.0f;  // sum(x^2)
     if (active) {
 #pragma unroll
       for (int c = 0; c < C; ++c)
@@ -125,25 +115,100 @@ void norm_fwd_kernel(const void* __restrict__ xv, const void* __restrict__ gv,
           out.store_stream(y + (rb + col) * EB);
         }
       }
-      // one lane stores the row's statistics (a predicated vector store)
-      if (s == 0 && lane == 0) {
-        if (mean_out && KIND == kLayerNorm) mean_out[r] = mu;
-        if (rstd_out) rstd_out[r] = rs;
-      }
+      // one lane stores the row's statistic (a predicated vector store)
+      if (s == 0 && lane == 0 && rstd_out) rstd_out[r] = rs;
     }
   };
 
-  constexpr int D = prefetch_depth<Tg, VEC, C>();
-  XBuf<Tg, VEC, C> buf[D];
+  if constexpr (KIND == kLayerNorm) {
+    // LayerNorm: the two exchanges a row needs are pipelined across rows, so
+    // a row costs one barrier. Step k exchanges row k's sum of squared
+    // deviations together with row k+1's sum of x; the prologue exchanges
+    // the first row's sum of x alone. Each sum keeps its own order, so mean
+    // and rstd are those of the unpipelined two-pass form. The ring holds one
+    // more row, as row k+1 is read one step earlier.
+    constexpr int D = prefetch_depth<Tg, VEC, C>() + 1;
+    XBuf<Tg, VEC, C> buf[D];
+    auto xsum = [&](XBuf<Tg, VEC, C>& b, bool active) {
+      float sx = 0.0f;
+      if (active) {
 #pragma unroll
-  for (int k = 0; k < D - 1; ++k)
-    if (k < iters) fetch(buf[k], row_of(k));
-  for (int it = 0; it < iters; it += D) {
+        for (int c = 0; c < C; ++c)
+          if (col0 + c * cstride < N)
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const int k = it + d;
-      if (k + D - 1 < iters) fetch(buf[(d + D - 1) % D], row_of(k + D - 1));
-      if (k < iters) process(buf[d], row_of(k));
+            for (int v = 0; v < VEC; ++v) sx += b.x[c].get(v);
+      }
+      return sx;
+    };
+#pragma unroll
+    for (int k = 0; k < D - 1; ++k)
+      if (k < iters) fetch(buf[k], row_of(k));
+    float unused = 0.0f;
+    float sx0 = iters > 0 ? xsum(buf[0], row_of(0) < M) : 0.0f;
+    row_sum2<false>(unused, sx0, red, phase, lane, wave, S, p);
+    float mu_next = sx0 * inv_n;
+    for (int it = 0; it < iters; it += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const int k = it + d;
+        if (k + D - 1 < iters) fetch(buf[(d + D - 1) % D], row_of(k + D - 1));
+        if (k < iters) {
+          XBuf<Tg, VEC, C>& b = buf[d];
+          const int64_t r = row_of(k);
+          const bool active = r < M;
+          const float mu = mu_next;
+          float s2 = 0.0f;
+          if (active) {
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+              if (col0 + c * cstride < N)
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) {
+                  const float xc = b.x[c].get(v) - mu;
+                  s2 = __builtin_fmaf(xc, xc, s2);
+                }
+          }
+          float sx1 = k + 1 < iters ? xsum(buf[(d + 1) % D], row_of(k + 1) < M) : 0.0f;
+          keep_packed(b.x);
+          row_sum2<true>(sx1, s2, red, phase, lane, wave, S, p);
+          mu_next = sx1 * inv_n;
+          if (active) {
+            const float rs = 1.0f / __builtin_sqrtf(__builtin_fmaf(s2, inv_n, eps));
+            const int64_t rb = r * (int64_t)N;
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+              const int col = col0 + c * cstride;
+              if (col < N) {
+                float o[VEC];
+#pragma unroll
+                for (int v = 0; v < VEC; ++v)
+                  o[v] = __builtin_fmaf((b.x[c].get(v) - mu) * rs, gam[c][v], bet[c][v]);
+                PK out;
+                out.set(o);
+                out.store_stream(y + (rb + col) * EB);
+              }
+            }
+            if (s == 0 && lane == 0) {
+              if (mean_out) mean_out[r] = mu;
+              if (rstd_out) rstd_out[r] = rs;
+            }
+          }
+        }
+      }
+    }
+  } else {
+    constexpr int D = prefetch_depth<Tg, VEC, C>();
+    XBuf<Tg, VEC, C> buf[D];
+#pragma unroll
+    for (int k = 0; k < D - 1; ++k)
+      if (k < iters) fetch(buf[k], row_of(k));
+    for (int it = 0; it < iters; it += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const int k = it + d;
+        if (k + D - 1 < iters) fetch(buf[(d + D - 1) % D], row_of(k + D - 1));
+        if (k < iters) process(buf[d], row_of(k));
+      }
     }
   }
 }
