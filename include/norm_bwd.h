@@ -136,10 +136,14 @@ int norm_bwd_rmsnorm(const void *x, const void *dy, const void *gamma,
                      void *stream);
 
 /*
- * Workspace size in bytes for the automatic plan of (kind, M, N, io_dtype):
- * groups * N * 4 bytes per gradient vector (two when with_dbeta != 0).
- * Returns 0 for M = 0 or N = 0, and (size_t)-1 for invalid arguments.
- * Host-only; launches nothing.
+ * Workspace size in bytes that norm_bwd_layernorm / norm_bwd_rmsnorm (and
+ * norm_bwd_ex with automatic groups) need for (kind, M, N, io_dtype), in
+ * either statistics mode: on the fused path the larger of the two automatic
+ * plans' groups * N * 4 bytes per gradient vector (two vectors when
+ * with_dbeta != 0), and never less than the wide-row path's recomputed
+ * statistics (M * 4 bytes, LayerNorm M * 8). Returns (size_t)-1 for invalid
+ * arguments, including M * N * 4 above 2^62 (which every entry point
+ * rejects). Host-only; launches nothing.
  */
 size_t norm_bwd_workspace_bytes(int kind, int64_t M, int64_t N, int io_dtype,
                                 int with_dbeta);
@@ -298,7 +302,8 @@ int norm_bwd_execute_partials(const norm_bwd_plan_t *plan, const void *x,
  * the second plane when dbeta != NULL), summed in one fixed order that
  * depends only on `groups`, rounded to wgrad_dtype. groups = 0 writes zeros.
  * The workspace holds fp32 [with_dbeta ? 2 : 1][groups][N] as kernel A
- * writes it.
+ * writes it. groups * N * 8 above 2^62 is NORM_BWD_ERR_INVALID_ARG; a
+ * workspace shorter than the partials is NORM_BWD_ERR_WORKSPACE.
  */
 int norm_bwd_reduce_partials(int64_t groups, int64_t N, int wgrad_dtype,
                              const void *workspace, size_t workspace_bytes,

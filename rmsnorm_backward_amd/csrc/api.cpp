@@ -429,7 +429,8 @@ size_t norm_bwd_workspace_bytes(int kind, int64_t M, int64_t N, int io_dtype, in
   // enough for the automatic plan of either statistics mode, on the fused
   // path or (rows too wide for it, or unaligned) the row-loop path
   if ((kind != NORM_BWD_LAYERNORM && kind != NORM_BWD_RMSNORM) || nb::dtype_bytes(io_dtype) == 0 ||
-      M < 0 || N < 0 || N > INT32_MAX)
+      M < 0 || N < 0 || N > INT32_MAX ||
+      (N > 0 && M > (int64_t)(((uint64_t)1 << 62) / (uint64_t)N / 4u)))
     return (size_t)-1;
   size_t need = rowloop_workspace(kind, M, true);
   if (nb::fused_fits(N, io_dtype, with_dbeta ? 1 : 0, true)) {
@@ -555,6 +556,9 @@ int norm_bwd_reduce_partials(int64_t groups, int64_t N, int wgrad_dtype, const v
                              size_t workspace_bytes, void* dgamma, void* dbeta, void* stream) {
   if (groups < 0 || N < 0) return set_error(NORM_BWD_ERR_INVALID_ARG, "groups and N must be >= 0");
   if (N > INT32_MAX) return set_error(NORM_BWD_ERR_UNSUPPORTED, "N too large");
+  // the partials' size below must not wrap around
+  if (N > 0 && groups > (int64_t)(((uint64_t)1 << 62) / (uint64_t)N / 8u))
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "groups * N too large");
   const size_t need = (size_t)(dbeta ? 2 : 1) * (size_t)groups * (size_t)N * 4u;
   Buffers b{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dgamma, dbeta,
             const_cast<void*>(workspace), workspace_bytes};

@@ -130,6 +130,9 @@ def test_workspace_bytes_rejects_bad_arguments(nb):
     assert lib.norm_bwd_workspace_bytes(0, 10, 10, 9, 0) == bad
     assert lib.norm_bwd_workspace_bytes(0, -1, 10, 0, 0) == bad
     assert lib.norm_bwd_workspace_bytes(0, 10, 1 << 31, 2, 0) == bad
+    # M * N beyond what the entry points accept (and M * 8 would wrap)
+    assert lib.norm_bwd_workspace_bytes(0, 1 << 62, 1, 0, 0) == bad
+    assert lib.norm_bwd_workspace_bytes(1, 1 << 40, 1 << 21, 2, 0) == bad
     # rows wider than the fused path: the wide-row path's statistics only
     assert lib.norm_bwd_workspace_bytes(0, 10, 40000, 2, 1) == 10 * 8
     assert lib.norm_bwd_workspace_bytes(1, 10, 40000, 2, 0) == 10 * 4
@@ -311,6 +314,10 @@ def test_reduce_and_probe_reject(nb):
     assert lib.norm_bwd_reduce_partials(4, 8, 0, _addr(0), 1 << 20, None, None, None) == 1
     assert lib.norm_bwd_reduce_partials(4, 8, 5, _addr(0), 1 << 20, _addr(1), None, None) == 2
     assert lib.norm_bwd_reduce_partials(4, 8, 1, _addr(0), 16, _addr(1), None, None) == 3
+    # groups * N whose byte count would wrap around to a small size
+    assert lib.norm_bwd_reduce_partials(1 << 61, 8, 0, _addr(0), 1 << 20, _addr(1), None, None) == 1
+    assert lib.norm_bwd_reduce_partials(1 << 59, 1 << 4, 0, _addr(0), 0, _addr(1), _addr(2),
+                                        None) == 1
     assert lib.norm_bwd_probe_copy(_addr(0), _addr(1), 17, None) == 1
     assert lib.norm_bwd_probe_copy(_addr(0), ctypes.c_void_p(B + 8), 1024, None) == 1
 
