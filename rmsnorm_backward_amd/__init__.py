@@ -37,6 +37,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 F32, F16, BF16 = 0, 1, 2
 LAYERNORM, RMSNORM = 0, 1
 _DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+_CODE_DTYPE = {v: k for k, v in _DTYPE_CODE.items()}
 _KIND_CODE = {"layernorm": LAYERNORM, "rmsnorm": RMSNORM, LAYERNORM: LAYERNORM, RMSNORM: RMSNORM}
 
 
@@ -172,6 +173,21 @@ def _gpu(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _tensor(t: torch.Tensor, name: str, dev: torch.device, dtype: Optional[torch.dtype] = None,
+            numel: Optional[int] = None, contiguous: bool = True):
+    """Check a tensor the library reads or writes through a raw pointer: on
+    x's GPU, contiguous (unless the entry point takes a row stride), and of
+    the dtype and element count the kernels assume, so no kernel can read or
+    write past it."""
+    (_gpu if contiguous else _gpu_any)(t, name)
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, x on {dev}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements (got {t.numel()})")
+
+
 def _addr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
@@ -223,8 +239,8 @@ def norm_bwd_make_plan(kind, M: int, N: int, io_dtype, with_dbeta: bool,
 def _backward(kind, x, dy, gamma, mean, rstd, eps, wgrad_dtype, dx, dgamma, dbeta,
               with_dbeta, workspace, stream, plan: Optional[NormBwdPlan]):
     lib = load_library()
-    for t, n in ((x, "x"), (dy, "dy"), (gamma, "gamma")):
-        _gpu(t, n)
+    _gpu(x, "x")
+    dev = x.device
     # rstd None (LayerNorm: mean and rstd None) selects the recompute mode
     recompute = rstd is None
     if kind == LAYERNORM and (mean is None) != recompute:
@@ -233,26 +249,31 @@ def _backward(kind, x, dy, gamma, mean, rstd, eps, wgrad_dtype, dx, dgamma, dbet
         raise ValueError("an explicit plan needs the saved statistics")
     M, N = _rows(x)
     io = _code(x.dtype, "x")
-    if dy.dtype != x.dtype or gamma.dtype != x.dtype:
-        raise ValueError("x, dy and gamma must share one dtype")
-    if dy.shape != x.shape or gamma.numel() != N:
-        raise ValueError("shape mismatch: dy like x, gamma [N]")
+    if plan is not None and (plan.M, plan.N, plan.io_dtype) != (M, N, io):
+        raise ValueError(f"the plan is for {plan.M}x{plan.N} of dtype code {plan.io_dtype}, "
+                         f"x is {M}x{N} of dtype code {io}")
+    if not isinstance(dy, torch.Tensor) or dy.shape != x.shape:
+        raise ValueError("dy must have x's shape")
+    _tensor(dy, "dy", dev, x.dtype)
+    _tensor(gamma, "gamma", dev, x.dtype, N)
     for t, n in ((rstd, "rstd"), (mean if kind == LAYERNORM else None, "mean")):
         if t is not None:
-            _gpu(t, n)
-            if t.dtype != torch.float32 or t.numel() != M:
-                raise ValueError("mean and rstd must be float32 [M]")
-    wgrad_dtype = wgrad_dtype or torch.float32
+            _tensor(t, n, dev, torch.float32, M)
+    # dgamma/dbeta are written in wgrad_dtype: by default that of a given dgamma
+    wgrad_dtype = wgrad_dtype or (dgamma.dtype if dgamma is not None else torch.float32)
     wcode = _code(wgrad_dtype, "wgrad")
-    dev = x.device
     if dx is None:
         dx = torch.empty_like(x)
     if dgamma is None:
         dgamma = torch.empty(N, dtype=wgrad_dtype, device=dev)
     if with_dbeta and dbeta is None:
         dbeta = torch.empty(N, dtype=wgrad_dtype, device=dev)
-    for t, n in ((dx, "dx"), (dgamma, "dgamma")) + (((dbeta, "dbeta"),) if dbeta is not None else ()):
-        _gpu(t, n)
+    _tensor(dx, "dx", dev, x.dtype, M * N)
+    _tensor(dgamma, "dgamma", dev, wgrad_dtype, N)
+    if dbeta is not None:
+        _tensor(dbeta, "dbeta", dev, wgrad_dtype, N)
+    if workspace is not None:
+        _tensor(workspace, "workspace", dev)
     s = _stream(stream, dev)
     with torch.cuda.device(dev):
         if plan is None:
@@ -322,45 +343,41 @@ def norm_bwd_ex(kind: str, x: torch.Tensor, dy: torch.Tensor, gamma: torch.Tenso
     lib = load_library()
     code = kind = _KIND_CODE[kind]
     M, N, ldx = _rows2d(x, "x")
+    dev = x.device
     M2, N2, lddy = _rows2d(dy, "dy")
-    _gpu(gamma, "gamma")
-    if (M2, N2) != (M, N) or gamma.numel() != N:
-        raise ValueError("dy must match x; gamma must have N elements")
-    if dy.dtype != x.dtype or gamma.dtype != x.dtype:
-        raise ValueError("x, dy and gamma must share one dtype")
+    if (M2, N2) != (M, N):
+        raise ValueError("dy must match x")
+    _tensor(dy, "dy", dev, x.dtype, contiguous=False)
+    _tensor(gamma, "gamma", dev, x.dtype, N)
     if kind == RMSNORM:
         mean = None
     for t, n in ((mean, "mean"), (rstd, "rstd")):
         if t is not None:
-            _gpu(t, n)
-            if t.dtype != torch.float32 or t.numel() != M:
-                raise ValueError("mean and rstd must be float32 [M]")
+            _tensor(t, n, dev, torch.float32, M)
     if with_dbeta is None:
         with_dbeta = dbeta is not None or (kind == LAYERNORM and not accumulate)
-    dev = x.device
     if accumulate and (dgamma is None or (with_dbeta and dbeta is None)):
         raise ValueError("accumulate=True needs the dgamma (and dbeta) to add into")
     wgrad_dtype = wgrad_dtype or (dgamma.dtype if dgamma is not None else torch.float32)
     if dx is None:
         dx = torch.empty((M, N), dtype=x.dtype, device=dev)
     M3, N3, lddx = _rows2d(dx, "dx")
-    if (M3, N3) != (M, N) or dx.dtype != x.dtype:
-        raise ValueError("dx must be [M, N] in x's dtype")
+    if (M3, N3) != (M, N):
+        raise ValueError("dx must be [M, N]")
+    _tensor(dx, "dx", dev, x.dtype, contiguous=False)
     if dgamma is None:
         dgamma = torch.empty(N, dtype=wgrad_dtype, device=dev)
     if with_dbeta and dbeta is None:
         dbeta = torch.empty(N, dtype=wgrad_dtype, device=dev)
     for t, n in ((dgamma, "dgamma"), (dbeta, "dbeta")):
         if t is not None:
-            _gpu(t, n)
-            if t.dtype != wgrad_dtype or t.numel() != N:
-                raise ValueError(f"{n} must be [N] in wgrad_dtype")
+            _tensor(t, n, dev, wgrad_dtype, N)
     io = _code(x.dtype, "x")
-    need = (norm_bwd_make_plan(kind, M, N, io, dbeta is not None, groups).workspace_bytes
-            if groups else _auto_workspace(kind, M, N, io, dbeta is not None))
     if workspace is None:
+        need = (norm_bwd_make_plan(kind, M, N, io, dbeta is not None, groups).workspace_bytes
+                if groups else _auto_workspace(kind, M, N, io, dbeta is not None))
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    _gpu(workspace, "workspace")
+    _tensor(workspace, "workspace", dev)
     a = NormBwdArgs()
     a.kind, a.io_dtype, a.wgrad_dtype = code, io, _code(wgrad_dtype, "wgrad")
     a.flags = ACCUMULATE if accumulate else 0
@@ -387,33 +404,29 @@ def norm_bwd_wgrad(kind, x: torch.Tensor, dy: torch.Tensor, mean: Optional[torch
     """dgamma (and dbeta) alone by the column walk (no dx, no workspace)."""
     lib = load_library()
     code = kind = _KIND_CODE[kind]
-    for t, n in ((x, "x"), (dy, "dy"), (rstd, "rstd")):
-        _gpu(t, n)
+    _gpu(x, "x")
+    dev = x.device
+    M, N = _rows(x)
+    if not isinstance(dy, torch.Tensor) or dy.shape != x.shape:
+        raise ValueError("dy must have x's shape")
+    _tensor(dy, "dy", dev, x.dtype)
     if kind == LAYERNORM:
-        _gpu(mean, "mean")
+        _tensor(mean, "mean", dev, torch.float32, M)
     else:
         mean = None
-    M, N = _rows(x)
-    if dy.shape != x.shape or dy.dtype != x.dtype:
-        raise ValueError("dy must match x")
-    for t in (mean, rstd):
-        if t is not None and (t.dtype != torch.float32 or t.numel() != M):
-            raise ValueError("mean and rstd must be float32 [M]")
+    _tensor(rstd, "rstd", dev, torch.float32, M)
     if with_dbeta is None:
         with_dbeta = dbeta is not None or (kind == LAYERNORM and not accumulate)
     if accumulate and (dgamma is None or (with_dbeta and dbeta is None)):
         raise ValueError("accumulate=True needs the dgamma (and dbeta) to add into")
     wgrad_dtype = wgrad_dtype or (dgamma.dtype if dgamma is not None else torch.float32)
-    dev = x.device
     if dgamma is None:
         dgamma = torch.empty(N, dtype=wgrad_dtype, device=dev)
     if with_dbeta and dbeta is None:
         dbeta = torch.empty(N, dtype=wgrad_dtype, device=dev)
     for t, n in ((dgamma, "dgamma"), (dbeta, "dbeta")):
         if t is not None:
-            _gpu(t, n)
-            if t.dtype != wgrad_dtype or t.numel() != N:
-                raise ValueError(f"{n} must be [N] in wgrad_dtype")
+            _tensor(t, n, dev, wgrad_dtype, N)
     s = _stream(stream, dev)
     with torch.cuda.device(dev):
         st = lib.norm_bwd_wgrad(code, _ptr(x), _ptr(dy), _ptr(mean), _ptr(rstd), M, N,
@@ -435,12 +448,20 @@ def norm_bwd_execute_partials(plan: NormBwdPlan, x, dy, gamma, mean, rstd, dx, w
                               stream=None):
     """Kernel A alone (dx and the per-group partials in `workspace`)."""
     lib = load_library()
-    for t, n in ((x, "x"), (dy, "dy"), (gamma, "gamma"), (rstd, "rstd"), (dx, "dx"),
-                 (workspace, "workspace")):
-        _gpu(t, n)
+    _gpu(x, "x")
+    dev = x.device
+    dt = _CODE_DTYPE.get(plan.io_dtype)
+    if dt is None:
+        raise ValueError(f"plan.io_dtype {plan.io_dtype} unknown")
+    M, N = plan.M, plan.N
+    for t, n in ((x, "x"), (dy, "dy"), (dx, "dx")):
+        _tensor(t, n, dev, dt, M * N)
+    _tensor(gamma, "gamma", dev, dt, N)
+    _tensor(rstd, "rstd", dev, torch.float32, M)
     if plan.kind == LAYERNORM:
-        _gpu(mean, "mean")
-    s = _stream(stream, x.device)
+        _tensor(mean, "mean", dev, torch.float32, M)
+    _tensor(workspace, "workspace", dev)
+    s = _stream(stream, dev)
     with torch.cuda.device(x.device):
         st = lib.norm_bwd_execute_partials(
             ctypes.byref(plan), _ptr(x), _ptr(dy), _ptr(gamma),
@@ -454,13 +475,13 @@ def norm_bwd_reduce_partials(groups: int, N: int, workspace: torch.Tensor,
                              stream=None):
     """Kernel B alone: fixed-order sum of the per-group partials."""
     lib = load_library()
-    _gpu(workspace, "workspace")
     _gpu(dgamma, "dgamma")
+    dev = dgamma.device
+    _tensor(dgamma, "dgamma", dev, None, N)
     if dbeta is not None:
-        _gpu(dbeta, "dbeta")
-        if dbeta.dtype != dgamma.dtype:
-            raise ValueError("dgamma and dbeta must share a dtype")
-    s = _stream(stream, dgamma.device)
+        _tensor(dbeta, "dbeta", dev, dgamma.dtype, N)
+    _tensor(workspace, "workspace", dev)
+    s = _stream(stream, dev)
     with torch.cuda.device(dgamma.device):
         st = lib.norm_bwd_reduce_partials(groups, N, _code(dgamma.dtype, "dgamma"), _ptr(workspace),
                                           workspace.numel() * workspace.element_size(),
@@ -471,25 +492,22 @@ def norm_bwd_reduce_partials(groups: int, N: int, workspace: torch.Tensor,
 def _forward(kind, x, gamma, beta, eps, y, mean, rstd, want_mean, want_rstd, stream):
     lib = load_library()
     _gpu(x, "x")
-    _gpu(gamma, "gamma")
-    if beta is not None:
-        _gpu(beta, "beta")
+    dev = x.device
     M, N = _rows(x)
     io = _code(x.dtype, "x")
-    if gamma.dtype != x.dtype or (beta is not None and beta.dtype != x.dtype):
-        raise ValueError("x, gamma and beta must share one dtype")
-    if gamma.numel() != N or (beta is not None and beta.numel() != N):
-        raise ValueError("gamma and beta must have N elements")
-    dev = x.device
+    _tensor(gamma, "gamma", dev, x.dtype, N)
+    if beta is not None:
+        _tensor(beta, "beta", dev, x.dtype, N)
     if y is None:
         y = torch.empty_like(x)
     if want_mean and mean is None:
         mean = torch.empty(M, dtype=torch.float32, device=dev)
     if want_rstd and rstd is None:
         rstd = torch.empty(M, dtype=torch.float32, device=dev)
-    for t, n in ((y, "y"), (mean, "mean"), (rstd, "rstd")):
+    _tensor(y, "y", dev, x.dtype, M * N)
+    for t, n in ((mean, "mean"), (rstd, "rstd")):
         if t is not None:
-            _gpu(t, n)
+            _tensor(t, n, dev, torch.float32, M)
     s = _stream(stream, dev)
     with torch.cuda.device(dev):
         if kind == LAYERNORM:
@@ -520,7 +538,7 @@ def norm_bwd_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
     """Plain streaming copy kernel (bandwidth and counter calibration)."""
     lib = load_library()
     _gpu(src, "src")
-    _gpu(dst, "dst")
+    _tensor(dst, "dst", src.device)
     n = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() < n:
         raise ValueError("dst smaller than src")
