@@ -37,8 +37,13 @@
  * are valid once the caller synchronises that stream. Arguments are checked
  * on the host before anything is launched: on a non-zero status nothing was
  * enqueued, except NORM_BWD_ERR_HIP, which reports a failed launch.
- * norm_bwd_last_error() gives a message for the calling thread's last failure.
- * Nothing prints or aborts.
+ * Before launching, the library reads (and so clears) the calling thread's
+ * pending HIP error with hipGetLastError, so that a launch failure it reports
+ * is its own. norm_bwd_last_error() gives a message for the calling thread's
+ * last failure. Nothing aborts, and nothing prints unless the environment
+ * variable NORM_BWD_LOG is set to a non-empty value other than "0" when the
+ * first failure occurs: then every failing call also writes its message to
+ * stderr.
  */
 #ifndef NORM_BWD_H
 #define NORM_BWD_H

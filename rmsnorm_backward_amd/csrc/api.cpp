@@ -5,6 +5,7 @@
 #include <hip/hip_runtime_api.h>
 #include <math.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "nb_launch.hpp"
@@ -15,15 +16,27 @@ namespace {
 
 thread_local char g_last_error[256] = "";
 
+// NORM_BWD_LOG set to a non-empty value other than "0": each failing call
+// also writes its message to stderr. Read once, on the first failure.
+bool log_errors() {
+  static const bool on = [] {
+    const char* v = getenv("NORM_BWD_LOG");
+    return v && v[0] && strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
 int set_error(int status, const char* what) {
   snprintf(g_last_error, sizeof(g_last_error), "%s: %s", norm_bwd_status_string(status),
            what ? what : "");
+  if (log_errors()) fprintf(stderr, "norm_bwd: %s\n", g_last_error);
   return status;
 }
 
 int hip_error(hipError_t e, const char* where) {
   snprintf(g_last_error, sizeof(g_last_error), "%s: %s: %s",
            norm_bwd_status_string(NORM_BWD_ERR_HIP), where, hipGetErrorString(e));
+  if (log_errors()) fprintf(stderr, "norm_bwd: %s\n", g_last_error);
   return NORM_BWD_ERR_HIP;
 }
 

@@ -436,3 +436,32 @@ def test_binding_refuses_cpu_tensors(nb):
         nb.norm_fwd_rmsnorm(x, g)
     with pytest.raises(ValueError, match="GPU"):
         nb.norm_bwd_wgrad("rmsnorm", x, x, None, torch.ones(4))
+
+
+def _log_probe(env_value):
+    """A fresh process that makes one failing call; returns its stderr."""
+    import os
+    import subprocess
+    import sys
+    env = dict(os.environ)
+    env.pop("NORM_BWD_LOG", None)
+    if env_value is not None:
+        env["NORM_BWD_LOG"] = env_value
+    code = ("import ctypes, rmsnorm_backward_amd as nb\n"
+            "lib = nb.load_library()\n"
+            "p = nb.NormBwdPlan()\n"
+            "assert lib.norm_bwd_make_plan(7, 4, 8, 0, 0, 0, ctypes.byref(p)) == 1\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    return r.stderr
+
+
+def test_errors_print_only_with_norm_bwd_log():
+    """The library is silent by default; NORM_BWD_LOG=1 writes each failure's
+    message to stderr (the same text norm_bwd_last_error returns)."""
+    assert "norm_bwd:" not in _log_probe(None)
+    assert "norm_bwd:" not in _log_probe("0")
+    err = _log_probe("1")
+    assert "norm_bwd: NORM_BWD_ERR_INVALID_ARG" in err
