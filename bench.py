@@ -200,7 +200,20 @@ def cpu_baseline(w, inp):
         f", fp64 passes (dx, dgamma{', dbeta' if w.kind == 'layernorm' else ''}) repeated " \
         f"{reps}x, {total:.1f} s total, mean per pass"
     return {"value": round(ws.algorithmic_bytes() / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "sample": sample, "seconds_per_pass": round(dt, 4)}
+            "kind": "oracle", "sample": sample, "seconds_per_pass": round(dt, 4),
+            "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main(argv=None) -> int:
@@ -319,6 +332,8 @@ def main(argv=None) -> int:
         step(i)
     torch.cuda.synchronize()
     ms = time_loop(torch, step, args.steps, stream)
+    # the spread of the step time: 20 loops of 25 steps, each loop's mean
+    chunks = sorted(time_loop(torch, step, 25, stream) for _ in range(20))
     ms_a = time_loop(torch, step_a, args.steps, stream)
     ms_b = time_loop(torch, step_b, max(args.steps, 50), stream)
     for i in range(min(args.warmup, 50)):
@@ -434,6 +449,10 @@ def main(argv=None) -> int:
             "stats_dtype": "f32", "eps": w.eps, "seed": w.seed,
             "algorithmic_bytes": alg, "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
             "rows_per_s": round(w.M / (ms * 1e-3), 1),
+            "step_us_spread": {"loops": len(chunks), "steps_per_loop": 25,
+                               "median": round(chunks[len(chunks) // 2] * 1e3, 3),
+                               "min": round(chunks[0] * 1e3, 3),
+                               "max": round(chunks[-1] * 1e3, 3)},
             "kernel_a_us": round(ms_a * 1e3, 3), "kernel_b_us": round(ms_b * 1e3, 3),
             "copy_probe_GBps": round(copy_gbps, 1),
             "copy_probe_bytes": cp_bytes,
