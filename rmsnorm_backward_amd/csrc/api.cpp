@@ -163,6 +163,7 @@ int launch_partials(const norm_bwd_plan_t& p, const Buffers& b, hipStream_t stre
   a.lds = p.lds_bytes;
   a.recompute = recompute ? 1 : 0;
   a.eps = eps;
+  a.ws_stream = nb::stream_workspace(p.workspace_bytes) ? 1 : 0;
   a.stream = stream;
   (void)hipGetLastError();  // clear a stale error so a launch failure is ours
   hipError_t e;
@@ -179,9 +180,11 @@ int launch_reduce(int64_t groups, int64_t N, int wgrad_dtype, const void* ws, vo
                   void* dbeta, hipStream_t stream, bool accumulate = false) {
   if (N == 0) return NORM_BWD_OK;
   if (accumulate && groups == 0) return NORM_BWD_OK;  // adds the empty sum: nothing
+  const size_t bytes = (size_t)(dbeta ? 2 : 1) * (size_t)groups * (size_t)N * 4u;
   (void)hipGetLastError();
   hipError_t e = nb::launch_reduce(wgrad_dtype, static_cast<const float*>(ws), groups, (int)N,
-                                   dgamma, dbeta, accumulate ? 1 : 0, stream);
+                                   dgamma, dbeta, accumulate ? 1 : 0,
+                                   nb::stream_workspace(bytes) ? 1 : 0, stream);
   if (e != hipSuccess) return hip_error(e, "kernel B launch");
   return NORM_BWD_OK;
 }

@@ -45,6 +45,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <class Tg> __device__ __forceinline__ float lo16_to_f32(uint32_t w);
 template <class Tg> __device__ __forceinline__ float hi16_to_f32(uint32_t w);
@@ -430,7 +431,9 @@ __device__ __forceinline__ void process_row(RowBuf<Tg, VEC, C>& b, const float (
   }
 }
 
-template <int KIND, bool RECOMP, class Tg, int VEC, int C, int NACC>
+// WSNT: the partial rows are stored non-temporally (chosen for large
+// workspaces by the planner's stream_workspace); the values are the same.
+template <int KIND, bool RECOMP, class Tg, int VEC, int C, int NACC, bool WSNT>
 __global__ __launch_bounds__((max_threads_for<VEC, C>()))
 void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dyv,
                         const void* __restrict__ gv, const float* __restrict__ mean,
@@ -548,14 +551,23 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
         for (int c = 0; c < C; ++c) {
           const int col = col0 + c * cstride;
           if (col < N) {
+            // WSNT: non-temporal stores (large workspaces, see the planner's
+            // stream_workspace)
             if constexpr (VEC % 4 == 0) {
 #pragma unroll
-              for (int v = 0; v < VEC; v += 4)
-                *reinterpret_cast<float4*>(dst + col + v) =
-                    make_float4(acc[a][c][v], acc[a][c][v + 1], acc[a][c][v + 2], acc[a][c][v + 3]);
+              for (int v = 0; v < VEC; v += 4) {
+                const f32x4 t = {acc[a][c][v], acc[a][c][v + 1], acc[a][c][v + 2],
+                                 acc[a][c][v + 3]};
+                f32x4* q = reinterpret_cast<f32x4*>(dst + col + v);
+                if constexpr (WSNT) __builtin_nontemporal_store(t, q);
+                else *q = t;
+              }
             } else {
 #pragma unroll
-              for (int v = 0; v < VEC; ++v) dst[col + v] = acc[a][c][v];
+              for (int v = 0; v < VEC; ++v) {
+                if constexpr (WSNT) __builtin_nontemporal_store(acc[a][c][v], dst + col + v);
+                else dst[col + v] = acc[a][c][v];
+              }
             }
           }
         }
@@ -589,16 +601,40 @@ template <class OutT> __device__ __forceinline__ float load_out(const void* p, i
   }
 }
 
+// Sum of partial rows [lo, hi) of column `col` in ascending order, NT loads
+// in batches of kReduceUnroll (non-temporal loads when NT).
+template <bool NT>
+__device__ __forceinline__ float sum_groups(const float* __restrict__ src, int64_t lo,
+                                            int64_t hi, int N, int col) {
+  auto ld = [&](int64_t g) {
+    const float* p = src + g * (int64_t)N + col;
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+  };
+  float sum = 0.0f;
+  int64_t g = lo;
+  for (; g + kReduceUnroll <= hi; g += kReduceUnroll) {
+    float t[kReduceUnroll];
+#pragma unroll
+    for (int k = 0; k < kReduceUnroll; ++k) t[k] = ld(g + k);
+#pragma unroll
+    for (int k = 0; k < kReduceUnroll; ++k) sum += t[k];
+  }
+  for (; g < hi; ++g) sum += ld(g);
+  return sum;
+}
+
 // Lane = feature (each wave load reads 256 contiguous bytes of one partial
 // row); wave q sums groups [q*G/16, (q+1)*G/16) in ascending order, issuing
 // kReduceUnroll loads before adding them in order; wave 0 then adds the 16
 // slice sums in slice order. With `accumulate` the output's previous value is
-// added to that sum (old + sum, one rounding to the output type).
+// added to that sum (old + sum, one rounding to the output type). ws_stream
+// selects non-temporal loads; the sums are the same either way.
 template <class OutT>
 __global__ __launch_bounds__(kReduceWaves * 64)
 void reduce_partials_kernel(const float* __restrict__ ws, int64_t G, int N,
                             void* __restrict__ dgamma, void* __restrict__ dbeta,
-                            int accumulate) {
+                            int accumulate, int ws_stream) {
   __shared__ float part[kReduceWaves][kReduceCols];
   const int lane = threadIdx.x & 63;
   const int q = threadIdx.x >> 6;
@@ -608,17 +644,8 @@ void reduce_partials_kernel(const float* __restrict__ ws, int64_t G, int N,
   const int64_t lo = G * q / kReduceWaves;
   const int64_t hi = G * (q + 1) / kReduceWaves;
   float sum = 0.0f;
-  if (col < N) {
-    int64_t g = lo;
-    for (; g + kReduceUnroll <= hi; g += kReduceUnroll) {
-      float t[kReduceUnroll];
-#pragma unroll
-      for (int k = 0; k < kReduceUnroll; ++k) t[k] = src[(g + k) * (int64_t)N + col];
-#pragma unroll
-      for (int k = 0; k < kReduceUnroll; ++k) sum += t[k];
-    }
-    for (; g < hi; ++g) sum += src[g * (int64_t)N + col];
-  }
+  if (col < N)
+    sum = ws_stream ? sum_groups<true>(src, lo, hi, N, col) : sum_groups<false>(src, lo, hi, N, col);
   part[q][lane] = sum;
   __syncthreads();
   if (q == 0 && col < N) {

@@ -26,6 +26,7 @@ struct LaunchA {
   int S, P, threads, grid, lds;
   int recompute;  // 1: mean/rstd are NULL and recomputed from x with eps
   float eps;
+  int ws_stream;  // 1: non-temporal stores of the partials (16-byte vector rows)
   hipStream_t stream;
 };
 
@@ -103,7 +104,7 @@ hipError_t launch_f_f32(const LaunchF& f);
 hipError_t launch_f_f16(const LaunchF& f);
 hipError_t launch_f_bf16(const LaunchF& f);
 hipError_t launch_reduce(int wgrad_dtype, const float* ws, int64_t G, int N, void* dgamma,
-                         void* dbeta, int accumulate, hipStream_t stream);
+                         void* dbeta, int accumulate, int ws_stream, hipStream_t stream);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
 }  // namespace nb

@@ -15,12 +15,22 @@ constexpr int lane_elem_limit() {
   return !FULL ? 8 : (Tg::kBytes == 4 ? 16 : (NACC == 2 ? 32 : 64));
 }
 
-template <class Tg, int KIND, bool RECOMP, int NACC, int VEC, int C>
-hipError_t launch_one(const LaunchA& a) {
-  hipLaunchKernelGGL((dx_partials_kernel<KIND, RECOMP, Tg, VEC, C, NACC>), dim3(a.grid),
+template <class Tg, int KIND, bool RECOMP, int NACC, int VEC, int C, bool WSNT>
+hipError_t launch_one_policy(const LaunchA& a) {
+  hipLaunchKernelGGL((dx_partials_kernel<KIND, RECOMP, Tg, VEC, C, NACC, WSNT>), dim3(a.grid),
                      dim3(a.threads), a.lds, a.stream, a.x, a.dy, a.gamma, a.mean, a.rstd, a.dx,
                      a.ws, a.M, a.N, a.ldx, a.ldy, a.ldo, a.G, a.R, a.S, a.P, a.eps);
   return hipGetLastError();
+}
+
+// The non-temporal partials store exists for 16-byte vector rows only (the
+// one-element-per-lane path serves unaligned rows and keeps cached stores).
+template <class Tg, int KIND, bool RECOMP, int NACC, int VEC, int C>
+hipError_t launch_one(const LaunchA& a) {
+  if constexpr (VEC > 1) {
+    if (a.ws_stream) return launch_one_policy<Tg, KIND, RECOMP, NACC, VEC, C, true>(a);
+  }
+  return launch_one_policy<Tg, KIND, RECOMP, NACC, VEC, C, false>(a);
 }
 
 template <class Tg, int KIND, bool RECOMP, int NACC, bool FULL>

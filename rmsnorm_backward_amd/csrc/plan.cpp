@@ -20,6 +20,12 @@ constexpr int64_t kRecomputeLnTargetWaves = 4096;
 // needs twice the waves (16 per compute unit) for as many bytes in flight.
 constexpr int64_t kForwardTargetWaves = 4096;
 constexpr int64_t kMinRowsPerGroup = 4;
+// Group counts above this are rounded down to a multiple of it, so that the
+// workgroups (one per group) spread evenly over the 256 compute units. LayerNorm
+// recompute of 1151x8192 fp16: 288 groups (the rows-per-group cap) 30.4 us,
+// 256 groups 24.2 us; 192, 288 and 384 groups were slower than 256 or 512 on
+// every shape measured.
+constexpr int64_t kGroupQuantum = 256;
 constexpr int64_t kMaxGrid = 1 << 20;
 constexpr int kMaxLdsBytes = 65536 - 1024;  // dynamic LDS; the kernel adds 256 B static
 constexpr int kTargetThreads = 512;
@@ -124,6 +130,15 @@ bool fused_fits(int64_t N, int io_dtype, int with_dbeta, bool vec_ok16) {
 
 int64_t rowloop_grid(int64_t M) { return M < 512 ? (M < 1 ? 1 : M) : 512; }
 
+// Partials of 16 MiB (8192 features, both gradients, 256 groups) written
+// with cached stores cost up to 5 us more per step than with non-temporal
+// stores read back with non-temporal loads (1151x8192 fp16 LayerNorm 25.5 ->
+// 20.7 us, 8192x8192 bf16 80.6 -> 77.2 us); 8 MiB showed no difference, and
+// at 4 MiB (the 16384x4096 RMSNorm step) the cached form was 0.4 us faster.
+constexpr size_t kStreamWorkspaceBytes = (size_t)12 << 20;
+
+bool stream_workspace(size_t bytes) { return bytes >= kStreamWorkspaceBytes; }
+
 int64_t forward_grid(int64_t M, int S, int P) {
   if (M <= 0) return 0;
   int64_t g = kForwardTargetWaves / (S * P);
@@ -143,7 +158,7 @@ int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype, bool recompute
   if (M <= 0) return 0;
   // Enough workgroups for about kTargetWaves waves in flight (8 per compute
   // unit on a 256-CU part), never fewer than kMinRowsPerGroup rows per
-  // group. The geometry is itself a function of (kind, N, io_dtype), so the
+  // group, above kGroupQuantum a multiple of it. The geometry is itself a function of (kind, N, io_dtype), so the
   // group count depends on the problem only, never on the device.
   norm_bwd_plan_t g;
   const char* why = nullptr;
@@ -154,6 +169,7 @@ int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype, bool recompute
               waves;
   const int64_t cap = ceil_div(M, kMinRowsPerGroup);
   if (G > cap) G = cap;
+  if (G > kGroupQuantum) G -= G % kGroupQuantum;
   return G < 1 ? 1 : G;
 }
 

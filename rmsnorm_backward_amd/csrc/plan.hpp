@@ -30,6 +30,10 @@ int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok
 // of io_dtype; wider rows take the row-loop path.
 bool fused_fits(int64_t N, int io_dtype, int with_dbeta, bool vec_ok16);
 
+// Whether kernels A and B move a workspace of `bytes` with non-temporal
+// stores and loads rather than cached ones.
+bool stream_workspace(size_t bytes);
+
 // Workgroups of the row-loop kernel for M rows: one 16-wave workgroup per row,
 // at most two per compute unit.
 int64_t rowloop_grid(int64_t M);

@@ -16,21 +16,21 @@ void copy_probe_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, i
 
 
 hipError_t launch_reduce(int wgrad_dtype, const float* ws, int64_t G, int N, void* dgamma,
-                         void* dbeta, int accumulate, hipStream_t stream) {
+                         void* dbeta, int accumulate, int ws_stream, hipStream_t stream) {
   const dim3 grid((unsigned)((N + kReduceCols - 1) / kReduceCols), dbeta ? 2u : 1u);
   const dim3 block(kReduceWaves * 64);
   switch (wgrad_dtype) {
     case NORM_BWD_F32:
       hipLaunchKernelGGL(reduce_partials_kernel<TF32>, grid, block, 0, stream, ws, G, N, dgamma,
-                         dbeta, accumulate);
+                         dbeta, accumulate, ws_stream);
       break;
     case NORM_BWD_F16:
       hipLaunchKernelGGL(reduce_partials_kernel<TF16>, grid, block, 0, stream, ws, G, N, dgamma,
-                         dbeta, accumulate);
+                         dbeta, accumulate, ws_stream);
       break;
     case NORM_BWD_BF16:
       hipLaunchKernelGGL(reduce_partials_kernel<TBF16>, grid, block, 0, stream, ws, G, N, dgamma,
-                         dbeta, accumulate);
+                         dbeta, accumulate, ws_stream);
       break;
     default:
       return hipErrorInvalidValue;

@@ -93,19 +93,24 @@ def test_status_strings(nb):
 
 def _auto_groups(nb, kind, M, N, dt, recompute=False):
     """The documented rule: about 2048 waves in flight (4096 for LayerNorm in
-    recompute mode), >= 4 rows per group, where the waves per workgroup come
-    from the (dbeta-less) geometry."""
+    recompute mode), >= 4 rows per group, above 256 a multiple of 256, where
+    the waves per workgroup come from the (dbeta-less) geometry."""
     if M == 0:
         return 0
     waves = nb.norm_bwd_make_plan(kind, 1, N, dt, False).threads // 64 if N else 8
     target = 4096 if (recompute and kind == "layernorm") else 2048
-    return max(1, min(target // waves, -(-M // 4)))
+    g = min(target // waves, -(-M // 4))
+    if g > 256:
+        g -= g % 256
+    return max(1, g)
 
 
 @pytest.mark.parametrize("kind,M,N,dt,db", [
     ("layernorm", 128, 512, torch.float32, True),
     ("rmsnorm", 128, 512, torch.float32, False),
     ("layernorm", 1151, 8192, torch.float16, True),
+    ("layernorm", 2000, 2048, torch.bfloat16, True),
+    ("rmsnorm", 3000, 1024, torch.bfloat16, False),
     ("rmsnorm", 16384, 4096, torch.bfloat16, False),
     ("layernorm", 65536, 8192, torch.bfloat16, True),
     ("rmsnorm", 262144, 768, torch.bfloat16, False),
