@@ -15,9 +15,19 @@ The functions carry the C names:
 * ``norm_fwd_layernorm(x, gamma, beta, eps)`` -> (y, mean, rstd),
   ``norm_fwd_rmsnorm(x, gamma, eps)`` -> (y, rstd): the forward pass that
   produces the statistics the backward consumes
+* ``norm_bwd_ex(kind, x, dy, gamma, mean, rstd, eps, ...)``: row-strided 2-D
+  views, an explicit group count, accumulation into given dgamma/dbeta
+* ``norm_bwd_wgrad(kind, x, dy, mean, rstd)`` -> (dgamma, dbeta or None): the
+  weight gradients alone (column walk, no workspace)
 * ``norm_bwd_workspace_bytes``, ``norm_bwd_make_plan``, ``norm_bwd_execute``,
   ``norm_bwd_execute_partials``, ``norm_bwd_reduce_partials``,
   ``norm_bwd_probe_copy``, ``norm_bwd_status_string``, ``norm_bwd_last_error``.
+
+Every tensor handed to the library is checked first: on x's GPU, contiguous
+unless a row stride is taken, and of the dtype and element count the kernels
+assume. The library only sees raw pointers, so this is what keeps a kernel
+inside the tensors. ``rmsnorm_backward_amd.autograd`` wraps the forward and
+backward as torch.autograd Functions and nn.Modules.
 """
 
 from __future__ import annotations
