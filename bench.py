@@ -219,8 +219,9 @@ def cpu_model() -> str:
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one GPU; "
-              "the multi-GPU sharding is a design note only. Use --gpus 1.", file=sys.stderr)
+        print(f"bench.py: --gpus {args.gpus} is not supported: the library and this benchmark "
+              "run on one GPU (the sharding across GPUs is described, not implemented). "
+              "Use --gpus 1.", file=sys.stderr)
         return 2
 
     import torch
