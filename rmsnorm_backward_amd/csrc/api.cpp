@@ -282,7 +282,10 @@ int run_wide(int kind, const Buffers& b, int64_t M, int64_t N, int io_dtype, int
     l.ldy = b.ldy;
     l.ldo = b.ldo;
     l.eps = eps;
-    l.grid = nb::rowloop_grid(M);
+    l.chunks = l.vec_full ? nb::rowreg_chunks(N, io_dtype, true,
+                                              recompute && kind == NORM_BWD_LAYERNORM)
+                          : 0;
+    l.grid = l.chunks ? nb::rowreg_grid(M) : nb::rowloop_grid(M);
     l.stream = stream;
     (void)hipGetLastError();  // clear a stale error so a launch failure is ours
     hipError_t e;
@@ -382,7 +385,11 @@ int run_forward(int kind, const void* x, const void* gamma, const void* beta, in
   nb::LaunchF f;
   f.kind = kind;
   f.vec_full = wide ? ((vec_ok && ((size_t)N * eb) % 16 == 0) ? 1 : 0) : (g.vec > 1 ? 1 : 0);
-  f.chunks = wide ? 0 : g.chunks;
+  // wide rows: held in registers (4 or 8 chunks per thread) or streamed (0)
+  f.chunks = wide ? (f.vec_full ? nb::rowreg_chunks(N, io_dtype, true,
+                                                    kind == NORM_BWD_LAYERNORM && beta)
+                                : 0)
+                  : g.chunks;
   f.x = x;
   f.gamma = gamma;
   f.beta = beta;
@@ -395,7 +402,7 @@ int run_forward(int kind, const void* x, const void* gamma, const void* beta, in
   f.S = wide ? 0 : g.waves_per_row;
   f.P = wide ? 0 : g.rows_in_flight;
   f.threads = wide ? 0 : g.threads;
-  f.grid = wide ? (int)nb::rowloop_grid(M)
+  f.grid = wide ? (int)(f.chunks ? nb::rowreg_grid(M) : nb::rowloop_grid(M))
                 : (int)nb::forward_grid(M, g.waves_per_row, g.rows_in_flight);
   f.stream = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so a launch failure is ours

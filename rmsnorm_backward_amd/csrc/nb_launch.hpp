@@ -65,10 +65,11 @@ struct LaunchW {
   hipStream_t stream;
 };
 
-struct LaunchL {  // dx for wide rows (row loop)
+struct LaunchL {  // dx for wide rows
   int kind;
   int recompute;
   int vec_full;
+  int chunks;       // 4 or 8: the row held in registers (16-byte chunks per thread); 0: row loop
   const void* x;
   const void* dy;
   const void* gamma;
@@ -83,7 +84,8 @@ struct LaunchL {  // dx for wide rows (row loop)
   hipStream_t stream;
 };
 
-hipError_t launch_fl_f32(const LaunchF& f);  // forward for wide rows (row loop)
+// forward for wide rows: chunks 4 or 8 holds the row in registers, 0 streams it
+hipError_t launch_fl_f32(const LaunchF& f);
 hipError_t launch_fl_f16(const LaunchF& f);
 hipError_t launch_fl_bf16(const LaunchF& f);
 hipError_t launch_l_f32(const LaunchL& l);

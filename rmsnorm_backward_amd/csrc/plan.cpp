@@ -130,6 +130,26 @@ bool fused_fits(int64_t N, int io_dtype, int with_dbeta, bool vec_ok16) {
 
 int64_t rowloop_grid(int64_t M) { return M < 512 ? (M < 1 ? 1 : M) : 512; }
 
+// The register-held wide-row kernels run 1024 threads (16 waves) per row;
+// with 64 elements of x and dy per thread one workgroup fills a compute
+// unit's register file, so the grid is one workgroup per compute unit.
+constexpr int64_t kRowThreads = 1024;
+
+// At 8 chunks the row's x and dy take 64 of the 128 registers a thread of a
+// 1024-thread workgroup has; LayerNorm recompute (backward) and LayerNorm
+// with beta (forward) need more than the rest and would spill, so those rows
+// keep the row loop.
+int rowreg_chunks(int64_t N, int io_dtype, bool vec_ok16, bool ln_heavy) {
+  const int eb = dtype_bytes(io_dtype);
+  if (!vec_ok16 || eb == 0 || N <= 0 || ((int64_t)N * eb) % 16 != 0) return 0;
+  const int64_t per_chunk = kRowThreads * (16 / eb);
+  if (N <= 4 * per_chunk) return 4;
+  if (N <= 8 * per_chunk && !ln_heavy) return 8;
+  return 0;
+}
+
+int64_t rowreg_grid(int64_t M) { return M < 256 ? (M < 1 ? 1 : M) : 256; }
+
 // Partials of 16 MiB (8192 features, both gradients, 256 groups) written
 // with cached stores cost up to 5 us more per step than with non-temporal
 // stores read back with non-temporal loads (1151x8192 fp16 LayerNorm 25.5 ->

@@ -30,6 +30,14 @@ int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok
 // of io_dtype; wider rows take the row-loop path.
 bool fused_fits(int64_t N, int io_dtype, int with_dbeta, bool vec_ok16);
 
+// Rows too wide for the fused kernels that one 1024-thread workgroup can hold
+// in registers: the number of 16-byte chunks per thread (4 or 8), or 0 when
+// the row needs the row loop (also for rows that are not 16-byte aligned).
+// `ln_heavy`: LayerNorm recompute (backward) or LayerNorm with beta
+// (forward), which do not fit at 8 chunks.
+int rowreg_chunks(int64_t N, int io_dtype, bool vec_ok16, bool ln_heavy);
+int64_t rowreg_grid(int64_t M);
+
 // Whether kernels A and B move a workspace of `bytes` with non-temporal
 // stores and loads rather than cached ones.
 bool stream_workspace(size_t bytes);
