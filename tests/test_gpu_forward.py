@@ -132,7 +132,10 @@ WIDE_FWD = [(kind, dt, M, N)
 @pytest.mark.parametrize("kind,dt,M,N", WIDE_FWD, ids=lambda v: str(v).replace("torch.", ""))
 def test_forward_wide_rows(nb, kind, dt, M, N):
     """Rows wider than the fused forward holds (or unaligned beyond 8192) take
-    the row-loop forward; same results to the same tolerance."""
+    the wide-row forward: held in registers when they fit (32776 and 65536
+    16-bit, 40000 fp32 hold their row; LayerNorm with beta at 8 chunks and
+    100003 stream it), streamed by the row loop otherwise. Same results to
+    the same tolerance."""
     base = W.LN_F32_128x512 if kind == "layernorm" else W.RMS_F32_128x512
     w = W.scaled(base, M=M, N=N, io_dtype=dt, seed=40 + M + N)
     inp = W.make_inputs(w)

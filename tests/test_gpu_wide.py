@@ -1,9 +1,12 @@
 """Rows too wide for the fused kernels (the wide-row path) against the oracle.
 
 Above the fused limits (fp32: 16384; fp16/bf16: 16384 with dbeta, 32768
-without; unaligned rows: 8192) the named entry points compute dx with the
-row-loop kernel (one workgroup per row, the row streamed in chunks) and the
-weight gradients with the column walk. Same formulas ("Norm backward in
+without; unaligned rows: 8192) the named entry points compute dx with one
+workgroup per row -- the row held in its registers when it fits (16-byte
+aligned, up to 65536 16-bit or 32768 fp32 elements; 16385 fp32, 20000 bf16
+with dbeta, 32776, 40000 strided and 65536 here), else streamed in chunks by
+the row loop (40000 fp32, 100000, the unaligned rows, LayerNorm recompute at
+8 chunks) -- and the weight gradients with the column walk. Same formulas ("Norm backward in
 Triton", "The gradients"), same tolerances as the fused path.
 """
 
