@@ -73,7 +73,11 @@ WIDE = [(kind, dt, M, N)
         for dt, M, N in ((torch.float32, 37, 16385), (torch.float32, 5, 40000),
                          (torch.bfloat16, 64, 20000), (torch.float16, 3, 32776),
                          (torch.bfloat16, 9, 100000), (torch.bfloat16, 4, 100003),
-                         (torch.float16, 21, 9001), (torch.bfloat16, 600, 65536))]
+                         (torch.float16, 21, 9001), (torch.bfloat16, 600, 65536),
+                         # the register-held kernels at their edges: 4 and 8
+                         # full chunks, a last chunk barely used, one row
+                         (torch.bfloat16, 1, 32768), (torch.float32, 2, 32768),
+                         (torch.float16, 3, 16392), (torch.bfloat16, 5, 65528))]
 
 
 @pytest.mark.parametrize("kind,dt,M,N", WIDE, ids=lambda v: str(v).replace("torch.", ""))
