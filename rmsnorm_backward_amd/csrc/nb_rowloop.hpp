@@ -241,8 +241,8 @@ void fwd_rowloop_kernel(const void* __restrict__ xv, const void* __restrict__ gv
 // kRowWaves * 64 * VEC * C elements (C = 8: 65536 16-bit or 32768 fp32
 // elements). One row per workgroup at a time, rows strided over the grid.
 // Thread t holds the VEC-element chunks starting at (c * 1024 + t) * VEC,
-// c < C, of x, dy and gamma, so each is read once per row for both the row
-// sums and dx, where dx_rowloop_kernel streams the row twice. Same formulas
+// c < C, of x and dy, so each is read once per row for both the row sums and
+// dx, where dx_rowloop_kernel streams the row twice. Same formulas
 // as dx_rowloop_kernel ("Norm backward in Triton", "The gradients"); the
 // weight gradients come from the column walk. Sums over the 16 waves are
 // added in wave order, so results are reproducible.
@@ -305,7 +305,7 @@ void dx_rowreg_kernel(const void* __restrict__ xv, const void* __restrict__ dyv,
             s2 = __builtin_fmaf(dyh, xb[c].get(v) - mu, s2);
           }
         }
-        }
+      }
       keep_packed(xb);
       keep_packed(yb);
       block_sum3(s1, s2, unused, buf, phase, lane, wave);
@@ -335,7 +335,7 @@ void dx_rowreg_kernel(const void* __restrict__ xv, const void* __restrict__ dyv,
             s2 = __builtin_fmaf(dyh, xc, s2);
           }
         }
-        }
+      }
       keep_packed(xb);
       keep_packed(yb);
       block_sum3(sxx, s1, s2, buf, phase, lane, wave);
