@@ -347,6 +347,42 @@ def test_stream_semantics(nb):
             assert torch.equal(a.cpu(), b)
 
 
+def test_concurrent_streams_do_not_interfere(nb):
+    """Calls on separate streams, each with its own outputs and workspace,
+    may run at the same time: four different problems issued back to back on
+    four streams (default priority), several times over, give bitwise the
+    results each gives alone."""
+    cases = [W.scaled(W.RMS_BF16_16384x4096, M=2000, N=4096),
+             W.scaled(W.LN_F16_1151x8192, M=700),
+             W.scaled(W.LN_BF16_65536x8192, M=300, N=24576),      # wide rows
+             W.scaled(W.RMS_F32_128x512, M=3000, N=768)]
+    prepared = []
+    for w in cases:
+        inp = backward_inputs(w)
+        g = to_gpu(inp)
+        prepared.append((w, g, run(nb, w, g)))
+    streams = [torch.cuda.Stream() for _ in cases]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for rep in range(3):
+        for (w, g, _), s in zip(prepared, streams):
+            with torch.cuda.stream(s):
+                if w.kind == "layernorm":
+                    o = nb.norm_bwd_layernorm(g["x"], g["dy"], g["gamma"], g["mean"], g["rstd"],
+                                              w.eps, wgrad_dtype=w.wgrad_dtype)
+                else:
+                    o = nb.norm_bwd_rmsnorm(g["x"], g["dy"], g["gamma"], g["rstd"], w.eps,
+                                            wgrad_dtype=w.wgrad_dtype)
+                outs.append((rep, w, o))
+    torch.cuda.synchronize()
+    for rep, w, o in outs:
+        ref = next(r for (ww, _, r) in prepared if ww is w)
+        for a, b in zip(o, ref):
+            if b is not None:
+                assert torch.equal(a.cpu(), b), (w.name, rep)
+
+
 def test_two_phase_api_matches_full_call(nb):
     w = W.scaled(W.LN_BF16_65536x8192, M=2048, N=2048)
     g = to_gpu(backward_inputs(w))
