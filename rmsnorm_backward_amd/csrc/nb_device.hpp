@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace nb {
 
 // ---------------------------------------------------------------- element types
@@ -226,6 +228,17 @@ constexpr int prefetch_depth() {
   return max_threads_for<VEC, C>() == 1024 ? (bytes <= 32 ? 3 : 1) : (bytes <= 64 ? 2 : 1);
 }
 
+// Whether kernel A pipelines the two exchanges of LayerNorm recompute across
+// rows. It reads the next row from the ring, so the ring must hold two rows;
+// and fp16 rows of 16 elements per lane with both gradients are left out:
+// pipelined, that kernel needed 3 registers more than the 128 a 1024-thread
+// workgroup allows and spilled (bf16 fits, with 123).
+template <class Tg, int VEC, int C, int NACC>
+constexpr bool pipeline_ln_recompute() {
+  return prefetch_depth<Tg, VEC, C>() >= 2 &&
+         !(std::is_same<Tg, TF16>::value && VEC * C == 16 && NACC == 2);
+}
+
 // ---------------------------------------------------------------- kernel A
 // Turn per-lane partial sums into row sums: the wave butterfly, then, when
 // S > 1 waves share the row, an exchange through LDS in which the S wave sums
@@ -256,6 +269,46 @@ __device__ __forceinline__ void row_sum2(float& a, float& b, float (*red)[kMaxWa
     }
     a = ta;
     b = tb;
+  }
+  ++phase;
+}
+
+// Four row sums in one exchange (pipelined LayerNorm recompute: one row's
+// second pair of sums travels with the next row's first pair). Each sum is
+// formed exactly as row_sum2 forms it: the wave butterfly, then the S slice
+// sums added in slice order. Same calling rules as row_sum2, with its own
+// double buffer.
+__device__ __forceinline__ void row_sum4(float& a, float& b, float& c, float& d,
+                                         float (*red4)[kMaxWaves][4], int& phase, int lane,
+                                         int wave, int S, int p) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  c = wave_sum(c);
+  d = wave_sum(d);
+  if (S > 1) {
+    const int buf = phase & 1;
+    if (lane == 0) {
+      red4[buf][wave][0] = a;
+      red4[buf][wave][1] = b;
+      red4[buf][wave][2] = c;
+      red4[buf][wave][3] = d;
+    }
+    __syncthreads();
+    float4 mine = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (lane < S) mine = *reinterpret_cast<const float4*>(&red4[buf][p * S + lane][0]);
+    const int ab = __builtin_bit_cast(int, mine.x), bb = __builtin_bit_cast(int, mine.y);
+    const int cb = __builtin_bit_cast(int, mine.z), db = __builtin_bit_cast(int, mine.w);
+    float ta = 0.0f, tb = 0.0f, tc = 0.0f, td = 0.0f;
+    for (int q = 0; q < S; ++q) {
+      ta += __builtin_bit_cast(float, __builtin_amdgcn_readlane(ab, q));
+      tb += __builtin_bit_cast(float, __builtin_amdgcn_readlane(bb, q));
+      tc += __builtin_bit_cast(float, __builtin_amdgcn_readlane(cb, q));
+      td += __builtin_bit_cast(float, __builtin_amdgcn_readlane(db, q));
+    }
+    a = ta;
+    b = tb;
+    c = tc;
+    d = td;
   }
   ++phase;
 }
@@ -326,6 +379,97 @@ __device__ __forceinline__ void fetch_row(RowBuf<Tg, VEC, C>& b, const char* __r
 // the same exchange), then with mean = sum(x)/N sums xc^2 and dyhat * xc;
 // RMSNorm sums x^2 and dyhat * x in one exchange. rstd = 1/sqrt(sum(xc^2)/N
 // + eps). The dgamma terms, which need rstd, are accumulated in pass 2.
+// LayerNorm recompute, first pass over a row held in registers: sum(x) and
+// sum(dy * gamma), and the row's dbeta terms into the accumulators.
+template <class Tg, int VEC, int C, int NACC>
+__device__ __forceinline__ void ln_recompute_sums1(const RowBuf<Tg, VEC, C>& b,
+                                                   const float (&gam)[C][VEC],
+                                                   float (&acc)[NACC][C][VEC], bool active,
+                                                   int N, int col0, int cstride, float& sx,
+                                                   float& s1) {
+  sx = 0.0f;
+  s1 = 0.0f;
+  if (active) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      if (col0 + c * cstride < N) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          const float dyv = b.dy[c].get(v);
+          sx += b.x[c].get(v);
+          s1 = __builtin_fmaf(dyv, gam[c][v], s1);
+          if (NACC == 2) acc[NACC - 1][c][v] += dyv;
+        }
+      }
+    }
+  }
+}
+
+// Recompute, second pass: sum(xc^2) and sum(dyhat * xc) with xc = x - mean
+// (RMSNorm: mean 0, and its dbeta terms here, as it has no first pass).
+template <int KIND, class Tg, int VEC, int C, int NACC>
+__device__ __forceinline__ void recompute_sums2(const RowBuf<Tg, VEC, C>& b,
+                                                const float (&gam)[C][VEC],
+                                                float (&acc)[NACC][C][VEC], bool active, int N,
+                                                int col0, int cstride, float mu, float& sxx,
+                                                float& s2) {
+  sxx = 0.0f;
+  s2 = 0.0f;
+  if (active) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      if (col0 + c * cstride < N) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          const float xc = b.x[c].get(v) - mu;
+          const float dyv = b.dy[c].get(v);
+          sxx = __builtin_fmaf(xc, xc, sxx);
+          s2 = __builtin_fmaf(dyv * gam[c][v], xc, s2);
+          if (KIND != kLayerNorm && NACC == 2) acc[NACC - 1][c][v] += dyv;
+        }
+      }
+    }
+  }
+}
+
+// dx of one row from its statistics and row sums:
+//   dx = dyhat * rstd + xc * c2 + c1, c2 = -rstd^2 * mean(dyhat * xhat),
+//   c1 = -rstd * s1 / N (LayerNorm), and in recompute mode the row's dgamma
+// terms, which need rstd.
+template <int KIND, bool RECOMP, class Tg, int VEC, int C, int NACC>
+__device__ __forceinline__ void write_dx(const RowBuf<Tg, VEC, C>& b, const float (&gam)[C][VEC],
+                                         float (&acc)[NACC][C][VEC], char* __restrict__ dx,
+                                         int64_t r, bool active, int N, int64_t ldo, float inv_n,
+                                         float mu, float rs, float s1, float s2, int col0,
+                                         int cstride) {
+  constexpr int EB = Tg::kBytes;
+  if (active) {
+    const float m2 = s2 * inv_n * rs;  // mean_j(dyhat * xhat)
+    const float c2 = -(rs * rs) * m2;
+    const float c1 = (KIND == kLayerNorm) ? -rs * (s1 * inv_n) : 0.0f;
+    const int64_t rb = r * ldo;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int col = col0 + c * cstride;
+      if (col < N) {
+        float o[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          const float xc = b.x[c].get(v) - mu;
+          const float dyh = b.dy[c].get(v) * gam[c][v];
+          o[v] = __builtin_fmaf(dyh, rs, __builtin_fmaf(xc, c2, c1));
+          // recompute mode: the dgamma term, now that rstd is known
+          if constexpr (RECOMP)
+            acc[0][c][v] = __builtin_fmaf(b.dy[c].get(v) * xc, rs, acc[0][c][v]);
+        }
+        Pack<Tg, VEC> out;
+        out.set(o);
+        out.store_stream(dx + (rb + col) * EB);
+      }
+    }
+  }
+}
+
 template <int KIND, bool RECOMP, class Tg, int VEC, int C, int NACC>
 __device__ __forceinline__ void process_row(RowBuf<Tg, VEC, C>& b, const float (&gam)[C][VEC],
                                             float (&acc)[NACC][C][VEC], char* __restrict__ dx,
@@ -333,7 +477,6 @@ __device__ __forceinline__ void process_row(RowBuf<Tg, VEC, C>& b, const float (
                                             bool active, int N, int64_t ldo, float inv_n, float eps,
                                             int col0, int cstride, int lane, int wave, int S,
                                             int p) {
-  constexpr int EB = Tg::kBytes;
   float s1 = 0.0f, s2 = 0.0f;
   float mu, rs;
   if constexpr (!RECOMP) {
@@ -363,72 +506,22 @@ __device__ __forceinline__ void process_row(RowBuf<Tg, VEC, C>& b, const float (
   } else {
     mu = 0.0f;
     if constexpr (KIND == kLayerNorm) {
-      float sx = 0.0f;
-      if (active) {
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-          if (col0 + c * cstride < N) {
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) {
-              const float dyv = b.dy[c].get(v);
-              sx += b.x[c].get(v);
-              s1 = __builtin_fmaf(dyv, gam[c][v], s1);
-              if (NACC == 2) acc[NACC - 1][c][v] += dyv;
-            }
-          }
-        }
-      }
+      float sx;
+      ln_recompute_sums1(b, gam, acc, active, N, col0, cstride, sx, s1);
       keep_packed(b.x);
       keep_packed(b.dy);
       row_sum2<true>(sx, s1, red, phase, lane, wave, S, p);
       mu = sx * inv_n;
     }
-    float sxx = 0.0f;
-    if (active) {
-#pragma unroll
-      for (int c = 0; c < C; ++c) {
-        if (col0 + c * cstride < N) {
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) {
-            const float xc = b.x[c].get(v) - mu;
-            const float dyv = b.dy[c].get(v);
-            sxx = __builtin_fmaf(xc, xc, sxx);
-            s2 = __builtin_fmaf(dyv * gam[c][v], xc, s2);
-            if (KIND != kLayerNorm && NACC == 2) acc[NACC - 1][c][v] += dyv;
-          }
-        }
-      }
-    }
+    float sxx;
+    recompute_sums2<KIND>(b, gam, acc, active, N, col0, cstride, mu, sxx, s2);
     keep_packed(b.x);
     keep_packed(b.dy);
     row_sum2<true>(sxx, s2, red, phase, lane, wave, S, p);
     rs = 1.0f / __builtin_sqrtf(__builtin_fmaf(sxx, inv_n, eps));
   }
-  if (active) {
-    const float m2 = s2 * inv_n * rs;  // mean_j(dyhat * xhat)
-    const float c2 = -(rs * rs) * m2;
-    const float c1 = (KIND == kLayerNorm) ? -rs * (s1 * inv_n) : 0.0f;
-    const int64_t rb = r * ldo;
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const int col = col0 + c * cstride;
-      if (col < N) {
-        float o[VEC];
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-          const float xc = b.x[c].get(v) - mu;
-          const float dyh = b.dy[c].get(v) * gam[c][v];
-          o[v] = __builtin_fmaf(dyh, rs, __builtin_fmaf(xc, c2, c1));
-          // recompute mode: the dgamma term, now that rstd is known
-          if constexpr (RECOMP)
-            acc[0][c][v] = __builtin_fmaf(b.dy[c].get(v) * xc, rs, acc[0][c][v]);
-        }
-        Pack<Tg, VEC> out;
-        out.set(o);
-        out.store_stream(dx + (rb + col) * EB);
-      }
-    }
-  }
+  write_dx<KIND, RECOMP>(b, gam, acc, dx, r, active, N, ldo, inv_n, mu, rs, s1, s2, col0,
+                         cstride);
 }
 
 // WSNT: the partial rows are stored non-temporally (chosen for large
@@ -501,19 +594,72 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
                                 cstride);
       }
     }
-    for (int it = 0; it < iters; it += D) {
+    if constexpr (RECOMP && KIND == kLayerNorm && pipeline_ln_recompute<Tg, VEC, C, NACC>()) {
+      // LayerNorm recompute needs two exchanges per row (sum x, then the
+      // squared deviations from the mean). Pipelined across rows, step k
+      // exchanges row k's second pair of sums together with row k + 1's
+      // first pair (read from the ring, where row k + 1 already is), so a
+      // row costs one barrier. Every sum keeps its own order, and each
+      // accumulator still takes the rows in ascending order, so the results
+      // are those of process_row.
+      __shared__ __align__(16) float red4[2][kMaxWaves][4];
+      float mu = 0.0f, s1 = 0.0f;
+      if (iters > 0) {
+        float sx;
+        const int64_t r0 = row_of(0);
+        ln_recompute_sums1(buf[0], gam, acc, r0 < M, N, col0, cstride, sx, s1);
+        keep_packed(buf[0].x);
+        keep_packed(buf[0].dy);
+        row_sum2<true>(sx, s1, red, phase, lane, wave, S, p);
+        mu = sx * inv_n;
+      }
+      for (int it = 0; it < iters; it += D) {
 #pragma unroll
-      for (int d = 0; d < D; ++d) {
-        const int k = it + d;
-        if (k + D - 1 < iters) {
-          const int64_t rf = row_of(k + D - 1);
-          fetch_row<KIND, RECOMP>(buf[(d + D - 1) % D], x, dy, mean, rstd, rf, rf < M, N, ldx,
-                                  ldy, col0, cstride);
+        for (int d = 0; d < D; ++d) {
+          const int k = it + d;
+          if (k + D - 1 < iters) {
+            const int64_t rf = row_of(k + D - 1);
+            fetch_row<KIND, RECOMP>(buf[(d + D - 1) % D], x, dy, mean, rstd, rf, rf < M, N,
+                                    ldx, ldy, col0, cstride);
+          }
+          if (k < iters) {
+            RB& b = buf[d];
+            const int64_t rk = row_of(k);
+            float sxx, s2, sx_next = 0.0f, s1_next = 0.0f;
+            recompute_sums2<KIND>(b, gam, acc, rk < M, N, col0, cstride, mu, sxx, s2);
+            if (k + 1 < iters) {
+              RB& nx = buf[(d + 1) % D];
+              ln_recompute_sums1(nx, gam, acc, row_of(k + 1) < M, N, col0, cstride, sx_next,
+                                 s1_next);
+              keep_packed(nx.x);
+              keep_packed(nx.dy);
+            }
+            keep_packed(b.x);
+            keep_packed(b.dy);
+            row_sum4(sxx, s2, sx_next, s1_next, red4, phase, lane, wave, S, p);
+            const float rs = 1.0f / __builtin_sqrtf(__builtin_fmaf(sxx, inv_n, eps));
+            write_dx<KIND, RECOMP>(b, gam, acc, dx, rk, rk < M, N, ldo, inv_n, mu, rs, s1, s2,
+                                   col0, cstride);
+            mu = sx_next * inv_n;
+            s1 = s1_next;
+          }
         }
-        if (k < iters) {
-          const int64_t rk = row_of(k);
-          process_row<KIND, RECOMP>(buf[d], gam, acc, dx, red, phase, rk, rk < M, N, ldo,
-                                    inv_n, eps, col0, cstride, lane, wave, S, p);
+      }
+    } else {
+      for (int it = 0; it < iters; it += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          const int k = it + d;
+          if (k + D - 1 < iters) {
+            const int64_t rf = row_of(k + D - 1);
+            fetch_row<KIND, RECOMP>(buf[(d + D - 1) % D], x, dy, mean, rstd, rf, rf < M, N,
+                                    ldx, ldy, col0, cstride);
+          }
+          if (k < iters) {
+            const int64_t rk = row_of(k);
+            process_row<KIND, RECOMP>(buf[d], gam, acc, dx, red, phase, rk, rk < M, N, ldo,
+                                      inv_n, eps, col0, cstride, lane, wave, S, p);
+          }
         }
       }
     }
