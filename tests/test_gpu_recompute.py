@@ -139,7 +139,12 @@ def test_recompute_full_size_sampled(nb, w):
 
 @pytest.mark.parametrize("w", [W.scaled(W.RMS_BF16_16384x4096, M=1024),
                                W.scaled(W.LN_BF16_65536x8192, M=600),
-                               W.scaled(W.LN_F32_128x512, M=300, N=1000)],
+                               W.scaled(W.LN_F32_128x512, M=300, N=1000),
+                               # LayerNorm's exchanges pipelined across rows,
+                               # groups ending on inactive rows
+                               W.scaled(W.LN_BF16_65536x8192, M=2001, N=4096),
+                               # the fp16 kernel that keeps the two-exchange order
+                               W.LN_F16_1151x8192],
                          ids=lambda w: w.name)
 def test_recompute_matches_forward_statistics_bitwise(nb, w):
     """Where the backward's lane layout equals the forward's, the recomputed
