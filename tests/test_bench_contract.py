@@ -68,3 +68,19 @@ def test_committed_traffic_is_read_from_the_right_lines(name):
         assert got_f == f
     else:
         assert got_f is None
+
+
+def test_profile_summaries_pick_the_step_kernel():
+    """The trace and counter summaries compare the benchmark's kernel A (saved
+    statistics) with the events, not the recompute-mode instantiation the same
+    run also launches."""
+    is_step_kernel_a = profiling.is_step_kernel_a
+    assert is_step_kernel_a("void nb::dx_partials_kernel<1, false, nb::TBF16, 8, 2, 1, false>(a)")
+    assert is_step_kernel_a("nb::dx_partials_kernel<0, false, nb::TF16, 8, 2, 2, true>")
+    assert not is_step_kernel_a("void nb::dx_partials_kernel<1, true, nb::TBF16, 8, 2, 1, false>")
+    assert not is_step_kernel_a("nb::reduce_partials_kernel<nb::TF32>")
+    for name in ("rmsnorm_bf16_16384x4096", "layernorm_bf16_65536x8192"):
+        text = open(os.path.join(ROOT, "profiles", f"kernels_{name}.md")).read()
+        ratio = float(re.search(r"kernel A by the trace: [\d.]+ us \(events / trace = ([\d.]+)\)",
+                                text).group(1))
+        assert 0.95 < ratio < 1.05, (name, ratio)
