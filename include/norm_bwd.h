@@ -76,10 +76,12 @@ extern "C" {
  * is a multiple of 16 / element size and x, dy, gamma, dx start on 16-byte
  * boundaries; other rows use one element per lane. Wider rows (up to
  * INT32_MAX) take the wide-row path in norm_bwd_layernorm, norm_bwd_rmsnorm,
- * norm_bwd_ex (automatic groups) and the forward: a row-loop kernel streams
- * each row in chunks (one workgroup per row) for dx or y, and the column walk
- * (see norm_bwd_wgrad) forms dgamma/dbeta, with no workspace beyond the
- * recomputed statistics (4 or 8 bytes per row) in recompute mode. The
+ * norm_bwd_ex (automatic groups) and the forward: one workgroup per row
+ * computes dx or y, holding the row in its registers when it fits (aligned
+ * rows up to 65536 16-bit or 32768 fp32 elements) and otherwise streaming it
+ * in chunks, and the column walk (see norm_bwd_wgrad) forms dgamma/dbeta,
+ * with no workspace beyond the recomputed statistics (4 or 8 bytes per row)
+ * in recompute mode. The
  * explicit-plan entry points (norm_bwd_make_plan, norm_bwd_execute*) cover
  * the fused path only and return NORM_BWD_ERR_UNSUPPORTED beyond it.
  */
