@@ -165,9 +165,18 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 def _stream(stream, device) -> ctypes.c_void_p:
+    """The stream to launch on: torch's current stream of the tensors' device
+    by default. A torch stream of another device is refused (its kernels
+    would touch this device's memory from there); a raw handle (int) is the
+    caller's responsibility."""
     if stream is None:
         stream = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    if hasattr(stream, "cuda_stream"):
+        sdev = getattr(stream, "device", None)
+        if sdev is not None and torch.device(sdev) != torch.device(device):
+            raise ValueError(f"stream is on {sdev}, the tensors on {device}")
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
 
 
 def _gpu_any(t: torch.Tensor, name: str):

@@ -179,3 +179,21 @@ def test_forward_rejects(cpu_binding, over, match):
     beta = kw.pop("beta")
     with pytest.raises(ValueError, match=match):
         nb.norm_fwd_layernorm(i["x"], i["gamma"], beta, 1e-5, **kw)
+
+
+def test_stream_of_another_device_is_refused(monkeypatch):
+    """A torch stream object whose device differs from the tensors' is
+    refused before any launch."""
+    class FakeStream:
+        cuda_stream = 1234
+        device = torch.device("cuda", 1)
+
+    with pytest.raises(ValueError, match="stream is on"):
+        nb._stream(FakeStream(), torch.device("cuda", 0))
+
+    class SameStream:
+        cuda_stream = 1234
+        device = torch.device("cuda", 0)
+
+    assert nb._stream(SameStream(), torch.device("cuda", 0)).value == 1234
+    assert nb._stream(5678, torch.device("cuda", 0)).value == 5678
