@@ -6,7 +6,13 @@ Tolerances (all comparisons in fp64, oracle unrounded):
   dx plus 2^-18 * T_j (T_j below), the fp32 arithmetic bound with at most 16
   elements per lane, which only matters where the terms of dx_j cancel.
 * fp16/bf16 I/O, dx:
-  - max_j |got - ref| <= 2e-2 over the whole tensor, and
+  - |got - ref| <= 2e-2 + u * |ref| for every element, u = 2^-8 (bf16) or
+    2^-11 (fp16) the rounding of the stored value to nearest even: the 2e-2
+    bounds the computation, on top of that rounding (as for stored fp16/bf16
+    weight gradients below). A bf16 value of magnitude 8 or more is stored
+    with spacing 2^-4, so no stored value could be within 2e-2 of every exact
+    result there; where |dx| < 0.1, as in every workload here, the added term
+    is below 4e-4. And
   - per row, max_j |got - ref| <= tau * max_j |ref| + 2^-16 * max_j T_j with
     tau = 2^-7 (bf16) or 2^-10 (fp16). Rounding fp32 to bf16 (fp16) to nearest
     even moves a value by at most 2^-8 (2^-11) of itself, so tau is twice the
@@ -121,8 +127,10 @@ def check_dx(io_dtype, got, ref, what="dx", scale=None, coef32=2.0 ** -18):
         return {"max_abs": float(err.max())}
     if not np.all(np.isfinite(g)):
         _fail(what + " (non-finite)", g, r, np.unravel_index(np.argmax(~np.isfinite(g)), g.shape))
-    if err.max() > 2e-2:
-        _fail(what + " max-abs 2e-2", g, r, np.unravel_index(np.argmax(err), err.shape))
+    lim_abs = 2e-2 + OUT_ROUND[io_dtype] * np.abs(r)
+    if not np.all(err <= lim_abs):
+        _fail(what + " max-abs 2e-2 (+ output rounding)", g, r,
+              np.unravel_index(np.argmax(err - lim_abs), err.shape))
     row_err = err.reshape(err.shape[0], -1).max(axis=1)
     row_ref = np.abs(r).reshape(r.shape[0], -1).max(axis=1)
     row_lim = TAU[io_dtype] * row_ref

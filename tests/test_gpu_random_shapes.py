@@ -1,0 +1,111 @@
+"""A seeded sweep of random problem shapes against the oracle.
+
+The targeted parity tests pick their shapes; this sweep draws them: kind,
+I/O dtype, N (biased towards widths around vector, chunk and path limits,
+but also arbitrary), M (including 1 and a few rows), dbeta on or off, saved
+or recomputed statistics, contiguous or row-strided storage, and the
+weight-gradient dtype. Every case runs through the public entry points
+(norm_bwd_layernorm / norm_bwd_rmsnorm, or norm_bwd_ex for strides) and is
+compared with the fp64 oracle under the same tolerances as the other parity
+tests. The draw is fixed, so a failure names a reproducible case.
+"""
+
+from __future__ import annotations
+
+import random
+
+import pytest
+import torch
+
+import oracle
+import parity
+from inputs import backward_inputs
+from rmsnorm_backward_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = (torch.float32, torch.float16, torch.bfloat16)
+EDGE_N = [1, 2, 3, 7, 8, 9, 15, 16, 17, 63, 64, 65, 255, 256, 257, 511, 512, 768, 1000, 1023,
+          1024, 1025, 2047, 2048, 4095, 4096, 4097, 8191, 8192, 8193, 16383, 16384, 16385,
+          20000, 32767, 32768, 32769]
+
+
+def _cases(n=48, seed=20261202):
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        kind = rng.choice(("layernorm", "rmsnorm"))
+        dt = rng.choice(DTYPES)
+        N = rng.choice(EDGE_N) if rng.random() < 0.7 else rng.randint(1, 40000)
+        if dt == torch.float32:
+            N = min(N, 24000)
+        M = rng.choice((1, 2, 3, 5, 17)) if rng.random() < 0.3 else rng.randint(1, 300)
+        M = max(1, min(M, 2_000_000 // max(N, 1)))     # keep the fp64 oracle quick
+        with_db = kind == "layernorm" if rng.random() < 0.6 else rng.random() < 0.5
+        recompute = rng.random() < 0.3
+        pad = rng.choice((0, 0, 0, 8, 24, 5))        # row padding in elements (0 = contiguous)
+        wg = torch.float32 if rng.random() < 0.75 else dt
+        out.append((i, kind, dt, M, N, with_db, recompute, pad, wg))
+    return out
+
+
+def _strided(t, pad):
+    M, N = t.shape
+    buf = torch.zeros(M * (N + pad), dtype=t.dtype, device="cuda")
+    v = buf.view(M, N + pad)[:, :N]
+    v.copy_(t.cuda())
+    return v
+
+
+@pytest.fixture(scope="module")
+def nb():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import rmsnorm_backward_amd as nbmod
+    nbmod.load_library()
+    return nbmod
+
+
+@pytest.mark.parametrize("case", _cases(), ids=lambda c: "-".join(str(v).replace("torch.", "")
+                                                                   for v in c))
+def test_random_shape(nb, case):
+    i, kind, dt, M, N, with_db, recompute, pad, wg = case
+    base = W.LN_F32_128x512 if kind == "layernorm" else W.RMS_F32_128x512
+    w = W.scaled(base, M=M, N=N, io_dtype=dt, wgrad_dtype=wg, seed=9000 + i)
+    inp = backward_inputs(w)
+    x = _strided(inp["x"], pad) if pad else inp["x"].cuda()
+    dy = _strided(inp["dy"], pad) if pad else inp["dy"].cuda()
+    g = inp["gamma"].cuda()
+    mean = None if (recompute or kind == "rmsnorm") else inp["mean"].cuda()
+    rstd = None if recompute else inp["rstd"].cuda()
+    if pad:
+        dx, dg, db = nb.norm_bwd_ex(kind, x, dy, g, mean, rstd, w.eps, wgrad_dtype=wg,
+                                    with_dbeta=with_db)
+    elif kind == "layernorm":
+        dx, dg, db = nb.norm_bwd_layernorm(x, dy, g, mean, rstd, w.eps, wgrad_dtype=wg,
+                                           with_dbeta=with_db)
+    else:
+        dx, dg, db = nb.norm_bwd_rmsnorm(x, dy, g, rstd, w.eps, wgrad_dtype=wg,
+                                         with_dbeta=with_db)
+    torch.cuda.synchronize()
+    dx, dg = dx.cpu(), dg.cpu()
+    assert (db is not None) == with_db
+    if recompute:
+        m64, r64 = oracle.fwd_stats(kind, inp["x"], w.eps)          # fp64, not rounded
+        rdx = oracle.bwd_dx(kind, inp["x"], inp["dy"], inp["gamma"], m64, r64)
+        t_dx, t_dg = parity.recompute_terms(kind, inp["x"], inp["dy"], inp["gamma"], m64, r64)
+        parity.check_dx(dt, dx, rdx, scale=t_dx, coef32=2.0 ** -16)
+        rdg, rdb = oracle.bwd_wgrad(kind, inp["x"], inp["dy"], m64, r64)
+        extra = 2.0 ** -16 * t_dg
+    else:
+        rdx, rdg, rdb = oracle.bwd(kind, inp["x"], inp["dy"], inp["gamma"], inp.get("mean"),
+                                   inp["rstd"])
+        scale = parity.dx_term_scale(kind, inp["x"], inp["dy"], inp["gamma"], inp.get("mean"),
+                                     inp["rstd"])
+        parity.check_dx(dt, dx, rdx, scale=scale)
+        extra = None
+    # passed in their own dtype, the weight gradients' output rounding is
+    # part of the bound
+    assert dg.dtype == wg
+    parity.check_wgrad(dt, dg, rdg, extra=extra)
+    if with_db:
+        parity.check_wgrad(dt, db.cpu(), rdb, "dbeta")
