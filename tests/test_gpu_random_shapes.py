@@ -1,4 +1,5 @@
-"""A seeded sweep of random problem shapes against the oracle.
+"""Seeded sweeps of random problem shapes against the oracle: the backward,
+the forward and the column walk.
 
 The targeted parity tests pick their shapes; this sweep draws them: kind,
 I/O dtype, N (biased towards widths around vector, chunk and path limits,
@@ -7,7 +8,9 @@ or recomputed statistics, contiguous or row-strided storage, and the
 weight-gradient dtype. Every case runs through the public entry points
 (norm_bwd_layernorm / norm_bwd_rmsnorm, or norm_bwd_ex for strides) and is
 compared with the fp64 oracle under the same tolerances as the other parity
-tests. The draw is fixed, so a failure names a reproducible case.
+tests. The draw is fixed, so a failure names a reproducible case. The forward
+(beta on or off, statistics requested or not) and norm_bwd_wgrad
+(accumulating or not) get sweeps of their own.
 """
 
 from __future__ import annotations
@@ -30,7 +33,7 @@ EDGE_N = [1, 2, 3, 7, 8, 9, 15, 16, 17, 63, 64, 65, 255, 256, 257, 511, 512, 768
           20000, 32767, 32768, 32769]
 
 
-def _cases(n=48, seed=20261202):
+def _cases(n=200, seed=20261202):
     rng = random.Random(seed)
     out = []
     for i in range(n):
@@ -109,3 +112,94 @@ def test_random_shape(nb, case):
     parity.check_wgrad(dt, dg, rdg, extra=extra)
     if with_db:
         parity.check_wgrad(dt, db.cpu(), rdb, "dbeta")
+
+
+def _fwd_cases(n=80, seed=1202):
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        kind = rng.choice(("layernorm", "rmsnorm"))
+        dt = rng.choice(DTYPES)
+        N = rng.choice(EDGE_N + [40000, 65536, 65537]) if rng.random() < 0.7 \
+            else rng.randint(1, 70000)
+        M = rng.choice((1, 2, 3, 7)) if rng.random() < 0.3 else rng.randint(1, 300)
+        M = max(1, min(M, 2_000_000 // max(N, 1)))
+        beta = kind == "layernorm" and rng.random() < 0.6
+        stats = rng.random() < 0.8
+        out.append((i, kind, dt, M, N, beta, stats))
+    return out
+
+
+@pytest.mark.parametrize("case", _fwd_cases(), ids=lambda c: "-".join(
+    str(v).replace("torch.", "") for v in c))
+def test_random_forward(nb, case):
+    """y and the statistics of the forward (fused, register-held or streamed
+    wide rows) against the oracle's forward."""
+    i, kind, dt, M, N, with_beta, stats = case
+    base = W.LN_F32_128x512 if kind == "layernorm" else W.RMS_F32_128x512
+    w = W.scaled(base, M=M, N=N, io_dtype=dt, seed=7000 + i)
+    inp = W.make_inputs(w)
+    x, gamma = inp["x"], inp["gamma"]
+    beta = None
+    if with_beta:
+        beta = torch.rand(N, generator=torch.Generator().manual_seed(i)).to(dt)
+    if kind == "layernorm":
+        y, mean, rstd = nb.norm_fwd_layernorm(x.cuda(), gamma.cuda(),
+                                              None if beta is None else beta.cuda(), w.eps,
+                                              want_stats=stats)
+    else:
+        y, rstd = nb.norm_fwd_rmsnorm(x.cuda(), gamma.cuda(), w.eps, want_stats=stats)
+        mean = None
+    torch.cuda.synchronize()
+    ry, rm, rr = oracle.fwd(kind, x, gamma, beta, w.eps)
+    if stats:
+        parity.check_forward(dt, kind, x, gamma, beta, y.cpu(),
+                             None if mean is None else mean.cpu(), rstd.cpu(), ry, rm, rr)
+    else:
+        assert rstd is None and mean is None
+        parity.check_forward(dt, kind, x, gamma, beta, y.cpu(), None, None, ry, rm, rr)
+
+
+def _wgrad_cases(n=60, seed=2026):
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        kind = rng.choice(("layernorm", "rmsnorm"))
+        dt = rng.choice(DTYPES)
+        N = rng.choice(EDGE_N + [40000, 65537]) if rng.random() < 0.7 else rng.randint(1, 70000)
+        M = rng.choice((1, 2, 5)) if rng.random() < 0.3 else rng.randint(1, 400)
+        M = max(1, min(M, 2_000_000 // max(N, 1)))
+        with_db = rng.random() < 0.5
+        acc = rng.random() < 0.3
+        wg = torch.float32 if rng.random() < 0.75 else dt
+        out.append((i, kind, dt, M, N, with_db, acc, wg))
+    return out
+
+
+@pytest.mark.parametrize("case", _wgrad_cases(), ids=lambda c: "-".join(
+    str(v).replace("torch.", "") for v in c))
+def test_random_wgrad(nb, case):
+    """dgamma/dbeta by the column walk (norm_bwd_wgrad), plain or accumulated
+    into an existing fp32 buffer, against the oracle."""
+    i, kind, dt, M, N, with_db, acc, wg = case
+    if acc:
+        wg = torch.float32
+    base = W.LN_F32_128x512 if kind == "layernorm" else W.RMS_F32_128x512
+    w = W.scaled(base, M=M, N=N, io_dtype=dt, wgrad_dtype=wg, seed=8000 + i)
+    inp = backward_inputs(w)
+    mean = inp["mean"].cuda() if kind == "layernorm" else None
+    old = torch.randn(N, generator=torch.Generator().manual_seed(i)) if acc else None
+    dg = old.clone().cuda() if acc else None
+    db = old.clone().cuda() if (acc and with_db) else None
+    dg, db = nb.norm_bwd_wgrad(kind, inp["x"].cuda(), inp["dy"].cuda(), mean,
+                               inp["rstd"].cuda(), wgrad_dtype=wg, dgamma=dg, dbeta=db,
+                               with_dbeta=with_db, accumulate=acc)
+    torch.cuda.synchronize()
+    rdg, rdb = oracle.bwd_wgrad(kind, inp["x"], inp["dy"], inp.get("mean"), inp["rstd"])
+    got_g = dg.cpu() - old if acc else dg.cpu()
+    extra = 2.0 ** -24 * old.abs() if acc else None
+    parity.check_wgrad(dt, got_g, rdg, extra=extra)
+    assert (db is not None) == with_db
+    if with_db:
+        got_b = db.cpu() - old if acc else db.cpu()
+        parity.check_wgrad(dt, got_b, rdb, "dbeta", extra=extra)
