@@ -199,9 +199,50 @@ def cpu_baseline(w, inp):
               f"first {rows} of {w.M} rows x {w.N}") + \
         f", fp64 passes (dx, dgamma{', dbeta' if w.kind == 'layernorm' else ''}) repeated " \
         f"{reps}x, {total:.1f} s total, mean per pass"
-    return {"value": round(ws.algorithmic_bytes() / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "sample": sample, "seconds_per_pass": round(dt, 4),
-            "cpu_model": cpu_model()}
+    out = {"value": round(ws.algorithmic_bytes() / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+           "kind": "oracle", "sample": sample, "seconds_per_pass": round(dt, 4),
+           "cpu_model": cpu_model()}
+    out["all_cores"] = cpu_baseline_threads(o, w, x, dy, gamma, mean, rstd,
+                                            ws.algorithmic_bytes())
+    return out
+
+
+def cpu_baseline_threads(o, w, x, dy, gamma, mean, rstd, nbytes, seconds=5.0):
+    """The same, unchanged oracle run on every core this process may use (at
+    most 16): each thread takes a contiguous slice of the sample's rows (the
+    C calls release the interpreter lock), and the slices' dgamma (dbeta)
+    sums are added in slice order. Reported beside the one-thread figure."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except AttributeError:
+        threads = os.cpu_count() or 1
+    threads = max(1, min(threads, 16, x.shape[0]))
+    bounds = np.linspace(0, x.shape[0], threads + 1).astype(int)
+    want_db = w.kind == "layernorm"
+
+    def part(i):
+        lo, hi = bounds[i], bounds[i + 1]
+        return o.bwd(w.kind, x[lo:hi], dy[lo:hi], gamma,
+                     None if mean is None else mean[lo:hi], rstd[lo:hi], want_dbeta=want_db)
+
+    reps, total = 0, 0.0
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while reps < 200 and (total < seconds or reps < 1):
+            t0 = time.perf_counter()
+            res = list(ex.map(part, range(threads)))
+            for k in (1, 2) if want_db else (1,):
+                acc = res[0][k].copy()
+                for r in res[1:]:
+                    acc += r[k]
+            total += time.perf_counter() - t0
+            reps += 1
+    dt = total / reps
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "seconds_per_pass": round(dt, 4), "reps": reps}
 
 
 def cpu_model() -> str:

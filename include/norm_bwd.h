@@ -269,10 +269,12 @@ typedef struct norm_bwd_plan {
 
 /*
  * Fill *plan for (kind, M, N, io_dtype, with_dbeta). groups = 0 chooses the
- * automatic group count (2048 / (waves per workgroup), at most ceil(M / 4):
- * a function of the problem only, never of the device); groups > 0 asks for
- * that many row groups,
- * clamped to M so that no group is empty. The plan
+ * automatic group count: 2048 waves in flight divided by the waves per
+ * workgroup, at most ceil(M / 4), and above 256 rounded down to a multiple of
+ * 256 -- a function of the problem only, never of the device (the entry points
+ * that recompute LayerNorm statistics aim at 4096 waves instead). groups > 0
+ * asks for that many row groups, clamped to M so that no group is empty. A
+ * plan is for saved statistics. The plan
  * assumes 16-byte aligned base pointers; norm_bwd_execute rejects a plan
  * whose vec the pointers do not allow. Host-only. Returns a status code.
  */

@@ -178,8 +178,9 @@ int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype, bool recompute
   if (M <= 0) return 0;
   // Enough workgroups for about kTargetWaves waves in flight (8 per compute
   // unit on a 256-CU part), never fewer than kMinRowsPerGroup rows per
-  // group, above kGroupQuantum a multiple of it. The geometry is itself a function of (kind, N, io_dtype), so the
-  // group count depends on the problem only, never on the device.
+  // group, above kGroupQuantum a multiple of it. The geometry is itself a
+  // function of (kind, N, io_dtype), so the group count depends on the
+  // problem only, never on the device.
   norm_bwd_plan_t g;
   const char* why = nullptr;
   int waves = 8;

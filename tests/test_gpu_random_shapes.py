@@ -5,8 +5,10 @@ The targeted parity tests pick their shapes; this sweep draws them: kind,
 I/O dtype, N (biased towards widths around vector, chunk and path limits,
 but also arbitrary), M (including 1 and a few rows), dbeta on or off, saved
 or recomputed statistics, contiguous or row-strided storage, and the
-weight-gradient dtype. Every case runs through the public entry points
-(norm_bwd_layernorm / norm_bwd_rmsnorm, or norm_bwd_ex for strides) and is
+weight-gradient dtype; strided cases also draw accumulation into existing
+fp32 weight gradients and explicit group counts. Every case runs through the
+public entry points (norm_bwd_layernorm / norm_bwd_rmsnorm, or norm_bwd_ex
+for strides) and is
 compared with the fp64 oracle under the same tolerances as the other parity
 tests. The draw is fixed, so a failure names a reproducible case. The forward
 (beta on or off, statistics requested or not) and norm_bwd_wgrad
@@ -48,7 +50,10 @@ def _cases(n=200, seed=20261202):
         recompute = rng.random() < 0.3
         pad = rng.choice((0, 0, 0, 8, 24, 5))        # row padding in elements (0 = contiguous)
         wg = torch.float32 if rng.random() < 0.75 else dt
-        out.append((i, kind, dt, M, N, with_db, recompute, pad, wg))
+        # norm_bwd_ex only (pad > 0): accumulate into fp32 buffers, groups
+        acc = pad > 0 and rng.random() < 0.3
+        groups = rng.choice((1, 2, 7, 64, 300, 1000)) if pad > 0 and rng.random() < 0.3 else 0
+        out.append((i, kind, dt, M, N, with_db, recompute, pad, wg, acc, groups))
     return out
 
 
@@ -71,7 +76,13 @@ def nb():
 @pytest.mark.parametrize("case", _cases(), ids=lambda c: "-".join(str(v).replace("torch.", "")
                                                                    for v in c))
 def test_random_shape(nb, case):
-    i, kind, dt, M, N, with_db, recompute, pad, wg = case
+    i, kind, dt, M, N, with_db, recompute, pad, wg, acc, groups = case
+    if acc:
+        wg = torch.float32
+    if N > 8192:
+        # explicit groups are for rows the fused path holds at any row
+        # alignment (NORM_BWD_MAX_N_UNALIGNED); wider ones are UNSUPPORTED
+        groups = 0
     base = W.LN_F32_128x512 if kind == "layernorm" else W.RMS_F32_128x512
     w = W.scaled(base, M=M, N=N, io_dtype=dt, wgrad_dtype=wg, seed=9000 + i)
     inp = backward_inputs(w)
@@ -80,9 +91,13 @@ def test_random_shape(nb, case):
     g = inp["gamma"].cuda()
     mean = None if (recompute or kind == "rmsnorm") else inp["mean"].cuda()
     rstd = None if recompute else inp["rstd"].cuda()
+    old = torch.randn(N, generator=torch.Generator().manual_seed(i)) if acc else None
     if pad:
+        dg0 = old.clone().cuda() if acc else None
+        db0 = old.clone().cuda() if (acc and with_db) else None
         dx, dg, db = nb.norm_bwd_ex(kind, x, dy, g, mean, rstd, w.eps, wgrad_dtype=wg,
-                                    with_dbeta=with_db)
+                                    with_dbeta=with_db, dgamma=dg0, dbeta=db0,
+                                    accumulate=acc, groups=groups)
     elif kind == "layernorm":
         dx, dg, db = nb.norm_bwd_layernorm(x, dy, g, mean, rstd, w.eps, wgrad_dtype=wg,
                                            with_dbeta=with_db)
@@ -107,11 +122,21 @@ def test_random_shape(nb, case):
         parity.check_dx(dt, dx, rdx, scale=scale)
         extra = None
     # passed in their own dtype, the weight gradients' output rounding is
-    # part of the bound
+    # part of the bound; accumulated ones are compared as (new - old), with
+    # the fp32 rounding of old + sum
     assert dg.dtype == wg
-    parity.check_wgrad(dt, dg, rdg, extra=extra)
-    if with_db:
-        parity.check_wgrad(dt, db.cpu(), rdb, "dbeta")
+    if acc:
+        old64 = old.double().abs().numpy()
+        a_extra = 2.0 ** -24 * (old64 + abs(parity.f64(rdg)))
+        parity.check_wgrad(dt, dg - old, rdg,
+                           extra=a_extra if extra is None else a_extra + parity.f64(extra))
+        if with_db:
+            b_extra = 2.0 ** -24 * (old64 + abs(parity.f64(rdb)))
+            parity.check_wgrad(dt, db.cpu() - old, rdb, "dbeta", extra=b_extra)
+    else:
+        parity.check_wgrad(dt, dg, rdg, extra=extra)
+        if with_db:
+            parity.check_wgrad(dt, db.cpu(), rdb, "dbeta")
 
 
 def _fwd_cases(n=80, seed=1202):
