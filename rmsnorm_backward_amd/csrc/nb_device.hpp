@@ -239,6 +239,18 @@ constexpr bool pipeline_ln_recompute() {
          !(std::is_same<Tg, TF16>::value && VEC * C == 16 && NACC == 2);
 }
 
+// Whether kernel A runs its steady-state loop (every row and every lane
+// chunk in bounds, so no per-lane or per-row conditions). Kernels whose row
+// sits in 16-byte vectors with at most 32 elements per lane, with saved
+// statistics. Left out, because the extra loop made them spill under their
+// register budget: recompute mode, one element per lane, 64 elements per
+// lane, and fp16 rows of 16 elements per lane with both gradients.
+template <bool RECOMP, class Tg, int VEC, int C, int NACC>
+constexpr bool steady_loop() {
+  return !RECOMP && VEC > 1 && VEC * C <= 32 &&
+         !(std::is_same<Tg, TF16>::value && VEC * C == 16 && NACC == 2);
+}
+
 // ---------------------------------------------------------------- kernel A
 // Turn per-lane partial sums into row sums: the wave butterfly, then, when
 // S > 1 waves share the row, an exchange through LDS in which the S wave sums
@@ -336,7 +348,7 @@ struct RowBuf {
 // for a lane's chunks past the row's end; process_row never reads those
 // registers (it skips exactly the same cases). With RECOMP the statistics are
 // not loaded: process_row computes them from x.
-template <int KIND, bool RECOMP, class Tg, int VEC, int C>
+template <int KIND, bool RECOMP, bool ALL, class Tg, int VEC, int C>
 __device__ __forceinline__ void fetch_row(RowBuf<Tg, VEC, C>& b, const char* __restrict__ x,
                                           const char* __restrict__ dy,
                                           const float* __restrict__ mean,
@@ -344,7 +356,7 @@ __device__ __forceinline__ void fetch_row(RowBuf<Tg, VEC, C>& b, const char* __r
                                           int N, int64_t ldx, int64_t ldy, int col0,
                                           int cstride) {
   constexpr int EB = Tg::kBytes;
-  if (active) {
+  if (ALL || active) {
     if constexpr (!RECOMP) {
       const int64_t rz = r + opaque_lane_zero();
       b.rs = rstd[rz];
@@ -354,7 +366,7 @@ __device__ __forceinline__ void fetch_row(RowBuf<Tg, VEC, C>& b, const char* __r
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int col = col0 + c * cstride;
-      if (col < N) {
+      if (ALL || col < N) {
         b.x[c].load_stream(x + (xb + col) * EB);
         b.dy[c].load_stream(dy + (yb + col) * EB);
       }
@@ -381,7 +393,7 @@ __device__ __forceinline__ void fetch_row(RowBuf<Tg, VEC, C>& b, const char* __r
 // + eps). The dgamma terms, which need rstd, are accumulated in pass 2.
 // LayerNorm recompute, first pass over a row held in registers: sum(x) and
 // sum(dy * gamma), and the row's dbeta terms into the accumulators.
-template <class Tg, int VEC, int C, int NACC>
+template <bool ALL = false, class Tg, int VEC, int C, int NACC>
 __device__ __forceinline__ void ln_recompute_sums1(const RowBuf<Tg, VEC, C>& b,
                                                    const float (&gam)[C][VEC],
                                                    float (&acc)[NACC][C][VEC], bool active,
@@ -389,10 +401,10 @@ __device__ __forceinline__ void ln_recompute_sums1(const RowBuf<Tg, VEC, C>& b,
                                                    float& s1) {
   sx = 0.0f;
   s1 = 0.0f;
-  if (active) {
+  if (ALL || active) {
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      if (col0 + c * cstride < N) {
+      if (ALL || col0 + c * cstride < N) {
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
           const float dyv = b.dy[c].get(v);
@@ -407,7 +419,7 @@ __device__ __forceinline__ void ln_recompute_sums1(const RowBuf<Tg, VEC, C>& b,
 
 // Recompute, second pass: sum(xc^2) and sum(dyhat * xc) with xc = x - mean
 // (RMSNorm: mean 0, and its dbeta terms here, as it has no first pass).
-template <int KIND, class Tg, int VEC, int C, int NACC>
+template <int KIND, bool ALL = false, class Tg, int VEC, int C, int NACC>
 __device__ __forceinline__ void recompute_sums2(const RowBuf<Tg, VEC, C>& b,
                                                 const float (&gam)[C][VEC],
                                                 float (&acc)[NACC][C][VEC], bool active, int N,
@@ -415,10 +427,10 @@ __device__ __forceinline__ void recompute_sums2(const RowBuf<Tg, VEC, C>& b,
                                                 float& s2) {
   sxx = 0.0f;
   s2 = 0.0f;
-  if (active) {
+  if (ALL || active) {
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      if (col0 + c * cstride < N) {
+      if (ALL || col0 + c * cstride < N) {
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
           const float xc = b.x[c].get(v) - mu;
@@ -436,14 +448,14 @@ __device__ __forceinline__ void recompute_sums2(const RowBuf<Tg, VEC, C>& b,
 //   dx = dyhat * rstd + xc * c2 + c1, c2 = -rstd^2 * mean(dyhat * xhat),
 //   c1 = -rstd * s1 / N (LayerNorm), and in recompute mode the row's dgamma
 // terms, which need rstd.
-template <int KIND, bool RECOMP, class Tg, int VEC, int C, int NACC>
+template <int KIND, bool RECOMP, bool ALL = false, class Tg, int VEC, int C, int NACC>
 __device__ __forceinline__ void write_dx(const RowBuf<Tg, VEC, C>& b, const float (&gam)[C][VEC],
                                          float (&acc)[NACC][C][VEC], char* __restrict__ dx,
                                          int64_t r, bool active, int N, int64_t ldo, float inv_n,
                                          float mu, float rs, float s1, float s2, int col0,
                                          int cstride) {
   constexpr int EB = Tg::kBytes;
-  if (active) {
+  if (ALL || active) {
     const float m2 = s2 * inv_n * rs;  // mean_j(dyhat * xhat)
     const float c2 = -(rs * rs) * m2;
     const float c1 = (KIND == kLayerNorm) ? -rs * (s1 * inv_n) : 0.0f;
@@ -451,7 +463,7 @@ __device__ __forceinline__ void write_dx(const RowBuf<Tg, VEC, C>& b, const floa
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int col = col0 + c * cstride;
-      if (col < N) {
+      if (ALL || col < N) {
         float o[VEC];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
@@ -470,7 +482,7 @@ __device__ __forceinline__ void write_dx(const RowBuf<Tg, VEC, C>& b, const floa
   }
 }
 
-template <int KIND, bool RECOMP, class Tg, int VEC, int C, int NACC>
+template <int KIND, bool RECOMP, bool ALL = false, class Tg, int VEC, int C, int NACC>
 __device__ __forceinline__ void process_row(RowBuf<Tg, VEC, C>& b, const float (&gam)[C][VEC],
                                             float (&acc)[NACC][C][VEC], char* __restrict__ dx,
                                             float (*red)[kMaxWaves][2], int& phase, int64_t r,
@@ -482,10 +494,10 @@ __device__ __forceinline__ void process_row(RowBuf<Tg, VEC, C>& b, const float (
   if constexpr (!RECOMP) {
     mu = b.mu;
     rs = b.rs;
-    if (active) {
+    if (ALL || active) {
 #pragma unroll
       for (int c = 0; c < C; ++c) {
-        if (col0 + c * cstride < N) {
+        if (ALL || col0 + c * cstride < N) {
 #pragma unroll
           for (int v = 0; v < VEC; ++v) {
             const float xc = b.x[c].get(v) - mu;
@@ -507,21 +519,21 @@ __device__ __forceinline__ void process_row(RowBuf<Tg, VEC, C>& b, const float (
     mu = 0.0f;
     if constexpr (KIND == kLayerNorm) {
       float sx;
-      ln_recompute_sums1(b, gam, acc, active, N, col0, cstride, sx, s1);
+      ln_recompute_sums1<ALL>(b, gam, acc, active, N, col0, cstride, sx, s1);
       keep_packed(b.x);
       keep_packed(b.dy);
       row_sum2<true>(sx, s1, red, phase, lane, wave, S, p);
       mu = sx * inv_n;
     }
     float sxx;
-    recompute_sums2<KIND>(b, gam, acc, active, N, col0, cstride, mu, sxx, s2);
+    recompute_sums2<KIND, ALL>(b, gam, acc, active, N, col0, cstride, mu, sxx, s2);
     keep_packed(b.x);
     keep_packed(b.dy);
     row_sum2<true>(sxx, s2, red, phase, lane, wave, S, p);
     rs = 1.0f / __builtin_sqrtf(__builtin_fmaf(sxx, inv_n, eps));
   }
-  write_dx<KIND, RECOMP>(b, gam, acc, dx, r, active, N, ldo, inv_n, mu, rs, s1, s2, col0,
-                         cstride);
+  write_dx<KIND, RECOMP, ALL>(b, gam, acc, dx, r, active, N, ldo, inv_n, mu, rs, s1, s2, col0,
+                              cstride);
 }
 
 // WSNT: the partial rows are stored non-temporally (chosen for large
@@ -586,12 +598,40 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
     // while it computes.
     constexpr int D = prefetch_depth<Tg, VEC, C>();
     RB buf[D];
+    // Steady state: when the lanes cover the row exactly and the group has
+    // enough iterations in which every row-lane has a row, those iterations
+    // run through a loop with no per-lane or per-row conditions. Every load
+    // and store then issues on every path, so the compiler can wait for
+    // exactly the row it needs (vmcnt counts the loads issued since) instead
+    // of draining all loads in flight. The general loop below takes the
+    // iterations that remain, from the same ring state.
+    const int kfull = (int)(rows / P);  // iterations whose P rows all exist
+    int it0 = 0;
+    if (steady_loop<RECOMP, Tg, VEC, C, NACC>() && N == C * cstride && kfull >= 2 * D - 1) {
 #pragma unroll
-    for (int k = 0; k < D - 1; ++k) {
-      if (k < iters) {
-        const int64_t rk = row_of(k);
-        fetch_row<KIND, RECOMP>(buf[k], x, dy, mean, rstd, rk, rk < M, N, ldx, ldy, col0,
-                                cstride);
+      for (int k = 0; k < D - 1; ++k)
+        fetch_row<KIND, RECOMP, true>(buf[k], x, dy, mean, rstd, row_of(k), true, N, ldx, ldy,
+                                      col0, cstride);
+      if constexpr (steady_loop<RECOMP, Tg, VEC, C, NACC>()) {
+        for (; it0 + 2 * D - 2 < kfull; it0 += D) {
+#pragma unroll
+          for (int d = 0; d < D; ++d) {
+            const int k = it0 + d;
+            fetch_row<KIND, RECOMP, true>(buf[(d + D - 1) % D], x, dy, mean, rstd,
+                                          row_of(k + D - 1), true, N, ldx, ldy, col0, cstride);
+            process_row<KIND, RECOMP, true>(buf[d], gam, acc, dx, red, phase, row_of(k), true, N,
+                                            ldo, inv_n, eps, col0, cstride, lane, wave, S, p);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < D - 1; ++k) {
+        if (k < iters) {
+          const int64_t rk = row_of(k);
+          fetch_row<KIND, RECOMP, false>(buf[k], x, dy, mean, rstd, rk, rk < M, N, ldx, ldy,
+                                         col0, cstride);
+        }
       }
     }
     if constexpr (RECOMP && KIND == kLayerNorm && pipeline_ln_recompute<Tg, VEC, C, NACC>()) {
@@ -619,7 +659,7 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
           const int k = it + d;
           if (k + D - 1 < iters) {
             const int64_t rf = row_of(k + D - 1);
-            fetch_row<KIND, RECOMP>(buf[(d + D - 1) % D], x, dy, mean, rstd, rf, rf < M, N,
+            fetch_row<KIND, RECOMP, false>(buf[(d + D - 1) % D], x, dy, mean, rstd, rf, rf < M, N,
                                     ldx, ldy, col0, cstride);
           }
           if (k < iters) {
@@ -646,13 +686,13 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
         }
       }
     } else {
-      for (int it = 0; it < iters; it += D) {
+      for (int it = it0; it < iters; it += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
           const int k = it + d;
           if (k + D - 1 < iters) {
             const int64_t rf = row_of(k + D - 1);
-            fetch_row<KIND, RECOMP>(buf[(d + D - 1) % D], x, dy, mean, rstd, rf, rf < M, N,
+            fetch_row<KIND, RECOMP, false>(buf[(d + D - 1) % D], x, dy, mean, rstd, rf, rf < M, N,
                                     ldx, ldy, col0, cstride);
           }
           if (k < iters) {
