@@ -241,13 +241,14 @@ constexpr bool pipeline_ln_recompute() {
 
 // Whether kernel A runs its steady-state loop (every row and every lane
 // chunk in bounds, so no per-lane or per-row conditions). Kernels whose row
-// sits in 16-byte vectors with at most 32 elements per lane, with saved
-// statistics. Left out, because the extra loop made them spill under their
-// register budget: recompute mode, one element per lane, 64 elements per
-// lane, and fp16 rows of 16 elements per lane with both gradients.
+// sits in 16-byte vectors: with saved statistics up to 32 elements per lane,
+// in recompute mode one vector per operand per lane. Left out, because the
+// extra loop made them spill under their register budget: one element per
+// lane, 64 elements per lane, fp16 rows of 16 elements per lane with both
+// gradients, and recompute mode with more than 16 bytes per operand.
 template <bool RECOMP, class Tg, int VEC, int C, int NACC>
 constexpr bool steady_loop() {
-  return !RECOMP && VEC > 1 && VEC * C <= 32 &&
+  return VEC > 1 && VEC * C <= 32 && (!RECOMP || VEC * C * Tg::kBytes <= 16) &&
          !(std::is_same<Tg, TF16>::value && VEC * C == 16 && NACC == 2);
 }
 
@@ -607,12 +608,17 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
     // iterations that remain, from the same ring state.
     const int kfull = (int)(rows / P);  // iterations whose P rows all exist
     int it0 = 0;
-    if (steady_loop<RECOMP, Tg, VEC, C, NACC>() && N == C * cstride && kfull >= 2 * D - 1) {
+    constexpr bool kPipelined =
+        RECOMP && KIND == kLayerNorm && pipeline_ln_recompute<Tg, VEC, C, NACC>();
+    const bool steady =
+        steady_loop<RECOMP, Tg, VEC, C, NACC>() && N == C * cstride && kfull >= 2 * D - 1;
+    if (steady) {
 #pragma unroll
       for (int k = 0; k < D - 1; ++k)
         fetch_row<KIND, RECOMP, true>(buf[k], x, dy, mean, rstd, row_of(k), true, N, ldx, ldy,
                                       col0, cstride);
-      if constexpr (steady_loop<RECOMP, Tg, VEC, C, NACC>()) {
+      // (the pipelined LayerNorm recompute loop runs its own steady state)
+      if constexpr (steady_loop<RECOMP, Tg, VEC, C, NACC>() && !kPipelined) {
         for (; it0 + 2 * D - 2 < kfull; it0 += D) {
 #pragma unroll
           for (int d = 0; d < D; ++d) {
@@ -634,7 +640,7 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
         }
       }
     }
-    if constexpr (RECOMP && KIND == kLayerNorm && pipeline_ln_recompute<Tg, VEC, C, NACC>()) {
+    if constexpr (kPipelined) {
       // LayerNorm recompute needs two exchanges per row (sum x, then the
       // squared deviations from the mean). Pipelined across rows, step k
       // exchanges row k's second pair of sums together with row k + 1's
@@ -653,7 +659,44 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
         row_sum2<true>(sx, s1, red, phase, lane, wave, S, p);
         mu = sx * inv_n;
       }
-      for (int it = 0; it < iters; it += D) {
+      // Step k: row k's second pair of sums and row k + 1's first pair in
+      // one exchange, then row k's dx. `all`: as in the steady-state loop.
+      auto step = [&](auto all, int d, int k) {
+        constexpr bool ALL = decltype(all)::value;
+        RB& b = buf[d];
+        const int64_t rk = row_of(k);
+        float sxx, s2, sx_next = 0.0f, s1_next = 0.0f;
+        recompute_sums2<KIND, ALL>(b, gam, acc, rk < M, N, col0, cstride, mu, sxx, s2);
+        if (ALL || k + 1 < iters) {
+          RB& nx = buf[(d + 1) % D];
+          ln_recompute_sums1<ALL>(nx, gam, acc, row_of(k + 1) < M, N, col0, cstride, sx_next,
+                                  s1_next);
+          keep_packed(nx.x);
+          keep_packed(nx.dy);
+        }
+        keep_packed(b.x);
+        keep_packed(b.dy);
+        row_sum4(sxx, s2, sx_next, s1_next, red4, phase, lane, wave, S, p);
+        const float rs = 1.0f / __builtin_sqrtf(__builtin_fmaf(sxx, inv_n, eps));
+        write_dx<KIND, RECOMP, ALL>(b, gam, acc, dx, rk, rk < M, N, ldo, inv_n, mu, rs, s1, s2,
+                                    col0, cstride);
+        mu = sx_next * inv_n;
+        s1 = s1_next;
+      };
+      if constexpr (steady_loop<RECOMP, Tg, VEC, C, NACC>()) {
+        if (steady) {
+          for (; it0 + 2 * D - 2 < kfull; it0 += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+              const int k = it0 + d;
+              fetch_row<KIND, RECOMP, true>(buf[(d + D - 1) % D], x, dy, mean, rstd,
+                                            row_of(k + D - 1), true, N, ldx, ldy, col0, cstride);
+              step(std::true_type(), d, k);
+            }
+          }
+        }
+      }
+      for (int it = it0; it < iters; it += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
           const int k = it + d;
@@ -662,27 +705,7 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
             fetch_row<KIND, RECOMP, false>(buf[(d + D - 1) % D], x, dy, mean, rstd, rf, rf < M, N,
                                     ldx, ldy, col0, cstride);
           }
-          if (k < iters) {
-            RB& b = buf[d];
-            const int64_t rk = row_of(k);
-            float sxx, s2, sx_next = 0.0f, s1_next = 0.0f;
-            recompute_sums2<KIND>(b, gam, acc, rk < M, N, col0, cstride, mu, sxx, s2);
-            if (k + 1 < iters) {
-              RB& nx = buf[(d + 1) % D];
-              ln_recompute_sums1(nx, gam, acc, row_of(k + 1) < M, N, col0, cstride, sx_next,
-                                 s1_next);
-              keep_packed(nx.x);
-              keep_packed(nx.dy);
-            }
-            keep_packed(b.x);
-            keep_packed(b.dy);
-            row_sum4(sxx, s2, sx_next, s1_next, red4, phase, lane, wave, S, p);
-            const float rs = 1.0f / __builtin_sqrtf(__builtin_fmaf(sxx, inv_n, eps));
-            write_dx<KIND, RECOMP>(b, gam, acc, dx, rk, rk < M, N, ldo, inv_n, mu, rs, s1, s2,
-                                   col0, cstride);
-            mu = sx_next * inv_n;
-            s1 = s1_next;
-          }
+          if (k < iters) step(std::false_type(), d, k);
         }
       }
     } else {
