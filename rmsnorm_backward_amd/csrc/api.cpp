@@ -366,7 +366,7 @@ int run_forward(int kind, const void* x, const void* gamma, const void* beta, in
   norm_bwd_plan_t g;
   const char* why = nullptr;
   // rows the fused forward cannot hold in registers take the row-loop kernel
-  const bool wide = nb::make_geometry(kind, N, io_dtype, 0, vec_ok, &g, &why) != NORM_BWD_OK;
+  const bool wide = nb::make_geometry(kind, N, io_dtype, 0, vec_ok, &g, &why, true) != NORM_BWD_OK;
   if (wide && N > INT32_MAX) return set_error(NORM_BWD_ERR_UNSUPPORTED, "N too large");
   // y and the statistics must not overlap the inputs or each other
   const size_t mat = (size_t)M * (size_t)N * (size_t)eb, vec = (size_t)N * (size_t)eb;

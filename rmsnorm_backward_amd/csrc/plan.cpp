@@ -11,7 +11,18 @@
 namespace nb {
 
 namespace {
-constexpr int64_t kTargetWaves = 2048;  // waves in flight the group count aims at
+// Kernel A with saved statistics: one workgroup per compute unit on a
+// 256-CU part (4096 x 16384 bf16 RMSNorm step: 72.6 us at 256 groups, 89.5 us
+// at the 128 that 2048 waves in flight would give).
+constexpr int64_t kSavedStatsGroups = 256;
+// Kernel A: rows in flight per workgroup, the fewest (a power of two) whose
+// x and dy together reach this many bytes (step times with four rotating
+// buffer sets: 65536 x 1024 bf16 RMSNorm 68.5 us at 4 rows, 76.4 us at 8;
+// 262144 x 768 218.5 us at 8, 229.6 us at 4; 16384 x 4096 69.2 us at 1,
+// 69.9 us at 2).
+constexpr int64_t kRowBytesInFlight = 16384;
+// Recompute mode aims at a number of waves in flight instead.
+constexpr int64_t kTargetWaves = 2048;
 // LayerNorm in recompute mode exchanges twice per row; a second workgroup per
 // compute unit hides that latency (65536 x 8192 bf16: 570 us at 512 groups
 // against 645 us at 256), so it aims at twice the waves.
@@ -28,8 +39,15 @@ constexpr int64_t kMinRowsPerGroup = 4;
 constexpr int64_t kGroupQuantum = 256;
 constexpr int64_t kMaxGrid = 1 << 20;
 constexpr int kMaxLdsBytes = 65536 - 1024;  // dynamic LDS; the kernel adds 256 B static
-constexpr int kTargetThreads = 512;
-constexpr int kPreferredLaneElems = 16;
+// The forward and kernel A in recompute mode fill this many threads with
+// rows instead (recompute with one row per workgroup: 16384 x 4096 bf16
+// RMSNorm 76.0 us against 73.2 us at 512 threads, LayerNorm 89.7 us against
+// 85.2 us).
+constexpr int kRowStatsThreads = 512;
+// At most this many bytes of each operand per lane (16 bf16/fp16 or 8 fp32
+// elements) before wider lanes are considered: 16384 x 4096 fp32 RMSNorm
+// step 129.9 us at 32 bytes (8 waves per row), 149.2 us at 64 (4 waves).
+constexpr int kPreferredLaneBytes = 32;
 // Column-walk workgroups to aim for: one per compute unit. With the kernel's
 // XCD-aware tile order (line neighbours share an L2) narrow tiles cost no
 // extra HBM traffic, and the widest tile giving 256 tiles was the fastest on
@@ -72,7 +90,7 @@ int kernel_a_max_threads(int lane_elems) { return lane_elems > 16 ? 512 : 1024; 
 // Lane layout of kernel A for rows of N elements (fills vec, chunks,
 // waves_per_row, rows_in_flight, threads, lds_bytes of *p).
 int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok16,
-                  norm_bwd_plan_t* p, const char** why) {
+                  norm_bwd_plan_t* p, const char** why, bool row_stats) {
   (void)kind;
   const int eb = dtype_bytes(io_dtype);
   const int nacc = with_dbeta ? 2 : 1;
@@ -92,24 +110,33 @@ int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok
                        : with_dbeta ? NORM_BWD_MAX_N_16BIT_DBETA : NORM_BWD_MAX_N_16BIT;
   if (N > max_n) return fail(why, "N exceeds the fused path's limit", NORM_BWD_ERR_UNSUPPORTED);
 
-  // Prefer at most kPreferredLaneElems elements per lane (the pipelined
-  // kernel holds three rows of them in registers), then the smallest S (fewer
-  // waves coupled by a barrier per row), then the smallest C. Wider lanes are
-  // used only when nothing narrower covers N.
+  // Prefer at most kPreferredLaneBytes bytes of each operand per lane (the
+  // pipelined kernel holds three rows of them in registers), then the
+  // smallest S (fewer waves coupled by a barrier per row), then the smallest
+  // C. Wider lanes are used only when nothing narrower covers N.
   int S = 0, C = 0;
   for (int pass = 0; pass < 2 && !S; ++pass) {
     for (int s = 1; s <= 16 && !S; s *= 2) {
       for (int c = 1; c <= 8; c *= 2) {
         if (!kernel_a_exists(io_dtype, full, with_dbeta, c)) continue;
-        if (pass == 0 && p->vec * c > kPreferredLaneElems) continue;
+        if (pass == 0 && p->vec * c * eb > kPreferredLaneBytes) continue;
         if (s * 64 > kernel_a_max_threads(p->vec * c)) continue;
         if ((int64_t)s * 64 * p->vec * c >= N) { S = s; C = c; break; }
       }
     }
   }
   if (!S) return fail(why, "no kernel geometry covers N", NORM_BWD_ERR_UNSUPPORTED);
-  int P = kTargetThreads / (64 * S);
-  if (P < 1) P = 1;
+  // Rows in flight: the kernels that compute row statistics fill
+  // kRowStatsThreads; kernel A with saved statistics takes the fewest rows
+  // whose x and dy reach kRowBytesInFlight.
+  int P = 1;
+  if (row_stats) {
+    P = kRowStatsThreads / (64 * S);
+    if (P < 1) P = 1;
+  } else {
+    while (P < 16 && (int64_t)P * 2 * N * eb < kRowBytesInFlight) P *= 2;
+    while (P > 1 && S * P > 16) P /= 2;
+  }
   while (P > 1 && S * P * 64 > kernel_a_max_threads(p->vec * C)) P /= 2;
   int lds = nacc * S * C * 64 * p->vec * 4;
   if (P == 1 || lds > kMaxLdsBytes) { P = 1; lds = 0; }
@@ -124,7 +151,7 @@ int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok
 bool fused_fits(int64_t N, int io_dtype, int with_dbeta, bool vec_ok16) {
   norm_bwd_plan_t g;
   const char* why = nullptr;
-  return make_geometry(NORM_BWD_RMSNORM, N, io_dtype, with_dbeta, vec_ok16, &g, &why) ==
+  return make_geometry(NORM_BWD_RMSNORM, N, io_dtype, with_dbeta, vec_ok16, &g, &why, false) ==
          NORM_BWD_OK;
 }
 
@@ -176,18 +203,21 @@ int wgrad_lanes_per_row(int64_t N, int vec) {
 
 int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype, bool recompute) {
   if (M <= 0) return 0;
-  // Enough workgroups for about kTargetWaves waves in flight (8 per compute
-  // unit on a 256-CU part), never fewer than kMinRowsPerGroup rows per
-  // group, above kGroupQuantum a multiple of it. The geometry is itself a
-  // function of (kind, N, io_dtype), so the group count depends on the
+  // Saved statistics: kSavedStatsGroups. Recompute mode: enough workgroups
+  // for about kTargetWaves waves in flight (8 per compute unit on a 256-CU
+  // part; twice that for LayerNorm). Never fewer than kMinRowsPerGroup rows
+  // per group, above kGroupQuantum a multiple of it. The geometry is itself
+  // a function of (kind, N, io_dtype), so the group count depends on the
   // problem only, never on the device.
-  norm_bwd_plan_t g;
-  const char* why = nullptr;
-  int waves = 8;
-  if (N > 0 && make_geometry(kind, N, io_dtype, 0, true, &g, &why) == NORM_BWD_OK)
-    waves = g.threads / 64;
-  int64_t G = ((recompute && kind == NORM_BWD_LAYERNORM) ? kRecomputeLnTargetWaves : kTargetWaves) /
-              waves;
+  int64_t G = kSavedStatsGroups;
+  if (recompute) {
+    norm_bwd_plan_t g;
+    const char* why = nullptr;
+    int waves = 8;
+    if (N > 0 && make_geometry(kind, N, io_dtype, 0, true, &g, &why, true) == NORM_BWD_OK)
+      waves = g.threads / 64;
+    G = (kind == NORM_BWD_LAYERNORM ? kRecomputeLnTargetWaves : kTargetWaves) / waves;
+  }
   const int64_t cap = ceil_div(M, kMinRowsPerGroup);
   if (G > cap) G = cap;
   if (G > kGroupQuantum) G -= G % kGroupQuantum;
@@ -217,7 +247,7 @@ int make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,
   const int nacc = with_dbeta ? 2 : 1;
 
   const char* gwhy = nullptr;
-  const int st = make_geometry(kind, N, io_dtype, with_dbeta, vec_ok16, &p, &gwhy);
+  const int st = make_geometry(kind, N, io_dtype, with_dbeta, vec_ok16, &p, &gwhy, recompute);
   if (st != NORM_BWD_OK) return fail(why, gwhy, st);
   if (N == 0) {  // nothing to compute
     *plan = p;

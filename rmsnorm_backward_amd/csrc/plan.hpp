@@ -21,10 +21,13 @@ bool kernel_a_exists(int io_dtype, int vec_full, int with_dbeta, int chunks);
 // Largest workgroup kernel A accepts for vec * chunks elements per lane.
 int kernel_a_max_threads(int lane_elems);
 
-// Kernel A lane layout for rows of N elements (vec, chunks, waves_per_row,
-// rows_in_flight, threads, lds_bytes of *plan). Returns a status.
+// Lane layout for rows of N elements (vec, chunks, waves_per_row,
+// rows_in_flight, threads, lds_bytes of *plan), for kernel A with saved
+// statistics or, with `row_stats`, for the kernels that compute row
+// statistics (the forward, kernel A in recompute mode): the lane layout is
+// the same, the rows in flight differ. Returns a status.
 int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok16,
-                  norm_bwd_plan_t* plan, const char** why);
+                  norm_bwd_plan_t* plan, const char** why, bool row_stats);
 
 // Whether the fused kernels (rows held in registers) cover rows of N elements
 // of io_dtype; wider rows take the row-loop path.

@@ -91,15 +91,35 @@ def test_status_strings(nb):
     assert nb.norm_bwd_status_string(99) == "NORM_BWD_ERR_UNKNOWN"
 
 
+def _row_stats_rows(p, db):
+    """Rows in flight of the kernels that compute row statistics (forward,
+    recompute mode) on plan p's lane layout: as many as fill 512 threads,
+    within the launch bound; one when the combine buffer would not fit."""
+    S, C, vec = p.waves_per_row, p.chunks, p.vec
+    P = max(1, 512 // (64 * S))
+    while P > 1 and S * P * 64 > (512 if vec * C > 16 else 1024):
+        P //= 2
+    if P > 1 and (2 if db else 1) * S * C * 64 * vec * 4 > 65536 - 1024:
+        P = 1
+    return P
+
+
 def _auto_groups(nb, kind, M, N, dt, recompute=False):
-    """The documented rule: about 2048 waves in flight (4096 for LayerNorm in
-    recompute mode), >= 4 rows per group, above 256 a multiple of 256, where
-    the waves per workgroup come from the (dbeta-less) geometry."""
+    """The documented rule: 256 groups with saved statistics; in recompute
+    mode about 2048 waves in flight (4096 for LayerNorm), the waves per
+    workgroup coming from the (dbeta-less) geometry; always >= 4 rows per
+    group, above 256 a multiple of 256."""
     if M == 0:
         return 0
-    waves = nb.norm_bwd_make_plan(kind, 1, N, dt, False).threads // 64 if N else 8
-    target = 4096 if (recompute and kind == "layernorm") else 2048
-    g = min(target // waves, -(-M // 4))
+    if recompute:
+        waves = 8
+        if N:
+            p = nb.norm_bwd_make_plan(kind, 1, N, dt, False)
+            waves = p.waves_per_row * _row_stats_rows(p, False)
+        g = (4096 if kind == "layernorm" else 2048) // waves
+    else:
+        g = 256
+    g = min(g, -(-M // 4))
     if g > 256:
         g -= g % 256
     return max(1, g)
@@ -160,6 +180,17 @@ def test_plan_invariants(nb, kind, dt, M, N, db, groups):
     p = nb.norm_bwd_make_plan(kind, M, N, dt, db, groups)
     S, P, C, vec = p.waves_per_row, p.rows_in_flight, p.chunks, p.vec
     assert vec in (1, 16 // eb) and (vec == 1 or N % vec == 0)
+    # rows in flight: the fewest (a power of two) whose x and dy reach 16 KiB,
+    # within 16 waves and the kernel's launch bound; one when the combine
+    # buffer would not fit
+    want = 1
+    while want < 16 and want * 2 * N * eb < 16384:
+        want *= 2
+    while want > 1 and (S * want > 16 or S * want * 64 > (512 if vec * C > 16 else 1024)):
+        want //= 2
+    if want > 1 and (2 if db else 1) * S * C * 64 * vec * 4 > 65536 - 1024:
+        want = 1
+    assert P == want
     assert S * 64 * vec * C >= N                       # the lanes cover the row
     assert p.threads == 64 * S * P and 1 <= S * P <= 16
     assert C in (1, 2, 4, 8)
