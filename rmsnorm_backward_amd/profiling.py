@@ -120,16 +120,23 @@ def _counter_rows(path, counter):
     for r in rows:
         if r.get("Counter_Name") != counter:
             continue
-        key = (r["Dispatch_Id"], r["Kernel_Name"])
+        key = (int(r["Dispatch_Id"]), r["Kernel_Name"], r.get("Grid_Size", ""))
         per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
     return per_dispatch
 
 
 def _mean_for(per_dispatch, needle):
+    """Median counter value per dispatch of a kernel, and the dispatch count.
+    For the column walk only the launches of the benchmarked workload count:
+    bench.py also runs it for the wide-row workload, after the benchmarked
+    one, so the (kernel, grid) pair dispatched first is taken."""
     if needle == KERNEL_A:
-        vals = [v for (d, name), v in per_dispatch.items() if is_step_kernel_a(name)]
+        vals = [v for (d, name, g), v in per_dispatch.items() if is_step_kernel_a(name)]
+    elif needle == COLWALK:
+        hits = sorted((d, name, g, v) for (d, name, g), v in per_dispatch.items() if needle in name)
+        vals = [v for d, name, g, v in hits if hits and (name, g) == hits[0][1:3]]
     else:
-        vals = [v for (d, name), v in per_dispatch.items() if needle in name]
+        vals = [v for (d, name, g), v in per_dispatch.items() if needle in name]
     return (statistics.median(vals), len(vals)) if vals else (None, 0)
 
 
