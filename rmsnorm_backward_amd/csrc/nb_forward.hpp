@@ -86,17 +86,33 @@ void norm_fwd_kernel(const void* __restrict__ xv, const void* __restrict__ gv,
   const bool cover = N == C * cstride;
 
   // `all` (Flag<true>): the row exists and every chunk is inside it, so no
-  // condition is evaluated.
+  // condition is evaluated, and x and y go through the row's buffer
+  // resource (scalar base, 32-bit lane offset).
   auto fetch = [&](auto all, XBuf<Tg, VEC, C>& b, int64_t r) {
     constexpr bool ALL = decltype(all)::value;
     if (ALL || r < M) {
       const int64_t rb = r * (int64_t)N;
+      if constexpr (ALL) {
+        const __amdgpu_buffer_rsrc_t rx = row_rsrc(x + rb * EB, (uint32_t)N * EB);
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const int col = col0 + c * cstride;
-        if (ALL || col < N) b.x[c].load_stream(x + (rb + col) * EB);
+        for (int c = 0; c < C; ++c)
+          b.x[c].load_stream_buf(rx, (uint32_t)(col0 + c * cstride) * EB);
+      } else {
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          const int col = col0 + c * cstride;
+          if (col < N) b.x[c].load_stream(x + (rb + col) * EB);
+        }
       }
     }
+  };
+  // store one lane's chunk c of y (row base rb, in elements)
+  auto store_y = [&](auto all, const PK& out, int64_t rb, int col) {
+    constexpr bool ALL = decltype(all)::value;
+    if constexpr (ALL)
+      out.store_stream_buf(row_rsrc(y + rb * EB, (uint32_t)N * EB), (uint32_t)col * EB);
+    else
+      out.store_stream(y + (rb + col) * EB);
   };
 
   int phase = 0;
@@ -132,7 +148,7 @@ void norm_fwd_kernel(const void* __restrict__ xv, const void* __restrict__ gv,
             o[v] = __builtin_fmaf((b.x[c].get(v) - mu) * rs, gam[c][v], bet[c][v]);
           PK out;
           out.set(o);
-          out.store_stream(y + (rb + col) * EB);
+          store_y(all, out, rb, col);
         }
       }
       // one lane stores the row's statistic (a predicated vector store)
@@ -199,7 +215,7 @@ void norm_fwd_kernel(const void* __restrict__ xv, const void* __restrict__ gv,
               o[v] = __builtin_fmaf((b.x[c].get(v) - mu) * rs, gam[c][v], bet[c][v]);
             PK out;
             out.set(o);
-            out.store_stream(y + (rb + col) * EB);
+            store_y(all, out, rb, col);
           }
         }
         if (s == 0 && lane == 0) {
