@@ -1,0 +1,164 @@
+"""The steady-state row loop of kernel A and of the forward against the fp64
+oracle (needs a gfx950 GPU).
+
+When the lanes cover a row exactly and a workgroup has at least 2D - 1 full
+iterations ahead (D, the register ring's depth: 3 here, 4 for the LayerNorm
+forward), kernel A and the forward run those iterations through a loop with
+no per-lane or per-row conditions and then hand the ring to the general loop
+for the rest. These cases put few groups (or forward sweeps) over many rows so
+that the loop runs, with group lengths just below and at the threshold, tails
+of every length after it, and one, two, four and eight rows in flight per
+workgroup, for both kinds, all three element types, saved statistics and
+recompute mode. Every output is compared element by element with the oracle.
+"""
+
+from __future__ import annotations
+
+import pytest
+import torch
+
+import oracle
+import parity
+from inputs import backward_inputs
+from rmsnorm_backward_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+BASE = {"layernorm": W.LN_F16_1151x8192, "rmsnorm": W.RMS_BF16_16384x4096}
+
+
+@pytest.fixture(scope="module")
+def nb():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    import rmsnorm_backward_amd as nbmod
+    nbmod.load_library()
+    return nbmod
+
+
+def workload(kind, dt, M, N):
+    w = BASE[kind]
+    wg = w.wgrad_dtype if dt == w.io_dtype else torch.float32
+    return W.scaled(w, M=M, N=N, io_dtype=dt, wgrad_dtype=wg,
+                    name=f"{kind}_{W._dt(dt)}_{M}x{N}")
+
+
+def compare(w, inp, out, mean, rstd, with_db):
+    dx, dg, db = (None if t is None else t.cpu() for t in out)
+    rdx, rdg, rdb = oracle.bwd(w.kind, inp["x"], inp["dy"], inp["gamma"], mean, rstd,
+                               want_dbeta=True)
+    scale = parity.dx_term_scale(w.kind, inp["x"], inp["dy"], inp["gamma"], mean, rstd)
+    parity.check_dx(w.io_dtype, dx, rdx, scale=scale)
+    parity.check_wgrad(w.io_dtype, dg, rdg)
+    if with_db:
+        parity.check_wgrad(w.io_dtype, db, rdb, "dbeta")
+
+
+# (kind, dtype, N, groups, row counts): N is covered exactly by the lanes;
+# the rows per workgroup in flight (P) follow from N; group lengths around
+# 5 * P rows (the threshold for D = 3) and tails of 0 .. D - 1 iterations
+# and 0 .. P - 1 rows after the last full pass.
+SAVED = [
+    ("rmsnorm", torch.bfloat16, 4096, 3, (12, 15, 19, 26, 50)),       # P = 1
+    ("layernorm", torch.bfloat16, 8192, 2, (8, 10, 15, 23)),          # P = 1, both gradients
+    ("layernorm", torch.bfloat16, 2048, 2, (18, 20, 23, 42, 61)),     # P = 2, both gradients
+    ("rmsnorm", torch.bfloat16, 1024, 2, (38, 40, 47, 83, 126)),      # P = 4
+    ("layernorm", torch.float32, 512, 2, (40, 45, 90, 133)),          # P = 4, both gradients
+    ("rmsnorm", torch.bfloat16, 512, 2, (78, 80, 95, 161, 250)),      # P = 8
+    ("rmsnorm", torch.float16, 2048, 1, (9, 10, 11, 12, 29)),         # one group: P = 2
+]
+
+
+def _saved_cases():
+    for kind, dt, N, G, Ms in SAVED:
+        for M in Ms:
+            yield kind, dt, N, G, M
+
+
+@pytest.mark.parametrize("kind,dt,N,G,M", list(_saved_cases()),
+                         ids=lambda v: str(v).replace("torch.", ""))
+def test_steady_loop_saved_statistics(nb, kind, dt, N, G, M):
+    w = workload(kind, dt, M, N)
+    with_db = kind == "layernorm"
+    inp = backward_inputs(w)
+    plan = nb.norm_bwd_make_plan(kind, M, N, dt, with_db, G)
+    assert plan.waves_per_row * 64 * plan.vec * plan.chunks == N   # lanes cover the row
+    g = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor) and k != "outliers"}
+    print(f"[run] {w.name} groups={G} P={plan.rows_in_flight}", flush=True)
+    out = nb.norm_bwd_execute(plan, g["x"], g["dy"], g["gamma"], g.get("mean"), g["rstd"],
+                              wgrad_dtype=w.wgrad_dtype)
+    torch.cuda.synchronize()
+    compare(w, inp, out, inp.get("mean"), inp["rstd"], with_db)
+
+
+# Recompute mode runs the steady-state loop where a lane holds one 16-byte
+# vector per operand (RMSNorm, and LayerNorm's pipelined loop).
+RECOMPUTE = [
+    ("rmsnorm", torch.bfloat16, 512, 2, (78, 80, 95, 250)),           # P = 8
+    ("layernorm", torch.bfloat16, 512, 2, (78, 80, 95, 250)),         # P = 8, pipelined
+    ("layernorm", torch.float32, 256, 1, (39, 40, 41, 77)),           # P = 8, pipelined
+]
+
+
+def _recompute_cases():
+    for kind, dt, N, G, Ms in RECOMPUTE:
+        for M in Ms:
+            yield kind, dt, N, G, M
+
+
+@pytest.mark.parametrize("kind,dt,N,G,M", list(_recompute_cases()),
+                         ids=lambda v: str(v).replace("torch.", ""))
+def test_steady_loop_recompute(nb, kind, dt, N, G, M):
+    w = workload(kind, dt, M, N)
+    with_db = kind == "layernorm"
+    inp = W.make_inputs(w)
+    print(f"[run] recompute {w.name} groups={G}", flush=True)
+    out = nb.norm_bwd_ex(kind, inp["x"].cuda(), inp["dy"].cuda(), inp["gamma"].cuda(), None, None,
+                         w.eps, wgrad_dtype=w.wgrad_dtype, with_dbeta=with_db, groups=G)
+    torch.cuda.synchronize()
+    # the reference: the oracle's backward on the oracle's unrounded fp64
+    # statistics; the tolerance adds the first-order effect of the kernel's
+    # own fp32 statistics (parity.recompute_terms)
+    x, dy, gamma = inp["x"], inp["dy"], inp["gamma"]
+    dx, dg, db = (None if t is None else t.cpu() for t in out)
+    mean, rstd = oracle.fwd_stats(kind, x, w.eps)
+    rdx = oracle.bwd_dx(kind, x, dy, gamma, mean, rstd)
+    t_dx, t_dg = parity.recompute_terms(kind, x, dy, gamma, mean, rstd)
+    parity.check_dx(w.io_dtype, dx, rdx, scale=t_dx, coef32=2.0 ** -16)
+    rdg, rdb = oracle.bwd_wgrad(kind, x, dy, mean, rstd, want_dbeta=True)
+    parity.check_wgrad(w.io_dtype, dg, rdg, extra=2.0 ** -16 * t_dg)
+    if with_db:
+        parity.check_wgrad(w.io_dtype, db, rdb, "dbeta")
+
+
+# The forward: a sweep of rows_per_sweep = grid * P rows (4096 / S for
+# these N), so the steady-state loop needs at least 5 sweeps (7 for the
+# LayerNorm forward, whose ring is one row deeper).
+FORWARD = [
+    ("rmsnorm", torch.bfloat16, 512, (4096 * 5 - 1, 4096 * 5 + 1000, 4096 * 9 + 17)),
+    ("layernorm", torch.bfloat16, 512, (4096 * 7 - 3, 4096 * 7 + 5, 4096 * 11 + 300)),
+    ("rmsnorm", torch.float32, 1024, (2048 * 5 + 7, 2048 * 8 + 2047)),
+]
+
+
+def _forward_cases():
+    for kind, dt, N, Ms in FORWARD:
+        for M in Ms:
+            yield kind, dt, N, M
+
+
+@pytest.mark.parametrize("kind,dt,N,M", list(_forward_cases()),
+                         ids=lambda v: str(v).replace("torch.", ""))
+def test_steady_loop_forward(nb, kind, dt, N, M):
+    w = workload(kind, dt, M, N)
+    inp = W.make_inputs(w)
+    x, g = inp["x"], inp["gamma"]
+    print(f"[run] forward {w.name}", flush=True)
+    if kind == "layernorm":
+        y, mean, rstd = nb.norm_fwd_layernorm(x.cuda(), g.cuda(), None, w.eps)
+    else:
+        y, rstd = nb.norm_fwd_rmsnorm(x.cuda(), g.cuda(), w.eps)
+        mean = None
+    torch.cuda.synchronize()
+    ry, rm, rr = oracle.fwd(kind, x, g, None, w.eps)
+    parity.check_forward(w.io_dtype, kind, x, g, None, y.cpu(),
+                         None if mean is None else mean.cpu(), rstd.cpu(), ry, rm, rr)
