@@ -262,37 +262,50 @@ constexpr int max_threads_for() { return VEC * C > 16 ? 512 : 1024; }
 
 // Rows of x/dy held in registers per wave (a ring: D - 1 rows in flight
 // while one is processed), sized by the bytes each lane holds per operand and
-// the register budget the launch bound leaves (128 VGPRs at 1024 threads,
-// 256 at 512): 32 B -> 3 rows; 64 B -> 2 rows within 256 VGPRs; otherwise 1
-// (no prefetch).
-template <class Tg, int VEC, int C>
+// the register budget the launch bound MAXT leaves (128 VGPRs at 1024
+// threads, 256 at 512): up to 32 B -> 3 rows; 64 B -> 2 rows within 256
+// VGPRs; otherwise 1 (no prefetch).
+template <class Tg, int VEC, int C, int MAXT = max_threads_for<VEC, C>()>
 constexpr int prefetch_depth() {
   constexpr int bytes = VEC * C * Tg::kBytes;
-  return max_threads_for<VEC, C>() == 1024 ? (bytes <= 32 ? 3 : 1) : (bytes <= 64 ? 2 : 1);
+  return bytes <= 32 ? 3 : (MAXT <= 512 && bytes <= 64 ? 2 : 1);
+}
+
+// Kernel A in recompute mode also exists with a 512-thread launch bound
+// (256 VGPRs) where a lane holds 32 bytes of each operand: the recompute
+// plans' 512-thread workgroups then take the steady-state loop, which did not
+// fit the 128 VGPRs of the 1024-thread bound (16384 x 4096 bf16 RMSNorm
+// recompute step 73.8 -> 70.4 us, 65536 x 8192 LayerNorm 565 -> 551 us).
+template <bool RECOMP, class Tg, int VEC, int C>
+constexpr bool has_narrow_bound() {
+  return RECOMP && VEC > 1 && VEC * C * Tg::kBytes == 32 && max_threads_for<VEC, C>() == 1024;
 }
 
 // Whether kernel A pipelines the two exchanges of LayerNorm recompute across
 // rows. It reads the next row from the ring, so the ring must hold two rows;
 // and fp16 rows of 16 elements per lane with both gradients are left out:
-// pipelined, that kernel needed 3 registers more than the 128 a 1024-thread
-// workgroup allows and spilled (bf16 fits, with 123).
-template <class Tg, int VEC, int C, int NACC>
+// pipelined under the 1024-thread bound that kernel needed 3 registers more
+// than the 128 it allows and spilled (bf16 fits, with 123); under the
+// 512-thread bound it fits but ran 1% slower on 1151 x 8192.
+template <class Tg, int VEC, int C, int NACC, int MAXT = max_threads_for<VEC, C>()>
 constexpr bool pipeline_ln_recompute() {
-  return prefetch_depth<Tg, VEC, C>() >= 2 &&
+  return prefetch_depth<Tg, VEC, C, MAXT>() >= 2 &&
          !(std::is_same<Tg, TF16>::value && VEC * C == 16 && NACC == 2);
 }
 
 // Whether kernel A runs its steady-state loop (every row and every lane
 // chunk in bounds, so no per-lane or per-row conditions). Kernels whose row
 // sits in 16-byte vectors: with saved statistics up to 32 elements per lane,
-// in recompute mode one vector per operand per lane. Left out, because the
-// extra loop made them spill under their register budget: one element per
-// lane, 64 elements per lane, fp16 rows of 16 elements per lane with both
-// gradients, and recompute mode with more than 16 bytes per operand.
-template <bool RECOMP, class Tg, int VEC, int C, int NACC>
+// in recompute mode one vector per operand per lane (32 bytes under the
+// 512-thread bound). Left out, because the extra loop made them spill under
+// their register budget: one element per lane, 64 elements per lane, fp16
+// rows of 16 elements per lane with both gradients under the 1024-thread
+// bound, and recompute mode with more bytes per operand.
+template <bool RECOMP, class Tg, int VEC, int C, int NACC, int MAXT = max_threads_for<VEC, C>()>
 constexpr bool steady_loop() {
-  return VEC > 1 && VEC * C <= 32 && (!RECOMP || VEC * C * Tg::kBytes <= 16) &&
-         !(std::is_same<Tg, TF16>::value && VEC * C == 16 && NACC == 2);
+  return VEC > 1 && VEC * C <= 32 &&
+         (!RECOMP || VEC * C * Tg::kBytes <= (MAXT <= 512 ? 32 : 16)) &&
+         !(std::is_same<Tg, TF16>::value && VEC * C == 16 && NACC == 2 && MAXT == 1024);
 }
 
 // ---------------------------------------------------------------- kernel A
@@ -603,8 +616,10 @@ __device__ __forceinline__ void process_row(RowBuf<Tg, VEC, C>& b, const float (
 
 // WSNT: the partial rows are stored non-temporally (chosen for large
 // workspaces by the planner's stream_workspace); the values are the same.
-template <int KIND, bool RECOMP, class Tg, int VEC, int C, int NACC, bool WSNT>
-__global__ __launch_bounds__((max_threads_for<VEC, C>()))
+// MAXT: the launch bound (max_threads_for, or 512 where has_narrow_bound).
+template <int KIND, bool RECOMP, class Tg, int VEC, int C, int NACC, bool WSNT,
+          int MAXT = max_threads_for<VEC, C>()>
+__global__ __launch_bounds__(MAXT)
 void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dyv,
                         const void* __restrict__ gv, const float* __restrict__ mean,
                         const float* __restrict__ rstd, void* __restrict__ dxv,
@@ -661,7 +676,7 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
     // Ring of D row buffers: the loads of row k + D - 1 are issued before
     // row k is processed, so each wave keeps D - 1 rows of x and dy in flight
     // while it computes.
-    constexpr int D = prefetch_depth<Tg, VEC, C>();
+    constexpr int D = prefetch_depth<Tg, VEC, C, MAXT>();
     RB buf[D];
     // Steady state: when the lanes cover the row exactly and the group has
     // enough iterations in which every row-lane has a row, those iterations
@@ -675,16 +690,16 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
     const int kfull = (int)(rows / P);  // iterations whose P rows all exist
     int it0 = 0;
     constexpr bool kPipelined =
-        RECOMP && KIND == kLayerNorm && pipeline_ln_recompute<Tg, VEC, C, NACC>();
+        RECOMP && KIND == kLayerNorm && pipeline_ln_recompute<Tg, VEC, C, NACC, MAXT>();
     const bool steady =
-        steady_loop<RECOMP, Tg, VEC, C, NACC>() && N == C * cstride && kfull >= 2 * D - 1;
+        steady_loop<RECOMP, Tg, VEC, C, NACC, MAXT>() && N == C * cstride && kfull >= 2 * D - 1;
     if (steady) {
 #pragma unroll
       for (int k = 0; k < D - 1; ++k)
         fetch_row<KIND, RECOMP, true, true>(buf[k], x, dy, mean, rstd, row_of(k), true, N, ldx,
                                             ldy, col0, cstride);
       // (the pipelined LayerNorm recompute loop runs its own steady state)
-      if constexpr (steady_loop<RECOMP, Tg, VEC, C, NACC>() && !kPipelined) {
+      if constexpr (steady_loop<RECOMP, Tg, VEC, C, NACC, MAXT>() && !kPipelined) {
         for (; it0 + 2 * D - 2 < kfull; it0 += D) {
 #pragma unroll
           for (int d = 0; d < D; ++d) {
@@ -753,7 +768,7 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
         mu = sx_next * inv_n;
         s1 = s1_next;
       };
-      if constexpr (steady_loop<RECOMP, Tg, VEC, C, NACC>()) {
+      if constexpr (steady_loop<RECOMP, Tg, VEC, C, NACC, MAXT>()) {
         if (steady) {
           for (; it0 + 2 * D - 2 < kfull; it0 += D) {
 #pragma unroll

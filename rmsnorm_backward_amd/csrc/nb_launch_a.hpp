@@ -15,12 +15,22 @@ constexpr int lane_elem_limit() {
   return !FULL ? 8 : (Tg::kBytes == 4 ? 16 : (NACC == 2 ? 32 : 64));
 }
 
+template <class Tg, int KIND, bool RECOMP, int NACC, int VEC, int C, bool WSNT, int MAXT>
+hipError_t launch_bounded(const LaunchA& a) {
+  hipLaunchKernelGGL((dx_partials_kernel<KIND, RECOMP, Tg, VEC, C, NACC, WSNT, MAXT>),
+                     dim3(a.grid), dim3(a.threads), a.lds, a.stream, a.x, a.dy, a.gamma, a.mean,
+                     a.rstd, a.dx, a.ws, a.M, a.N, a.ldx, a.ldy, a.ldo, a.G, a.R, a.S, a.P, a.eps);
+  return hipGetLastError();
+}
+
+// Workgroups of at most 512 threads take the 512-thread-bound instantiation
+// where one exists (has_narrow_bound: recompute mode at 32 bytes per lane).
 template <class Tg, int KIND, bool RECOMP, int NACC, int VEC, int C, bool WSNT>
 hipError_t launch_one_policy(const LaunchA& a) {
-  hipLaunchKernelGGL((dx_partials_kernel<KIND, RECOMP, Tg, VEC, C, NACC, WSNT>), dim3(a.grid),
-                     dim3(a.threads), a.lds, a.stream, a.x, a.dy, a.gamma, a.mean, a.rstd, a.dx,
-                     a.ws, a.M, a.N, a.ldx, a.ldy, a.ldo, a.G, a.R, a.S, a.P, a.eps);
-  return hipGetLastError();
+  if constexpr (has_narrow_bound<RECOMP, Tg, VEC, C>()) {
+    if (a.threads <= 512) return launch_bounded<Tg, KIND, RECOMP, NACC, VEC, C, WSNT, 512>(a);
+  }
+  return launch_bounded<Tg, KIND, RECOMP, NACC, VEC, C, WSNT, max_threads_for<VEC, C>()>(a);
 }
 
 // The non-temporal partials store exists for 16-byte vector rows only (the
