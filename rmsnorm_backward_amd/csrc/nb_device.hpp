@@ -276,9 +276,13 @@ constexpr int prefetch_depth() {
 // plans' 512-thread workgroups then take the steady-state loop, which did not
 // fit the 128 VGPRs of the 1024-thread bound (16384 x 4096 bf16 RMSNorm
 // recompute step 73.8 -> 70.4 us, 65536 x 8192 LayerNorm 565 -> 551 us).
-template <bool RECOMP, class Tg, int VEC, int C>
+// So does the saved-statistics fp16 kernel with 16 elements per lane and
+// both gradients, the one saved-statistics kernel whose steady-state loop
+// spilled under the 1024-thread bound.
+template <bool RECOMP, class Tg, int VEC, int C, int NACC>
 constexpr bool has_narrow_bound() {
-  return RECOMP && VEC > 1 && VEC * C * Tg::kBytes == 32 && max_threads_for<VEC, C>() == 1024;
+  return VEC > 1 && VEC * C * Tg::kBytes == 32 && max_threads_for<VEC, C>() == 1024 &&
+         (RECOMP || (std::is_same<Tg, TF16>::value && NACC == 2));
 }
 
 // Whether kernel A pipelines the two exchanges of LayerNorm recompute across

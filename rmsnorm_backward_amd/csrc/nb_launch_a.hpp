@@ -24,11 +24,15 @@ hipError_t launch_bounded(const LaunchA& a) {
 }
 
 // Workgroups of at most 512 threads take the 512-thread-bound instantiation
-// where one exists (has_narrow_bound: recompute mode at 32 bytes per lane).
+// where one exists (has_narrow_bound) when their groups are long enough for
+// its steady-state loop (at least 5 full iterations of P rows, the ring
+// being 3 deep); short groups keep the 1024-thread-bound kernel (1151 x 8192
+// fp16 LayerNorm, 4 or 5 rows per group: 20.9 us against 21.6 us).
 template <class Tg, int KIND, bool RECOMP, int NACC, int VEC, int C, bool WSNT>
 hipError_t launch_one_policy(const LaunchA& a) {
-  if constexpr (has_narrow_bound<RECOMP, Tg, VEC, C>()) {
-    if (a.threads <= 512) return launch_bounded<Tg, KIND, RECOMP, NACC, VEC, C, WSNT, 512>(a);
+  if constexpr (has_narrow_bound<RECOMP, Tg, VEC, C, NACC>()) {
+    if (a.threads <= 512 && a.R >= (int64_t)5 * a.P + 1)
+      return launch_bounded<Tg, KIND, RECOMP, NACC, VEC, C, WSNT, 512>(a);
   }
   return launch_bounded<Tg, KIND, RECOMP, NACC, VEC, C, WSNT, max_threads_for<VEC, C>()>(a);
 }

@@ -65,6 +65,10 @@ SAVED = [
     ("layernorm", torch.float32, 512, 2, (40, 45, 90, 133)),          # P = 4, both gradients
     ("rmsnorm", torch.bfloat16, 512, 2, (78, 80, 95, 161, 250)),      # P = 8
     ("rmsnorm", torch.float16, 2048, 1, (9, 10, 11, 12, 29)),         # one group: P = 2
+    # fp16 with both gradients: groups of 11 rows and more (5 * P + 1) take
+    # the 512-thread-bound kernel and its steady-state loop, shorter ones the
+    # 1024-thread-bound kernel without it
+    ("layernorm", torch.float16, 2048, 2, (18, 20, 22, 23, 61)),      # P = 2
 ]
 
 
