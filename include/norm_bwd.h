@@ -269,14 +269,17 @@ typedef struct norm_bwd_plan {
 
 /*
  * Fill *plan for (kind, M, N, io_dtype, with_dbeta). groups = 0 chooses the
- * automatic group count: 2048 waves in flight divided by the waves per
- * workgroup, at most ceil(M / 4), and above 256 rounded down to a multiple of
- * 256 -- a function of the problem only, never of the device (the entry points
- * that recompute LayerNorm statistics aim at 4096 waves instead). groups > 0
- * asks for that many row groups, clamped to M so that no group is empty. A
- * plan is for saved statistics. The plan
- * assumes 16-byte aligned base pointers; norm_bwd_execute rejects a plan
- * whose vec the pointers do not allow. Host-only. Returns a status code.
+ * automatic group count: 256, at most ceil(M / 4) -- a function of the
+ * problem only, never of the device. (The entry points that recompute the
+ * statistics plan their own groups: 2048 waves in flight divided by the waves
+ * per workgroup, 4096 for LayerNorm, at most ceil(M / 4), above 256 rounded
+ * down to a multiple of 256.) groups > 0 asks for that many row groups,
+ * clamped to M so that no group is empty. The lane layout takes at most 32
+ * bytes of each operand per lane, then the fewest waves per row; the rows in
+ * flight per workgroup are the fewest whose x and dy reach 16 KiB. A plan is
+ * for saved statistics. The plan assumes 16-byte aligned base pointers;
+ * norm_bwd_execute rejects a plan whose vec the pointers do not allow.
+ * Host-only. Returns a status code.
  */
 int norm_bwd_make_plan(int kind, int64_t M, int64_t N, int io_dtype,
                        int with_dbeta, int64_t groups, norm_bwd_plan_t *plan);
