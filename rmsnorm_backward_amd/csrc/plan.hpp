@@ -60,8 +60,8 @@ int64_t forward_grid(int64_t M, int S, int P);
 int wgrad_lanes_per_row(int64_t N, int vec);
 
 // Automatic group count for (kind, M, N, io_dtype) and the statistics mode:
-// about 2048 waves in flight (4096 for LayerNorm in recompute mode), at least
-// 4 rows per group. Independent of the device.
+// 256 with saved statistics; in recompute mode about 2048 waves in flight
+// (4096 for LayerNorm); at least 4 rows per group. Independent of the device.
 int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype, bool recompute = false);
 
 // Fill *plan (see norm_bwd_make_plan). `vec_ok16` says whether the caller's
