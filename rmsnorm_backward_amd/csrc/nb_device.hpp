@@ -90,8 +90,9 @@ constexpr int kBufNonTemporal = 2;
 
 // A raw buffer resource over `bytes` bytes starting at p (stride 0; the
 // fourth word is the 32-bit data format gfx9-family parts take for raw
-// buffers). Loads at offsets past `bytes` read zeros, stores there write
-// nothing: the hardware's range check stands in for per-lane conditions.
+// buffers). The kernels address a row through it from a scalar base and a
+// 32-bit lane offset, and only where every lane's offset is inside the row
+// (the hardware would read zeros and drop stores past `bytes`).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
                                            0x00020000);
@@ -150,10 +151,8 @@ struct Pack {
       __builtin_nontemporal_store((uint16_t)w[0], reinterpret_cast<uint16_t*>(p));
     }
   }
-  // Streaming loads/stores through a buffer resource that spans the row
-  // (row_rsrc): at an offset past the row's end the load returns zeros and
-  // the store writes nothing, so lanes past the end need no condition and
-  // every lane issues the same memory instructions.
+  // Streaming loads/stores at byte offset `off` of a row's buffer resource
+  // (row_rsrc), with the same non-temporal hint as load_stream/store_stream.
   __device__ __forceinline__ void load_stream_buf(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
     if constexpr (kBytes == 16) {
       const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kBufNonTemporal);

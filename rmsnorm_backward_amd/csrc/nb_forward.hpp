@@ -106,7 +106,7 @@ void norm_fwd_kernel(const void* __restrict__ xv, const void* __restrict__ gv,
       }
     }
   };
-  // store one lane's chunk c of y (row base rb, in elements)
+  // store one lane's vector of y at column col (row base rb, in elements)
   auto store_y = [&](auto all, const PK& out, int64_t rb, int col) {
     constexpr bool ALL = decltype(all)::value;
     if constexpr (ALL)
