@@ -304,6 +304,8 @@ constexpr bool pipeline_ln_recompute() {
 // their register budget: one element per lane, 64 elements per lane, fp16
 // rows of 16 elements per lane with both gradients under the 1024-thread
 // bound, and recompute mode with more bytes per operand.
+constexpr int64_t kSteadyGroupBytes = (int64_t)2 << 20;
+
 template <bool RECOMP, class Tg, int VEC, int C, int NACC, int MAXT = max_threads_for<VEC, C>()>
 constexpr bool steady_loop() {
   return VEC > 1 && VEC * C <= 32 &&
@@ -694,8 +696,12 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
     int it0 = 0;
     constexpr bool kPipelined =
         RECOMP && KIND == kLayerNorm && pipeline_ln_recompute<Tg, VEC, C, NACC, MAXT>();
-    const bool steady =
-        steady_loop<RECOMP, Tg, VEC, C, NACC, MAXT>() && N == C * cstride && kfull >= 2 * D - 1;
+    // Groups that sweep more than kSteadyGroupBytes of each operand keep the
+    // general loop: there the steady-state loop lost 1.3-2% (65536 x 8192
+    // bf16 LayerNorm, 4 MiB per group), while at 2 MiB it was even
+    // (32768 x 8192) and up to 1 MiB it gained 2.5-5%.
+    const bool steady = steady_loop<RECOMP, Tg, VEC, C, NACC, MAXT>() && N == C * cstride &&
+                        kfull >= 2 * D - 1 && rows * (int64_t)N * EB <= kSteadyGroupBytes;
     if (steady) {
 #pragma unroll
       for (int k = 0; k < D - 1; ++k)
