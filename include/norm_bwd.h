@@ -270,10 +270,10 @@ typedef struct norm_bwd_plan {
 /*
  * Fill *plan for (kind, M, N, io_dtype, with_dbeta). groups = 0 chooses the
  * automatic group count: 256, at most ceil(M / 4) -- a function of the
- * problem only, never of the device. (The entry points that recompute the
- * statistics plan their own groups: 2048 waves in flight divided by the waves
- * per workgroup, 4096 for LayerNorm, at most ceil(M / 4), above 256 rounded
- * down to a multiple of 256.) groups > 0 asks for that many row groups,
+ * problem only, never of the device. (The entry points that recompute
+ * LayerNorm statistics plan their own: 512-thread workgroups and about 4096
+ * waves in flight, at most ceil(M / 4) groups, above 256 rounded down to a
+ * multiple of 256; RMSNorm recompute plans as here.) groups > 0 asks for that many row groups,
  * clamped to M so that no group is empty. The lane layout takes at most 32
  * bytes of each operand per lane, then the fewest waves per row; the rows in
  * flight per workgroup are the fewest whose x and dy reach 16 KiB. A plan is

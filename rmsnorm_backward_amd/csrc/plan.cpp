@@ -11,8 +11,8 @@
 namespace nb {
 
 namespace {
-// Kernel A with saved statistics: one workgroup per compute unit on a
-// 256-CU part (4096 x 16384 bf16 RMSNorm step: 72.6 us at 256 groups, 89.5 us
+// Kernel A with saved statistics (and in RMSNorm recompute mode): one
+// workgroup per compute unit on a 256-CU part (4096 x 16384 bf16 RMSNorm step: 72.6 us at 256 groups, 89.5 us
 // at the 128 that 2048 waves in flight would give).
 constexpr int64_t kSavedStatsGroups = 256;
 // Kernel A: rows in flight per workgroup, the fewest (a power of two) whose
@@ -21,11 +21,9 @@ constexpr int64_t kSavedStatsGroups = 256;
 // 262144 x 768 218.5 us at 8, 229.6 us at 4; 16384 x 4096 69.2 us at 1,
 // 69.9 us at 2).
 constexpr int64_t kRowBytesInFlight = 16384;
-// Recompute mode aims at a number of waves in flight instead.
-constexpr int64_t kTargetWaves = 2048;
 // LayerNorm in recompute mode exchanges twice per row; a second workgroup per
 // compute unit hides that latency (65536 x 8192 bf16: 570 us at 512 groups
-// against 645 us at 256), so it aims at twice the waves.
+// against 645 us at 256), so it aims at 4096 waves in flight.
 constexpr int64_t kRecomputeLnTargetWaves = 4096;
 // The forward streams one operand per row where kernel A streams two, so it
 // needs twice the waves (16 per compute unit) for as many bytes in flight.
@@ -39,10 +37,12 @@ constexpr int64_t kMinRowsPerGroup = 4;
 constexpr int64_t kGroupQuantum = 256;
 constexpr int64_t kMaxGrid = 1 << 20;
 constexpr int kMaxLdsBytes = 65536 - 1024;  // dynamic LDS; the kernel adds 256 B static
-// The forward and kernel A in recompute mode fill this many threads with
-// rows instead (recompute with one row per workgroup: 16384 x 4096 bf16
-// RMSNorm 76.0 us against 73.2 us at 512 threads, LayerNorm 89.7 us against
-// 85.2 us).
+// The forward and kernel A in LayerNorm recompute mode fill this many
+// threads with rows instead (LayerNorm recompute with the saved-statistics
+// rules: 65536 x 8192 bf16 563 -> 655 us, 16384 x 4096 82.4 -> 84.9 us).
+// RMSNorm recompute, one exchange per row as with saved statistics, takes
+// the saved-statistics rules (16384 x 4096 bf16 70.2 -> 67.9 us, 65536 x
+// 1024 75.6 -> 69.3 us, 4096 x 16384 105.7 -> 76.6 us).
 constexpr int kRowStatsThreads = 512;
 // At most this many bytes of each operand per lane (16 bf16/fp16 or 8 fp32
 // elements) before wider lanes are considered: 16384 x 4096 fp32 RMSNorm
@@ -203,20 +203,20 @@ int wgrad_lanes_per_row(int64_t N, int vec) {
 
 int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype, bool recompute) {
   if (M <= 0) return 0;
-  // Saved statistics: kSavedStatsGroups. Recompute mode: enough workgroups
-  // for about kTargetWaves waves in flight (8 per compute unit on a 256-CU
-  // part; twice that for LayerNorm). Never fewer than kMinRowsPerGroup rows
+  // kSavedStatsGroups, except in LayerNorm recompute mode: enough
+  // workgroups for about kRecomputeLnTargetWaves waves in flight (16 per
+  // compute unit on a 256-CU part). Never fewer than kMinRowsPerGroup rows
   // per group, above kGroupQuantum a multiple of it. The geometry is itself
   // a function of (kind, N, io_dtype), so the group count depends on the
   // problem only, never on the device.
   int64_t G = kSavedStatsGroups;
-  if (recompute) {
+  if (recompute && kind == NORM_BWD_LAYERNORM) {
     norm_bwd_plan_t g;
     const char* why = nullptr;
     int waves = 8;
     if (N > 0 && make_geometry(kind, N, io_dtype, 0, true, &g, &why, true) == NORM_BWD_OK)
       waves = g.threads / 64;
-    G = (kind == NORM_BWD_LAYERNORM ? kRecomputeLnTargetWaves : kTargetWaves) / waves;
+    G = kRecomputeLnTargetWaves / waves;
   }
   const int64_t cap = ceil_div(M, kMinRowsPerGroup);
   if (G > cap) G = cap;
@@ -247,7 +247,8 @@ int make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,
   const int nacc = with_dbeta ? 2 : 1;
 
   const char* gwhy = nullptr;
-  const int st = make_geometry(kind, N, io_dtype, with_dbeta, vec_ok16, &p, &gwhy, recompute);
+  const int st = make_geometry(kind, N, io_dtype, with_dbeta, vec_ok16, &p, &gwhy,
+                               recompute && kind == NORM_BWD_LAYERNORM);
   if (st != NORM_BWD_OK) return fail(why, gwhy, st);
   if (N == 0) {  // nothing to compute
     *plan = p;

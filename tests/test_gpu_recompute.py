@@ -138,12 +138,12 @@ def test_recompute_full_size_sampled(nb, w):
 
 
 def recompute_plan(nb, kind, M, N, dt, db):
-    """The plan recompute mode runs, as a saved-statistics plan: the same
-    lane layout, the rows in flight that fill 512 threads (one when the
-    combine buffer would not fit in LDS), and the recompute group count
-    (about 2048 waves in flight, 4096 for LayerNorm, counted on the
-    dbeta-less layout; at least 4 rows per group; above 256 a multiple of
-    256)."""
+    """The plan recompute mode runs, as a saved-statistics plan. RMSNorm
+    recompute takes the saved-statistics plan itself. LayerNorm recompute
+    keeps the lane layout but fills 512 threads with rows (one when the
+    combine buffer would not fit in LDS), with its own group count (about
+    4096 waves in flight, counted on the dbeta-less layout; at least 4 rows
+    per group; above 256 a multiple of 256)."""
     def rows(S, C, vec, nacc):
         P = max(1, 512 // (64 * S))
         while P > 1 and S * P * 64 > (512 if vec * C > 16 else 1024):
@@ -151,8 +151,10 @@ def recompute_plan(nb, kind, M, N, dt, db):
         return 1 if P > 1 and nacc * S * C * 64 * vec * 4 > 65536 - 1024 else P
 
     base = nb.norm_bwd_make_plan(kind, M, N, dt, db)
+    if kind == "rmsnorm":
+        return base
     S, C, vec = base.waves_per_row, base.chunks, base.vec
-    G = min((4096 if kind == "layernorm" else 2048) // (S * rows(S, C, vec, 1)), -(-M // 4))
+    G = min(4096 // (S * rows(S, C, vec, 1)), -(-M // 4))
     G = max(1, G - G % 256 if G > 256 else G)
     p = nb.norm_bwd_make_plan(kind, M, N, dt, db, G)
     P = rows(S, C, vec, 2 if db else 1)

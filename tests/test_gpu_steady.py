@@ -96,14 +96,15 @@ def test_steady_loop_saved_statistics(nb, kind, dt, N, G, M):
 
 # Recompute mode runs the steady-state loop where a lane holds one 16-byte
 # vector per operand (RMSNorm, and LayerNorm's pipelined loop), and two under
-# the 512-thread launch bound its 512-thread workgroups take (the fp16
-# LayerNorm kernel with both gradients there keeps its two exchanges per row).
+# the 512-thread launch bound that workgroups of up to 512 threads take when
+# their groups hold at least 5 * P + 1 rows (the fp16 LayerNorm kernel with
+# both gradients there keeps its two exchanges per row).
 RECOMPUTE = [
     ("rmsnorm", torch.bfloat16, 512, 2, (78, 80, 95, 250)),           # P = 8
     ("layernorm", torch.bfloat16, 512, 2, (78, 80, 95, 250)),         # P = 8, pipelined
     ("layernorm", torch.float32, 256, 1, (39, 40, 41, 77)),           # P = 8, pipelined
     ("layernorm", torch.float16, 2048, 2, (38, 40, 47, 126)),         # P = 4, two exchanges
-    ("rmsnorm", torch.bfloat16, 4096, 3, (24, 30, 35, 77)),           # P = 2, 512-thread bound
+    ("rmsnorm", torch.bfloat16, 4096, 3, (12, 15, 19, 77)),           # P = 1, 512-thread bound
 ]
 
 

@@ -105,18 +105,18 @@ def _row_stats_rows(p, db):
 
 
 def _auto_groups(nb, kind, M, N, dt, recompute=False):
-    """The documented rule: 256 groups with saved statistics; in recompute
-    mode about 2048 waves in flight (4096 for LayerNorm), the waves per
-    workgroup coming from the (dbeta-less) geometry; always >= 4 rows per
+    """The documented rule: 256 groups, except in LayerNorm recompute mode:
+    about 4096 waves in flight, the waves per workgroup coming from the
+    (dbeta-less) lane layout with 512-thread workgroups; always >= 4 rows per
     group, above 256 a multiple of 256."""
     if M == 0:
         return 0
-    if recompute:
+    if recompute and kind == "layernorm":
         waves = 8
         if N:
             p = nb.norm_bwd_make_plan(kind, 1, N, dt, False)
             waves = p.waves_per_row * _row_stats_rows(p, False)
-        g = (4096 if kind == "layernorm" else 2048) // waves
+        g = 4096 // waves
     else:
         g = 256
     g = min(g, -(-M // 4))
