@@ -237,8 +237,8 @@ int norm_bwd_wgrad(int kind, const void *x, const void *dy, const float *mean,
 
 /*
  * (Declared above.) norm_bwd_workspace_bytes returns enough for the automatic
- * plan of either statistics mode: LayerNorm in recompute mode plans twice the
- * row groups (two workgroups per compute unit hide its second exchange per
+ * plan of either statistics mode: LayerNorm in recompute mode plans more row
+ * groups (a second workgroup per compute unit hides its second exchange per
  * row), so for LayerNorm it is max(saved-statistics plan, recompute plan).
  */
 
@@ -273,8 +273,9 @@ typedef struct norm_bwd_plan {
  * problem only, never of the device. (The entry points that recompute
  * LayerNorm statistics plan their own: 512-thread workgroups and about 4096
  * waves in flight, at most ceil(M / 4) groups, above 256 rounded down to a
- * multiple of 256; RMSNorm recompute plans as here.) groups > 0 asks for that many row groups,
- * clamped to M so that no group is empty. The lane layout takes at most 32
+ * multiple of 256; RMSNorm recompute plans as here.) groups > 0 asks for
+ * that many row groups, clamped to M so that no group is empty. The lane
+ * layout takes at most 32
  * bytes of each operand per lane, then the fewest waves per row; the rows in
  * flight per workgroup are the fewest whose x and dy reach 16 KiB. A plan is
  * for saved statistics. The plan assumes 16-byte aligned base pointers;
