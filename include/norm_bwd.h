@@ -275,9 +275,9 @@ typedef struct norm_bwd_plan {
  * waves in flight, at most ceil(M / 4) groups, above 256 rounded down to a
  * multiple of 256; RMSNorm recompute plans as here.) groups > 0 asks for
  * that many row groups, clamped to M so that no group is empty. The lane
- * layout takes at most 32
- * bytes of each operand per lane, then the fewest waves per row; the rows in
- * flight per workgroup are the fewest whose x and dy reach 16 KiB. A plan is
+ * layout takes at most 32 bytes of each operand per lane, then the fewest
+ * waves per row; the rows in flight per workgroup are the fewest whose x and
+ * dy reach 16 KiB. A plan is
  * for saved statistics. The plan assumes 16-byte aligned base pointers;
  * norm_bwd_execute rejects a plan whose vec the pointers do not allow.
  * Host-only. Returns a status code.
