@@ -4,21 +4,33 @@
 One step = one full backward pass (kernel A: dx + per-group partial
 dgamma/dbeta; kernel B: fixed-order reduction of the partials) over one batch
 of synthetic, seeded inputs already resident in HBM. The headline workload is
-the 16384 x 4096 bf16 RMSNorm backward (fp32 rstd and dgamma).
+the 16384 x 4096 bf16 RMSNorm backward (fp32 rstd and dgamma), the worked
+example of "Norm backward in Triton -- the dγ/dβ reduction".
+
+A default run measures, in this order: the streaming ceiling (a
+2-read:1-write non-temporal triad probe swept over launch shapes), the
+headline workload (exactly --steps timed steps after --warmup untimed ones,
+plus its forward, recompute mode, strided/accumulating call and column walk),
+then each other workload (128 x 512 fp32 LayerNorm and RMSNorm, 1151 x 8192
+fp16 LayerNorm, 65536 x 8192 bf16 LayerNorm, 262144 x 768 bf16 RMSNorm), and
+last the fp64 CPU oracle on each workload's inputs, on one thread and on
+every core. --workload NAME measures that one workload alone.
 
 Timing: HIP events recorded on the stream the library launches on (torch's
-current stream), around exactly --steps calls after --warmup untimed calls.
-Input/output buffer sets are rotated so that consecutive steps touch
-different memory (the set count makes the rotation exceed the 256 MB
-Infinity Cache several times over): every step streams from HBM.
+current stream). Input/output buffer sets are rotated so that consecutive
+steps touch different memory (the set count makes the rotation exceed the
+256 MB Infinity Cache several times over): every step streams from HBM,
+except where all sets together fit in that cache (128 x 512, flagged
+cache_resident).
 
 The saved statistics the backward reads are produced by the library's GPU
 forward; the forward is also timed on its own (config.forward).
 
-Prints ONE JSON line. `value` is algorithmic GB/s of the whole step:
-  bytes = read x, dy, gamma, saved stats; write dx, dgamma(, dbeta)
-(workspace traffic excluded). `roofline` is kernel A alone against the
-8 TB/s HBM peak; `cpu_baseline` is the fp64 CPU oracle timed on this host.
+Prints ONE JSON line. `value` is algorithmic GB/s of the headline's whole
+step: bytes = read x, dy, gamma, saved stats; write dx, dgamma(, dbeta)
+(workspace traffic excluded). `roofline` is kernel A alone against the 8 TB/s
+HBM peak; `cpu_baseline` is the fp64 CPU oracle timed on this host;
+`config.workloads` holds one entry per workload with the same figures.
 """
 
 from __future__ import annotations
@@ -50,6 +62,14 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="one-thread oracle time on the primary workload")
+    ap.add_argument("--cpu-seconds-other", type=float, default=3.0,
+                    help="one-thread oracle time on each other workload")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the forward, recompute, strided and column-walk measurements")
+    ap.add_argument("--no-wide", action="store_true", help="skip the wide-row measurement")
+    ap.add_argument("--no-triad", action="store_true", help="skip the triad ceiling sweep")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0 = auto)")
     ap.add_argument("--groups", type=int, default=0, help="explicit row-group count (0 = auto)")
     return ap.parse_args(argv)
@@ -169,9 +189,10 @@ def measure_wide(torch, nb, W, lib, dev, stream, args):
             "forward_pct_of_peak": round(100 * f_bytes / (ms_f * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2)}
 
 
-def cpu_baseline(w, inp):
+def cpu_baseline(w, inp, seconds=10.0, seconds_threads=5.0):
     """The fp64 oracle (plain C, one thread) on the same workload, timed on
-    this host. Inputs are widened to fp64 before the clock starts."""
+    this host for about `seconds`; then on every core for `seconds_threads`.
+    Inputs are widened to fp64 before the clock starts."""
     import numpy as np
 
     import oracle
@@ -185,9 +206,10 @@ def cpu_baseline(w, inp):
     m64, r64 = o.fwd_stats(w.kind, x, w.eps)
     rstd = r64.astype(np.float32).astype(np.float64)
     mean = m64.astype(np.float32).astype(np.float64) if w.kind == "layernorm" else None
-    # repeat the pass until about 10 s of CPU time has accumulated (at most 200)
+    # repeat the pass until about `seconds` of CPU time has accumulated (at
+    # most 200 passes)
     reps, total = 0, 0.0
-    while reps < 200 and (total < 10.0 or reps < 1):
+    while reps < 200 and (total < seconds or reps < 1):
         t0 = time.perf_counter()
         o.bwd(w.kind, x, dy, gamma, mean, rstd, want_dbeta=w.kind == "layernorm")
         total += time.perf_counter() - t0
@@ -203,7 +225,7 @@ def cpu_baseline(w, inp):
            "kind": "oracle", "sample": sample, "seconds_per_pass": round(dt, 4),
            "cpu_model": cpu_model()}
     out["all_cores"] = cpu_baseline_threads(o, w, x, dy, gamma, mean, rstd,
-                                            ws.algorithmic_bytes())
+                                            ws.algorithmic_bytes(), seconds_threads)
     return out
 
 
@@ -257,32 +279,40 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def main(argv=None) -> int:
-    args = parse_args(argv)
-    if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: the library and this benchmark "
-              "run on one GPU (the sharding across GPUs is described, not implemented). "
-              "Use --gpus 1.", file=sys.stderr)
-        return 2
+def triad_sweep(torch, nb, dev, stream, operand_bytes):
+    """The 2-read:1-write streaming ceiling: norm_bwd_probe_triad over three
+    operands of `operand_bytes` each (together several times the 256 MB
+    Infinity Cache), swept over launch shapes; the fastest is the ceiling."""
+    n = operand_bytes // 4
+    a = torch.empty(n, dtype=torch.int32, device=dev).fill_(1)
+    b = torch.empty_like(a).fill_(2)
+    c = torch.empty_like(a)
+    sweep = []
+    for grid in (1024, 2048, 4096, 8192, 0):
+        for unroll in (1, 2, 4, 8):
+            for _ in range(3):
+                nb.norm_bwd_probe_triad(a, b, c, grid, unroll)
+            ms = time_loop(torch, lambda i: nb.norm_bwd_probe_triad(a, b, c, grid, unroll), 10,
+                           stream)
+            sweep.append((grid, unroll, 3 * operand_bytes / (ms * 1e-3) / 1e9))
+    torch.cuda.synchronize()
+    ok = bool(torch.all(c == 3).item())
+    del a, b, c
+    torch.cuda.empty_cache()
+    best = max(sweep, key=lambda t: t[2])
+    return {"kernel": "triad_probe_kernel", "what": "c = a + b, 16-byte non-temporal loads and "
+            "stores, 2 reads : 1 write as kernel A", "bytes_per_operand": operand_bytes,
+            "GBps": round(best[2], 1), "grid": best[0], "unroll": best[1],
+            "pct_of_peak": round(100 * best[2] / PEAK_HBM_GBPS, 2), "result_ok": ok,
+            "sweep_min_GBps": round(min(t[2] for t in sweep), 1), "launch_shapes": len(sweep)}
 
-    import torch
 
-    import rmsnorm_backward_amd as nb
-    from rmsnorm_backward_amd import workloads as W
-
-    if not os.path.exists(nb.LIB_PATH):
-        from rmsnorm_backward_amd import _build
-        _build.build()
-    lib = nb.load_library()
-    if not torch.cuda.is_available():
-        print("bench.py: no GPU visible", file=sys.stderr)
-        return 1
-    w = W.WORKLOADS[args.workload] if args.workload else W.HEADLINE
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream(dev)
+def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, extras, triad):
+    """Time one workload's backward step (kernel A + kernel B through the named
+    entry point), kernel A alone and kernel B alone on rotating buffer sets;
+    with `extras` also the forward, recompute mode, the strided/accumulating
+    call and the column walk. Returns (entry, plan dict, extras dict, inputs)."""
     sh = ctypes.c_void_p(stream.cuda_stream)
-
     inp = W.make_inputs(w)
     with_db = w.kind == "layernorm"
     io = nb._DTYPE_CODE[w.io_dtype]
@@ -353,6 +383,67 @@ def main(argv=None) -> int:
         if st:
             raise RuntimeError(nb.norm_bwd_last_error())
 
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms = time_loop(torch, step, steps, stream)
+    # the spread of the step time: 20 loops of 25 steps, each loop's mean
+    chunks = sorted(time_loop(torch, step, 25, stream) for _ in range(20))
+    ms_a = time_loop(torch, step_a, steps, stream)
+    ms_b = time_loop(torch, step_b, max(steps, 50), stream)
+
+    alg = w.algorithmic_bytes()
+    value = alg / (ms * 1e-3) / 1e9
+    a_bytes = kernel_a_bytes(w)
+    achieved = a_bytes / (ms_a * 1e-3) / 1e9
+    entry = {
+        "workload": w.name, "kind": w.kind, "M": w.M, "N": w.N,
+        "io_dtype": W._dt(w.io_dtype), "wgrad_dtype": W._dt(w.wgrad_dtype), "eps": w.eps,
+        "seed": w.seed, "algorithmic_bytes": alg, "steps": steps,
+        "step_us": round(ms * 1e3, 3), "GBps": round(value, 2),
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+        "rows_per_s": round(w.M / (ms * 1e-3), 1),
+        "step_us_spread": {"loops": len(chunks), "steps_per_loop": 25,
+                           "median": round(chunks[len(chunks) // 2] * 1e3, 3),
+                           "min": round(chunks[0] * 1e3, 3), "max": round(chunks[-1] * 1e3, 3)},
+        "kernel_a_us": round(ms_a * 1e3, 3), "kernel_a_bytes": a_bytes,
+        "kernel_a_GBps": round(achieved, 2),
+        "kernel_a_frac": round(achieved / PEAK_HBM_GBPS, 4),
+        "kernel_a_traffic": committed_traffic(w.name),
+        "kernel_b_alone_us": round(ms_b * 1e3, 3),
+        "kernel_b_in_place_us": round((ms - ms_a) * 1e3, 3),
+        "workspace_bytes": plan.workspace_bytes,
+        "counted_GBps_incl_workspace": round((alg + 2 * plan.workspace_bytes) / (ms * 1e-3) / 1e9,
+                                             2),
+        "buffer_sets": nsets,
+        "cache_resident": nsets * set_bytes <= MALL_BYTES,
+    }
+    if triad:
+        entry["pct_of_triad"] = round(100 * value / triad["GBps"], 2)
+        entry["kernel_a_pct_of_triad"] = round(100 * achieved / triad["GBps"], 2)
+    plan_d = {k: v for k, v in plan.as_dict().items()
+              if k in ("groups", "rows_per_group", "vec", "chunks", "waves_per_row",
+                       "rows_in_flight", "threads", "grid")}
+    entry["plan"] = plan_d
+    more = {}
+    if extras:
+        more = measure_extras(torch, nb, W, lib, dev, stream, w, args, steps, warmup, sets,
+                              base, full_args, dgamma, dbeta, ws, io, wg, set_bytes)
+    del sets, base, ws, dgamma, dbeta, full_args, part_args
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return entry, more, inp
+
+
+def measure_extras(torch, nb, W, lib, dev, stream, w, args, steps, warmup, sets, base, full_args,
+                   dgamma, dbeta, ws, io, wg, set_bytes):
+    """The forward, recompute mode, norm_bwd_ex (strided, accumulating) and the
+    column walk on the same buffers; the copy probe; wide rows."""
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    nsets = len(sets)
+    with_db = w.kind == "layernorm"
+    P = ctypes.c_void_p
+    ptr = lambda t: None if t is None else P(t.data_ptr())  # noqa: E731
     # the forward that produces the statistics, into per-set y and stats
     # buffers (y lands in the dx buffer of the set, which the backward rewrites)
     fwd_args = []
@@ -370,22 +461,14 @@ def main(argv=None) -> int:
         if st:
             raise RuntimeError(nb.norm_bwd_last_error())
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    ms = time_loop(torch, step, args.steps, stream)
-    # the spread of the step time: 20 loops of 25 steps, each loop's mean
-    chunks = sorted(time_loop(torch, step, 25, stream) for _ in range(20))
-    ms_a = time_loop(torch, step_a, args.steps, stream)
-    ms_b = time_loop(torch, step_b, max(args.steps, 50), stream)
-    for i in range(min(args.warmup, 50)):
+    for i in range(min(warmup, 50)):
         step_f(i)
-    ms_f = time_loop(torch, step_f, args.steps, stream)
+    ms_f = time_loop(torch, step_f, steps, stream)
     f_bytes = forward_bytes(w, "beta" in base)
 
     # the backward in recompute mode: NULL statistics, recomputed from x
     rc_args = [(a[0], a[1], a[2], None, None) + a[5:] if w.kind == "layernorm"
-                else (a[0], a[1], a[2], None) + a[4:] for a in full_args]
+               else (a[0], a[1], a[2], None) + a[4:] for a in full_args]
     fn_rc = lib.norm_bwd_layernorm if w.kind == "layernorm" else lib.norm_bwd_rmsnorm
 
     def step_rc(i):
@@ -393,9 +476,9 @@ def main(argv=None) -> int:
         if st:
             raise RuntimeError(nb.norm_bwd_last_error())
 
-    for i in range(min(args.warmup, 50)):
+    for i in range(min(warmup, 50)):
         step_rc(i)
-    ms_rc = time_loop(torch, step_rc, args.steps, stream)
+    ms_rc = time_loop(torch, step_rc, steps, stream)
     rc_bytes = w.algorithmic_bytes() - w.M * (8 if w.kind == "layernorm" else 4)
 
     # norm_bwd_ex: x, dy, dx as row-strided views (row stride N + 64 elements)
@@ -432,9 +515,9 @@ def main(argv=None) -> int:
     dgamma.zero_()
     if dbeta is not None:
         dbeta.zero_()
-    for i in range(min(args.warmup, 50)):
+    for i in range(min(warmup, 50)):
         step_ex(i)
-    ms_ex = time_loop(torch, step_ex, args.steps, stream)
+    ms_ex = time_loop(torch, step_ex, steps, stream)
 
     # weight gradients alone by the column walk (no dx, no workspace)
     def step_cw(i):
@@ -445,16 +528,54 @@ def main(argv=None) -> int:
         if st:
             raise RuntimeError(nb.norm_bwd_last_error())
 
-    for i in range(min(args.warmup, 50)):
+    for i in range(min(warmup, 50)):
         step_cw(i)
-    ms_cw = time_loop(torch, step_cw, args.steps, stream)
+    ms_cw = time_loop(torch, step_cw, steps, stream)
     cw_bytes = w.M * (2 * w.N * w.io_bytes + (8 if with_db else 4)) + \
         w.N * w.wgrad_bytes * (2 if with_db else 1)
     ex_bytes = w.algorithmic_bytes() + w.N * w.wgrad_bytes * (2 if with_db else 1)
     del ex_keep, ex_args
+    torch.cuda.empty_cache()
 
-    # copy probe: the achievable streaming ceiling next to the kernels
-    cp_bytes = min(512 << 20, max(set_bytes // 3 * 2, 64 << 20)) // 16 * 16
+    wide = measure_wide(torch, nb, W, lib, dev, stream, args) if not args.no_wide else None
+    out = {
+        "forward": {
+            "kernel": "norm_fwd_kernel", "us": round(ms_f * 1e3, 3),
+            "bytes_per_launch": f_bytes, "with_beta": "beta" in base,
+            "GBps": round(f_bytes / (ms_f * 1e-3) / 1e9, 2),
+            "traffic": committed_forward_traffic(w.name),
+            "pct_of_peak": round(100 * f_bytes / (ms_f * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+        },
+        "recompute": {
+            "what": "whole backward step with mean/rstd recomputed from x (no stats read)",
+            "groups": nb.norm_bwd_workspace_bytes(w.kind, w.M, w.N, io, with_db) //
+            (w.N * 4 * (2 if with_db else 1)),
+            "us": round(ms_rc * 1e3, 3), "bytes": rc_bytes,
+            "GBps": round(rc_bytes / (ms_rc * 1e-3) / 1e9, 2),
+            "pct_of_peak": round(100 * rc_bytes / (ms_rc * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+        },
+        "strided_accumulate": {
+            "what": "norm_bwd_ex: x, dy, dx row stride N+64, dgamma/dbeta accumulated",
+            "us": round(ms_ex * 1e3, 3), "bytes": ex_bytes,
+            "GBps": round(ex_bytes / (ms_ex * 1e-3) / 1e9, 2),
+            "pct_of_peak": round(100 * ex_bytes / (ms_ex * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+        },
+        "colwalk_wgrad": {
+            "what": "dgamma/dbeta alone by the column walk (reads x, dy, stats; no dx)",
+            "kernel": "wgrad_colwalk_kernel", "us": round(ms_cw * 1e3, 3), "bytes": cw_bytes,
+            "GBps": round(cw_bytes / (ms_cw * 1e-3) / 1e9, 2),
+            "pct_of_peak": round(100 * cw_bytes / (ms_cw * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+        },
+    }
+    if wide is not None:
+        out["wide_rows"] = wide
+    return out
+
+
+def copy_probe(torch, nb, dev, stream, nbytes):
+    """The library's plain copy kernel over `nbytes` (the counter calibration
+    reference of the profiles)."""
+    cp_bytes = nbytes // 16 * 16
     src = torch.empty(cp_bytes // 4, dtype=torch.int32, device=dev).fill_(1)
     dsts = [torch.empty_like(src) for _ in range(2)]
     srcs = [src, src.clone()]
@@ -462,87 +583,120 @@ def main(argv=None) -> int:
         nb.norm_bwd_probe_copy(srcs[i % 2], dsts[i % 2])
     ms_cp = time_loop(torch, lambda i: nb.norm_bwd_probe_copy(srcs[i % 2], dsts[i % 2]),
                       20, stream)
-    copy_gbps = 2 * cp_bytes / (ms_cp * 1e-3) / 1e9
     del src, dsts, srcs
+    torch.cuda.empty_cache()
+    return cp_bytes, 2 * cp_bytes / (ms_cp * 1e-3) / 1e9
 
-    wide = measure_wide(torch, nb, W, lib, dev, stream, args)
 
-    alg = w.algorithmic_bytes()
-    value = alg / (ms * 1e-3) / 1e9
-    a_bytes = kernel_a_bytes(w)
-    achieved = a_bytes / (ms_a * 1e-3) / 1e9
-    traffic = committed_traffic(w.name)
+# The default run: the five workloads (the first with its RMSNorm variant),
+# in their order; the headline is measured first and carries the line's
+# top-level fields.
+DEFAULT_ORDER = ("layernorm_f32_128x512", "rmsnorm_f32_128x512", "layernorm_f16_1151x8192",
+                 "rmsnorm_bf16_16384x4096", "layernorm_bf16_65536x8192",
+                 "rmsnorm_bf16_262144x768")
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: the library and this benchmark "
+              "run on one GPU (the sharding across GPUs is described, not implemented). "
+              "Use --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import rmsnorm_backward_amd as nb
+    from rmsnorm_backward_amd import workloads as W
+
+    if not os.path.exists(nb.LIB_PATH):
+        from rmsnorm_backward_amd import _build
+        _build.build()
+    lib = nb.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    primary = W.WORKLOADS[args.workload] if args.workload else W.HEADLINE
+    others = [] if args.workload else [W.WORKLOADS[n] for n in DEFAULT_ORDER
+                                       if n != primary.name]
+
+    # the streaming ceiling (first: it also brings the GPU clock up)
+    triad = triad_sweep(torch, nb, dev, stream, 512 << 20) if not args.no_triad else None
+    print(f"bench.py: triad ceiling {triad and triad['GBps']} GB/s", file=sys.stderr, flush=True)
+
+    entries = {}
+    cpu_inputs = {}
+    entry, extras, inp = measure_workload(torch, nb, W, lib, dev, stream, primary, args,
+                                          args.steps, args.warmup, not args.no_extras, triad)
+    entries[primary.name] = entry
+    cpu_inputs[primary.name] = inp
+    print(f"bench.py: {primary.name} step {entry['step_us']} us", file=sys.stderr, flush=True)
+    cp_bytes, copy_gbps = copy_probe(torch, nb, dev, stream,
+                                     min(512 << 20, max(2 * primary.M * primary.N *
+                                                        primary.io_bytes, 64 << 20)))
+    for w in others:
+        e, _, inp = measure_workload(torch, nb, W, lib, dev, stream, w, args,
+                                     max(args.steps, 200), max(args.warmup, 20), False, triad)
+        entries[w.name] = e
+        cpu_inputs[w.name] = inp
+        print(f"bench.py: {w.name} step {e['step_us']} us", file=sys.stderr, flush=True)
+
+    # the CPU oracle on the same inputs (after every GPU measurement)
+    if not args.no_cpu_baseline:
+        for name, e in entries.items():
+            w = W.WORKLOADS[name]
+            secs = args.cpu_seconds if name == primary.name else args.cpu_seconds_other
+            e["cpu_oracle"] = cpu_baseline(w, cpu_inputs[name], secs, max(secs / 2, 1.0))
+            print(f"bench.py: {name} cpu oracle {e['cpu_oracle']['value']} GB/s",
+                  file=sys.stderr, flush=True)
+    del cpu_inputs
+
+    e = entries[primary.name]
+    order = [n for n in DEFAULT_ORDER if n in entries] + \
+        [n for n in entries if n not in DEFAULT_ORDER]
+    config = {
+        "workload": primary.name, "kind": primary.kind, "M": primary.M, "N": primary.N,
+        "io_dtype": e["io_dtype"], "wgrad_dtype": e["wgrad_dtype"], "stats_dtype": "f32",
+        "eps": primary.eps, "seed": primary.seed, "algorithmic_bytes": e["algorithmic_bytes"],
+        "pct_of_peak": e["pct_of_peak"], "rows_per_s": e["rows_per_s"],
+        "step_us_spread": e["step_us_spread"],
+        "kernel_a_us": e["kernel_a_us"], "kernel_b_us": e["kernel_b_alone_us"],
+        "kernel_b_in_place_us": e["kernel_b_in_place_us"],
+        "copy_probe_GBps": round(copy_gbps, 1), "copy_probe_bytes": cp_bytes,
+        "triad_probe": triad,
+        "pct_of_triad": e.get("pct_of_triad"),
+        "buffer_sets": e["buffer_sets"], "workspace_bytes": e["workspace_bytes"],
+        "counted_GBps_incl_workspace": e["counted_GBps_incl_workspace"],
+        "plan": e["plan"],
+    }
+    config.update(extras)
+    config["workloads"] = [entries[n] for n in order]
     result = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": e["GBps"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 6),
+        "ms_per_step": round(e["step_us"] / 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {
-            "workload": w.name, "kind": w.kind, "M": w.M, "N": w.N,
-            "io_dtype": W._dt(w.io_dtype), "wgrad_dtype": W._dt(w.wgrad_dtype),
-            "stats_dtype": "f32", "eps": w.eps, "seed": w.seed,
-            "algorithmic_bytes": alg, "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
-            "rows_per_s": round(w.M / (ms * 1e-3), 1),
-            "step_us_spread": {"loops": len(chunks), "steps_per_loop": 25,
-                               "median": round(chunks[len(chunks) // 2] * 1e3, 3),
-                               "min": round(chunks[0] * 1e3, 3),
-                               "max": round(chunks[-1] * 1e3, 3)},
-            "kernel_a_us": round(ms_a * 1e3, 3), "kernel_b_us": round(ms_b * 1e3, 3),
-            "copy_probe_GBps": round(copy_gbps, 1),
-            "copy_probe_bytes": cp_bytes,
-            "pct_of_copy_probe": round(100 * value / copy_gbps, 2),
-            "buffer_sets": nsets,
-            "workspace_bytes": plan.workspace_bytes,
-            "counted_GBps_incl_workspace": round(
-                (alg + 2 * plan.workspace_bytes) / (ms * 1e-3) / 1e9, 2),
-            "forward": {
-                "kernel": "norm_fwd_kernel", "us": round(ms_f * 1e3, 3),
-                "bytes_per_launch": f_bytes, "with_beta": "beta" in base,
-                "GBps": round(f_bytes / (ms_f * 1e-3) / 1e9, 2),
-                "traffic": committed_forward_traffic(w.name),
-                "pct_of_peak": round(100 * f_bytes / (ms_f * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
-            },
-            "recompute": {
-                "what": "whole backward step with mean/rstd recomputed from x (no stats read)",
-                "groups": nb.norm_bwd_workspace_bytes(w.kind, w.M, w.N, io, with_db) //
-                (w.N * 4 * (2 if with_db else 1)),
-                "us": round(ms_rc * 1e3, 3), "bytes": rc_bytes,
-                "GBps": round(rc_bytes / (ms_rc * 1e-3) / 1e9, 2),
-                "pct_of_peak": round(100 * rc_bytes / (ms_rc * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
-            },
-            "strided_accumulate": {
-                "what": "norm_bwd_ex: x, dy, dx row stride N+64, dgamma/dbeta accumulated",
-                "us": round(ms_ex * 1e3, 3), "bytes": ex_bytes,
-                "GBps": round(ex_bytes / (ms_ex * 1e-3) / 1e9, 2),
-                "pct_of_peak": round(100 * ex_bytes / (ms_ex * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
-            },
-            "colwalk_wgrad": {
-                "what": "dgamma/dbeta alone by the column walk (reads x, dy, stats; no dx)",
-                "kernel": "wgrad_colwalk_kernel", "us": round(ms_cw * 1e3, 3), "bytes": cw_bytes,
-                "GBps": round(cw_bytes / (ms_cw * 1e-3) / 1e9, 2),
-                "pct_of_peak": round(100 * cw_bytes / (ms_cw * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
-            },
-            "wide_rows": wide,
-            "plan": {k: v for k, v in plan.as_dict().items()
-                     if k in ("groups", "rows_per_group", "vec", "chunks", "waves_per_row",
-                              "rows_in_flight", "threads", "grid")},
-        },
+        "config": config,
         "roofline": {
-            "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
-            "kernel": "dx_partials_kernel", "bytes_per_launch": a_bytes,
+            "bound": "hbm", "achieved": e["kernel_a_GBps"], "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": e["kernel_a_frac"], "traffic": e["kernel_a_traffic"],
+            "kernel": "dx_partials_kernel", "bytes_per_launch": e["kernel_a_bytes"],
         },
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, inp)
+    if "cpu_oracle" in e:
+        result["cpu_baseline"] = e["cpu_oracle"]
     print(json.dumps(result), flush=True)
     return 0
 

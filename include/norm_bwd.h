@@ -358,6 +358,25 @@ const char *norm_bwd_last_error(void);
  */
 int norm_bwd_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
 
+/*
+ * Measurement aid, not part of the backward pass: the streaming ceiling for
+ * kernel A's access mix (the dx pass reads x and dy and writes dx once each:
+ * "Norm backward in Triton", "Worked numbers", counts exactly these bytes).
+ * c = a + b over `bytes` bytes of each operand, taken as 32-bit words, with
+ * 16-byte non-temporal loads and stores, on `stream`. Moves 3 * bytes.
+ *   a, b     read; c written; 16-byte aligned device pointers; c may not
+ *            overlap a or b (a and b may be the same buffer)
+ *   bytes    bytes per operand, a multiple of 16
+ *   grid     workgroups of 256 threads (1 .. 2^20), or 0 for one pass over
+ *            the data (each thread handles `unroll` vectors once)
+ *   unroll   16-byte vectors per operand each thread loads before it stores
+ *            (1, 2, 4 or 8)
+ * Returns a status code; NORM_BWD_ERR_INVALID_ARG for arguments outside these
+ * ranges, with nothing launched.
+ */
+int norm_bwd_probe_triad(const void *a, const void *b, void *c, size_t bytes, int grid,
+                         int unroll, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,8 @@ The functions carry the C names:
   weight gradients alone (column walk, no workspace)
 * ``norm_bwd_workspace_bytes``, ``norm_bwd_make_plan``, ``norm_bwd_execute``,
   ``norm_bwd_execute_partials``, ``norm_bwd_reduce_partials``,
-  ``norm_bwd_probe_copy``, ``norm_bwd_status_string``, ``norm_bwd_last_error``.
+  ``norm_bwd_probe_copy``, ``norm_bwd_probe_triad``, ``norm_bwd_status_string``,
+  ``norm_bwd_last_error``.
 
 Every tensor handed to the library is checked first: on x's GPU, contiguous
 unless a row stride is taken, and of the dtype and element count the kernels
@@ -131,6 +132,7 @@ def load_library():
             "norm_bwd_status_string": [i32],
             "norm_bwd_last_error": [],
             "norm_bwd_probe_copy": [vp, vp, sz, vp],
+            "norm_bwd_probe_triad": [vp, vp, vp, sz, i32, i32, vp],
             "norm_fwd_layernorm": [vp, vp, vp, i64, i64, i32, fp, vp, vp, vp, vp],
             "norm_fwd_rmsnorm": [vp, vp, i64, i64, i32, fp, vp, vp, vp],
             "norm_bwd_ex": [ctypes.POINTER(NormBwdArgs)],
@@ -566,10 +568,26 @@ def norm_bwd_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
         _check(lib.norm_bwd_probe_copy(_ptr(src), _ptr(dst), n, s))
 
 
+def norm_bwd_probe_triad(a: torch.Tensor, b: torch.Tensor, c: torch.Tensor, grid: int = 0,
+                         unroll: int = 4, stream=None):
+    """Streaming ceiling probe: c = a + b (32-bit words), 16-byte non-temporal
+    accesses; moves 3 * a's bytes."""
+    lib = load_library()
+    _gpu(a, "a")
+    _tensor(b, "b", a.device)
+    _tensor(c, "c", a.device)
+    n = a.numel() * a.element_size()
+    if b.numel() * b.element_size() < n or c.numel() * c.element_size() < n:
+        raise ValueError("b and c must hold at least a's bytes")
+    s = _stream(stream, a.device)
+    with torch.cuda.device(a.device):
+        _check(lib.norm_bwd_probe_triad(_ptr(a), _ptr(b), _ptr(c), n, grid, unroll, s))
+
+
 __all__ = [
     "norm_bwd_layernorm", "norm_bwd_rmsnorm", "norm_bwd_workspace_bytes", "norm_bwd_make_plan",
     "norm_bwd_execute", "norm_bwd_execute_partials", "norm_bwd_reduce_partials",
-    "norm_bwd_probe_copy", "norm_bwd_status_string", "norm_bwd_last_error", "NormBwdPlan",
+    "norm_bwd_probe_copy", "norm_bwd_probe_triad", "norm_bwd_status_string", "norm_bwd_last_error", "NormBwdPlan",
     "norm_fwd_layernorm", "norm_fwd_rmsnorm", "norm_bwd_ex", "NormBwdArgs", "ACCUMULATE",
     "norm_bwd_wgrad",
     "NormBwdError", "load_library", "library_path",

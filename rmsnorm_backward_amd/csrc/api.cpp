@@ -616,4 +616,27 @@ int norm_bwd_probe_copy(const void* src, void* dst, size_t bytes, void* stream) 
   return NORM_BWD_OK;
 }
 
+int norm_bwd_probe_triad(const void* a, const void* b, void* c, size_t bytes, int grid,
+                         int unroll, void* stream) {
+  if (bytes == 0) return NORM_BWD_OK;
+  if (!a || !b || !c || bytes % 16 != 0 || !aligned16(a) || !aligned16(b) || !aligned16(c))
+    return set_error(NORM_BWD_ERR_INVALID_ARG,
+                     "triad probe needs non-NULL, 16-byte aligned buffers of a 16-byte multiple");
+  if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8)
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "triad probe unroll must be 1, 2, 4 or 8");
+  if (grid < 0 || grid > (1 << 20))
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "triad probe grid must be in [0, 2^20]");
+  if (nb::ranges_overlap(c, bytes, a, bytes) || nb::ranges_overlap(c, bytes, b, bytes))
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "triad probe output overlaps an input");
+  if (grid == 0) {  // one pass: every thread handles `unroll` vectors once
+    const uint64_t per_block = 256ull * (uint64_t)unroll;
+    const uint64_t g = (bytes / 16 + per_block - 1) / per_block;
+    grid = (int)(g > (1u << 20) ? (1u << 20) : g);
+  }
+  (void)hipGetLastError();  // clear a stale error so a launch failure is ours
+  hipError_t e = nb::launch_triad(a, b, c, bytes, grid, unroll, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_error(e, "triad probe launch");
+  return NORM_BWD_OK;
+}
+
 }  // extern "C"

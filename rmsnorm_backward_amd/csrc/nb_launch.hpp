@@ -108,5 +108,7 @@ hipError_t launch_f_bf16(const LaunchF& f);
 hipError_t launch_reduce(int wgrad_dtype, const float* ws, int64_t G, int N, void* dgamma,
                          void* dbeta, int accumulate, int ws_stream, hipStream_t stream);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+hipError_t launch_triad(const void* a, const void* b, void* c, size_t bytes, int grid,
+                        int unroll, hipStream_t stream);
 
 }  // namespace nb

@@ -35,6 +35,7 @@ KERNEL_B = "reduce_partials_kernel"
 FORWARD = "norm_fwd_kernel"
 COLWALK = "wgrad_colwalk_kernel"
 COPY = "copy_probe_kernel"
+TRIAD = "triad_probe_kernel"
 _HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCE = os.path.join(_HERE, "csrc", "nb_device.hpp")
 FORWARD_SOURCES = (KERNEL_SOURCE, os.path.join(_HERE, "csrc", "nb_forward.hpp"))
@@ -83,7 +84,7 @@ def stats_summary(stats_csv: str, bench_json: str, cmds) -> str:
     out += list(cmds) + ["```", "",
                          "| kernel | calls | average (us) | min (us) | max (us) | share |",
                          "|---|---|---|---|---|---|"]
-    avg_a = avg_f = None
+    avg_a = avg_f = avg_b = avg_t = None
     calls_a = -1
     for r in rows:
         name = r["Name"]
@@ -93,12 +94,26 @@ def stats_summary(stats_csv: str, bench_json: str, cmds) -> str:
             avg_a, calls_a = avg, int(r["Calls"])
         if FORWARD in name:
             avg_f = avg
+        if KERNEL_B in name:
+            avg_b = avg
+        if TRIAD in name and (avg_t is None or avg < avg_t):
+            avg_t = avg
         out.append(f"| `{short}` | {r['Calls']} | {avg:.2f} | {float(r['MinNs'])/1e3:.2f} | "
                    f"{float(r['MaxNs'])/1e3:.2f} | {float(r['Percentage']):.1f}% |")
     out += ["", "Benchmark line of the same run (HIP events on the launch stream):", "",
             f"- step: {b['ms_per_step']*1e3:.2f} us, {b['value']} GB/s ({c['pct_of_peak']}% of 8 TB/s)",
-            f"- kernel A by events: {c['kernel_a_us']} us; kernel B by events: {c['kernel_b_us']} us",
+            f"- kernel A by events: {c['kernel_a_us']} us",
             f"- plan: {json.dumps(c['plan'])}"]
+    if "kernel_b_in_place_us" in c:
+        out.append(f"- kernel B in place (step minus kernel A, events): "
+                   f"{c['kernel_b_in_place_us']} us")
+    if avg_b is not None:
+        out.append(f"- kernel B by the trace (average over every launch of the run): "
+                   f"{avg_b:.2f} us")
+    tri = c.get("triad_probe")
+    if tri:
+        out.append(f"- triad ceiling by events: {tri['GBps']} GB/s (grid {tri['grid']}, unroll "
+                   f"{tri['unroll']}); step at {c.get('pct_of_triad')}% of it")
     if avg_a is not None:
         out.append(f"- kernel A by the trace: {avg_a:.2f} us "
                    f"(events / trace = {c['kernel_a_us'] / avg_a:.3f})")

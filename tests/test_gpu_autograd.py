@@ -63,9 +63,11 @@ def test_module_forward_backward(ag, kind, dt, shape):
     rdg, rdb = oracle.bwd_wgrad(kind, x2, dy2, rm, rr)
     t_dx, t_dg = parity.recompute_terms(kind, x2, dy2, inp["gamma"], rm, rr)
     parity.check_dx(dt, x.grad.view(M, N).cpu(), rdx, scale=t_dx, coef32=2.0 ** -16)
-    parity.check_wgrad(dt, mod.weight.grad.cpu(), rdg, extra=2.0 ** -16 * t_dg)
+    bg, bb = parity.wgrad_bounds(kind, x2, dy2, rm, rr,
+                                 parity.depth_path(M, N, dt, kind == "layernorm"))
+    parity.check_wgrad(dt, mod.weight.grad.cpu(), rdg, extra=2.0 ** -16 * t_dg, **bg)
     if kind == "layernorm":
-        parity.check_wgrad(dt, mod.bias.grad.cpu(), rdb, "dbeta")
+        parity.check_wgrad(dt, mod.bias.grad.cpu(), rdb, "dbeta", **bb)
     assert x.grad.shape == x.shape and x.grad.dtype == dt
 
 

@@ -47,6 +47,12 @@ def reference(w, inp, with_db):
     return rdx, rdg, (rdb if with_db else None), scale
 
 
+def wbounds(w, inp, extra_depth=0):
+    """check_wgrad keywords (dgamma, dbeta) for an automatic fused plan of M rows."""
+    return parity.wgrad_bounds(w.kind, inp["x"], inp["dy"], inp.get("mean"), inp["rstd"],
+                               parity.depth_fused(w.M) + extra_depth)
+
+
 @pytest.mark.parametrize("dt,pad", [(torch.bfloat16, 8), (torch.bfloat16, 3), (torch.float32, 4),
                                     (torch.float16, 64), (torch.float32, 1)],
                          ids=lambda v: str(v).replace("torch.", ""))
@@ -69,10 +75,11 @@ def test_row_strides(nb, kind, dt, pad):
     torch.cuda.synchronize()
     assert dx.data_ptr() == dxv.data_ptr()
     rdx, rdg, rdb, scale = reference(w, inp, with_db)
+    bg, bb = wbounds(w, inp)
     parity.check_dx(dt, dx.cpu(), rdx, scale=scale)
-    parity.check_wgrad(dt, dg.cpu(), rdg)
+    parity.check_wgrad(dt, dg.cpu(), rdg, **bg)
     if with_db:
-        parity.check_wgrad(dt, db.cpu(), rdb, "dbeta")
+        parity.check_wgrad(dt, db.cpu(), rdb, "dbeta", **bb)
     # the padding between dx's rows is untouched
     full = dxv.as_strided((w.M, N + 3 * pad), (N + 3 * pad, 1))
     assert torch.all(full[:, N:].float().cpu() == CANARY)
@@ -130,8 +137,10 @@ def test_accumulate_two_micro_batches(nb, wdt):
         p_g, p_b = oracle.bwd_wgrad(w.kind, inp["x"][:250], inp["dy"][:250], inp["mean"][:250],
                                     inp["rstd"][:250], want_dbeta=True)
         extra, extra_b = 2.0 ** -7 * abs(p_g), 2.0 ** -7 * abs(p_b)
-    parity.check_wgrad(w.io_dtype, dg.cpu(), rdg, extra=extra)
-    parity.check_wgrad(w.io_dtype, db.cpu(), rdb, "dbeta", extra=extra_b)
+    # each micro-batch's sum, then one fp32 addition into the buffer
+    bg, bb = wbounds(w, inp, extra_depth=1)
+    parity.check_wgrad(w.io_dtype, dg.cpu(), rdg, extra=extra, **bg)
+    parity.check_wgrad(w.io_dtype, db.cpu(), rdb, "dbeta", extra=extra_b, **bb)
 
 
 def test_accumulate_empty_batch_leaves_gradients(nb):

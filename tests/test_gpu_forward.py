@@ -252,7 +252,9 @@ def test_forward_then_backward(nb, w):
     rdx, rdg, rdb = oracle.bwd(w.kind, inp["x"], inp["dy"], inp["gamma"], mean_c, rstd_c)
     scale = parity.dx_term_scale(w.kind, inp["x"], inp["dy"], inp["gamma"], mean_c, rstd_c)
     parity.check_dx(w.io_dtype, dx.cpu(), rdx, scale=scale)
-    parity.check_wgrad(w.io_dtype, dg.cpu(), rdg)
+    bg, bb = parity.wgrad_bounds(w.kind, inp["x"], inp["dy"], mean_c, rstd_c,
+                                 parity.depth_path(w.M, w.N, w.io_dtype, db is not None))
+    parity.check_wgrad(w.io_dtype, dg.cpu(), rdg, **bg)
     if db is not None:
-        parity.check_wgrad(w.io_dtype, db.cpu(), rdb, "dbeta")
+        parity.check_wgrad(w.io_dtype, db.cpu(), rdb, "dbeta", **bb)
     assert np.isfinite(rdx).all()

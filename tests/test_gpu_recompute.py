@@ -56,10 +56,12 @@ def compare(w, x, dy, gamma, out, with_db, eps=None, rows=None, cols=None):
     rdg, rdb = oracle.bwd_wgrad(w.kind, xc, dyc, mean, rstd, want_dbeta=True)
     _, t_dg = parity.recompute_terms(w.kind, xc, dyc, gamma if cols is None else gamma[cols],
                                      mean, rstd)
+    bg, bb = parity.wgrad_bounds(w.kind, xc, dyc, mean, rstd,
+                                 parity.depth_path(x.shape[0], x.shape[1], w.io_dtype, with_db))
     parity.check_wgrad(w.io_dtype, dg if cols is None else dg[cols], rdg,
-                       extra=2.0 ** -16 * t_dg)
+                       extra=2.0 ** -16 * t_dg, **bg)
     if with_db:
-        parity.check_wgrad(w.io_dtype, db if cols is None else db[cols], rdb, "dbeta")
+        parity.check_wgrad(w.io_dtype, db if cols is None else db[cols], rdb, "dbeta", **bb)
 
 
 SMALL = [

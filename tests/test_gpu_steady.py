@@ -42,15 +42,17 @@ def workload(kind, dt, M, N):
                     name=f"{kind}_{W._dt(dt)}_{M}x{N}")
 
 
-def compare(w, inp, out, mean, rstd, with_db):
+def compare(w, inp, out, mean, rstd, with_db, groups):
     dx, dg, db = (None if t is None else t.cpu() for t in out)
     rdx, rdg, rdb = oracle.bwd(w.kind, inp["x"], inp["dy"], inp["gamma"], mean, rstd,
                                want_dbeta=True)
     scale = parity.dx_term_scale(w.kind, inp["x"], inp["dy"], inp["gamma"], mean, rstd)
     parity.check_dx(w.io_dtype, dx, rdx, scale=scale)
-    parity.check_wgrad(w.io_dtype, dg, rdg)
+    bg, bb = parity.wgrad_bounds(w.kind, inp["x"], inp["dy"], mean, rstd,
+                                 parity.depth_fused(w.M, groups))
+    parity.check_wgrad(w.io_dtype, dg, rdg, **bg)
     if with_db:
-        parity.check_wgrad(w.io_dtype, db, rdb, "dbeta")
+        parity.check_wgrad(w.io_dtype, db, rdb, "dbeta", **bb)
 
 
 # (kind, dtype, N, groups, row counts): N is covered exactly by the lanes;
@@ -91,7 +93,7 @@ def test_steady_loop_saved_statistics(nb, kind, dt, N, G, M):
     out = nb.norm_bwd_execute(plan, g["x"], g["dy"], g["gamma"], g.get("mean"), g["rstd"],
                               wgrad_dtype=w.wgrad_dtype)
     torch.cuda.synchronize()
-    compare(w, inp, out, inp.get("mean"), inp["rstd"], with_db)
+    compare(w, inp, out, inp.get("mean"), inp["rstd"], with_db, G)
 
 
 # Recompute mode runs the steady-state loop where a lane holds one 16-byte
@@ -104,7 +106,9 @@ RECOMPUTE = [
     ("layernorm", torch.bfloat16, 512, 2, (78, 80, 95, 250)),         # P = 8, pipelined
     ("layernorm", torch.float32, 256, 1, (39, 40, 41, 77)),           # P = 8, pipelined
     ("layernorm", torch.float16, 2048, 2, (38, 40, 47, 126)),         # P = 4, two exchanges
-    ("rmsnorm", torch.bfloat16, 4096, 3, (12, 15, 19, 77)),           # P = 1, 512-thread bound
+    # P = 1, 512-thread bound; M = 16 gives groups of 6, 5 and 5 rows, the
+    # narrow kernel at its threshold (5 * P rows) with every group
+    ("rmsnorm", torch.bfloat16, 4096, 3, (12, 15, 16, 19, 77)),
 ]
 
 
@@ -134,9 +138,10 @@ def test_steady_loop_recompute(nb, kind, dt, N, G, M):
     t_dx, t_dg = parity.recompute_terms(kind, x, dy, gamma, mean, rstd)
     parity.check_dx(w.io_dtype, dx, rdx, scale=t_dx, coef32=2.0 ** -16)
     rdg, rdb = oracle.bwd_wgrad(kind, x, dy, mean, rstd, want_dbeta=True)
-    parity.check_wgrad(w.io_dtype, dg, rdg, extra=2.0 ** -16 * t_dg)
+    bg, bb = parity.wgrad_bounds(kind, x, dy, mean, rstd, parity.depth_fused(M, G))
+    parity.check_wgrad(w.io_dtype, dg, rdg, extra=2.0 ** -16 * t_dg, **bg)
     if with_db:
-        parity.check_wgrad(w.io_dtype, db, rdb, "dbeta")
+        parity.check_wgrad(w.io_dtype, db, rdb, "dbeta", **bb)
 
 
 # The forward: a sweep of rows_per_sweep = grid * P rows (4096 / S for

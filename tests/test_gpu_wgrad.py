@@ -38,9 +38,11 @@ def run(nb, w, inp, with_db, wgrad=None, **kw):
 def check(w, inp, dg, db, cols=None):
     x, dy = (inp["x"], inp["dy"]) if cols is None else (inp["x"][:, cols], inp["dy"][:, cols])
     rdg, rdb = oracle.bwd_wgrad(w.kind, x, dy, inp.get("mean"), inp["rstd"], want_dbeta=True)
-    parity.check_wgrad(w.io_dtype, dg if cols is None else dg[cols], rdg)
+    bg, bb = parity.wgrad_bounds(w.kind, x, dy, inp.get("mean"), inp["rstd"],
+                                 parity.depth_colwalk(x.shape[0]))
+    parity.check_wgrad(w.io_dtype, dg if cols is None else dg[cols], rdg, **bg)
     if db is not None:
-        parity.check_wgrad(w.io_dtype, db if cols is None else db[cols], rdb, "dbeta")
+        parity.check_wgrad(w.io_dtype, db if cols is None else db[cols], rdb, "dbeta", **bb)
 
 
 SMALL = [
@@ -100,7 +102,9 @@ def test_wgrad_full_size_sampled(nb, w):
         cols = torch.unique(torch.cat([cols, inp["outliers"]]))
     check(w, inp, dg, db, cols=cols)
     if db is not None:  # dbeta over every column is the column sum of dy
-        parity.check_wgrad(w.io_dtype, db, inp["dy"].double().sum(0), "dbeta(all)")
+        _, ab = parity.abs_terms(w.kind, inp["x"], inp["dy"], inp.get("mean"), inp["rstd"])
+        parity.check_wgrad(w.io_dtype, db, inp["dy"].double().sum(0), "dbeta(all)", absum=ab,
+                           depth=parity.depth_colwalk(w.M))
 
 
 def test_wgrad_agrees_with_fused_path_and_is_deterministic(nb):
@@ -113,8 +117,11 @@ def test_wgrad_agrees_with_fused_path_and_is_deterministic(nb):
     _, fg, fb = nb.norm_bwd_layernorm(g["x"], g["dy"], g["gamma"], g["mean"], g["rstd"], w.eps)
     torch.cuda.synchronize()
     rdg, rdb = oracle.bwd_wgrad(w.kind, inp["x"], inp["dy"], inp["mean"], inp["rstd"])
-    parity.check_wgrad(w.io_dtype, fg.cpu(), rdg)
-    parity.check_wgrad(w.io_dtype, a[0], rdg)
+    bg, _ = parity.wgrad_bounds(w.kind, inp["x"], inp["dy"], inp["mean"], inp["rstd"], 0)
+    parity.check_wgrad(w.io_dtype, fg.cpu(), rdg, absum=bg["absum"],
+                       depth=parity.depth_fused(w.M))
+    parity.check_wgrad(w.io_dtype, a[0], rdg, absum=bg["absum"],
+                       depth=parity.depth_colwalk(w.M))
     # the two orders differ, so the bits may too, by rounding only
     assert torch.allclose(a[0], fg.cpu(), rtol=1e-4, atol=1e-4 * float(fg.abs().max()))
 

@@ -51,9 +51,11 @@ def check_saved(w, inp, out, with_db):
     scale = parity.dx_term_scale(w.kind, inp["x"], inp["dy"], inp["gamma"], inp.get("mean"),
                                  inp["rstd"])
     parity.check_dx(w.io_dtype, dx, rdx, scale=scale)
-    parity.check_wgrad(w.io_dtype, dg, rdg)
+    bg, bb = parity.wgrad_bounds(w.kind, inp["x"], inp["dy"], inp.get("mean"), inp["rstd"],
+                                 parity.depth_colwalk(w.M))
+    parity.check_wgrad(w.io_dtype, dg, rdg, **bg)
     if with_db:
-        parity.check_wgrad(w.io_dtype, db, rdb, "dbeta")
+        parity.check_wgrad(w.io_dtype, db, rdb, "dbeta", **bb)
 
 
 def check_recompute(w, inp, out, with_db):
@@ -63,9 +65,11 @@ def check_recompute(w, inp, out, with_db):
     t_dx, t_dg = parity.recompute_terms(w.kind, inp["x"], inp["dy"], inp["gamma"], mean, rstd)
     parity.check_dx(w.io_dtype, dx, rdx, scale=t_dx, coef32=2.0 ** -16)
     rdg, rdb = oracle.bwd_wgrad(w.kind, inp["x"], inp["dy"], mean, rstd)
-    parity.check_wgrad(w.io_dtype, dg, rdg, extra=2.0 ** -16 * t_dg)
+    bg, bb = parity.wgrad_bounds(w.kind, inp["x"], inp["dy"], mean, rstd,
+                                 parity.depth_colwalk(w.M))
+    parity.check_wgrad(w.io_dtype, dg, rdg, extra=2.0 ** -16 * t_dg, **bg)
     if with_db:
-        parity.check_wgrad(w.io_dtype, db, rdb, "dbeta")
+        parity.check_wgrad(w.io_dtype, db, rdb, "dbeta", **bb)
 
 
 WIDE = [(kind, dt, M, N)
@@ -123,9 +127,12 @@ def test_wide_rows_strided_and_accumulated(nb):
     scale = parity.dx_term_scale(w.kind, inp["x"], inp["dy"], inp["gamma"], inp["mean"],
                                  inp["rstd"])
     parity.check_dx(w.io_dtype, dx.cpu(), rdx, scale=scale)
-    parity.check_wgrad(w.io_dtype, (dg - old).cpu(), rdg, extra=2.0 ** -24 * abs(old.cpu()))
+    bg, bb = parity.wgrad_bounds(w.kind, inp["x"], inp["dy"], inp["mean"], inp["rstd"],
+                                 parity.depth_colwalk(w.M))
+    parity.check_wgrad(w.io_dtype, (dg - old).cpu(), rdg, extra=2.0 ** -24 * abs(old.cpu()),
+                       **bg)
     parity.check_wgrad(w.io_dtype, (db - old).cpu(), rdb, "dbeta",
-                       extra=2.0 ** -24 * abs(old.cpu()))
+                       extra=2.0 ** -24 * abs(old.cpu()), **bb)
     # explicit groups are a fused-path notion
     with pytest.raises(nb.NormBwdError) as e:
         nb.norm_bwd_ex("layernorm", x, dy, inp["gamma"].cuda(), inp["mean"].cuda(),

@@ -39,7 +39,7 @@ def test_header_declares_the_documented_entry_points():
                  "norm_bwd_make_plan", "norm_bwd_execute", "norm_bwd_execute_partials",
                  "norm_bwd_reduce_partials", "norm_bwd_status_string", "norm_bwd_last_error",
                  "norm_bwd_probe_copy", "norm_fwd_layernorm", "norm_fwd_rmsnorm", "norm_bwd_ex",
-                 "norm_bwd_wgrad"):
+                 "norm_bwd_wgrad", "norm_bwd_probe_triad"):
         assert want in names
 
 
@@ -356,6 +356,16 @@ def test_reduce_and_probe_reject(nb):
                                         None) == 1
     assert lib.norm_bwd_probe_copy(_addr(0), _addr(1), 17, None) == 1
     assert lib.norm_bwd_probe_copy(_addr(0), ctypes.c_void_p(B + 8), 1024, None) == 1
+    # the triad probe: sizes, alignment, unroll, grid and overlap, nothing launched
+    T = lib.norm_bwd_probe_triad
+    assert T(_addr(0), _addr(1), _addr(2), 0, 0, 4, None) == 0          # nothing to do
+    assert T(_addr(0), _addr(1), _addr(2), 24, 0, 4, None) == 1         # not a 16-byte multiple
+    assert T(ctypes.c_void_p(B + 8), _addr(1), _addr(2), 1024, 0, 4, None) == 1
+    assert T(None, _addr(1), _addr(2), 1024, 0, 4, None) == 1
+    assert T(_addr(0), _addr(1), _addr(2), 1024, 0, 3, None) == 1       # unroll
+    assert T(_addr(0), _addr(1), _addr(2), 1024, -1, 4, None) == 1      # grid
+    assert T(_addr(0), _addr(1), _addr(2), 1024, (1 << 20) + 1, 4, None) == 1
+    assert T(_addr(0), _addr(1), ctypes.c_void_p(B + 512), 1024, 0, 4, None) == 1  # c overlaps a
 
 
 def _fwd(nb, kind, **over):
