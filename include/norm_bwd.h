@@ -216,6 +216,34 @@ typedef struct norm_bwd_args {
 int norm_bwd_ex(const norm_bwd_args_t *args);
 
 /*
+ * norm_bwd_ex for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, results and checks, with the workspace taken from a
+ * static array of NORM_BWD_STATIC_SCRATCH_BYTES in the library's device code
+ * instead of args->workspace. Nothing is allocated by this call, by the
+ * library or by any routine it calls.
+ *
+ *   args      as for norm_bwd_ex, except that args->workspace must be NULL
+ *             and args->workspace_bytes 0 (else NORM_BWD_ERR_INVALID_ARG).
+ *   The problem's workspace (norm_bwd_workspace_bytes for automatic groups,
+ *   norm_bwd_make_plan(...).workspace_bytes for explicit groups, as for
+ *   norm_bwd_ex) must fit in NORM_BWD_STATIC_SCRATCH_BYTES, else
+ *   NORM_BWD_ERR_WORKSPACE, with nothing launched.
+ *   The stream must belong to the calling thread's current device
+ *   (NORM_BWD_ERR_INVALID_ARG otherwise); NULL is that device's default
+ *   stream.
+ * Each device holds one copy of the array, from the first call on it until
+ * the process ends. Calls on one device share it: two calls whose work
+ * overlaps in time on one device (on different streams, or from different
+ * threads without ordering) race on it and their results are undefined.
+ * Calls ordered on one stream are safe; each call writes every byte of the
+ * workspace it reads, so no state carries over between calls.
+ */
+#define NORM_BWD_STATIC_SCRATCH_BYTES (32u << 20)   /* 32 MiB per device */
+
+int norm_bwd_ex_static(const norm_bwd_args_t *args);
+
+/*
  * Weight gradients alone, by a column walk: dgamma[j] = sum over rows of
  * dy * xhat (and dbeta[j] = sum of dy) without dx and without a workspace.
  * Each workgroup owns a tile of adjacent columns and walks all M rows, as the

@@ -17,6 +17,8 @@ The functions carry the C names:
   produces the statistics the backward consumes
 * ``norm_bwd_ex(kind, x, dy, gamma, mean, rstd, eps, ...)``: row-strided 2-D
   views, an explicit group count, accumulation into given dgamma/dbeta
+* ``norm_bwd_ex_static(...)``: the same with the workspace in the library's
+  static scratch (no workspace argument), for callers that cannot allocate
 * ``norm_bwd_wgrad(kind, x, dy, mean, rstd)`` -> (dgamma, dbeta or None): the
   weight gradients alone (column walk, no workspace)
 * ``norm_bwd_workspace_bytes``, ``norm_bwd_make_plan``, ``norm_bwd_execute``,
@@ -81,6 +83,8 @@ class NormBwdPlan(ctypes.Structure):
 
 
 ACCUMULATE = 1
+# bytes of the static scratch of norm_bwd_ex_static (NORM_BWD_STATIC_SCRATCH_BYTES)
+STATIC_SCRATCH_BYTES = 32 << 20
 
 
 class NormBwdArgs(ctypes.Structure):
@@ -136,6 +140,7 @@ def load_library():
             "norm_fwd_layernorm": [vp, vp, vp, i64, i64, i32, fp, vp, vp, vp, vp],
             "norm_fwd_rmsnorm": [vp, vp, i64, i64, i32, fp, vp, vp, vp],
             "norm_bwd_ex": [ctypes.POINTER(NormBwdArgs)],
+            "norm_bwd_ex_static": [ctypes.POINTER(NormBwdArgs)],
             "norm_bwd_wgrad": [i32, vp, vp, vp, vp, i64, i64, i32, i32, vp, vp, ctypes.c_uint, vp],
         }
         for name, args in sigs.items():
@@ -361,6 +366,25 @@ def norm_bwd_ex(kind: str, x: torch.Tensor, dy: torch.Tensor, gamma: torch.Tenso
     """Extended backward (norm_bwd_ex): x, dy (and dx) may be row-strided 2-D
     views; accumulate=True adds into the given dgamma/dbeta. Returns
     (dx, dgamma, dbeta)."""
+    return _ex(False, kind, x, dy, gamma, mean, rstd, eps, wgrad_dtype, dx, dgamma, dbeta,
+               with_dbeta, accumulate, groups, workspace, stream)
+
+
+def norm_bwd_ex_static(kind: str, x: torch.Tensor, dy: torch.Tensor, gamma: torch.Tensor,
+                       mean: Optional[torch.Tensor] = None, rstd: Optional[torch.Tensor] = None,
+                       eps: float = 1e-5, *, wgrad_dtype: Optional[torch.dtype] = None, dx=None,
+                       dgamma=None, dbeta=None, with_dbeta: Optional[bool] = None,
+                       accumulate: bool = False, groups: int = 0, stream=None):
+    """norm_bwd_ex_static: norm_bwd_ex with the workspace in the library's
+    static scratch (no workspace argument; the library allocates nothing).
+    Outputs not given are allocated here with torch.empty; a caller that must
+    not allocate passes dx, dgamma (and dbeta). Returns (dx, dgamma, dbeta)."""
+    return _ex(True, kind, x, dy, gamma, mean, rstd, eps, wgrad_dtype, dx, dgamma, dbeta,
+               with_dbeta, accumulate, groups, None, stream)
+
+
+def _ex(static, kind, x, dy, gamma, mean, rstd, eps, wgrad_dtype, dx, dgamma, dbeta, with_dbeta,
+        accumulate, groups, workspace, stream):
     lib = load_library()
     code = kind = _KIND_CODE[kind]
     M, N, ldx = _rows2d(x, "x")
@@ -394,11 +418,12 @@ def norm_bwd_ex(kind: str, x: torch.Tensor, dy: torch.Tensor, gamma: torch.Tenso
         if t is not None:
             _tensor(t, n, dev, wgrad_dtype, N)
     io = _code(x.dtype, "x")
-    if workspace is None:
-        need = (norm_bwd_make_plan(kind, M, N, io, dbeta is not None, groups).workspace_bytes
-                if groups else _auto_workspace(kind, M, N, io, dbeta is not None))
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    _tensor(workspace, "workspace", dev)
+    if not static:
+        if workspace is None:
+            need = (norm_bwd_make_plan(kind, M, N, io, dbeta is not None, groups).workspace_bytes
+                    if groups else _auto_workspace(kind, M, N, io, dbeta is not None))
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        _tensor(workspace, "workspace", dev)
     a = NormBwdArgs()
     a.kind, a.io_dtype, a.wgrad_dtype = code, io, _code(wgrad_dtype, "wgrad")
     a.flags = ACCUMULATE if accumulate else 0
@@ -408,12 +433,13 @@ def norm_bwd_ex(kind: str, x: torch.Tensor, dy: torch.Tensor, gamma: torch.Tenso
     a.gamma, a.mean, a.rstd = _addr(gamma), _addr(mean), _addr(rstd)
     a.dx, a.lddx = _addr(dx), lddx
     a.dgamma, a.dbeta = _addr(dgamma), _addr(dbeta)
-    a.workspace = _addr(workspace)
-    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    if not static:
+        a.workspace = _addr(workspace)
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
     a.stream = _stream(stream, dev).value
     a.eps = float(eps)
     with torch.cuda.device(dev):
-        st = lib.norm_bwd_ex(ctypes.byref(a))
+        st = (lib.norm_bwd_ex_static if static else lib.norm_bwd_ex)(ctypes.byref(a))
     _check(st)
     return dx, dgamma, dbeta
 
@@ -588,7 +614,8 @@ __all__ = [
     "norm_bwd_layernorm", "norm_bwd_rmsnorm", "norm_bwd_workspace_bytes", "norm_bwd_make_plan",
     "norm_bwd_execute", "norm_bwd_execute_partials", "norm_bwd_reduce_partials",
     "norm_bwd_probe_copy", "norm_bwd_probe_triad", "norm_bwd_status_string", "norm_bwd_last_error", "NormBwdPlan",
-    "norm_fwd_layernorm", "norm_fwd_rmsnorm", "norm_bwd_ex", "NormBwdArgs", "ACCUMULATE",
+    "norm_fwd_layernorm", "norm_fwd_rmsnorm", "norm_bwd_ex", "norm_bwd_ex_static",
+    "NormBwdArgs", "ACCUMULATE", "STATIC_SCRATCH_BYTES",
     "norm_bwd_wgrad",
     "NormBwdError", "load_library", "library_path",
 ]

@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include "nb_api.hpp"
 #include "nb_launch.hpp"
 #include "norm_bwd.h"
 #include "plan.hpp"
@@ -248,10 +249,15 @@ size_t rowloop_workspace(int kind, int64_t M, bool recompute) {
 // Rows too wide for the fused kernels: dx by the row-loop kernel (which also
 // stores the statistics in recompute mode), then the weight gradients by the
 // column walk.
-int run_wide(int kind, const Buffers& b, int64_t M, int64_t N, int io_dtype, int wgrad_dtype,
-             float eps, bool recompute, bool accumulate, hipStream_t stream) {
+int run_wide(int kind, Buffers b, int64_t M, int64_t N, int io_dtype, int wgrad_dtype,
+             float eps, bool recompute, bool accumulate, hipStream_t stream,
+             nb::WorkspaceProvider provider) {
   if (N > INT32_MAX) return set_error(NORM_BWD_ERR_UNSUPPORTED, "N too large");
   const size_t need = rowloop_workspace(kind, M, recompute);
+  if (provider) {
+    const int ps = provider(need, &b.ws, &b.ws_bytes, stream);
+    if (ps != NORM_BWD_OK) return ps;
+  }
   int st = check_buffers(kind, M, N, io_dtype, wgrad_dtype, true, true, need, b, recompute);
   if (st != NORM_BWD_OK) return st;
   if (N == 0) return NORM_BWD_OK;
@@ -304,7 +310,8 @@ int run_wide(int kind, const Buffers& b, int64_t M, int64_t N, int io_dtype, int
 // The whole backward with an automatic or explicit group count: the named
 // entry points and norm_bwd_ex. Row strides of b must be filled in (>= N).
 int run_backward(int kind, Buffers b, int64_t M, int64_t N, int io_dtype, int wgrad_dtype,
-                 float eps, int64_t groups, bool accumulate, void* stream) {
+                 float eps, int64_t groups, bool accumulate, void* stream,
+                 nb::WorkspaceProvider provider = nullptr) {
   if (!(eps >= 0.0f) || isinf(eps))
     return set_error(NORM_BWD_ERR_INVALID_ARG, "eps must be finite and >= 0");
   // NULL statistics (LayerNorm: both) select the recompute mode
@@ -324,13 +331,18 @@ int run_backward(int kind, Buffers b, int64_t M, int64_t N, int io_dtype, int wg
       return set_error(NORM_BWD_ERR_UNSUPPORTED, "explicit groups need rows the fused path holds");
     if (wgrad_dtype != NORM_BWD_F32 && wgrad_dtype != io_dtype)
       return set_error(NORM_BWD_ERR_UNSUPPORTED, "wgrad_dtype must be NORM_BWD_F32 or io_dtype");
-    return run_wide(kind, b, M, N, io_dtype, wgrad_dtype, eps, recompute, accumulate, s);
+    return run_wide(kind, b, M, N, io_dtype, wgrad_dtype, eps, recompute, accumulate, s,
+                    provider);
   }
   norm_bwd_plan_t p;
   const char* why = nullptr;
   int st = nb::make_plan(kind, M, N, io_dtype, b.dbeta ? 1 : 0, groups, vec_ok, &p, &why,
                          recompute);
   if (st != NORM_BWD_OK) return set_error(st, why);
+  if (provider) {
+    st = provider(p.workspace_bytes, &b.ws, &b.ws_bytes, stream);
+    if (st != NORM_BWD_OK) return st;
+  }
   st = check_buffers(kind, M, N, io_dtype, wgrad_dtype, true, true, p.workspace_bytes, b,
                      recompute);
   if (st != NORM_BWD_OK) return st;
@@ -418,6 +430,35 @@ int run_forward(int kind, const void* x, const void* gamma, const void* beta, in
 
 }  // namespace
 
+namespace nb {
+
+int report_error(int status, const char* what) { return set_error(status, what); }
+int report_hip_error(hipError_t e, const char* where) { return hip_error(e, where); }
+
+int run_ex(const norm_bwd_args_t* a, WorkspaceProvider provider) {
+  if (!a) return set_error(NORM_BWD_ERR_INVALID_ARG, "args is NULL");
+  if (a->kind != NORM_BWD_LAYERNORM && a->kind != NORM_BWD_RMSNORM)
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "kind invalid");
+  if (a->flags & ~(uint32_t)NORM_BWD_ACCUMULATE)
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "unknown flag bits");
+  if (a->M < 0 || a->N < 0) return set_error(NORM_BWD_ERR_INVALID_ARG, "M and N must be >= 0");
+  if (a->groups < 0) return set_error(NORM_BWD_ERR_INVALID_ARG, "groups must be >= 0");
+  if (a->reserved != 0) return set_error(NORM_BWD_ERR_INVALID_ARG, "reserved must be 0");
+  Buffers b{a->x, a->dy, a->gamma, a->mean, a->rstd, a->dx, a->dgamma, a->dbeta,
+            a->workspace, a->workspace_bytes};
+  b.ldx = a->ldx;
+  b.ldy = a->lddy;
+  b.ldo = a->lddx;
+  if (a->ldx < 0 || a->lddy < 0 || a->lddx < 0)
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "row strides must be >= 0");
+  int st = check_strides(a->M, a->N, b);
+  if (st != NORM_BWD_OK) return st;
+  return run_backward(a->kind, b, a->M, a->N, a->io_dtype, a->wgrad_dtype, a->eps, a->groups,
+                      (a->flags & NORM_BWD_ACCUMULATE) != 0, a->stream, provider);
+}
+
+}  // namespace nb
+
 extern "C" {
 
 int norm_fwd_layernorm(const void* x, const void* gamma, const void* beta, int64_t M, int64_t N,
@@ -477,27 +518,7 @@ int norm_bwd_make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_db
   return NORM_BWD_OK;
 }
 
-int norm_bwd_ex(const norm_bwd_args_t* a) {
-  if (!a) return set_error(NORM_BWD_ERR_INVALID_ARG, "args is NULL");
-  if (a->kind != NORM_BWD_LAYERNORM && a->kind != NORM_BWD_RMSNORM)
-    return set_error(NORM_BWD_ERR_INVALID_ARG, "kind invalid");
-  if (a->flags & ~(uint32_t)NORM_BWD_ACCUMULATE)
-    return set_error(NORM_BWD_ERR_INVALID_ARG, "unknown flag bits");
-  if (a->M < 0 || a->N < 0) return set_error(NORM_BWD_ERR_INVALID_ARG, "M and N must be >= 0");
-  if (a->groups < 0) return set_error(NORM_BWD_ERR_INVALID_ARG, "groups must be >= 0");
-  if (a->reserved != 0) return set_error(NORM_BWD_ERR_INVALID_ARG, "reserved must be 0");
-  Buffers b{a->x, a->dy, a->gamma, a->mean, a->rstd, a->dx, a->dgamma, a->dbeta,
-            a->workspace, a->workspace_bytes};
-  b.ldx = a->ldx;
-  b.ldy = a->lddy;
-  b.ldo = a->lddx;
-  if (a->ldx < 0 || a->lddy < 0 || a->lddx < 0)
-    return set_error(NORM_BWD_ERR_INVALID_ARG, "row strides must be >= 0");
-  int st = check_strides(a->M, a->N, b);
-  if (st != NORM_BWD_OK) return st;
-  return run_backward(a->kind, b, a->M, a->N, a->io_dtype, a->wgrad_dtype, a->eps, a->groups,
-                      (a->flags & NORM_BWD_ACCUMULATE) != 0, a->stream);
-}
+int norm_bwd_ex(const norm_bwd_args_t* a) { return nb::run_ex(a, nullptr); }
 
 int norm_bwd_wgrad(int kind, const void* x, const void* dy, const float* mean, const float* rstd,
                    int64_t M, int64_t N, int io_dtype, int wgrad_dtype, void* dgamma,
