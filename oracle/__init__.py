@@ -150,10 +150,13 @@ _default: Optional[Oracle] = None
 
 
 def default() -> Oracle:
+    """The oracle the tests use: liboracle.so, built when missing or stale;
+    or, with NORM_ORACLE_LIBRARY set, that compiled copy of norm_oracle.c
+    (the sanitizer test runs the pins against an instrumented build)."""
     global _default
     with _lock:
         if _default is None:
-            _default = Oracle(build())
+            _default = Oracle(os.environ.get("NORM_ORACLE_LIBRARY") or build())
     return _default
 
 
