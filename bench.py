@@ -423,7 +423,7 @@ def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, ext
         entry["kernel_a_pct_of_triad"] = round(100 * achieved / triad["GBps"], 2)
     plan_d = {k: v for k, v in plan.as_dict().items()
               if k in ("groups", "rows_per_group", "vec", "chunks", "waves_per_row",
-                       "rows_in_flight", "threads", "grid")}
+                       "rows_in_flight", "rows_per_wave", "threads", "grid")}
     entry["plan"] = plan_d
     more = {}
     if extras:

@@ -274,9 +274,17 @@ int norm_bwd_wgrad(int kind, const void *x, const void *dy, const float *mean,
  * An execution plan: the row grouping and the launch geometry of kernel A.
  * Produced by norm_bwd_make_plan; a caller may change `groups` (then call
  * norm_bwd_make_plan again with it) or the geometry fields for tuning, and
- * norm_bwd_execute re-validates every field. Results depend on groups and
- * rows_in_flight (dgamma/dbeta order) and on vec, chunks, waves_per_row
- * (order of the in-row sums), never on the device.
+ * norm_bwd_execute re-validates every field. Results depend on groups,
+ * rows_in_flight and rows_per_wave (dgamma/dbeta order) and on vec, chunks,
+ * waves_per_row, rows_per_wave (order of the in-row sums), never on the
+ * device.
+ *
+ * Two lane layouts. rows_per_wave = 1: a row is split over waves_per_row
+ * waves of 64 lanes, each lane holding chunks vectors of vec elements.
+ * rows_per_wave = 2 (16-byte vectors only, waves_per_row = 1, chunks 1 or
+ * 3, N = 32 * vec * chunks exactly): each 32-lane half of a wave holds a row
+ * of its own; threads = 32 * rows_in_flight (at most 512), and a row pair's
+ * byte span (groups * N + N elements) must stay below 2^32.
  */
 typedef struct norm_bwd_plan {
     int32_t kind;            /* NORM_BWD_LAYERNORM / RMSNORM */
@@ -292,6 +300,7 @@ typedef struct norm_bwd_plan {
     int32_t threads;         /* 64 * S * P, kernel A's workgroup size */
     int32_t grid;            /* kernel A workgroups (groups are strided over them) */
     int32_t lds_bytes;       /* kernel A dynamic LDS */
+    int32_t rows_per_wave;   /* 1, or 2: each 32-lane half of a wave takes a row */
     size_t workspace_bytes;  /* with_dbeta ? 2 : 1, times groups * N * 4 */
 } norm_bwd_plan_t;
 
@@ -305,7 +314,10 @@ typedef struct norm_bwd_plan {
  * that many row groups, clamped to M so that no group is empty. The lane
  * layout takes at most 32 bytes of each operand per lane, then the fewest
  * waves per row; the rows in flight per workgroup are the fewest whose x and
- * dy reach 16 KiB. A plan is
+ * dy reach 16 KiB. RMSNorm rows that 64-lane waves would cover with idle
+ * lanes and 32 lanes cover exactly (N = 32 * vec * 1 or 3: 256 or 768 16-bit,
+ * 128 or 384 fp32 elements) take two rows per wave instead, with the fewest
+ * rows in flight whose x and dy reach 8 KiB. A plan is
  * for saved statistics. The plan assumes 16-byte aligned base pointers;
  * norm_bwd_execute rejects a plan whose vec the pointers do not allow.
  * Host-only. Returns a status code.

@@ -70,7 +70,7 @@ class NormBwdPlan(ctypes.Structure):
         ("chunks", ctypes.c_int32), ("waves_per_row", ctypes.c_int32),
         ("rows_in_flight", ctypes.c_int32), ("threads", ctypes.c_int32),
         ("grid", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
-        ("workspace_bytes", ctypes.c_size_t),
+        ("rows_per_wave", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
     ]
 
     def as_dict(self):

@@ -165,6 +165,7 @@ int launch_partials(const norm_bwd_plan_t& p, const Buffers& b, hipStream_t stre
   a.recompute = recompute ? 1 : 0;
   a.eps = eps;
   a.ws_stream = nb::stream_workspace(p.workspace_bytes) ? 1 : 0;
+  a.rows_per_wave = p.rows_per_wave;
   a.stream = stream;
   (void)hipGetLastError();  // clear a stale error so a launch failure is ours
   hipError_t e;
@@ -336,8 +337,10 @@ int run_backward(int kind, Buffers b, int64_t M, int64_t N, int io_dtype, int wg
   }
   norm_bwd_plan_t p;
   const char* why = nullptr;
+  int64_t max_ld = b.ldx > b.ldy ? b.ldx : b.ldy;
+  if (b.ldo > max_ld) max_ld = b.ldo;
   int st = nb::make_plan(kind, M, N, io_dtype, b.dbeta ? 1 : 0, groups, vec_ok, &p, &why,
-                         recompute);
+                         recompute, max_ld);
   if (st != NORM_BWD_OK) return set_error(st, why);
   if (provider) {
     st = provider(p.workspace_bytes, &b.ws, &b.ws_bytes, stream);

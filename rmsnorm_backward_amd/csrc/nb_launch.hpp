@@ -27,6 +27,7 @@ struct LaunchA {
   int recompute;  // 1: mean/rstd are NULL and recomputed from x with eps
   float eps;
   int ws_stream;  // 1: non-temporal stores of the partials (16-byte vector rows)
+  int rows_per_wave;  // 2: the two-rows-per-wave kernel (nb_tworow.hpp), P = rows in flight
   hipStream_t stream;
 };
 
@@ -99,6 +100,9 @@ hipError_t launch_w_bf16(const LaunchW& w);
 hipError_t launch_a_f32(const LaunchA& a);
 hipError_t launch_a_f16(const LaunchA& a);
 hipError_t launch_a_bf16(const LaunchA& a);
+hipError_t launch_a_tworow_f32(const LaunchA& a);
+hipError_t launch_a_tworow_f16(const LaunchA& a);
+hipError_t launch_a_tworow_bf16(const LaunchA& a);
 hipError_t launch_a_recompute_f32(const LaunchA& a);
 hipError_t launch_a_recompute_f16(const LaunchA& a);
 hipError_t launch_a_recompute_bf16(const LaunchA& a);

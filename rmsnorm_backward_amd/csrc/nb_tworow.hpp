@@ -1,0 +1,304 @@
+// nb_tworow.hpp -- kernel A for rows that 32 lanes cover exactly with
+// 16-byte vectors (N = 32 * VEC * C, C = 1 or 3; for 16-bit elements 256 or
+// 768 features), with saved statistics. Such rows leave half the lanes of a
+// 64-lane layout idle in their last chunk and keep it out of the branch-free
+// steady-state loop; here every wave takes two rows at once, one per 32-lane
+// half, so every lane holds data and every load and store instruction moves
+// two 512-byte runs.
+//
+// What is computed is kernel A's (nb_device.hpp), from the same formulas of
+// "Norm backward in Triton -- the dγ/dβ reduction", "The gradients": dx per
+// row, and per row group g (the rows r with r mod G == g) the group's partial
+// dgamma (and dbeta) in fp32 registers, stored once into the workspace.
+//
+// Layout. Lane l of wave w is in half h = l / 32 and covers the columns
+// (l mod 32) * VEC + c * 32 * VEC, c < C, of its row. With P waves per
+// workgroup, iteration k of group g gives half h of wave w the group's row
+// j = 2 * (k * P + w) + h, i.e. row r = g + j * G. A half's row sums are
+// complete after a 32-lane butterfly (no exchange between waves, no
+// barrier). Each half accumulates its rows in ascending order; at the end of
+// the group the two halves are added (half 0 + half 1), then the P waves in
+// wave order through LDS. The summation order depends on (M, G, P) only.
+#pragma once
+
+#include "nb_device.hpp"
+
+namespace nb {
+
+// Sum over each 32-lane half of the wave: the 16-lane DPP butterfly of
+// wave_sum, then half 0 takes (lanes 0-15) + (lanes 16-31) and half 1
+// (lanes 32-47) + (lanes 48-63), each in that order.
+__device__ __forceinline__ float half_sum(float v, bool hi) {
+  v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141>(v);  // row_half_mirror
+  v += dpp_f32<0x140>(v);  // row_mirror
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  const float lo = r0 + r1, hi_sum = r2 + r3;
+  return hi ? hi_sum : lo;
+}
+
+constexpr int kTwoRowDepth = 3;         // ring of row pairs (two in flight)
+constexpr int kTwoRowMaxThreads = 512;  // launch bound: 256 VGPRs per lane
+
+// Loads of one row pair. RALL (steady state): both rows exist; the wave
+// addresses them through one buffer resource based at its first row, the
+// second half adding `hoff` bytes (G rows further). Otherwise each lane
+// loads through its own address, and only when its row exists.
+template <int KIND, bool RALL, class Tg, int VEC, int C>
+__device__ __forceinline__ void fetch_pair(RowBuf<Tg, VEC, C>& b, const char* __restrict__ x,
+                                           const char* __restrict__ dy,
+                                           const float* __restrict__ mean,
+                                           const float* __restrict__ rstd, int64_t r0, int64_t r,
+                                           bool active, int64_t ldx, int64_t ldy, uint32_t hoff_x,
+                                           uint32_t hoff_y, uint32_t span_x, uint32_t span_y,
+                                           int col0, int cstride) {
+  constexpr int EB = Tg::kBytes;
+  if (RALL || active) {
+    const int64_t rz = r + opaque_lane_zero();
+    b.rs = rstd[rz];
+    b.mu = (KIND == kLayerNorm) ? mean[rz] : 0.0f;
+    if constexpr (RALL) {
+      const __amdgpu_buffer_rsrc_t rx = row_rsrc(x + r0 * ldx * EB, span_x);
+      const __amdgpu_buffer_rsrc_t ry = row_rsrc(dy + r0 * ldy * EB, span_y);
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const uint32_t off = (uint32_t)(col0 + c * cstride) * EB;
+        b.x[c].load_stream_buf(rx, hoff_x + off);
+        b.dy[c].load_stream_buf(ry, hoff_y + off);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int64_t col = col0 + c * cstride;
+        b.x[c].load_stream(x + (r * ldx + col) * EB);
+        b.dy[c].load_stream(dy + (r * ldy + col) * EB);
+      }
+    }
+  }
+}
+
+// One row pair once its operands are in registers: the weight-gradient terms
+// into the accumulators, the half's row sums, then dx (RALL: through the
+// pair's buffer resource, as fetch_pair).
+template <int KIND, bool RALL, class Tg, int VEC, int C, int NACC>
+__device__ __forceinline__ void process_pair(RowBuf<Tg, VEC, C>& b, const float (&gam)[C][VEC],
+                                             float (&acc)[NACC][C][VEC], char* __restrict__ dx,
+                                             int64_t r0, int64_t r, bool active, bool hi,
+                                             int64_t ldo, uint32_t hoff_o, uint32_t span_o,
+                                             float inv_n, int col0, int cstride) {
+  constexpr int EB = Tg::kBytes;
+  const float mu = b.mu, rs = b.rs;
+  float s1 = 0.0f, s2 = 0.0f;
+  if (RALL || active) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        const float xc = b.x[c].get(v) - mu;
+        const float dyv = b.dy[c].get(v);
+        const float dyh = dyv * gam[c][v];
+        if (KIND == kLayerNorm) s1 = __builtin_fmaf(dyv, gam[c][v], s1);
+        s2 = __builtin_fmaf(dyh, xc, s2);
+        acc[0][c][v] = __builtin_fmaf(dyv * xc, rs, acc[0][c][v]);
+        if (NACC == 2) acc[NACC - 1][c][v] += dyv;
+      }
+    }
+  }
+  pin(acc);
+  keep_packed(b.x);
+  keep_packed(b.dy);
+  // every lane takes part in the butterfly (rows that do not exist add zeros
+  // to a sum nobody uses)
+  s2 = half_sum(s2, hi);
+  if (KIND == kLayerNorm) s1 = half_sum(s1, hi);
+  if (RALL || active) {
+    const float m2 = s2 * inv_n * rs;  // mean_j(dyhat * xhat)
+    const float c2 = -(rs * rs) * m2;
+    const float c1 = (KIND == kLayerNorm) ? -rs * (s1 * inv_n) : 0.0f;
+    __amdgpu_buffer_rsrc_t ro;
+    if constexpr (RALL) ro = row_rsrc(dx + r0 * ldo * EB, span_o);
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int col = col0 + c * cstride;
+      float o[VEC];
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        const float xc = b.x[c].get(v) - mu;
+        const float dyh = b.dy[c].get(v) * gam[c][v];
+        o[v] = __builtin_fmaf(dyh, rs, __builtin_fmaf(xc, c2, c1));
+      }
+      Pack<Tg, VEC> out;
+      out.set(o);
+      if constexpr (RALL) out.store_stream_buf(ro, hoff_o + (uint32_t)col * EB);
+      else out.store_stream(dx + (r * ldo + col) * EB);
+    }
+  }
+}
+
+// P = waves per workgroup (2 * P rows in flight). span_* = bytes from a row
+// pair's first row to the end of its second row (G * ld + N elements), which
+// the host checked to be below 2^32.
+template <int KIND, class Tg, int C, int NACC, bool WSNT>
+__global__ __launch_bounds__(kTwoRowMaxThreads)
+void dx_partials_tworow_kernel(const void* __restrict__ xv, const void* __restrict__ dyv,
+                               const void* __restrict__ gv, const float* __restrict__ mean,
+                               const float* __restrict__ rstd, void* __restrict__ dxv,
+                               float* __restrict__ ws, int64_t M, int N, int64_t ldx,
+                               int64_t ldy, int64_t ldo, int64_t G, int P) {
+  constexpr int EB = Tg::kBytes;
+  constexpr int VEC = 16 / EB;
+  constexpr int D = kTwoRowDepth;
+  using PK = Pack<Tg, VEC>;
+  using RB = RowBuf<Tg, VEC, C>;
+  const char* __restrict__ x = static_cast<const char*>(xv);
+  const char* __restrict__ dy = static_cast<const char*>(dyv);
+  const char* __restrict__ gm = static_cast<const char*>(gv);
+  char* __restrict__ dx = static_cast<char*>(dxv);
+  extern __shared__ float comb[];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5;
+  const bool hi = h != 0;
+  const int col0 = (lane & 31) * VEC;
+  constexpr int cstride = 32 * VEC;
+  const float inv_n = 1.0f / (float)N;
+  // the second half's row is G rows after the first half's
+  const uint32_t hoff_x = (uint32_t)(h * G * ldx * EB);
+  const uint32_t hoff_y = (uint32_t)(h * G * ldy * EB);
+  const uint32_t hoff_o = (uint32_t)(h * G * ldo * EB);
+  const uint32_t span_x = (uint32_t)((G * ldx + N) * EB);
+  const uint32_t span_y = (uint32_t)((G * ldy + N) * EB);
+  const uint32_t span_o = (uint32_t)((G * ldo + N) * EB);
+
+  float gam[C][VEC];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    PK t;
+    t.load(gm + (int64_t)(col0 + c * cstride) * EB);
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) gam[c][v] = t.get(v);
+  }
+
+  for (int64_t g = blockIdx.x; g < G; g += gridDim.x) {
+    const int64_t rows = (M - g + G - 1) / G;  // rows of group g
+    const int iters = (int)((rows + 2 * P - 1) / (2 * P));
+    // first row of wave w's pair in iteration k (uniform), and this lane's row
+    auto pair0 = [&](int k) { return g + (int64_t)(2 * (k * P + w)) * G; };
+    auto row_of = [&](int k) { return pair0(k) + h * G; };
+    auto exists = [&](int k) { return (int64_t)(2 * (k * P + w) + h) < rows; };
+
+    float acc[NACC][C][VEC];
+#pragma unroll
+    for (int a = 0; a < NACC; ++a)
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[a][c][v] = 0.0f;
+
+    RB buf[D];
+    // Steady state (as kernel A's): iterations in which all 2P rows exist run
+    // through a loop with no per-lane or per-row conditions; the general loop
+    // takes the remaining iterations from the same ring state.
+    const int kfull = (int)(rows / (2 * P));
+    int it0 = 0;
+    const bool steady =
+        kfull >= 2 * D - 1 && rows * (int64_t)N * EB <= kSteadyGroupBytes;
+    if (steady) {
+#pragma unroll
+      for (int k = 0; k < D - 1; ++k)
+        fetch_pair<KIND, true>(buf[k], x, dy, mean, rstd, pair0(k), row_of(k), true, ldx, ldy,
+                               hoff_x, hoff_y, span_x, span_y, col0, cstride);
+      for (; it0 + 2 * D - 2 < kfull; it0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          const int k = it0 + d;
+          fetch_pair<KIND, true>(buf[(d + D - 1) % D], x, dy, mean, rstd, pair0(k + D - 1),
+                                 row_of(k + D - 1), true, ldx, ldy, hoff_x, hoff_y, span_x,
+                                 span_y, col0, cstride);
+          process_pair<KIND, true>(buf[d], gam, acc, dx, pair0(k), row_of(k), true, hi, ldo,
+                                   hoff_o, span_o, inv_n, col0, cstride);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < D - 1; ++k)
+        if (k < iters)
+          fetch_pair<KIND, false>(buf[k], x, dy, mean, rstd, pair0(k), row_of(k), exists(k), ldx,
+                                  ldy, hoff_x, hoff_y, span_x, span_y, col0, cstride);
+    }
+    for (int it = it0; it < iters; it += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const int k = it + d;
+        if (k + D - 1 < iters)
+          fetch_pair<KIND, false>(buf[(d + D - 1) % D], x, dy, mean, rstd, pair0(k + D - 1),
+                                  row_of(k + D - 1), exists(k + D - 1), ldx, ldy, hoff_x,
+                                  hoff_y, span_x, span_y, col0, cstride);
+        if (k < iters)
+          process_pair<KIND, false>(buf[d], gam, acc, dx, pair0(k), row_of(k), exists(k), hi,
+                                    ldo, hoff_o, span_o, inv_n, col0, cstride);
+      }
+    }
+
+    // the two halves: half 0 + half 1 (the same sum in both halves)
+#pragma unroll
+    for (int a = 0; a < NACC; ++a)
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          const float other = __shfl_xor(acc[a][c][v], 32);
+          acc[a][c][v] = hi ? other + acc[a][c][v] : acc[a][c][v] + other;
+        }
+    // the P waves in wave order 0, 1, ..., P-1 (half 0 of each)
+    if (P > 1) {
+      for (int q = 1; q < P; ++q) {
+        if (w == q && !hi) {
+#pragma unroll
+          for (int a = 0; a < NACC; ++a)
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+              for (int v = 0; v < VEC; ++v)
+                comb[((a * C + c) * 32 + (lane & 31)) * VEC + v] = acc[a][c][v];
+        }
+        __syncthreads();
+        if (w == 0) {
+#pragma unroll
+          for (int a = 0; a < NACC; ++a)
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+              for (int v = 0; v < VEC; ++v)
+                acc[a][c][v] += comb[((a * C + c) * 32 + (lane & 31)) * VEC + v];
+        }
+        __syncthreads();
+      }
+    }
+    if (w == 0 && !hi) {
+#pragma unroll
+      for (int a = 0; a < NACC; ++a) {
+        float* __restrict__ dst = ws + ((int64_t)a * G + g) * (int64_t)N;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          const int col = col0 + c * cstride;
+#pragma unroll
+          for (int v = 0; v < VEC; v += 4) {
+            const f32x4 t = {acc[a][c][v], acc[a][c][v + 1], acc[a][c][v + 2], acc[a][c][v + 3]};
+            f32x4* q = reinterpret_cast<f32x4*>(dst + col + v);
+            if constexpr (WSNT) __builtin_nontemporal_store(t, q);
+            else *q = t;
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace nb

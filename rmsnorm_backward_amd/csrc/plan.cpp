@@ -54,6 +54,14 @@ constexpr int kPreferredLaneBytes = 32;
 // every bf16 workload measured (N = 4096: 32-byte rows, 97 us vs 118 us at
 // 64 bytes; N = 8192: 64-byte rows, 527 us vs 570 us at 128 bytes).
 constexpr int64_t kWgradTargetTiles = 256;
+// The two-rows-per-wave kernel's launch bound (nb_tworow.hpp).
+constexpr int kTwoRowMaxThreads = 512;
+// Its rows in flight per workgroup: the fewest (even, a power of two) whose x
+// and dy reach this many bytes. Interleaved on the same buffers, one row per
+// wave against two: 262144 x 768 bf16 RMSNorm 219.1 us against 210.7 us at 4
+// rows (8: 220.9, 16: 231.1); 1048576 x 256 317.5 against 285.7 at 8 rows
+// (4: 411.4, 16: 309.6). Rings deeper than 3 row pairs were slower.
+constexpr int64_t kTwoRowBytesInFlight = 8192;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -87,16 +95,33 @@ bool kernel_a_exists(int io_dtype, int vec_full, int with_dbeta, int chunks) {
 
 int kernel_a_max_threads(int lane_elems) { return lane_elems > 16 ? 512 : 1024; }
 
+int two_row_chunks(int64_t N, int io_dtype) {
+  const int eb = dtype_bytes(io_dtype);
+  if (eb == 0 || N <= 0) return 0;
+  const int64_t vw = 16 / eb;
+  if (N % (64 * vw) == 0) return 0;  // 64-lane waves cover it without idle lanes
+  for (int c : {1, 3})
+    if (N == (int64_t)c * 32 * vw) return c;
+  return 0;
+}
+
+bool two_row_span_ok(int64_t G, int64_t N, int64_t ld, int io_dtype) {
+  const int eb = dtype_bytes(io_dtype);
+  if (ld < N) ld = N;
+  if (G < 0 || eb == 0 || G > ((int64_t)1 << 32) / (ld > 0 ? ld : 1)) return false;
+  return (G * ld + N) * eb < ((int64_t)1 << 32);
+}
+
 // Lane layout of kernel A for rows of N elements (fills vec, chunks,
 // waves_per_row, rows_in_flight, threads, lds_bytes of *p).
 int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok16,
-                  norm_bwd_plan_t* p, const char** why, bool row_stats) {
-  (void)kind;
+                  norm_bwd_plan_t* p, const char** why, bool row_stats, bool two_row_ok) {
   const int eb = dtype_bytes(io_dtype);
   const int nacc = with_dbeta ? 2 : 1;
   const int vw = 16 / eb;
   const int full = (vec_ok16 && N % vw == 0) ? 1 : 0;
   p->vec = full ? vw : 1;
+  p->rows_per_wave = 1;
   if (N == 0) {  // a minimal valid geometry
     p->chunks = 1;
     p->waves_per_row = 1;
@@ -145,6 +170,23 @@ int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok
   p->rows_in_flight = P;
   p->threads = 64 * S * P;
   p->lds_bytes = lds;
+  // Two rows per wave where 32 lanes cover the row exactly (kernel A with
+  // saved statistics), for RMSNorm: LayerNorm, with its second row sum, gained
+  // nothing from it (131072 x 768 bf16 with dbeta: 115.5 us with one row per
+  // wave, 115.7 us at best with two), so it keeps one row per wave.
+  const int c2 = (two_row_ok && !row_stats && full && kind == NORM_BWD_RMSNORM)
+                     ? two_row_chunks(N, io_dtype) : 0;
+  if (c2) {
+    int P2 = 2;
+    while (P2 * 32 < kTwoRowMaxThreads && (int64_t)P2 * 2 * N * eb < kTwoRowBytesInFlight)
+      P2 *= 2;
+    p->rows_per_wave = 2;
+    p->chunks = c2;
+    p->waves_per_row = 1;
+    p->rows_in_flight = P2;
+    p->threads = 32 * P2;
+    p->lds_bytes = P2 > 2 ? nacc * c2 * 32 * p->vec * 4 : 0;
+  }
   return NORM_BWD_OK;
 }
 
@@ -226,7 +268,7 @@ int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype, bool recompute
 
 int make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,
               int64_t groups, bool vec_ok16, norm_bwd_plan_t* plan, const char** why,
-              bool recompute) {
+              bool recompute, int64_t max_ld) {
   if (!plan) return fail(why, "plan is NULL", NORM_BWD_ERR_INVALID_ARG);
   if (kind != NORM_BWD_LAYERNORM && kind != NORM_BWD_RMSNORM)
     return fail(why, "kind must be NORM_BWD_LAYERNORM or NORM_BWD_RMSNORM", NORM_BWD_ERR_INVALID_ARG);
@@ -248,7 +290,7 @@ int make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,
 
   const char* gwhy = nullptr;
   const int st = make_geometry(kind, N, io_dtype, with_dbeta, vec_ok16, &p, &gwhy,
-                               recompute && kind == NORM_BWD_LAYERNORM);
+                               recompute && kind == NORM_BWD_LAYERNORM, !recompute);
   if (st != NORM_BWD_OK) return fail(why, gwhy, st);
   if (N == 0) {  // nothing to compute
     *plan = p;
@@ -261,6 +303,10 @@ int make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,
     p.groups = G;
     p.rows_per_group = ceil_div(M, G);
     p.grid = (int32_t)(G < kMaxGrid ? G : kMaxGrid);
+    // a row pair too far apart for 32-bit offsets keeps one row per wave
+    if (p.rows_per_wave == 2 && !two_row_span_ok(G, N, max_ld ? max_ld : N, io_dtype))
+      make_geometry(kind, N, io_dtype, with_dbeta, vec_ok16, &p, &gwhy,
+                    recompute && kind == NORM_BWD_LAYERNORM, false);
   } else {
     p.rows_per_group = 1;
     p.groups = 0;
@@ -268,6 +314,42 @@ int make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,
   }
   p.workspace_bytes = (size_t)nacc * (size_t)p.groups * (size_t)N * 4u;
   *plan = p;
+  return NORM_BWD_OK;
+}
+
+// The remaining checks of a two-rows-per-wave plan (fields up to vec done).
+static int validate_two_row(const norm_bwd_plan_t* p, const char** why) {
+  const int nacc = p->with_dbeta ? 2 : 1;
+  if (p->vec != 16 / dtype_bytes(p->io_dtype))
+    return fail(why, "plan.rows_per_wave = 2 needs 16-byte vectors", NORM_BWD_ERR_INVALID_ARG);
+  if ((p->chunks != 1 && p->chunks != 3) || p->N != (int64_t)p->chunks * 32 * p->vec)
+    return fail(why, "plan.rows_per_wave = 2 needs chunks 1 or 3 and N = 32 * vec * chunks",
+                NORM_BWD_ERR_UNSUPPORTED);
+  if (p->waves_per_row != 1)
+    return fail(why, "plan.rows_per_wave = 2 needs waves_per_row = 1", NORM_BWD_ERR_INVALID_ARG);
+  const int P = p->rows_in_flight;
+  if (P < 2 || P % 2 != 0 || 32 * P > kTwoRowMaxThreads)
+    return fail(why, "plan.rows_in_flight must be even, in [2, 16], with rows_per_wave = 2",
+                NORM_BWD_ERR_INVALID_ARG);
+  if (p->threads != 32 * P)
+    return fail(why, "plan.threads must be 32 * rows_in_flight with rows_per_wave = 2",
+                NORM_BWD_ERR_INVALID_ARG);
+  const int want_lds = P > 2 ? nacc * p->chunks * 32 * p->vec * 4 : 0;
+  if (p->lds_bytes != want_lds)
+    return fail(why, "plan.lds_bytes inconsistent", NORM_BWD_ERR_INVALID_ARG);
+  if (p->M == 0) {
+    if (p->groups != 0) return fail(why, "plan.groups must be 0 when M = 0", NORM_BWD_ERR_INVALID_ARG);
+    return NORM_BWD_OK;
+  }
+  if (p->groups < 1 || p->groups > p->M)
+    return fail(why, "plan.groups must be in [1, M]", NORM_BWD_ERR_INVALID_ARG);
+  if (p->rows_per_group != ceil_div(p->M, p->groups))
+    return fail(why, "plan.rows_per_group must be ceil(M / groups)", NORM_BWD_ERR_INVALID_ARG);
+  if (p->grid < 1 || p->grid > p->groups || p->grid > kMaxGrid)
+    return fail(why, "plan.grid must be in [1, groups]", NORM_BWD_ERR_INVALID_ARG);
+  if (!two_row_span_ok(p->groups, p->N, p->N, p->io_dtype))
+    return fail(why, "plan.rows_per_wave = 2: groups * N too large for 32-bit offsets",
+                NORM_BWD_ERR_INVALID_ARG);
   return NORM_BWD_OK;
 }
 
@@ -290,6 +372,9 @@ int validate_plan(const norm_bwd_plan_t* p, const char** why) {
   else if (p->vec == 1) full = 0;
   else return fail(why, "plan.vec must be 16/elem_size (with N a multiple of it) or 1",
                    NORM_BWD_ERR_INVALID_ARG);
+  if (p->rows_per_wave == 2) return validate_two_row(p, why);
+  if (p->rows_per_wave != 1)
+    return fail(why, "plan.rows_per_wave must be 1 or 2", NORM_BWD_ERR_INVALID_ARG);
   if (!kernel_a_exists(p->io_dtype, full, p->with_dbeta, p->chunks))
     return fail(why, "plan.chunks: no kernel for this vec*chunks", NORM_BWD_ERR_UNSUPPORTED);
   const int S = p->waves_per_row, P = p->rows_in_flight;

@@ -26,8 +26,20 @@ int kernel_a_max_threads(int lane_elems);
 // statistics or, with `row_stats`, for the kernels that compute row
 // statistics (the forward, kernel A in recompute mode): the lane layout is
 // the same, the rows in flight differ. Returns a status.
+// `two_row_ok`: the caller can run the two-rows-per-wave kernel (saved
+// statistics); RMSNorm rows it covers exactly then take that layout.
 int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok16,
-                  norm_bwd_plan_t* plan, const char** why, bool row_stats);
+                  norm_bwd_plan_t* plan, const char** why, bool row_stats,
+                  bool two_row_ok = false);
+
+// The two-rows-per-wave layout for rows of N elements: its chunk count (1 or
+// 3) when 32 lanes of 16-byte vectors cover N exactly and 64-lane waves would
+// not, else 0.
+int two_row_chunks(int64_t N, int io_dtype);
+
+// Whether a row pair of the two-row layout, G rows apart with row stride ld
+// (elements), spans fewer than 2^32 bytes (its 32-bit buffer offsets).
+bool two_row_span_ok(int64_t G, int64_t N, int64_t ld, int io_dtype);
 
 // Whether the fused kernels (rows held in registers) cover rows of N elements
 // of io_dtype; wider rows take the row-loop path.
@@ -60,16 +72,20 @@ int64_t forward_grid(int64_t M, int S, int P);
 int wgrad_lanes_per_row(int64_t N, int vec);
 
 // Automatic group count for (kind, M, N, io_dtype) and the statistics mode:
-// 256 with saved statistics; in recompute mode about 2048 waves in flight
-// (4096 for LayerNorm); at least 4 rows per group. Independent of the device.
+// 256, except LayerNorm in recompute mode (about 4096 waves in flight: 512
+// for its 512-thread workgroups); at least 4 rows per group, above 256 a
+// multiple of 256. Independent of the device.
 int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype, bool recompute = false);
 
 // Fill *plan (see norm_bwd_make_plan). `vec_ok16` says whether the caller's
 // pointers are 16-byte aligned. Writes a message into *why on failure.
-// `recompute`: the plan is for recompute mode (affects the automatic groups).
+// `recompute`: the plan is for recompute mode (affects the automatic groups;
+// the two-row layout serves saved statistics only). `max_ld`: the largest
+// row stride in elements of x, dy and dx (0: N), for the two-row layout's
+// span.
 int make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,
               int64_t groups, bool vec_ok16, norm_bwd_plan_t* plan, const char** why,
-              bool recompute = false);
+              bool recompute = false, int64_t max_ld = 0);
 
 // Check every field of a (possibly caller-edited) plan. Returns a status.
 int validate_plan(const norm_bwd_plan_t* plan, const char** why);

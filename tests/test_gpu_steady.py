@@ -176,3 +176,89 @@ def test_steady_loop_forward(nb, kind, dt, N, M):
     ry, rm, rr = oracle.fwd(kind, x, g, None, w.eps)
     parity.check_forward(w.io_dtype, kind, x, g, None, y.cpu(),
                          None if mean is None else mean.cpu(), rstd.cpu(), ry, rm, rr)
+
+
+# The two-rows-per-wave kernel (rows that 32 lanes of 16-byte vectors cover
+# exactly: N = 32 * VEC * 1 or 3). Its steady-state loop needs at least
+# 5 * P rows per group (P = rows in flight, two per wave, a 3-deep ring);
+# row counts around that threshold and with every kind of tail. The planner
+# takes it for RMSNorm; LayerNorm plans are edited to it here, with the rows
+# in flight the RMSNorm rule gives.
+TWO_ROW = [
+    ("rmsnorm", torch.bfloat16, 768, 2),      # P = 8 (4 waves)
+    ("layernorm", torch.bfloat16, 768, 2),    # both gradients
+    ("layernorm", torch.float16, 256, 3),     # one chunk, P = 16
+    ("rmsnorm", torch.float16, 768, 1),       # one group
+    ("rmsnorm", torch.float32, 384, 2),       # fp32, three chunks of 4
+    ("layernorm", torch.float32, 128, 1),     # fp32, one chunk
+]
+
+
+def _two_row_cases():
+    for kind, dt, N, G in TWO_ROW:
+        eb = torch.tensor([], dtype=dt).element_size()
+        P = 2
+        while P < 16 and P * 2 * N * eb < 8192:
+            P *= 2
+        for M in (G * 5 * P - 1, G * 5 * P, G * 5 * P + 1, G * (6 * P + 3) + 1,
+                  G * (8 * P - 1), 3):
+            yield kind, dt, N, G, M
+
+
+@pytest.mark.parametrize("kind,dt,N,G,M", list(_two_row_cases()),
+                         ids=lambda v: str(v).replace("torch.", ""))
+def test_two_row_kernel(nb, kind, dt, N, G, M):
+    w = workload(kind, dt, M, N)
+    with_db = kind == "layernorm"
+    inp = backward_inputs(w)
+    plan = nb.norm_bwd_make_plan(kind, M, N, dt, with_db, G)
+    if kind == "layernorm":
+        assert plan.rows_per_wave == 1
+        ref = nb.norm_bwd_make_plan("rmsnorm", M, N, dt, with_db, G)
+        plan.rows_per_wave, plan.chunks, plan.waves_per_row = 2, ref.chunks, 1
+        plan.rows_in_flight, plan.threads = ref.rows_in_flight, ref.threads
+        plan.lds_bytes = (2 if with_db else 1) * ref.chunks * 32 * ref.vec * 4 \
+            if ref.rows_in_flight > 2 else 0
+    assert plan.rows_per_wave == 2 and plan.waves_per_row == 1
+    g = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor) and k != "outliers"}
+    print(f"[run] two-row {w.name} groups={G} P={plan.rows_in_flight}", flush=True)
+    out = nb.norm_bwd_execute(plan, g["x"], g["dy"], g["gamma"], g.get("mean"), g["rstd"],
+                              wgrad_dtype=w.wgrad_dtype)
+    torch.cuda.synchronize()
+    compare(w, inp, out, inp.get("mean"), inp["rstd"], with_db, G)
+
+
+@pytest.mark.parametrize("P", [2, 4, 16])
+def test_two_row_rows_in_flight(nb, P):
+    """Edited plans with other rows in flight (1, 2 or 8 waves) stay within
+    tolerance; 90 rows in 3 groups leave every kind of tail."""
+    w = workload("layernorm", torch.bfloat16, 5 * 16 * 3 + 90, 768)
+    inp = backward_inputs(w)
+    plan = nb.norm_bwd_make_plan("layernorm", w.M, w.N, w.io_dtype, True, 3)
+    plan.rows_per_wave, plan.chunks, plan.waves_per_row = 2, 3, 1
+    plan.rows_in_flight, plan.threads = P, 32 * P
+    plan.lds_bytes = 2 * plan.chunks * 32 * plan.vec * 4 if P > 2 else 0
+    g = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor) and k != "outliers"}
+    out = nb.norm_bwd_execute(plan, g["x"], g["dy"], g["gamma"], g["mean"], g["rstd"])
+    torch.cuda.synchronize()
+    compare(w, inp, out, inp["mean"], inp["rstd"], True, 3)
+
+
+def test_two_row_strided_rows_are_bit_identical(nb):
+    """Row strides (16-byte aligned) give the bits of contiguous rows on the
+    two-row layout."""
+    w = workload("rmsnorm", torch.bfloat16, 1000, 768)
+    inp = backward_inputs(w)
+    x, dy, gam, rs = (inp[k].cuda() for k in ("x", "dy", "gamma", "rstd"))
+
+    def strided(t, ld):
+        buf = torch.zeros(t.shape[0] * ld, dtype=t.dtype, device="cuda")
+        v = buf.view(t.shape[0], ld)[:, :t.shape[1]]
+        v.copy_(t)
+        return v
+
+    ref = nb.norm_bwd_ex("rmsnorm", x, dy, gam, None, rs, w.eps)
+    got = nb.norm_bwd_ex("rmsnorm", strided(x, 768 + 8), strided(dy, 768 + 64), gam, None, rs,
+                         w.eps, dx=strided(torch.zeros_like(x), 768 + 24))
+    torch.cuda.synchronize()
+    assert torch.equal(got[0].cpu(), ref[0].cpu()) and torch.equal(got[1].cpu(), ref[1].cpu())

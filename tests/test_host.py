@@ -50,9 +50,10 @@ def test_library_exports_every_declared_symbol(nb):
 
 
 def test_plan_struct_layout_matches_header(nb):
-    # norm_bwd_plan_t: 4 int32, 4 int64, 6 int32, size_t -> 80 bytes
-    assert ctypes.sizeof(nb.NormBwdPlan) == 80
-    assert nb.NormBwdPlan.workspace_bytes.offset == 72
+    # norm_bwd_plan_t: 4 int32, 4 int64, 7 int32, size_t -> 88 bytes
+    assert ctypes.sizeof(nb.NormBwdPlan) == 88
+    assert nb.NormBwdPlan.rows_per_wave.offset == 72
+    assert nb.NormBwdPlan.workspace_bytes.offset == 80
     assert nb.NormBwdPlan.chunks.offset == 48
 
 
@@ -167,7 +168,8 @@ GEOMS = [(kind, dt, M, N, db, g)
          for kind in ("layernorm", "rmsnorm")
          for dt in (torch.float32, torch.float16, torch.bfloat16)
          for (M, N) in ((1, 1), (3, 7), (17, 63), (64, 64), (65, 65), (1151, 8192),
-                        (2, 768), (100, 4096), (7, 16384), (9, 1000))
+                        (2, 768), (100, 4096), (7, 16384), (9, 1000), (300, 256),
+                        (1000, 384), (33, 128), (5000, 768))
          for db in (False, True)
          for g in (0, 1, 5)]
 
@@ -180,6 +182,22 @@ def test_plan_invariants(nb, kind, dt, M, N, db, groups):
     p = nb.norm_bwd_make_plan(kind, M, N, dt, db, groups)
     S, P, C, vec = p.waves_per_row, p.rows_in_flight, p.chunks, p.vec
     assert vec in (1, 16 // eb) and (vec == 1 or N % vec == 0)
+    nacc = 2 if db else 1
+    vw = 16 // eb
+    # RMSNorm rows that 64-lane waves would cover with idle lanes and 32 lanes
+    # cover exactly (N = 32 * vw * 1 or 3) take two rows per wave
+    c2 = next((c for c in (1, 3) if N == c * 32 * vw), 0) if N % (64 * vw) else 0
+    if c2 and kind == "rmsnorm":
+        assert p.rows_per_wave == 2 and vec == vw and S == 1 and C == c2
+        want = 2
+        while want * 32 < 512 and want * 2 * N * eb < 8192:
+            want *= 2
+        assert P == want and p.threads == 32 * P
+        assert p.lds_bytes == (nacc * C * 32 * vec * 4 if P > 2 else 0)
+        assert 1 <= p.groups <= M and p.rows_per_group == -(-M // p.groups)
+        assert p.workspace_bytes == nacc * p.groups * N * 4
+        return
+    assert p.rows_per_wave == 1
     # rows in flight: the fewest (a power of two) whose x and dy reach 16 KiB,
     # within 16 waves and the kernel's launch bound; one when the combine
     # buffer would not fit
@@ -205,6 +223,25 @@ def test_plan_invariants(nb, kind, dt, M, N, db, groups):
     assert p.workspace_bytes == nacc * p.groups * N * 4
     assert p.lds_bytes == (nacc * S * C * 64 * vec * 4 if P > 1 else 0)
     assert p.lds_bytes <= 65536
+
+
+def test_two_row_layout_needs_32_bit_pair_offsets(nb):
+    """The two-row layout addresses a row pair (G rows apart) with 32-bit
+    offsets; plans whose pair would span 2^32 bytes keep one row per wave,
+    and a two-row plan edited to such a group count is refused."""
+    p = nb.norm_bwd_make_plan("rmsnorm", 1 << 23, 768, torch.bfloat16, False, 1 << 21)
+    assert p.rows_per_wave == 2            # (2^21 + 1) * 768 * 2 < 2^32
+    p = nb.norm_bwd_make_plan("rmsnorm", 1 << 23, 768, torch.bfloat16, False, 3 << 20)
+    assert p.rows_per_wave == 1            # (3 * 2^20 + 1) * 768 * 2 >= 2^32
+    p = nb.norm_bwd_make_plan("rmsnorm", 1 << 23, 768, torch.bfloat16, False, 1 << 21)
+    p.groups = 3 << 20
+    p.rows_per_group = -(-p.M // p.groups)
+    p.grid = 1 << 20
+    p.workspace_bytes = p.groups * 768 * 4
+    lib = nb.load_library()
+    st = lib.norm_bwd_execute(ctypes.byref(p), _addr(0), _addr(1), _addr(2), None, _addr(3), 0,
+                              _addr(4), _addr(5), None, _addr(6), p.workspace_bytes, None)
+    assert st == 1 and "32-bit" in nb.norm_bwd_last_error()
 
 
 def test_groups_do_not_depend_on_device(nb):
