@@ -37,7 +37,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import math
 import os
@@ -51,7 +50,6 @@ sys.path.insert(0, ROOT)
 METRIC = "norm-backward achieved HBM GB/s and % of peak (16384×4096 bf16 RMSNorm)"
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E, published
 MALL_BYTES = 256 << 20        # Infinity Cache
-KERNEL_SOURCE = os.path.join(ROOT, "rmsnorm_backward_amd", "csrc", "nb_device.hpp")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -61,6 +59,13 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
+    ap.add_argument("--shape", default=None,
+                    help="KIND_DTYPE_MxN (e.g. rmsnorm_bf16_65536x1024): that shape alone, with "
+                         "the distributions of the headline (RMSNorm) or of 65536x8192 "
+                         "(LayerNorm)")
+    ap.add_argument("--plan", default=None,
+                    help="plan field overrides, e.g. rows_in_flight=8,rows_per_wave=1 (the "
+                         "explicit-plan path; the library validates the edited plan)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="one-thread oracle time on the primary workload")
@@ -76,8 +81,9 @@ def parse_args(argv=None):
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of kernel A's sources (the committed counters hold while it does)."""
+    from rmsnorm_backward_amd import profiling
+    return profiling.kernel_source_hash()
 
 
 def committed_traffic(workload: str):
@@ -123,6 +129,37 @@ def forward_bytes(w, with_beta: bool) -> int:
     s = w.io_bytes
     stats = 8 if w.kind == "layernorm" else 4
     return w.M * (2 * w.N * s + stats) + w.N * s * (2 if with_beta else 1)
+
+
+def parse_shape(W, torch, spec: str):
+    """KIND_DTYPE_MxN -> a workload of that shape with the distributions of
+    the headline (RMSNorm) or of 65536 x 8192 (LayerNorm)."""
+    kind, dt, mn = spec.split("_")
+    M, N = (int(v) for v in mn.split("x"))
+    dtype = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+    base = W.LN_BF16_65536x8192 if kind == "layernorm" else W.HEADLINE
+    if kind not in ("layernorm", "rmsnorm"):
+        raise ValueError(f"unknown kind in --shape {spec}")
+    return W.scaled(base, M=M, N=N, io_dtype=dtype, name=spec)
+
+
+def edit_plan(plan, spec: str, with_db: bool):
+    """Apply --plan overrides (field=value, comma separated) and make threads
+    and lds_bytes consistent with them, as the planner would."""
+    for item in filter(None, spec.split(",")):
+        k, v = item.split("=")
+        if k not in ("rows_in_flight", "rows_per_wave", "waves_per_row", "chunks"):
+            raise ValueError(f"--plan: cannot set {k}")
+        setattr(plan, k, int(v))
+    nacc = 2 if with_db else 1
+    S, C, P, vec = plan.waves_per_row, plan.chunks, plan.rows_in_flight, plan.vec
+    if plan.rows_per_wave == 2:
+        plan.threads = 32 * P
+        plan.lds_bytes = nacc * C * 32 * vec * 4 if P > 2 else 0
+    else:
+        plan.threads = 64 * S * P
+        plan.lds_bytes = nacc * S * C * 64 * vec * 4 if P > 1 else 0
+    return plan
 
 
 def time_loop(torch, fn, steps, stream):
@@ -304,7 +341,37 @@ def triad_sweep(torch, nb, dev, stream, operand_bytes):
             "stores, 2 reads : 1 write as kernel A", "bytes_per_operand": operand_bytes,
             "GBps": round(best[2], 1), "grid": best[0], "unroll": best[1],
             "pct_of_peak": round(100 * best[2] / PEAK_HBM_GBPS, 2), "result_ok": ok,
-            "sweep_min_GBps": round(min(t[2] for t in sweep), 1), "launch_shapes": len(sweep)}
+            "sweep_min_GBps": round(min(t[2] for t in sweep), 1), "launch_shapes": len(sweep),
+            "sweep": [[g, u, round(v, 1)] for g, u, v in sweep]}
+
+
+# Launch shapes of the same-size triad (grid, unroll); grid 0 = one pass.
+SAME_SIZE_SHAPES = ((0, 1), (0, 2), (0, 4), (256, 4), (512, 4), (1024, 2), (1024, 4), (2048, 2))
+
+
+def triad_same_size(torch, nb, dev, stream, operand_bytes, steps):
+    """The triad over three operands of one workload's x (dy, dx) size, on
+    enough rotating buffer sets to stream from HBM like kernel A: the
+    achievable rate for that many bytes per launch, fixed costs included."""
+    n = max(4, operand_bytes // 16 * 4)
+    nsets = max(2, min(64, math.ceil(4 * MALL_BYTES / (3 * n * 4))))
+    sets = [[torch.empty(n, dtype=torch.int32, device=dev).fill_(k) for k in (1, 2, 0)]
+            for _ in range(nsets)]
+    best = (0.0, None)
+    for grid, unroll in SAME_SIZE_SHAPES:
+        def go(i):
+            a, b, c = sets[i % nsets]
+            nb.norm_bwd_probe_triad(a, b, c, grid, unroll)
+        for i in range(5):
+            go(i)
+        ms = time_loop(torch, go, steps, stream)
+        gbps = 3 * n * 4 / (ms * 1e-3) / 1e9
+        if gbps > best[0]:
+            best = (gbps, (grid, unroll), ms)
+    del sets
+    torch.cuda.empty_cache()
+    return {"GBps": round(best[0], 1), "us": round(best[2] * 1e3, 3),
+            "grid": best[1][0], "unroll": best[1][1], "bytes_per_launch": 3 * n * 4}
 
 
 def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, extras, triad):
@@ -318,6 +385,8 @@ def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, ext
     io = nb._DTYPE_CODE[w.io_dtype]
     wg = nb._DTYPE_CODE[w.wgrad_dtype]
     plan = nb.norm_bwd_make_plan(w.kind, w.M, w.N, w.io_dtype, with_db, args.groups)
+    if args.plan:
+        plan = edit_plan(plan, args.plan, with_db)
     set_bytes = 3 * w.M * w.N * w.io_bytes
     nsets = args.sets or max(2, math.ceil(4 * MALL_BYTES / max(set_bytes, 1)))
     nsets = min(nsets, 64)
@@ -359,7 +428,7 @@ def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, ext
                           ptr(s.get("mean")), ptr(s["rstd"]), ptr(s["dx"]), ptr(ws), ws.numel(),
                           sh))
     fn = lib.norm_bwd_layernorm if w.kind == "layernorm" else lib.norm_bwd_rmsnorm
-    if args.groups:
+    if args.groups or args.plan:
         fn = None
 
     def step(i):
@@ -391,6 +460,16 @@ def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, ext
     chunks = sorted(time_loop(torch, step, 25, stream) for _ in range(20))
     ms_a = time_loop(torch, step_a, steps, stream)
     ms_b = time_loop(torch, step_b, max(steps, 50), stream)
+    # the kernel boundary: kernel A, then a dependent 16-byte copy on the stream
+    tiny = torch.zeros(8, dtype=torch.int32, device=dev)
+    tiny_src, tiny_dst = ptr(tiny[:4]), ptr(tiny[4:])
+
+    def step_a_gap(i):
+        step_a(i)
+        if lib.norm_bwd_probe_copy(tiny_src, tiny_dst, 16, sh):
+            raise RuntimeError(nb.norm_bwd_last_error())
+
+    ms_a_gap = time_loop(torch, step_a_gap, steps, stream)
 
     alg = w.algorithmic_bytes()
     value = alg / (ms * 1e-3) / 1e9
@@ -412,6 +491,7 @@ def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, ext
         "kernel_a_traffic": committed_traffic(w.name),
         "kernel_b_alone_us": round(ms_b * 1e3, 3),
         "kernel_b_in_place_us": round((ms - ms_a) * 1e3, 3),
+        "kernel_boundary_us": round((ms_a_gap - ms_a) * 1e3, 3),
         "workspace_bytes": plan.workspace_bytes,
         "counted_GBps_incl_workspace": round((alg + 2 * plan.workspace_bytes) / (ms * 1e-3) / 1e9,
                                              2),
@@ -421,6 +501,9 @@ def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, ext
     if triad:
         entry["pct_of_triad"] = round(100 * value / triad["GBps"], 2)
         entry["kernel_a_pct_of_triad"] = round(100 * achieved / triad["GBps"], 2)
+        same = triad_same_size(torch, nb, dev, stream, w.M * w.N * w.io_bytes, max(steps, 50))
+        entry["triad_same_bytes"] = same
+        entry["kernel_a_pct_of_triad_same_bytes"] = round(100 * achieved / same["GBps"], 2)
     plan_d = {k: v for k, v in plan.as_dict().items()
               if k in ("groups", "rows_per_group", "vec", "chunks", "waves_per_row",
                        "rows_in_flight", "rows_per_wave", "threads", "grid")}
@@ -620,9 +703,12 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
-    primary = W.WORKLOADS[args.workload] if args.workload else W.HEADLINE
-    others = [] if args.workload else [W.WORKLOADS[n] for n in DEFAULT_ORDER
-                                       if n != primary.name]
+    if args.shape:
+        primary = parse_shape(W, torch, args.shape)
+    else:
+        primary = W.WORKLOADS[args.workload] if args.workload else W.HEADLINE
+    single = bool(args.workload or args.shape or args.plan or args.groups)
+    others = [] if single else [W.WORKLOADS[n] for n in DEFAULT_ORDER if n != primary.name]
 
     # the streaming ceiling (first: it also brings the GPU clock up)
     triad = triad_sweep(torch, nb, dev, stream, 512 << 20) if not args.no_triad else None
@@ -648,7 +734,7 @@ def main(argv=None) -> int:
     # the CPU oracle on the same inputs (after every GPU measurement)
     if not args.no_cpu_baseline:
         for name, e in entries.items():
-            w = W.WORKLOADS[name]
+            w = primary if name == primary.name else W.WORKLOADS[name]
             secs = args.cpu_seconds if name == primary.name else args.cpu_seconds_other
             e["cpu_oracle"] = cpu_baseline(w, cpu_inputs[name], secs, max(secs / 2, 1.0))
             print(f"bench.py: {name} cpu oracle {e['cpu_oracle']['value']} GB/s",

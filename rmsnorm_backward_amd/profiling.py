@@ -31,6 +31,7 @@ import statistics
 import sys
 
 KERNEL_A = "dx_partials_kernel"
+KERNEL_A_TWOROW = "dx_partials_tworow_kernel"
 KERNEL_B = "reduce_partials_kernel"
 FORWARD = "norm_fwd_kernel"
 COLWALK = "wgrad_colwalk_kernel"
@@ -38,6 +39,8 @@ COPY = "copy_probe_kernel"
 TRIAD = "triad_probe_kernel"
 _HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCE = os.path.join(_HERE, "csrc", "nb_device.hpp")
+# kernel A's sources: the one-row-per-wave kernel and the two-rows-per-wave one
+KERNEL_A_SOURCES = (KERNEL_SOURCE, os.path.join(_HERE, "csrc", "nb_tworow.hpp"))
 FORWARD_SOURCES = (KERNEL_SOURCE, os.path.join(_HERE, "csrc", "nb_forward.hpp"))
 
 
@@ -50,8 +53,8 @@ def _hash(paths) -> str:
 
 
 def kernel_source_hash() -> str:
-    """Hash of kernel A's source (the counters are valid while it holds)."""
-    return _hash([KERNEL_SOURCE])
+    """Hash of kernel A's sources (the counters are valid while it holds)."""
+    return _hash(KERNEL_A_SOURCES)
 
 
 def forward_source_hash() -> str:
@@ -71,8 +74,10 @@ def _bench(path):
 def is_step_kernel_a(name: str) -> bool:
     """Kernel A as the benchmark's step and roofline time it: the instantiation
     that reads the saved statistics (template argument RECOMP = false), not
-    the recompute-mode one the same run also launches."""
-    return re.search(KERNEL_A + r"<\s*\d+\s*,\s*false\s*,", name) is not None
+    the recompute-mode one the same run also launches; or the
+    two-rows-per-wave kernel, which exists for saved statistics only."""
+    return (re.search(KERNEL_A + r"<\s*\d+\s*,\s*false\s*,", name) is not None or
+            KERNEL_A_TWOROW in name)
 
 
 def stats_summary(stats_csv: str, bench_json: str, cmds) -> str:

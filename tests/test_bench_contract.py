@@ -89,3 +89,26 @@ def test_profile_summaries_pick_the_step_kernel():
         ratio = float(re.search(r"kernel A by the trace: [\d.]+ us \(events / trace = ([\d.]+)\)",
                                 text).group(1))
         assert 0.95 < ratio < 1.05, (name, ratio)
+
+
+@pytest.mark.parametrize("spec", ["rmsnorm_bf16_262144x768", "layernorm_f16_1151x8192",
+                                  "rmsnorm_f32_1000x384", "layernorm_bf16_4096x4096",
+                                  "rmsnorm_f16_100000x256", "layernorm_f32_128x512"])
+def test_shape_and_plan_options(spec):
+    """--shape builds the named shape; --plan with no edits reproduces the
+    planner's threads and LDS (so an edit changes only what it names)."""
+    import torch
+    import rmsnorm_backward_amd as nb
+    w = bench.parse_shape(W, torch, spec)
+    kind, dt, mn = spec.split("_")
+    assert (w.kind, W._dt(w.io_dtype), f"{w.M}x{w.N}") == (kind, dt, mn)
+    with_db = w.kind == "layernorm"
+    p = nb.norm_bwd_make_plan(w.kind, w.M, w.N, w.io_dtype, with_db)
+    want = (p.threads, p.lds_bytes)
+    q = bench.edit_plan(p.copy(), "", with_db)
+    assert (q.threads, q.lds_bytes) == want
+    if p.rows_per_wave == 2:
+        q = bench.edit_plan(p.copy(), "rows_in_flight=8", with_db)
+        assert q.threads == 256
+    with pytest.raises(ValueError):
+        bench.edit_plan(p.copy(), "groups=3", with_db)
