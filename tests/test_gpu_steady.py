@@ -262,3 +262,113 @@ def test_two_row_strided_rows_are_bit_identical(nb):
                          w.eps, dx=strided(torch.zeros_like(x), 768 + 24))
     torch.cuda.synchronize()
     assert torch.equal(got[0].cpu(), ref[0].cpu()) and torch.equal(got[1].cpu(), ref[1].cpu())
+
+
+# Seeded random cases aimed at the steady-state loops: few groups over many
+# rows (so the loops run), saved statistics through an explicit plan, recompute
+# mode, and norm_bwd_ex with row strides accumulating onto zeros. Widths cover
+# the exact-cover layouts (including the two-rows-per-wave ones) and some
+# ragged ones.
+_COVER_N = {torch.float32: [128, 256, 384, 512, 1024, 2048, 4096, 8192],
+            torch.float16: [256, 512, 768, 1024, 2048, 4096, 8192, 16384],
+            torch.bfloat16: [256, 512, 768, 1024, 2048, 4096, 8192, 16384]}
+
+
+def _random_steady_cases(n=120, seed=3141):
+    import random
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        kind = rng.choice(("layernorm", "rmsnorm"))
+        dt = rng.choice((torch.float32, torch.float16, torch.bfloat16))
+        N = rng.choice(_COVER_N[dt]) if rng.random() < 0.8 else rng.choice((1000, 3000, 6144))
+        G = rng.choice((1, 2, 3, 5))
+        rows = rng.randint(1, 90)
+        M = max(1, min(G * rows + rng.randint(0, G - 1), 2_000_000 // N))
+        mode = rng.choice(("saved", "saved", "recompute", "ex"))
+        pad = rng.choice((8, 64, 128))
+        out.append((i, mode, kind, dt, M, N, G, pad))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_steady_cases(),
+                         ids=lambda c: "-".join(str(v).replace("torch.", "") for v in c))
+def test_steady_random(nb, case):
+    i, mode, kind, dt, M, N, G, pad = case
+    w = workload(kind, dt, M, N)
+    with_db = kind == "layernorm"
+    print(f"[run] {mode} {w.name} groups={G}", flush=True)
+    if mode == "recompute":
+        inp = W.make_inputs(w)
+        out = nb.norm_bwd_ex(kind, inp["x"].cuda(), inp["dy"].cuda(), inp["gamma"].cuda(), None,
+                             None, w.eps, wgrad_dtype=w.wgrad_dtype, with_dbeta=with_db,
+                             groups=G)
+        torch.cuda.synchronize()
+        x, dy, gamma = inp["x"], inp["dy"], inp["gamma"]
+        dx, dg, db = (None if t is None else t.cpu() for t in out)
+        mean, rstd = oracle.fwd_stats(kind, x, w.eps)
+        rdx = oracle.bwd_dx(kind, x, dy, gamma, mean, rstd)
+        t_dx, t_dg = parity.recompute_terms(kind, x, dy, gamma, mean, rstd)
+        parity.check_dx(w.io_dtype, dx, rdx, scale=t_dx, coef32=2.0 ** -16)
+        rdg, rdb = oracle.bwd_wgrad(kind, x, dy, mean, rstd, want_dbeta=True)
+        bg, bb = parity.wgrad_bounds(kind, x, dy, mean, rstd, parity.depth_fused(M, G))
+        parity.check_wgrad(w.io_dtype, dg, rdg, extra=2.0 ** -16 * t_dg, **bg)
+        if with_db:
+            parity.check_wgrad(w.io_dtype, db, rdb, "dbeta", **bb)
+        return
+    inp = backward_inputs(w)
+    g = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor) and k != "outliers"}
+    if mode == "saved":
+        plan = nb.norm_bwd_make_plan(kind, M, N, dt, with_db, G)
+        out = nb.norm_bwd_execute(plan, g["x"], g["dy"], g["gamma"], g.get("mean"), g["rstd"],
+                                  wgrad_dtype=w.wgrad_dtype)
+    else:  # row-strided views, accumulating onto zeros
+        xs = torch.zeros(M, N + pad, dtype=dt, device="cuda")
+        ys = torch.zeros(M, N + pad, dtype=dt, device="cuda")
+        dxs = torch.zeros(M, N + pad, dtype=dt, device="cuda")
+        xs[:, :N] = g["x"]
+        ys[:, :N] = g["dy"]
+        dg0 = torch.zeros(N, dtype=w.wgrad_dtype, device="cuda")
+        db0 = torch.zeros(N, dtype=w.wgrad_dtype, device="cuda") if with_db else None
+        out = nb.norm_bwd_ex(kind, xs[:, :N], ys[:, :N], g["gamma"], g.get("mean"), g["rstd"],
+                             w.eps, dx=dxs[:, :N], dgamma=dg0, dbeta=db0, accumulate=True,
+                             groups=G)
+    torch.cuda.synchronize()
+    compare(w, inp, out, inp.get("mean"), inp["rstd"], with_db, G)
+
+
+def _random_forward_cases(n=24, seed=2718):
+    import random
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        kind = rng.choice(("layernorm", "rmsnorm"))
+        dt = rng.choice((torch.float32, torch.float16, torch.bfloat16))
+        N = rng.choice((256, 512, 768, 1024, 2048)) if dt != torch.float32 else \
+            rng.choice((256, 512, 1024))
+        M = min(rng.randint(16000, 40000), 20_000_000 // N)
+        beta = kind == "layernorm" and rng.random() < 0.5
+        out.append((i, kind, dt, M, N, beta))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_forward_cases(),
+                         ids=lambda c: "-".join(str(v).replace("torch.", "") for v in c))
+def test_forward_steady_random(nb, case):
+    """Seeded forward cases long enough for the forward's steady-state loop."""
+    i, kind, dt, M, N, with_beta = case
+    w = workload(kind, dt, M, N)
+    inp = W.make_inputs(w)
+    x, gm = inp["x"], inp["gamma"]
+    beta = torch.rand(N, generator=torch.Generator().manual_seed(i)).to(dt) if with_beta else None
+    print(f"[run] forward {w.name} beta={with_beta}", flush=True)
+    if kind == "layernorm":
+        y, mean, rstd = nb.norm_fwd_layernorm(x.cuda(), gm.cuda(),
+                                              None if beta is None else beta.cuda(), w.eps)
+    else:
+        y, rstd = nb.norm_fwd_rmsnorm(x.cuda(), gm.cuda(), w.eps)
+        mean = None
+    torch.cuda.synchronize()
+    ry, rm, rr = oracle.fwd(kind, x, gm, beta, w.eps)
+    parity.check_forward(w.io_dtype, kind, x, gm, beta, y.cpu(),
+                         None if mean is None else mean.cpu(), rstd.cpu(), ry, rm, rr)
