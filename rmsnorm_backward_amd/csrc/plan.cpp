@@ -100,7 +100,8 @@ int two_row_chunks(int64_t N, int io_dtype) {
   if (eb == 0 || N <= 0) return 0;
   const int64_t vw = 16 / eb;
   if (N % (64 * vw) == 0) return 0;  // 64-lane waves cover it without idle lanes
-  for (int c : {1, 3})
+  const int chunk_counts[] = {1, 3};
+  for (int c : chunk_counts)
     if (N == (int64_t)c * 32 * vw) return c;
   return 0;
 }
