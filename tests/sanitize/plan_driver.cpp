@@ -62,10 +62,25 @@ int main() {
                          why ? why : "");
                   if (N == 0) continue;
                   const int eb = nb::dtype_bytes(dt);
-                  EXPECT((int64_t)p.waves_per_row * 64 * p.vec * p.chunks >= N, "coverage");
-                  EXPECT(p.threads == 64 * p.waves_per_row * p.rows_in_flight, "threads");
-                  EXPECT(p.threads <= nb::kernel_a_max_threads(p.vec * p.chunks), "bound");
                   EXPECT(p.vec == 1 || (N * eb) % 16 == 0, "vector rows");
+                  if (p.rows_per_wave == 2) {
+                    // two rows per wave: 32 lanes cover the row exactly
+                    EXPECT(kind == NORM_BWD_RMSNORM && !rc && p.vec == 16 / eb,
+                           "two-row layout for RMSNorm with saved statistics");
+                    EXPECT((int64_t)32 * p.vec * p.chunks == N &&
+                               (p.chunks == 1 || p.chunks == 3),
+                           "two-row coverage");
+                    EXPECT(p.waves_per_row == 1 && p.rows_in_flight % 2 == 0 &&
+                               p.threads == 32 * p.rows_in_flight && p.threads <= 512,
+                           "two-row threads");
+                    if (M > 0)
+                      EXPECT(nb::two_row_span_ok(p.groups, N, N, dt), "two-row span");
+                  } else {
+                    EXPECT(p.rows_per_wave == 1, "rows_per_wave");
+                    EXPECT((int64_t)p.waves_per_row * 64 * p.vec * p.chunks >= N, "coverage");
+                    EXPECT(p.threads == 64 * p.waves_per_row * p.rows_in_flight, "threads");
+                    EXPECT(p.threads <= nb::kernel_a_max_threads(p.vec * p.chunks), "bound");
+                  }
                   if (M > 0) {
                     EXPECT(p.groups >= 1 && p.groups <= M, "groups in [1, M]");
                     EXPECT(p.rows_per_group * p.groups >= M, "groups cover M");
@@ -113,6 +128,8 @@ int main() {
       {"lds", [](norm_bwd_plan_t& p) { p.lds_bytes += 4; }},
       {"kind", [](norm_bwd_plan_t& p) { p.kind = 5; }},
       {"with_dbeta", [](norm_bwd_plan_t& p) { p.with_dbeta = 2; }},
+      {"rows_per_wave 3", [](norm_bwd_plan_t& p) { p.rows_per_wave = 3; }},
+      {"rows_per_wave 2, N not covered", [](norm_bwd_plan_t& p) { p.rows_per_wave = 2; }},
   };
   for (const Edit& e : edits) {
     norm_bwd_plan_t p = good;
