@@ -153,12 +153,20 @@ def edit_plan(plan, spec: str, with_db: bool):
         setattr(plan, k, int(v))
     nacc = 2 if with_db else 1
     S, C, P, vec = plan.waves_per_row, plan.chunks, plan.rows_in_flight, plan.vec
+    M = plan.M
     if plan.rows_per_wave == 2:
         plan.threads = 32 * P
         plan.lds_bytes = nacc * C * 32 * vec * 4 if P > 2 else 0
+        # groups of adjacent row pairs
+        pairs = -(-M // 2)
+        plan.groups = min(plan.groups, pairs)
+        plan.rows_per_group = 2 * -(-pairs // plan.groups) if plan.groups else 0
     else:
         plan.threads = 64 * S * P
         plan.lds_bytes = nacc * S * C * 64 * vec * 4 if P > 1 else 0
+        plan.rows_per_group = -(-M // plan.groups) if plan.groups else 1
+    plan.grid = min(plan.groups, 1 << 20)
+    plan.workspace_bytes = nacc * plan.groups * plan.N * 4
     return plan
 
 
@@ -349,19 +357,26 @@ def triad_sweep(torch, nb, dev, stream, operand_bytes):
 SAME_SIZE_SHAPES = ((0, 1), (0, 2), (0, 4), (256, 4), (512, 4), (1024, 2), (1024, 4), (2048, 2))
 
 
-def triad_same_size(torch, nb, dev, stream, operand_bytes, steps):
+def triad_same_size(torch, nb, lib, dev, stream, operand_bytes, steps):
     """The triad over three operands of one workload's x (dy, dx) size, on
     enough rotating buffer sets to stream from HBM like kernel A: the
-    achievable rate for that many bytes per launch, fixed costs included."""
+    achievable rate for that many bytes per launch, fixed costs included.
+    Launched through the C entry point with prepared arguments, as kernel A
+    is timed."""
     n = max(4, operand_bytes // 16 * 4)
     nsets = max(2, min(64, math.ceil(4 * MALL_BYTES / (3 * n * 4))))
     sets = [[torch.empty(n, dtype=torch.int32, device=dev).fill_(k) for k in (1, 2, 0)]
             for _ in range(nsets)]
+    P = ctypes.c_void_p
+    sh = P(stream.cuda_stream)
+    ptrs = [[P(t.data_ptr()) for t in s] for s in sets]
+    nbytes = n * 4
     best = (0.0, None)
     for grid, unroll in SAME_SIZE_SHAPES:
         def go(i):
-            a, b, c = sets[i % nsets]
-            nb.norm_bwd_probe_triad(a, b, c, grid, unroll)
+            a, b, c = ptrs[i % nsets]
+            if lib.norm_bwd_probe_triad(a, b, c, nbytes, grid, unroll, sh):
+                raise RuntimeError(nb.norm_bwd_last_error())
         for i in range(5):
             go(i)
         ms = time_loop(torch, go, steps, stream)
@@ -501,7 +516,8 @@ def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, ext
     if triad:
         entry["pct_of_triad"] = round(100 * value / triad["GBps"], 2)
         entry["kernel_a_pct_of_triad"] = round(100 * achieved / triad["GBps"], 2)
-        same = triad_same_size(torch, nb, dev, stream, w.M * w.N * w.io_bytes, max(steps, 50))
+        same = triad_same_size(torch, nb, lib, dev, stream, w.M * w.N * w.io_bytes,
+                               max(steps, 50))
         entry["triad_same_bytes"] = same
         entry["kernel_a_pct_of_triad_same_bytes"] = round(100 * achieved / same["GBps"], 2)
     plan_d = {k: v for k, v in plan.as_dict().items()

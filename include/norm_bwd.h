@@ -282,9 +282,11 @@ int norm_bwd_wgrad(int kind, const void *x, const void *dy, const float *mean,
  * Two lane layouts. rows_per_wave = 1: a row is split over waves_per_row
  * waves of 64 lanes, each lane holding chunks vectors of vec elements.
  * rows_per_wave = 2 (16-byte vectors only, waves_per_row = 1, chunks 1 or
- * 3, N = 32 * vec * chunks exactly): each 32-lane half of a wave holds a row
- * of its own; threads = 32 * rows_in_flight (at most 512), and a row pair's
- * byte span (groups * N + N elements) must stay below 2^32.
+ * 3, N = 32 * vec * chunks exactly): rows go in adjacent pairs (2q, 2q + 1),
+ * group g is the pairs with q mod groups == g (groups at most ceil(M / 2),
+ * rows_per_group = 2 * ceil(ceil(M / 2) / groups)), and each 32-lane half of
+ * a wave holds one row of a pair; threads = 32 * rows_in_flight (at most
+ * 512).
  */
 typedef struct norm_bwd_plan {
     int32_t kind;            /* NORM_BWD_LAYERNORM / RMSNORM */
@@ -292,7 +294,8 @@ typedef struct norm_bwd_plan {
     int32_t with_dbeta;      /* 1: kernel A also sums dy for dbeta */
     int32_t vec;             /* elements per lane per load (16 bytes, or 1) */
     int64_t M, N;            /* problem size */
-    int64_t groups;          /* G: row groups = workspace rows; group g = rows r, r mod G == g */
+    int64_t groups;          /* G: row groups = workspace rows; group g = rows r, r mod G == g
+                                (two rows per wave: row pairs q, q mod G == g) */
     int64_t rows_per_group;  /* ceil(M / G): the most rows any group holds */
     int32_t chunks;          /* C: loads of `vec` elements per lane per row slice */
     int32_t waves_per_row;   /* S: 64-lane waves sharing one row */

@@ -8,17 +8,20 @@
 //
 // What is computed is kernel A's (nb_device.hpp), from the same formulas of
 // "Norm backward in Triton -- the dγ/dβ reduction", "The gradients": dx per
-// row, and per row group g (the rows r with r mod G == g) the group's partial
-// dgamma (and dbeta) in fp32 registers, stored once into the workspace.
+// row, and per row group g (below) the group's partial dgamma (and dbeta) in
+// fp32 registers, stored once into the workspace.
 //
-// Layout. Lane l of wave w is in half h = l / 32 and covers the columns
+// Layout. Rows go in pairs (2q, 2q + 1), and row group g is the pairs with
+// q mod G == g (disjoint groups, as kernel A's, with pairs in place of rows).
+// Lane l of wave w is in half h = l / 32 and covers the columns
 // (l mod 32) * VEC + c * 32 * VEC, c < C, of its row. With P waves per
-// workgroup, iteration k of group g gives half h of wave w the group's row
-// j = 2 * (k * P + w) + h, i.e. row r = g + j * G. A half's row sums are
-// complete after a 32-lane butterfly (no exchange between waves, no
-// barrier). Each half accumulates its rows in ascending order; at the end of
-// the group the two halves are added (half 0 + half 1), then the P waves in
-// wave order through LDS. The summation order depends on (M, G, P) only.
+// workgroup, iteration k of group g gives wave w the group's pair
+// q = g + (k * P + w) * G and its half h row 2q + h: the two halves of a load
+// instruction read adjacent rows. A half's row sums are complete after a
+// 32-lane butterfly (no exchange between waves, no barrier). Each half
+// accumulates its rows in ascending order; at the end of the group the two
+// halves are added (half 0 + half 1), then the P waves in wave order through
+// LDS. The summation order depends on (M, G, P) only.
 #pragma once
 
 #include "nb_device.hpp"
@@ -47,8 +50,8 @@ constexpr int kTwoRowMaxThreads = 512;  // launch bound: 256 VGPRs per lane
 
 // Loads of one row pair. RALL (steady state): both rows exist; the wave
 // addresses them through one buffer resource based at its first row, the
-// second half adding `hoff` bytes (G rows further). Otherwise each lane
-// loads through its own address, and only when its row exists.
+// second half adding `hoff` bytes (one row stride). Otherwise each lane loads
+// through its own address, and only when its row exists.
 template <int KIND, bool RALL, class Tg, int VEC, int C>
 __device__ __forceinline__ void fetch_pair(RowBuf<Tg, VEC, C>& b, const char* __restrict__ x,
                                            const char* __restrict__ dy,
@@ -141,8 +144,8 @@ __device__ __forceinline__ void process_pair(RowBuf<Tg, VEC, C>& b, const float 
 }
 
 // P = waves per workgroup (2 * P rows in flight). span_* = bytes from a row
-// pair's first row to the end of its second row (G * ld + N elements), which
-// the host checked to be below 2^32.
+// pair's first row to the end of its second row (ld + N elements), which the
+// host checked to be below 2^32.
 template <int KIND, class Tg, int C, int NACC, bool WSNT>
 __global__ __launch_bounds__(kTwoRowMaxThreads)
 void dx_partials_tworow_kernel(const void* __restrict__ xv, const void* __restrict__ dyv,
@@ -168,13 +171,13 @@ void dx_partials_tworow_kernel(const void* __restrict__ xv, const void* __restri
   const int col0 = (lane & 31) * VEC;
   constexpr int cstride = 32 * VEC;
   const float inv_n = 1.0f / (float)N;
-  // the second half's row is G rows after the first half's
-  const uint32_t hoff_x = (uint32_t)(h * G * ldx * EB);
-  const uint32_t hoff_y = (uint32_t)(h * G * ldy * EB);
-  const uint32_t hoff_o = (uint32_t)(h * G * ldo * EB);
-  const uint32_t span_x = (uint32_t)((G * ldx + N) * EB);
-  const uint32_t span_y = (uint32_t)((G * ldy + N) * EB);
-  const uint32_t span_o = (uint32_t)((G * ldo + N) * EB);
+  // the second half's row is the next row
+  const uint32_t hoff_x = (uint32_t)(h * ldx * EB);
+  const uint32_t hoff_y = (uint32_t)(h * ldy * EB);
+  const uint32_t hoff_o = (uint32_t)(h * ldo * EB);
+  const uint32_t span_x = (uint32_t)((ldx + N) * EB);
+  const uint32_t span_y = (uint32_t)((ldy + N) * EB);
+  const uint32_t span_o = (uint32_t)((ldo + N) * EB);
 
   float gam[C][VEC];
 #pragma unroll
@@ -186,12 +189,14 @@ void dx_partials_tworow_kernel(const void* __restrict__ xv, const void* __restri
   }
 
   for (int64_t g = blockIdx.x; g < G; g += gridDim.x) {
-    const int64_t rows = (M - g + G - 1) / G;  // rows of group g
-    const int iters = (int)((rows + 2 * P - 1) / (2 * P));
-    // first row of wave w's pair in iteration k (uniform), and this lane's row
-    auto pair0 = [&](int k) { return g + (int64_t)(2 * (k * P + w)) * G; };
-    auto row_of = [&](int k) { return pair0(k) + h * G; };
-    auto exists = [&](int k) { return (int64_t)(2 * (k * P + w) + h) < rows; };
+    // group g = the row pairs (2q, 2q + 1) with q mod G == g
+    const int64_t npairs = ((M + 1) / 2 - g + G - 1) / G;     // pairs of group g
+    const int64_t nfull = (M / 2 > g) ? (M / 2 - g + G - 1) / G : 0;  // complete pairs
+    const int64_t rows = 2 * nfull;  // (for the steady-state byte rule)
+    const int iters = (int)((npairs + P - 1) / P);
+    auto pair0 = [&](int k) { return 2 * (g + (int64_t)(k * P + w) * G); };
+    auto row_of = [&](int k) { return pair0(k) + h; };
+    auto exists = [&](int k) { return row_of(k) < M; };
 
     float acc[NACC][C][VEC];
 #pragma unroll
@@ -205,7 +210,7 @@ void dx_partials_tworow_kernel(const void* __restrict__ xv, const void* __restri
     // Steady state (as kernel A's): iterations in which all 2P rows exist run
     // through a loop with no per-lane or per-row conditions; the general loop
     // takes the remaining iterations from the same ring state.
-    const int kfull = (int)(rows / (2 * P));
+    const int kfull = (int)(nfull / P);
     int it0 = 0;
     const bool steady =
         kfull >= 2 * D - 1 && rows * (int64_t)N * EB <= kSteadyGroupBytes;

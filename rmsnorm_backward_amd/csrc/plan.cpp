@@ -106,11 +106,15 @@ int two_row_chunks(int64_t N, int io_dtype) {
   return 0;
 }
 
-bool two_row_span_ok(int64_t G, int64_t N, int64_t ld, int io_dtype) {
+bool two_row_span_ok(int64_t N, int64_t ld, int io_dtype) {
   const int eb = dtype_bytes(io_dtype);
   if (ld < N) ld = N;
-  if (G < 0 || eb == 0 || G > ((int64_t)1 << 32) / (ld > 0 ? ld : 1)) return false;
-  return (G * ld + N) * eb < ((int64_t)1 << 32);
+  if (eb == 0 || ld > ((int64_t)1 << 32)) return false;
+  return (ld + N) * eb < ((int64_t)1 << 32);
+}
+
+int64_t two_row_rows_per_group(int64_t M, int64_t G) {
+  return G > 0 ? 2 * ceil_div(ceil_div(M, 2), G) : 0;
 }
 
 // Lane layout of kernel A for rows of N elements (fills vec, chunks,
@@ -299,15 +303,17 @@ int make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,
   }
 
   if (M > 0) {
-    int64_t G = groups ? groups : auto_groups(kind, M, N, io_dtype, recompute);
-    if (G > M) G = M;  // every group holds at least one row
-    p.groups = G;
-    p.rows_per_group = ceil_div(M, G);
-    p.grid = (int32_t)(G < kMaxGrid ? G : kMaxGrid);
-    // a row pair too far apart for 32-bit offsets keeps one row per wave
-    if (p.rows_per_wave == 2 && !two_row_span_ok(G, N, max_ld ? max_ld : N, io_dtype))
+    // a row pair whose stride needs offsets beyond 32 bits keeps one row per wave
+    if (p.rows_per_wave == 2 && !two_row_span_ok(N, max_ld ? max_ld : N, io_dtype))
       make_geometry(kind, N, io_dtype, with_dbeta, vec_ok16, &p, &gwhy,
                     recompute && kind == NORM_BWD_LAYERNORM, false);
+    int64_t G = groups ? groups : auto_groups(kind, M, N, io_dtype, recompute);
+    // every group holds at least one row (two-row plans: one row pair)
+    const int64_t units = p.rows_per_wave == 2 ? ceil_div(M, 2) : M;
+    if (G > units) G = units;
+    p.groups = G;
+    p.rows_per_group = p.rows_per_wave == 2 ? two_row_rows_per_group(M, G) : ceil_div(M, G);
+    p.grid = (int32_t)(G < kMaxGrid ? G : kMaxGrid);
   } else {
     p.rows_per_group = 1;
     p.groups = 0;
@@ -342,14 +348,16 @@ static int validate_two_row(const norm_bwd_plan_t* p, const char** why) {
     if (p->groups != 0) return fail(why, "plan.groups must be 0 when M = 0", NORM_BWD_ERR_INVALID_ARG);
     return NORM_BWD_OK;
   }
-  if (p->groups < 1 || p->groups > p->M)
-    return fail(why, "plan.groups must be in [1, M]", NORM_BWD_ERR_INVALID_ARG);
-  if (p->rows_per_group != ceil_div(p->M, p->groups))
-    return fail(why, "plan.rows_per_group must be ceil(M / groups)", NORM_BWD_ERR_INVALID_ARG);
+  if (p->groups < 1 || p->groups > ceil_div(p->M, 2))
+    return fail(why, "plan.groups must be in [1, ceil(M / 2)] with rows_per_wave = 2",
+                NORM_BWD_ERR_INVALID_ARG);
+  if (p->rows_per_group != two_row_rows_per_group(p->M, p->groups))
+    return fail(why, "plan.rows_per_group must be 2 * ceil(ceil(M / 2) / groups)",
+                NORM_BWD_ERR_INVALID_ARG);
   if (p->grid < 1 || p->grid > p->groups || p->grid > kMaxGrid)
     return fail(why, "plan.grid must be in [1, groups]", NORM_BWD_ERR_INVALID_ARG);
-  if (!two_row_span_ok(p->groups, p->N, p->N, p->io_dtype))
-    return fail(why, "plan.rows_per_wave = 2: groups * N too large for 32-bit offsets",
+  if (!two_row_span_ok(p->N, p->N, p->io_dtype))
+    return fail(why, "plan.rows_per_wave = 2: a row pair too long for 32-bit offsets",
                 NORM_BWD_ERR_INVALID_ARG);
   return NORM_BWD_OK;
 }

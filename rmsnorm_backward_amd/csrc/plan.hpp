@@ -37,9 +37,13 @@ int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok
 // not, else 0.
 int two_row_chunks(int64_t N, int io_dtype);
 
-// Whether a row pair of the two-row layout, G rows apart with row stride ld
-// (elements), spans fewer than 2^32 bytes (its 32-bit buffer offsets).
-bool two_row_span_ok(int64_t G, int64_t N, int64_t ld, int io_dtype);
+// Whether a row pair of the two-row layout (adjacent rows, row stride ld
+// elements) spans fewer than 2^32 bytes (its 32-bit buffer offsets).
+bool two_row_span_ok(int64_t N, int64_t ld, int io_dtype);
+
+// The most rows a group of the two-row layout holds: groups are sets of row
+// pairs, so 2 * ceil(ceil(M / 2) / G).
+int64_t two_row_rows_per_group(int64_t M, int64_t G);
 
 // Whether the fused kernels (rows held in registers) cover rows of N elements
 // of io_dtype; wider rows take the row-loop path.

@@ -73,8 +73,12 @@ int main() {
                     EXPECT(p.waves_per_row == 1 && p.rows_in_flight % 2 == 0 &&
                                p.threads == 32 * p.rows_in_flight && p.threads <= 512,
                            "two-row threads");
-                    if (M > 0)
-                      EXPECT(nb::two_row_span_ok(p.groups, N, N, dt), "two-row span");
+                    if (M > 0) {
+                      EXPECT(nb::two_row_span_ok(N, N, dt), "two-row span");
+                      EXPECT(p.groups >= 1 && 2 * p.groups <= M + 1, "groups of row pairs");
+                      EXPECT(p.rows_per_group == nb::two_row_rows_per_group(M, p.groups),
+                             "rows per group of row pairs");
+                    }
                   } else {
                     EXPECT(p.rows_per_wave == 1, "rows_per_wave");
                     EXPECT((int64_t)p.waves_per_row * 64 * p.vec * p.chunks >= N, "coverage");
@@ -84,13 +88,15 @@ int main() {
                   if (M > 0) {
                     EXPECT(p.groups >= 1 && p.groups <= M, "groups in [1, M]");
                     EXPECT(p.rows_per_group * p.groups >= M, "groups cover M");
+                    EXPECT(p.rows_per_wave == 2 || p.rows_per_group == (M + p.groups - 1) / p.groups,
+                           "rows per group");
                     EXPECT(p.grid >= 1 && p.grid <= p.groups, "grid");
                     EXPECT(p.workspace_bytes ==
                                (size_t)(db ? 2 : 1) * (size_t)p.groups * (size_t)N * 4u,
                            "workspace");
                     if (G == 0)  // automatic groups never depend on the device
                       EXPECT(p.groups == nb::auto_groups(kind, M, N, dt, rc != 0) ||
-                                 p.groups == M,
+                                 p.groups == M || p.groups == (M + 1) / 2,
                              "automatic groups");
                   }
                 }

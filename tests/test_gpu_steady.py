@@ -217,6 +217,8 @@ def test_two_row_kernel(nb, kind, dt, N, G, M):
         ref = nb.norm_bwd_make_plan("rmsnorm", M, N, dt, with_db, G)
         plan.rows_per_wave, plan.chunks, plan.waves_per_row = 2, ref.chunks, 1
         plan.rows_in_flight, plan.threads = ref.rows_in_flight, ref.threads
+        plan.groups, plan.rows_per_group, plan.grid = ref.groups, ref.rows_per_group, ref.grid
+        plan.workspace_bytes = (2 if with_db else 1) * ref.groups * N * 4
         plan.lds_bytes = (2 if with_db else 1) * ref.chunks * 32 * ref.vec * 4 \
             if ref.rows_in_flight > 2 else 0
     assert plan.rows_per_wave == 2 and plan.waves_per_row == 1
@@ -237,6 +239,8 @@ def test_two_row_rows_in_flight(nb, P):
     plan = nb.norm_bwd_make_plan("layernorm", w.M, w.N, w.io_dtype, True, 3)
     plan.rows_per_wave, plan.chunks, plan.waves_per_row = 2, 3, 1
     plan.rows_in_flight, plan.threads = P, 32 * P
+    pairs = -(-w.M // 2)                   # groups of adjacent row pairs
+    plan.rows_per_group = 2 * -(-pairs // 3)
     plan.lds_bytes = 2 * plan.chunks * 32 * plan.vec * 4 if P > 2 else 0
     g = {k: v.cuda() for k, v in inp.items() if isinstance(v, torch.Tensor) and k != "outliers"}
     out = nb.norm_bwd_execute(plan, g["x"], g["dy"], g["gamma"], g["mean"], g["rstd"])

@@ -194,7 +194,11 @@ def test_plan_invariants(nb, kind, dt, M, N, db, groups):
             want *= 2
         assert P == want and p.threads == 32 * P
         assert p.lds_bytes == (nacc * C * 32 * vec * 4 if P > 2 else 0)
-        assert 1 <= p.groups <= M and p.rows_per_group == -(-M // p.groups)
+        # groups of adjacent row pairs: never an empty one
+        pairs = -(-M // 2)
+        assert 1 <= p.groups <= pairs and p.rows_per_group == 2 * -(-pairs // p.groups)
+        if groups:
+            assert p.groups == min(groups, pairs)
         assert p.workspace_bytes == nacc * p.groups * N * 4
         return
     assert p.rows_per_wave == 1
@@ -225,23 +229,27 @@ def test_plan_invariants(nb, kind, dt, M, N, db, groups):
     assert p.lds_bytes <= 65536
 
 
-def test_two_row_layout_needs_32_bit_pair_offsets(nb):
-    """The two-row layout addresses a row pair (G rows apart) with 32-bit
-    offsets; plans whose pair would span 2^32 bytes keep one row per wave,
-    and a two-row plan edited to such a group count is refused."""
-    p = nb.norm_bwd_make_plan("rmsnorm", 1 << 23, 768, torch.bfloat16, False, 1 << 21)
-    assert p.rows_per_wave == 2            # (2^21 + 1) * 768 * 2 < 2^32
+def test_two_row_plans_group_row_pairs(nb):
+    """Two-row plans group adjacent row pairs: groups are clamped to the pair
+    count, rows_per_group counts whole pairs, any group count keeps the layout
+    (a pair spans one row stride), and an edited plan that breaks these rules
+    is refused."""
     p = nb.norm_bwd_make_plan("rmsnorm", 1 << 23, 768, torch.bfloat16, False, 3 << 20)
-    assert p.rows_per_wave == 1            # (3 * 2^20 + 1) * 768 * 2 >= 2^32
-    p = nb.norm_bwd_make_plan("rmsnorm", 1 << 23, 768, torch.bfloat16, False, 1 << 21)
-    p.groups = 3 << 20
-    p.rows_per_group = -(-p.M // p.groups)
-    p.grid = 1 << 20
-    p.workspace_bytes = p.groups * 768 * 4
+    assert p.rows_per_wave == 2 and p.groups == 3 << 20
+    p = nb.norm_bwd_make_plan("rmsnorm", 7, 768, torch.bfloat16, False, 100)
+    assert p.rows_per_wave == 2 and p.groups == 4 and p.rows_per_group == 2
+    p = nb.norm_bwd_make_plan("rmsnorm", 1001, 768, torch.bfloat16, False, 10)
+    assert p.rows_per_group == 2 * 51
     lib = nb.load_library()
-    st = lib.norm_bwd_execute(ctypes.byref(p), _addr(0), _addr(1), _addr(2), None, _addr(3), 0,
-                              _addr(4), _addr(5), None, _addr(6), p.workspace_bytes, None)
-    assert st == 1 and "32-bit" in nb.norm_bwd_last_error()
+    for field, value in (("groups", 5), ("rows_per_group", 1)):
+        q = nb.norm_bwd_make_plan("rmsnorm", 7, 768, torch.bfloat16, False, 100)
+        setattr(q, field, value)
+        if field == "groups":
+            q.workspace_bytes = 5 * 768 * 4
+        st = lib.norm_bwd_execute(ctypes.byref(q), _addr(0), _addr(1), _addr(2), None,
+                                  _addr(3), 0, _addr(4), _addr(5), None, _addr(6),
+                                  q.workspace_bytes, None)
+        assert st == 1, field
 
 
 def test_groups_do_not_depend_on_device(nb):
