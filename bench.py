@@ -163,7 +163,7 @@ def edit_plan(plan, spec: str, with_db: bool):
         plan.rows_per_group = 2 * -(-pairs // plan.groups) if plan.groups else 0
     else:
         plan.threads = 64 * S * P
-        plan.lds_bytes = nacc * S * C * 64 * vec * 4 if P > 1 else 0
+        plan.lds_bytes = S * C * 64 * vec * 4 if P > 1 else 0
         plan.rows_per_group = -(-M // plan.groups) if plan.groups else 1
     plan.grid = min(plan.groups, 1 << 20)
     plan.workspace_bytes = nacc * plan.groups * plan.N * 4

@@ -302,7 +302,8 @@ typedef struct norm_bwd_plan {
     int32_t rows_in_flight;  /* P: rows a workgroup processes at once */
     int32_t threads;         /* 64 * S * P, kernel A's workgroup size */
     int32_t grid;            /* kernel A workgroups (groups are strided over them) */
-    int32_t lds_bytes;       /* kernel A dynamic LDS */
+    int32_t lds_bytes;       /* kernel A dynamic LDS: S * C * 64 * vec * 4 when P > 1
+                                (one row per wave), else 0 */
     int32_t rows_per_wave;   /* 1, or 2: each 32-lane half of a wave takes a row */
     size_t workspace_bytes;  /* with_dbeta ? 2 : 1, times groups * N * 4 */
 } norm_bwd_plan_t;
@@ -317,7 +318,9 @@ typedef struct norm_bwd_plan {
  * that many row groups, clamped to M so that no group is empty. The lane
  * layout takes at most 32 bytes of each operand per lane, then the fewest
  * waves per row; the rows in flight per workgroup are the fewest whose x and
- * dy reach 16 KiB. RMSNorm rows that 64-lane waves would cover with idle
+ * dy reach 16 KiB, and at least two where a group holds more than 2 MiB of
+ * each operand (rows_per_group * N * element size), as far as 16 waves, the
+ * kernel's launch bound and 63 KiB of LDS allow. RMSNorm rows that 64-lane waves would cover with idle
  * lanes and 32 lanes cover exactly (N = 32 * vec * 1 or 3: 256 or 768 16-bit,
  * 128 or 384 fp32 elements) take two rows per wave instead, with the fewest
  * rows in flight whose x and dy reach 8 KiB. A plan is

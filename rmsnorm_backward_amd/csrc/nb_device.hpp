@@ -699,7 +699,9 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
     // Groups that sweep more than kSteadyGroupBytes of each operand keep the
     // general loop: there the steady-state loop lost 1.3-2% (65536 x 8192
     // bf16 LayerNorm, 4 MiB per group), while at 2 MiB it was even
-    // (32768 x 8192) and up to 1 MiB it gained 2.5-5%.
+    // (32768 x 8192) and up to 1 MiB it gained 2.5-5%. The planner gives
+    // such groups two rows in flight (the planner's copy of this bound must
+    // stay equal to it).
     const bool steady = steady_loop<RECOMP, Tg, VEC, C, NACC, MAXT>() && N == C * cstride &&
                         kfull >= 2 * D - 1 && rows * (int64_t)N * EB <= kSteadyGroupBytes;
     if (steady) {
@@ -822,29 +824,32 @@ void dx_partials_kernel(const void* __restrict__ xv, const void* __restrict__ dy
       }
     }
 
-    // Combine the P row-lanes' partials in the fixed order 0, 1, ..., P-1.
+    // Combine the P row-lanes' partials in the fixed order 0, 1, ..., P-1,
+    // one accumulator (dgamma, then dbeta) at a time through one plane of
+    // S * C * 64 * VEC floats: half the LDS of exchanging both at once, so
+    // LayerNorm rows of 8192 bf16 with both gradients (8 waves a row) can run
+    // two rows in flight within 64 KiB.
     if (P > 1) {
-      for (int q = 1; q < P; ++q) {
-        if (p == q) {
 #pragma unroll
-          for (int a = 0; a < NACC; ++a)
-#pragma unroll
-            for (int c = 0; c < C; ++c)
-#pragma unroll
-              for (int v = 0; v < VEC; ++v)
-                comb[(((a * C + c) * S + s) * 64 + lane) * VEC + v] = acc[a][c][v];
-        }
-        __syncthreads();
-        if (p == 0) {
-#pragma unroll
-          for (int a = 0; a < NACC; ++a)
+      for (int a = 0; a < NACC; ++a) {
+        for (int q = 1; q < P; ++q) {
+          if (p == q) {
 #pragma unroll
             for (int c = 0; c < C; ++c)
 #pragma unroll
               for (int v = 0; v < VEC; ++v)
-                acc[a][c][v] += comb[(((a * C + c) * S + s) * 64 + lane) * VEC + v];
+                comb[((c * S + s) * 64 + lane) * VEC + v] = acc[a][c][v];
+          }
+          __syncthreads();
+          if (p == 0) {
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+              for (int v = 0; v < VEC; ++v)
+                acc[a][c][v] += comb[((c * S + s) * 64 + lane) * VEC + v];
+          }
+          __syncthreads();
         }
-        __syncthreads();
       }
     }
     if (p == 0) {

@@ -21,6 +21,16 @@ constexpr int64_t kSavedStatsGroups = 256;
 // 262144 x 768 218.5 us at 8, 229.6 us at 4; 16384 x 4096 69.2 us at 1,
 // 69.9 us at 2).
 constexpr int64_t kRowBytesInFlight = 16384;
+// Groups that sweep more than this many bytes of each operand run kernel A's
+// general loop rather than its steady-state loop (the kernel holds the same
+// bound). There one row in flight leaves HBM idle between rows, and two rows
+// in flight were faster on every shape measured (bf16, saved statistics):
+// 131072 x 4096 LayerNorm 643 -> 528 us, RMSNorm 580 -> 527 us; 65536 x 8192
+// LayerNorm 527 -> 520 us, RMSNorm 527 -> 522 us; 262144 x 4096 RMSNorm
+// 1168 -> 1154 us; 65536 x 4096 fp32 even. Inside the bound the steady-state
+// loop with one row was faster (65536 x 4096 RMSNorm 268 us against 272 us,
+// 32768 x 8192 LayerNorm 264 against 270 us).
+constexpr int64_t kSteadyGroupBytes = (int64_t)2 << 20;
 // LayerNorm in recompute mode exchanges twice per row; a second workgroup per
 // compute unit hides that latency (65536 x 8192 bf16: 570 us at 512 groups
 // against 645 us at 256), so it aims at 4096 waves in flight.
@@ -117,6 +127,10 @@ int64_t two_row_rows_per_group(int64_t M, int64_t G) {
   return G > 0 ? 2 * ceil_div(ceil_div(M, 2), G) : 0;
 }
 
+// LDS of kernel A's combine of P > 1 row-lanes: one plane of per-lane
+// partials (S waves, C chunks of vec floats), reused for dgamma and dbeta.
+static int combine_lds_bytes(int S, int C, int vec) { return S * C * 64 * vec * 4; }
+
 // Lane layout of kernel A for rows of N elements (fills vec, chunks,
 // waves_per_row, rows_in_flight, threads, lds_bytes of *p).
 int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok16,
@@ -168,7 +182,7 @@ int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok
     while (P > 1 && S * P > 16) P /= 2;
   }
   while (P > 1 && S * P * 64 > kernel_a_max_threads(p->vec * C)) P /= 2;
-  int lds = nacc * S * C * 64 * p->vec * 4;
+  int lds = combine_lds_bytes(S, C, p->vec);
   if (P == 1 || lds > kMaxLdsBytes) { P = 1; lds = 0; }
   p->chunks = C;
   p->waves_per_row = S;
@@ -314,6 +328,18 @@ int make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,
     p.groups = G;
     p.rows_per_group = p.rows_per_wave == 2 ? two_row_rows_per_group(M, G) : ceil_div(M, G);
     p.grid = (int32_t)(G < kMaxGrid ? G : kMaxGrid);
+    // groups on the general loop: two rows in flight (the rows-in-flight
+    // rules of saved statistics, which RMSNorm recompute shares)
+    const int S = p.waves_per_row, C = p.chunks;
+    if (!(recompute && kind == NORM_BWD_LAYERNORM) && p.rows_per_wave == 1 &&
+        p.rows_in_flight == 1 &&
+        p.rows_per_group * N * dtype_bytes(io_dtype) > kSteadyGroupBytes && 2 * S <= 16 &&
+        2 * S * 64 <= kernel_a_max_threads(p.vec * C) &&
+        combine_lds_bytes(S, C, p.vec) <= kMaxLdsBytes) {
+      p.rows_in_flight = 2;
+      p.threads = 2 * S * 64;
+      p.lds_bytes = combine_lds_bytes(S, C, p.vec);
+    }
   } else {
     p.rows_per_group = 1;
     p.groups = 0;
@@ -395,7 +421,7 @@ int validate_plan(const norm_bwd_plan_t* p, const char** why) {
     return fail(why, "plan.threads above the kernel's launch bound", NORM_BWD_ERR_INVALID_ARG);
   if ((int64_t)S * 64 * p->vec * p->chunks < p->N)
     return fail(why, "plan geometry does not cover N", NORM_BWD_ERR_INVALID_ARG);
-  const int want_lds = P > 1 ? nacc * S * p->chunks * 64 * p->vec * 4 : 0;
+  const int want_lds = P > 1 ? combine_lds_bytes(S, p->chunks, p->vec) : 0;
   if (p->lds_bytes != want_lds || want_lds > kMaxLdsBytes)
     return fail(why, "plan.lds_bytes inconsistent (or above 63 KiB)", NORM_BWD_ERR_INVALID_ARG);
   if (p->M == 0) {

@@ -162,6 +162,27 @@ def test_explicit_groups(nb, groups):
     compare_full(w, inp, out, True, groups=groups)
 
 
+@pytest.mark.parametrize("kind,dt,M,N,groups", [
+    ("layernorm", torch.bfloat16, 777, 8192, 2),     # both gradients, 8 waves a row
+    ("rmsnorm", torch.bfloat16, 2003, 4096, 3),      # ragged last group
+    ("layernorm", torch.float16, 600, 4096, 1),
+    ("rmsnorm", torch.float32, 515, 2048, 1),
+])
+def test_general_loop_two_rows_in_flight(nb, kind, dt, M, N, groups):
+    """Groups that sweep more than 2 MiB of each operand run kernel A's general
+    loop with two rows in flight, combined one accumulator at a time."""
+    base = W.LN_BF16_65536x8192 if kind == "layernorm" else W.RMS_BF16_16384x4096
+    w = W.scaled(base, M=M, N=N, io_dtype=dt)
+    with_db = kind == "layernorm"
+    p = nb.norm_bwd_make_plan(kind, M, N, dt, with_db, groups)
+    eb = torch.tensor([], dtype=dt).element_size()
+    # one row in flight by the row-size rule; two for the group size
+    assert p.rows_in_flight == 2 and 2 * N * eb >= 16384 and p.rows_per_group * N * eb > 2 << 20
+    inp = backward_inputs(w)
+    out = run(nb, w, to_gpu(inp), plan=p)
+    compare_full(w, inp, out, with_db, groups=groups)
+
+
 @pytest.mark.parametrize("kind", ["layernorm", "rmsnorm"])
 @pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16])
 def test_wgrad_in_io_dtype(nb, kind, dt):

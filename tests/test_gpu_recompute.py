@@ -146,22 +146,23 @@ def recompute_plan(nb, kind, M, N, dt, db):
     combine buffer would not fit in LDS), with its own group count (about
     4096 waves in flight, counted on the dbeta-less layout; at least 4 rows
     per group; above 256 a multiple of 256)."""
-    def rows(S, C, vec, nacc):
+    def rows(S, C, vec):
         P = max(1, 512 // (64 * S))
         while P > 1 and S * P * 64 > (512 if vec * C > 16 else 1024):
             P //= 2
-        return 1 if P > 1 and nacc * S * C * 64 * vec * 4 > 65536 - 1024 else P
+        # the combine buffer: one plane of per-lane partials
+        return 1 if P > 1 and S * C * 64 * vec * 4 > 65536 - 1024 else P
 
     base = nb.norm_bwd_make_plan(kind, M, N, dt, db)
     if kind == "rmsnorm":
         return base
     S, C, vec = base.waves_per_row, base.chunks, base.vec
-    G = min(4096 // (S * rows(S, C, vec, 1)), -(-M // 4))
+    G = min(4096 // (S * rows(S, C, vec)), -(-M // 4))
     G = max(1, G - G % 256 if G > 256 else G)
     p = nb.norm_bwd_make_plan(kind, M, N, dt, db, G)
-    P = rows(S, C, vec, 2 if db else 1)
+    P = rows(S, C, vec)
     p.rows_in_flight, p.threads = P, 64 * S * P
-    p.lds_bytes = (2 if db else 1) * S * C * 64 * vec * 4 if P > 1 else 0
+    p.lds_bytes = S * C * 64 * vec * 4 if P > 1 else 0
     return p
 
 

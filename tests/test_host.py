@@ -169,7 +169,7 @@ GEOMS = [(kind, dt, M, N, db, g)
          for dt in (torch.float32, torch.float16, torch.bfloat16)
          for (M, N) in ((1, 1), (3, 7), (17, 63), (64, 64), (65, 65), (1151, 8192),
                         (2, 768), (100, 4096), (7, 16384), (9, 1000), (300, 256),
-                        (1000, 384), (33, 128), (5000, 768))
+                        (1000, 384), (33, 128), (5000, 768), (65536, 8192), (131072, 4096))
          for db in (False, True)
          for g in (0, 1, 5)]
 
@@ -204,14 +204,21 @@ def test_plan_invariants(nb, kind, dt, M, N, db, groups):
     assert p.rows_per_wave == 1
     # rows in flight: the fewest (a power of two) whose x and dy reach 16 KiB,
     # within 16 waves and the kernel's launch bound; one when the combine
-    # buffer would not fit
+    # buffer (one plane of per-lane partials) would not fit; two when a group
+    # sweeps more than 2 MiB of each operand (kernel A's general loop) and
+    # the same limits allow it
+    max_thr = 512 if vec * C > 16 else 1024
+    plane = S * C * 64 * vec * 4
     want = 1
     while want < 16 and want * 2 * N * eb < 16384:
         want *= 2
-    while want > 1 and (S * want > 16 or S * want * 64 > (512 if vec * C > 16 else 1024)):
+    while want > 1 and (S * want > 16 or S * want * 64 > max_thr):
         want //= 2
-    if want > 1 and (2 if db else 1) * S * C * 64 * vec * 4 > 65536 - 1024:
+    if want > 1 and plane > 65536 - 1024:
         want = 1
+    if (want == 1 and -(-M // p.groups) * N * eb > 2 << 20 and 2 * S <= 16
+            and 2 * S * 64 <= max_thr and plane <= 65536 - 1024):
+        want = 2
     assert P == want
     assert S * 64 * vec * C >= N                       # the lanes cover the row
     assert p.threads == 64 * S * P and 1 <= S * P <= 16
@@ -225,7 +232,7 @@ def test_plan_invariants(nb, kind, dt, M, N, db, groups):
     assert 1 <= p.grid <= p.groups
     nacc = 2 if db else 1
     assert p.workspace_bytes == nacc * p.groups * N * 4
-    assert p.lds_bytes == (nacc * S * C * 64 * vec * 4 if P > 1 else 0)
+    assert p.lds_bytes == (S * C * 64 * vec * 4 if P > 1 else 0)
     assert p.lds_bytes <= 65536
 
 
@@ -250,6 +257,31 @@ def test_two_row_plans_group_row_pairs(nb):
                                   _addr(3), 0, _addr(4), _addr(5), None, _addr(6),
                                   q.workspace_bytes, None)
         assert st == 1, field
+
+
+def test_general_loop_groups_take_two_rows(nb):
+    """Groups sweeping more than 2 MiB of each operand (kernel A's general
+    loop) get two rows in flight; groups within it keep one. The planner and
+    the kernel hold the 2 MiB bound separately and must agree."""
+    csrc = os.path.join(ROOT, "rmsnorm_backward_amd", "csrc")
+    pat = re.compile(r"constexpr int64_t kSteadyGroupBytes = \(int64_t\)(\d+) << (\d+);")
+    vals = [pat.findall(open(os.path.join(csrc, f)).read()) for f in ("plan.cpp", "nb_device.hpp")]
+    assert len(vals[0]) == 1 and vals[0] == vals[1], vals
+    bf = torch.bfloat16
+    p = nb.norm_bwd_make_plan("rmsnorm", 16384, 4096, bf, False)      # 512 KiB per group
+    assert (p.rows_in_flight, p.threads, p.lds_bytes) == (1, 256, 0)
+    p = nb.norm_bwd_make_plan("layernorm", 65536, 8192, bf, True)     # 4 MiB per group
+    assert (p.waves_per_row, p.rows_in_flight, p.threads, p.lds_bytes) == (8, 2, 1024, 32768)
+    p = nb.norm_bwd_make_plan("rmsnorm", 131072, 4096, bf, False)
+    assert (p.waves_per_row, p.rows_in_flight, p.threads, p.lds_bytes) == (4, 2, 512, 16384)
+    p = nb.norm_bwd_make_plan("rmsnorm", 32768, 8192, bf, False)      # exactly 2 MiB
+    assert p.rows_in_flight == 1
+    # explicit groups count too: 8 groups of 2048 rows hold 16 MiB each
+    p = nb.norm_bwd_make_plan("rmsnorm", 16384, 4096, bf, False, 8)
+    assert p.rows_in_flight == 2
+    # fp32 rows of 8192 need 16 waves: a second row would exceed 16 waves
+    p = nb.norm_bwd_make_plan("rmsnorm", 65536, 8192, torch.float32, False)
+    assert (p.waves_per_row, p.rows_in_flight) == (16, 1)
 
 
 def test_groups_do_not_depend_on_device(nb):
