@@ -21,7 +21,13 @@ current stream). Input/output buffer sets are rotated so that consecutive
 steps touch different memory (the set count makes the rotation exceed the
 256 MB Infinity Cache several times over): every step streams from HBM,
 except where all sets together fit in that cache (128 x 512, flagged
-cache_resident).
+cache_resident). The x, dy and dx buffers of the sets (at least four) are
+carved from one pool in a seeded random order with random gaps, so the
+rotation averages over the operands' relative placement in HBM: kernel A on
+long row groups moves by up to 10% with it (65536 x 8192 bf16 LayerNorm,
+527-578 us over ten placements) while the triad does not (512-517 us); a
+single placement would inherit whatever the run's earlier allocations left.
+The same-size triad runs on the same buffers.
 
 The saved statistics the backward reads are produced by the library's GPU
 forward; the forward is also timed on its own (config.forward).
@@ -40,6 +46,7 @@ import ctypes
 import json
 import math
 import os
+import random
 import re
 import sys
 import time
@@ -357,19 +364,40 @@ def triad_sweep(torch, nb, dev, stream, operand_bytes):
 SAME_SIZE_SHAPES = ((0, 1), (0, 2), (0, 4), (256, 4), (512, 4), (1024, 2), (1024, 4), (2048, 2))
 
 
-def triad_same_size(torch, nb, lib, dev, stream, operand_bytes, steps):
-    """The triad over three operands of one workload's x (dy, dx) size, on
-    enough rotating buffer sets to stream from HBM like kernel A: the
-    achievable rate for that many bytes per launch, fixed costs included.
-    Launched through the C entry point with prepared arguments, as kernel A
-    is timed."""
-    n = max(4, operand_bytes // 16 * 4)
-    nsets = max(2, min(64, math.ceil(4 * MALL_BYTES / (3 * n * 4))))
-    sets = [[torch.empty(n, dtype=torch.int32, device=dev).fill_(k) for k in (1, 2, 0)]
-            for _ in range(nsets)]
+def placed_buffers(torch, dev, dtype, shape, count, seed):
+    """`count` tensors of `shape` carved from one pool (returned second) in a
+    seeded random order with random gaps of up to half a tensor between them,
+    at 2 MiB granularity (4 KiB for tensors under 2 MiB): each buffer set's x,
+    dy and dx then sit at random relative offsets, and a timing that rotates
+    over the sets averages over the placement."""
+    eb = torch.tensor([], dtype=dtype).element_size()
+    numel = math.prod(shape)
+    align = (2 << 20) if numel * eb >= (2 << 20) else 4096
+    slots = -(-numel * eb // align)
+    rng = random.Random(seed)
+    gaps = [rng.randrange(0, slots // 2 + 1) for _ in range(count)]
+    order = list(range(count))
+    rng.shuffle(order)
+    pool = torch.empty((sum(gaps) + count * slots) * align // eb, dtype=dtype, device=dev)
+    out, pos = [None] * count, 0
+    for gap, k in zip(gaps, order):
+        pos += gap
+        out[k] = pool[pos * align // eb:pos * align // eb + numel].view(shape)
+        pos += slots
+    return out, pool
+
+
+def triad_same_size(torch, nb, lib, dev, stream, sets, operand_bytes, steps):
+    """The triad over one workload's own x and dy into its dx (as 32-bit
+    words), rotating over the same buffer sets as kernel A: the achievable
+    rate for that many bytes per launch at the same placement, fixed costs
+    included. Launched through the C entry point with prepared arguments, as
+    kernel A is timed. Overwrites dx."""
+    n = operand_bytes // 16 * 4
+    nsets = len(sets)
     P = ctypes.c_void_p
     sh = P(stream.cuda_stream)
-    ptrs = [[P(t.data_ptr()) for t in s] for s in sets]
+    ptrs = [[P(s[k].data_ptr()) for k in ("x", "dy", "dx")] for s in sets]
     nbytes = n * 4
     best = (0.0, None)
     for grid, unroll in SAME_SIZE_SHAPES:
@@ -383,8 +411,6 @@ def triad_same_size(torch, nb, lib, dev, stream, operand_bytes, steps):
         gbps = 3 * n * 4 / (ms * 1e-3) / 1e9
         if gbps > best[0]:
             best = (gbps, (grid, unroll), ms)
-    del sets
-    torch.cuda.empty_cache()
     return {"GBps": round(best[0], 1), "us": round(best[2] * 1e3, 3),
             "grid": best[1][0], "unroll": best[1][1], "bytes_per_launch": 3 * n * 4}
 
@@ -403,7 +429,7 @@ def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, ext
     if args.plan:
         plan = edit_plan(plan, args.plan, with_db)
     set_bytes = 3 * w.M * w.N * w.io_bytes
-    nsets = args.sets or max(2, math.ceil(4 * MALL_BYTES / max(set_bytes, 1)))
+    nsets = args.sets or max(4, math.ceil(4 * MALL_BYTES / max(set_bytes, 1)))
     nsets = min(nsets, 64)
     base = {k: inp[k].to(dev) for k in ("x", "dy", "gamma", "beta") if k in inp}
     # the saved statistics the backward reads come from the GPU forward
@@ -413,10 +439,13 @@ def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, ext
     else:
         _, base["rstd"] = nb.norm_fwd_rmsnorm(base["x"], base["gamma"], w.eps)
     torch.cuda.synchronize()
+    big, pool = placed_buffers(torch, dev, w.io_dtype, (w.M, w.N), 3 * nsets, w.seed)
     sets = []
     for i in range(nsets):
-        s = {k: (v if i == 0 else v.clone()) for k, v in base.items()}
-        s["dx"] = torch.empty_like(base["x"])
+        s = {k: (v if i == 0 else v.clone()) for k, v in base.items() if k not in ("x", "dy")}
+        s["x"], s["dy"], s["dx"] = big[3 * i], big[3 * i + 1], big[3 * i + 2]
+        s["x"].copy_(base["x"])
+        s["dy"].copy_(base["dy"])
         s["f_mean"] = torch.empty_like(base["rstd"])
         s["f_rstd"] = torch.empty_like(base["rstd"])
         sets.append(s)
@@ -511,12 +540,13 @@ def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, ext
         "counted_GBps_incl_workspace": round((alg + 2 * plan.workspace_bytes) / (ms * 1e-3) / 1e9,
                                              2),
         "buffer_sets": nsets,
+        "placement": "x, dy, dx of the sets at seeded random offsets in one pool",
         "cache_resident": nsets * set_bytes <= MALL_BYTES,
     }
     if triad:
         entry["pct_of_triad"] = round(100 * value / triad["GBps"], 2)
         entry["kernel_a_pct_of_triad"] = round(100 * achieved / triad["GBps"], 2)
-        same = triad_same_size(torch, nb, lib, dev, stream, w.M * w.N * w.io_bytes,
+        same = triad_same_size(torch, nb, lib, dev, stream, sets, w.M * w.N * w.io_bytes,
                                max(steps, 50))
         entry["triad_same_bytes"] = same
         entry["kernel_a_pct_of_triad_same_bytes"] = round(100 * achieved / same["GBps"], 2)
@@ -528,7 +558,7 @@ def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, ext
     if extras:
         more = measure_extras(torch, nb, W, lib, dev, stream, w, args, steps, warmup, sets,
                               base, full_args, dgamma, dbeta, ws, io, wg, set_bytes)
-    del sets, base, ws, dgamma, dbeta, full_args, part_args
+    del sets, big, pool, base, ws, dgamma, dbeta, full_args, part_args
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return entry, more, inp

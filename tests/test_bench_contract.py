@@ -112,3 +112,24 @@ def test_shape_and_plan_options(spec):
         assert q.threads == 256
     with pytest.raises(ValueError):
         bench.edit_plan(p.copy(), "groups=3", with_db)
+
+
+@pytest.mark.parametrize("shape,count", [((4096, 1024), 12), ((128, 512), 9), ((1151, 77), 5)])
+def test_placed_buffers_are_disjoint_aligned_and_seeded(shape, count):
+    """The bench's buffer sets: disjoint views inside one pool, at 2 MiB (or,
+    under 2 MiB, 4 KiB) offsets from the pool's start, the same for the same
+    seed and different for another."""
+    import torch
+    bufs, pool = bench.placed_buffers(torch, "cpu", torch.bfloat16, shape, count, 7)
+    nbytes = shape[0] * shape[1] * 2
+    align = (2 << 20) if nbytes >= (2 << 20) else 4096
+    base, end = pool.data_ptr(), pool.data_ptr() + pool.numel() * 2
+    offs = sorted(b.data_ptr() - base for b in bufs)
+    assert all(b.shape == shape and b.is_contiguous() for b in bufs)
+    assert all(o % align == 0 for o in offs)
+    assert all(b - a >= nbytes for a, b in zip(offs, offs[1:]))
+    assert base + offs[-1] + nbytes <= end
+    again, _ = bench.placed_buffers(torch, "cpu", torch.bfloat16, shape, count, 7)
+    assert [b.data_ptr() - base for b in bufs] == [b.data_ptr() - _.data_ptr() for b in again]
+    other, p2 = bench.placed_buffers(torch, "cpu", torch.bfloat16, shape, count, 8)
+    assert [b.data_ptr() - base for b in bufs] != [b.data_ptr() - p2.data_ptr() for b in other]
