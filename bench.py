@@ -84,6 +84,16 @@ def parse_args(argv=None):
     ap.add_argument("--no-triad", action="store_true", help="skip the triad ceiling sweep")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0 = auto)")
     ap.add_argument("--groups", type=int, default=0, help="explicit row-group count (0 = auto)")
+    ap.add_argument("--triad-policies", action="store_true",
+                    help="also sweep the triad over every load/store cache policy, at 512 MiB "
+                         "and at the first workload's x size (config.triad_policies)")
+    ap.add_argument("--placements", type=int, default=0,
+                    help="also time the workload over this many seeded random placements of its "
+                         "operands, with the triad on the same buffers (config.workloads[]."
+                         "placements)")
+    ap.add_argument("--compare-plan", default=None,
+                    help="with --placements: also time this edited plan (as --plan) on the same "
+                         "buffers of every placement")
     return ap.parse_args(argv)
 
 
@@ -347,17 +357,74 @@ def triad_sweep(torch, nb, dev, stream, operand_bytes):
             ms = time_loop(torch, lambda i: nb.norm_bwd_probe_triad(a, b, c, grid, unroll), 10,
                            stream)
             sweep.append((grid, unroll, 3 * operand_bytes / (ms * 1e-3) / 1e9))
+    # the one-pass buffer-load form (kernel A's addressing), non-temporal
+    for unroll in (1, 2, 4):
+        def go(i, unroll=unroll):
+            nb.norm_bwd_probe_triad_policy(a, b, c, unroll, nb.POLICY_NT, nb.POLICY_NT)
+        for i in range(3):
+            go(i)
+        ms = time_loop(torch, go, 10, stream)
+        sweep.append(("buffer", unroll, 3 * operand_bytes / (ms * 1e-3) / 1e9))
     torch.cuda.synchronize()
     ok = bool(torch.all(c == 3).item())
     del a, b, c
     torch.cuda.empty_cache()
     best = max(sweep, key=lambda t: t[2])
-    return {"kernel": "triad_probe_kernel", "what": "c = a + b, 16-byte non-temporal loads and "
-            "stores, 2 reads : 1 write as kernel A", "bytes_per_operand": operand_bytes,
+    return {"kernel": "triad_policy_kernel" if best[0] == "buffer" else "triad_probe_kernel",
+            "what": "c = a + b, 16-byte non-temporal loads and stores, 2 reads : 1 write as "
+            "kernel A (grid 'buffer': the one-pass buffer-load form)",
+            "bytes_per_operand": operand_bytes,
             "GBps": round(best[2], 1), "grid": best[0], "unroll": best[1],
             "pct_of_peak": round(100 * best[2] / PEAK_HBM_GBPS, 2), "result_ok": ok,
             "sweep_min_GBps": round(min(t[2] for t in sweep), 1), "launch_shapes": len(sweep),
             "sweep": [[g, u, round(v, 1)] for g, u, v in sweep]}
+
+
+def triad_policy_sweep(torch, nb, lib, dev, stream, operand_bytes, steps):
+    """norm_bwd_probe_triad_policy over every pair of load and store cache
+    policies (ORs of sc0, nt, sc1) and 1, 2, 4 vectors per thread, on
+    operands of `operand_bytes` (rounded down to 16 KiB) rotated over enough
+    sets to stream from HBM; best of two rounds per variant."""
+    nbytes = min(operand_bytes, 0xFFFFFFFF - 16383) // 16384 * 16384
+    n = nbytes // 4
+    nsets = max(1, min(16, math.ceil(4 * MALL_BYTES / (3 * nbytes))))
+    sets = [[torch.empty(n, dtype=torch.int32, device=dev).fill_(k) for k in (1, 2, 0)]
+            for _ in range(nsets)]
+    P = ctypes.c_void_p
+    sh = P(stream.cuda_stream)
+    ptrs = [[P(t.data_ptr()) for t in s] for s in sets]
+    times = {}
+    for _ in range(2):
+        for unroll in (1, 2, 4):
+            for lp in nb.POLICIES:
+                for sp in nb.POLICIES:
+                    def go(i):
+                        a, b, c = ptrs[i % nsets]
+                        if lib.norm_bwd_probe_triad_policy(a, b, c, nbytes, unroll, lp, sp, sh):
+                            raise RuntimeError(nb.norm_bwd_last_error())
+                    for i in range(3):
+                        go(i)
+                    ms = time_loop(torch, go, steps, stream)
+                    key = (lp, sp, unroll)
+                    times[key] = min(times.get(key, ms), ms)
+    torch.cuda.synchronize()
+    ok = all(bool(torch.all(s[2] == 3).item()) for s in sets)
+    del sets
+    torch.cuda.empty_cache()
+    gbps = {k: 3 * nbytes / (ms * 1e-3) / 1e9 for k, ms in times.items()}
+    nt_both = [v for (lp, sp, _), v in gbps.items() if lp & nb.POLICY_NT and sp & nb.POLICY_NT]
+    other = [v for (lp, sp, _), v in gbps.items()
+             if not (lp & nb.POLICY_NT and sp & nb.POLICY_NT)]
+    best = max(gbps, key=gbps.get)
+    return {"what": "c = a + b in one pass, 16-byte buffer loads and stores under each load and "
+                    "store cache policy (1 sc0, 2 nt, 16 sc1, and their ORs), 1-4 vectors a "
+                    "thread", "bytes_per_operand": nbytes, "buffer_sets": nsets,
+            "result_ok": ok, "best": {"load_policy": best[0], "store_policy": best[1],
+                                      "unroll": best[2], "GBps": round(gbps[best], 1)},
+            "nt_on_both_GBps": [round(min(nt_both), 1), round(max(nt_both), 1)],
+            "otherwise_GBps": [round(min(other), 1), round(max(other), 1)],
+            "all": [[lp, sp, u, round(v, 1)] for (lp, sp, u), v in
+                    sorted(gbps.items(), key=lambda kv: -kv[1])]}
 
 
 # Launch shapes of the same-size triad (grid, unroll); grid 0 = one pass.
@@ -387,32 +454,166 @@ def placed_buffers(torch, dev, dtype, shape, count, seed):
     return out, pool
 
 
+def triad_launchers(nb, lib, nbytes, sh, shapes=SAME_SIZE_SHAPES):
+    """(label, call(a, b, c)) for every triad form tried as a ceiling on
+    operands of nbytes: norm_bwd_probe_triad at each (grid, unroll) of
+    `shapes` (global loads), and norm_bwd_probe_triad_policy with
+    non-temporal loads and stores at 1, 2 and 4 vectors a thread (buffer
+    loads, as kernel A streams) where nbytes allows it."""
+    out = []
+    for grid, unroll in shapes:
+        def call(a, b, c, grid=grid, unroll=unroll):
+            if lib.norm_bwd_probe_triad(a, b, c, nbytes, grid, unroll, sh):
+                raise RuntimeError(nb.norm_bwd_last_error())
+        out.append((f"global grid {grid} unroll {unroll}", call))
+    for unroll in (1, 2, 4):
+        if nbytes % (4096 * unroll) or nbytes > 0xFFFFFFFF - 16383:
+            continue
+        def call(a, b, c, unroll=unroll):
+            if lib.norm_bwd_probe_triad_policy(a, b, c, nbytes, unroll, nb.POLICY_NT,
+                                               nb.POLICY_NT, sh):
+                raise RuntimeError(nb.norm_bwd_last_error())
+        out.append((f"buffer nt unroll {unroll}", call))
+    return out
+
+
 def triad_same_size(torch, nb, lib, dev, stream, sets, operand_bytes, steps):
     """The triad over one workload's own x and dy into its dx (as 32-bit
     words), rotating over the same buffer sets as kernel A: the achievable
     rate for that many bytes per launch at the same placement, fixed costs
-    included. Launched through the C entry point with prepared arguments, as
-    kernel A is timed. Overwrites dx."""
-    n = operand_bytes // 16 * 4
+    included, best of the forms triad_launchers lists. Launched through the C
+    entry points with prepared arguments, as kernel A is timed. Overwrites
+    dx."""
+    nbytes = operand_bytes // 16 * 16
     nsets = len(sets)
     P = ctypes.c_void_p
     sh = P(stream.cuda_stream)
     ptrs = [[P(s[k].data_ptr()) for k in ("x", "dy", "dx")] for s in sets]
-    nbytes = n * 4
-    best = (0.0, None)
-    for grid, unroll in SAME_SIZE_SHAPES:
+    best = (0.0, None, None)
+    for label, call in triad_launchers(nb, lib, nbytes, sh):
         def go(i):
-            a, b, c = ptrs[i % nsets]
-            if lib.norm_bwd_probe_triad(a, b, c, nbytes, grid, unroll, sh):
-                raise RuntimeError(nb.norm_bwd_last_error())
+            call(*ptrs[i % nsets])
         for i in range(5):
             go(i)
         ms = time_loop(torch, go, steps, stream)
-        gbps = 3 * n * 4 / (ms * 1e-3) / 1e9
+        gbps = 3 * nbytes / (ms * 1e-3) / 1e9
         if gbps > best[0]:
-            best = (gbps, (grid, unroll), ms)
-    return {"GBps": round(best[0], 1), "us": round(best[2] * 1e3, 3),
-            "grid": best[1][0], "unroll": best[1][1], "bytes_per_launch": 3 * n * 4}
+            best = (gbps, label, ms)
+    return {"GBps": round(best[0], 1), "us": round(best[2] * 1e3, 3), "form": best[1],
+            "bytes_per_launch": 3 * nbytes}
+
+
+def backward_args(w, sets, plan, dgamma, dbeta, ws, io, wg, sh):
+    """Prepared C arguments per buffer set: those of the named entry point
+    (automatic plan) and those of norm_bwd_execute_partials (explicit plan)."""
+    P = ctypes.c_void_p
+    ptr = lambda t: None if t is None else P(t.data_ptr())  # noqa: E731
+    full_args, part_args = [], []
+    for s in sets:
+        if w.kind == "layernorm":
+            full_args.append((ptr(s["x"]), ptr(s["dy"]), ptr(s["gamma"]), ptr(s["mean"]),
+                              ptr(s["rstd"]), w.M, w.N, io, wg, w.eps, ptr(s["dx"]), ptr(dgamma),
+                              ptr(dbeta), ptr(ws), ws.numel(), sh))
+        else:
+            full_args.append((ptr(s["x"]), ptr(s["dy"]), ptr(s["gamma"]), ptr(s["rstd"]), w.M,
+                              w.N, io, wg, w.eps, ptr(s["dx"]), ptr(dgamma), ptr(dbeta), ptr(ws),
+                              ws.numel(), sh))
+        part_args.append((ctypes.byref(plan), ptr(s["x"]), ptr(s["dy"]), ptr(s["gamma"]),
+                          ptr(s.get("mean")), ptr(s["rstd"]), ptr(s["dx"]), ptr(ws), ws.numel(),
+                          sh))
+    return full_args, part_args
+
+
+def backward_step(nb, lib, w, explicit, full_args, part_args, wg, dgamma, dbeta):
+    """step(i): the whole backward on buffer set i mod len(sets), through the
+    named entry point or, with an explicit plan, norm_bwd_execute."""
+    P = ctypes.c_void_p
+    dg = P(dgamma.data_ptr())
+    db = None if dbeta is None else P(dbeta.data_ptr())
+    fn = lib.norm_bwd_layernorm if w.kind == "layernorm" else lib.norm_bwd_rmsnorm
+    n = len(full_args)
+
+    def step(i):
+        if explicit:
+            a = part_args[i % n]
+            st = lib.norm_bwd_execute(a[0], a[1], a[2], a[3], a[4], a[5], wg, a[6], dg, db, a[7],
+                                      a[8], a[9])
+        else:
+            st = fn(*full_args[i % n])
+        if st:
+            raise RuntimeError(nb.norm_bwd_last_error())
+    return step
+
+
+def placement_study(torch, nb, lib, dev, stream, w, args, base, plan, count):
+    """The backward step and the triad over `count` placements of the
+    operands: for each, two buffer sets whose x, dy and dx are carved from
+    one pool at seeded random offsets (placed_buffers), timed with the
+    benchmark's plan and, with --compare-plan, with the edited plan on the
+    same buffers, then the triad on the same buffers (best of its one-pass
+    global-load and buffer-load forms). Returns per-placement times and their summary."""
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    with_db = w.kind == "layernorm"
+    io = nb._DTYPE_CODE[w.io_dtype]
+    wg = nb._DTYPE_CODE[w.wgrad_dtype]
+    variants = [("plan", plan, bool(args.groups or args.plan))]
+    if args.compare_plan:
+        other = nb.norm_bwd_make_plan(w.kind, w.M, w.N, w.io_dtype, with_db, args.groups)
+        variants.append(("compare_plan", edit_plan(other, args.compare_plan, with_db), True))
+    ws_bytes = max([p.workspace_bytes for _, p, _ in variants] +
+                   [nb.norm_bwd_workspace_bytes(w.kind, w.M, w.N, io, with_db)])
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    dgamma = torch.empty(w.N, dtype=w.wgrad_dtype, device=dev)
+    dbeta = torch.empty(w.N, dtype=w.wgrad_dtype, device=dev) if with_db else None
+    steps = max(50, int(0.2e6 / max(1.0, w.algorithmic_bytes() / 6.0e6)))
+    nbytes = w.M * w.N * w.io_bytes // 16 * 16
+    rows = []
+    for j in range(count):
+        big, pool = placed_buffers(torch, dev, w.io_dtype, (w.M, w.N), 6,
+                                   w.seed * 1000003 + 7919 * (j + 1))
+        sets = []
+        for i in range(2):
+            s = {k: v for k, v in base.items() if k not in ("x", "dy")}
+            s["x"], s["dy"], s["dx"] = big[3 * i], big[3 * i + 1], big[3 * i + 2]
+            s["x"].copy_(base["x"])
+            s["dy"].copy_(base["dy"])
+            sets.append(s)
+        row = {"placement": j,
+               "offsets_MiB": [round((t.data_ptr() - pool.data_ptr()) / 2**20) for t in big]}
+        for name, p, explicit in variants:
+            full_args, part_args = backward_args(w, sets, p, dgamma, dbeta, ws, io, wg, sh)
+            step = backward_step(nb, lib, w, explicit, full_args, part_args, wg, dgamma, dbeta)
+            for i in range(steps // 4):
+                step(i)
+            row[name + "_us"] = round(min(time_loop(torch, step, steps, stream)
+                                          for _ in range(2)) * 1e3, 2)
+        ptrs = [[ctypes.c_void_p(s[k].data_ptr()) for k in ("x", "dy", "dx")] for s in sets]
+        best = None
+        for _, call in triad_launchers(nb, lib, nbytes, sh, ((0, 1), (0, 4))):
+            def go(i):
+                call(*ptrs[i % 2])
+            for i in range(4):
+                go(i)
+            ms = time_loop(torch, go, steps, stream)
+            best = ms if best is None else min(best, ms)
+        row["triad_us"] = round(best * 1e3, 2)
+        rows.append(row)
+        print(f"bench.py: placement {j}: " + ", ".join(f"{k} {v}" for k, v in row.items()
+                                                       if k.endswith("_us")),
+              file=sys.stderr, flush=True)
+        del sets, big, pool
+        torch.cuda.empty_cache()
+    out = {"what": "backward step (kernel A + B) and the triad on the same buffers, per "
+                   "placement of x, dy, dx (two sets each)", "count": count, "steps": steps,
+           "per_placement": rows}
+    for key in [k for k in rows[0] if k.endswith("_us")]:
+        v = [r[key] for r in rows]
+        out[key.replace("_us", "")] = {"mean_us": round(sum(v) / len(v), 2), "min_us": min(v),
+                                       "max_us": max(v)}
+    if args.compare_plan:
+        out["compare_plan_spec"] = args.compare_plan
+        out["plan_faster_in"] = sum(r["plan_us"] < r["compare_plan_us"] for r in rows)
+    return out
 
 
 def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, extras, triad):
@@ -458,32 +659,9 @@ def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, ext
     P = ctypes.c_void_p
     ptr = lambda t: None if t is None else P(t.data_ptr())  # noqa: E731
 
-    full_args, part_args = [], []
-    for s in sets:
-        if w.kind == "layernorm":
-            full_args.append((ptr(s["x"]), ptr(s["dy"]), ptr(s["gamma"]), ptr(s["mean"]),
-                              ptr(s["rstd"]), w.M, w.N, io, wg, w.eps, ptr(s["dx"]), ptr(dgamma),
-                              ptr(dbeta), ptr(ws), ws.numel(), sh))
-        else:
-            full_args.append((ptr(s["x"]), ptr(s["dy"]), ptr(s["gamma"]), ptr(s["rstd"]), w.M,
-                              w.N, io, wg, w.eps, ptr(s["dx"]), ptr(dgamma), ptr(dbeta), ptr(ws),
-                              ws.numel(), sh))
-        part_args.append((ctypes.byref(plan), ptr(s["x"]), ptr(s["dy"]), ptr(s["gamma"]),
-                          ptr(s.get("mean")), ptr(s["rstd"]), ptr(s["dx"]), ptr(ws), ws.numel(),
-                          sh))
-    fn = lib.norm_bwd_layernorm if w.kind == "layernorm" else lib.norm_bwd_rmsnorm
-    if args.groups or args.plan:
-        fn = None
-
-    def step(i):
-        if fn is None:
-            a = part_args[i % nsets]
-            st = lib.norm_bwd_execute(a[0], a[1], a[2], a[3], a[4], a[5], wg, a[6], ptr(dgamma),
-                                      ptr(dbeta), a[7], a[8], a[9])
-        else:
-            st = fn(*full_args[i % nsets])
-        if st:
-            raise RuntimeError(nb.norm_bwd_last_error())
+    full_args, part_args = backward_args(w, sets, plan, dgamma, dbeta, ws, io, wg, sh)
+    step = backward_step(nb, lib, w, bool(args.groups or args.plan), full_args, part_args, wg,
+                         dgamma, dbeta)
 
     def step_a(i):
         st = lib.norm_bwd_execute_partials(*part_args[i % nsets])
@@ -554,6 +732,9 @@ def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, ext
               if k in ("groups", "rows_per_group", "vec", "chunks", "waves_per_row",
                        "rows_in_flight", "rows_per_wave", "threads", "grid")}
     entry["plan"] = plan_d
+    if args.placements and w.name == args.primary_name:
+        entry["placements"] = placement_study(torch, nb, lib, dev, stream, w, args, base, plan,
+                                              args.placements)
     more = {}
     if extras:
         more = measure_extras(torch, nb, W, lib, dev, stream, w, args, steps, warmup, sets,
@@ -753,12 +934,24 @@ def main(argv=None) -> int:
         primary = parse_shape(W, torch, args.shape)
     else:
         primary = W.WORKLOADS[args.workload] if args.workload else W.HEADLINE
+    args.primary_name = primary.name
+    if args.compare_plan and not args.placements:
+        print("bench.py: --compare-plan needs --placements", file=sys.stderr)
+        return 2
     single = bool(args.workload or args.shape or args.plan or args.groups)
     others = [] if single else [W.WORKLOADS[n] for n in DEFAULT_ORDER if n != primary.name]
 
     # the streaming ceiling (first: it also brings the GPU clock up)
     triad = triad_sweep(torch, nb, dev, stream, 512 << 20) if not args.no_triad else None
     print(f"bench.py: triad ceiling {triad and triad['GBps']} GB/s", file=sys.stderr, flush=True)
+    policies = None
+    if args.triad_policies:
+        policies = [triad_policy_sweep(torch, nb, lib, dev, stream, nbytes, 20)
+                    for nbytes in (512 << 20, primary.M * primary.N * primary.io_bytes)]
+        for p in policies:
+            print(f"bench.py: triad policies at {p['bytes_per_operand']} B: best {p['best']}, "
+                  f"nt on both {p['nt_on_both_GBps']}, otherwise {p['otherwise_GBps']} GB/s",
+                  file=sys.stderr, flush=True)
 
     entries = {}
     cpu_inputs = {}
@@ -801,6 +994,7 @@ def main(argv=None) -> int:
         "copy_probe_GBps": round(copy_gbps, 1), "copy_probe_bytes": cp_bytes,
         "triad_probe": triad,
         "pct_of_triad": e.get("pct_of_triad"),
+        "triad_policies": policies,
         "buffer_sets": e["buffer_sets"], "workspace_bytes": e["workspace_bytes"],
         "counted_GBps_incl_workspace": e["counted_GBps_incl_workspace"],
         "plan": e["plan"],

@@ -423,6 +423,25 @@ int norm_bwd_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
 int norm_bwd_probe_triad(const void *a, const void *b, void *c, size_t bytes, int grid,
                          int unroll, void *stream);
 
+/*
+ * Measurement aid, not part of the backward pass: the triad above in one pass
+ * with 16-byte raw buffer loads and stores under a chosen cache policy, to
+ * find which policy streams kernel A's 2-read:1-write mix fastest.
+ *   a, b, c       as for norm_bwd_probe_triad
+ *   bytes         bytes per operand: a multiple of 4096 * unroll, at most
+ *                 NORM_BWD_PROBE_POLICY_MAX_BYTES (32-bit buffer offsets)
+ *   unroll        16-byte vectors per operand per thread: 1, 2 or 4
+ *   load_policy, store_policy
+ *                 cache-policy bits of the gfx950 vector memory
+ *                 instructions, any OR of 1 (sc0), 2 (nt) and 16 (sc1);
+ *                 0 is the default policy
+ * Returns a status code; NORM_BWD_ERR_INVALID_ARG for arguments outside these
+ * ranges, with nothing launched.
+ */
+#define NORM_BWD_PROBE_POLICY_MAX_BYTES (0xFFFFFFFFu - 16383u)
+int norm_bwd_probe_triad_policy(const void *a, const void *b, void *c, size_t bytes,
+                                int unroll, int load_policy, int store_policy, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -137,6 +137,7 @@ def load_library():
             "norm_bwd_last_error": [],
             "norm_bwd_probe_copy": [vp, vp, sz, vp],
             "norm_bwd_probe_triad": [vp, vp, vp, sz, i32, i32, vp],
+            "norm_bwd_probe_triad_policy": [vp, vp, vp, sz, i32, i32, i32, vp],
             "norm_fwd_layernorm": [vp, vp, vp, i64, i64, i32, fp, vp, vp, vp, vp],
             "norm_fwd_rmsnorm": [vp, vp, i64, i64, i32, fp, vp, vp, vp],
             "norm_bwd_ex": [ctypes.POINTER(NormBwdArgs)],
@@ -610,10 +611,37 @@ def norm_bwd_probe_triad(a: torch.Tensor, b: torch.Tensor, c: torch.Tensor, grid
         _check(lib.norm_bwd_probe_triad(_ptr(a), _ptr(b), _ptr(c), n, grid, unroll, s))
 
 
+# Cache-policy bits of the gfx950 vector memory instructions, for
+# norm_bwd_probe_triad_policy: any OR of them is a policy.
+POLICY_SC0, POLICY_NT, POLICY_SC1 = 1, 2, 16
+POLICIES = (0, 1, 2, 3, 16, 17, 18, 19)
+
+
+def norm_bwd_probe_triad_policy(a: torch.Tensor, b: torch.Tensor, c: torch.Tensor,
+                                unroll: int = 1, load_policy: int = POLICY_NT,
+                                store_policy: int = POLICY_NT, stream=None):
+    """The triad in one pass with 16-byte buffer accesses under the given
+    load and store cache policies; moves 3 * a's bytes (a multiple of
+    4096 * unroll)."""
+    lib = load_library()
+    _gpu(a, "a")
+    _tensor(b, "b", a.device)
+    _tensor(c, "c", a.device)
+    n = a.numel() * a.element_size()
+    if b.numel() * b.element_size() < n or c.numel() * c.element_size() < n:
+        raise ValueError("b and c must hold at least a's bytes")
+    s = _stream(stream, a.device)
+    with torch.cuda.device(a.device):
+        _check(lib.norm_bwd_probe_triad_policy(_ptr(a), _ptr(b), _ptr(c), n, unroll,
+                                               load_policy, store_policy, s))
+
+
 __all__ = [
     "norm_bwd_layernorm", "norm_bwd_rmsnorm", "norm_bwd_workspace_bytes", "norm_bwd_make_plan",
     "norm_bwd_execute", "norm_bwd_execute_partials", "norm_bwd_reduce_partials",
-    "norm_bwd_probe_copy", "norm_bwd_probe_triad", "norm_bwd_status_string", "norm_bwd_last_error", "NormBwdPlan",
+    "norm_bwd_probe_copy", "norm_bwd_probe_triad", "norm_bwd_probe_triad_policy",
+    "POLICIES", "POLICY_SC0", "POLICY_NT", "POLICY_SC1",
+    "norm_bwd_status_string", "norm_bwd_last_error", "NormBwdPlan",
     "norm_fwd_layernorm", "norm_fwd_rmsnorm", "norm_bwd_ex", "norm_bwd_ex_static",
     "NormBwdArgs", "ACCUMULATE", "STATIC_SCRATCH_BYTES",
     "norm_bwd_wgrad",

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(LIB_DIR, "libnorm_bwd.so")
 SOURCES = ["api.cpp", "plan.cpp", "reduce.hip", "kernels_f32.hip", "kernels_f16.hip",
            "kernels_bf16.hip", "kernels_f32_recompute.hip", "kernels_f16_recompute.hip",
            "kernels_bf16_recompute.hip", "wgrad.hip", "rowloop.hip", "noalloc.hip",
-           "tworow.hip"]
+           "tworow.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

@@ -663,4 +663,28 @@ int norm_bwd_probe_triad(const void* a, const void* b, void* c, size_t bytes, in
   return NORM_BWD_OK;
 }
 
+int norm_bwd_probe_triad_policy(const void* a, const void* b, void* c, size_t bytes, int unroll,
+                                int load_policy, int store_policy, void* stream) {
+  if (bytes == 0) return NORM_BWD_OK;
+  if (!a || !b || !c || !aligned16(a) || !aligned16(b) || !aligned16(c))
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "triad policy probe needs non-NULL, 16-byte "
+                                               "aligned buffers");
+  if (unroll != 1 && unroll != 2 && unroll != 4)
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "triad policy probe unroll must be 1, 2 or 4");
+  if (bytes % (4096u * (unsigned)unroll) != 0 || bytes > NORM_BWD_PROBE_POLICY_MAX_BYTES)
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "triad policy probe bytes must be a multiple of "
+                                               "4096 * unroll, at most 2^32 - 4096 * 4");
+  const auto valid = [](int p) { return p >= 0 && (p & ~(1 | 2 | 16)) == 0; };
+  if (!valid(load_policy) || !valid(store_policy))
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "triad policy probe policies must be ORs of "
+                                               "1 (sc0), 2 (nt) and 16 (sc1)");
+  if (nb::ranges_overlap(c, bytes, a, bytes) || nb::ranges_overlap(c, bytes, b, bytes))
+    return set_error(NORM_BWD_ERR_INVALID_ARG, "triad policy probe output overlaps an input");
+  (void)hipGetLastError();
+  hipError_t e = nb::launch_triad_policy(a, b, c, (uint32_t)bytes, unroll, load_policy,
+                                         store_policy, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_error(e, "triad policy probe launch");
+  return NORM_BWD_OK;
+}
+
 }  // extern "C"

@@ -114,5 +114,7 @@ hipError_t launch_reduce(int wgrad_dtype, const float* ws, int64_t G, int N, voi
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 hipError_t launch_triad(const void* a, const void* b, void* c, size_t bytes, int grid,
                         int unroll, hipStream_t stream);
+hipError_t launch_triad_policy(const void* a, const void* b, void* c, uint32_t bytes, int unroll,
+                               int load_policy, int store_policy, hipStream_t stream);
 
 }  // namespace nb

@@ -89,7 +89,7 @@ def stats_summary(stats_csv: str, bench_json: str, cmds) -> str:
     out += list(cmds) + ["```", "",
                          "| kernel | calls | average (us) | min (us) | max (us) | share |",
                          "|---|---|---|---|---|---|"]
-    avg_a = avg_f = avg_b = avg_t = None
+    avg_a = avg_f = avg_b = None
     calls_a = -1
     for r in rows:
         name = r["Name"]
@@ -101,8 +101,6 @@ def stats_summary(stats_csv: str, bench_json: str, cmds) -> str:
             avg_f = avg
         if KERNEL_B in name:
             avg_b = avg
-        if TRIAD in name and (avg_t is None or avg < avg_t):
-            avg_t = avg
         out.append(f"| `{short}` | {r['Calls']} | {avg:.2f} | {float(r['MinNs'])/1e3:.2f} | "
                    f"{float(r['MaxNs'])/1e3:.2f} | {float(r['Percentage']):.1f}% |")
     out += ["", "Benchmark line of the same run (HIP events on the launch stream):", "",

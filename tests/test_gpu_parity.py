@@ -463,6 +463,23 @@ def test_triad_probe(nb, n16, grid, unroll):
     assert torch.all(cbuf[4 * n16:] == -7)
 
 
+@pytest.mark.parametrize("unroll", [1, 2, 4])
+def test_triad_policy_probe(nb, unroll):
+    """The cache-policy triad computes c = a + b on 32-bit words under every
+    load and store policy, and writes nothing past c's end."""
+    n = 4096 * unroll * 5 // 4          # 32-bit words: 5 workgroups
+    g = torch.Generator(device="cuda").manual_seed(unroll)
+    a = torch.randint(0, 1 << 30, (n,), dtype=torch.int32, device="cuda", generator=g)
+    b = torch.randint(0, 1 << 30, (n,), dtype=torch.int32, device="cuda", generator=g)
+    for lp in nb.POLICIES:
+        for sp in nb.POLICIES:
+            cbuf = torch.full((n + 1024,), -7, dtype=torch.int32, device="cuda")
+            nb.norm_bwd_probe_triad_policy(a, b, cbuf[:n], unroll, lp, sp)
+            torch.cuda.synchronize()
+            assert torch.equal(cbuf[:n], a + b), (lp, sp)
+            assert torch.all(cbuf[n:] == -7), (lp, sp)
+
+
 def test_copy_probe(nb):
     src = torch.randint(0, 1 << 30, (1 << 20,), dtype=torch.int32, device="cuda")
     dst = torch.zeros_like(src)

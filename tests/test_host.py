@@ -39,7 +39,7 @@ def test_header_declares_the_documented_entry_points():
                  "norm_bwd_make_plan", "norm_bwd_execute", "norm_bwd_execute_partials",
                  "norm_bwd_reduce_partials", "norm_bwd_status_string", "norm_bwd_last_error",
                  "norm_bwd_probe_copy", "norm_fwd_layernorm", "norm_fwd_rmsnorm", "norm_bwd_ex",
-                 "norm_bwd_wgrad", "norm_bwd_probe_triad"):
+                 "norm_bwd_wgrad", "norm_bwd_probe_triad", "norm_bwd_probe_triad_policy"):
         assert want in names
 
 
@@ -443,6 +443,19 @@ def test_reduce_and_probe_reject(nb):
     assert T(_addr(0), _addr(1), _addr(2), 1024, -1, 4, None) == 1      # grid
     assert T(_addr(0), _addr(1), _addr(2), 1024, (1 << 20) + 1, 4, None) == 1
     assert T(_addr(0), _addr(1), ctypes.c_void_p(B + 512), 1024, 0, 4, None) == 1  # c overlaps a
+    # the cache-policy triad: sizes (4096 * unroll multiples, 32-bit range),
+    # unroll, policy bits, alignment and overlap, nothing launched
+    TP = lib.norm_bwd_probe_triad_policy
+    assert TP(_addr(0), _addr(1), _addr(2), 0, 1, 2, 2, None) == 0
+    assert TP(_addr(0), _addr(1), _addr(2), 2048, 1, 2, 2, None) == 1
+    assert TP(_addr(0), _addr(1), _addr(2), 4096, 2, 2, 2, None) == 1
+    assert TP(_addr(0), _addr(1), _addr(2), 8192, 8, 2, 2, None) == 1
+    assert TP(_addr(0), _addr(1), _addr(2), 1 << 32, 1, 2, 2, None) == 1
+    assert TP(_addr(0), _addr(1), _addr(2), 4096, 1, 4, 2, None) == 1  # not a policy bit
+    assert TP(_addr(0), _addr(1), _addr(2), 4096, 1, 2, 32, None) == 1
+    assert TP(_addr(0), _addr(1), _addr(2), 4096, 1, -1, 2, None) == 1
+    assert TP(ctypes.c_void_p(B + 8), _addr(1), _addr(2), 4096, 1, 2, 2, None) == 1
+    assert TP(_addr(0), _addr(1), ctypes.c_void_p(B + 512), 4096, 1, 2, 2, None) == 1
 
 
 def _fwd(nb, kind, **over):
