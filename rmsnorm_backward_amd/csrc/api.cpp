@@ -415,10 +415,11 @@ int run_forward(int kind, const void* x, const void* gamma, const void* beta, in
   f.N = (int)N;
   f.eps = eps;
   f.S = wide ? 0 : g.waves_per_row;
-  f.P = wide ? 0 : g.rows_in_flight;
-  f.threads = wide ? 0 : g.threads;
+  f.P = wide ? 0 : nb::forward_rows_in_flight(M, g.waves_per_row, g.rows_in_flight,
+                                              g.vec * g.chunks);
+  f.threads = wide ? 0 : 64 * f.S * f.P;
   f.grid = wide ? (int)(f.chunks ? nb::rowreg_grid(M) : nb::rowloop_grid(M))
-                : (int)nb::forward_grid(M, g.waves_per_row, g.rows_in_flight);
+                : (int)nb::forward_grid(M, f.S, f.P);
   f.stream = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so a launch failure is ours
   hipError_t e;

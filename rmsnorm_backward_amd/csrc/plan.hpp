@@ -70,6 +70,12 @@ int64_t rowloop_grid(int64_t M);
 // sweep of rows.
 int64_t forward_grid(int64_t M, int S, int P);
 
+// Rows in flight of the forward for M rows, given the row-statistics
+// geometry's S waves per row, P rows in flight and vec * chunks elements per
+// lane: 2P (1024 threads) when 16 waves and the launch bound allow it and
+// every row-lane of the resulting grid still gets at least 4 rows, else P.
+int forward_rows_in_flight(int64_t M, int S, int P, int lane_elems);
+
 // Lanes per row of the column-walk tile (tile = lpr * vec columns) for N
 // columns: the widest tile (up to 64 columns) that still gives at least 256
 // tiles, and at least one lane.

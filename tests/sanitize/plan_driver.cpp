@@ -100,6 +100,30 @@ int main() {
                              "automatic groups");
                   }
                 }
+  // the forward's launch: row-statistics geometry, rows in flight and grid
+  long forwards = 0;
+  for (int kind : kinds)
+    for (int dt : dtypes)
+      for (int64_t M : Ms)
+        for (int64_t N : Ns)
+          for (int vec_ok = 0; vec_ok < 2; ++vec_ok) {
+            if (M == 0 || N == 0) continue;
+            norm_bwd_plan_t g;
+            const char* why = nullptr;
+            if (nb::make_geometry(kind, N, dt, 0, vec_ok != 0, &g, &why, true) != NORM_BWD_OK)
+              continue;
+            ++forwards;
+            const int S = g.waves_per_row, P0 = g.rows_in_flight;
+            const int P = nb::forward_rows_in_flight(M, S, P0, g.vec * g.chunks);
+            EXPECT(P == P0 || P == 2 * P0, "forward P %d from %d", P, P0);
+            EXPECT(S * P <= 16, "forward waves S %d P %d", S, P);
+            EXPECT(64 * S * P <= nb::kernel_a_max_threads(g.vec * g.chunks), "forward bound");
+            const int64_t grid = nb::forward_grid(M, S, P);
+            EXPECT(grid >= 1 && grid <= (M + P - 1) / P, "forward grid %lld", (long long)grid);
+            if (P == 2 * P0) EXPECT(M >= 4 * grid * P, "forward rows per lane");
+          }
+  EXPECT(forwards > 1000, "forward cases %ld", forwards);
+
   // invalid arguments are refused with a status, and leave no half-filled plan used
   const struct { int kind, dt; int64_t M, N; int db; int64_t G; } bad[] = {
       {7, NORM_BWD_BF16, 8, 8, 0, 0}, {NORM_BWD_RMSNORM, 9, 8, 8, 0, 0},
