@@ -775,6 +775,24 @@ def measure_extras(torch, nb, W, lib, dev, stream, w, args, steps, warmup, sets,
         step_f(i)
     ms_f = time_loop(torch, step_f, steps, stream)
     f_bytes = forward_bytes(w, "beta" in base)
+    # the forward's own ceiling: one read and one write (the triad probe
+    # reading x twice, so HBM sees x once), on the same buffers into y
+    f_ceiling = None
+    nbytes = w.M * w.N * w.io_bytes
+    for unroll in (1, 2, 4):
+        if nbytes % (4096 * unroll) or nbytes > 0xFFFFFFFF - 16383:
+            continue
+        one = [(P(s["x"].data_ptr()), P(s["dx"].data_ptr())) for s in sets]
+
+        def step_c(i, unroll=unroll):
+            xp, yp = one[i % nsets]
+            if lib.norm_bwd_probe_triad_policy(xp, xp, yp, nbytes, unroll, nb.POLICY_NT,
+                                               nb.POLICY_NT, sh):
+                raise RuntimeError(nb.norm_bwd_last_error())
+        for i in range(5):
+            step_c(i)
+        ms_c = time_loop(torch, step_c, steps, stream)
+        f_ceiling = ms_c if f_ceiling is None else min(f_ceiling, ms_c)
 
     # the backward in recompute mode: NULL statistics, recomputed from x
     rc_args = [(a[0], a[1], a[2], None, None) + a[5:] if w.kind == "layernorm"
@@ -855,6 +873,9 @@ def measure_extras(torch, nb, W, lib, dev, stream, w, args, steps, warmup, sets,
             "GBps": round(f_bytes / (ms_f * 1e-3) / 1e9, 2),
             "traffic": committed_forward_traffic(w.name),
             "pct_of_peak": round(100 * f_bytes / (ms_f * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+            "one_read_one_write_ceiling_us": None if f_ceiling is None else
+            round(f_ceiling * 1e3, 3),
+            "pct_of_ceiling": None if f_ceiling is None else round(100 * f_ceiling / ms_f, 2),
         },
         "recompute": {
             "what": "whole backward step with mean/rstd recomputed from x (no stats read)",
