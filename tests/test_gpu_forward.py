@@ -205,6 +205,40 @@ def test_forward_statistics_optional_and_deterministic(nb):
     assert torch.isfinite(y).all() and torch.isfinite(r).all()
 
 
+@pytest.mark.parametrize("kind,dt,M,m,N", [
+    ("layernorm", torch.bfloat16, 4096, 600, 8192),    # 1 -> 2 rows in flight
+    ("rmsnorm", torch.bfloat16, 8192, 1000, 4096),     # 2 -> 4
+    ("rmsnorm", torch.float32, 4096, 300, 4096),       # 1 -> 2
+    ("layernorm", torch.float16, 1151, 500, 8192),     # too few rows: stays at 1
+])
+def test_forward_rows_do_not_depend_on_the_launch(nb, kind, dt, M, m, N):
+    """The forward doubles its rows in flight only where each row-lane keeps
+    at least 4 rows, so a large batch and its first m rows launch with
+    different geometry; every output row is the same bit for bit, and both
+    match the oracle."""
+    base = W.LN_BF16_65536x8192 if kind == "layernorm" else W.RMS_BF16_16384x4096
+    w = W.scaled(base, M=M, N=N, io_dtype=dt)
+    inp = W.make_inputs(w)
+    x, g = inp["x"].cuda(), inp["gamma"].cuda()
+    if kind == "layernorm":
+        b = _beta(w, inp).cuda()
+        big = nb.norm_fwd_layernorm(x, g, b, w.eps)
+        small = nb.norm_fwd_layernorm(x[:m].contiguous(), g, b, w.eps)
+    else:
+        big = nb.norm_fwd_rmsnorm(x, g, w.eps)
+        small = nb.norm_fwd_rmsnorm(x[:m].contiguous(), g, w.eps)
+    torch.cuda.synchronize()
+    for t_big, t_small in zip(big, small):
+        assert torch.equal(t_big[:m], t_small)
+    rows = slice(0, 64)
+    beta = _beta(w, inp) if kind == "layernorm" else None
+    if kind == "layernorm":
+        got = (big[0][rows].cpu(), big[1][rows].cpu(), big[2][rows].cpu())
+    else:
+        got = (big[0][rows].cpu(), None, big[1][rows].cpu())
+    check(W.scaled(w, M=64), inp["x"][rows], inp["gamma"], beta, got)
+
+
 def test_forward_misaligned_rows_take_the_scalar_path(nb):
     w = W.scaled(W.RMS_BF16_16384x4096, M=37, N=1000)
     inp = W.make_inputs(w)
