@@ -179,8 +179,16 @@ def test_general_loop_two_rows_in_flight(nb, kind, dt, M, N, groups):
     # one row in flight by the row-size rule; two for the group size
     assert p.rows_in_flight == 2 and 2 * N * eb >= 16384 and p.rows_per_group * N * eb > 2 << 20
     inp = backward_inputs(w)
-    out = run(nb, w, to_gpu(inp), plan=p)
+    g = to_gpu(inp)
+    out = run(nb, w, g, plan=p)
     compare_full(w, inp, out, with_db, groups=groups)
+    # one row in flight: each row's sums keep their order, so dx is the same
+    # bit for bit; only the order of the group sums (dgamma, dbeta) changes
+    q = p.copy()
+    q.rows_in_flight, q.threads, q.lds_bytes = 1, 64 * p.waves_per_row, 0
+    one = run(nb, w, g, plan=q)
+    assert torch.equal(one[0], out[0])
+    compare_full(w, inp, one, with_db, groups=groups)
 
 
 @pytest.mark.parametrize("kind", ["layernorm", "rmsnorm"])
