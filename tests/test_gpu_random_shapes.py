@@ -57,6 +57,29 @@ def _cases(n=200, seed=20261202):
     return out
 
 
+def _long_group_cases(n=40, seed=20261203):
+    """Explicit group counts (1 to 3) with enough rows that every group
+    sweeps more than 2 MiB of each operand: kernel A's general loop, where
+    the planner keeps two rows in flight; the last group is ragged."""
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        kind = rng.choice(("layernorm", "rmsnorm"))
+        dt = rng.choice(DTYPES)
+        eb = 4 if dt == torch.float32 else 2
+        N = rng.choice((512, 768, 1000, 1024, 2048, 3000, 4096, 4100, 8192))
+        groups = rng.choice((1, 1, 2, 3))
+        need = (2 << 20) // (N * eb) + 1              # rows per group beyond 2 MiB
+        M = groups * need + rng.randint(0, need - 1)
+        with_db = kind == "layernorm" if rng.random() < 0.6 else rng.random() < 0.5
+        recompute = rng.random() < 0.25
+        pad = rng.choice((0, 0, 8, 24, 5))
+        wg = torch.float32 if rng.random() < 0.75 else dt
+        acc = rng.random() < 0.2
+        out.append((1000 + i, kind, dt, M, N, with_db, recompute, pad, wg, acc, groups))
+    return out
+
+
 def _strided(t, pad):
     M, N = t.shape
     buf = torch.zeros(M * (N + pad), dtype=t.dtype, device="cuda")
@@ -76,6 +99,18 @@ def nb():
 @pytest.mark.parametrize("case", _cases(), ids=lambda c: "-".join(str(v).replace("torch.", "")
                                                                    for v in c))
 def test_random_shape(nb, case):
+    _run_backward_case(nb, case)
+
+
+@pytest.mark.parametrize("case", _long_group_cases(),
+                         ids=lambda c: "-".join(str(v).replace("torch.", "") for v in c))
+def test_random_long_groups(nb, case):
+    _run_backward_case(nb, case)
+
+
+def _run_backward_case(nb, case):
+    """One drawn case through the public entry points (norm_bwd_ex when rows
+    are strided or groups are explicit), compared with the oracle."""
     i, kind, dt, M, N, with_db, recompute, pad, wg, acc, groups = case
     if acc:
         wg = torch.float32
@@ -86,13 +121,14 @@ def test_random_shape(nb, case):
     base = W.LN_F32_128x512 if kind == "layernorm" else W.RMS_F32_128x512
     w = W.scaled(base, M=M, N=N, io_dtype=dt, wgrad_dtype=wg, seed=9000 + i)
     inp = backward_inputs(w)
-    x = _strided(inp["x"], pad) if pad else inp["x"].cuda()
-    dy = _strided(inp["dy"], pad) if pad else inp["dy"].cuda()
+    use_ex = pad > 0 or groups > 0 or acc
+    x = _strided(inp["x"], pad) if use_ex else inp["x"].cuda()
+    dy = _strided(inp["dy"], pad) if use_ex else inp["dy"].cuda()
     g = inp["gamma"].cuda()
     mean = None if (recompute or kind == "rmsnorm") else inp["mean"].cuda()
     rstd = None if recompute else inp["rstd"].cuda()
     old = torch.randn(N, generator=torch.Generator().manual_seed(i)) if acc else None
-    if pad:
+    if use_ex:
         dg0 = old.clone().cuda() if acc else None
         db0 = old.clone().cuda() if (acc and with_db) else None
         dx, dg, db = nb.norm_bwd_ex(kind, x, dy, g, mean, rstd, w.eps, wgrad_dtype=wg,
@@ -138,18 +174,22 @@ def test_random_shape(nb, case):
     else:
         bg, bb = parity.wgrad_bounds(kind, inp["x"], inp["dy"], inp.get("mean"), inp["rstd"],
                                      depth)
+    # the named deep-sum case for fp32 (parity.FP32_DEEP_SUM_DEPTH)
+    long_g = parity.fp32_deep_sum_extra(dt, bg)
+    long_b = parity.fp32_deep_sum_extra(dt, bb)
     if acc:
         old64 = old.double().abs().numpy()
         a_extra = 2.0 ** -24 * (old64 + abs(parity.f64(rdg)))
-        parity.check_wgrad(dt, dg - old, rdg,
-                           extra=a_extra if extra is None else a_extra + parity.f64(extra), **bg)
+        parity.check_wgrad(dt, dg - old, rdg, extra=parity.add_extra(a_extra, extra, long_g),
+                           **bg)
         if with_db:
             b_extra = 2.0 ** -24 * (old64 + abs(parity.f64(rdb)))
-            parity.check_wgrad(dt, db.cpu() - old, rdb, "dbeta", extra=b_extra, **bb)
+            parity.check_wgrad(dt, db.cpu() - old, rdb, "dbeta",
+                               extra=parity.add_extra(b_extra, long_b), **bb)
     else:
-        parity.check_wgrad(dt, dg, rdg, extra=extra, **bg)
+        parity.check_wgrad(dt, dg, rdg, extra=parity.add_extra(extra, long_g), **bg)
         if with_db:
-            parity.check_wgrad(dt, db.cpu(), rdb, "dbeta", **bb)
+            parity.check_wgrad(dt, db.cpu(), rdb, "dbeta", extra=long_b, **bb)
 
 
 def _fwd_cases(n=80, seed=1202):

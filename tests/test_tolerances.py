@@ -109,6 +109,37 @@ def test_half_weight_gradients_bound():
         parity.check_wgrad(torch.bfloat16, torch.from_numpy(dg), rdg)
 
 
+def test_fp32_deep_sums_need_the_summation_bound():
+    """The named deep-sum case: a float32 sum of 1327 rows in one or two
+    groups misses the plain 1e-5 bound on columns that cancel (by 2-3x here),
+    and meets it with the fp32 summation term; the same rows in 256 groups
+    (depth 58) meet the plain bound. Up to depth 128, and for half
+    precision, no term is added."""
+    w = W.scaled(W.LN_F32_128x512, M=1327, N=1000, seed=10000)
+    inp = backward_inputs(w)
+    x, dy, rs, mu = (_np(inp, k) for k in ("x", "dy", "rstd", "mean"))
+    rdg, _ = oracle.bwd_wgrad(w.kind, inp["x"], inp["dy"], inp["mean"], inp["rstd"])
+    for groups in (1, 2):
+        dg, _ = fp32_wgrad(w.kind, x, dy, mu, rs, groups=groups)
+        with pytest.raises(parity.Mismatch):
+            parity.check_wgrad(torch.float32, torch.from_numpy(dg), rdg)
+        bg, _ = parity.wgrad_bounds(w.kind, inp["x"], inp["dy"], inp["mean"], inp["rstd"],
+                                    parity.depth_fused(w.M, groups))
+        assert bg["depth"] > parity.FP32_DEEP_SUM_DEPTH
+        s = parity.check_wgrad(torch.float32, torch.from_numpy(dg), rdg,
+                               extra=parity.fp32_deep_sum_extra(torch.float32, bg))
+        assert s["max_err_over_bound"] < 0.01
+    dg, _ = fp32_wgrad(w.kind, x, dy, mu, rs, groups=256)
+    assert parity.depth_fused(w.M, 256) <= parity.FP32_DEEP_SUM_DEPTH
+    parity.check_wgrad(torch.float32, torch.from_numpy(dg), rdg)
+    # the automatic plans of the named workloads stay within the depth
+    assert parity.depth_fused(128, 32) == 42 and parity.depth_fused(16384, 256) == 116
+    a = np.ones(3)
+    assert parity.fp32_deep_sum_extra(torch.float32, {"absum": a, "depth": 128}) is None
+    assert parity.fp32_deep_sum_extra(torch.bfloat16, {"absum": a, "depth": 500}) is None
+    assert parity.fp32_deep_sum_extra(torch.float32, {"absum": a, "depth": 129}) is not None
+
+
 def test_summation_depths():
     # the fused path: a group's rows, 16 row-lanes, a slice of groups, 16 slices
     assert parity.depth_fused(16384, 256) == 64 + 16 + 16 + 16 + 4
