@@ -170,6 +170,26 @@ int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok
     }
   }
   if (!S) return fail(why, "no kernel geometry covers N", NORM_BWD_ERR_UNSUPPORTED);
+  // Widths that waves of kPreferredLaneBytes lanes cover exactly, with a wave
+  // count that is not a power of two (5120 16-bit elements: 5 waves of 32
+  // bytes a lane), take that count: no idle lanes, and the rows run the
+  // steady-state loop. Kernel A, bf16 RMSNorm, fraction of 8 TB/s (power of
+  // two with idle lanes -> exact): 16384 x 5120 0.697 -> 0.762 (LayerNorm
+  // 0.634 -> 0.723), x 3072 0.695 -> 0.737, x 7168 0.738 -> 0.756, x 6144
+  // 0.746 -> 0.753; 8192 x 12288 0.732 -> 0.746. (An exact layout of 16-byte
+  // lanes was slower: 65536 x 1536, 3 waves of one chunk, 0.720 -> 0.709, so
+  // only the preferred lane size counts.)
+  if (full && (int64_t)S * 64 * p->vec * C != N) {
+    const int c = kPreferredLaneBytes / (p->vec * eb);
+    const int64_t per_wave = (int64_t)64 * p->vec * c;
+    if (c >= 1 && kernel_a_exists(io_dtype, full, with_dbeta, c) && N % per_wave == 0) {
+      const int64_t s = N / per_wave;
+      if (s >= 1 && s <= 16 && s * 64 <= kernel_a_max_threads(p->vec * c)) {
+        S = (int)s;
+        C = c;
+      }
+    }
+  }
   // Rows in flight: the kernels that compute row statistics fill
   // kRowStatsThreads; kernel A with saved statistics takes the fewest rows
   // whose x and dy reach kRowBytesInFlight.

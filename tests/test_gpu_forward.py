@@ -239,6 +239,26 @@ def test_forward_rows_do_not_depend_on_the_launch(nb, kind, dt, M, m, N):
     check(W.scaled(w, M=64), inp["x"][rows], inp["gamma"], beta, got)
 
 
+@pytest.mark.parametrize("kind,dt,M,N", [
+    ("rmsnorm", torch.bfloat16, 700, 5120), ("layernorm", torch.bfloat16, 300, 7168),
+    ("layernorm", torch.float16, 513, 3072), ("rmsnorm", torch.float32, 333, 1536),
+    ("layernorm", torch.bfloat16, 4100, 5120)])      # 1024 threads of rows in flight
+def test_forward_exact_non_power_of_two_waves(nb, kind, dt, M, N):
+    """The forward on the widths whose rows take 3, 5 or 7 waves."""
+    base = W.LN_BF16_65536x8192 if kind == "layernorm" else W.RMS_BF16_16384x4096
+    w = W.scaled(base, M=M, N=N, io_dtype=dt)
+    inp = W.make_inputs(w)
+    x, g = inp["x"].cuda(), inp["gamma"].cuda()
+    beta = _beta(w, inp)
+    if kind == "layernorm":
+        got = nb.norm_fwd_layernorm(x, g, beta.cuda(), w.eps)
+    else:
+        y, r = nb.norm_fwd_rmsnorm(x, g, w.eps)
+        got = (y, None, r)
+    torch.cuda.synchronize()
+    check(w, inp["x"], inp["gamma"], beta, tuple(None if t is None else t.cpu() for t in got))
+
+
 def test_forward_misaligned_rows_take_the_scalar_path(nb):
     w = W.scaled(W.RMS_BF16_16384x4096, M=37, N=1000)
     inp = W.make_inputs(w)

@@ -191,6 +191,32 @@ def test_general_loop_two_rows_in_flight(nb, kind, dt, M, N, groups):
     compare_full(w, inp, one, with_db, groups=groups)
 
 
+@pytest.mark.parametrize("kind,dt,M,N,groups", [
+    ("rmsnorm", torch.bfloat16, 1001, 5120, 0),
+    ("layernorm", torch.bfloat16, 777, 5120, 0),
+    ("rmsnorm", torch.float16, 513, 3072, 0),
+    ("layernorm", torch.bfloat16, 300, 7168, 0),
+    ("rmsnorm", torch.bfloat16, 257, 12288, 0),
+    ("layernorm", torch.float32, 301, 5120, 0),
+    ("rmsnorm", torch.float32, 333, 1536, 0),
+    ("layernorm", torch.float16, 1000, 6144, 0),
+    ("layernorm", torch.bfloat16, 601, 5120, 2),   # general loop, two rows in flight
+])
+def test_exact_non_power_of_two_waves(nb, kind, dt, M, N, groups):
+    """Widths that waves of 32-byte lanes cover exactly run 3, 5, 6, 7, 10 or
+    12 waves per row: the row exchange sums that many wave partials in order,
+    and the results match the oracle."""
+    base = W.LN_BF16_65536x8192 if kind == "layernorm" else W.RMS_BF16_16384x4096
+    w = W.scaled(base, M=M, N=N, io_dtype=dt)
+    with_db = kind == "layernorm"
+    p = nb.norm_bwd_make_plan(kind, M, N, dt, with_db, groups)
+    S = p.waves_per_row
+    assert S & (S - 1) != 0 and S * 64 * p.vec * p.chunks == N
+    inp = backward_inputs(w)
+    out = run(nb, w, to_gpu(inp), plan=p if groups else None)
+    compare_full(w, inp, out, with_db, groups=groups or None)
+
+
 @pytest.mark.parametrize("kind", ["layernorm", "rmsnorm"])
 @pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16])
 def test_wgrad_in_io_dtype(nb, kind, dt):

@@ -112,6 +112,18 @@ def test_recompute_edge_shapes(nb, kind, dt, M, N):
     compare(w, inp["x"], inp["dy"], inp["gamma"], out, with_db)
 
 
+@pytest.mark.parametrize("kind,dt,M,N", [
+    ("rmsnorm", torch.bfloat16, 700, 5120), ("layernorm", torch.bfloat16, 300, 7168),
+    ("layernorm", torch.float16, 513, 3072), ("rmsnorm", torch.float32, 333, 1536)])
+def test_recompute_exact_non_power_of_two_waves(nb, kind, dt, M, N):
+    base = W.LN_F32_128x512 if kind == "layernorm" else W.RMS_F32_128x512
+    w = W.scaled(base, M=M, N=N, io_dtype=dt, wgrad_dtype=torch.float32, seed=700 + N)
+    inp = W.make_inputs(w)
+    with_db = kind == "layernorm"
+    out = run_recompute(nb, w, inp["x"], inp["dy"], inp["gamma"], with_db)
+    compare(w, inp["x"], inp["dy"], inp["gamma"], out, with_db)
+
+
 def test_recompute_constant_rows(nb):
     """A constant LayerNorm row has var = 0: rstd = 1/sqrt(eps), xhat = 0, so
     dx = rstd * (dyhat - mean(dyhat)) and its dgamma terms vanish."""
@@ -173,7 +185,10 @@ def recompute_plan(nb, kind, M, N, dt, db):
                                # groups ending on inactive rows
                                W.scaled(W.LN_BF16_65536x8192, M=2001, N=4096),
                                # the fp16 kernel that keeps the two-exchange order
-                               W.LN_F16_1151x8192],
+                               W.LN_F16_1151x8192,
+                               # 5 and 3 waves per row
+                               W.scaled(W.RMS_BF16_16384x4096, M=700, N=5120),
+                               W.scaled(W.LN_BF16_65536x8192, M=500, N=3072)],
                          ids=lambda w: w.name)
 def test_recompute_matches_forward_statistics_bitwise(nb, w):
     """The forward and recompute mode share the lane layout, so the

@@ -100,7 +100,7 @@ def _row_stats_rows(p, db):
     P = max(1, 512 // (64 * S))
     while P > 1 and S * P * 64 > (512 if vec * C > 16 else 1024):
         P //= 2
-    if P > 1 and (2 if db else 1) * S * C * 64 * vec * 4 > 65536 - 1024:
+    if P > 1 and S * C * 64 * vec * 4 > 65536 - 1024:    # one combine plane
         P = 1
     return P
 
@@ -282,6 +282,31 @@ def test_general_loop_groups_take_two_rows(nb):
     # fp32 rows of 8192 need 16 waves: a second row would exceed 16 waves
     p = nb.norm_bwd_make_plan("rmsnorm", 65536, 8192, torch.float32, False)
     assert (p.waves_per_row, p.rows_in_flight) == (16, 1)
+
+
+@pytest.mark.parametrize("dt,N,S", [
+    (torch.bfloat16, 3072, 3), (torch.bfloat16, 5120, 5), (torch.float16, 6144, 6),
+    (torch.bfloat16, 7168, 7), (torch.bfloat16, 10240, 10), (torch.bfloat16, 12288, 12),
+    (torch.bfloat16, 14336, 14), (torch.float32, 1536, 3), (torch.float32, 5120, 10),
+    (torch.float32, 7168, 14)])
+@pytest.mark.parametrize("kind,db", [("rmsnorm", False), ("layernorm", True)])
+def test_exact_wave_counts(nb, kind, db, dt, N, S):
+    """Widths that waves of 32-byte lanes cover exactly take that many waves,
+    a power of two or not: no idle lanes."""
+    p = nb.norm_bwd_make_plan(kind, 4096, N, dt, db)
+    eb = torch.tensor([], dtype=dt).element_size()
+    assert p.rows_per_wave == 1 and p.vec * p.chunks * eb == 32
+    assert p.waves_per_row == S and S * 64 * p.vec * p.chunks == N
+
+
+@pytest.mark.parametrize("N", [1536, 2560, 3584])
+def test_inexact_widths_keep_power_of_two_waves(nb, N):
+    """Widths that 32-byte lanes do not cover exactly keep the fewest
+    power-of-two waves that cover them."""
+    p = nb.norm_bwd_make_plan("rmsnorm", 4096, N, torch.bfloat16, False)
+    S = p.waves_per_row
+    assert S & (S - 1) == 0 and S * 64 * p.vec * p.chunks > N
+    assert (S // 2) * 64 * p.vec * p.chunks < N
 
 
 def test_groups_do_not_depend_on_device(nb):
