@@ -21,6 +21,10 @@ constexpr int64_t kSavedStatsGroups = 256;
 // 262144 x 768 218.5 us at 8, 229.6 us at 4; 16384 x 4096 69.2 us at 1,
 // 69.9 us at 2).
 constexpr int64_t kRowBytesInFlight = 16384;
+// The same for RMSNorm rows laid out on 16-byte lanes (one chunk): 65536 x
+// 1536 bf16 best at 2 rows (12 KiB; 4 rows 0.714, 2 rows 0.759 of 8 TB/s),
+// 32768 x 3584 at 1 row (14 KiB; 114.0 against 119.6 us at 2).
+constexpr int64_t kRowBytesInFlight16 = 12288;
 // Groups that sweep more than this many bytes of each operand run kernel A's
 // general loop rather than its steady-state loop (the kernel holds the same
 // bound). There one row in flight leaves HBM idle between rows, and two rows
@@ -134,7 +138,7 @@ static int combine_lds_bytes(int S, int C, int vec) { return S * C * 64 * vec * 
 // Lane layout of kernel A for rows of N elements (fills vec, chunks,
 // waves_per_row, rows_in_flight, threads, lds_bytes of *p).
 int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok16,
-                  norm_bwd_plan_t* p, const char** why, bool row_stats, bool two_row_ok) {
+                  norm_bwd_plan_t* p, const char** why, bool row_stats, bool saved_stats) {
   const int eb = dtype_bytes(io_dtype);
   const int nacc = with_dbeta ? 2 : 1;
   const int vw = 16 / eb;
@@ -176,9 +180,7 @@ int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok
   // steady-state loop. Kernel A, bf16 RMSNorm, fraction of 8 TB/s (power of
   // two with idle lanes -> exact): 16384 x 5120 0.697 -> 0.762 (LayerNorm
   // 0.634 -> 0.723), x 3072 0.695 -> 0.737, x 7168 0.738 -> 0.756, x 6144
-  // 0.746 -> 0.753; 8192 x 12288 0.732 -> 0.746. (An exact layout of 16-byte
-  // lanes was slower: 65536 x 1536, 3 waves of one chunk, 0.720 -> 0.709, so
-  // only the preferred lane size counts.)
+  // 0.746 -> 0.753; 8192 x 12288 0.732 -> 0.746.
   if (full && (int64_t)S * 64 * p->vec * C != N) {
     const int c = kPreferredLaneBytes / (p->vec * eb);
     const int64_t per_wave = (int64_t)64 * p->vec * c;
@@ -190,15 +192,43 @@ int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok
       }
     }
   }
+  // Widths that 32-byte lanes cannot cover exactly but 16-byte lanes can,
+  // with an odd wave count (1536, 2560, 3584 16-bit elements: 3, 5, 7 waves
+  // of one chunk), take that layout too. Paired on the same buffers over ten
+  // placements, bf16, A + B (power of two with idle lanes -> exact):
+  // RMSNorm 65536 x 1536 106.4 -> 102.1 us (2 rows in flight), 32768 x 2560
+  // 92.3 -> 88.0 us (2 rows), 32768 x 3584 120.7 -> 114.0 us (1 row; 119.6
+  // with 2); LayerNorm 32768 x 2560 99.9 -> 91.1 us, 32768 x 3584 124.7 ->
+  // 121.3 us (2 rows each). RMSNorm with saved statistics takes the fewest
+  // rows whose x and dy reach kRowBytesInFlight16; LayerNorm keeps
+  // kRowBytesInFlight and takes the layout only where that means at most two
+  // rows: 65536 x 1536 LayerNorm was slower with it (109.2 -> 114.2 us with 2
+  // rows; 1 row far slower still). The forward and recompute mode share the
+  // layout (their row sums then run in one order) with their own rows in
+  // flight.
+  bool exact16 = false;
+  if (full && (int64_t)S * 64 * p->vec * C != N && kernel_a_exists(io_dtype, full, with_dbeta, 1)) {
+    const int64_t per_wave = (int64_t)64 * p->vec;
+    const int64_t s = N % per_wave == 0 ? N / per_wave : 0;
+    const bool rows_ok = kind == NORM_BWD_RMSNORM || 2 * (2 * N * eb) >= kRowBytesInFlight;
+    if (s >= 1 && s <= 16 && rows_ok) {
+      S = (int)s;
+      C = 1;
+      exact16 = true;
+    }
+  }
   // Rows in flight: the kernels that compute row statistics fill
   // kRowStatsThreads; kernel A with saved statistics takes the fewest rows
-  // whose x and dy reach kRowBytesInFlight.
+  // whose x and dy reach kRowBytesInFlight (kRowBytesInFlight16 for RMSNorm
+  // on 16-byte lanes).
   int P = 1;
   if (row_stats) {
     P = kRowStatsThreads / (64 * S);
     if (P < 1) P = 1;
   } else {
-    while (P < 16 && (int64_t)P * 2 * N * eb < kRowBytesInFlight) P *= 2;
+    const int64_t target = exact16 && saved_stats && kind == NORM_BWD_RMSNORM
+                               ? kRowBytesInFlight16 : kRowBytesInFlight;
+    while (P < 16 && (int64_t)P * 2 * N * eb < target) P *= 2;
     while (P > 1 && S * P > 16) P /= 2;
   }
   while (P > 1 && S * P * 64 > kernel_a_max_threads(p->vec * C)) P /= 2;
@@ -213,7 +243,7 @@ int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok
   // saved statistics), for RMSNorm: LayerNorm, with its second row sum, gained
   // nothing from it (131072 x 768 bf16 with dbeta: 115.5 us with one row per
   // wave, 115.7 us at best with two), so it keeps one row per wave.
-  const int c2 = (two_row_ok && !row_stats && full && kind == NORM_BWD_RMSNORM)
+  const int c2 = (saved_stats && !row_stats && full && kind == NORM_BWD_RMSNORM)
                      ? two_row_chunks(N, io_dtype) : 0;
   if (c2) {
     int P2 = 2;
@@ -270,6 +300,9 @@ bool stream_workspace(size_t bytes) { return bytes >= kStreamWorkspaceBytes; }
 int64_t forward_grid(int64_t M, int S, int P) {
   if (M <= 0) return 0;
   int64_t g = kForwardTargetWaves / (S * P);
+  // wave counts that are not powers of two would leave a partial second
+  // round of workgroups (14 waves: 292): whole multiples of 256 instead
+  if (g > kGroupQuantum) g -= g % kGroupQuantum;
   const int64_t sweep = ceil_div(M, P);
   if (g > sweep) g = sweep;
   if (g > kMaxGrid) g = kMaxGrid;

@@ -26,11 +26,13 @@ int kernel_a_max_threads(int lane_elems);
 // statistics or, with `row_stats`, for the kernels that compute row
 // statistics (the forward, kernel A in recompute mode): the lane layout is
 // the same, the rows in flight differ. Returns a status.
-// `two_row_ok`: the caller can run the two-rows-per-wave kernel (saved
-// statistics); RMSNorm rows it covers exactly then take that layout.
+// `saved_stats`: the plan is for kernel A with saved statistics, which can
+// run the two-rows-per-wave kernel (RMSNorm rows 32 lanes cover exactly then
+// take that layout) and has its own rows-in-flight target for RMSNorm rows
+// on 16-byte lanes.
 int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok16,
                   norm_bwd_plan_t* plan, const char** why, bool row_stats,
-                  bool two_row_ok = false);
+                  bool saved_stats = false);
 
 // The two-rows-per-wave layout for rows of N elements: its chunk count (1 or
 // 3) when 32 lanes of 16-byte vectors cover N exactly and 64-lane waves would
@@ -66,8 +68,8 @@ bool stream_workspace(size_t bytes);
 int64_t rowloop_grid(int64_t M);
 
 // Workgroups of the forward kernel for M rows with S waves per row and P rows
-// in flight: enough for about 4096 waves (16 per compute unit), at most one
-// sweep of rows.
+// in flight: enough for about 4096 waves (16 per compute unit), above 256 a
+// multiple of 256, at most one sweep of rows.
 int64_t forward_grid(int64_t M, int S, int P);
 
 // Rows in flight of the forward for M rows, given the row-statistics

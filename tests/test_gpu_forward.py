@@ -242,7 +242,9 @@ def test_forward_rows_do_not_depend_on_the_launch(nb, kind, dt, M, m, N):
 @pytest.mark.parametrize("kind,dt,M,N", [
     ("rmsnorm", torch.bfloat16, 700, 5120), ("layernorm", torch.bfloat16, 300, 7168),
     ("layernorm", torch.float16, 513, 3072), ("rmsnorm", torch.float32, 333, 1536),
-    ("layernorm", torch.bfloat16, 4100, 5120)])      # 1024 threads of rows in flight
+    ("layernorm", torch.bfloat16, 4100, 5120),       # 1024 threads of rows in flight
+    ("rmsnorm", torch.bfloat16, 2001, 1536), ("layernorm", torch.bfloat16, 777, 2560),
+    ("rmsnorm", torch.float16, 5000, 3584)])          # 16-byte lanes
 def test_forward_exact_non_power_of_two_waves(nb, kind, dt, M, N):
     """The forward on the widths whose rows take 3, 5 or 7 waves."""
     base = W.LN_BF16_65536x8192 if kind == "layernorm" else W.RMS_BF16_16384x4096

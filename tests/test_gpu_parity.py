@@ -201,11 +201,20 @@ def test_general_loop_two_rows_in_flight(nb, kind, dt, M, N, groups):
     ("rmsnorm", torch.float32, 333, 1536, 0),
     ("layernorm", torch.float16, 1000, 6144, 0),
     ("layernorm", torch.bfloat16, 601, 5120, 2),   # general loop, two rows in flight
+    # 16-byte lanes, one chunk: 3, 5, 7, 9 waves per row
+    ("rmsnorm", torch.bfloat16, 2001, 1536, 0),
+    ("rmsnorm", torch.float16, 1001, 2560, 0),
+    ("layernorm", torch.bfloat16, 777, 2560, 0),
+    ("rmsnorm", torch.bfloat16, 1001, 3584, 0),
+    ("layernorm", torch.float16, 513, 3584, 0),
+    ("rmsnorm", torch.bfloat16, 300, 4608, 0),
+    ("layernorm", torch.float32, 701, 1280, 0),
+    ("rmsnorm", torch.bfloat16, 1201, 3584, 2),    # general loop, two rows in flight
 ])
 def test_exact_non_power_of_two_waves(nb, kind, dt, M, N, groups):
-    """Widths that waves of 32-byte lanes cover exactly run 3, 5, 6, 7, 10 or
-    12 waves per row: the row exchange sums that many wave partials in order,
-    and the results match the oracle."""
+    """Widths that waves of 32-byte (or, failing that, 16-byte) lanes cover
+    exactly run 3 to 12 waves per row: the row exchange sums that many wave
+    partials in order, and the results match the oracle."""
     base = W.LN_BF16_65536x8192 if kind == "layernorm" else W.RMS_BF16_16384x4096
     w = W.scaled(base, M=M, N=N, io_dtype=dt)
     with_db = kind == "layernorm"

@@ -114,7 +114,9 @@ def test_recompute_edge_shapes(nb, kind, dt, M, N):
 
 @pytest.mark.parametrize("kind,dt,M,N", [
     ("rmsnorm", torch.bfloat16, 700, 5120), ("layernorm", torch.bfloat16, 300, 7168),
-    ("layernorm", torch.float16, 513, 3072), ("rmsnorm", torch.float32, 333, 1536)])
+    ("layernorm", torch.float16, 513, 3072), ("rmsnorm", torch.float32, 333, 1536),
+    ("rmsnorm", torch.bfloat16, 1001, 1536), ("layernorm", torch.bfloat16, 300, 2560),
+    ("rmsnorm", torch.float16, 600, 3584)])
 def test_recompute_exact_non_power_of_two_waves(nb, kind, dt, M, N):
     base = W.LN_F32_128x512 if kind == "layernorm" else W.RMS_F32_128x512
     w = W.scaled(base, M=M, N=N, io_dtype=dt, wgrad_dtype=torch.float32, seed=700 + N)
@@ -167,6 +169,19 @@ def recompute_plan(nb, kind, M, N, dt, db):
 
     base = nb.norm_bwd_make_plan(kind, M, N, dt, db)
     if kind == "rmsnorm":
+        # the saved-statistics rules, except that rows on 16-byte lanes with
+        # an odd wave count aim at 16 KiB of x and dy in flight, not 12 KiB
+        S, C, vec, eb = base.waves_per_row, base.chunks, base.vec, dt.itemsize
+        if base.rows_per_wave == 1 and C == 1 and S > 1 and S % 2 and S * 64 * vec == N:
+            P = 1
+            while P < 16 and P * 2 * N * eb < 16384:
+                P *= 2
+            while P > 1 and (S * P > 16 or S * P * 64 > 1024):
+                P //= 2
+            p = base.copy()
+            p.rows_in_flight, p.threads = P, 64 * S * P
+            p.lds_bytes = S * C * 64 * vec * 4 if P > 1 else 0
+            return p
         return base
     S, C, vec = base.waves_per_row, base.chunks, base.vec
     G = min(4096 // (S * rows(S, C, vec)), -(-M // 4))
@@ -188,7 +203,10 @@ def recompute_plan(nb, kind, M, N, dt, db):
                                W.LN_F16_1151x8192,
                                # 5 and 3 waves per row
                                W.scaled(W.RMS_BF16_16384x4096, M=700, N=5120),
-                               W.scaled(W.LN_BF16_65536x8192, M=500, N=3072)],
+                               W.scaled(W.LN_BF16_65536x8192, M=500, N=3072),
+                               # 7 waves of 16-byte lanes
+                               W.scaled(W.RMS_BF16_16384x4096, M=900, N=3584),
+                               W.scaled(W.LN_BF16_65536x8192, M=400, N=3584)],
                          ids=lambda w: w.name)
 def test_recompute_matches_forward_statistics_bitwise(nb, w):
     """The forward and recompute mode share the lane layout, so the

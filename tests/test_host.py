@@ -209,8 +209,12 @@ def test_plan_invariants(nb, kind, dt, M, N, db, groups):
     # the same limits allow it
     max_thr = 512 if vec * C > 16 else 1024
     plane = S * C * 64 * vec * 4
+    # RMSNorm rows laid out on 16-byte lanes with an odd wave count (no
+    # exact 32-byte layout exists) aim at 12 KiB of x and dy in flight
+    exact16 = (kind == "rmsnorm" and C == 1 and vec == vw and S * 64 * vec == N
+               and S % 2 == 1 and S > 1)
     want = 1
-    while want < 16 and want * 2 * N * eb < 16384:
+    while want < 16 and want * 2 * N * eb < (12288 if exact16 else 16384):
         want *= 2
     while want > 1 and (S * want > 16 or S * want * 64 > max_thr):
         want //= 2
@@ -299,11 +303,29 @@ def test_exact_wave_counts(nb, kind, db, dt, N, S):
     assert p.waves_per_row == S and S * 64 * p.vec * p.chunks == N
 
 
-@pytest.mark.parametrize("N", [1536, 2560, 3584])
-def test_inexact_widths_keep_power_of_two_waves(nb, N):
-    """Widths that 32-byte lanes do not cover exactly keep the fewest
-    power-of-two waves that cover them."""
-    p = nb.norm_bwd_make_plan("rmsnorm", 4096, N, torch.bfloat16, False)
+@pytest.mark.parametrize("kind,db,dt,N,S,P", [
+    ("rmsnorm", False, torch.bfloat16, 1536, 3, 2), ("rmsnorm", False, torch.bfloat16, 2560, 5, 2),
+    ("rmsnorm", False, torch.bfloat16, 3584, 7, 1), ("rmsnorm", False, torch.float16, 4608, 9, 1),
+    ("layernorm", True, torch.bfloat16, 2560, 5, 2), ("layernorm", True, torch.bfloat16, 3584, 7, 2),
+    ("rmsnorm", False, torch.float32, 1280, 5, 2), ("layernorm", True, torch.float32, 1280, 5, 2)])
+def test_exact_sixteen_byte_lanes(nb, kind, db, dt, N, S, P):
+    """Widths that 32-byte lanes cannot cover exactly but 16-byte lanes can,
+    with an odd wave count, take one chunk per lane; RMSNorm aims at 12 KiB
+    of rows in flight, LayerNorm keeps 16 KiB and takes the layout only at
+    two rows or fewer."""
+    p = nb.norm_bwd_make_plan(kind, 32768, N, dt, db)
+    assert p.rows_per_wave == 1 and p.chunks == 1 and p.waves_per_row == S
+    assert S * 64 * p.vec == N and p.rows_in_flight == P
+
+
+@pytest.mark.parametrize("kind,dt,N", [("rmsnorm", torch.bfloat16, 1280),
+                                       ("layernorm", torch.bfloat16, 1280),
+                                       ("layernorm", torch.bfloat16, 1536),
+                                       ("layernorm", torch.float32, 768)])
+def test_inexact_widths_keep_power_of_two_waves(nb, kind, dt, N):
+    """Widths no exact layout covers (or, for LayerNorm, only one with more
+    than two rows in flight) keep the fewest power-of-two waves."""
+    p = nb.norm_bwd_make_plan(kind, 4096, N, dt, kind == "layernorm")
     S = p.waves_per_row
     assert S & (S - 1) == 0 and S * 64 * p.vec * p.chunks > N
     assert (S // 2) * 64 * p.vec * p.chunks < N
