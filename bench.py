@@ -87,6 +87,10 @@ def parse_args(argv=None):
     ap.add_argument("--triad-policies", action="store_true",
                     help="also sweep the triad over every load/store cache policy, at 512 MiB "
                          "and at the first workload's x size (config.triad_policies)")
+    ap.add_argument("--widths", default=None,
+                    help="also time bf16 RMSNorm and LayerNorm at these row widths (comma "
+                         "separated), about 64M elements per operand each "
+                         "(config.widths)")
     ap.add_argument("--placements", type=int, default=0,
                     help="also time the workload over this many seeded random placements of its "
                          "operands, with the triad on the same buffers (config.workloads[]."
@@ -991,6 +995,23 @@ def main(argv=None) -> int:
         cpu_inputs[w.name] = inp
         print(f"bench.py: {w.name} step {e['step_us']} us", file=sys.stderr, flush=True)
 
+    # row widths of common models: the lane layout the planner takes for each
+    width_entries = []
+    if args.widths:
+        for n in (int(v) for v in args.widths.split(",") if v):
+            m = max(256, (64 << 20) // n)
+            for kind, base in (("rmsnorm", W.HEADLINE), ("layernorm", W.LN_BF16_65536x8192)):
+                w = W.scaled(base, M=m, N=n, name=f"{kind}_bf16_{m}x{n}")
+                e, _, _ = measure_workload(torch, nb, W, lib, dev, stream, w, args,
+                                           max(args.steps, 200), max(args.warmup, 50), False,
+                                           triad)
+                width_entries.append({k: e.get(k) for k in (
+                    "workload", "kind", "M", "N", "step_us", "GBps", "pct_of_peak",
+                    "kernel_a_us", "kernel_a_frac", "kernel_a_pct_of_triad_same_bytes",
+                    "plan")})
+                print(f"bench.py: {w.name} step {e['step_us']} us, kernel A "
+                      f"{e['kernel_a_frac']} of 8 TB/s", file=sys.stderr, flush=True)
+
     # the CPU oracle on the same inputs (after every GPU measurement)
     if not args.no_cpu_baseline:
         for name, e in entries.items():
@@ -1022,6 +1043,8 @@ def main(argv=None) -> int:
     }
     config.update(extras)
     config["workloads"] = [entries[n] for n in order]
+    if width_entries:
+        config["widths"] = width_entries
     result = {
         "metric": METRIC,
         "value": e["GBps"],

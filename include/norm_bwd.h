@@ -322,11 +322,11 @@ typedef struct norm_bwd_plan {
  * rows in flight per workgroup are the fewest whose x and dy reach 16 KiB,
  * and at least two where a group holds more than 2 MiB of each operand
  * (rows_per_group * N * element size), as far as 16 waves, the kernel's
- * launch bound and 63 KiB of LDS allow. RMSNorm rows that 64-lane waves would
- * cover with idle lanes and 32 lanes cover exactly (N = 32 * vec * 1 or 3:
- * 256 or 768 16-bit, 128 or 384 fp32 elements) take two rows per wave
- * instead, with the fewest rows in flight whose x and dy reach 8 KiB. A plan
- * is for saved statistics. The plan assumes 16-byte aligned base pointers;
+ * launch bound and 63 KiB of LDS allow. Rows that 64-lane waves would cover
+ * with idle lanes and 32 lanes cover exactly (N = 32 * vec * 1 or 3: 256 or
+ * 768 16-bit, 128 or 384 fp32 elements) take two rows per wave instead, with
+ * the fewest rows in flight whose x and dy reach 8 KiB (RMSNorm) or 16 KiB
+ * (LayerNorm). A plan is for saved statistics. The plan assumes 16-byte aligned base pointers;
  * norm_bwd_execute rejects a plan whose vec the pointers do not allow.
  * Host-only. Returns a status code.
  */

@@ -76,6 +76,13 @@ constexpr int kTwoRowMaxThreads = 512;
 // rows (8: 220.9, 16: 231.1); 1048576 x 256 317.5 against 285.7 at 8 rows
 // (4: 411.4, 16: 309.6). Rings deeper than 3 row pairs were slower.
 constexpr int64_t kTwoRowBytesInFlight = 8192;
+// LayerNorm, with its second row sum, needs more rows in flight on that
+// layout: paired on the same buffers over six placements, A + B, against one
+// row per wave (64 lanes with idle lanes): 87381 x 768 bf16 78.7 -> 76.5 us
+// at 8 rows (4: 83.8, 16: 81.6), 262144 x 768 224.8 -> 219.0 us (4: 233.6),
+// 131072 x 768 fp16 116.1 -> 111.8 us (4: 129.4, 16: 119.1); 262144 x 256
+// bf16 88.6 -> 74.2 us at 16 rows (8: 74.6).
+constexpr int64_t kTwoRowBytesInFlightLN = 16384;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -240,15 +247,13 @@ int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok
   p->threads = 64 * S * P;
   p->lds_bytes = lds;
   // Two rows per wave where 32 lanes cover the row exactly (kernel A with
-  // saved statistics), for RMSNorm: LayerNorm, with its second row sum, gained
-  // nothing from it (131072 x 768 bf16 with dbeta: 115.5 us with one row per
-  // wave, 115.7 us at best with two), so it keeps one row per wave.
-  const int c2 = (saved_stats && !row_stats && full && kind == NORM_BWD_RMSNORM)
-                     ? two_row_chunks(N, io_dtype) : 0;
+  // saved statistics).
+  const int c2 = (saved_stats && !row_stats && full) ? two_row_chunks(N, io_dtype) : 0;
   if (c2) {
+    const int64_t target =
+        kind == NORM_BWD_LAYERNORM ? kTwoRowBytesInFlightLN : kTwoRowBytesInFlight;
     int P2 = 2;
-    while (P2 * 32 < kTwoRowMaxThreads && (int64_t)P2 * 2 * N * eb < kTwoRowBytesInFlight)
-      P2 *= 2;
+    while (P2 * 32 < kTwoRowMaxThreads && (int64_t)P2 * 2 * N * eb < target) P2 *= 2;
     p->rows_per_wave = 2;
     p->chunks = c2;
     p->waves_per_row = 1;

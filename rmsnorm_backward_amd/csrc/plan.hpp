@@ -27,9 +27,9 @@ int kernel_a_max_threads(int lane_elems);
 // statistics (the forward, kernel A in recompute mode): the lane layout is
 // the same, the rows in flight differ. Returns a status.
 // `saved_stats`: the plan is for kernel A with saved statistics, which can
-// run the two-rows-per-wave kernel (RMSNorm rows 32 lanes cover exactly then
-// take that layout) and has its own rows-in-flight target for RMSNorm rows
-// on 16-byte lanes.
+// run the two-rows-per-wave kernel (rows 32 lanes cover exactly then take
+// that layout) and has its own rows-in-flight target for RMSNorm rows on
+// 16-byte lanes.
 int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok16,
                   norm_bwd_plan_t* plan, const char** why, bool row_stats,
                   bool saved_stats = false);

@@ -65,8 +65,7 @@ int main() {
                   EXPECT(p.vec == 1 || (N * eb) % 16 == 0, "vector rows");
                   if (p.rows_per_wave == 2) {
                     // two rows per wave: 32 lanes cover the row exactly
-                    EXPECT(kind == NORM_BWD_RMSNORM && !rc && p.vec == 16 / eb,
-                           "two-row layout for RMSNorm with saved statistics");
+                    EXPECT(!rc && p.vec == 16 / eb, "two-row layout with saved statistics");
                     EXPECT((int64_t)32 * p.vec * p.chunks == N &&
                                (p.chunks == 1 || p.chunks == 3),
                            "two-row coverage");

@@ -184,13 +184,14 @@ def test_plan_invariants(nb, kind, dt, M, N, db, groups):
     assert vec in (1, 16 // eb) and (vec == 1 or N % vec == 0)
     nacc = 2 if db else 1
     vw = 16 // eb
-    # RMSNorm rows that 64-lane waves would cover with idle lanes and 32 lanes
-    # cover exactly (N = 32 * vw * 1 or 3) take two rows per wave
+    # rows that 64-lane waves would cover with idle lanes and 32 lanes cover
+    # exactly (N = 32 * vw * 1 or 3) take two rows per wave, with 8 KiB
+    # (RMSNorm) or 16 KiB (LayerNorm) of x and dy in flight
     c2 = next((c for c in (1, 3) if N == c * 32 * vw), 0) if N % (64 * vw) else 0
-    if c2 and kind == "rmsnorm":
+    if c2:
         assert p.rows_per_wave == 2 and vec == vw and S == 1 and C == c2
         want = 2
-        while want * 32 < 512 and want * 2 * N * eb < 8192:
+        while want * 32 < 512 and want * 2 * N * eb < (16384 if kind == "layernorm" else 8192):
             want *= 2
         assert P == want and p.threads == 32 * P
         assert p.lds_bytes == (nacc * C * 32 * vec * 4 if P > 2 else 0)
