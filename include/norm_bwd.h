@@ -326,7 +326,8 @@ typedef struct norm_bwd_plan {
  * with idle lanes and 32 lanes cover exactly (N = 32 * vec * 1 or 3: 256 or
  * 768 16-bit, 128 or 384 fp32 elements) take two rows per wave instead, with
  * the fewest rows in flight whose x and dy reach 8 KiB (RMSNorm) or 16 KiB
- * (LayerNorm). A plan is for saved statistics. The plan assumes 16-byte aligned base pointers;
+ * (LayerNorm; recompute mode: 16 KiB in both kinds, and LayerNorm
+ * recompute keeps 256 groups there). A plan is for saved statistics. The plan assumes 16-byte aligned base pointers;
  * norm_bwd_execute rejects a plan whose vec the pointers do not allow.
  * Host-only. Returns a status code.
  */
@@ -381,6 +382,10 @@ int norm_bwd_reduce_partials(int64_t groups, int64_t N, int wgrad_dtype,
  *   x [M,N], gamma [N], beta [N] or NULL (read, io_dtype)
  *   y [M,N] io_dtype (written); mean, rstd fp32 [M] (written; either may be
  *   NULL to skip it)
+ * The row sums run on the backward's lane layout for N, so that recompute
+ * mode (same x, same eps, 16-byte aligned pointers in both calls) forms the
+ * statistics this forward stores bit for bit; widths of the two-rows-per-wave
+ * layout take it here too.
  * Any N up to INT32_MAX (wider than the fused limits without dbeta: the
  * row-loop forward, three passes over each row). Asynchronous on `stream`;
  * checked on the host first (status codes as above). Allocates nothing.

@@ -415,11 +415,19 @@ int run_forward(int kind, const void* x, const void* gamma, const void* beta, in
   f.N = (int)N;
   f.eps = eps;
   f.S = wide ? 0 : g.waves_per_row;
-  f.P = wide ? 0 : nb::forward_rows_in_flight(M, g.waves_per_row, g.rows_in_flight,
-                                              g.vec * g.chunks);
-  f.threads = wide ? 0 : 64 * f.S * f.P;
-  f.grid = wide ? (int)(f.chunks ? nb::rowreg_grid(M) : nb::rowloop_grid(M))
-                : (int)nb::forward_grid(M, f.S, f.P);
+  f.rows_per_wave = wide ? 1 : g.rows_per_wave;
+  if (f.rows_per_wave == 2) {
+    // two rows per wave: P waves of a row pair each, over ceil(M / 2) pairs
+    f.P = nb::forward_two_row_waves(M);
+    f.threads = 64 * f.P;
+    f.grid = (int)nb::forward_two_row_grid(M, f.P);
+  } else {
+    f.P = wide ? 0 : nb::forward_rows_in_flight(M, g.waves_per_row, g.rows_in_flight,
+                                                g.vec * g.chunks);
+    f.threads = wide ? 0 : 64 * f.S * f.P;
+    f.grid = wide ? (int)(f.chunks ? nb::rowreg_grid(M) : nb::rowloop_grid(M))
+                  : (int)nb::forward_grid(M, f.S, f.P);
+  }
   f.stream = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so a launch failure is ours
   hipError_t e;

@@ -45,6 +45,7 @@ struct LaunchF {
   int N;
   float eps;
   int S, P, threads, grid;
+  int rows_per_wave;  // 2: the two-rows-per-wave forward (nb_tworow.hpp), P = waves
   hipStream_t stream;
 };
 
@@ -109,6 +110,9 @@ hipError_t launch_a_recompute_bf16(const LaunchA& a);
 hipError_t launch_f_f32(const LaunchF& f);
 hipError_t launch_f_f16(const LaunchF& f);
 hipError_t launch_f_bf16(const LaunchF& f);
+hipError_t launch_f_tworow_f32(const LaunchF& f);
+hipError_t launch_f_tworow_f16(const LaunchF& f);
+hipError_t launch_f_tworow_bf16(const LaunchF& f);
 hipError_t launch_reduce(int wgrad_dtype, const float* ws, int64_t G, int N, void* dgamma,
                          void* dbeta, int accumulate, int ws_stream, hipStream_t stream);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);

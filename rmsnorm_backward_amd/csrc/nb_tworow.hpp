@@ -1,10 +1,13 @@
-// nb_tworow.hpp -- kernel A for rows that 32 lanes cover exactly with
-// 16-byte vectors (N = 32 * VEC * C, C = 1 or 3; for 16-bit elements 256 or
-// 768 features), with saved statistics. Such rows leave half the lanes of a
-// 64-lane layout idle in their last chunk and keep it out of the branch-free
+// nb_tworow.hpp -- kernel A and the forward for rows that 32 lanes cover
+// exactly with 16-byte vectors (N = 32 * VEC * C, C = 1 or 3; for 16-bit
+// elements 256 or 768 features). Such rows leave half the lanes of a 64-lane
+// layout idle in their last chunk and keep it out of the branch-free
 // steady-state loop; here every wave takes two rows at once, one per 32-lane
 // half, so every lane holds data and every load and store instruction moves
-// two 512-byte runs.
+// two 512-byte runs. Kernel A takes saved statistics or (RECOMP) recomputes
+// them; the forward computes them. Both compute a row's statistics with the
+// same helpers (lane sums in chunk order, then the half's butterfly), so
+// recompute mode sees the statistics the forward saved, bit for bit.
 //
 // What is computed is kernel A's (nb_device.hpp), from the same formulas of
 // "Norm backward in Triton -- the dγ/dβ reduction", "The gradients": dx per
@@ -45,6 +48,32 @@ __device__ __forceinline__ float half_sum(float v, bool hi) {
   return hi ? hi_sum : lo;
 }
 
+// A lane's part of a row's statistics, in the order the forward and
+// recompute mode share: sum(x), and sum((x - mu)^2) by fused multiply-adds,
+// chunk by chunk, element by element.
+template <class Tg, int VEC, int C>
+__device__ __forceinline__ float lane_sum_x(const Pack<Tg, VEC> (&x)[C]) {
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) s += x[c].get(v);
+  return s;
+}
+
+template <class Tg, int VEC, int C>
+__device__ __forceinline__ float lane_sum_sq(const Pack<Tg, VEC> (&x)[C], float mu) {
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      const float xc = x[c].get(v) - mu;
+      s = __builtin_fmaf(xc, xc, s);
+    }
+  return s;
+}
+
 constexpr int kTwoRowDepth = 3;         // ring of row pairs (two in flight)
 constexpr int kTwoRowMaxThreads = 512;  // launch bound: 256 VGPRs per lane
 
@@ -52,7 +81,7 @@ constexpr int kTwoRowMaxThreads = 512;  // launch bound: 256 VGPRs per lane
 // addresses them through one buffer resource based at its first row, the
 // second half adding `hoff` bytes (one row stride). Otherwise each lane loads
 // through its own address, and only when its row exists.
-template <int KIND, bool RALL, class Tg, int VEC, int C>
+template <int KIND, bool RECOMP, bool RALL, class Tg, int VEC, int C>
 __device__ __forceinline__ void fetch_pair(RowBuf<Tg, VEC, C>& b, const char* __restrict__ x,
                                            const char* __restrict__ dy,
                                            const float* __restrict__ mean,
@@ -62,9 +91,11 @@ __device__ __forceinline__ void fetch_pair(RowBuf<Tg, VEC, C>& b, const char* __
                                            int col0, int cstride) {
   constexpr int EB = Tg::kBytes;
   if (RALL || active) {
-    const int64_t rz = r + opaque_lane_zero();
-    b.rs = rstd[rz];
-    b.mu = (KIND == kLayerNorm) ? mean[rz] : 0.0f;
+    if constexpr (!RECOMP) {
+      const int64_t rz = r + opaque_lane_zero();
+      b.rs = rstd[rz];
+      b.mu = (KIND == kLayerNorm) ? mean[rz] : 0.0f;
+    }
     if constexpr (RALL) {
       const __amdgpu_buffer_rsrc_t rx = row_rsrc(x + r0 * ldx * EB, span_x);
       const __amdgpu_buffer_rsrc_t ry = row_rsrc(dy + r0 * ldy * EB, span_y);
@@ -87,38 +118,84 @@ __device__ __forceinline__ void fetch_pair(RowBuf<Tg, VEC, C>& b, const char* __
 
 // One row pair once its operands are in registers: the weight-gradient terms
 // into the accumulators, the half's row sums, then dx (RALL: through the
-// pair's buffer resource, as fetch_pair).
-template <int KIND, bool RALL, class Tg, int VEC, int C, int NACC>
+// pair's buffer resource, as fetch_pair). RECOMP: the statistics come from
+// the row itself, as kernel A's recompute mode forms them (LayerNorm: sum(x)
+// with sum(dyhat), then with mean = sum(x)/N sum((x - mean)^2) with
+// sum(dyhat * (x - mean)); RMSNorm: sum(x^2) with sum(dyhat * x)), and the
+// dgamma terms, which need rstd, join the dx pass. Every lane takes part in
+// each butterfly (rows that do not exist add zeros to sums nobody uses).
+template <int KIND, bool RECOMP, bool RALL, class Tg, int VEC, int C, int NACC>
 __device__ __forceinline__ void process_pair(RowBuf<Tg, VEC, C>& b, const float (&gam)[C][VEC],
                                              float (&acc)[NACC][C][VEC], char* __restrict__ dx,
                                              int64_t r0, int64_t r, bool active, bool hi,
                                              int64_t ldo, uint32_t hoff_o, uint32_t span_o,
-                                             float inv_n, int col0, int cstride) {
+                                             float inv_n, float eps, int col0, int cstride) {
   constexpr int EB = Tg::kBytes;
-  const float mu = b.mu, rs = b.rs;
+  float mu, rs;
   float s1 = 0.0f, s2 = 0.0f;
-  if (RALL || active) {
+  if constexpr (!RECOMP) {
+    mu = b.mu;
+    rs = b.rs;
+    if (RALL || active) {
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
+      for (int c = 0; c < C; ++c) {
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        const float xc = b.x[c].get(v) - mu;
-        const float dyv = b.dy[c].get(v);
-        const float dyh = dyv * gam[c][v];
-        if (KIND == kLayerNorm) s1 = __builtin_fmaf(dyv, gam[c][v], s1);
-        s2 = __builtin_fmaf(dyh, xc, s2);
-        acc[0][c][v] = __builtin_fmaf(dyv * xc, rs, acc[0][c][v]);
-        if (NACC == 2) acc[NACC - 1][c][v] += dyv;
+        for (int v = 0; v < VEC; ++v) {
+          const float xc = b.x[c].get(v) - mu;
+          const float dyv = b.dy[c].get(v);
+          const float dyh = dyv * gam[c][v];
+          if (KIND == kLayerNorm) s1 = __builtin_fmaf(dyv, gam[c][v], s1);
+          s2 = __builtin_fmaf(dyh, xc, s2);
+          acc[0][c][v] = __builtin_fmaf(dyv * xc, rs, acc[0][c][v]);
+          if (NACC == 2) acc[NACC - 1][c][v] += dyv;
+        }
       }
     }
+    pin(acc);
+    keep_packed(b.x);
+    keep_packed(b.dy);
+    s2 = half_sum(s2, hi);
+    if (KIND == kLayerNorm) s1 = half_sum(s1, hi);
+  } else {
+    mu = 0.0f;
+    if constexpr (KIND == kLayerNorm) {
+      float sx = 0.0f;
+      if (RALL || active) {
+        sx = lane_sum_x(b.x);
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) {
+            const float dyv = b.dy[c].get(v);
+            s1 = __builtin_fmaf(dyv, gam[c][v], s1);
+            if (NACC == 2) acc[NACC - 1][c][v] += dyv;
+          }
+      }
+      keep_packed(b.x);
+      keep_packed(b.dy);
+      sx = half_sum(sx, hi);
+      s1 = half_sum(s1, hi);
+      mu = sx * inv_n;
+    }
+    float sxx = 0.0f;
+    if (RALL || active) {
+      sxx = lane_sum_sq(b.x, mu);
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          const float xc = b.x[c].get(v) - mu;
+          const float dyv = b.dy[c].get(v);
+          s2 = __builtin_fmaf(dyv * gam[c][v], xc, s2);
+          if (KIND != kLayerNorm && NACC == 2) acc[NACC - 1][c][v] += dyv;
+        }
+    }
+    keep_packed(b.x);
+    keep_packed(b.dy);
+    sxx = half_sum(sxx, hi);
+    s2 = half_sum(s2, hi);
+    rs = 1.0f / __builtin_sqrtf(__builtin_fmaf(sxx, inv_n, eps));
   }
-  pin(acc);
-  keep_packed(b.x);
-  keep_packed(b.dy);
-  // every lane takes part in the butterfly (rows that do not exist add zeros
-  // to a sum nobody uses)
-  s2 = half_sum(s2, hi);
-  if (KIND == kLayerNorm) s1 = half_sum(s1, hi);
   if (RALL || active) {
     const float m2 = s2 * inv_n * rs;  // mean_j(dyhat * xhat)
     const float c2 = -(rs * rs) * m2;
@@ -134,6 +211,9 @@ __device__ __forceinline__ void process_pair(RowBuf<Tg, VEC, C>& b, const float 
         const float xc = b.x[c].get(v) - mu;
         const float dyh = b.dy[c].get(v) * gam[c][v];
         o[v] = __builtin_fmaf(dyh, rs, __builtin_fmaf(xc, c2, c1));
+        // recompute mode: the dgamma term, now that rstd is known
+        if constexpr (RECOMP)
+          acc[0][c][v] = __builtin_fmaf(b.dy[c].get(v) * xc, rs, acc[0][c][v]);
       }
       Pack<Tg, VEC> out;
       out.set(o);
@@ -146,13 +226,13 @@ __device__ __forceinline__ void process_pair(RowBuf<Tg, VEC, C>& b, const float 
 // P = waves per workgroup (2 * P rows in flight). span_* = bytes from a row
 // pair's first row to the end of its second row (ld + N elements), which the
 // host checked to be below 2^32.
-template <int KIND, class Tg, int C, int NACC, bool WSNT>
+template <int KIND, bool RECOMP, class Tg, int C, int NACC, bool WSNT>
 __global__ __launch_bounds__(kTwoRowMaxThreads)
 void dx_partials_tworow_kernel(const void* __restrict__ xv, const void* __restrict__ dyv,
                                const void* __restrict__ gv, const float* __restrict__ mean,
                                const float* __restrict__ rstd, void* __restrict__ dxv,
                                float* __restrict__ ws, int64_t M, int N, int64_t ldx,
-                               int64_t ldy, int64_t ldo, int64_t G, int P) {
+                               int64_t ldy, int64_t ldo, int64_t G, int P, float eps) {
   constexpr int EB = Tg::kBytes;
   constexpr int VEC = 16 / EB;
   constexpr int D = kTwoRowDepth;
@@ -217,24 +297,24 @@ void dx_partials_tworow_kernel(const void* __restrict__ xv, const void* __restri
     if (steady) {
 #pragma unroll
       for (int k = 0; k < D - 1; ++k)
-        fetch_pair<KIND, true>(buf[k], x, dy, mean, rstd, pair0(k), row_of(k), true, ldx, ldy,
+        fetch_pair<KIND, RECOMP, true>(buf[k], x, dy, mean, rstd, pair0(k), row_of(k), true, ldx, ldy,
                                hoff_x, hoff_y, span_x, span_y, col0, cstride);
       for (; it0 + 2 * D - 2 < kfull; it0 += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
           const int k = it0 + d;
-          fetch_pair<KIND, true>(buf[(d + D - 1) % D], x, dy, mean, rstd, pair0(k + D - 1),
+          fetch_pair<KIND, RECOMP, true>(buf[(d + D - 1) % D], x, dy, mean, rstd, pair0(k + D - 1),
                                  row_of(k + D - 1), true, ldx, ldy, hoff_x, hoff_y, span_x,
                                  span_y, col0, cstride);
-          process_pair<KIND, true>(buf[d], gam, acc, dx, pair0(k), row_of(k), true, hi, ldo,
-                                   hoff_o, span_o, inv_n, col0, cstride);
+          process_pair<KIND, RECOMP, true>(buf[d], gam, acc, dx, pair0(k), row_of(k), true, hi, ldo,
+                                   hoff_o, span_o, inv_n, eps, col0, cstride);
         }
       }
     } else {
 #pragma unroll
       for (int k = 0; k < D - 1; ++k)
         if (k < iters)
-          fetch_pair<KIND, false>(buf[k], x, dy, mean, rstd, pair0(k), row_of(k), exists(k), ldx,
+          fetch_pair<KIND, RECOMP, false>(buf[k], x, dy, mean, rstd, pair0(k), row_of(k), exists(k), ldx,
                                   ldy, hoff_x, hoff_y, span_x, span_y, col0, cstride);
     }
     for (int it = it0; it < iters; it += D) {
@@ -242,12 +322,12 @@ void dx_partials_tworow_kernel(const void* __restrict__ xv, const void* __restri
       for (int d = 0; d < D; ++d) {
         const int k = it + d;
         if (k + D - 1 < iters)
-          fetch_pair<KIND, false>(buf[(d + D - 1) % D], x, dy, mean, rstd, pair0(k + D - 1),
+          fetch_pair<KIND, RECOMP, false>(buf[(d + D - 1) % D], x, dy, mean, rstd, pair0(k + D - 1),
                                   row_of(k + D - 1), exists(k + D - 1), ldx, ldy, hoff_x,
                                   hoff_y, span_x, span_y, col0, cstride);
         if (k < iters)
-          process_pair<KIND, false>(buf[d], gam, acc, dx, pair0(k), row_of(k), exists(k), hi,
-                                    ldo, hoff_o, span_o, inv_n, col0, cstride);
+          process_pair<KIND, RECOMP, false>(buf[d], gam, acc, dx, pair0(k), row_of(k), exists(k), hi,
+                                    ldo, hoff_o, span_o, inv_n, eps, col0, cstride);
       }
     }
 
@@ -302,6 +382,139 @@ void dx_partials_tworow_kernel(const void* __restrict__ xv, const void* __restri
           }
         }
       }
+    }
+  }
+}
+
+// The forward on the same layout: per row, the statistics from lane_sum_x /
+// lane_sum_sq and the half's butterfly (as recompute mode forms them), then
+// y = gamma * (x - mean) * rstd + beta, and mean/rstd stored as fp32 by the
+// first lane of each half. Rows carry no cross-row state, so in sweep k
+// wave w of workgroup b takes the pair q = (k * gridDim.x + b) * P + w: all
+// workgroups sweep one address window together. Rows are contiguous (row
+// stride N); the host checked 2 * N * EB < 2^32.
+template <int KIND, class Tg, int C, bool BETA>
+__global__ __launch_bounds__(kTwoRowMaxThreads)
+void norm_fwd_tworow_kernel(const void* __restrict__ xv, const void* __restrict__ gv,
+                            const void* __restrict__ bv, void* __restrict__ yv,
+                            float* __restrict__ mean_out, float* __restrict__ rstd_out,
+                            int64_t M, int N, float eps, int P) {
+  constexpr int EB = Tg::kBytes;
+  constexpr int VEC = 16 / EB;
+  constexpr int D = kTwoRowDepth;
+  using PK = Pack<Tg, VEC>;
+  const char* __restrict__ x = static_cast<const char*>(xv);
+  char* __restrict__ y = static_cast<char*>(yv);
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5;
+  const bool hi = h != 0;
+  const int col0 = (lane & 31) * VEC;
+  constexpr int cstride = 32 * VEC;
+  const float inv_n = 1.0f / (float)N;
+  const uint32_t hoff = (uint32_t)(h * N * EB);
+  const uint32_t span = (uint32_t)(2 * N * EB);
+
+  float gam[C][VEC], bet[C][VEC];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int64_t col = col0 + c * cstride;
+    PK tg, tb;
+    tg.load(static_cast<const char*>(gv) + col * EB);
+    if (BETA) tb.load(static_cast<const char*>(bv) + col * EB);
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      gam[c][v] = tg.get(v);
+      bet[c][v] = BETA ? tb.get(v) : 0.0f;
+    }
+  }
+
+  const int64_t per_sweep = (int64_t)gridDim.x * P;
+  const int iters = (int)(((M + 1) / 2 + per_sweep - 1) / per_sweep);
+  const int kfull = (int)((M / 2) / per_sweep);  // sweeps of complete pairs only
+  auto pair0 = [&](int k) { return 2 * (((int64_t)k * gridDim.x + blockIdx.x) * P + w); };
+
+  PK buf[D][C];
+  // RALL: both rows of the pair exist; they go through one buffer resource
+  // based at the pair's first row.
+  auto fetch = [&](auto all, PK (&b)[C], int k) {
+    constexpr bool RALL = decltype(all)::value;
+    const int64_t r0 = pair0(k), r = r0 + h;
+    if (RALL || r < M) {
+      if constexpr (RALL) {
+        const __amdgpu_buffer_rsrc_t rx = row_rsrc(x + r0 * N * EB, span);
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+          b[c].load_stream_buf(rx, hoff + (uint32_t)(col0 + c * cstride) * EB);
+      } else {
+#pragma unroll
+        for (int c = 0; c < C; ++c) b[c].load_stream(x + (r * N + col0 + c * cstride) * EB);
+      }
+    }
+  };
+  auto process = [&](auto all, PK (&b)[C], int k) {
+    constexpr bool RALL = decltype(all)::value;
+    const int64_t r0 = pair0(k), r = r0 + h;
+    const bool active = RALL || r < M;
+    float mu = 0.0f;
+    if constexpr (KIND == kLayerNorm) {
+      float sx = active ? lane_sum_x(b) : 0.0f;
+      keep_packed(b);
+      sx = half_sum(sx, hi);
+      mu = sx * inv_n;
+    }
+    float sxx = active ? lane_sum_sq(b, mu) : 0.0f;
+    keep_packed(b);
+    sxx = half_sum(sxx, hi);
+    if (active) {
+      const float rs = 1.0f / __builtin_sqrtf(__builtin_fmaf(sxx, inv_n, eps));
+      __amdgpu_buffer_rsrc_t ry;
+      if constexpr (RALL) ry = row_rsrc(y + r0 * N * EB, span);
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int col = col0 + c * cstride;
+        float o[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v)
+          o[v] = __builtin_fmaf((b[c].get(v) - mu) * rs, gam[c][v], bet[c][v]);
+        PK out;
+        out.set(o);
+        if constexpr (RALL) out.store_stream_buf(ry, hoff + (uint32_t)col * EB);
+        else out.store_stream(y + (r * N + col) * EB);
+      }
+      // the first lane of each half stores its row's statistics
+      if ((lane & 31) == 0) {
+        if (KIND == kLayerNorm && mean_out) mean_out[r] = mu;
+        if (rstd_out) rstd_out[r] = rs;
+      }
+    }
+  };
+
+  // the steady state and general loop of kernel A's ring
+  int it0 = 0;
+  if (kfull >= 2 * D - 1) {
+#pragma unroll
+    for (int k = 0; k < D - 1; ++k) fetch(std::true_type(), buf[k], k);
+    for (; it0 + 2 * D - 2 < kfull; it0 += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const int k = it0 + d;
+        fetch(std::true_type(), buf[(d + D - 1) % D], k + D - 1);
+        process(std::true_type(), buf[d], k);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < D - 1; ++k)
+      if (k < iters) fetch(std::false_type(), buf[k], k);
+  }
+  for (int it = it0; it < iters; it += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int k = it + d;
+      if (k + D - 1 < iters) fetch(std::false_type(), buf[(d + D - 1) % D], k + D - 1);
+      if (k < iters) process(std::false_type(), buf[d], k);
     }
   }
 }

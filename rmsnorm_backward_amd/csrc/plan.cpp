@@ -83,6 +83,18 @@ constexpr int64_t kTwoRowBytesInFlight = 8192;
 // 131072 x 768 fp16 116.1 -> 111.8 us (4: 129.4, 16: 119.1); 262144 x 256
 // bf16 88.6 -> 74.2 us at 16 rows (8: 74.6).
 constexpr int64_t kTwoRowBytesInFlightLN = 16384;
+// Recompute mode (both kinds) takes the LayerNorm target too: A + B on the
+// same buffers, RMSNorm 1048576 x 256 bf16 296.5 us at 8 KiB (8 rows) against
+// 266.7 at 16 KiB (16 rows), 262144 x 768 214.8 against 217.4, 262144 x 384
+// fp32 even; 32 KiB was slower in every case (226.2, 266.7, 224.9).
+// The two-row forward: 8 waves per workgroup (its launch bound) and about
+// this many waves in all (256 workgroups). Forward step times against 4096
+// waves (512 workgroups) and against the one-row-per-wave forward: 1048576 x
+// 256 bf16 RMSNorm 192.6 us (197.4; 329.0), 262144 x 256 LayerNorm 51.6
+// (50.4; 93.1), 262144 x 768 RMSNorm 140.1 (142.9; 140.5), LayerNorm 141.7
+// (144.1; 146.0), 131072 x 768 fp16 LayerNorm 70.1 (72.1; 82.6), 262144 x 384
+// fp32 RMSNorm 139.2 (144.0; 147.4).
+constexpr int64_t kForwardTwoRowTargetWaves = 2048;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -145,7 +157,8 @@ static int combine_lds_bytes(int S, int C, int vec) { return S * C * 64 * vec * 
 // Lane layout of kernel A for rows of N elements (fills vec, chunks,
 // waves_per_row, rows_in_flight, threads, lds_bytes of *p).
 int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok16,
-                  norm_bwd_plan_t* p, const char** why, bool row_stats, bool saved_stats) {
+                  norm_bwd_plan_t* p, const char** why, bool row_stats, bool saved_stats,
+                  bool two_row) {
   const int eb = dtype_bytes(io_dtype);
   const int nacc = with_dbeta ? 2 : 1;
   const int vw = 16 / eb;
@@ -246,12 +259,13 @@ int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok
   p->rows_in_flight = P;
   p->threads = 64 * S * P;
   p->lds_bytes = lds;
-  // Two rows per wave where 32 lanes cover the row exactly (kernel A with
-  // saved statistics).
-  const int c2 = (saved_stats && !row_stats && full) ? two_row_chunks(N, io_dtype) : 0;
+  // Two rows per wave where 32 lanes cover the row exactly, for every kernel
+  // that has the layout (kernel A in both statistics modes, the forward), so
+  // that the forward and recompute mode form a row's statistics in one order.
+  const int c2 = (two_row && full) ? two_row_chunks(N, io_dtype) : 0;
   if (c2) {
-    const int64_t target =
-        kind == NORM_BWD_LAYERNORM ? kTwoRowBytesInFlightLN : kTwoRowBytesInFlight;
+    const int64_t target = (kind == NORM_BWD_LAYERNORM || !saved_stats)
+                               ? kTwoRowBytesInFlightLN : kTwoRowBytesInFlight;
     int P2 = 2;
     while (P2 * 32 < kTwoRowMaxThreads && (int64_t)P2 * 2 * N * eb < target) P2 *= 2;
     p->rows_per_wave = 2;
@@ -267,8 +281,8 @@ int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok
 bool fused_fits(int64_t N, int io_dtype, int with_dbeta, bool vec_ok16) {
   norm_bwd_plan_t g;
   const char* why = nullptr;
-  return make_geometry(NORM_BWD_RMSNORM, N, io_dtype, with_dbeta, vec_ok16, &g, &why, false) ==
-         NORM_BWD_OK;
+  return make_geometry(NORM_BWD_RMSNORM, N, io_dtype, with_dbeta, vec_ok16, &g, &why, false,
+                       true) == NORM_BWD_OK;
 }
 
 int64_t rowloop_grid(int64_t M) { return M < 512 ? (M < 1 ? 1 : M) : 512; }
@@ -330,6 +344,20 @@ int forward_rows_in_flight(int64_t M, int S, int P, int lane_elems) {
   return M >= kForwardRowsPerLaneMin * lanes ? P2 : P;
 }
 
+int forward_two_row_waves(int64_t M) {
+  (void)M;
+  return kTwoRowMaxThreads / 64;
+}
+
+int64_t forward_two_row_grid(int64_t M, int W) {
+  if (M <= 0 || W <= 0) return 0;
+  int64_t g = kForwardTwoRowTargetWaves / W;
+  const int64_t sweep = ceil_div(ceil_div(M, 2), W);  // one sweep of row pairs
+  if (g > sweep) g = sweep;
+  if (g > kMaxGrid) g = kMaxGrid;
+  return g < 1 ? 1 : g;
+}
+
 int wgrad_lanes_per_row(int64_t N, int vec) {
   int lpr = 64 / vec;  // the 64-column tile
   while (lpr > 1 && ceil_div(N, (int64_t)lpr * vec) < kWgradTargetTiles) lpr >>= 1;
@@ -349,9 +377,13 @@ int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype, bool recompute
     norm_bwd_plan_t g;
     const char* why = nullptr;
     int waves = 8;
-    if (N > 0 && make_geometry(kind, N, io_dtype, 0, true, &g, &why, true) == NORM_BWD_OK)
+    bool two_row = false;
+    if (N > 0 && make_geometry(kind, N, io_dtype, 0, true, &g, &why, true, false) == NORM_BWD_OK) {
       waves = g.threads / 64;
-    G = kRecomputeLnTargetWaves / waves;
+      two_row = g.rows_per_wave == 2;
+    }
+    // (the two-row layout has no barrier per row: the saved-statistics count)
+    if (!two_row) G = kRecomputeLnTargetWaves / waves;
   }
   const int64_t cap = ceil_div(M, kMinRowsPerGroup);
   if (G > cap) G = cap;
@@ -383,7 +415,7 @@ int make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,
 
   const char* gwhy = nullptr;
   const int st = make_geometry(kind, N, io_dtype, with_dbeta, vec_ok16, &p, &gwhy,
-                               recompute && kind == NORM_BWD_LAYERNORM, !recompute);
+                               recompute && kind == NORM_BWD_LAYERNORM, !recompute, true);
   if (st != NORM_BWD_OK) return fail(why, gwhy, st);
   if (N == 0) {  // nothing to compute
     *plan = p;
@@ -394,7 +426,7 @@ int make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,
     // a row pair whose stride needs offsets beyond 32 bits keeps one row per wave
     if (p.rows_per_wave == 2 && !two_row_span_ok(N, max_ld ? max_ld : N, io_dtype))
       make_geometry(kind, N, io_dtype, with_dbeta, vec_ok16, &p, &gwhy,
-                    recompute && kind == NORM_BWD_LAYERNORM, false);
+                    recompute && kind == NORM_BWD_LAYERNORM, !recompute, false);
     int64_t G = groups ? groups : auto_groups(kind, M, N, io_dtype, recompute);
     // every group holds at least one row (two-row plans: one row pair)
     const int64_t units = p.rows_per_wave == 2 ? ceil_div(M, 2) : M;

@@ -22,17 +22,18 @@ bool kernel_a_exists(int io_dtype, int vec_full, int with_dbeta, int chunks);
 int kernel_a_max_threads(int lane_elems);
 
 // Lane layout for rows of N elements (vec, chunks, waves_per_row,
-// rows_in_flight, threads, lds_bytes of *plan), for kernel A with saved
-// statistics or, with `row_stats`, for the kernels that compute row
-// statistics (the forward, kernel A in recompute mode): the lane layout is
-// the same, the rows in flight differ. Returns a status.
-// `saved_stats`: the plan is for kernel A with saved statistics, which can
-// run the two-rows-per-wave kernel (rows 32 lanes cover exactly then take
-// that layout) and has its own rows-in-flight target for RMSNorm rows on
-// 16-byte lanes.
+// rows_in_flight, threads, lds_bytes, rows_per_wave of *plan), for kernel A
+// with saved statistics or, with `row_stats`, for the kernels that compute
+// row statistics with a barrier per row (the forward, LayerNorm recompute
+// mode): the lane layout is the same, the rows in flight differ. Returns a
+// status. `saved_stats`: kernel A with saved statistics, which has its own
+// rows-in-flight target for RMSNorm rows on 16-byte lanes. `two_row`: rows
+// that 32 lanes cover exactly take the two-rows-per-wave layout (every mode
+// has it; its rows in flight are those of kernel A, which the forward
+// replaces by its own).
 int make_geometry(int kind, int64_t N, int io_dtype, int with_dbeta, bool vec_ok16,
                   norm_bwd_plan_t* plan, const char** why, bool row_stats,
-                  bool saved_stats = false);
+                  bool saved_stats = false, bool two_row = true);
 
 // The two-rows-per-wave layout for rows of N elements: its chunk count (1 or
 // 3) when 32 lanes of 16-byte vectors cover N exactly and 64-lane waves would
@@ -78,6 +79,14 @@ int64_t forward_grid(int64_t M, int S, int P);
 // every row-lane of the resulting grid still gets at least 4 rows, else P.
 int forward_rows_in_flight(int64_t M, int S, int P, int lane_elems);
 
+// Waves per workgroup of the two-rows-per-wave forward for M rows (each wave
+// two rows): the kernel's launch bound, 8.
+int forward_two_row_waves(int64_t M);
+
+// Workgroups of the two-rows-per-wave forward for M rows and W waves per
+// workgroup: about 2048 waves, at most one sweep of the ceil(M / 2) pairs.
+int64_t forward_two_row_grid(int64_t M, int W);
+
 // Lanes per row of the column-walk tile (tile = lpr * vec columns) for N
 // columns: the widest tile (up to 64 columns) that still gives at least 256
 // tiles, and at least one lane.
@@ -91,8 +100,8 @@ int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype, bool recompute
 
 // Fill *plan (see norm_bwd_make_plan). `vec_ok16` says whether the caller's
 // pointers are 16-byte aligned. Writes a message into *why on failure.
-// `recompute`: the plan is for recompute mode (affects the automatic groups;
-// the two-row layout serves saved statistics only). `max_ld`: the largest
+// `recompute`: the plan is for recompute mode (affects the automatic groups
+// and rows in flight). `max_ld`: the largest
 // row stride in elements of x, dy and dx (0: N), for the two-row layout's
 // span.
 int make_plan(int kind, int64_t M, int64_t N, int io_dtype, int with_dbeta,

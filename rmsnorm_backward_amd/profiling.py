@@ -34,6 +34,7 @@ KERNEL_A = "dx_partials_kernel"
 KERNEL_A_TWOROW = "dx_partials_tworow_kernel"
 KERNEL_B = "reduce_partials_kernel"
 FORWARD = "norm_fwd_kernel"
+FORWARD_TWOROW = "norm_fwd_tworow_kernel"
 COLWALK = "wgrad_colwalk_kernel"
 COPY = "copy_probe_kernel"
 TRIAD = "triad_probe_kernel"
@@ -41,7 +42,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCE = os.path.join(_HERE, "csrc", "nb_device.hpp")
 # kernel A's sources: the one-row-per-wave kernel and the two-rows-per-wave one
 KERNEL_A_SOURCES = (KERNEL_SOURCE, os.path.join(_HERE, "csrc", "nb_tworow.hpp"))
-FORWARD_SOURCES = (KERNEL_SOURCE, os.path.join(_HERE, "csrc", "nb_forward.hpp"))
+FORWARD_SOURCES = (KERNEL_SOURCE, os.path.join(_HERE, "csrc", "nb_forward.hpp"),
+                   os.path.join(_HERE, "csrc", "nb_tworow.hpp"))
 
 
 def _hash(paths) -> str:
@@ -74,10 +76,15 @@ def _bench(path):
 def is_step_kernel_a(name: str) -> bool:
     """Kernel A as the benchmark's step and roofline time it: the instantiation
     that reads the saved statistics (template argument RECOMP = false), not
-    the recompute-mode one the same run also launches; or the
-    two-rows-per-wave kernel, which exists for saved statistics only."""
-    return (re.search(KERNEL_A + r"<\s*\d+\s*,\s*false\s*,", name) is not None or
-            KERNEL_A_TWOROW in name)
+    the recompute-mode one the same run also launches, of either layout (one
+    or two rows per wave)."""
+    return re.search("(" + KERNEL_A + "|" + KERNEL_A_TWOROW + r")<\s*\d+\s*,\s*false\s*,",
+                     name) is not None
+
+
+def is_forward(name: str) -> bool:
+    """The fused forward of either layout (not the row-loop forward)."""
+    return FORWARD in name or FORWARD_TWOROW in name
 
 
 def stats_summary(stats_csv: str, bench_json: str, cmds) -> str:
@@ -97,7 +104,7 @@ def stats_summary(stats_csv: str, bench_json: str, cmds) -> str:
         avg = float(r["AverageNs"]) / 1e3
         if is_step_kernel_a(name) and int(r["Calls"]) > calls_a:
             avg_a, calls_a = avg, int(r["Calls"])
-        if FORWARD in name:
+        if is_forward(name):
             avg_f = avg
         if KERNEL_B in name:
             avg_b = avg
@@ -150,6 +157,8 @@ def _mean_for(per_dispatch, needle):
     one, so the (kernel, grid) pair dispatched first is taken."""
     if needle == KERNEL_A:
         vals = [v for (d, name, g), v in per_dispatch.items() if is_step_kernel_a(name)]
+    elif needle == FORWARD:
+        vals = [v for (d, name, g), v in per_dispatch.items() if is_forward(name)]
     elif needle == COLWALK:
         hits = sorted((d, name, g, v) for (d, name, g), v in per_dispatch.items() if needle in name)
         vals = [v for d, name, g, v in hits if hits and (name, g) == hits[0][1:3]]

@@ -65,7 +65,7 @@ int main() {
                   EXPECT(p.vec == 1 || (N * eb) % 16 == 0, "vector rows");
                   if (p.rows_per_wave == 2) {
                     // two rows per wave: 32 lanes cover the row exactly
-                    EXPECT(!rc && p.vec == 16 / eb, "two-row layout with saved statistics");
+                    EXPECT(p.vec == 16 / eb, "two-row layout on 16-byte lanes");
                     EXPECT((int64_t)32 * p.vec * p.chunks == N &&
                                (p.chunks == 1 || p.chunks == 3),
                            "two-row coverage");
@@ -112,6 +112,17 @@ int main() {
             if (nb::make_geometry(kind, N, dt, 0, vec_ok != 0, &g, &why, true) != NORM_BWD_OK)
               continue;
             ++forwards;
+            if (g.rows_per_wave == 2) {
+              // two rows per wave: waves of a row pair each over ceil(M / 2) pairs
+              EXPECT(vec_ok && (int64_t)32 * g.vec * g.chunks == N, "forward two-row coverage");
+              const int W = nb::forward_two_row_waves(M);
+              EXPECT(W >= 1 && 64 * W <= 512, "forward two-row waves %d", W);
+              const int64_t pairs = (M + 1) / 2;
+              const int64_t grid = nb::forward_two_row_grid(M, W);
+              EXPECT(grid >= 1 && grid <= (pairs + W - 1) / W, "forward two-row grid");
+              EXPECT(nb::two_row_span_ok(N, N, dt), "forward two-row span");
+              continue;
+            }
             const int S = g.waves_per_row, P0 = g.rows_in_flight;
             const int P = nb::forward_rows_in_flight(M, S, P0, g.vec * g.chunks);
             EXPECT(P == P0 || P == 2 * P0, "forward P %d from %d", P, P0);

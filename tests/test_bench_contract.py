@@ -84,6 +84,11 @@ def test_profile_summaries_pick_the_step_kernel():
     assert is_step_kernel_a("nb::dx_partials_kernel<0, false, nb::TF16, 8, 2, 2, true>")
     assert not is_step_kernel_a("void nb::dx_partials_kernel<1, true, nb::TBF16, 8, 2, 1, false>")
     assert not is_step_kernel_a("nb::reduce_partials_kernel<nb::TF32>")
+    assert is_step_kernel_a("void nb::dx_partials_tworow_kernel<1, false, nb::TBF16, 3, 1, false>(a)")
+    assert not is_step_kernel_a("void nb::dx_partials_tworow_kernel<0, true, nb::TBF16, 3, 2, false>")
+    assert profiling.is_forward("void nb::norm_fwd_tworow_kernel<1, nb::TBF16, 3, false>(a)")
+    assert profiling.is_forward("void nb::norm_fwd_kernel<1, nb::TBF16, 8, 1, false>(a)")
+    assert not profiling.is_forward("void nb::fwd_rowloop_kernel<1, nb::TBF16>(a)")
     for name in ("rmsnorm_bf16_16384x4096", "layernorm_bf16_65536x8192"):
         text = open(os.path.join(ROOT, "profiles", f"kernels_{name}.md")).read()
         ratio = float(re.search(r"kernel A by the trace: [\d.]+ us \(events / trace = ([\d.]+)\)",

@@ -261,6 +261,39 @@ def test_forward_exact_non_power_of_two_waves(nb, kind, dt, M, N):
     check(w, inp["x"], inp["gamma"], beta, tuple(None if t is None else t.cpu() for t in got))
 
 
+@pytest.mark.parametrize("kind,dt,M,m,N", [
+    ("rmsnorm", torch.bfloat16, 1, 1, 768), ("layernorm", torch.bfloat16, 2, 1, 768),
+    ("layernorm", torch.float16, 3, 2, 256), ("rmsnorm", torch.float16, 8193, 77, 256),
+    ("layernorm", torch.float32, 515, 3, 384), ("rmsnorm", torch.float32, 1000, 999, 128),
+    # sweeps of complete pairs (the steady-state loop), then a last pair of one row
+    ("layernorm", torch.bfloat16, 45001, 1001, 768),
+    ("rmsnorm", torch.bfloat16, 65536, 4097, 256)])
+def test_forward_two_rows_per_wave(nb, kind, dt, M, m, N):
+    """Rows that 32 lanes of 16-byte vectors cover exactly (N = 32 * vec *
+    1 or 3) run two rows per wave. Every row matches the oracle, and a
+    row's outputs do not depend on which pair or sweep it fell in: the
+    first m rows alone (another grid, another pairing of the last row)
+    give the same bits."""
+    base = W.LN_BF16_65536x8192 if kind == "layernorm" else W.RMS_BF16_16384x4096
+    w = W.scaled(base, M=M, N=N, io_dtype=dt, seed=900 + M + N)
+    inp = W.make_inputs(w)
+    x, g = inp["x"].cuda(), inp["gamma"].cuda()
+    beta = _beta(w, inp)
+
+    def fwd(xx):
+        if kind == "layernorm":
+            return nb.norm_fwd_layernorm(xx, g, beta.cuda(), w.eps)
+        y, r = nb.norm_fwd_rmsnorm(xx, g, w.eps)
+        return (y, None, r)
+
+    big, small = fwd(x), fwd(x[:m].contiguous())
+    torch.cuda.synchronize()
+    for t_big, t_small in zip(big, small):
+        if t_big is not None:
+            assert torch.equal(t_big[:m], t_small)
+    check(w, inp["x"], inp["gamma"], beta, tuple(None if t is None else t.cpu() for t in big))
+
+
 def test_forward_misaligned_rows_take_the_scalar_path(nb):
     w = W.scaled(W.RMS_BF16_16384x4096, M=37, N=1000)
     inp = W.make_inputs(w)

@@ -126,6 +126,22 @@ def test_recompute_exact_non_power_of_two_waves(nb, kind, dt, M, N):
     compare(w, inp["x"], inp["dy"], inp["gamma"], out, with_db)
 
 
+@pytest.mark.parametrize("kind,dt,M,N", [
+    ("rmsnorm", torch.bfloat16, 1, 768), ("layernorm", torch.bfloat16, 3, 256),
+    ("rmsnorm", torch.float32, 999, 128), ("layernorm", torch.float16, 4097, 768),
+    # groups of at least 20 complete pairs: the steady-state loop
+    ("layernorm", torch.bfloat16, 20001, 768), ("rmsnorm", torch.float16, 30000, 256),
+    ("layernorm", torch.float32, 12001, 384), ("rmsnorm", torch.bfloat16, 24576, 768)])
+def test_recompute_two_rows_per_wave(nb, kind, dt, M, N):
+    """Recompute mode on the two-rows-per-wave layout (each 32-lane half forms
+    its row's statistics), both gradients."""
+    base = W.LN_F32_128x512 if kind == "layernorm" else W.RMS_F32_128x512
+    w = W.scaled(base, M=M, N=N, io_dtype=dt, wgrad_dtype=torch.float32, seed=800 + N)
+    inp = W.make_inputs(w)
+    out = run_recompute(nb, w, inp["x"], inp["dy"], inp["gamma"], True)
+    compare(w, inp["x"], inp["dy"], inp["gamma"], out, True)
+
+
 def test_recompute_constant_rows(nb):
     """A constant LayerNorm row has var = 0: rstd = 1/sqrt(eps), xhat = 0, so
     dx = rstd * (dyhat - mean(dyhat)) and its dgamma terms vanish."""
@@ -154,8 +170,10 @@ def test_recompute_full_size_sampled(nb, w):
 
 
 def recompute_plan(nb, kind, M, N, dt, db):
-    """The plan recompute mode runs, as a saved-statistics plan. RMSNorm
-    recompute takes the saved-statistics plan itself. LayerNorm recompute
+    """The plan recompute mode runs, as a saved-statistics plan. Rows on the
+    two-rows-per-wave layout take the saved-statistics plan with 16 KiB of x
+    and dy in flight in both kinds. RMSNorm recompute otherwise takes the
+    saved-statistics plan itself. LayerNorm recompute
     keeps the lane layout but fills 512 threads with rows (one when the
     combine buffer would not fit in LDS), with its own group count (about
     4096 waves in flight, counted on the dbeta-less layout; at least 4 rows
@@ -168,6 +186,15 @@ def recompute_plan(nb, kind, M, N, dt, db):
         return 1 if P > 1 and S * C * 64 * vec * 4 > 65536 - 1024 else P
 
     base = nb.norm_bwd_make_plan(kind, M, N, dt, db)
+    if base.rows_per_wave == 2:
+        # RMSNorm recompute aims at LayerNorm's 16 KiB of x and dy in flight
+        P = 2
+        while P * 32 < 512 and P * 2 * N * dt.itemsize < 16384:
+            P *= 2
+        p = base.copy()
+        p.rows_in_flight, p.threads = P, 32 * P
+        p.lds_bytes = (2 if db else 1) * base.chunks * 32 * base.vec * 4 if P > 2 else 0
+        return p
     if kind == "rmsnorm":
         # the saved-statistics rules, except that rows on 16-byte lanes with
         # an odd wave count aim at 16 KiB of x and dy in flight, not 12 KiB
@@ -206,7 +233,14 @@ def recompute_plan(nb, kind, M, N, dt, db):
                                W.scaled(W.LN_BF16_65536x8192, M=500, N=3072),
                                # 7 waves of 16-byte lanes
                                W.scaled(W.RMS_BF16_16384x4096, M=900, N=3584),
-                               W.scaled(W.LN_BF16_65536x8192, M=400, N=3584)],
+                               W.scaled(W.LN_BF16_65536x8192, M=400, N=3584),
+                               # two rows per wave (odd M: a last pair of one row)
+                               W.scaled(W.RMS_BF16_262144x768, M=3001),
+                               W.scaled(W.LN_BF16_65536x8192, M=2001, N=768),
+                               W.scaled(W.RMS_BF16_16384x4096, M=999, N=256),
+                               W.scaled(W.LN_BF16_65536x8192, M=20000, N=256),
+                               W.scaled(W.LN_F32_128x512, M=515, N=384),
+                               W.scaled(W.RMS_F32_128x512, M=77, N=128)],
                          ids=lambda w: w.name)
 def test_recompute_matches_forward_statistics_bitwise(nb, w):
     """The forward and recompute mode share the lane layout, so the

@@ -108,14 +108,15 @@ def _row_stats_rows(p, db):
 def _auto_groups(nb, kind, M, N, dt, recompute=False):
     """The documented rule: 256 groups, except in LayerNorm recompute mode:
     about 4096 waves in flight, the waves per workgroup coming from the
-    (dbeta-less) lane layout with 512-thread workgroups; always >= 4 rows per
-    group, above 256 a multiple of 256."""
+    (dbeta-less) lane layout with 512-thread workgroups (rows on the
+    two-rows-per-wave layout, which has no barrier per row, keep 256);
+    always >= 4 rows per group, above 256 a multiple of 256."""
     if M == 0:
         return 0
-    if recompute and kind == "layernorm":
+    p = nb.norm_bwd_make_plan(kind, 1, N, dt, False) if N else None
+    if recompute and kind == "layernorm" and not (p and p.rows_per_wave == 2):
         waves = 8
         if N:
-            p = nb.norm_bwd_make_plan(kind, 1, N, dt, False)
             waves = p.waves_per_row * _row_stats_rows(p, False)
         g = 4096 // waves
     else:
@@ -135,6 +136,8 @@ def _auto_groups(nb, kind, M, N, dt, recompute=False):
     ("rmsnorm", 16384, 4096, torch.bfloat16, False),
     ("layernorm", 65536, 8192, torch.bfloat16, True),
     ("rmsnorm", 262144, 768, torch.bfloat16, False),
+    ("layernorm", 262144, 768, torch.bfloat16, True),     # two rows per wave
+    ("layernorm", 5000, 384, torch.float32, True),
     ("rmsnorm", 0, 768, torch.bfloat16, True),
     ("layernorm", 5, 0, torch.float16, True),
 ])
