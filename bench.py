@@ -870,9 +870,12 @@ def measure_extras(torch, nb, W, lib, dev, stream, w, args, steps, warmup, sets,
     torch.cuda.empty_cache()
 
     wide = measure_wide(torch, nb, W, lib, dev, stream, args) if not args.no_wide else None
+    # the forward takes the backward's lane layout (two rows per wave or one)
+    two_row = nb.norm_bwd_make_plan(w.kind, w.M, w.N, io, with_db).rows_per_wave == 2
     out = {
         "forward": {
-            "kernel": "norm_fwd_kernel", "us": round(ms_f * 1e3, 3),
+            "kernel": "norm_fwd_tworow_kernel" if two_row else "norm_fwd_kernel",
+            "us": round(ms_f * 1e3, 3),
             "bytes_per_launch": f_bytes, "with_beta": "beta" in base,
             "GBps": round(f_bytes / (ms_f * 1e-3) / 1e9, 2),
             "traffic": committed_forward_traffic(w.name),
@@ -883,8 +886,7 @@ def measure_extras(torch, nb, W, lib, dev, stream, w, args, steps, warmup, sets,
         },
         "recompute": {
             "what": "whole backward step with mean/rstd recomputed from x (no stats read)",
-            "groups": nb.norm_bwd_workspace_bytes(w.kind, w.M, w.N, io, with_db) //
-            (w.N * 4 * (2 if with_db else 1)),
+            "workspace_bytes": nb.norm_bwd_workspace_bytes(w.kind, w.M, w.N, io, with_db),
             "us": round(ms_rc * 1e3, 3), "bytes": rc_bytes,
             "GBps": round(rc_bytes / (ms_rc * 1e-3) / 1e9, 2),
             "pct_of_peak": round(100 * rc_bytes / (ms_rc * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
@@ -1062,7 +1064,8 @@ def main(argv=None) -> int:
         "roofline": {
             "bound": "hbm", "achieved": e["kernel_a_GBps"], "peak": PEAK_HBM_GBPS,
             "unit": "GB/s", "frac": e["kernel_a_frac"], "traffic": e["kernel_a_traffic"],
-            "kernel": "dx_partials_kernel", "bytes_per_launch": e["kernel_a_bytes"],
+            "kernel": "dx_partials_tworow_kernel" if e["plan"].get("rows_per_wave") == 2
+            else "dx_partials_kernel", "bytes_per_launch": e["kernel_a_bytes"],
         },
     }
     if "cpu_oracle" in e:
