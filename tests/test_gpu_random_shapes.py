@@ -12,7 +12,8 @@ for strides) and is
 compared with the fp64 oracle under the same tolerances as the other parity
 tests. The draw is fixed, so a failure names a reproducible case. The forward
 (beta on or off, statistics requested or not) and norm_bwd_wgrad
-(accumulating or not) get sweeps of their own.
+(accumulating or not) get sweeps of their own, and the widths of the
+two-rows-per-wave layout a backward and a forward sweep of their own.
 """
 
 from __future__ import annotations
@@ -80,6 +81,28 @@ def _long_group_cases(n=40, seed=20261203):
     return out
 
 
+def _two_row_cases(n=48, seed=20261204):
+    """Widths of the two-rows-per-wave layout (32 lanes of 16-byte vectors:
+    256 or 768 16-bit elements, 128 or 384 fp32), saved or recomputed
+    statistics, odd and even M up to sizes where groups run the steady-state
+    loop, strides and explicit groups."""
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        kind = rng.choice(("layernorm", "rmsnorm"))
+        dt = rng.choice(DTYPES)
+        N = rng.choice((128, 384) if dt == torch.float32 else (256, 768))
+        M = rng.choice((1, 2, 3, 511, 513)) if rng.random() < 0.3 else rng.randint(1, 12000)
+        with_db = kind == "layernorm" if rng.random() < 0.6 else rng.random() < 0.5
+        recompute = rng.random() < 0.5
+        pad = rng.choice((0, 0, 0, 8, 24))
+        wg = torch.float32 if rng.random() < 0.75 else dt
+        acc = pad > 0 and rng.random() < 0.3
+        groups = rng.choice((1, 3, 64, 1000)) if pad > 0 and rng.random() < 0.4 else 0
+        out.append((2000 + i, kind, dt, M, N, with_db, recompute, pad, wg, acc, groups))
+    return out
+
+
 def _strided(t, pad):
     M, N = t.shape
     buf = torch.zeros(M * (N + pad), dtype=t.dtype, device="cuda")
@@ -105,6 +128,12 @@ def test_random_shape(nb, case):
 @pytest.mark.parametrize("case", _long_group_cases(),
                          ids=lambda c: "-".join(str(v).replace("torch.", "") for v in c))
 def test_random_long_groups(nb, case):
+    _run_backward_case(nb, case)
+
+
+@pytest.mark.parametrize("case", _two_row_cases(),
+                         ids=lambda c: "-".join(str(v).replace("torch.", "") for v in c))
+def test_random_two_row_widths(nb, case):
     _run_backward_case(nb, case)
 
 
@@ -174,9 +203,9 @@ def _run_backward_case(nb, case):
     else:
         bg, bb = parity.wgrad_bounds(kind, inp["x"], inp["dy"], inp.get("mean"), inp["rstd"],
                                      depth)
-    # the named deep-sum case for fp32 (parity.FP32_DEEP_SUM_DEPTH)
-    long_g = parity.fp32_deep_sum_extra(dt, bg)
-    long_b = parity.fp32_deep_sum_extra(dt, bb)
+    # the named long-sum case for fp32 (parity.fp32_long_sum_extra)
+    long_g = parity.fp32_long_sum_extra(dt, bg, rdg)
+    long_b = parity.fp32_long_sum_extra(dt, bb, rdb)
     if acc:
         old64 = old.double().abs().numpy()
         a_extra = 2.0 ** -24 * (old64 + abs(parity.f64(rdg)))
@@ -208,7 +237,21 @@ def _fwd_cases(n=80, seed=1202):
     return out
 
 
-@pytest.mark.parametrize("case", _fwd_cases(), ids=lambda c: "-".join(
+def _fwd_two_row_cases(n=24, seed=1203):
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        kind = rng.choice(("layernorm", "rmsnorm"))
+        dt = rng.choice(DTYPES)
+        N = rng.choice((128, 384) if dt == torch.float32 else (256, 768))
+        M = rng.choice((1, 2, 3, 4097)) if rng.random() < 0.3 else rng.randint(1, 20000)
+        beta = kind == "layernorm" and rng.random() < 0.6
+        stats = rng.random() < 0.8
+        out.append((100 + i, kind, dt, M, N, beta, stats))
+    return out
+
+
+@pytest.mark.parametrize("case", _fwd_cases() + _fwd_two_row_cases(), ids=lambda c: "-".join(
     str(v).replace("torch.", "") for v in c))
 def test_random_forward(nb, case):
     """y and the statistics of the forward (fused, register-held or streamed

@@ -109,35 +109,51 @@ def test_half_weight_gradients_bound():
         parity.check_wgrad(torch.bfloat16, torch.from_numpy(dg), rdg)
 
 
-def test_fp32_deep_sums_need_the_summation_bound():
-    """The named deep-sum case: a float32 sum of 1327 rows in one or two
-    groups misses the plain 1e-5 bound on columns that cancel (by 2-3x here),
-    and meets it with the fp32 summation term; the same rows in 256 groups
-    (depth 58) meet the plain bound. Up to depth 128, and for half
-    precision, no term is added."""
-    w = W.scaled(W.LN_F32_128x512, M=1327, N=1000, seed=10000)
-    inp = backward_inputs(w)
-    x, dy, rs, mu = (_np(inp, k) for k in ("x", "dy", "rstd", "mean"))
-    rdg, _ = oracle.bwd_wgrad(w.kind, inp["x"], inp["dy"], inp["mean"], inp["rstd"])
-    for groups in (1, 2):
+def test_fp32_long_sums_need_the_summation_bound():
+    """The named long-sum case: float32 column sums that cancel far below
+    their partial sums. Evaluated in float32 in the kernels' order, 1327 rows
+    in one or two groups (a deep chain) and 8192 rows in 256 groups (many
+    rows, depth 84) miss the plain 1e-5 bound on such columns; every column
+    that misses it is in the case, where the fp32 summation term meets it,
+    and the case takes few columns (at most 1/8 of them in 256 groups, 1/4
+    in the deep chains; the plain bound holds on the rest). The
+    same 1327 rows in 256 groups meet the plain bound (the case, a bound on
+    what fp32 may cost, still takes a few of their columns); the 128 x 512
+    workloads have no column in it. Half precision never is."""
+    def check(w, groups, plain_fails, most_named=8):
+        inp = backward_inputs(w)
+        x, dy, rs, mu = (_np(inp, k) for k in ("x", "dy", "rstd", "mean"))
+        if mu is None:
+            mu = np.zeros(w.M, F)
+        rdg, _ = oracle.bwd_wgrad(w.kind, inp["x"], inp["dy"], inp.get("mean"), inp["rstd"])
         dg, _ = fp32_wgrad(w.kind, x, dy, mu, rs, groups=groups)
-        with pytest.raises(parity.Mismatch):
-            parity.check_wgrad(torch.float32, torch.from_numpy(dg), rdg)
-        bg, _ = parity.wgrad_bounds(w.kind, inp["x"], inp["dy"], inp["mean"], inp["rstd"],
+        bg, _ = parity.wgrad_bounds(w.kind, inp["x"], inp["dy"], inp.get("mean"), inp["rstd"],
                                     parity.depth_fused(w.M, groups))
-        assert bg["depth"] > parity.FP32_DEEP_SUM_DEPTH
-        s = parity.check_wgrad(torch.float32, torch.from_numpy(dg), rdg,
-                               extra=parity.fp32_deep_sum_extra(torch.float32, bg))
-        assert s["max_err_over_bound"] < 0.01
-    dg, _ = fp32_wgrad(w.kind, x, dy, mu, rs, groups=256)
-    assert parity.depth_fused(w.M, 256) <= parity.FP32_DEEP_SUM_DEPTH
-    parity.check_wgrad(torch.float32, torch.from_numpy(dg), rdg)
-    # the automatic plans of the named workloads stay within the depth
-    assert parity.depth_fused(128, 32) == 42 and parity.depth_fused(16384, 256) == 116
-    a = np.ones(3)
-    assert parity.fp32_deep_sum_extra(torch.float32, {"absum": a, "depth": 128}) is None
-    assert parity.fp32_deep_sum_extra(torch.bfloat16, {"absum": a, "depth": 500}) is None
-    assert parity.fp32_deep_sum_extra(torch.float32, {"absum": a, "depth": 129}) is not None
+        extra = parity.fp32_long_sum_extra(torch.float32, bg, rdg)
+        err = np.abs(dg.astype(np.float64) - rdg)
+        over = err > 1e-5 + 1e-5 * np.abs(rdg)
+        if plain_fails:
+            assert over.any() and extra is not None and np.all(extra[over] > 0)
+            with pytest.raises(parity.Mismatch):
+                parity.check_wgrad(torch.float32, torch.from_numpy(dg), rdg)
+            parity.check_wgrad(torch.float32, torch.from_numpy(dg), rdg, extra=extra)
+            named = extra > 0
+            assert np.max(err[named] / extra[named]) < 0.05     # far inside the added term
+            assert np.count_nonzero(named) <= w.N // most_named
+        else:
+            parity.check_wgrad(torch.float32, torch.from_numpy(dg), rdg)
+            assert extra is None or np.count_nonzero(extra) <= w.N // most_named
+        return bg, rdg, extra
+
+    deep = W.scaled(W.LN_F32_128x512, M=1327, N=1000, seed=10000)
+    for groups in (1, 2):                 # a chain of 664 to 1327 rows: more columns
+        check(deep, groups, True, most_named=4)
+    check(deep, 256, False)
+    bg, rdg, _ = check(W.scaled(W.LN_F32_128x512, M=8192, N=256, seed=10001), 256, True)
+    assert bg["depth"] <= 128
+    for w in (W.LN_F32_128x512, W.RMS_F32_128x512):
+        assert check(w, 32, False)[2] is None
+    assert parity.fp32_long_sum_extra(torch.bfloat16, bg, rdg) is None
 
 
 def test_summation_depths():
