@@ -549,6 +549,41 @@ def backward_step(nb, lib, w, explicit, full_args, part_args, wg, dgamma, dbeta)
     return step
 
 
+def graph_step_time(torch, nb, w, sets, dgamma, dbeta, ws, steps):
+    """ms per backward step replayed from a captured HIP graph: one capture
+    of a step on every buffer set in turn (the named entry point through the
+    binding, on the capturing stream), warmed up on a side stream first,
+    replayed until at least `steps` steps have run. The launches' host cost
+    drops out, so on small workloads this is the GPU's own time per step."""
+    def call(s):
+        if w.kind == "layernorm":
+            nb.norm_bwd_layernorm(s["x"], s["dy"], s["gamma"], s["mean"], s["rstd"], w.eps,
+                                  wgrad_dtype=w.wgrad_dtype, dx=s["dx"], dgamma=dgamma,
+                                  dbeta=dbeta, with_dbeta=dbeta is not None, workspace=ws)
+        else:
+            nb.norm_bwd_rmsnorm(s["x"], s["dy"], s["gamma"], s["rstd"], w.eps,
+                                wgrad_dtype=w.wgrad_dtype, dx=s["dx"], dgamma=dgamma,
+                                dbeta=dbeta, with_dbeta=dbeta is not None, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for s in sets:
+            call(s)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for s in sets:
+            call(s)
+    replays = max(2, math.ceil(steps / len(sets)))
+    graph.replay()
+    stream = torch.cuda.current_stream()
+    ms = time_loop(torch, lambda i: graph.replay(), replays, stream) / len(sets)
+    del graph
+    return ms
+
+
 def placement_study(torch, nb, lib, dev, stream, w, args, base, plan, count):
     """The backward step and the triad over `count` placements of the
     operands: for each, two buffer sets whose x, dy and dx are carved from
@@ -682,6 +717,7 @@ def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, ext
         step(i)
     torch.cuda.synchronize()
     ms = time_loop(torch, step, steps, stream)
+    ms_graph = graph_step_time(torch, nb, w, sets, dgamma, dbeta, ws, steps)
     # the spread of the step time: 20 loops of 25 steps, each loop's mean
     chunks = sorted(time_loop(torch, step, 25, stream) for _ in range(20))
     ms_a = time_loop(torch, step_a, steps, stream)
@@ -708,6 +744,8 @@ def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, ext
         "step_us": round(ms * 1e3, 3), "GBps": round(value, 2),
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "rows_per_s": round(w.M / (ms * 1e-3), 1),
+        "graph_step_us": round(ms_graph * 1e3, 3),
+        "graph_GBps": round(alg / (ms_graph * 1e-3) / 1e9, 2),
         "step_us_spread": {"loops": len(chunks), "steps_per_loop": 25,
                            "median": round(chunks[len(chunks) // 2] * 1e3, 3),
                            "min": round(chunks[0] * 1e3, 3), "max": round(chunks[-1] * 1e3, 3)},
