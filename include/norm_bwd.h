@@ -266,8 +266,9 @@ int norm_bwd_wgrad(int kind, const void *x, const void *dy, const float *mean,
 /*
  * (Declared above.) norm_bwd_workspace_bytes returns enough for the automatic
  * plan of either statistics mode: LayerNorm in recompute mode plans more row
- * groups (a second workgroup per compute unit hides its second exchange per
- * row), so for LayerNorm it is max(saved-statistics plan, recompute plan).
+ * groups on one row per wave (a second workgroup per compute unit hides its
+ * second exchange per row), so for LayerNorm it is max(saved-statistics
+ * plan, recompute plan).
  */
 
 /*
@@ -312,9 +313,10 @@ typedef struct norm_bwd_plan {
  * Fill *plan for (kind, M, N, io_dtype, with_dbeta). groups = 0 chooses the
  * automatic group count: 256, at most ceil(M / 4) -- a function of the
  * problem only, never of the device. (The entry points that recompute
- * LayerNorm statistics plan their own: 512-thread workgroups and about 4096
- * waves in flight, at most ceil(M / 4) groups, above 256 rounded down to a
- * multiple of 256; RMSNorm recompute plans as here.) groups > 0 asks for
+ * LayerNorm statistics on one row per wave plan their own: 512-thread
+ * workgroups and about 4096 waves in flight, at most ceil(M / 4) groups,
+ * above 256 rounded down to a multiple of 256; RMSNorm recompute, and
+ * LayerNorm recompute on two rows per wave, take the groups as here.) groups > 0 asks for
  * that many row groups, clamped to M so that no group is empty. The lane
  * layout takes at most 32 bytes of each operand per lane, then the fewest
  * waves per row (a power of two), except that widths which waves of 32-byte

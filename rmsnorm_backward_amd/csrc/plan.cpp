@@ -366,9 +366,9 @@ int wgrad_lanes_per_row(int64_t N, int vec) {
 
 int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype, bool recompute) {
   if (M <= 0) return 0;
-  // kSavedStatsGroups, except in LayerNorm recompute mode: enough
-  // workgroups for about kRecomputeLnTargetWaves waves in flight (16 per
-  // compute unit on a 256-CU part). Never fewer than kMinRowsPerGroup rows
+  // kSavedStatsGroups, except in LayerNorm recompute mode on one row per
+  // wave: enough workgroups for about kRecomputeLnTargetWaves waves in
+  // flight (16 per compute unit on a 256-CU part). Never fewer than kMinRowsPerGroup rows
   // per group, above kGroupQuantum a multiple of it. The geometry is itself
   // a function of (kind, N, io_dtype), so the group count depends on the
   // problem only, never on the device.

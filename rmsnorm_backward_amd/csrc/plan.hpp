@@ -93,9 +93,9 @@ int64_t forward_two_row_grid(int64_t M, int W);
 int wgrad_lanes_per_row(int64_t N, int vec);
 
 // Automatic group count for (kind, M, N, io_dtype) and the statistics mode:
-// 256, except LayerNorm in recompute mode (about 4096 waves in flight: 512
-// for its 512-thread workgroups); at least 4 rows per group, above 256 a
-// multiple of 256. Independent of the device.
+// 256, except LayerNorm in recompute mode on one row per wave (about 4096
+// waves in flight: 512 for its 512-thread workgroups); at least 4 rows per
+// group, above 256 a multiple of 256. Independent of the device.
 int64_t auto_groups(int kind, int64_t M, int64_t N, int io_dtype, bool recompute = false);
 
 // Fill *plan (see norm_bwd_make_plan). `vec_ok16` says whether the caller's
