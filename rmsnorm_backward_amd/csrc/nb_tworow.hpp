@@ -392,7 +392,8 @@ void dx_partials_tworow_kernel(const void* __restrict__ xv, const void* __restri
 // first lane of each half. Rows carry no cross-row state, so in sweep k
 // wave w of workgroup b takes the pair q = (k * gridDim.x + b) * P + w: all
 // workgroups sweep one address window together. Rows are contiguous (row
-// stride N); the host checked 2 * N * EB < 2^32.
+// stride N), and the launch checks N = 32 * VEC * C, so a pair spans at most
+// 2 * 768 * 2 bytes and its 32-bit buffer offsets cannot overflow.
 template <int KIND, class Tg, int C, bool BETA>
 __global__ __launch_bounds__(kTwoRowMaxThreads)
 void norm_fwd_tworow_kernel(const void* __restrict__ xv, const void* __restrict__ gv,

@@ -46,11 +46,21 @@ FORWARD_SOURCES = (KERNEL_SOURCE, os.path.join(_HERE, "csrc", "nb_forward.hpp"),
                    os.path.join(_HERE, "csrc", "nb_tworow.hpp"))
 
 
+def _code_only(text: str) -> str:
+    """The source without its comments, trailing blanks and empty lines: an
+    edit of a comment does not change the kernel the counters were taken on.
+    (The kernel sources hold no string literals that contain comment
+    markers.)"""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", line).rstrip() for line in text.splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def _hash(paths) -> str:
     h = hashlib.sha256()
     for p in paths:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -138,3 +138,13 @@ def test_placed_buffers_are_disjoint_aligned_and_seeded(shape, count):
     assert [b.data_ptr() - base for b in bufs] == [b.data_ptr() - _.data_ptr() for b in again]
     other, p2 = bench.placed_buffers(torch, "cpu", torch.bfloat16, shape, count, 8)
     assert [b.data_ptr() - base for b in bufs] != [b.data_ptr() - p2.data_ptr() for b in other]
+
+
+def test_source_hash_ignores_comments_only():
+    """The counters stay valid across comment edits of the kernel sources,
+    and not across code edits."""
+    code = "int f(int a) {\n  return a + 1;  // one more\n}\n/* a\n   block */\n"
+    base = profiling._code_only(code)
+    assert base == profiling._code_only(code.replace("one more", "plus one") + "\n\n// end\n")
+    assert base != profiling._code_only(code.replace("a + 1", "a + 2"))
+    assert "one more" not in base and "block" not in base
