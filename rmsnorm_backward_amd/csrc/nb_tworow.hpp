@@ -308,6 +308,16 @@ void dx_partials_tworow_kernel(const void* __restrict__ xv, const void* __restri
                                  span_y, col0, cstride);
           process_pair<KIND, RECOMP, true>(buf[d], gam, acc, dx, pair0(k), row_of(k), true, hi, ldo,
                                    hoff_o, span_o, inv_n, eps, col0, cstride);
+          // RMSNorm with saved statistics: keep the next pair's arithmetic
+          // below this point. Hoisted above the loop top, it needed the
+          // pair loaded last and so a wait for nearly every load in flight
+          // (vmcnt counts in order): the ring drained once a loop (waits
+          // down to 1 of 18 loads). Fenced, the waits keep 6-16 in flight:
+          // 262144 x 768 bf16 202.5 -> 195.1 us, 1048576 x 256 270.9 ->
+          // 261.0, fp32 x 384 222.8 -> 212.0, fp32 x 128 135.6 -> 132.1.
+          // LayerNorm and recompute mode were even or slower fenced (fp32
+          // LayerNorm x 128 +7.8%, RMSNorm recompute x 256 +19.8%).
+          if constexpr (!RECOMP && KIND == kRmsNorm) __builtin_amdgcn_sched_barrier(0);
         }
       }
     } else {
