@@ -95,6 +95,11 @@ def parse_args(argv=None):
                     help="also time the workload over this many seeded random placements of its "
                          "operands, with the triad on the same buffers (config.workloads[]."
                          "placements)")
+    ap.add_argument("--compare-lib", default=None,
+                    help="another build of the library (a .so path): time its backward step "
+                         "against this build's on the same buffers, in alternating loops, and "
+                         "check that one step of each gives the same bytes "
+                         "(config.workloads[].compare_lib)")
     ap.add_argument("--compare-plan", default=None,
                     help="with --placements: also time this edited plan (as --plan) on the same "
                          "buffers of every placement")
@@ -549,6 +554,39 @@ def backward_step(nb, lib, w, explicit, full_args, part_args, wg, dgamma, dbeta)
     return step
 
 
+def compare_builds(torch, nb, lib, other, w, sets, full_args, dgamma, dbeta, ws, io, stream,
+                   steps, path, rounds=8):
+    """The backward step (named entry point, automatic plan) of this build and
+    of `other`, another build of the library, on the same buffer sets and
+    workspace, timed in alternating loops of `steps` steps (`rounds` each);
+    and whether one step of each on buffer set 0 writes the same bytes."""
+    with_db = dbeta is not None
+    need = other.norm_bwd_workspace_bytes(0 if w.kind == "layernorm" else 1, w.M, w.N, io,
+                                          int(with_db))
+    if need > ws.numel():
+        raise RuntimeError(f"{path} needs a {need}-byte workspace, the bench holds {ws.numel()}")
+    fa = backward_step(nb, lib, w, False, full_args, None, None, dgamma, dbeta)
+    fb = backward_step(nb, other, w, False, full_args, None, None, dgamma, dbeta)
+    outs = []
+    for f in (fa, fb):
+        f(0)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (sets[0]["dx"], dgamma, dbeta) if t is not None])
+    same = all(torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+               for a, b in zip(outs[0], outs[1]))
+    for i in range(max(10, steps // 2)):
+        fa(i)
+        fb(i)
+    ta, tb = [], []
+    for _ in range(rounds):
+        ta.append(time_loop(torch, fa, steps, stream))
+        tb.append(time_loop(torch, fb, steps, stream))
+    ma, mb = sorted(ta)[len(ta) // 2], sorted(tb)[len(tb) // 2]
+    return {"path": path, "rounds": rounds, "steps_per_round": steps,
+            "this_step_us": round(ma * 1e3, 3), "other_step_us": round(mb * 1e3, 3),
+            "other_over_this": round(mb / ma, 4), "bitwise_equal": bool(same)}
+
+
 def graph_step_time(torch, nb, w, sets, dgamma, dbeta, ws, steps):
     """ms per backward step replayed from a captured HIP graph: one capture
     of a step on every buffer set in turn (the named entry point through the
@@ -718,6 +756,10 @@ def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, ext
     torch.cuda.synchronize()
     ms = time_loop(torch, step, steps, stream)
     ms_graph = graph_step_time(torch, nb, w, sets, dgamma, dbeta, ws, steps)
+    cmp = None
+    if args.compare_lib:
+        cmp = compare_builds(torch, nb, lib, nb.load_library_at(args.compare_lib), w, sets,
+                             full_args, dgamma, dbeta, ws, io, stream, steps, args.compare_lib)
     # the spread of the step time: 20 loops of 25 steps, each loop's mean
     chunks = sorted(time_loop(torch, step, 25, stream) for _ in range(20))
     ms_a = time_loop(torch, step_a, steps, stream)
@@ -745,6 +787,7 @@ def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, ext
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "rows_per_s": round(w.M / (ms * 1e-3), 1),
         "graph_step_us": round(ms_graph * 1e3, 3),
+        **({"compare_lib": cmp} if cmp else {}),
         "graph_GBps": round(alg / (ms_graph * 1e-3) / 1e9, 2),
         "step_us_spread": {"loops": len(chunks), "steps_per_loop": 25,
                            "median": round(chunks[len(chunks) // 2] * 1e3, 3),

@@ -111,6 +111,45 @@ def library_path() -> str:
     return LIB_PATH
 
 
+def _declare(lib, strict: bool = True) -> None:
+    """Set the argument and result types of the library's entry points.
+    strict=False leaves out the entry points a build does not export (an
+    older build, loaded to compare with)."""
+    vp, i32, i64, sz, fp = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                            ctypes.c_size_t, ctypes.c_float)
+    P = ctypes.POINTER(NormBwdPlan)
+    sigs = {
+        "norm_bwd_layernorm": [vp, vp, vp, vp, vp, i64, i64, i32, i32, fp, vp, vp, vp, vp, sz, vp],
+        "norm_bwd_rmsnorm": [vp, vp, vp, vp, i64, i64, i32, i32, fp, vp, vp, vp, vp, sz, vp],
+        "norm_bwd_workspace_bytes": [i32, i64, i64, i32, i32],
+        "norm_bwd_make_plan": [i32, i64, i64, i32, i32, i64, P],
+        "norm_bwd_execute": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp],
+        "norm_bwd_execute_partials": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "norm_bwd_reduce_partials": [i64, i64, i32, vp, sz, vp, vp, vp],
+        "norm_bwd_status_string": [i32],
+        "norm_bwd_last_error": [],
+        "norm_bwd_probe_copy": [vp, vp, sz, vp],
+        "norm_bwd_probe_triad": [vp, vp, vp, sz, i32, i32, vp],
+        "norm_bwd_probe_triad_policy": [vp, vp, vp, sz, i32, i32, i32, vp],
+        "norm_fwd_layernorm": [vp, vp, vp, i64, i64, i32, fp, vp, vp, vp, vp],
+        "norm_fwd_rmsnorm": [vp, vp, i64, i64, i32, fp, vp, vp, vp],
+        "norm_bwd_ex": [ctypes.POINTER(NormBwdArgs)],
+        "norm_bwd_ex_static": [ctypes.POINTER(NormBwdArgs)],
+        "norm_bwd_wgrad": [i32, vp, vp, vp, vp, i64, i64, i32, i32, vp, vp, ctypes.c_uint, vp],
+    }
+    restypes = {"norm_bwd_workspace_bytes": ctypes.c_size_t,
+                "norm_bwd_status_string": ctypes.c_char_p,
+                "norm_bwd_last_error": ctypes.c_char_p}
+    for name, args in sigs.items():
+        f = getattr(lib, name, None)
+        if f is None:
+            if strict:
+                raise RuntimeError(f"the library does not export {name}")
+            continue
+        f.argtypes = args
+        f.restype = restypes.get(name, ctypes.c_int)
+
+
 def load_library():
     """Load the HIP library (raises if it has not been built)."""
     global _lib
@@ -122,37 +161,20 @@ def load_library():
                 f"{LIB_PATH} is missing: build it first (python -m rmsnorm_backward_amd._build "
                 "or __graft_entry__.build()). There is no CPU fallback.")
         lib = ctypes.CDLL(LIB_PATH)
-        vp, i32, i64, sz, fp = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
-                                ctypes.c_size_t, ctypes.c_float)
-        P = ctypes.POINTER(NormBwdPlan)
-        sigs = {
-            "norm_bwd_layernorm": [vp, vp, vp, vp, vp, i64, i64, i32, i32, fp, vp, vp, vp, vp, sz, vp],
-            "norm_bwd_rmsnorm": [vp, vp, vp, vp, i64, i64, i32, i32, fp, vp, vp, vp, vp, sz, vp],
-            "norm_bwd_workspace_bytes": [i32, i64, i64, i32, i32],
-            "norm_bwd_make_plan": [i32, i64, i64, i32, i32, i64, P],
-            "norm_bwd_execute": [P, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp],
-            "norm_bwd_execute_partials": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
-            "norm_bwd_reduce_partials": [i64, i64, i32, vp, sz, vp, vp, vp],
-            "norm_bwd_status_string": [i32],
-            "norm_bwd_last_error": [],
-            "norm_bwd_probe_copy": [vp, vp, sz, vp],
-            "norm_bwd_probe_triad": [vp, vp, vp, sz, i32, i32, vp],
-            "norm_bwd_probe_triad_policy": [vp, vp, vp, sz, i32, i32, i32, vp],
-            "norm_fwd_layernorm": [vp, vp, vp, i64, i64, i32, fp, vp, vp, vp, vp],
-            "norm_fwd_rmsnorm": [vp, vp, i64, i64, i32, fp, vp, vp, vp],
-            "norm_bwd_ex": [ctypes.POINTER(NormBwdArgs)],
-            "norm_bwd_ex_static": [ctypes.POINTER(NormBwdArgs)],
-            "norm_bwd_wgrad": [i32, vp, vp, vp, vp, i64, i64, i32, i32, vp, vp, ctypes.c_uint, vp],
-        }
-        for name, args in sigs.items():
-            f = getattr(lib, name)
-            f.argtypes = args
-            f.restype = ctypes.c_int
-        lib.norm_bwd_workspace_bytes.restype = ctypes.c_size_t
-        lib.norm_bwd_status_string.restype = ctypes.c_char_p
-        lib.norm_bwd_last_error.restype = ctypes.c_char_p
+        _declare(lib)
         _lib = lib
         return lib
+
+
+def load_library_at(path: str):
+    """Another build of the library at `path`, loaded beside this one (its
+    own symbols and kernels), for timing two builds on the same buffers.
+    Entry points that build does not export stay undeclared."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} does not exist")
+    lib = ctypes.CDLL(os.path.abspath(path))
+    _declare(lib, strict=False)
+    return lib
 
 
 def norm_bwd_status_string(status: int) -> str:

@@ -148,3 +148,19 @@ def test_source_hash_ignores_comments_only():
     assert base == profiling._code_only(code.replace("one more", "plus one") + "\n\n// end\n")
     assert base != profiling._code_only(code.replace("a + 1", "a + 2"))
     assert "one more" not in base and "block" not in base
+
+
+def test_compare_lib_loads_another_build():
+    """--compare-lib takes a path to another build; the binding loads it
+    beside the default library with its entry points declared, and refuses a
+    missing path."""
+    import rmsnorm_backward_amd as nb
+    assert bench.parse_args(["--compare-lib", "/tmp/x.so"]).compare_lib == "/tmp/x.so"
+    assert bench.parse_args([]).compare_lib is None
+    other = nb.load_library_at(nb.library_path())
+    assert other.norm_bwd_rmsnorm.argtypes is not None
+    assert other.norm_bwd_workspace_bytes.restype is not None
+    assert other.norm_bwd_workspace_bytes(1, 16384, 4096, 2, 0) == \
+        nb.load_library().norm_bwd_workspace_bytes(1, 16384, 4096, 2, 0)
+    with pytest.raises(RuntimeError):
+        nb.load_library_at("/nonexistent/libnorm_bwd.so")
