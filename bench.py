@@ -96,10 +96,10 @@ def parse_args(argv=None):
                          "operands, with the triad on the same buffers (config.workloads[]."
                          "placements)")
     ap.add_argument("--compare-lib", default=None,
-                    help="another build of the library (a .so path): time its backward step "
-                         "against this build's on the same buffers, in alternating loops, and "
-                         "check that one step of each gives the same bytes "
-                         "(config.workloads[].compare_lib)")
+                    help="another build of the library (a .so path): time its backward step, "
+                         "recompute mode and forward against this build's on the same buffers, "
+                         "in alternating loops, and check that one call of each gives the same "
+                         "bytes (config.workloads[].compare_lib)")
     ap.add_argument("--compare-plan", default=None,
                     help="with --placements: also time this edited plan (as --plan) on the same "
                          "buffers of every placement")
@@ -556,35 +556,63 @@ def backward_step(nb, lib, w, explicit, full_args, part_args, wg, dgamma, dbeta)
 
 def compare_builds(torch, nb, lib, other, w, sets, full_args, dgamma, dbeta, ws, io, stream,
                    steps, path, rounds=8):
-    """The backward step (named entry point, automatic plan) of this build and
-    of `other`, another build of the library, on the same buffer sets and
-    workspace, timed in alternating loops of `steps` steps (`rounds` each);
-    and whether one step of each on buffer set 0 writes the same bytes."""
+    """This build and `other`, another build of the library, on the same
+    buffer sets and workspace: the backward step (named entry point,
+    automatic plan), the backward in recompute mode (NULL statistics) and the
+    forward, each timed in alternating loops of `steps` steps (`rounds`
+    each), and whether one call of each build on buffer set 0 writes the
+    same bytes."""
     with_db = dbeta is not None
-    need = other.norm_bwd_workspace_bytes(0 if w.kind == "layernorm" else 1, w.M, w.N, io,
-                                          int(with_db))
+    kind = 0 if w.kind == "layernorm" else 1
+    need = other.norm_bwd_workspace_bytes(kind, w.M, w.N, io, int(with_db))
     if need > ws.numel():
         raise RuntimeError(f"{path} needs a {need}-byte workspace, the bench holds {ws.numel()}")
-    fa = backward_step(nb, lib, w, False, full_args, None, None, dgamma, dbeta)
-    fb = backward_step(nb, other, w, False, full_args, None, None, dgamma, dbeta)
-    outs = []
-    for f in (fa, fb):
-        f(0)
-        torch.cuda.synchronize()
-        outs.append([t.clone() for t in (sets[0]["dx"], dgamma, dbeta) if t is not None])
-    same = all(torch.equal(a.view(torch.uint8), b.view(torch.uint8))
-               for a, b in zip(outs[0], outs[1]))
-    for i in range(max(10, steps // 2)):
-        fa(i)
-        fb(i)
-    ta, tb = [], []
-    for _ in range(rounds):
-        ta.append(time_loop(torch, fa, steps, stream))
-        tb.append(time_loop(torch, fb, steps, stream))
-    ma, mb = sorted(ta)[len(ta) // 2], sorted(tb)[len(tb) // 2]
-    return {"path": path, "rounds": rounds, "steps_per_round": steps,
-            "this_step_us": round(ma * 1e3, 3), "other_step_us": round(mb * 1e3, 3),
-            "other_over_this": round(mb / ma, 4), "bitwise_equal": bool(same)}
+    P = ctypes.c_void_p
+    sh = P(stream.cuda_stream)
+    ptr = lambda t: None if t is None else P(t.data_ptr())  # noqa: E731
+    rc_args = [(a[0], a[1], a[2], None, None) + a[5:] if kind == 0
+               else (a[0], a[1], a[2], None) + a[4:] for a in full_args]
+    fwd_args = [(ptr(s["x"]), ptr(s["gamma"]), ptr(s.get("beta")), w.M, w.N, io, w.eps,
+                 ptr(s["dx"]), ptr(s["f_mean"]), ptr(s["f_rstd"]), sh) if kind == 0
+                else (ptr(s["x"]), ptr(s["gamma"]), w.M, w.N, io, w.eps, ptr(s["dx"]),
+                      ptr(s["f_rstd"]), sh) for s in sets]
+    bwd = "norm_bwd_layernorm" if kind == 0 else "norm_bwd_rmsnorm"
+    fwd = "norm_fwd_layernorm" if kind == 0 else "norm_fwd_rmsnorm"
+    s0 = sets[0]
+    modes = {
+        "backward": (bwd, full_args, (s0["dx"], dgamma, dbeta)),
+        "recompute": (bwd, rc_args, (s0["dx"], dgamma, dbeta)),
+        "forward": (fwd, fwd_args, (s0["dx"], s0["f_mean"] if kind == 0 else None, s0["f_rstd"])),
+    }
+    out = {"path": path, "rounds": rounds, "steps_per_round": steps}
+    for mode, (name, args, outputs) in modes.items():
+        def make(L, name=name, args=args):
+            fn = getattr(L, name)
+
+            def step(i):
+                st = fn(*args[i % len(args)])
+                if st:
+                    raise RuntimeError(f"{name} returned {st}")
+            return step
+        fa, fb = make(lib), make(other)
+        snaps = []
+        for f in (fa, fb):
+            f(0)
+            torch.cuda.synchronize()
+            snaps.append([t.clone() for t in outputs if t is not None])
+        same = all(torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+                   for a, b in zip(snaps[0], snaps[1]))
+        for i in range(max(10, steps // 2)):
+            fa(i)
+            fb(i)
+        ta, tb = [], []
+        for _ in range(rounds):
+            ta.append(time_loop(torch, fa, steps, stream))
+            tb.append(time_loop(torch, fb, steps, stream))
+        ma, mb = sorted(ta)[len(ta) // 2], sorted(tb)[len(tb) // 2]
+        out[mode] = {"this_us": round(ma * 1e3, 3), "other_us": round(mb * 1e3, 3),
+                     "other_over_this": round(mb / ma, 4), "bitwise_equal": bool(same)}
+    return out
 
 
 def graph_step_time(torch, nb, w, sets, dgamma, dbeta, ws, steps):
@@ -732,6 +760,11 @@ def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, ext
     # enough for the explicit plan and for the automatic plan of either
     # statistics mode (LayerNorm recompute plans more row groups)
     ws_bytes = max(plan.workspace_bytes, nb.norm_bwd_workspace_bytes(w.kind, w.M, w.N, io, with_db))
+    # another build to compare with may plan a larger workspace
+    other = nb.load_library_at(args.compare_lib) if args.compare_lib else None
+    if other is not None:
+        ws_bytes = max(ws_bytes, other.norm_bwd_workspace_bytes(
+            0 if w.kind == "layernorm" else 1, w.M, w.N, io, int(with_db)))
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     P = ctypes.c_void_p
     ptr = lambda t: None if t is None else P(t.data_ptr())  # noqa: E731
@@ -758,8 +791,8 @@ def measure_workload(torch, nb, W, lib, dev, stream, w, args, steps, warmup, ext
     ms_graph = graph_step_time(torch, nb, w, sets, dgamma, dbeta, ws, steps)
     cmp = None
     if args.compare_lib:
-        cmp = compare_builds(torch, nb, lib, nb.load_library_at(args.compare_lib), w, sets,
-                             full_args, dgamma, dbeta, ws, io, stream, steps, args.compare_lib)
+        cmp = compare_builds(torch, nb, lib, other, w, sets, full_args, dgamma, dbeta, ws, io,
+                             stream, steps, args.compare_lib)
     # the spread of the step time: 20 loops of 25 steps, each loop's mean
     chunks = sorted(time_loop(torch, step, 25, stream) for _ in range(20))
     ms_a = time_loop(torch, step_a, steps, stream)
