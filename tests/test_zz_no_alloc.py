@@ -49,6 +49,9 @@ PAIRS = [
      ("layernorm", torch.float16, 500, 2048, True, True, 8, True, 0)),
     (("layernorm", torch.float32, 2000, 1536, False, True, 4, False, 333),
      ("rmsnorm", torch.float32, 129, 1000, False, True, 0, True, 7)),
+    # two rows per wave: strided saved statistics, then recompute, accumulating
+    (("layernorm", torch.bfloat16, 20001, 768, False, True, 8, False, 0),
+     ("layernorm", torch.bfloat16, 513, 256, True, True, 0, True, 0)),
     # rows beyond the fused limits: the workspace holds recomputed statistics
     (("layernorm", torch.float32, 64, 20000, True, True, 0, False, 0),
      ("rmsnorm", torch.float32, 5, 17000, True, False, 0, False, 0)),
