@@ -235,7 +235,14 @@ void dx_partials_tworow_kernel(const void* __restrict__ xv, const void* __restri
                                int64_t ldy, int64_t ldo, int64_t G, int P, float eps) {
   constexpr int EB = Tg::kBytes;
   constexpr int VEC = 16 / EB;
-  constexpr int D = kTwoRowDepth;
+  // LayerNorm with saved statistics keeps one pair less in flight: with its
+  // heavier arithmetic it needs every SIMD busy (4 waves a workgroup), and a
+  // ring of 3 then put twice the bytes in flight that the layout runs best
+  // with. Ring of 2 against 3, on the same buffers: 87381 x 768 bf16 73.2
+  // against 76.9 us, 262144 x 768 206.8 against 218.7, 262144 x 256 73.9
+  // against 74.4, fp32 x 384 even; recompute mode was slower with it (x 768
+  // +2.5 and +4.3%, x 256 +12%).
+  constexpr int D = (KIND == kLayerNorm && !RECOMP) ? 2 : kTwoRowDepth;
   using PK = Pack<Tg, VEC>;
   using RB = RowBuf<Tg, VEC, C>;
   const char* __restrict__ x = static_cast<const char*>(xv);
