@@ -99,10 +99,12 @@ def _same_pattern(got, ref, what):
     assert np.array_equal(np.isneginf(g), np.isneginf(r)), f"{what}: -inf positions differ"
 
 
+@pytest.mark.parametrize("M,N", [(64, 512), (65, 384), (64, 128)],
+                         ids=["one-row-per-wave", "two-rows-3-chunks", "two-rows-1-chunk"])
 @pytest.mark.parametrize("kind", ["rmsnorm", "layernorm"])
-def test_non_finite_inputs_propagate_like_the_arithmetic(nb, kind):
+def test_non_finite_inputs_propagate_like_the_arithmetic(nb, kind, M, N):
     base = W.RMS_F32_128x512 if kind == "rmsnorm" else W.LN_F32_128x512
-    w = W.scaled(base, M=64, N=512)
+    w = W.scaled(base, M=M, N=N)
     inp = backward_inputs(w)
     x, dy = inp["x"].clone(), inp["dy"].clone()
     x[3, 17] = float("nan")
@@ -128,3 +130,32 @@ def test_non_finite_inputs_propagate_like_the_arithmetic(nb, kind):
     # rows without a non-finite input stay finite
     clean = [r for r in range(w.M) if r not in (3, 9, 20)]
     assert torch.isfinite(dx.cpu()[clean]).all()
+
+
+@pytest.mark.parametrize("N", [512, 384, 128])
+@pytest.mark.parametrize("kind", ["rmsnorm", "layernorm"])
+def test_forward_non_finite_rows(nb, kind, N):
+    """A NaN or an infinity in a row of x makes that row's statistics and y
+    non-finite as the oracle's arithmetic does; the other rows, including
+    the other row of a two-row pair, stay finite."""
+    base = W.RMS_F32_128x512 if kind == "rmsnorm" else W.LN_F32_128x512
+    w = W.scaled(base, M=33, N=N)
+    inp = W.make_inputs(w)
+    x = inp["x"].clone()
+    x[4, 7] = float("nan")
+    x[11, N - 1] = float("inf")
+    x[32, 0] = float("-inf")                 # the last row: a pair of one row
+    g = inp["gamma"]
+    if kind == "layernorm":
+        y, mean, rstd = nb.norm_fwd_layernorm(x.cuda(), g.cuda(), None, w.eps)
+    else:
+        y, rstd = nb.norm_fwd_rmsnorm(x.cuda(), g.cuda(), w.eps)
+        mean = None
+    torch.cuda.synchronize()
+    ry, rm, rr = oracle.fwd(kind, x, g, None, w.eps)
+    _same_pattern(y.cpu(), ry, "y")
+    _same_pattern(rstd.cpu(), rr, "rstd")
+    if mean is not None:
+        _same_pattern(mean.cpu(), rm, "mean")
+    clean = [r for r in range(w.M) if r not in (4, 11, 32)]
+    assert torch.isfinite(y.cpu()[clean]).all() and torch.isfinite(rstd.cpu()[clean]).all()
