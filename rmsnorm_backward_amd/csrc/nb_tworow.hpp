@@ -74,7 +74,7 @@ __device__ __forceinline__ float lane_sum_sq(const Pack<Tg, VEC> (&x)[C], float 
   return s;
 }
 
-constexpr int kTwoRowDepth = 3;         // ring of row pairs (two in flight)
+constexpr int kTwoRowDepth = 3;  // ring of row pairs (two ahead; LayerNorm saved: see the kernel)
 constexpr int kTwoRowMaxThreads = 512;  // launch bound: 256 VGPRs per lane
 
 // Loads of one row pair. RALL (steady state): both rows exist; the wave

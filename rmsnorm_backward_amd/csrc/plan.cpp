@@ -74,7 +74,8 @@ constexpr int kTwoRowMaxThreads = 512;
 // and dy reach this many bytes. Interleaved on the same buffers, one row per
 // wave against two: 262144 x 768 bf16 RMSNorm 219.1 us against 210.7 us at 4
 // rows (8: 220.9, 16: 231.1); 1048576 x 256 317.5 against 285.7 at 8 rows
-// (4: 411.4, 16: 309.6). Rings deeper than 3 row pairs were slower.
+// (4: 411.4, 16: 309.6). Rings deeper than 3 row pairs were slower (LayerNorm
+// with saved statistics runs a ring of 2: nb_tworow.hpp).
 constexpr int64_t kTwoRowBytesInFlight = 8192;
 // LayerNorm, with its second row sum, needs more rows in flight on that
 // layout: paired on the same buffers over six placements, A + B, against one
