@@ -235,14 +235,19 @@ void dx_partials_tworow_kernel(const void* __restrict__ xv, const void* __restri
                                int64_t ldy, int64_t ldo, int64_t G, int P, float eps) {
   constexpr int EB = Tg::kBytes;
   constexpr int VEC = 16 / EB;
-  // LayerNorm with saved statistics keeps one pair less in flight: with its
-  // heavier arithmetic it needs every SIMD busy (4 waves a workgroup), and a
-  // ring of 3 then put twice the bytes in flight that the layout runs best
-  // with. Ring of 2 against 3, on the same buffers: 87381 x 768 bf16 73.2
-  // against 76.9 us, 262144 x 768 206.8 against 218.7, 262144 x 256 73.9
-  // against 74.4, fp32 x 384 even; recompute mode was slower with it (x 768
-  // +2.5 and +4.3%, x 256 +12%).
-  constexpr int D = (KIND == kLayerNorm && !RECOMP) ? 2 : kTwoRowDepth;
+  // LayerNorm with saved statistics, and RMSNorm recompute on rows of three
+  // chunks, keep one pair less in flight: their workgroups of 4 waves (every
+  // SIMD busy with their heavier arithmetic) put twice the bytes in flight
+  // with a ring of 3 that the 2-wave RMSNorm workgroups do. Ring of 2
+  // against 3, on the same buffers: LayerNorm 87381 x 768 bf16 73.2 against
+  // 76.9 us, 262144 x 768 206.8 against 218.7, 262144 x 256 73.9 against
+  // 74.4, fp32 x 384 even; RMSNorm recompute 262144 x 768 210.0 against
+  // 217.8, fp32 x 384 213.9 against 215.8. Slower with it: LayerNorm
+  // recompute (x 768 +2.5 and +4.3%, x 256 +12%), RMSNorm recompute of one
+  // chunk (x 256 +7%), RMSNorm with saved statistics (2-wave workgroups:
+  // x 768 +25%, x 256 +13%).
+  constexpr int D = ((KIND == kLayerNorm && !RECOMP) || (KIND == kRmsNorm && RECOMP && C == 3))
+                        ? 2 : kTwoRowDepth;
   using PK = Pack<Tg, VEC>;
   using RB = RowBuf<Tg, VEC, C>;
   const char* __restrict__ x = static_cast<const char*>(xv);
