@@ -88,6 +88,8 @@ constexpr int64_t kTwoRowBytesInFlightLN = 16384;
 // same buffers, RMSNorm 1048576 x 256 bf16 296.5 us at 8 KiB (8 rows) against
 // 266.7 at 16 KiB (16 rows), 262144 x 768 214.8 against 217.4, 262144 x 384
 // fp32 even; 32 KiB was slower in every case (226.2, 266.7, 224.9).
+// LayerNorm recompute at 8 KiB instead: 262144 x 768 bf16 299.9 against
+// 221.0 us, 87381 x 768 105.7 against 77.5, 262144 x 256 85.0 against 74.9.
 // The two-row forward: 8 waves per workgroup (its launch bound) and about
 // this many waves in all (256 workgroups). Forward step times against 4096
 // waves (512 workgroups) and against the one-row-per-wave forward: 1048576 x
