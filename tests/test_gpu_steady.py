@@ -121,6 +121,10 @@ def _recompute_cases():
 @pytest.mark.parametrize("kind,dt,N,G,M", list(_recompute_cases()),
                          ids=lambda v: str(v).replace("torch.", ""))
 def test_steady_loop_recompute(nb, kind, dt, N, G, M):
+    recompute_and_compare(nb, kind, dt, N, G, M)
+
+
+def recompute_and_compare(nb, kind, dt, N, G, M):
     w = workload(kind, dt, M, N)
     with_db = kind == "layernorm"
     inp = W.make_inputs(w)
@@ -179,11 +183,11 @@ def test_steady_loop_forward(nb, kind, dt, N, M):
 
 
 # The two-rows-per-wave kernel (rows that 32 lanes of 16-byte vectors cover
-# exactly: N = 32 * VEC * 1 or 3). Its steady-state loop needs at least
-# 5 * P rows per group (P = rows in flight, two per wave, a 3-deep ring);
-# row counts around that threshold and with every kind of tail. The planner
-# takes it for RMSNorm; LayerNorm plans are edited to it here, with the rows
-# in flight the RMSNorm rule gives.
+# exactly: N = 32 * VEC * 1 or 3). Its steady-state loop needs 2 * D - 1
+# complete iterations, that is (2 * D - 1) * P rows per group (P = rows in
+# flight, two per wave), with a ring of D row pairs: 3 for RMSNorm with saved
+# statistics (5 * P rows), 2 for LayerNorm with saved statistics (3 * P
+# rows). Row counts around that threshold and with every kind of tail.
 TWO_ROW = [
     ("rmsnorm", torch.bfloat16, 768, 2),      # P = 8 (4 waves)
     ("layernorm", torch.bfloat16, 768, 2),    # both gradients
@@ -200,8 +204,9 @@ def _two_row_cases():
         P = 2
         while P < 16 and P * 2 * N * eb < (16384 if kind == "layernorm" else 8192):
             P *= 2
-        for M in (G * 5 * P - 1, G * 5 * P, G * 5 * P + 1, G * (6 * P + 3) + 1,
-                  G * (8 * P - 1), 3):
+        T = 3 if kind == "layernorm" else 5          # 2 * D - 1 iterations
+        for M in (G * T * P - 1, G * T * P, G * T * P + 1, G * ((T + 1) * P + 3) + 1,
+                  G * ((T + 3) * P - 1), 3):
             yield kind, dt, N, G, M
 
 
@@ -237,6 +242,54 @@ def test_two_row_rows_in_flight(nb, P):
     out = nb.norm_bwd_execute(plan, g["x"], g["dy"], g["gamma"], g["mean"], g["rstd"])
     torch.cuda.synchronize()
     compare(w, inp, out, inp["mean"], inp["rstd"], True, 3)
+
+
+# Recompute mode on the two-rows-per-wave layout: 16 KiB of x and dy in
+# flight in both kinds, a ring of 2 row pairs for RMSNorm rows of three chunks
+# (3 * P rows per group for the steady-state loop), 3 otherwise (5 * P).
+TWO_ROW_RECOMPUTE = [
+    ("rmsnorm", torch.bfloat16, 768, 2),      # P = 8, ring of 2
+    ("rmsnorm", torch.float32, 384, 1),       # P = 8, ring of 2, one group
+    ("rmsnorm", torch.float16, 256, 2),       # P = 16, ring of 3
+    ("layernorm", torch.bfloat16, 768, 2),    # P = 8, ring of 3, both gradients
+    ("layernorm", torch.float32, 128, 3),     # P = 16, ring of 3
+]
+
+
+def _two_row_recompute_cases():
+    for kind, dt, N, G in TWO_ROW_RECOMPUTE:
+        eb = torch.tensor([], dtype=dt).element_size()
+        P = 2
+        while P < 16 and P * 2 * N * eb < 16384:
+            P *= 2
+        T = 3 if (kind == "rmsnorm" and N * eb == 3 * 512) else 5
+        for M in (G * T * P - 1, G * T * P, G * T * P + 1, G * ((T + 2) * P + 1) + 3):
+            yield kind, dt, N, G, M
+
+
+@pytest.mark.parametrize("kind,dt,N,G,M", list(_two_row_recompute_cases()),
+                         ids=lambda v: str(v).replace("torch.", ""))
+def test_two_row_recompute_steady(nb, kind, dt, N, G, M):
+    recompute_and_compare(nb, kind, dt, N, G, M)
+
+
+# The two-row forward: 8 waves a workgroup and up to 256 workgroups, so a
+# sweep covers 4096 rows; the steady-state loop needs 2 * D - 1 sweeps of
+# complete pairs, with a ring of D = 2 for rows of three chunks (12288 rows)
+# and D = 3 for rows of one (20480).
+FORWARD_TWO_ROW = [
+    ("rmsnorm", torch.bfloat16, 768, (12287, 12288, 12289, 4096 * 5 - 1)),
+    ("layernorm", torch.float32, 384, (12287, 12289)),
+    ("layernorm", torch.float16, 256, (20479, 20480, 20481, 4096 * 7 + 3)),
+    ("rmsnorm", torch.float32, 128, (20479, 20481)),
+]
+
+
+@pytest.mark.parametrize("kind,dt,N,M", [(k, d, n, m) for k, d, n, Ms in FORWARD_TWO_ROW
+                                         for m in Ms],
+                         ids=lambda v: str(v).replace("torch.", ""))
+def test_two_row_forward_steady(nb, kind, dt, N, M):
+    test_steady_loop_forward(nb, kind, dt, N, M)
 
 
 def test_two_row_strided_rows_are_bit_identical(nb):
