@@ -18,10 +18,11 @@
  * parallel over ("Norm & activation backward", section "Half two: dγ and dβ
  * reduce across the whole batch", its strategy table). This library takes the
  * deterministic two-pass route from that table: kernel A computes dx and, for
- * each of G disjoint row groups (group g = the rows r with r mod G == g), the
- * group's partial dgamma/dbeta in registers, stored once into a
- * caller-provided fp32 workspace[G, N]; kernel B sums the groups in one fixed
- * order. There are
+ * each of G disjoint row groups (group g = the rows r with r mod G == g; on
+ * the two-rows-per-wave layout, the adjacent row pairs (2q, 2q + 1) with
+ * q mod G == g), the group's partial dgamma/dbeta in registers, stored once
+ * into a caller-provided fp32 workspace[G, N]; kernel B sums the groups in
+ * one fixed order. There are
  * no atomics, so dx, dgamma and dbeta are bitwise identical across calls with
  * equal arguments (same kind, M, N, dtypes, groups, and pointer alignment
  * class) on the same device type. The group count never depends on the GPU's
@@ -297,7 +298,8 @@ typedef struct norm_bwd_plan {
     int64_t M, N;            /* problem size */
     int64_t groups;          /* G: row groups = workspace rows; group g = rows r, r mod G == g
                                 (two rows per wave: row pairs q, q mod G == g) */
-    int64_t rows_per_group;  /* ceil(M / G): the most rows any group holds */
+    int64_t rows_per_group;  /* ceil(M / G): the most rows any group holds
+                                (two rows per wave: 2 * ceil(ceil(M / 2) / G)) */
     int32_t chunks;          /* C: loads of `vec` elements per lane per row slice */
     int32_t waves_per_row;   /* S: 64-lane waves sharing one row */
     int32_t rows_in_flight;  /* P: rows a workgroup processes at once */
@@ -316,8 +318,9 @@ typedef struct norm_bwd_plan {
  * LayerNorm statistics on one row per wave plan their own: 512-thread
  * workgroups and about 4096 waves in flight, at most ceil(M / 4) groups,
  * above 256 rounded down to a multiple of 256; RMSNorm recompute, and
- * LayerNorm recompute on two rows per wave, take the groups as here.) groups > 0 asks for
- * that many row groups, clamped to M so that no group is empty. The lane
+ * LayerNorm recompute on two rows per wave, take the groups as here.)
+ * groups > 0 asks for that many row groups, clamped to M so that no group is
+ * empty. The lane
  * layout takes at most 32 bytes of each operand per lane, then the fewest
  * waves per row (a power of two), except that widths which waves of 32-byte
  * lanes cover exactly take that many waves (5120 16-bit elements: 5). The
@@ -329,8 +332,9 @@ typedef struct norm_bwd_plan {
  * 768 16-bit, 128 or 384 fp32 elements) take two rows per wave instead, with
  * the fewest rows in flight whose x and dy reach 8 KiB (RMSNorm) or 16 KiB
  * (LayerNorm; recompute mode: 16 KiB in both kinds, and LayerNorm
- * recompute keeps 256 groups there). A plan is for saved statistics. The plan assumes 16-byte aligned base pointers;
- * norm_bwd_execute rejects a plan whose vec the pointers do not allow.
+ * recompute keeps 256 groups there). A plan is for saved statistics. The
+ * plan assumes 16-byte aligned base pointers; norm_bwd_execute rejects a
+ * plan whose vec the pointers do not allow.
  * Host-only. Returns a status code.
  */
 int norm_bwd_make_plan(int kind, int64_t M, int64_t N, int io_dtype,
