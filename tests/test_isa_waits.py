@@ -91,6 +91,10 @@ CASES = [
     ("_ZN2nb18dx_partials_kernelILi1ELb0ENS_5TBF16ELi8ELi2ELi1ELb0ELi1024E", 8),
     # 65536 x 8192 bf16 LayerNorm with dbeta, non-temporal partials
     ("_ZN2nb18dx_partials_kernelILi0ELb0ENS_5TBF16ELi8ELi2ELi2ELb1ELi1024E", 6),
+    # the two-row forward on rows of 3 chunks (a ring of two row pairs): the
+    # next pair's 3 loads stay in flight (unfenced, the waits went down to 0)
+    ("_ZN2nb22norm_fwd_tworow_kernelILi0ENS_5TBF16ELi3ELb0E", 3),
+    ("_ZN2nb22norm_fwd_tworow_kernelILi1ENS_5TBF16ELi3ELb0E", 3),
 ]
 
 
