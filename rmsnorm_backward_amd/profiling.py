@@ -97,7 +97,11 @@ def is_forward(name: str) -> bool:
     return FORWARD in name or FORWARD_TWOROW in name
 
 
-def stats_summary(stats_csv: str, bench_json: str, cmds) -> str:
+def stats_summary(stats_csv: str, bench_json: str, cmds, kernel=None, forward=None) -> str:
+    """`kernel` / `forward`: substrings naming the instantiations to compare
+    with the events (a run over several workloads launches several); by
+    default the saved-statistics kernel A with the most calls and any fused
+    forward."""
     rows = list(csv.DictReader(open(stats_csv)))
     b = _bench(bench_json)
     c = b["config"]
@@ -112,9 +116,12 @@ def stats_summary(stats_csv: str, bench_json: str, cmds) -> str:
         name = r["Name"]
         short = name.split("(")[0].replace("void ", "")
         avg = float(r["AverageNs"]) / 1e3
-        if is_step_kernel_a(name) and int(r["Calls"]) > calls_a:
+        if kernel is not None:
+            if kernel in name:
+                avg_a = avg
+        elif is_step_kernel_a(name) and int(r["Calls"]) > calls_a:
             avg_a, calls_a = avg, int(r["Calls"])
-        if is_forward(name):
+        if (forward in name) if forward is not None else is_forward(name):
             avg_f = avg
         if KERNEL_B in name:
             avg_b = avg
@@ -254,6 +261,8 @@ def main(argv=None):
     s.add_argument("stats_csv")
     s.add_argument("bench_json")
     s.add_argument("--cmd", action="append", default=[])
+    s.add_argument("--kernel", default=None, help="substring naming kernel A's instantiation")
+    s.add_argument("--forward", default=None, help="substring naming the forward's")
     p = sub.add_parser("pmc")
     p.add_argument("fetch_csv")
     p.add_argument("write_csv")
@@ -261,7 +270,7 @@ def main(argv=None):
     p.add_argument("--cmd", action="append", default=[])
     a = ap.parse_args(argv)
     if a.what == "stats":
-        sys.stdout.write(stats_summary(a.stats_csv, a.bench_json, a.cmd))
+        sys.stdout.write(stats_summary(a.stats_csv, a.bench_json, a.cmd, a.kernel, a.forward))
     else:
         sys.stdout.write(pmc_summary(a.fetch_csv, a.write_csv, a.bench_json, a.cmd))
 

@@ -164,3 +164,29 @@ def test_compare_lib_loads_another_build():
         nb.load_library().norm_bwd_workspace_bytes(1, 16384, 4096, 2, 0)
     with pytest.raises(RuntimeError):
         nb.load_library_at("/nonexistent/libnorm_bwd.so")
+
+
+def test_stats_summary_names_the_instantiations(tmp_path):
+    """In a run over several workloads, --kernel and --forward pick the
+    named instantiations; without them the saved-statistics kernel A with the
+    most calls is taken."""
+    import json
+    head = "Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs,StdDev\n"
+    rows = [("void nb::dx_partials_kernel<1, false, nb::TBF16, 8, 2, 1, false, 1024>(a)", 100, 66000),
+            ("void nb::dx_partials_kernel<0, false, nb::TBF16, 8, 2, 2, true, 1024>(a)", 120, 540000),
+            ("void nb::dx_partials_kernel<1, true, nb::TBF16, 8, 2, 1, false, 512>(a)", 500, 70000),
+            ("void nb::norm_fwd_kernel<1, nb::TBF16, 8, 2, false>(a)", 50, 46000),
+            ("void nb::norm_fwd_kernel<0, nb::TBF16, 8, 2, false>(a)", 50, 370000)]
+    csv_path = tmp_path / "stats.csv"
+    csv_path.write_text(head + "".join(f'"{n}",{c},{c * a},{a},1.0,{a},{a},0\n' for n, c, a in rows))
+    cfg = {"workload": "rmsnorm_bf16_16384x4096", "pct_of_peak": 73.0, "kernel_a_us": 66.0,
+           "plan": {}, "forward": {"us": 46.0, "GBps": 5800, "pct_of_peak": 72.5}}
+    bj = tmp_path / "b.json"
+    bj.write_text(json.dumps({"ms_per_step": 0.0688, "value": 5850, "config": cfg}) + "\n")
+    text = profiling.stats_summary(str(csv_path), str(bj), ["cmd"],
+                                   kernel="dx_partials_kernel<1, false, nb::TBF16, 8, 2, 1, false, 1024>",
+                                   forward="norm_fwd_kernel<1, nb::TBF16, 8, 2, false>")
+    assert "kernel A by the trace: 66.00 us (events / trace = 1.000)" in text
+    assert "forward by the trace: 46.00 us (events / trace = 1.000)" in text
+    default = profiling.stats_summary(str(csv_path), str(bj), ["cmd"])
+    assert "kernel A by the trace: 540.00 us" in default
